@@ -1,0 +1,372 @@
+/*
+ * oracle.c -- plain, slow, obviously correct CPU reference for paged
+ * single-query decode attention, the INT8 symmetric KV quantizer and the
+ * slot-mapped cache write.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path (the HIP library
+ * and its Python binding) may include, link or call this file.  It shares no
+ * header, constant, helper or table with the HIP sources; dtype codes below
+ * are defined here on their own.
+ *
+ * Sources (the four web pages on paged KV caches):
+ *  - "Efficient AI Lecture 13: LLM deployment" notes (bittide.aicompass.dev
+ *    mirror), section "PagedAttention", the four numbered steps: the cache of
+ *    a sequence is cut into fixed-size logical blocks, physical blocks live
+ *    anywhere in memory, and a block table translates logical block ids to
+ *    physical ones.
+ *  - docs.lazyllm.ai "Lesson 4: model deployment and inference acceleration",
+ *    section 4.2 "PagedAttention": 16 tokens per block, per-request page
+ *    table, global block pool, and the attention equation
+ *    Attention(Q,K,V) = Softmax(Q K^T / sqrt(d)) V with Q of shape 1 x d and
+ *    K, V of shape T x d; paging leaves that equation unchanged.
+ *  - the same page, section 5.3 "KV Cache Quantization": symmetric INT8,
+ *    K_q = round(K / s_K), s_K = max|K| / 127.
+ *  - juejin.cn "LLM Engineer's Handbook -- inference optimization", the
+ *    absmax-quantization passage with its worked example (0.1 with absmax 3.2
+ *    gives code 4, dequantized 0.1008) and its PyTorch snippet that rounds
+ *    with half-to-even rounding.
+ *  - caojiahao2.github.io "LLM / MLLM inference", section 3.2, and the
+ *    juejin page's "optimized attention" passage: online softmax keeps a
+ *    running max and running sum; it is an exact rearrangement of the same
+ *    softmax, so this oracle computes the plain definition instead.
+ *
+ * Readings where the pages are silent (each one is listed with its reason in
+ * the design notes of the repository):
+ *  - one INT8 scale per (slot, kv head), separately for K and V;
+ *  - quantizer form: s = fl32(amax / 127), code = clamp(rne(fl32(x / s)),
+ *    -127, 127); amax == 0 gives s = 0 and all codes 0;
+ *  - q head h reads kv head h / (Hq / Hkv) (contiguous GQA groups);
+ *  - context_len == 0 gives an all-zero output row;
+ *  - slot < 0 in a slot mapping means "skip this token".
+ *
+ * Everything floating point in the attention is done in IEEE double.  The
+ * quantizer is done in IEEE single, because that is the precision the
+ * reading above fixes for it.  Build: gcc -O2 -fopenmp -ffp-contract=off.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Element type codes, defined here and only here. */
+enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_I8 = 3 };
+
+/* ------------------------------------------------------------------------ */
+/* Exact widening of stored elements to double.                             */
+/* ------------------------------------------------------------------------ */
+
+/* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+double oracle_f16_to_f64(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int expo = (h >> 10) & 0x1f;
+    int frac = h & 0x3ff;
+    double v;
+    if (expo == 0) {
+        v = ldexp((double)frac, -24);             /* subnormal: frac * 2^-14 * 2^-10 */
+    } else if (expo == 31) {
+        v = frac ? NAN : INFINITY;
+    } else {
+        v = ldexp((double)(1024 + frac), expo - 25);  /* (1.frac) * 2^(expo-15) */
+    }
+    return sign ? -v : v;
+}
+
+/* bfloat16 is the upper half of an IEEE binary32. */
+double oracle_bf16_to_f64(uint16_t b) {
+    uint32_t bits = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+static double elem(const void* base, size_t i, int dtype) {
+    switch (dtype) {
+    case OR_F32: return (double)((const float*)base)[i];
+    case OR_F16: return oracle_f16_to_f64(((const uint16_t*)base)[i]);
+    case OR_BF16: return oracle_bf16_to_f64(((const uint16_t*)base)[i]);
+    case OR_I8: return (double)((const int8_t*)base)[i];
+    default: return NAN;
+    }
+}
+
+static size_t elem_size(int dtype) {
+    return dtype == OR_F32 ? 4 : (dtype == OR_I8 ? 1 : 2);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Gather (paging) + dense attention for one (sequence, q head).            */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    const void* q; int q_dtype;
+    const void* k_cache; const void* v_cache; int cache_dtype;
+    const float* k_scale; const float* v_scale;
+    const int32_t* block_tables; int max_blocks_per_seq;
+    const int32_t* context_lens;
+    int B, Hq, Hkv, D, block_size, num_blocks;
+    double scale;
+} problem;
+
+/* Logical token t of sequence b, kv head kvh -> element index of its first
+ * channel in the pool [num_blocks][Hkv][block_size][D], and the index of its
+ * per-token scale in [num_blocks][Hkv][block_size].  Returns -1 if the block
+ * table names a block outside the pool. */
+static long token_row(const problem* P, int b, int kvh, int t, long* scale_idx) {
+    int logical = t / P->block_size;
+    int offset = t % P->block_size;
+    int32_t phys = P->block_tables[(size_t)b * P->max_blocks_per_seq + logical];
+    if (phys < 0 || phys >= P->num_blocks) return -1;
+    long row = ((long)phys * P->Hkv + kvh) * P->block_size + offset;
+    *scale_idx = row;
+    return row * P->D;
+}
+
+/* Gathered K and V of tokens [t0, t1) as dense double matrices. */
+static int gather(const problem* P, int b, int kvh, int t0, int t1, double* K, double* V) {
+    for (int t = t0; t < t1; ++t) {
+        long si = 0;
+        long base = token_row(P, b, kvh, t, &si);
+        if (base < 0) return -1;
+        double ks = 1.0, vs = 1.0;
+        if (P->cache_dtype == OR_I8) {
+            ks = (double)P->k_scale[si];
+            vs = (double)P->v_scale[si];
+        }
+        for (int d = 0; d < P->D; ++d) {
+            K[(size_t)(t - t0) * P->D + d] = elem(P->k_cache, base + d, P->cache_dtype) * ks;
+            V[(size_t)(t - t0) * P->D + d] = elem(P->v_cache, base + d, P->cache_dtype) * vs;
+        }
+    }
+    return 0;
+}
+
+/* Softmax-weighted sum over tokens [t0, t1) of sequence b for q head h.
+ * Outputs the max score m, the sum l of exp(s - m) and o = sum exp(s-m) V / l.
+ * n == 0 gives m = -inf, l = 0, o = 0. */
+static int attend(const problem* P, int b, int h, int t0, int t1, double* m_out, double* l_out,
+                  double* o) {
+    int D = P->D;
+    int g = P->Hq / P->Hkv;
+    int kvh = h / g;
+    int n = t1 - t0;
+    for (int d = 0; d < D; ++d) o[d] = 0.0;
+    if (n <= 0) { *m_out = -INFINITY; *l_out = 0.0; return 0; }
+
+    double* K = malloc(sizeof(double) * (size_t)n * D);
+    double* V = malloc(sizeof(double) * (size_t)n * D);
+    double* s = malloc(sizeof(double) * (size_t)n);
+    double* qv = malloc(sizeof(double) * (size_t)D);
+    if (!K || !V || !s || !qv) { free(K); free(V); free(s); free(qv); return -2; }
+    if (gather(P, b, kvh, t0, t1, K, V) != 0) { free(K); free(V); free(s); free(qv); return -1; }
+
+    size_t qbase = ((size_t)b * P->Hq + h) * D;
+    for (int d = 0; d < D; ++d) qv[d] = elem(P->q, qbase + d, P->q_dtype);
+
+    /* scores s_t = scale * <q, K_t> */
+    double m = -INFINITY;
+    for (int t = 0; t < n; ++t) {
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d) dot += qv[d] * K[(size_t)t * D + d];
+        s[t] = P->scale * dot;
+        if (s[t] > m) m = s[t];
+    }
+    /* softmax weights and weighted sum of V */
+    double l = 0.0;
+    for (int t = 0; t < n; ++t) {
+        double w = exp(s[t] - m);
+        l += w;
+        for (int d = 0; d < D; ++d) o[d] += w * V[(size_t)t * D + d];
+    }
+    for (int d = 0; d < D; ++d) o[d] /= l;
+    *m_out = m;
+    *l_out = l;
+    free(K); free(V); free(s); free(qv);
+    return 0;
+}
+
+static int set_threads(int nthreads) {
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+    return omp_get_max_threads();
+#else
+    (void)nthreads;
+    return 1;
+#endif
+}
+
+/* Full decode attention.  out: double [B][Hq][D].  rows: optional list of
+ * n_rows flattened (b * Hq + h) indices to compute; NULL computes all rows.
+ * Rows not listed are left untouched.  Returns 0, or a negative code when a
+ * block table entry points outside the pool (-1) or memory ran out (-2). */
+int oracle_paged_decode(double* out, const void* q, int q_dtype, const void* k_cache,
+                        const void* v_cache, int cache_dtype, const float* k_scale,
+                        const float* v_scale, const int32_t* block_tables,
+                        int max_blocks_per_seq, const int32_t* context_lens, int B, int Hq,
+                        int Hkv, int D, int block_size, int num_blocks, float scale,
+                        const int64_t* rows, long n_rows, int nthreads) {
+    problem P = {q, q_dtype, k_cache, v_cache, cache_dtype, k_scale, v_scale, block_tables,
+                 max_blocks_per_seq, context_lens, B, Hq, Hkv, D, block_size, num_blocks,
+                 (double)scale};
+    if (Hkv <= 0 || Hq % Hkv != 0 || block_size <= 0) return -3;
+    long total = rows ? n_rows : (long)B * Hq;
+    int status = 0;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long i = 0; i < total; ++i) {
+        long r = rows ? (long)rows[i] : i;
+        int b = (int)(r / Hq), h = (int)(r % Hq);
+        double m, l;
+        int rc = attend(&P, b, h, 0, context_lens[b], &m, &l, out + (size_t)r * D);
+        if (rc != 0) {
+#pragma omp critical
+            status = rc;
+        }
+    }
+    return status;
+}
+
+/* Split-context partials over partitions of `partition_size` tokens:
+ * for partition p of sequence b, tokens [p*P, min((p+1)*P, N_b)).
+ * m, l: double [B][Hq][NP]; o: double [B][Hq][NP][D].  Partitions with no
+ * token get m = -inf, l = 0, o = 0.  The max score m is in natural-log units
+ * of the score s = scale * <q, k>. */
+int oracle_paged_partials(double* m_part, double* l_part, double* o_part, const void* q,
+                          int q_dtype, const void* k_cache, const void* v_cache, int cache_dtype,
+                          const float* k_scale, const float* v_scale,
+                          const int32_t* block_tables, int max_blocks_per_seq,
+                          const int32_t* context_lens, int B, int Hq, int Hkv, int D,
+                          int block_size, int num_blocks, float scale, int partition_size,
+                          int num_partitions, int nthreads) {
+    problem P = {q, q_dtype, k_cache, v_cache, cache_dtype, k_scale, v_scale, block_tables,
+                 max_blocks_per_seq, context_lens, B, Hq, Hkv, D, block_size, num_blocks,
+                 (double)scale};
+    if (Hkv <= 0 || Hq % Hkv != 0 || partition_size <= 0) return -3;
+    long total = (long)B * Hq * num_partitions;
+    int status = 0;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long i = 0; i < total; ++i) {
+        int p = (int)(i % num_partitions);
+        long r = i / num_partitions;
+        int b = (int)(r / Hq), h = (int)(r % Hq);
+        int n = context_lens[b];
+        int t0 = p * partition_size;
+        int t1 = t0 + partition_size < n ? t0 + partition_size : n;
+        int rc = attend(&P, b, h, t0, t1, m_part + i, l_part + i, o_part + (size_t)i * D);
+        if (rc != 0) {
+#pragma omp critical
+            status = rc;
+        }
+    }
+    return status;
+}
+
+/* Merge of partials: out = sum_p w_p o_p / sum_p w_p with w_p = l_p e^{m_p}
+ * (computed relative to M = max_p m_p).  Partitions with l_p == 0 carry no
+ * weight.  A row whose partitions are all empty gives 0. */
+int oracle_merge_partials(double* out, const double* m_part, const double* l_part,
+                          const double* o_part, long rows, int num_partitions, int D) {
+    for (long r = 0; r < rows; ++r) {
+        const double* m = m_part + r * num_partitions;
+        const double* l = l_part + r * num_partitions;
+        double M = -INFINITY;
+        for (int p = 0; p < num_partitions; ++p)
+            if (l[p] > 0.0 && m[p] > M) M = m[p];
+        double* o = out + r * D;
+        for (int d = 0; d < D; ++d) o[d] = 0.0;
+        if (M == -INFINITY) continue;
+        double wsum = 0.0;
+        for (int p = 0; p < num_partitions; ++p) {
+            if (!(l[p] > 0.0)) continue;
+            double w = l[p] * exp(m[p] - M);
+            wsum += w;
+            for (int d = 0; d < D; ++d) o[d] += w * o_part[((size_t)r * num_partitions + p) * D + d];
+        }
+        for (int d = 0; d < D; ++d) o[d] /= wsum;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* INT8 symmetric quantization, one scale per row of D elements.            */
+/* ------------------------------------------------------------------------ */
+
+/* Widen one stored element to single precision.  Exact for f16/bf16/f32. */
+static float elem_f32(const void* base, size_t i, int dtype) {
+    return (float)elem(base, i, dtype);
+}
+
+/* Quantize one row: amax = max |x|; s = amax / 127 in single precision;
+ * code = clamp(round-half-even(x / s), -127, 127) with the division in single
+ * precision.  amax == 0 gives s = 0 and codes 0. */
+static void quantize_row(int8_t* codes, float* scale_out, const void* x, size_t base, int D,
+                         int dtype) {
+    float amax = 0.0f;
+    for (int d = 0; d < D; ++d) {
+        float a = fabsf(elem_f32(x, base + d, dtype));
+        if (a > amax) amax = a;
+    }
+    if (amax == 0.0f) {
+        *scale_out = 0.0f;
+        for (int d = 0; d < D; ++d) codes[d] = 0;
+        return;
+    }
+    volatile float s = amax / 127.0f;  /* one IEEE single-precision division */
+    for (int d = 0; d < D; ++d) {
+        volatile float r = elem_f32(x, base + d, dtype) / s;
+        float c = nearbyintf(r);  /* default rounding mode: to nearest, ties to even */
+        if (c > 127.0f) c = 127.0f;
+        if (c < -127.0f) c = -127.0f;
+        codes[d] = (int8_t)c;
+    }
+    *scale_out = s;
+}
+
+/* x: [rows][D] of dtype; codes: int8 [rows][D]; scales: float [rows]. */
+int oracle_quantize_rows(int8_t* codes, float* scales, const void* x, int dtype, long rows, int D) {
+    for (long r = 0; r < rows; ++r)
+        quantize_row(codes + (size_t)r * D, scales + r, x, (size_t)r * D, D, dtype);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Slot-mapped cache write on host byte images of the pool.                 */
+/* ------------------------------------------------------------------------ */
+
+/* k, v: [T][Hkv][D] of src_dtype.  k_cache, v_cache: [num_blocks][Hkv][block_size][D]
+ * of cache_dtype (equal to src_dtype, or OR_I8).  k_scale, v_scale: float
+ * [num_blocks][Hkv][block_size], used only for OR_I8.  Token i with
+ * slot = slot_mapping[i] >= 0 goes to block slot / block_size, offset
+ * slot % block_size, for every kv head.  Negative slots are skipped.
+ * Returns -1 if a slot is beyond the pool, -3 for an unsupported pairing. */
+int oracle_kv_cache_write(const void* k, const void* v, void* k_cache, void* v_cache,
+                          float* k_scale, float* v_scale, const int64_t* slot_mapping, long T,
+                          int Hkv, int D, int block_size, int num_blocks, int src_dtype,
+                          int cache_dtype) {
+    if (cache_dtype != src_dtype && cache_dtype != OR_I8) return -3;
+    if (cache_dtype == OR_I8 && src_dtype == OR_I8) return -3;
+    size_t es = elem_size(cache_dtype);
+    for (long i = 0; i < T; ++i) {
+        int64_t slot = slot_mapping[i];
+        if (slot < 0) continue;
+        if (slot >= (int64_t)num_blocks * block_size) return -1;
+        int64_t blk = slot / block_size, off = slot % block_size;
+        for (int h = 0; h < Hkv; ++h) {
+            size_t src = ((size_t)i * Hkv + h) * D;
+            size_t dst_row = ((size_t)blk * Hkv + h) * block_size + (size_t)off;
+            if (cache_dtype == OR_I8) {
+                quantize_row((int8_t*)k_cache + dst_row * D, k_scale + dst_row, k, src, D, src_dtype);
+                quantize_row((int8_t*)v_cache + dst_row * D, v_scale + dst_row, v, src, D, src_dtype);
+            } else {
+                memcpy((char*)k_cache + dst_row * D * es, (const char*)k + src * es, D * es);
+                memcpy((char*)v_cache + dst_row * D * es, (const char*)v + src * es, D * es);
+            }
+        }
+    }
+    return 0;
+}
+
+int oracle_num_threads(int nthreads) { return set_threads(nthreads); }

@@ -1,0 +1,423 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+- element widening: every fp16 / bf16 bit pattern against numpy / torch;
+- attention: torch's scaled_dot_product_attention in float64 on contiguous
+  K/V (the library routine the caojiahao2.github.io page shows in section 3.4),
+  closed forms (one token returns V_0; equal keys or a zero scale return the
+  mean of V; one dominant key returns its V), hand-placed blocks, and the
+  placement-permutation invariance the lazyllm page states in section 4.2
+  (paging leaves the attention equation unchanged);
+- split partials + merge: equal to the unsplit result for any partition size
+  (online softmax is an exact rearrangement: caojiahao2 section 3.2);
+- INT8 quantizer: the worked example of the juejin absmax passage, ties to
+  even, extreme codes, and exact rational arithmetic on random rows;
+- cache write: a hand-built slot mapping checked position by position.
+"""
+from fractions import Fraction
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+BS = 16
+
+
+def _golden(name):
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", name)
+    rows = []
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def _bits(t: torch.Tensor) -> np.ndarray:
+    """Raw storage of a torch CPU tensor as numpy (16-bit floats as uint16)."""
+    if t.dtype in (torch.float16, torch.bfloat16):
+        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    return t.contiguous().numpy()
+
+
+DT = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16", torch.int8: "i8"}
+
+
+# --------------------------------------------------------------------------
+# widening
+# --------------------------------------------------------------------------
+
+def test_f16_widening_every_bit_pattern():
+    L = oracle.lib()
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    want = bits.view(np.float16).astype(np.float64)
+    got = np.array([L.oracle_f16_to_f64(int(b)) for b in bits])
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+
+
+def test_bf16_widening_every_bit_pattern():
+    L = oracle.lib()
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    want = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([L.oracle_bf16_to_f64(int(b)) for b in bits])
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+
+
+# --------------------------------------------------------------------------
+# attention against a library routine on contiguous K/V
+# --------------------------------------------------------------------------
+
+def _paged_from_contiguous(K_list, V_list, num_blocks, seed, dtype):
+    """Place each sequence's contiguous K/V ([N][Hkv][D]) into a pool of 16-token
+    blocks at seeded random physical blocks; returns pool tensors and tables."""
+    g = np.random.default_rng(seed)
+    B = len(K_list)
+    Hkv, D = K_list[0].shape[1], K_list[0].shape[2]
+    need = [-(-k.shape[0] // BS) for k in K_list]
+    perm = g.permutation(num_blocks)
+    mbs = max(max(need), 1)
+    tables = np.full((B, mbs), -1, np.int32)
+    kpool = torch.full((num_blocks, Hkv, BS, D), float("nan"), dtype=dtype)
+    vpool = torch.full((num_blocks, Hkv, BS, D), float("nan"), dtype=dtype)
+    pos = 0
+    for b in range(B):
+        for j in range(need[b]):
+            phys = int(perm[pos]); pos += 1
+            tables[b, j] = phys
+            chunk_k = K_list[b][j * BS:(j + 1) * BS]          # [<=16][Hkv][D]
+            chunk_v = V_list[b][j * BS:(j + 1) * BS]
+            n = chunk_k.shape[0]
+            kpool[phys, :, :n, :] = chunk_k.transpose(0, 1)
+            vpool[phys, :, :n, :] = chunk_v.transpose(0, 1)
+    return kpool, vpool, tables
+
+
+def _sdpa(q, K, V, scale, g):
+    """Contiguous reference: q [Hq][D], K/V [N][Hkv][D] -> [Hq][D], float64."""
+    qq = q.to(torch.float64)[None, :, None, :]                 # [1][Hq][1][D]
+    kk = K.to(torch.float64).transpose(0, 1)[None]             # [1][Hkv][N][D]
+    vv = V.to(torch.float64).transpose(0, 1)[None]
+    out = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, scale=scale,
+                                                           enable_gqa=(g > 1))
+    return out[0, :, 0, :]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("Hq,Hkv,D", [(8, 8, 64), (8, 2, 128), (4, 1, 64), (6, 3, 32)])
+def test_attention_matches_sdpa(dtype, Hq, Hkv, D):
+    g_ = np.random.default_rng(7)
+    lens = [1, 15, 16, 17, 40, 100]
+    K_list = [torch.from_numpy(g_.standard_normal((n, Hkv, D), dtype=np.float32)).to(dtype)
+              for n in lens]
+    V_list = [torch.from_numpy(g_.standard_normal((n, Hkv, D), dtype=np.float32)).to(dtype)
+              for n in lens]
+    q = torch.from_numpy(g_.standard_normal((len(lens), Hq, D), dtype=np.float32)).to(dtype)
+    kp, vp, bt = _paged_from_contiguous(K_list, V_list, 32, 3, dtype)
+    scale = float(np.float32(1 / math.sqrt(D)))
+    out = oracle.paged_decode(_bits(q), DT[dtype], _bits(kp), _bits(vp), DT[dtype], bt,
+                              np.array(lens, np.int32), scale)
+    for b in range(len(lens)):
+        ref = _sdpa(q[b], K_list[b], V_list[b], scale, Hq // Hkv).numpy()
+        np.testing.assert_allclose(out[b], ref, rtol=0, atol=1e-12)
+
+
+def test_hand_placed_blocks():
+    """20 tokens, logical block 0 in physical block 3 and logical block 1 in
+    physical block 0, written element by element without any helper."""
+    D, Hkv = 4, 1
+    K = np.arange(20 * D, dtype=np.float32).reshape(20, D) / 50.0
+    V = (np.arange(20 * D, dtype=np.float32).reshape(20, D) % 7) - 3.0
+    kp = np.full((4, Hkv, BS, D), np.nan, np.float32)
+    vp = np.full((4, Hkv, BS, D), np.nan, np.float32)
+    for t in range(16):
+        kp[3, 0, t] = K[t]; vp[3, 0, t] = V[t]
+    for t in range(16, 20):
+        kp[0, 0, t - 16] = K[t]; vp[0, 0, t - 16] = V[t]
+    bt = np.array([[3, 0]], np.int32)
+    q = np.array([[[0.3, -0.2, 0.5, 0.1]]], np.float32)
+    out = oracle.paged_decode(q, "f32", kp, vp, "f32", bt, np.array([20], np.int32), 0.5)
+    s = 0.5 * (K.astype(np.float64) @ q[0, 0].astype(np.float64))
+    w = np.exp(s - s.max())
+    ref = (w[:, None] * V).sum(0) / w.sum()
+    np.testing.assert_allclose(out[0, 0], ref, rtol=0, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# closed forms
+# --------------------------------------------------------------------------
+
+def _tiny_pool(lens, Hq, Hkv, D, seed=0):
+    cfg = dict(B=len(lens), ctx=list(lens), Hq=Hq, Hkv=Hkv, D=D, dtype="f32", cache="f32",
+               pool=64, seed=seed, max_ctx=max(max(lens), 1))
+    return W.make_batch(cfg=cfg, device="cpu", seed=seed)
+
+
+def _run(b: W.Batch, q=None, scale=None, k_cache=None, v_cache=None):
+    return oracle.paged_decode(_bits(b.q if q is None else q), "f32",
+                               _bits(b.k_cache if k_cache is None else k_cache),
+                               _bits(b.v_cache if v_cache is None else v_cache), "f32",
+                               b.block_tables.numpy(), b.context_lens.numpy(),
+                               b.scale if scale is None else scale)
+
+
+def test_single_token_returns_v0_exactly():
+    b = _tiny_pool([1, 1, 1], 4, 2, 64)
+    out = _run(b)
+    for s in range(3):
+        blk = int(b.block_tables[s, 0])
+        for h in range(4):
+            v0 = b.v_cache[blk, h // 2, 0].to(torch.float64).numpy()
+            assert np.array_equal(out[s, h], v0)
+
+
+def test_identical_keys_give_mean_of_v():
+    b = _tiny_pool([37, 64], 4, 4, 64)
+    k = b.k_cache.clone()
+    blk0 = int(b.block_tables[0, 0])
+    k[:] = k[blk0:blk0 + 1, :, 0:1, :]  # every slot holds the same key row per head
+    out = _run(b, k_cache=k)
+    for s, n in enumerate([37, 64]):
+        rows = []
+        for t in range(n):
+            blk = int(b.block_tables[s, t // BS])
+            rows.append(b.v_cache[blk, :, t % BS].to(torch.float64))
+        mean = torch.stack(rows).mean(0).numpy()            # [Hkv][D]
+        np.testing.assert_allclose(out[s], mean, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("which", ["scale0", "q0"])
+def test_zero_logits_give_mean_of_v(which):
+    b = _tiny_pool([5, 50], 2, 2, 64)
+    if which == "scale0":
+        out = _run(b, scale=0.0)
+    else:
+        out = _run(b, q=torch.zeros_like(b.q))
+    for s, n in enumerate([5, 50]):
+        rows = [b.v_cache[int(b.block_tables[s, t // BS]), :, t % BS].to(torch.float64)
+                for t in range(n)]
+        np.testing.assert_allclose(out[s], torch.stack(rows).mean(0).numpy(), rtol=0,
+                                   atol=1e-12)
+
+
+def test_dominant_key_returns_its_value():
+    b = _tiny_pool([33], 1, 1, 64)
+    q = torch.zeros_like(b.q); q[0, 0, 0] = 1.0
+    k = b.k_cache.clone()
+    j = 21
+    blk, off = int(b.block_tables[0, j // BS]), j % BS
+    k[blk, 0, off, 0] = 1e4  # logit ~1250 above the rest: other weights < e^-1000
+    out = _run(b, q=q, k_cache=k)
+    np.testing.assert_array_equal(out[0, 0], b.v_cache[blk, 0, off].to(torch.float64).numpy())
+
+
+def test_zero_context_gives_zeros():
+    b = _tiny_pool([0, 3], 2, 2, 64)
+    out = _run(b)
+    assert np.array_equal(out[0], np.zeros_like(out[0]))
+    assert np.isfinite(out[1]).all()
+
+
+def test_unused_slots_never_read():
+    """Tails and unused blocks are NaN; block-table entries past the last block are -1."""
+    b = W.make_batch("tiny", device="cpu", poison=True)
+    assert torch.isnan(b.k_cache).any()
+    out = _run(b)
+    assert np.isfinite(out).all()
+
+
+def test_placement_permutation_invariance_bit_exact():
+    b = W.make_batch("tiny", device="cpu")
+    out = _run(b)
+    perm = np.random.default_rng(11).permutation(b.num_blocks)     # new position of block i
+    inv = np.argsort(perm)
+    k2 = b.k_cache[torch.from_numpy(inv)]                            # k2[perm[i]] = k[i]
+    v2 = b.v_cache[torch.from_numpy(inv)]
+    bt = b.block_tables.numpy().copy()
+    bt[bt >= 0] = perm[bt[bt >= 0]]
+    out2 = oracle.paged_decode(_bits(b.q), "f32", _bits(k2), _bits(v2), "f32", bt,
+                               b.context_lens.numpy(), b.scale)
+    assert np.array_equal(out, out2)
+
+
+# --------------------------------------------------------------------------
+# split partials + merge
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("P", [16, 32, 48, 64, 4096])
+def test_partials_merge_equals_full(P):
+    b = W.make_batch("tiny", device="cpu")
+    full = _run(b)
+    NP = -(-int(b.block_tables.shape[1]) * BS // P)
+    m, l, o = oracle.paged_partials(_bits(b.q), "f32", _bits(b.k_cache), _bits(b.v_cache), "f32",
+                                    b.block_tables.numpy(), b.context_lens.numpy(), b.scale, P,
+                                    NP)
+    merged = oracle.merge_partials(m, l, o)
+    np.testing.assert_allclose(merged, full, rtol=0, atol=1e-13)
+    # partitions that start past the context are empty
+    lens = b.context_lens.numpy()
+    for s in range(b.B):
+        for p in range(NP):
+            if p * P >= lens[s]:
+                assert l[s, :, p].max() == 0.0 and np.isneginf(m[s, :, p]).all()
+
+
+def test_merge_is_order_free_and_single_partition_is_identity():
+    g_ = np.random.default_rng(5)
+    m = g_.standard_normal((3, 2, 5)) * 4
+    l = g_.uniform(0.5, 9, (3, 2, 5))
+    o = g_.standard_normal((3, 2, 5, 8))
+    out = oracle.merge_partials(m, l, o)
+    p = g_.permutation(5)
+    np.testing.assert_allclose(oracle.merge_partials(m[..., p], l[..., p], o[..., p, :]), out,
+                               rtol=0, atol=1e-13)
+    np.testing.assert_allclose(oracle.merge_partials(m[..., :1], l[..., :1], o[..., :1, :]),
+                               o[..., 0, :], rtol=1e-15, atol=0)
+
+
+# --------------------------------------------------------------------------
+# INT8 quantizer
+# --------------------------------------------------------------------------
+
+def test_worked_absmax_example():
+    g = {k: float(v) for k, v in _golden("absmax_worked_example.txt")}
+    row = np.zeros(16, np.float32)
+    row[0] = g["absmax"]; row[1] = g["x"]; row[2] = -g["absmax"] / 2
+    codes, scales = oracle.quantize_rows(row[None], "f32")
+    assert codes[0, 1] == int(g["code"])
+    assert codes[0, 0] == 127
+    # the page's intermediate 3.97 to the two digits printed
+    assert abs(float(np.float32(g["x"]) / scales[0]) - g["x_over_absmax_times_127"]) < 5e-3
+    deq = float(codes[0, 1]) * float(scales[0])
+    assert abs(deq - g["dequant"]) < 5e-5
+    assert abs(abs(deq - float(np.float32(g["x"]))) - g["abs_error"]) < 5e-5
+    # the fp16-rounded inputs give the same code
+    r16 = row.astype(np.float16)
+    c16, _ = oracle.quantize_rows(r16.view(np.uint16)[None], "f16")
+    assert c16[0, 1] == int(g["code"])
+
+
+def test_ties_round_half_to_even():
+    rows = _golden("rne_ties.txt")
+    xs = np.array([float(r[0]) for r in rows], np.float32)
+    want = np.array([int(r[1]) for r in rows])
+    codes, scales = oracle.quantize_rows(xs[None], "f32")
+    assert scales[0] == 1.0
+    assert np.array_equal(codes[0].astype(int), want)
+
+
+def test_extremes_and_zero_row():
+    g_ = np.random.default_rng(2)
+    x = g_.standard_normal((64, 128)).astype(np.float32)
+    codes, scales = oracle.quantize_rows(x, "f32")
+    am = np.abs(x).argmax(1)
+    assert np.array_equal(codes[np.arange(64), am], np.sign(x[np.arange(64), am]) * 127)
+    assert codes.min() >= -127 and codes.max() <= 127
+    zc, zs = oracle.quantize_rows(np.zeros((2, 32), np.float32), "f32")
+    assert (zc == 0).all() and (zs == 0).all()
+
+
+def _rn32(v: Fraction) -> Fraction:
+    """Round a rational to the nearest IEEE binary32 (ties to even), normal range."""
+    if v == 0:
+        return Fraction(0)
+    sign = -1 if v < 0 else 1
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    assert -126 <= e <= 127
+    q = a / Fraction(2) ** (e - 23)          # in [2^23, 2^24)
+    n, r = divmod(q.numerator, q.denominator)
+    rem = Fraction(r, q.denominator)
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return sign * Fraction(n) * Fraction(2) ** (e - 23)
+
+
+def _rne_int(v: Fraction) -> int:
+    n = math.floor(v)
+    rem = v - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return n
+
+
+def _exact_quantize(row16: np.ndarray):
+    xs = [Fraction(float(x)) for x in row16.astype(np.float64)]
+    amax = max(abs(x) for x in xs)
+    s = _rn32(amax / 127)
+    return [max(-127, min(127, _rne_int(_rn32(x / s)))) for x in xs], s
+
+
+def test_quantizer_matches_exact_rational_arithmetic():
+    g_ = np.random.default_rng(123)
+    rows = g_.standard_normal((600, 128)).astype(np.float16)
+    codes, scales = oracle.quantize_rows(rows.view(np.uint16), "f16")
+    n_differs_from_mult_form = 0
+    for i in range(rows.shape[0]):
+        want, s = _exact_quantize(rows[i])
+        assert Fraction(float(scales[i])) == s
+        assert codes[i].tolist() == want, i
+        # count codes where x * (127 / amax) would have rounded differently
+        inv = _rn32(Fraction(127) / max(abs(Fraction(float(x))) for x in rows[i]))
+        alt = [max(-127, min(127, _rne_int(_rn32(Fraction(float(x)) * inv)))) for x in rows[i]]
+        n_differs_from_mult_form += sum(int(a != b) for a, b in zip(alt, want))
+    # the two forms on the pages really differ on this data, so this test
+    # tells a multiply-by-reciprocal quantizer apart from the divide form
+    assert n_differs_from_mult_form >= 1
+
+
+# --------------------------------------------------------------------------
+# cache write
+# --------------------------------------------------------------------------
+
+def test_cache_write_hand_built_slots():
+    NB, Hkv, D = 4, 2, 8
+    g_ = np.random.default_rng(3)
+    k = g_.standard_normal((3, Hkv, D)).astype(np.float32)
+    v = g_.standard_normal((3, Hkv, D)).astype(np.float32)
+    kc = np.full((NB, Hkv, BS, D), 7.0, np.float32)
+    vc = np.full((NB, Hkv, BS, D), -7.0, np.float32)
+    slots = np.array([5, -1, 37], np.int64)          # 37 = block 2, offset 5
+    oracle.kv_cache_write(k, v, kc, vc, slots, "f32", "f32")
+    expect_k = np.full_like(kc, 7.0); expect_v = np.full_like(vc, -7.0)
+    for h in range(Hkv):
+        expect_k[0, h, 5] = k[0, h]; expect_v[0, h, 5] = v[0, h]
+        expect_k[2, h, 5] = k[2, h]; expect_v[2, h, 5] = v[2, h]
+    assert np.array_equal(kc, expect_k) and np.array_equal(vc, expect_v)
+
+
+def test_cache_write_int8_uses_the_quantizer():
+    NB, Hkv, D = 3, 2, 16
+    g_ = np.random.default_rng(4)
+    k = g_.standard_normal((2, Hkv, D)).astype(np.float16)
+    v = g_.standard_normal((2, Hkv, D)).astype(np.float16)
+    kc = np.zeros((NB, Hkv, BS, D), np.int8); vc = np.zeros_like(kc)
+    ks = np.full((NB, Hkv, BS), np.nan, np.float32); vs = ks.copy()
+    slots = np.array([47, 0], np.int64)              # 47 = block 2, offset 15
+    oracle.kv_cache_write(k.view(np.uint16), v.view(np.uint16), kc, vc, slots, "f16", "i8",
+                          ks, vs)
+    ck, sk = oracle.quantize_rows(k.view(np.uint16), "f16")
+    cv, sv = oracle.quantize_rows(v.view(np.uint16), "f16")
+    for i, (blk, off) in enumerate([(2, 15), (0, 0)]):
+        assert np.array_equal(kc[blk, :, off], ck[i]) and np.array_equal(ks[blk, :, off], sk[i])
+        assert np.array_equal(vc[blk, :, off], cv[i]) and np.array_equal(vs[blk, :, off], sv[i])
+    assert np.isnan(ks).sum() == NB * Hkv * BS - 2 * Hkv
+
+
+def test_cache_write_rejects_slot_beyond_pool():
+    k = np.zeros((1, 1, 8), np.float32)
+    kc = np.zeros((2, 1, BS, 8), np.float32)
+    with pytest.raises(RuntimeError):
+        oracle.kv_cache_write(k, k, kc, kc.copy(), np.array([32], np.int64), "f32", "f32")
