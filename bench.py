@@ -1,0 +1,283 @@
+"""Decode-step benchmark for paged KV-cache attention on one MI355X.
+
+A step is one pass of the whole hot path over one synthetic batch: the
+slot-mapped cache write of every sequence's new token (INT8 quantize-on-write
+for the INT8 cache), then split-context paged decode attention with its
+in-kernel partition merge.  Inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line.  `value` is algorithmic bytes moved per step / wall time
+per step (GB/s); `roofline` reports the dominant kernel (paged decode) from HIP
+events on the stream it runs on; `cpu_baseline` times the CPU oracle on a
+bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--config llama7b]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+METRIC = "decode attention KV GB/s and % of HBM peak; KV-tokens/s at LLaMA-7B shape"
+WORKLOAD_NAMES = {
+    "tiny": "tiny-fp32-mha-decode",
+    "llama7b": "llama7b-mha-fp16-paged-decode",
+    "gqa": "gqa-32q8kv-bf16-paged-decode",
+    "long": "long-32k-fp16-split-decode",
+    "int8": "llama7b-mha-int8kv-paged-decode",
+}
+KERNEL_SOURCES = ["paged_decode.hip", "pkv_device.h", "pkv_internal.h", "pkv_api.hip"]
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_264_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", default="llama7b", choices=sorted(WORKLOAD_NAMES))
+    p.add_argument("--partition-size", type=int, default=None)
+    p.add_argument("--seed", type=int, default=None)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="target CPU time of the oracle baseline sample")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run only a plain 1 GiB device copy (for HBM counter calibration)")
+    return p.parse_args()
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
+
+
+def traffic_for(config: str, alg_bytes: int):
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, if
+    they were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None, None
+    with open(path) as f:
+        data = json.load(f)
+    rec = data.get(config)
+    if not rec or rec.get("kernel_sha") != kernel_sha():
+        return None, None
+    t = float(rec["fetch_bytes_per_launch"]) + float(rec["write_bytes_per_launch"])
+    return t, t / alg_bytes
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the decode path is built and measured on a "
+              f"single MI355X (got --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_264_amd as pkv
+    import workloads as W
+
+    torch.cuda.set_device(0)
+    cfg = W.CONFIGS[args.config]
+    batch = W.make_batch(args.config, device="cuda", seed=args.seed, poison=False)
+    if batch.k_src is not None and batch.k_src.shape[0] > 0:
+        pkv.kv_cache_write(batch.k_src, batch.v_src, batch.k_cache, batch.v_cache,
+                           batch.slot_src, batch.k_scale, batch.v_scale)
+    P = args.partition_size if args.partition_size is not None else cfg.get("partition_size", 0)
+    mbs = batch.block_tables.shape[1]
+    P_eff = P or pkv.default_partition_size(batch.B, batch.Hq, batch.Hkv, mbs)
+    out = torch.empty_like(batch.q)
+    NP = pkv.num_partitions(mbs, P_eff)
+    partials = (torch.empty((batch.B, batch.Hq, NP), dtype=torch.float32, device="cuda"),
+                torch.empty((batch.B, batch.Hq, NP), dtype=torch.float32, device="cuda"),
+                torch.empty((batch.B, batch.Hq, NP, batch.D), dtype=torch.float32, device="cuda"))
+    lens = batch.layout.context_lens
+    e_kv = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1}[cfg["cache"]]
+    e_q = {"f32": 4, "f16": 2, "bf16": 2}[cfg["dtype"]]
+    int8 = cfg["cache"] == "i8"
+    dec_bytes = W.algorithmic_bytes(lens, batch.Hq, batch.Hkv, batch.D, e_kv, e_q, int8)
+    n_new = int((batch.slot_new >= 0).sum())
+    # cache write: read new K/V rows, write them (codes + scales for INT8) and the slots
+    write_bytes = n_new * batch.Hkv * 2 * (batch.D * e_q + batch.D * e_kv + (4 if int8 else 0)) \
+        + n_new * 8
+    step_bytes = dec_bytes + write_bytes
+    kv_tokens = int(lens.sum())
+    stream = torch.cuda.current_stream()
+
+    # The step is what pkv_paged_attn_decode enqueues, called phase by phase so
+    # that HIP events bracket the decode kernel alone: cache write, phase 1
+    # (split-context decode; single-partition sequences finish here), phase 2
+    # (merge of the longer ones).
+    def step(ev0=None, ev1=None):
+        pkv.kv_cache_write(batch.k_new, batch.v_new, batch.k_cache, batch.v_cache,
+                           batch.slot_new, batch.k_scale, batch.v_scale)
+        if ev0 is not None:
+            ev0.record(stream)
+        pkv.paged_attn_decode_partials(batch.q, batch.k_cache, batch.v_cache, batch.block_tables,
+                                       batch.context_lens, batch.scale, P_eff,
+                                       k_scale=batch.k_scale, v_scale=batch.v_scale, out=out,
+                                       partials=partials)
+        if ev1 is not None:
+            ev1.record(stream)
+        if NP > 1:
+            pkv.paged_attn_reduce(*partials, batch.context_lens, P_eff, out=out,
+                                  skip_single_partition=True)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        step(e0, e1)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    assert torch.isfinite(out.float()).all()
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    dec_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    dec_avg_ms = float(np.mean(dec_ms))
+    achieved = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    traffic, traffic_ratio = traffic_for(args.config, dec_bytes)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg["cache"] if cfg["cache"] == "i8" else cfg["dtype"],
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD_NAMES[args.config],
+            "num_seqs": batch.B, "num_q_heads": batch.Hq, "num_kv_heads": batch.Hkv,
+            "head_dim": batch.D, "block_size": W.BLOCK_SIZE,
+            "context_lens": (f"U[{cfg['ctx'][0]},{cfg['ctx'][1]}]" if isinstance(cfg["ctx"], tuple)
+                             else cfg["ctx"] if len(set(cfg["ctx"])) > 1 else
+                             f"{cfg['ctx'][0]} x {len(cfg['ctx'])}"),
+            "sum_context_tokens": kv_tokens, "q_dtype": cfg["dtype"], "kv_dtype": cfg["cache"],
+            "partition_size": P_eff, "seed": batch.seed, "parallelism": "single-gpu",
+        },
+        "kv_tokens_per_s": round(kv_tokens / (ms_per_step * 1e-3), 1),
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "decode_kernel_us": round(dec_avg_ms * 1e3, 2),
+        "decode_alg_bytes": dec_bytes,
+        "step_alg_bytes": step_bytes,
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None if traffic is None else int(traffic),
+            "traffic_unit": "bytes/launch",
+            "traffic_over_alg": None if traffic_ratio is None else round(traffic_ratio, 4),
+            "kernel": "paged_decode_kernel", "kernel_sha": kernel_sha(),
+            "launches_per_step": {"kv_cache_write_kernel": 1, "paged_decode_kernel": 1,
+                                  "paged_reduce_kernel": 1 if NP > 1 else 0},
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = run_cpu_baseline(batch, args.config, args.cpu_seconds,
+                                                  e_kv, e_q, int8)
+    print(json.dumps(result), flush=True)
+
+
+def run_cpu_baseline(batch, cfg_name, target_s, e_kv, e_q, int8):
+    """Time the CPU oracle (as it stands) on the first sequences of the same
+    batch, sized to about `target_s` seconds, and express it in the metric's
+    unit (algorithmic GB/s)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads as W
+
+    lens = batch.layout.context_lens
+    threads = oracle.num_threads(len(os.sched_getaffinity(0)))
+
+    def view_for(n_seq):
+        seqs = np.arange(n_seq)
+        blocks = np.concatenate([batch.layout.block_tables[s, :W.blocks_needed(lens[s])]
+                                 for s in seqs]).astype(np.int64)
+        remap = np.full(batch.num_blocks, -1, np.int64)
+        remap[blocks] = np.arange(len(blocks))
+        bt = batch.layout.block_tables[:n_seq].copy()
+        bt[bt >= 0] = remap[bt[bt >= 0]]
+        idx = torch.from_numpy(blocks).cuda()
+
+        def h(t):
+            t = t.contiguous().cpu()
+            if t.dtype in (torch.float16, torch.bfloat16):
+                return t.view(torch.int16).numpy().view(np.uint16)
+            return t.numpy()
+
+        dt = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16",
+              torch.int8: "i8"}
+        kw = {}
+        if int8:
+            kw = dict(k_scale=h(batch.k_scale[idx]), v_scale=h(batch.v_scale[idx]))
+        return dict(q=h(batch.q[:n_seq]), q_dtype=dt[batch.q.dtype], k_cache=h(batch.k_cache[idx]),
+                    v_cache=h(batch.v_cache[idx]), cache_dtype=dt[batch.k_cache.dtype],
+                    block_tables=bt.astype(np.int32), context_lens=lens[:n_seq].astype(np.int32),
+                    scale=batch.scale, **kw)
+
+    # probe on one sequence, then size the sample
+    v1 = view_for(1)
+    t = time.perf_counter()
+    oracle.paged_decode(**v1)
+    t_one = max(time.perf_counter() - t, 1e-4)
+    per_tok = t_one / max(int(lens[0]), 1)
+    n_seq = 1
+    while n_seq < batch.B and per_tok * lens[:n_seq + 1].sum() < target_s:
+        n_seq += 1
+    v = view_for(n_seq)
+    t = time.perf_counter()
+    oracle.paged_decode(**v)
+    t_s = time.perf_counter() - t
+    sub = lens[:n_seq]
+    alg = W.algorithmic_bytes(sub, batch.Hq, batch.Hkv, batch.D, e_kv, e_q, int8)
+    return {
+        "value": round(alg / t_s / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "sample": f"first {n_seq} of {batch.B} sequences (all {batch.Hq} q heads, "
+                  f"{int(sub.sum())} context tokens), one fp64 oracle pass of {t_s:.2f} s",
+        "kv_tokens_per_s": round(float(sub.sum()) / t_s, 1),
+        "seconds": round(t_s, 3),
+    }
+
+
+if __name__ == "__main__":
+    main()

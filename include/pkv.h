@@ -1,0 +1,208 @@
+/*
+ * pkv.h -- C ABI of the paged KV-cache decode-attention library (libpkv.so)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (sources are the four web pages on paged KV
+ * caches; each entry point names the passage it implements):
+ *
+ *  - The KV cache of every sequence is cut into fixed-size blocks of
+ *    `block_size` = 16 tokens that live anywhere in a pre-allocated pool; a
+ *    per-sequence block table maps logical block j to a physical block id
+ *    ("Efficient AI Lecture 13" notes, section "PagedAttention", its four
+ *    numbered steps; docs.lazyllm.ai lesson 4, section 4.2).
+ *  - Decode attention for one new query token per sequence:
+ *        out[b][h] = softmax(scale * q[b][h] . K^T) V
+ *    over the context_lens[b] cached tokens of the kv head that q head h
+ *    reads; paging leaves the equation unchanged (lazyllm section 4.2, the
+ *    "attention invariance" equation with Q of shape 1 x d).
+ *  - Long contexts are split into partitions whose partial softmax results
+ *    (max score, sum of exponentials, normalized weighted sum) are merged
+ *    exactly; this is the running-max / running-sum rearrangement of online
+ *    softmax (caojiahao2.github.io, section 3.2; juejin "LLM Engineer's
+ *    Handbook", the FlashAttention-2 passage of "optimized attention").
+ *  - Optional INT8 KV cache: symmetric quantization with one fp32 scale per
+ *    (token slot, kv head), s = max|x| / 127, code = round(x / s)
+ *    (lazyllm section 5.3; juejin absmax passage with its worked example).
+ *
+ * Tensor layouts (row-major, all device memory unless stated):
+ *    q, out          [num_seqs][num_q_heads][head_dim]             q_dtype
+ *    k_cache,v_cache [num_blocks][num_kv_heads][block_size][head_dim] cache_dtype
+ *    k_scale,v_scale [num_blocks][num_kv_heads][block_size]        float (INT8 only)
+ *    block_tables    [num_seqs][max_blocks_per_seq]                int32
+ *    context_lens    [num_seqs]                                    int32
+ *    slot_mapping    [num_tokens]                                  int64
+ *  A slot is physical_block * block_size + offset.  q head h reads kv head
+ *  h / (num_q_heads / num_kv_heads).
+ *
+ * Conventions shared by every entry point:
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
+ *    legacy default stream).  No entry point allocates, frees or
+ *    synchronizes.  All pointers are borrowed until the enqueued work
+ *    completes; the caller owns every buffer.
+ *  - Argument errors that the host can see are reported before anything is
+ *    enqueued: the call returns a non-zero pkv_status and pkv_last_error()
+ *    describes it.  A failed kernel launch returns PKV_ERR_HIP.
+ *  - Device-resident data cannot be checked on the host without a
+ *    synchronization, so the kernels defend themselves instead:
+ *    context_lens[b] is clamped to [0, max_blocks_per_seq * block_size],
+ *    block ids outside [0, num_blocks) contribute nothing, and slots outside
+ *    the pool are skipped.  Such inputs are caller errors and their results
+ *    are unspecified, but no access leaves the buffers described here.
+ *  - Supported: block_size 16; head_dim 64, 128 or 256; (q_dtype,
+ *    cache_dtype) in {(F32,F32), (F16,F16), (BF16,BF16), (F16,I8),
+ *    (BF16,I8)}; num_q_heads a multiple of num_kv_heads.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PKV_OK = 0,
+    PKV_ERR_NULL = 1,        /* a required pointer is NULL                      */
+    PKV_ERR_SHAPE = 2,       /* a size is negative, zero where it must not be,
+                                or inconsistent with another                     */
+    PKV_ERR_DTYPE = 3,       /* unsupported dtype or dtype pairing               */
+    PKV_ERR_UNSUPPORTED = 4, /* head_dim / block_size outside the support set    */
+    PKV_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required       */
+    PKV_ERR_HIP = 6          /* the HIP runtime reported an error                */
+} pkv_status;
+
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_I8 = 3 } pkv_dtype;
+
+/*
+ * Slot-mapped cache append ("when a new token is generated only its keys and
+ * values are computed and added to the cache": juejin "LLM Engineer's
+ * Handbook", section "KV cache"), with optional INT8 quantize-on-write
+ * (lazyllm lesson 4, section 5.3; juejin absmax passage).
+ *
+ *  k, v          [num_tokens][num_kv_heads][head_dim], src_dtype (F32|F16|BF16)
+ *  k_cache/v_cache  pool (see layout above), cache_dtype == src_dtype or I8
+ *  k_scale/v_scale  required iff cache_dtype == I8, else ignored (may be NULL)
+ *  slot_mapping  token i goes to block slot/16, offset slot%16 for every kv
+ *                head; slot < 0 skips the token.  Slots must be distinct.
+ *
+ * INT8 rows: amax = max_d |x_d|; s = amax / 127 (IEEE single division);
+ * code_d = clamp(round_half_even(x_d / s), -127, 127); amax == 0 stores s = 0
+ * and zero codes.  Bytes of other slots are not touched.
+ */
+pkv_status pkv_kv_cache_write(const void* k, const void* v, void* k_cache, void* v_cache,
+                              float* k_scale, float* v_scale, const int64_t* slot_mapping,
+                              int64_t num_tokens, int num_kv_heads, int head_dim, int block_size,
+                              int64_t num_blocks, pkv_dtype src_dtype, pkv_dtype cache_dtype,
+                              hipStream_t stream);
+
+/*
+ * Partition size (tokens, a multiple of 16) that pkv_paged_attn_decode uses
+ * when it is passed partition_size == 0.  Returns 0 for invalid arguments.
+ */
+int pkv_default_partition_size(int num_seqs, int num_q_heads, int num_kv_heads,
+                               int max_blocks_per_seq);
+
+/*
+ * Bytes of workspace pkv_paged_attn_decode needs for these sizes
+ * (partition_size 0 means the default above).  Returns 0 for invalid sizes.
+ * The workspace holds the fp32 partial results of sequences longer than one
+ * partition; it needs no initialization and its contents after a call are
+ * unspecified.  Two decode calls that may run at the same time must not share
+ * a workspace.
+ */
+size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                 int max_blocks_per_seq, int partition_size);
+
+/*
+ * Single-query decode attention over the paged cache (lazyllm lesson 4,
+ * section 4.2 equation; "Efficient AI Lecture 13", "PagedAttention" steps),
+ * split over context partitions of `partition_size` tokens whose partial
+ * softmax results are merged exactly (online softmax: caojiahao2 section 3.2).
+ * Enqueues pkv_paged_attn_decode_partials with `out` set (sequences that fit
+ * in one partition are finished there) followed by pkv_paged_attn_reduce with
+ * skip_single_partition = 1, using the workspace for the partials.
+ *
+ *  out               [num_seqs][num_q_heads][head_dim], q_dtype, written
+ *  q                 [num_seqs][num_q_heads][head_dim], q_dtype
+ *  k_scale, v_scale  required iff cache_dtype == I8
+ *  scale             the softmax scale, normally 1/sqrt(head_dim)
+ *  partition_size    0 (library choice) or a positive multiple of 16
+ *  workspace         >= pkv_decode_workspace_size(...) bytes, 256-byte aligned
+ *
+ * context_lens[b] == 0 writes zeros for sequence b.  Only block-table entries
+ * j < ceil(context_lens[b] / 16) are read, and only slots of those blocks that
+ * lie below context_lens[b]; everything else in the pool may hold any bytes,
+ * NaN included.  Outputs are rounded to q_dtype with round-to-nearest-even.
+ * The result does not depend on where blocks sit in the pool (bit for bit),
+ * and repeated calls give bit-identical results.
+ */
+pkv_status pkv_paged_attn_decode(void* out, const void* q, const void* k_cache,
+                                 const void* v_cache, const float* k_scale, const float* v_scale,
+                                 const int32_t* block_tables, int max_blocks_per_seq,
+                                 const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                 int num_kv_heads, int head_dim, int block_size,
+                                 int64_t num_blocks, float scale, int partition_size,
+                                 void* workspace, size_t workspace_bytes, pkv_dtype q_dtype,
+                                 pkv_dtype cache_dtype, hipStream_t stream);
+
+/*
+ * Phase 1 of the split-context decode: per-partition partial results (for a
+ * caller that merges them itself, e.g. partitions computed on several
+ * devices, or that times the phases apart).  For partition p of sequence b
+ * (tokens [p*P, min((p+1)*P, N_b)), P = partition_size, N_b =
+ * context_lens[b]) and q head h:
+ *    m_part[b][h][p]    = max_t s_t,  s_t = scale * (q . k_t)  (natural units)
+ *    l_part[b][h][p]    = sum_t exp(s_t - m)
+ *    o_part[b][h][p][:] = sum_t exp(s_t - m) v_t / l
+ * Arrays are fp32 with num_partitions entries per (b, h); num_partitions must
+ * be >= ceil(max_blocks_per_seq * 16 / P).  Entries of partitions that start
+ * at or past N_b are not written.  partition_size must be given (no default).
+ * out == NULL: every non-empty partition writes its partial.  out != NULL
+ * ([num_seqs][num_q_heads][head_dim], q_dtype): sequences with
+ * N_b <= partition_size get their final attention output in `out` (zeros for
+ * N_b == 0) and write no partial.
+ */
+pkv_status pkv_paged_attn_decode_partials(void* out, float* m_part, float* l_part, float* o_part,
+                                          const void* q, const void* k_cache, const void* v_cache,
+                                          const float* k_scale, const float* v_scale,
+                                          const int32_t* block_tables, int max_blocks_per_seq,
+                                          const int32_t* context_lens, int num_seqs,
+                                          int num_q_heads, int num_kv_heads, int head_dim,
+                                          int block_size, int64_t num_blocks, float scale,
+                                          int partition_size, int num_partitions,
+                                          pkv_dtype q_dtype, pkv_dtype cache_dtype,
+                                          hipStream_t stream);
+
+/*
+ * Phase 2: exact merge of partials laid out as written by
+ * pkv_paged_attn_decode_partials (derived from the running-max / running-sum
+ * rule of online softmax, caojiahao2 section 3.2):
+ *    M = max_p m_p;  w_p = l_p exp(m_p - M);  out = sum_p w_p o_p / sum_p w_p
+ * over the ceil(N_b / partition_size) partitions of sequence b.  N_b == 0
+ * writes zeros.  skip_single_partition != 0 leaves `out` of sequences with at
+ * most one partition untouched (phase 1 with an output pointer finished
+ * them).  out is [num_seqs][num_q_heads][head_dim] in out_dtype (F32|F16|BF16),
+ * rounded to nearest even.
+ */
+pkv_status pkv_paged_attn_reduce(void* out, const float* m_part, const float* l_part,
+                                 const float* o_part, const int32_t* context_lens, int num_seqs,
+                                 int num_q_heads, int head_dim, int partition_size,
+                                 int num_partitions, int skip_single_partition,
+                                 pkv_dtype out_dtype, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* pkv_status_string(pkv_status status);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if
+ * none).  The pointer stays valid until the thread's next pkv_* call. */
+const char* pkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,258 @@
+"""Python binding of libpkv (paged KV-cache decode attention for MI355X).
+
+Thin ctypes layer over the C ABI declared in ``include/pkv.h``: it checks
+torch metadata (device, dtype, shape, contiguity), passes raw device pointers
+and the current HIP stream, and raises ``RuntimeError`` on a non-OK status.
+Every step of the computation runs in the library's HIP kernels; there is no
+fallback.  Function names are the C entry points without their ``pkv_``
+prefix.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "kv_cache_write", "paged_attn_decode", "paged_attn_decode_partials", "paged_attn_reduce",
+    "decode_workspace_size", "default_partition_size", "num_partitions",
+    "library_path", "PkvError", "BLOCK_SIZE",
+]
+
+BLOCK_SIZE = 16
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libpkv.so")
+
+F32, F16, BF16, I8 = 0, 1, 2, 3
+_DTYPE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16, torch.int8: I8}
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"pkv status {status}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"libpkv.so not found at {_LIB_PATH}: the HIP library must be built first "
+            "(python -m paged_kv_cache_264_amd.build, or __graft_entry__.build())")
+    L = ctypes.CDLL(_LIB_PATH)
+    P, I, I64, F, SZ = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
+                        ctypes.c_size_t)
+    L.pkv_kv_cache_write.argtypes = [P, P, P, P, P, P, P, I64, I, I, I, I64, I, I, P]
+    L.pkv_kv_cache_write.restype = I
+    L.pkv_default_partition_size.argtypes = [I, I, I, I]
+    L.pkv_default_partition_size.restype = I
+    L.pkv_decode_workspace_size.argtypes = [I, I, I, I, I, I]
+    L.pkv_decode_workspace_size.restype = SZ
+    L.pkv_paged_attn_decode.argtypes = [P, P, P, P, P, P, P, I, P, I, I, I, I, I, I64, F, I, P,
+                                        SZ, I, I, P]
+    L.pkv_paged_attn_decode.restype = I
+    L.pkv_paged_attn_decode_partials.argtypes = [P, P, P, P, P, P, P, P, P, P, I, P, I, I, I, I,
+                                                 I, I64, F, I, I, I, I, P]
+    L.pkv_paged_attn_decode_partials.restype = I
+    L.pkv_paged_attn_reduce.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, P]
+    L.pkv_paged_attn_reduce.restype = I
+    L.pkv_status_string.argtypes = [I]
+    L.pkv_status_string.restype = ctypes.c_char_p
+    L.pkv_last_error.argtypes = []
+    L.pkv_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check_status(rc: int):
+    if rc != 0:
+        L = _load()
+        raise PkvError(rc, f"{L.pkv_status_string(rc).decode()}: {L.pkv_last_error().decode()}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims (got {tuple(t.shape)})")
+    return t
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _code(dtype: torch.dtype, name: str) -> int:
+    if dtype not in _DTYPE:
+        raise TypeError(f"{name}: unsupported dtype {dtype}")
+    return _DTYPE[dtype]
+
+
+def default_partition_size(num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq) -> int:
+    return _load().pkv_default_partition_size(num_seqs, num_q_heads, num_kv_heads,
+                                              max_blocks_per_seq)
+
+
+def num_partitions(max_blocks_per_seq: int, partition_size: int) -> int:
+    return -(-max_blocks_per_seq * BLOCK_SIZE // partition_size)
+
+
+def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                          partition_size=0) -> int:
+    return _load().pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                             max_blocks_per_seq, partition_size)
+
+
+_ws_cache: dict = {}
+
+
+def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
+    """A workspace of at least nbytes on `device`, reused by later calls on
+    the same device (calls on one stream run one after another)."""
+    key = (device.type, device.index)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def kv_cache_write(k, v, k_cache, v_cache, slot_mapping, k_scale=None, v_scale=None):
+    """Write new tokens' K/V rows ([T][Hkv][D]) into the pool at their slots;
+    INT8 caches quantize on write (scales [NB][Hkv][16] float32)."""
+    _dev(k, "k", ndim=3)
+    _dev(v, "v", dtype=k.dtype, ndim=3)
+    _dev(k_cache, "k_cache", ndim=4)
+    _dev(v_cache, "v_cache", dtype=k_cache.dtype, ndim=4)
+    _dev(slot_mapping, "slot_mapping", dtype=torch.int64, ndim=1)
+    T, Hkv, D = k.shape
+    NB, Hkv2, bs, D2 = k_cache.shape
+    if v.shape != k.shape or v_cache.shape != k_cache.shape or (Hkv2, D2) != (Hkv, D):
+        raise ValueError("k/v and cache shapes disagree")
+    if slot_mapping.shape[0] != T:
+        raise ValueError("slot_mapping must have one entry per token")
+    if k_cache.dtype == torch.int8:
+        _dev(k_scale, "k_scale", dtype=torch.float32, ndim=3)
+        _dev(v_scale, "v_scale", dtype=torch.float32, ndim=3)
+        if tuple(k_scale.shape) != (NB, Hkv, bs) or v_scale.shape != k_scale.shape:
+            raise ValueError("scale arrays must be [num_blocks][num_kv_heads][16]")
+    rc = _load().pkv_kv_cache_write(_ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                    _ptr(v_scale), _ptr(slot_mapping), T, Hkv, D, bs, NB,
+                                    _code(k.dtype, "k"), _code(k_cache.dtype, "k_cache"),
+                                    _stream(k))
+    _check_status(rc)
+
+
+def _decode_common(q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale):
+    _dev(q, "q", ndim=3)
+    _dev(k_cache, "k_cache", ndim=4)
+    _dev(v_cache, "v_cache", dtype=k_cache.dtype, ndim=4)
+    _dev(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _dev(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    B, Hq, D = q.shape
+    NB, Hkv, bs, D2 = k_cache.shape
+    if D2 != D or v_cache.shape != k_cache.shape:
+        raise ValueError("q / cache shapes disagree")
+    if block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_tables and context_lens need one row per sequence")
+    if k_cache.dtype == torch.int8:
+        _dev(k_scale, "k_scale", dtype=torch.float32, ndim=3)
+        _dev(v_scale, "v_scale", dtype=torch.float32, ndim=3)
+    return B, Hq, D, NB, Hkv, bs
+
+
+def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None,
+                      k_scale=None, v_scale=None, partition_size=0, workspace=None):
+    """softmax(scale * q K^T) V per sequence and q head over the paged cache."""
+    B, Hq, D, NB, Hkv, bs = _decode_common(q, k_cache, v_cache, block_tables, context_lens,
+                                           k_scale, v_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", dtype=q.dtype, ndim=3)
+    mbs = block_tables.shape[1]
+    need = decode_workspace_size(B, Hq, Hkv, D, mbs, partition_size)
+    if workspace is None:
+        workspace = _workspace(q.device, need)
+    else:
+        _dev(workspace, "workspace")
+    rc = _load().pkv_paged_attn_decode(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_tables), mbs, _ptr(context_lens), B, Hq, Hkv, D, bs, NB, float(scale),
+        int(partition_size), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _code(q.dtype, "q"), _code(k_cache.dtype, "k_cache"), _stream(q))
+    _check_status(rc)
+    return out
+
+
+def paged_attn_decode_partials(q, k_cache, v_cache, block_tables, context_lens, scale,
+                               partition_size, num_partitions_=None, k_scale=None, v_scale=None,
+                               out=None, partials=None):
+    """Phase 1 of the split decode: per-partition (m, l, o) fp32 partials
+    m, l [B][Hq][NP] and o [B][Hq][NP][D].  With `out` given, sequences that fit
+    in one partition are finished into `out` and write no partial.  Entries
+    that are not written keep their previous contents (NaN when allocated
+    here).  Returns (m, l, o)."""
+    B, Hq, D, NB, Hkv, bs = _decode_common(q, k_cache, v_cache, block_tables, context_lens,
+                                           k_scale, v_scale)
+    mbs = block_tables.shape[1]
+    NP = num_partitions_ or num_partitions(mbs, partition_size)
+    if partials is None:
+        m = torch.full((B, Hq, NP), float("nan"), dtype=torch.float32, device=q.device)
+        l = torch.full_like(m, float("nan"))
+        o = torch.full((B, Hq, NP, D), float("nan"), dtype=torch.float32, device=q.device)
+    else:
+        m, l, o = partials
+        _dev(m, "m_part", dtype=torch.float32, ndim=3)
+        _dev(l, "l_part", dtype=torch.float32, ndim=3)
+        _dev(o, "o_part", dtype=torch.float32, ndim=4)
+        if tuple(m.shape) != (B, Hq, NP) or l.shape != m.shape or tuple(o.shape) != (B, Hq, NP, D):
+            raise ValueError("partials must be [B][Hq][NP] and [B][Hq][NP][D]")
+    if out is not None:
+        _dev(out, "out", dtype=q.dtype, ndim=3)
+    rc = _load().pkv_paged_attn_decode_partials(
+        _ptr(out), _ptr(m), _ptr(l), _ptr(o), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+        _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), mbs, _ptr(context_lens), B, Hq, Hkv, D,
+        bs, NB, float(scale), int(partition_size), NP, _code(q.dtype, "q"),
+        _code(k_cache.dtype, "k_cache"), _stream(q))
+    _check_status(rc)
+    return m, l, o
+
+
+def paged_attn_reduce(m_part, l_part, o_part, context_lens, partition_size, out=None,
+                      out_dtype=torch.float32, skip_single_partition=False):
+    """Phase 2: merge partials into out [B][Hq][D].  skip_single_partition
+    leaves sequences with at most one partition untouched."""
+    _dev(m_part, "m_part", dtype=torch.float32, ndim=3)
+    _dev(l_part, "l_part", dtype=torch.float32, ndim=3)
+    _dev(o_part, "o_part", dtype=torch.float32, ndim=4)
+    _dev(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    B, Hq, NP, D = o_part.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype, device=o_part.device)
+    _dev(out, "out", ndim=3)
+    rc = _load().pkv_paged_attn_reduce(_ptr(out), _ptr(m_part), _ptr(l_part), _ptr(o_part),
+                                       _ptr(context_lens), B, Hq, D, int(partition_size), NP,
+                                       1 if skip_single_partition else 0,
+                                       _code(out.dtype, "out"), _stream(o_part))
+    _check_status(rc)
+    return out

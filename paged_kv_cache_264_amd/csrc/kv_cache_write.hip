@@ -1,0 +1,157 @@
+// Slot-mapped cache append with optional INT8 quantize-on-write.
+//
+// Each new token's K and V rows are written into the pool at the slot the
+// block manager assigned (block = slot / 16, offset = slot % 16), for every kv
+// head; only the new token's keys and values are written (juejin "LLM
+// Engineer's Handbook", section "KV cache").  In INT8 mode every (token, kv
+// head) row gets one fp32 scale s = max|x| / 127 and codes
+// clamp(round_half_even(x / s), -127, 127) (docs.lazyllm.ai lesson 4,
+// section 5.3; the juejin absmax passage and its half-to-even rounding).
+//
+// Layout on gfx950: a row of D elements is handled by D/8 consecutive lanes,
+// 8 elements each (one 16-byte load for 16-bit sources); the INT8 absolute
+// maximum is a DPP max inside the row.  The division is IEEE single precision
+// (correctly rounded) and rounding uses v_rndne, so codes are bit-exact.
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <Elem SE> struct Src8 {
+    float x[8];
+    uint4 raw[ElemInfo<SE>::bytes == 4 ? 2 : 1];
+    __device__ __forceinline__ void load(const void* base, size_t elem_off) {
+        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const char*>(base) +
+                                                        elem_off * ElemInfo<SE>::bytes);
+        raw[0] = p[0];
+        if constexpr (ElemInfo<SE>::bytes == 4) raw[1] = p[1];
+    }
+    __device__ __forceinline__ void widen() {
+        if constexpr (SE == Elem::F32) {
+            const uint32_t w[8] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w,
+                                   raw[1].x, raw[1].y, raw[1].z, raw[1].w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = __builtin_bit_cast(float, w[i]);
+        } else {
+            const uint32_t w[4] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[2 * i] = SE == Elem::F16 ? lo_h(w[i]) : lo_bf(w[i]);
+                x[2 * i + 1] = SE == Elem::F16 ? hi_h(w[i]) : hi_bf(w[i]);
+            }
+        }
+    }
+    __device__ __forceinline__ void store_raw(void* base, size_t elem_off) const {
+        uint4* p = reinterpret_cast<uint4*>(static_cast<char*>(base) +
+                                            elem_off * ElemInfo<SE>::bytes);
+        p[0] = raw[0];
+        if constexpr (ElemInfo<SE>::bytes == 4) p[1] = raw[1];
+    }
+};
+
+// Quantize 8 elements of a row whose absolute maximum is `amax`; returns the
+// packed codes and the scale.
+template <int LPR>
+__device__ __forceinline__ uint2 quantize8(const float (&x)[8], float& scale_out) {
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+    amax = group_max<LPR>(amax);
+    uint32_t packed[2] = {0u, 0u};
+    float s = 0.f;
+    if (amax > 0.f) {
+        s = amax / 127.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float c = __builtin_rintf(x[i] / s);
+            c = fminf(fmaxf(c, -127.0f), 127.0f);
+            packed[i / 4] |= ((uint32_t)(int32_t)c & 0xffu) << (8 * (i % 4));
+        }
+    }
+    scale_out = s;
+    return make_uint2(packed[0], packed[1]);
+}
+
+template <Elem SE, Elem CE, int D>
+__global__ __launch_bounds__(kThreads) void kv_cache_write_kernel(CacheWriteArgs a) {
+    constexpr int LPR = D / 8;  // lanes per row
+    constexpr int RPB = kThreads / LPR;
+    const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+    const int j = threadIdx.x % LPR;
+    const int64_t n_rows = a.num_tokens * a.num_kv_heads;
+    if (row >= n_rows) return;  // whole rows leave together (rows are lane-aligned)
+    const int64_t tok = row / a.num_kv_heads;
+    const int h = (int)(row % a.num_kv_heads);
+    const int64_t slot = a.slot_mapping[tok];
+    if (slot < 0 || slot >= a.num_blocks * kBlockSize) return;
+    const int64_t blk = slot / kBlockSize, off = slot % kBlockSize;
+    const size_t src = (size_t)row * D + (size_t)j * 8;
+    const size_t dst_row = ((size_t)blk * a.num_kv_heads + h) * kBlockSize + (size_t)off;
+    const size_t dst = dst_row * D + (size_t)j * 8;
+
+    Src8<SE> k, v;
+    k.load(a.k, src);
+    v.load(a.v, src);
+    if constexpr (CE == Elem::I8) {
+        k.widen();
+        v.widen();
+        float ks, vs;
+        const uint2 kc = quantize8<LPR>(k.x, ks);
+        const uint2 vc = quantize8<LPR>(v.x, vs);
+        *reinterpret_cast<uint2*>(static_cast<int8_t*>(a.k_cache) + dst) = kc;
+        *reinterpret_cast<uint2*>(static_cast<int8_t*>(a.v_cache) + dst) = vc;
+        if (j == 0) {
+            a.k_scale[dst_row] = ks;
+            a.v_scale[dst_row] = vs;
+        }
+    } else {
+        k.store_raw(a.k_cache, dst);
+        v.store_raw(a.v_cache, dst);
+    }
+}
+
+template <Elem SE, Elem CE>
+hipError_t launch_d(const CacheWriteArgs& a, int d, hipStream_t s) {
+    const int64_t n_rows = a.num_tokens * a.num_kv_heads;
+    if (n_rows == 0) return hipSuccess;
+    const int rpb = kThreads / (d / 8);
+    const int64_t n_wg = (n_rows + rpb - 1) / rpb;
+    if (n_wg > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)n_wg), block(kThreads);
+    switch (d) {
+    case 64: hipLaunchKernelGGL((kv_cache_write_kernel<SE, CE, 64>), grid, block, 0, s, a); break;
+    case 128: hipLaunchKernelGGL((kv_cache_write_kernel<SE, CE, 128>), grid, block, 0, s, a); break;
+    case 256: hipLaunchKernelGGL((kv_cache_write_kernel<SE, CE, 256>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_kv_cache_write(const CacheWriteArgs& a, int src_dtype, int cache_dtype,
+                                 int head_dim, hipStream_t stream) {
+    const Elem se = static_cast<Elem>(src_dtype), ce = static_cast<Elem>(cache_dtype);
+    if (ce == se) {
+        switch (se) {
+        case Elem::F32: return launch_d<Elem::F32, Elem::F32>(a, head_dim, stream);
+        case Elem::F16: return launch_d<Elem::F16, Elem::F16>(a, head_dim, stream);
+        case Elem::BF16: return launch_d<Elem::BF16, Elem::BF16>(a, head_dim, stream);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    if (ce == Elem::I8) {
+        switch (se) {
+        case Elem::F32: return launch_d<Elem::F32, Elem::I8>(a, head_dim, stream);
+        case Elem::F16: return launch_d<Elem::F16, Elem::I8>(a, head_dim, stream);
+        case Elem::BF16: return launch_d<Elem::BF16, Elem::I8>(a, head_dim, stream);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace pkv

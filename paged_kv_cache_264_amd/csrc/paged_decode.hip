@@ -1,0 +1,473 @@
+// Split-context single-query decode attention over a paged KV cache, for
+// gfx950 (CDNA4, wave64).
+//
+// What is computed: for every sequence b and q head h,
+//     out[b][h] = softmax(scale * q[b][h] . K^T) V
+// over the sequence's cached tokens, which are fetched through its block table
+// from 16-token blocks anywhere in the pool (docs.lazyllm.ai lesson 4,
+// section 4.2: page table, global block pool, unchanged attention equation;
+// "Efficient AI Lecture 13" notes, "PagedAttention" steps 1-4).  The context is
+// cut into partitions of P tokens; each work-group reduces one partition with
+// an online softmax (running max m, running sum l: caojiahao2.github.io
+// section 3.2) and the partials are merged exactly afterwards.
+//
+// Mapping onto the hardware (decode streams every K/V byte exactly once, so
+// the kernel is HBM bound; the design goal is many outstanding 16-byte loads
+// per lane and little ALU work per byte):
+//   * grid: one work-group of 4 waves per (partition, q-head tile, sequence);
+//     a q-head tile is GT q heads that read the same kv head, so each K/V
+//     byte loaded feeds GT heads (GQA / MQA sharing).
+//   * cache tile layout [block][kv_head][16][D]: the 16 token rows of one
+//     (block, kv head) are contiguous, so a wave load of 16 bytes per lane
+//     reads 1 KiB of consecutive bytes (whole 128-byte lines).
+//   * a token row (D * elem bytes) is owned by L = row_bytes / 16 consecutive
+//     lanes; q.k is a per-lane partial dot (packed dot2 instructions for
+//     fp16 / bf16) finished by a DPP butterfly inside the row.
+//   * every row of lanes keeps its own online-softmax state (m, l, acc) for
+//     the tokens it sees, so the loop has no cross-row traffic; rows and waves
+//     are merged once at the end (shuffles, then LDS).
+//   * the exponential is exp2 with log2(e) folded into the scale.
+//   * tokens past the context are masked with selects (never a multiply), so
+//     whatever bytes sit in unused slots (NaN included) cannot leak.
+//   * a sequence whose context fits in one partition gets its final output
+//     here (when an output pointer is given); longer ones leave a partial
+//     (m, l, o) per partition for the merge kernel.  The merge runs as a
+//     second launch: merging inside this kernel would need device-scope
+//     release/acquire fences per work-group, which on gfx950 write back and
+//     invalidate the per-XCD L2 and cost far more than the extra launch.
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kNegBig = -3.0e38f;  // finite stand-in for -inf in running maxima
+
+template <Elem CE, int D> struct Geom {
+    static constexpr int EB = ElemInfo<CE>::bytes;
+    static constexpr int ROW = D * EB;           // bytes per token row
+    static constexpr int L = ROW / 16;           // lanes per token row
+    static constexpr int E = 16 / EB;            // cache elements per lane
+    static constexpr int R = kWave / L;          // token rows per wave load
+    static constexpr int LPB = kBlockSize / R;   // wave loads per 16-token block
+    static constexpr int U = LPB < 4 ? LPB : 4;  // wave loads per step
+    static constexpr int STEPS = LPB / U;
+    static_assert(L >= 1 && L <= kWave && (L & (L - 1)) == 0, "row must map to 2^k lanes");
+    static_assert(R * LPB == kBlockSize, "block must split into whole wave loads");
+};
+
+// ---- q slice held by a lane, and its dot product with one 16-byte K chunk --
+
+template <Elem QE, Elem CE, int E> struct QSlice;
+
+// fp32 / fp16 / bf16 cache: q kept in the cache's own packed format
+template <Elem T, int E> struct QSlice<T, T, E> {
+    uint4 v;
+    __device__ __forceinline__ void load(const void* q, size_t elem_off) {
+        v = *reinterpret_cast<const uint4*>(static_cast<const char*>(q) +
+                                            elem_off * ElemInfo<T>::bytes);
+    }
+    __device__ __forceinline__ float dot(const uint4& k) const {
+        if constexpr (T == Elem::F16) {
+            float d = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, v.x),
+                                             __builtin_bit_cast(half2_t, k.x), 0.0f, false);
+            d = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, v.y),
+                                       __builtin_bit_cast(half2_t, k.y), d, false);
+            d = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, v.z),
+                                       __builtin_bit_cast(half2_t, k.z), d, false);
+            d = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, v.w),
+                                       __builtin_bit_cast(half2_t, k.w), d, false);
+            return d;
+        } else if constexpr (T == Elem::BF16) {
+            float d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, v.x),
+                                                      __builtin_bit_cast(bf162_t, k.x), 0.0f,
+                                                      false);
+            d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, v.y),
+                                                __builtin_bit_cast(bf162_t, k.y), d, false);
+            d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, v.z),
+                                                __builtin_bit_cast(bf162_t, k.z), d, false);
+            d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, v.w),
+                                                __builtin_bit_cast(bf162_t, k.w), d, false);
+            return d;
+        } else {
+            float d = __builtin_bit_cast(float, v.x) * __builtin_bit_cast(float, k.x);
+            d = fmaf(__builtin_bit_cast(float, v.y), __builtin_bit_cast(float, k.y), d);
+            d = fmaf(__builtin_bit_cast(float, v.z), __builtin_bit_cast(float, k.z), d);
+            d = fmaf(__builtin_bit_cast(float, v.w), __builtin_bit_cast(float, k.w), d);
+            return d;
+        }
+    }
+};
+
+__device__ __forceinline__ float i8_at(uint32_t w, int k) {
+    return (float)(int8_t)(w >> (8 * k));
+}
+
+// INT8 cache: q widened to fp32 once; the codes are widened in the dot
+template <Elem QE> struct QSlice<QE, Elem::I8, 16> {
+    float v[16];
+    __device__ __forceinline__ void load(const void* q, size_t elem_off) {
+        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) + elem_off);
+        uint4 a = p[0], b = p[1];
+        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if constexpr (QE == Elem::F16) {
+                v[2 * i] = lo_h(w[i]);
+                v[2 * i + 1] = hi_h(w[i]);
+            } else {
+                v[2 * i] = lo_bf(w[i]);
+                v[2 * i + 1] = hi_bf(w[i]);
+            }
+        }
+    }
+    __device__ __forceinline__ float dot(const uint4& k) const {
+        const uint32_t w[4] = {k.x, k.y, k.z, k.w};
+        float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            d0 = fmaf(v[4 * i + 0], i8_at(w[i], 0), d0);
+            d1 = fmaf(v[4 * i + 1], i8_at(w[i], 1), d1);
+            d0 = fmaf(v[4 * i + 2], i8_at(w[i], 2), d0);
+            d1 = fmaf(v[4 * i + 3], i8_at(w[i], 3), d1);
+        }
+        return d0 + d1;
+    }
+};
+
+// widen one 16-byte V chunk to E floats
+template <Elem CE, int E> __device__ __forceinline__ void widen(const uint4& c, float (&x)[E]) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (CE == Elem::F32) {
+            x[i] = __builtin_bit_cast(float, w[i]);
+        } else if constexpr (CE == Elem::F16) {
+            x[2 * i] = lo_h(w[i]);
+            x[2 * i + 1] = hi_h(w[i]);
+        } else if constexpr (CE == Elem::BF16) {
+            x[2 * i] = lo_bf(w[i]);
+            x[2 * i + 1] = hi_bf(w[i]);
+        } else {
+            x[4 * i + 0] = i8_at(w[i], 0);
+            x[4 * i + 1] = i8_at(w[i], 1);
+            x[4 * i + 2] = i8_at(w[i], 2);
+            x[4 * i + 3] = i8_at(w[i], 3);
+        }
+    }
+}
+
+// 16-byte streaming load: every K/V byte is read exactly once per call, so
+// the loads carry the non-temporal hint and do not displace reusable lines
+// (q, block tables) from the caches.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_stream(const char* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// The K and V bytes (and INT8 scales) of one 16-token block of one kv head as
+// held by one wave: STEPS x U wave loads of 16 bytes per lane each.
+template <Elem CE, int D> struct BlockRegs {
+    using G = Geom<CE, D>;
+    uint4 k[G::STEPS][G::U], v[G::STEPS][G::U];
+    float ks[G::STEPS][G::U], vs[G::STEPS][G::U];
+    int jb;   // logical block index in the sequence
+    bool ok;  // the block id was inside the pool
+};
+
+template <Elem QE, Elem CE, int D, int GT>
+__global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs a) {
+    using G = Geom<CE, D>;
+    constexpr int L = G::L, E = G::E, R = G::R, U = G::U, STEPS = G::STEPS;
+    constexpr int NW = kDecodeWaves;
+    constexpr bool kInt8 = (CE == Elem::I8);
+
+    __shared__ float s_m[NW][GT];
+    __shared__ float s_l[NW][GT];
+    __shared__ float s_acc[NW][GT][D];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int row = lane / L;   // token row inside a wave load
+    const int slice = lane % L; // which E elements of the row this lane holds
+
+    // work-group -> (partition, tile, sequence); partitions vary fastest
+    const int NP = a.num_partitions;
+    const int part = blockIdx.x % NP;
+    const int rest = blockIdx.x / NP;
+    const int tile = rest % a.n_tiles;
+    const int b = rest / a.n_tiles;
+
+    const int P = a.partition_size;
+    int n = a.context_lens[b];
+    const int n_cap = a.max_blocks_per_seq * kBlockSize;
+    n = n < 0 ? 0 : (n > n_cap ? n_cap : n);
+    const int n_parts = (n + P - 1) / P;
+    const int Hq = a.num_q_heads;
+    const int h0 = tile * GT;
+    const int g = Hq / a.num_kv_heads;
+    const int kvh = h0 / g;
+
+    const bool direct_out = a.out != nullptr;
+    if (part >= n_parts) {
+        if (direct_out && n == 0 && part == 0) {  // empty context: the output is zero
+            for (int i = tid; i < GT * D; i += kDecodeThreads)
+                store_elem<QE>(a.out, ((size_t)b * Hq + h0 + i / D) * D + i % D, 0.0f);
+        }
+        return;
+    }
+
+    // q slices of the GT heads, and the running state of this lane's row
+    QSlice<QE, CE, E> qs[GT];
+#pragma unroll
+    for (int h = 0; h < GT; ++h) qs[h].load(a.q, ((size_t)b * Hq + h0 + h) * D + slice * E);
+
+    float m[GT], l[GT], acc[GT][E];
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+        m[h] = kNegBig;
+        l[h] = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
+    }
+
+    const int t_begin = part * P;
+    const int t_end = min(n, t_begin + P);
+    const int blk_begin = t_begin / kBlockSize;
+    const int blk_end = (t_end + kBlockSize - 1) / kBlockSize;
+    const int32_t* table = a.block_tables + (size_t)b * a.max_blocks_per_seq;
+    const float c = a.scale_log2;
+    const size_t tile_elems = (size_t)kBlockSize * D;
+
+    // Each wave takes a contiguous run of the partition's blocks.  Block ids
+    // are wave-uniform scalar loads, issued one block ahead of their use; they
+    // are counted apart from the vector K/V loads (lgkmcnt vs vmcnt), so
+    // waiting for an id never drains the K/V loads in flight.
+    const int nblk = blk_end - blk_begin;
+    const int per_wave = (nblk + NW - 1) / NW;
+    const int my0 = blk_begin + wave * per_wave;
+    const int n_my = max(0, min(per_wave, blk_end - my0));
+    const int32_t* my_ids = table + my0;
+
+    // Loads are issued without branches (a bad id reads block 0 and is masked
+    // out), so the compiler can count them and wait only for the block being
+    // consumed.
+    auto load_block = [&](BlockRegs<CE, D>& r, int phys, int i) {
+        r.jb = my0 + i;
+        r.ok = phys >= 0 && (int64_t)phys < a.num_blocks;  // a bad id contributes nothing
+        const size_t tile_idx = (size_t)(r.ok ? phys : 0) * a.num_kv_heads + kvh;
+        const char* kt = static_cast<const char*>(a.k_cache) + tile_idx * tile_elems * G::EB;
+        const char* vt = static_cast<const char*>(a.v_cache) + tile_idx * tile_elems * G::EB;
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int tok = (st * U + u) * R;  // first token of this wave load
+                r.k[st][u] = ld16_stream(kt + (size_t)tok * G::ROW + lane * 16);
+                r.v[st][u] = ld16_stream(vt + (size_t)tok * G::ROW + lane * 16);
+                if constexpr (kInt8) {
+                    r.ks[st][u] = a.k_scale[tile_idx * kBlockSize + tok + row];
+                    r.vs[st][u] = a.v_scale[tile_idx * kBlockSize + tok + row];
+                }
+            }
+        }
+    };
+
+    auto compute_block = [&](const BlockRegs<CE, D>& r) {
+        const int jb = r.jb;
+        const bool full = r.ok && (jb + 1) * kBlockSize <= n;
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) {
+            bool valid[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                valid[u] = full || (r.ok && jb * kBlockSize + (st * U + u) * R + row < n);
+
+            // scores of the U tokens this row sees, for every head of the tile,
+            // then the online-softmax update of (m, l) and the rescale of acc
+            float p[GT][U];
+#pragma unroll
+            for (int h = 0; h < GT; ++h) {
+                float s[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    float d = group_sum<L>(qs[h].dot(r.k[st][u]));
+                    if constexpr (kInt8) d *= r.ks[st][u];
+                    s[u] = valid[u] ? d * c : -INFINITY;
+                }
+                float mx = m[h];
+#pragma unroll
+                for (int u = 0; u < U; ++u) mx = fmaxf(mx, s[u]);
+                const float alpha = fast_exp2(m[h] - mx);
+                float psum = 0.f;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    p[h][u] = fast_exp2(s[u] - mx);
+                    psum += p[h][u];
+                }
+                l[h] = fmaf(l[h], alpha, psum);
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[h][e] *= alpha;
+                m[h] = mx;
+            }
+            // V: one wave load at a time, widened once and shared by the heads
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float vx[E];
+                widen<CE, E>(r.v[st][u], vx);
+                if constexpr (!kInt8) {
+                    if (!full) {
+#pragma unroll
+                        for (int e = 0; e < E; ++e) vx[e] = valid[u] ? vx[e] : 0.f;
+                    }
+                }
+#pragma unroll
+                for (int h = 0; h < GT; ++h) {
+                    float pv = p[h][u];
+                    if constexpr (kInt8) pv = valid[u] ? pv * r.vs[st][u] : 0.f;
+#pragma unroll
+                    for (int e = 0; e < E; ++e) acc[h][e] = fmaf(pv, vx[e], acc[h][e]);
+                }
+            }
+        }
+    };
+
+    // Two blocks in flight per wave: the loads of block i+1 are issued before
+    // block i is consumed, and the id of block i+2 is requested meanwhile.
+    // The steady-state loop body has no conditional load.
+    if (n_my > 0) {
+        BlockRegs<CE, D> ra, rb;
+        const int last = n_my - 1;
+        load_block(ra, my_ids[0], 0);
+        int next_id = my_ids[min(1, last)];
+        int i = 0;
+        for (; i + 2 < n_my; i += 2) {
+            load_block(rb, next_id, i + 1);
+            next_id = my_ids[i + 2];
+            compute_block(ra);
+            load_block(ra, next_id, i + 2);
+            next_id = my_ids[min(i + 3, last)];
+            compute_block(rb);
+        }
+        if (i + 1 < n_my) {
+            load_block(rb, next_id, i + 1);
+            compute_block(ra);
+            compute_block(rb);
+        } else {
+            compute_block(ra);
+        }
+    }
+
+    // ---- merge the R rows of each wave (lanes with equal `slice`) ----------
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+        float M = m[h];
+#pragma unroll
+        for (int off = L; off < kWave; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+        const float f = fast_exp2(m[h] - M);
+        float lh = l[h] * f;
+#pragma unroll
+        for (int off = L; off < kWave; off <<= 1) lh += __shfl_xor(lh, off);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            float x = acc[h][e] * f;
+#pragma unroll
+            for (int off = L; off < kWave; off <<= 1) x += __shfl_xor(x, off);
+            acc[h][e] = x;
+        }
+        if (lane == 0) {
+            s_m[wave][h] = M;
+            s_l[wave][h] = lh;
+        }
+        if (row == 0) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) s_acc[wave][h][slice * E + e] = acc[h][e];
+        }
+    }
+    __syncthreads();
+
+    // ---- merge the waves; write out (single partition) or the partial -----
+    const bool single = direct_out && (n_parts == 1);
+    for (int i = tid; i < GT * D; i += kDecodeThreads) {
+        const int h = i / D, d = i % D;
+        float M = s_m[0][h];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m[w][h]);
+        float lsum = 0.f, o = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float f = fast_exp2(s_m[w][h] - M);
+            lsum = fmaf(s_l[w][h], f, lsum);
+            o = fmaf(s_acc[w][h][d], f, o);
+        }
+        const size_t bh = (size_t)b * Hq + h0 + h;
+        if (single) {
+            store_elem<QE>(a.out, bh * D + d, o / lsum);
+        } else {
+            const size_t pi = bh * NP + part;
+            a.o_part[pi * D + d] = o / lsum;
+            if (d == 0) {
+                a.m_part[pi] = M * kLn2;  // natural-log units
+                a.l_part[pi] = lsum;
+            }
+        }
+    }
+}
+
+template <Elem QE, Elem CE, int D, int GT>
+hipError_t launch4(const DecodeArgs& a, hipStream_t stream) {
+    const int64_t n_wg = (int64_t)a.num_partitions * a.n_tiles * a.num_seqs;
+    if (n_wg <= 0) return hipSuccess;
+    if (n_wg > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((paged_decode_kernel<QE, CE, D, GT>), dim3((unsigned)n_wg),
+                       dim3(kDecodeThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <Elem QE, Elem CE, int D>
+hipError_t launch3(const DecodeArgs& a, int gt, hipStream_t s) {
+    switch (gt) {
+    case 1: return launch4<QE, CE, D, 1>(a, s);
+    case 2: return launch4<QE, CE, D, 2>(a, s);
+    case 4: return launch4<QE, CE, D, 4>(a, s);
+    case 8:
+        // INT8 tiles stop at 4 heads: 8 would hold 8 x 16 fp32 accumulators
+        // per lane and spill
+        if constexpr (CE != Elem::I8) return launch4<QE, CE, D, 8>(a, s);
+        return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <Elem QE, Elem CE>
+hipError_t launch2(const DecodeArgs& a, int d, int gt, hipStream_t s) {
+    switch (d) {
+    case 64: return launch3<QE, CE, 64>(a, gt, s);
+    case 128: return launch3<QE, CE, 128>(a, gt, s);
+    case 256: return launch3<QE, CE, 256>(a, gt, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_paged_decode(const DecodeArgs& a, int q_dtype, int cache_dtype, int head_dim,
+                               int heads_per_tile, hipStream_t stream) {
+    const Elem qe = static_cast<Elem>(q_dtype), ce = static_cast<Elem>(cache_dtype);
+    if (qe == Elem::F32 && ce == Elem::F32)
+        return launch2<Elem::F32, Elem::F32>(a, head_dim, heads_per_tile, stream);
+    if (qe == Elem::F16 && ce == Elem::F16)
+        return launch2<Elem::F16, Elem::F16>(a, head_dim, heads_per_tile, stream);
+    if (qe == Elem::BF16 && ce == Elem::BF16)
+        return launch2<Elem::BF16, Elem::BF16>(a, head_dim, heads_per_tile, stream);
+    if (qe == Elem::F16 && ce == Elem::I8)
+        return launch2<Elem::F16, Elem::I8>(a, head_dim, heads_per_tile, stream);
+    if (qe == Elem::BF16 && ce == Elem::I8)
+        return launch2<Elem::BF16, Elem::I8>(a, head_dim, heads_per_tile, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace pkv

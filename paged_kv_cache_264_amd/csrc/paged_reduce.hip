@@ -1,0 +1,109 @@
+// Merge of split-context partial softmax results.
+//
+// A partition p of a sequence carries its max score m_p (natural-log units),
+// l_p = sum exp(s - m_p) and o_p = sum exp(s - m_p) v / l_p.  The exact merge
+// is the running-max / running-sum rule of online softmax (caojiahao2.github.io
+// section 3.2) applied to whole partitions:
+//     M = max_p m_p,  w_p = l_p exp(m_p - M),  out = sum_p w_p o_p / sum_p w_p.
+// One work-group per (sequence, q head); the weights are computed once into
+// LDS and every lane then owns output channels.
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr int kReduceThreads = 256;
+constexpr int kWeightChunk = 1024;  // partitions whose weights sit in LDS at once
+
+template <Elem OE, int D>
+__global__ __launch_bounds__(kReduceThreads) void paged_reduce_kernel(ReduceArgs a) {
+    __shared__ float s_w[kWeightChunk];
+    __shared__ float s_red[kReduceThreads / kWave];
+
+    const int bh = blockIdx.x;
+    const int b = bh / a.num_q_heads;
+    const int tid = threadIdx.x;
+    const int P = a.partition_size;
+    int n = a.context_lens[b];
+    n = n < 0 ? 0 : n;
+    int n_parts = (int)(((int64_t)n + P - 1) / P);
+    n_parts = n_parts > a.num_partitions ? a.num_partitions : n_parts;
+
+    if (a.skip_single && n_parts <= 1) return;  // phase 1 wrote these outputs
+    if (n_parts == 0) {
+        for (int d = tid; d < D; d += kReduceThreads) store_elem<OE>(a.out, (size_t)bh * D + d, 0.f);
+        return;
+    }
+
+    const float* mp = a.m_part + (size_t)bh * a.num_partitions;
+    const float* lp = a.l_part + (size_t)bh * a.num_partitions;
+    const float* op = a.o_part + (size_t)bh * a.num_partitions * D;
+
+    // M = max over partitions (block-wide)
+    float M = -3.0e38f;
+    for (int p = tid; p < n_parts; p += kReduceThreads) M = fmaxf(M, mp[p]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    if ((tid & 63) == 0) s_red[tid >> 6] = M;
+    __syncthreads();
+    M = s_red[0];
+#pragma unroll
+    for (int w = 1; w < kReduceThreads / kWave; ++w) M = fmaxf(M, s_red[w]);
+
+    float o[(D + kReduceThreads - 1) / kReduceThreads];
+#pragma unroll
+    for (int i = 0; i < (D + kReduceThreads - 1) / kReduceThreads; ++i) o[i] = 0.f;
+    float wsum = 0.f;
+    for (int c0 = 0; c0 < n_parts; c0 += kWeightChunk) {
+        const int c1 = min(n_parts, c0 + kWeightChunk);
+        __syncthreads();
+        for (int p = c0 + tid; p < c1; p += kReduceThreads)
+            s_w[p - c0] = lp[p] * fast_exp2((mp[p] - M) * kLog2e);
+        __syncthreads();
+        for (int p = c0; p < c1; ++p) {
+            const float w = s_w[p - c0];
+            wsum += w;
+#pragma unroll
+            for (int i = 0; i < (D + kReduceThreads - 1) / kReduceThreads; ++i) {
+                const int d = tid + i * kReduceThreads;
+                if (d < D) o[i] = fmaf(w, op[(size_t)p * D + d], o[i]);
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < (D + kReduceThreads - 1) / kReduceThreads; ++i) {
+        const int d = tid + i * kReduceThreads;
+        if (d < D) store_elem<OE>(a.out, (size_t)bh * D + d, o[i] / wsum);
+    }
+}
+
+template <Elem OE>
+hipError_t launch_d(const ReduceArgs& a, int d, hipStream_t s) {
+    const int64_t n_wg = (int64_t)a.num_seqs * a.num_q_heads;
+    if (n_wg == 0) return hipSuccess;
+    if (n_wg > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)n_wg), block(kReduceThreads);
+    switch (d) {
+    case 64: hipLaunchKernelGGL((paged_reduce_kernel<OE, 64>), grid, block, 0, s, a); break;
+    case 128: hipLaunchKernelGGL((paged_reduce_kernel<OE, 128>), grid, block, 0, s, a); break;
+    case 256: hipLaunchKernelGGL((paged_reduce_kernel<OE, 256>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_paged_reduce(const ReduceArgs& a, int out_dtype, int head_dim,
+                               hipStream_t stream) {
+    switch (static_cast<Elem>(out_dtype)) {
+    case Elem::F32: return launch_d<Elem::F32>(a, head_dim, stream);
+    case Elem::F16: return launch_d<Elem::F16>(a, head_dim, stream);
+    case Elem::BF16: return launch_d<Elem::BF16>(a, head_dim, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace pkv

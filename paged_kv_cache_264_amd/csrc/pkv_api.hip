@@ -1,0 +1,309 @@
+// C ABI of libpkv: argument validation, launch configuration and workspace
+// layout.  Every entry point checks what the host can see before it enqueues
+// anything, never allocates, frees or synchronizes, and reports failures as a
+// pkv_status plus a thread-local message.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/pkv.h"
+#include "pkv_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+pkv_status fail(pkv_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+pkv_status ok() {
+    g_err[0] = '\0';
+    return PKV_OK;
+}
+
+pkv_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool is_float(pkv_dtype d) { return d == PKV_F32 || d == PKV_F16 || d == PKV_BF16; }
+
+bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int heads_per_tile(int g, pkv_dtype cache) {
+    const int cap = cache == PKV_I8 ? 4 : 8;
+    for (int t = cap; t > 1; t >>= 1)
+        if (g % t == 0) return t;
+    return 1;
+}
+
+int num_partitions(int mbs, int P) { return (int)(((int64_t)mbs * pkv::kBlockSize + P - 1) / P); }
+
+// Workspace layout: the fp32 partials m [B][Hq][NP], l [B][Hq][NP] and
+// o [B][Hq][NP][D], each region 256-byte aligned.
+struct WorkspaceLayout {
+    size_t m_off, l_off, o_off, total;
+};
+
+WorkspaceLayout layout(int B, int Hq, int D, int NP) {
+    WorkspaceLayout w;
+    const size_t pl = (size_t)B * Hq * NP;
+    w.m_off = 0;
+    w.l_off = align256(w.m_off + pl * sizeof(float));
+    w.o_off = align256(w.l_off + pl * sizeof(float));
+    w.total = align256(w.o_off + pl * D * sizeof(float));
+    return w;
+}
+
+// shape checks shared by the decode entry points
+pkv_status check_decode(const void* q, const void* k_cache, const void* v_cache,
+                        const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                        int mbs, const int32_t* context_lens, int B, int Hq, int Hkv, int D,
+                        int block_size, int64_t num_blocks, pkv_dtype q_dtype,
+                        pkv_dtype cache_dtype) {
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || mbs <= 0 || num_blocks <= 0)
+        return fail(PKV_ERR_SHAPE,
+                    "need num_seqs >= 0 and positive num_q_heads, num_kv_heads, "
+                    "max_blocks_per_seq, num_blocks (got %d, %d, %d, %d, %lld)",
+                    B, Hq, Hkv, mbs, (long long)num_blocks);
+    if (Hq % Hkv != 0)
+        return fail(PKV_ERR_SHAPE, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)", Hq,
+                    Hkv);
+    if (block_size != pkv::kBlockSize)
+        return fail(PKV_ERR_UNSUPPORTED, "block_size %d unsupported (only 16)", block_size);
+    if (!head_dim_ok(D))
+        return fail(PKV_ERR_UNSUPPORTED, "head_dim %d unsupported (64, 128, 256)", D);
+    const bool pair_ok = (is_float(q_dtype) && cache_dtype == q_dtype) ||
+                         ((q_dtype == PKV_F16 || q_dtype == PKV_BF16) && cache_dtype == PKV_I8);
+    if (!pair_ok)
+        return fail(PKV_ERR_DTYPE, "unsupported (q_dtype, cache_dtype) = (%d, %d)", (int)q_dtype,
+                    (int)cache_dtype);
+    if (B == 0) return ok();
+    if (!q || !k_cache || !v_cache || !block_tables || !context_lens)
+        return fail(PKV_ERR_NULL, "q, k_cache, v_cache, block_tables and context_lens are required");
+    if (cache_dtype == PKV_I8 && (!k_scale || !v_scale))
+        return fail(PKV_ERR_NULL, "k_scale and v_scale are required for an INT8 cache");
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+        return fail(PKV_ERR_SHAPE, "q, k_cache and v_cache must be 16-byte aligned");
+    if ((int64_t)Hkv * num_blocks * pkv::kBlockSize * D > (int64_t)1 << 62)
+        return fail(PKV_ERR_SHAPE, "pool too large");
+    return ok();
+}
+
+pkv::DecodeArgs make_args(const void* q, const void* k_cache, const void* v_cache,
+                          const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                          int mbs, const int32_t* context_lens, int B, int Hq, int Hkv,
+                          int64_t num_blocks, float scale, int P, int NP, int n_tiles) {
+    pkv::DecodeArgs a{};
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.num_blocks = num_blocks;
+    a.num_seqs = B;
+    a.num_q_heads = Hq;
+    a.num_kv_heads = Hkv;
+    a.max_blocks_per_seq = mbs;
+    a.partition_size = P;
+    a.num_partitions = NP;
+    a.n_tiles = n_tiles;
+    a.scale_log2 = scale * 1.44269504088896340736f;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(pkv_status s) {
+    switch (s) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "a required pointer is NULL";
+    case PKV_ERR_SHAPE: return "invalid or inconsistent sizes";
+    case PKV_ERR_DTYPE: return "unsupported dtype or dtype pairing";
+    case PKV_ERR_UNSUPPORTED: return "head_dim or block_size outside the supported set";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+const char* pkv_last_error(void) { return g_err; }
+
+int pkv_default_partition_size(int num_seqs, int num_q_heads, int num_kv_heads,
+                               int max_blocks_per_seq) {
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
+        num_q_heads % num_kv_heads != 0)
+        return 0;
+    // Measured on MI355X: a work-group pays a chain of dependent memory
+    // round trips (context length, block ids, first K/V tiles) before it
+    // streams, so long partitions stream best; they are cut only as far as
+    // needed to give the 256 CUs about 8 work-groups each at the maximum
+    // context (one tile per kv head).  Power of two in [256, 4096].
+    const int64_t seq_tiles = (int64_t)num_seqs * num_kv_heads;
+    const int64_t max_tokens = (int64_t)max_blocks_per_seq * pkv::kBlockSize;
+    const int64_t want = (max_tokens * seq_tiles + 2047) / 2048;  // tokens per work-group
+    int P = 256;
+    while (P < 4096 && P < want) P <<= 1;
+    return P;
+}
+
+size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                 int max_blocks_per_seq, int partition_size) {
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
+        num_q_heads % num_kv_heads != 0 || !head_dim_ok(head_dim) || partition_size < 0 ||
+        partition_size % pkv::kBlockSize != 0)
+        return 0;
+    const int P = partition_size ? partition_size
+                                 : pkv_default_partition_size(num_seqs, num_q_heads, num_kv_heads,
+                                                              max_blocks_per_seq);
+    return layout(num_seqs, num_q_heads, head_dim, num_partitions(max_blocks_per_seq, P)).total;
+}
+
+pkv_status pkv_kv_cache_write(const void* k, const void* v, void* k_cache, void* v_cache,
+                              float* k_scale, float* v_scale, const int64_t* slot_mapping,
+                              int64_t num_tokens, int num_kv_heads, int head_dim, int block_size,
+                              int64_t num_blocks, pkv_dtype src_dtype, pkv_dtype cache_dtype,
+                              hipStream_t stream) {
+    if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0)
+        return fail(PKV_ERR_SHAPE,
+                    "need num_tokens >= 0, num_kv_heads > 0 and num_blocks > 0 (got %lld, %d, %lld)",
+                    (long long)num_tokens, num_kv_heads, (long long)num_blocks);
+    if (block_size != pkv::kBlockSize)
+        return fail(PKV_ERR_UNSUPPORTED, "block_size %d unsupported (only 16)", block_size);
+    if (!head_dim_ok(head_dim))
+        return fail(PKV_ERR_UNSUPPORTED, "head_dim %d unsupported (64, 128, 256)", head_dim);
+    if (!is_float(src_dtype) || !(cache_dtype == src_dtype || cache_dtype == PKV_I8))
+        return fail(PKV_ERR_DTYPE, "unsupported (src_dtype, cache_dtype) = (%d, %d)",
+                    (int)src_dtype, (int)cache_dtype);
+    if (num_tokens == 0) return ok();
+    if (!k || !v || !k_cache || !v_cache || !slot_mapping)
+        return fail(PKV_ERR_NULL, "k, v, k_cache, v_cache and slot_mapping are required");
+    if (cache_dtype == PKV_I8 && (!k_scale || !v_scale))
+        return fail(PKV_ERR_NULL, "k_scale and v_scale are required for an INT8 cache");
+    if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+        return fail(PKV_ERR_SHAPE, "k, v, k_cache and v_cache must be 16-byte aligned");
+    pkv::CacheWriteArgs a{k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping,
+                          num_tokens, num_blocks, num_kv_heads};
+    return hip_status(
+        pkv::launch_kv_cache_write(a, (int)src_dtype, (int)cache_dtype, head_dim, stream),
+        "kv_cache_write launch");
+}
+
+pkv_status pkv_paged_attn_decode_partials(void* out, float* m_part, float* l_part, float* o_part,
+                                          const void* q, const void* k_cache, const void* v_cache,
+                                          const float* k_scale, const float* v_scale,
+                                          const int32_t* block_tables, int max_blocks_per_seq,
+                                          const int32_t* context_lens, int num_seqs,
+                                          int num_q_heads, int num_kv_heads, int head_dim,
+                                          int block_size, int64_t num_blocks, float scale,
+                                          int partition_size, int num_partitions_,
+                                          pkv_dtype q_dtype, pkv_dtype cache_dtype,
+                                          hipStream_t stream) {
+    pkv_status s = check_decode(q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                                max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                                num_kv_heads, head_dim, block_size, num_blocks, q_dtype,
+                                cache_dtype);
+    if (s != PKV_OK) return s;
+    if (partition_size <= 0 || partition_size % pkv::kBlockSize != 0)
+        return fail(PKV_ERR_SHAPE, "partition_size %d is not a positive multiple of 16",
+                    partition_size);
+    const int NP = num_partitions(max_blocks_per_seq, partition_size);
+    if (num_partitions_ < NP)
+        return fail(PKV_ERR_SHAPE, "num_partitions %d < ceil(max_blocks_per_seq*16/P) = %d",
+                    num_partitions_, NP);
+    if (num_seqs == 0) return ok();
+    if (!m_part || !l_part || !o_part)
+        return fail(PKV_ERR_NULL, "m_part, l_part and o_part are required");
+    if (out && !aligned16(out)) return fail(PKV_ERR_SHAPE, "out must be 16-byte aligned");
+    const int gt = heads_per_tile(num_q_heads / num_kv_heads, cache_dtype);
+    pkv::DecodeArgs a = make_args(q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                                  max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                                  num_kv_heads, num_blocks, scale, partition_size,
+                                  num_partitions_, num_q_heads / gt);
+    a.out = out;
+    a.m_part = m_part;
+    a.l_part = l_part;
+    a.o_part = o_part;
+    return hip_status(pkv::launch_paged_decode(a, (int)q_dtype, (int)cache_dtype, head_dim, gt,
+                                               stream),
+                      "paged_attn_decode_partials launch");
+}
+
+pkv_status pkv_paged_attn_reduce(void* out, const float* m_part, const float* l_part,
+                                 const float* o_part, const int32_t* context_lens, int num_seqs,
+                                 int num_q_heads, int head_dim, int partition_size,
+                                 int num_partitions_, int skip_single_partition,
+                                 pkv_dtype out_dtype, hipStream_t stream) {
+    if (num_seqs < 0 || num_q_heads <= 0 || num_partitions_ <= 0)
+        return fail(PKV_ERR_SHAPE, "need num_seqs >= 0, positive num_q_heads and num_partitions");
+    if (partition_size <= 0 || partition_size % pkv::kBlockSize != 0)
+        return fail(PKV_ERR_SHAPE, "partition_size %d is not a positive multiple of 16",
+                    partition_size);
+    if (!head_dim_ok(head_dim))
+        return fail(PKV_ERR_UNSUPPORTED, "head_dim %d unsupported (64, 128, 256)", head_dim);
+    if (!is_float(out_dtype)) return fail(PKV_ERR_DTYPE, "out_dtype must be F32, F16 or BF16");
+    if (num_seqs == 0) return ok();
+    if (!out || !m_part || !l_part || !o_part || !context_lens)
+        return fail(PKV_ERR_NULL, "out, m_part, l_part, o_part and context_lens are required");
+    pkv::ReduceArgs a{out, m_part, l_part, o_part, context_lens, num_seqs, num_q_heads,
+                      partition_size, num_partitions_, skip_single_partition ? 1 : 0};
+    return hip_status(pkv::launch_paged_reduce(a, (int)out_dtype, head_dim, stream),
+                      "paged_attn_reduce launch");
+}
+
+pkv_status pkv_paged_attn_decode(void* out, const void* q, const void* k_cache,
+                                 const void* v_cache, const float* k_scale, const float* v_scale,
+                                 const int32_t* block_tables, int max_blocks_per_seq,
+                                 const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                 int num_kv_heads, int head_dim, int block_size,
+                                 int64_t num_blocks, float scale, int partition_size,
+                                 void* workspace, size_t workspace_bytes, pkv_dtype q_dtype,
+                                 pkv_dtype cache_dtype, hipStream_t stream) {
+    pkv_status s = check_decode(q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                                max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                                num_kv_heads, head_dim, block_size, num_blocks, q_dtype,
+                                cache_dtype);
+    if (s != PKV_OK) return s;
+    if (partition_size < 0 || partition_size % pkv::kBlockSize != 0)
+        return fail(PKV_ERR_SHAPE, "partition_size %d is not 0 or a positive multiple of 16",
+                    partition_size);
+    if (num_seqs == 0) return ok();
+    if (!out) return fail(PKV_ERR_NULL, "out is required");
+    if (!aligned16(out)) return fail(PKV_ERR_SHAPE, "out must be 16-byte aligned");
+    const int P = partition_size ? partition_size
+                                 : pkv_default_partition_size(num_seqs, num_q_heads, num_kv_heads,
+                                                              max_blocks_per_seq);
+    const int NP = num_partitions(max_blocks_per_seq, P);
+    const WorkspaceLayout w = layout(num_seqs, num_q_heads, head_dim, NP);
+    if (!workspace || workspace_bytes < w.total)
+        return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+        return fail(PKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    char* ws = static_cast<char*>(workspace);
+    float* m = reinterpret_cast<float*>(ws + w.m_off);
+    float* l = reinterpret_cast<float*>(ws + w.l_off);
+    float* o = reinterpret_cast<float*>(ws + w.o_off);
+    s = pkv_paged_attn_decode_partials(out, m, l, o, q, k_cache, v_cache, k_scale, v_scale,
+                                       block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                                       num_q_heads, num_kv_heads, head_dim, block_size,
+                                       num_blocks, scale, P, NP, q_dtype, cache_dtype, stream);
+    if (s != PKV_OK) return s;
+    if (NP == 1) return ok();  // every sequence was finished in phase 1
+    return pkv_paged_attn_reduce(out, m, l, o, context_lens, num_seqs, num_q_heads, head_dim, P,
+                                 NP, 1, q_dtype, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,78 @@
+// Host-side interfaces between the C ABI (pkv_api.hip) and the kernel
+// translation units.  Internal to libpkv.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kBlockSize = 16;   // tokens per KV block
+constexpr int kDecodeThreads = 256;
+constexpr int kDecodeWaves = kDecodeThreads / 64;
+
+struct DecodeArgs {
+    void* out;
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    const float* k_scale;
+    const float* v_scale;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    float* m_part;       // [B][Hq][NP]
+    float* l_part;       // [B][Hq][NP]
+    float* o_part;       // [B][Hq][NP][D]
+    int64_t num_blocks;
+    int num_seqs;
+    int num_q_heads;
+    int num_kv_heads;
+    int max_blocks_per_seq;
+    int partition_size;  // tokens, multiple of 16
+    int num_partitions;  // NP: partial-array stride
+    int n_tiles;         // num_q_heads / heads_per_tile
+    float scale_log2;    // softmax scale * log2(e)
+};
+
+// Phase 1 of split-context decode.  With a.out set, sequences whose context
+// fits in one partition (or is empty) get their final output in a.out and
+// write no partial; with a.out == nullptr every non-empty partition writes its
+// partial.  Returns hipErrorInvalidValue for a combination with no kernel.
+hipError_t launch_paged_decode(const DecodeArgs& a, int q_dtype, int cache_dtype, int head_dim,
+                               int heads_per_tile, hipStream_t stream);
+
+struct ReduceArgs {
+    void* out;
+    const float* m_part;
+    const float* l_part;
+    const float* o_part;
+    const int32_t* context_lens;
+    int num_seqs;
+    int num_q_heads;
+    int partition_size;
+    int num_partitions;
+    int skip_single;     // sequences with <= 1 partition already hold their output
+};
+
+hipError_t launch_paged_reduce(const ReduceArgs& a, int out_dtype, int head_dim,
+                               hipStream_t stream);
+
+struct CacheWriteArgs {
+    const void* k;
+    const void* v;
+    void* k_cache;
+    void* v_cache;
+    float* k_scale;
+    float* v_scale;
+    const int64_t* slot_mapping;
+    int64_t num_tokens;
+    int64_t num_blocks;
+    int num_kv_heads;
+};
+
+hipError_t launch_kv_cache_write(const CacheWriteArgs& a, int src_dtype, int cache_dtype,
+                                 int head_dim, hipStream_t stream);
+
+
+}  // namespace pkv

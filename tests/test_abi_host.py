@@ -1,0 +1,174 @@
+"""Host-side checks of the C ABI (no GPU needed, nothing is launched).
+
+- libpkv.so loads and exports every function include/pkv.h declares;
+- argument errors that the host can see return the documented status before
+  anything is enqueued (these calls reach no HIP API);
+- the Python binding refuses tensors that are not on a GPU.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+LIB = os.path.join(ROOT, "paged_kv_cache_264_amd", "libpkv.so")
+
+OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EWS, EHIP = range(7)
+F32, F16, BF16, I8 = range(4)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libpkv.so is not built (run __graft_entry__.build())")
+    L = ctypes.CDLL(LIB)
+    L.pkv_last_error.restype = ctypes.c_char_p
+    L.pkv_status_string.restype = ctypes.c_char_p
+    L.pkv_decode_workspace_size.restype = ctypes.c_size_t
+    return L
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 8
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\sT\s(\S+)", out))
+    for n in names:
+        assert n in exported, n
+        getattr(lib, n)
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert lib.pkv_status_string(s)
+    assert lib.pkv_status_string(99) == b"unknown status"
+
+
+P = ctypes.c_void_p
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
+
+
+def decode(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, ks=None, vs=None, bt=FAKE, mbs=8, cl=FAKE, B=2,
+             Hq=8, Hkv=2, D=128, bs=16, NB=10, scale=0.1, P=0, ws=FAKE, wsb=1 << 30,
+             qd=F16, cd=F16)
+    a.update(kw)
+    f = lib.pkv_paged_attn_decode
+    f.argtypes = [P, P, P, P, P, P, P, ctypes.c_int, P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_int, P,
+                  ctypes.c_size_t, ctypes.c_int, ctypes.c_int, P]
+    return f(a["out"], a["q"], a["k"], a["v"], a["ks"], a["vs"], a["bt"], a["mbs"], a["cl"],
+             a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"], a["scale"], a["P"], a["ws"],
+             a["wsb"], a["qd"], a["cd"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hq=6, Hkv=4), ESHAPE),
+    (dict(Hkv=0), ESHAPE),
+    (dict(B=-1), ESHAPE),
+    (dict(D=96), EUNSUP),
+    (dict(bs=32), EUNSUP),
+    (dict(qd=F32, cd=F16), EDTYPE),
+    (dict(qd=F32, cd=I8), EDTYPE),
+    (dict(qd=I8, cd=I8), EDTYPE),
+    (dict(q=None), ENULL),
+    (dict(bt=None), ENULL),
+    (dict(cd=I8), ENULL),                 # INT8 cache without scales
+    (dict(out=None), ENULL),
+    (dict(P=24), ESHAPE),
+    (dict(P=-16), ESHAPE),
+    (dict(ws=None), EWS),
+    (dict(wsb=100), EWS),
+    (dict(q=ctypes.c_void_p(0x1004)), ESHAPE),   # misaligned
+])
+def test_decode_argument_errors(lib, kw, status):
+    assert decode(lib, **kw) == status
+    assert lib.pkv_last_error()
+
+
+def test_empty_batch_is_ok_without_launch(lib):
+    assert decode(lib, B=0, out=None, q=None, bt=None, cl=None, ws=None) == OK
+
+
+def test_workspace_size(lib):
+    f = lib.pkv_decode_workspace_size
+    f.argtypes = [ctypes.c_int] * 6
+    assert f(64, 32, 32, 128, 256, 512) > 64 * 32 * 8 * 128 * 4
+    assert f(64, 32, 32, 96, 256, 512) == 0
+    assert f(64, 32, 32, 128, 256, 24) == 0
+    assert f(4, 8, 3, 64, 8, 0) == 0
+    lib.pkv_default_partition_size.argtypes = [ctypes.c_int] * 4
+    for args in [(64, 32, 32, 256), (1, 32, 8, 2048), (16, 32, 32, 2048), (128, 32, 8, 512)]:
+        p = lib.pkv_default_partition_size(*args)
+        assert p >= 64 and p % 16 == 0
+
+
+def test_cache_write_argument_errors(lib):
+    f = lib.pkv_kv_cache_write
+    f.argtypes = [P, P, P, P, P, P, P, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_int64, ctypes.c_int, ctypes.c_int, P]
+    base = [FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 4, 2, 128, 16, 10, F16, F16, None]
+
+    def call(i, val):
+        a = list(base)
+        a[i] = val
+        return f(*a)
+
+    assert call(7, -1) == ESHAPE            # num_tokens
+    assert call(9, 80) == EUNSUP            # head_dim
+    assert call(10, 8) == EUNSUP            # block_size
+    assert call(13, BF16) == EDTYPE         # cache dtype != src and != I8
+    assert call(12, I8) == EDTYPE           # src must be float
+    assert call(0, None) == ENULL
+    assert call(13, I8) == ENULL            # INT8 without scales
+    assert call(7, 0) == OK                 # nothing to write: no launch
+
+
+def test_reduce_argument_errors(lib):
+    f = lib.pkv_paged_attn_reduce
+    f.argtypes = [P, P, P, P, P] + [ctypes.c_int] * 7 + [P]
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 128, 20, 4, 0, F16, None) == ESHAPE
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 100, 16, 4, 0, F16, None) == EUNSUP
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 128, 16, 4, 0, I8, None) == EDTYPE
+    assert f(None, FAKE, FAKE, FAKE, FAKE, 2, 4, 128, 16, 4, 1, F16, None) == ENULL
+    assert f(None, None, None, None, None, 0, 4, 128, 16, 4, 0, F16, None) == OK
+
+
+def test_partials_argument_errors(lib):
+    f = lib.pkv_paged_attn_decode_partials
+    I = ctypes.c_int
+    f.argtypes = [P, P, P, P, P, P, P, P, P, P, I, P, I, I, I, I, I, ctypes.c_int64,
+                  ctypes.c_float, I, I, I, I, P]
+    base = [None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 8, FAKE, 2, 8, 2, 128,
+            16, 10, 0.1, 64, 2, F16, F16, None]
+
+    def call(i, val):
+        a = list(base)
+        a[i] = val
+        return f(*a)
+
+    assert call(19, 0) == ESHAPE            # partition size must be given
+    assert call(19, 40) == ESHAPE           # not a multiple of 16
+    assert call(20, 1) == ESHAPE            # num_partitions < ceil(8*16/64)
+    assert call(1, None) == ENULL           # m_part
+    assert call(0, ctypes.c_void_p(0x1008)) == ESHAPE   # misaligned out
+
+
+def test_binding_rejects_host_tensors():
+    import paged_kv_cache_264_amd as pkv
+    q = torch.zeros((1, 4, 64))
+    with pytest.raises(ValueError):
+        pkv.paged_attn_decode(q, torch.zeros((4, 4, 16, 64)), torch.zeros((4, 4, 16, 64)),
+                              torch.zeros((1, 4), dtype=torch.int32),
+                              torch.zeros((1,), dtype=torch.int32), 0.125)

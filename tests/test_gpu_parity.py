@@ -1,0 +1,330 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: bit-exact for cache-write placement and INT8 codes / scales; max-abs
+error <= 2e-3 (fp16 KV), 1.6e-2 (bf16 KV), 2e-3 (INT8 KV, oracle on the same
+dequantized values) and 1e-5 (fp32 KV) for attention outputs.  Unused pool
+slots are NaN-poisoned in every attention case, so a kernel that reads outside
+a context cannot pass.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from helpers import (BS, DT, TOL, OracleView, as_f64, gpu_populate, gpu_step, host,
+                     max_abs_err, tol_for)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    import paged_kv_cache_264_amd as m
+    m._load()
+    return m
+
+
+def _cfg(dtype, cache, D, Hq, Hkv, lens, pool=None, seed=0):
+    return dict(B=len(lens), ctx=list(lens), Hq=Hq, Hkv=Hkv, D=D, dtype=dtype, cache=cache,
+                pool=pool, seed=seed, max_ctx=max(max(lens), 16))
+
+
+def _check_step(pkv, batch, seqs=None, partition_size=0, tol=None):
+    seqs = np.arange(batch.B) if seqs is None else np.asarray(seqs)
+    view = OracleView(batch, seqs)           # host copies taken before the GPU step
+    out = gpu_step(pkv, batch, partition_size=partition_size)
+    torch.cuda.synchronize()
+    view.write_new_tokens(batch)
+    ref = view.decode()
+    got = out[torch.from_numpy(seqs).to(out.device)]
+    err = max_abs_err(got, ref)
+    tol = tol_for(DT[batch.q.dtype], DT[batch.k_cache.dtype]) if tol is None else tol
+    print(f"[parity] {batch.name} B={batch.B} Hq={batch.Hq} Hkv={batch.Hkv} D={batch.D} "
+          f"{DT[batch.q.dtype]}/{DT[batch.k_cache.dtype]} P={partition_size} "
+          f"max_abs_err={err:.3e} tol={tol:.1e}", flush=True)
+    assert torch.isfinite(out.float()).all(), "non-finite output (poisoned slot read?)"
+    assert err <= tol
+    return out, view
+
+
+PAIRS = [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"), ("f16", "i8"), ("bf16", "i8")]
+LENS = [1, 15, 16, 17, 250, 700, 33]
+
+
+@pytest.mark.parametrize("dtype,cache", PAIRS)
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 2), (16, 2), (6, 3)])
+def test_decode_matrix(pkv, dtype, cache, D, Hq, Hkv):
+    batch = W.make_batch(cfg=_cfg(dtype, cache, D, Hq, Hkv, LENS, seed=D + Hq), device="cuda")
+    gpu_populate(pkv, batch)
+    _check_step(pkv, batch)
+
+
+@pytest.mark.parametrize("P", [16, 48, 64, 256, 1024])
+@pytest.mark.parametrize("dtype,cache", [("f16", "f16"), ("bf16", "i8")])
+def test_partition_sizes(pkv, P, dtype, cache):
+    batch = W.make_batch(cfg=_cfg(dtype, cache, 128, 8, 2, [5, 64, 129, 1000, 1500], seed=P),
+                         device="cuda")
+    gpu_populate(pkv, batch)
+    _check_step(pkv, batch, partition_size=P)
+
+
+def test_tiny_config(pkv):
+    batch = W.make_batch("tiny", device="cuda")
+    _check_step(pkv, batch)
+
+
+def test_zero_context_and_empty_batch(pkv):
+    batch = W.make_batch(cfg=_cfg("f16", "f16", 128, 4, 4, [0, 20, 0, 3]), device="cuda")
+    out = gpu_step(pkv, batch)
+    torch.cuda.synchronize()
+    assert (out[0] == 0).all() and (out[2] == 0).all()
+    _check_step(pkv, W.make_batch(cfg=_cfg("f16", "f16", 128, 4, 4, [0, 20, 0, 3]),
+                                  device="cuda"))
+    # B = 0 and T = 0 enqueue nothing and succeed
+    q = torch.empty((0, 4, 128), dtype=torch.float16, device="cuda")
+    res = pkv.paged_attn_decode(q, batch.k_cache, batch.v_cache,
+                                torch.empty((0, 4), dtype=torch.int32, device="cuda"),
+                                torch.empty((0,), dtype=torch.int32, device="cuda"), 0.1)
+    assert res.shape == (0, 4, 128)
+    e = torch.empty((0, 4, 128), dtype=torch.float16, device="cuda")
+    pkv.kv_cache_write(e, e, batch.k_cache, batch.v_cache,
+                       torch.empty((0,), dtype=torch.int64, device="cuda"))
+
+
+def test_single_token_returns_v0_exactly(pkv):
+    for dtype in ("f32", "f16", "bf16"):
+        batch = W.make_batch(cfg=_cfg(dtype, dtype, 128, 8, 2, [1, 1, 1]), device="cuda")
+        out = gpu_step(pkv, batch)
+        torch.cuda.synchronize()
+        for s in range(3):
+            v0 = batch.v_new[s]                    # position 0 is the new token
+            assert torch.equal(out[s], v0.repeat_interleave(4, dim=0)), dtype
+
+
+def test_identical_keys_give_mean_of_v(pkv):
+    batch = W.make_batch(cfg=_cfg("f32", "f32", 64, 2, 2, [40, 300]), device="cuda")
+    batch.k_new.copy_(batch.k_new[0:1].expand_as(batch.k_new))
+    for s, n in enumerate([40, 300]):
+        for t in range(n):
+            blk = int(batch.layout.block_tables[s, t // BS])
+            batch.k_cache[blk, :, t % BS] = batch.k_new[0]
+    out = gpu_step(pkv, batch)
+    torch.cuda.synchronize()
+    for s, n in enumerate([40, 300]):
+        rows = [batch.v_cache[int(batch.layout.block_tables[s, t // BS]), :, t % BS]
+                .double() for t in range(n)]
+        mean = torch.stack(rows).mean(0).cpu().numpy()
+        assert np.abs(as_f64(out[s]) - mean).max() < 1e-5
+
+
+def test_placement_permutation_invariance_bit_exact(pkv):
+    batch = W.make_batch(cfg=_cfg("bf16", "bf16", 128, 8, 2, [900, 31, 400]), device="cuda")
+    out1 = gpu_step(pkv, batch).clone()
+    NB = batch.num_blocks
+    perm = torch.from_numpy(np.random.default_rng(9).permutation(NB)).cuda()
+    inv = torch.argsort(perm)
+    k2, v2 = batch.k_cache[inv].contiguous(), batch.v_cache[inv].contiguous()
+    bt = batch.block_tables.clone().long()
+    bt = torch.where(bt >= 0, perm[bt.clamp(min=0)], bt).int().contiguous()
+    out2 = pkv.paged_attn_decode(batch.q, k2, v2, bt, batch.context_lens, batch.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
+
+
+def test_deterministic_reruns(pkv):
+    batch = W.make_batch(cfg=_cfg("f16", "i8", 128, 8, 8, [2000, 77, 1500, 16]), device="cuda")
+    gpu_populate(pkv, batch)
+    a = gpu_step(pkv, batch, partition_size=64).clone()
+    b = gpu_step(pkv, batch, partition_size=64).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# partials + standalone reduce
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,cache,P", [("f32", "f32", 16), ("f16", "f16", 64),
+                                           ("bf16", "bf16", 128), ("f16", "i8", 32)])
+def test_partials_and_reduce(pkv, dtype, cache, P):
+    lens = [3, 16, 100, 513, 0]
+    batch = W.make_batch(cfg=_cfg(dtype, cache, 64, 4, 2, lens, seed=P), device="cuda")
+    gpu_populate(pkv, batch)
+    view = OracleView(batch, np.arange(batch.B))
+    pkv.kv_cache_write(batch.k_new, batch.v_new, batch.k_cache, batch.v_cache, batch.slot_new,
+                       batch.k_scale, batch.v_scale)
+    view.write_new_tokens(batch)
+    NP = pkv.num_partitions(batch.block_tables.shape[1], P)
+    m, l, o = pkv.paged_attn_decode_partials(batch.q, batch.k_cache, batch.v_cache,
+                                             batch.block_tables, batch.context_lens, batch.scale,
+                                             P, k_scale=batch.k_scale, v_scale=batch.v_scale)
+    out = pkv.paged_attn_reduce(m, l, o, batch.context_lens, P, out_dtype=batch.q.dtype)
+    # phase 1 with an output pointer finishes single-partition sequences; the
+    # merge then skips them
+    out2 = torch.full_like(batch.q, float("nan"))
+    m2, l2, o2 = pkv.paged_attn_decode_partials(batch.q, batch.k_cache, batch.v_cache,
+                                                batch.block_tables, batch.context_lens,
+                                                batch.scale, P, k_scale=batch.k_scale,
+                                                v_scale=batch.v_scale, out=out2)
+    pkv.paged_attn_reduce(m2, l2, o2, batch.context_lens, P, out=out2, skip_single_partition=True)
+    torch.cuda.synchronize()
+    for s_, n in enumerate(lens):
+        if n <= P:   # finished in phase 1: no partial written
+            assert torch.isnan(m2[s_]).all()
+    rm, rl, ro = oracle.paged_partials(view.q, view.q_dtype, view.k_cache, view.v_cache,
+                                       view.cache_dtype, view.block_tables, view.context_lens,
+                                       view.scale, P, NP, k_scale=view.k_scale,
+                                       v_scale=view.v_scale)
+    tol = tol_for(dtype, cache)
+    for s, n in enumerate(lens):
+        npart = -(-n // P)
+        if npart == 0:
+            continue
+        assert np.abs(as_f64(m[s, :, :npart]) - rm[s, :, :npart]).max() < 1e-3 * max(
+            1.0, np.abs(rm[s, :, :npart]).max())
+        np.testing.assert_allclose(as_f64(l[s, :, :npart]), rl[s, :, :npart], rtol=1e-4)
+        assert np.abs(as_f64(o[s, :, :npart]) - ro[s, :, :npart]).max() <= tol
+    ref = view.decode()
+    assert max_abs_err(out, ref) <= tol
+    assert max_abs_err(out2, ref) <= tol
+    fused = pkv.paged_attn_decode(batch.q, batch.k_cache, batch.v_cache, batch.block_tables,
+                                  batch.context_lens, batch.scale, k_scale=batch.k_scale,
+                                  v_scale=batch.v_scale, partition_size=P)
+    torch.cuda.synchronize()
+    assert max_abs_err(fused, ref) <= tol
+
+
+def test_reduce_on_synthetic_partials(pkv):
+    g = np.random.default_rng(17)
+    B, Hq, NP, D, P = 3, 4, 9, 128, 32
+    m = g.standard_normal((B, Hq, NP)) * 3
+    l = g.uniform(1, 20, (B, Hq, NP))
+    o = g.standard_normal((B, Hq, NP, D))
+    lens = np.array([NP * P, 5 * P - 3, 0], np.int32)
+    out = pkv.paged_attn_reduce(torch.from_numpy(m).float().cuda(),
+                                torch.from_numpy(l).float().cuda(),
+                                torch.from_numpy(o).float().cuda(),
+                                torch.from_numpy(lens).cuda(), P)
+    torch.cuda.synchronize()
+    mf, lf, of = (x.astype(np.float32).astype(np.float64) for x in (m, l, o))
+    for s in range(B):
+        npart = -(-int(lens[s]) // P)
+        if npart == 0:
+            assert (out[s] == 0).all()
+            continue
+        ref = oracle.merge_partials(mf[s:s + 1, :, :npart], lf[s:s + 1, :, :npart],
+                                    of[s:s + 1, :, :npart])
+        assert np.abs(as_f64(out[s]) - ref[0]).max() < 1e-5
+
+
+# ---------------------------------------------------------------------------
+# cache write: bit-exact placement and INT8 codes
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("src,cache", [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"),
+                                       ("f32", "i8"), ("f16", "i8"), ("bf16", "i8")])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_cache_write_bit_exact(pkv, src, cache, D):
+    NB, Hkv, T = 40, 4, 64
+    g = np.random.default_rng(D)
+    slots = W.random_slots(NB, T, seed=D)
+    slots[::7] = -1                                          # skipped tokens
+    tdt = W.TORCH_DTYPE
+    k = torch.from_numpy(g.standard_normal((T, Hkv, D), dtype=np.float32) * 3).to(tdt[src])
+    v = torch.from_numpy(g.standard_normal((T, Hkv, D), dtype=np.float32)).to(tdt[src])
+    if cache == "i8":
+        k[0] = 0.0                                           # zero row -> s = 0
+        k[1, :, :] = 0.5; k[1, :, 0] = 127.0                  # ties with s = 1
+    # sentinel bytes everywhere in the pool
+    kc = torch.from_numpy(g.integers(0, 256, (NB, Hkv, BS, D * (4 if cache == "f32" else
+                                     2 if cache in ("f16", "bf16") else 1)), dtype=np.uint8))
+    vc = torch.from_numpy(g.integers(0, 256, kc.shape, dtype=np.uint8))
+    kc = kc.view(tdt[cache]).contiguous(); vc = vc.view(tdt[cache]).contiguous()
+    ks = vs = None
+    if cache == "i8":
+        ks = torch.from_numpy(g.standard_normal((NB, Hkv, BS), dtype=np.float32))
+        vs = torch.from_numpy(g.standard_normal((NB, Hkv, BS), dtype=np.float32))
+    hk, hv = host(kc), host(vc)
+    hks = None if ks is None else ks.numpy().copy()
+    hvs = None if vs is None else vs.numpy().copy()
+    oracle.kv_cache_write(host(k), host(v), hk, hv, slots, src, cache, hks, hvs)
+    gk, gv = kc.cuda(), vc.cuda()
+    gks = None if ks is None else ks.cuda()
+    gvs = None if vs is None else vs.cuda()
+    pkv.kv_cache_write(k.cuda(), v.cuda(), gk, gv, torch.from_numpy(slots).cuda(), gks, gvs)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(gk).view(np.uint8), hk.view(np.uint8))
+    assert np.array_equal(host(gv).view(np.uint8), hv.view(np.uint8))
+    if cache == "i8":
+        assert np.array_equal(host(gks).view(np.uint32), hks.view(np.uint32))
+        assert np.array_equal(host(gvs).view(np.uint32), hvs.view(np.uint32))
+
+
+def test_int8_codes_bit_exact_many_rows(pkv):
+    """400k fp16 rows of D=128 quantized by both sides, compared bit for bit."""
+    T, Hkv, D = 4096, 32, 128
+    g = torch.Generator(device="cuda"); g.manual_seed(2024)
+    k = torch.randn((T, Hkv, D), generator=g, device="cuda").half()
+    v = (torch.randn((T, Hkv, D), generator=g, device="cuda") * 7).half()
+    NB = T // BS
+    slots = torch.arange(T, dtype=torch.int64, device="cuda")
+    kc = torch.empty((NB, Hkv, BS, D), dtype=torch.int8, device="cuda")
+    vc = torch.empty_like(kc)
+    ks = torch.empty((NB, Hkv, BS), dtype=torch.float32, device="cuda")
+    vs = torch.empty_like(ks)
+    pkv.kv_cache_write(k, v, kc, vc, slots, ks, vs)
+    torch.cuda.synchronize()
+    codes, scales = oracle.quantize_rows(host(k), "f16")
+    # slot t = token t: block t // 16, offset t % 16 -> [NB][16][Hkv][D] order
+    got = host(kc).reshape(NB, Hkv, BS, D).transpose(0, 2, 1, 3).reshape(T, Hkv, D)
+    gsc = host(ks).reshape(NB, Hkv, BS).transpose(0, 2, 1).reshape(T, Hkv)
+    assert np.array_equal(got, codes)
+    assert np.array_equal(gsc.view(np.uint32), scales.view(np.uint32))
+    codes_v, scales_v = oracle.quantize_rows(host(v), "f16")
+    gotv = host(vc).reshape(NB, Hkv, BS, D).transpose(0, 2, 1, 3).reshape(T, Hkv, D)
+    assert np.array_equal(gotv, codes_v)
+    gsv = host(vs).reshape(NB, Hkv, BS).transpose(0, 2, 1).reshape(T, Hkv)
+    assert np.array_equal(gsv.view(np.uint32), scales_v.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# the five workloads at full size, in the launch configuration the bench uses
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "llama7b", "gqa", "long", "int8"])
+def test_full_config(pkv, name):
+    batch = W.make_batch(name, device="cuda", poison=True)
+    gpu_populate(pkv, batch)
+    lens = batch.layout.context_lens
+    order = np.argsort(lens)
+    seqs = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2])})
+    P = batch.cfg.get("partition_size", 0)
+    out, view = _check_step(pkv, batch, seqs=seqs, partition_size=P)
+    if name == "int8":
+        # the library's INT8 pool equals the oracle's, byte for byte, on the
+        # blocks of the sampled sequences
+        idx = torch.from_numpy(view.block_ids).cuda()
+        assert np.array_equal(host(batch.k_cache[idx]), view.k_cache)
+        assert np.array_equal(host(batch.v_cache[idx]), view.v_cache)
+        used = np.zeros((len(view.block_ids), batch.Hkv, BS), bool)
+        for i, (s, n) in enumerate(zip(view.seqs, view.context_lens)):
+            for t in range(n):
+                used[view.block_tables[i, t // BS], :, t % BS] = True
+        assert np.array_equal(host(batch.k_scale[idx])[used].view(np.uint32),
+                              view.k_scale[used].view(np.uint32))
+        assert np.array_equal(host(batch.v_scale[idx])[used].view(np.uint32),
+                              view.v_scale[used].view(np.uint32))
+
+
+def test_workspace_reuse_across_shapes(pkv):
+    """One cached workspace serves calls of different shapes back to back: a
+    call's partials never land on another call's merge counters."""
+    shapes = [([3000, 900, 5000], 8, 8, 128, 64), ([40, 300], 2, 2, 64, 16),
+              ([100] * 9, 16, 4, 64, 32), ([700, 1], 4, 4, 256, 48)]
+    for i, (lens, Hq, Hkv, D, P) in enumerate(shapes * 2):
+        batch = W.make_batch(cfg=_cfg("f16", "f16", D, Hq, Hkv, lens, seed=i), device="cuda")
+        _check_step(pkv, batch, partition_size=P)

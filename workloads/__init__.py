@@ -246,7 +246,7 @@ def make_batch(name: str | None = None, device="cpu", seed: int | None = None, p
     slot_new = np.array([slots_for(layout, b, [max(int(n) - 1, 0)])[0] if n > 0 else -1
                          for b, n in enumerate(lens)], np.int64)
 
-    k_scale = v_scale = k_src = v_src = slot_src = None
+    k_scale = v_scale = k_src = v_src = slot_src = src_offsets = None
     if cache == "i8":
         k_cache = torch.zeros((nb, Hkv, BLOCK_SIZE, D), dtype=torch.int8, device=device)
         v_cache = torch.zeros_like(k_cache)
@@ -262,6 +262,7 @@ def make_batch(name: str | None = None, device="cpu", seed: int | None = None, p
         _fill_normal_(k_src, seed, S_K, chunk_rows=1 << 14, post=k_post)
         _fill_normal_(v_src, seed, S_V, chunk_rows=1 << 14)
         slot_src = torch.from_numpy(slot_src_np).to(device)
+        src_offsets = np.concatenate([[0], np.cumsum([len(x) for x in slots])]).astype(np.int64)
     else:
         tdt = TORCH_DTYPE[cache]
         k_cache = torch.empty((nb, Hkv, BLOCK_SIZE, D), dtype=tdt, device=device)
@@ -288,7 +289,8 @@ def make_batch(name: str | None = None, device="cpu", seed: int | None = None, p
                  block_tables=torch.from_numpy(layout.block_tables).to(device),
                  context_lens=torch.from_numpy(lens).to(device), k_new=k_new, v_new=v_new,
                  slot_new=torch.from_numpy(slot_new).to(device), scale=scale, k_src=k_src,
-                 v_src=v_src, slot_src=slot_src, outlier_channels=outl)
+                 v_src=v_src, slot_src=slot_src, outlier_channels=outl,
+                 extra={"src_offsets": src_offsets})
 
 
 def random_slots(num_blocks: int, T: int, seed: int) -> np.ndarray:
