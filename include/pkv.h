@@ -152,15 +152,18 @@ pkv_status pkv_paged_attn_decode(void* out, const void* q, const void* k_cache,
 /*
  * Phase 1 of the split-context decode: per-partition partial results (for a
  * caller that merges them itself, e.g. partitions computed on several
- * devices, or that times the phases apart).  For partition p of sequence b
- * (tokens [p*P, min((p+1)*P, N_b)), P = partition_size, N_b =
- * context_lens[b]) and q head h:
+ * devices, or that times the phases apart).  The N_b = context_lens[b] tokens
+ * of sequence b are cut into ceil(N_b / P) partitions (P = partition_size) of
+ * equal length rounded up to whole blocks, span_b = 16 * ceil(ceil(N_b /
+ * count) / 16) <= P, so no partition is a short stub; partition p holds tokens
+ * [p * span_b, min((p + 1) * span_b, N_b)).  For partition p and q head h:
  *    m_part[b][h][p]    = max_t s_t,  s_t = scale * (q . k_t)  (natural units)
  *    l_part[b][h][p]    = sum_t exp(s_t - m)
  *    o_part[b][h][p][:] = sum_t exp(s_t - m) v_t / l
  * Arrays are fp32 with num_partitions entries per (b, h); num_partitions must
- * be >= ceil(max_blocks_per_seq * 16 / P).  Entries of partitions that start
- * at or past N_b are not written.  partition_size must be given (no default).
+ * be >= ceil(max_blocks_per_seq * 16 / P).  Entries of partitions
+ * p >= ceil(N_b / P) are not written.  partition_size must be given (no
+ * default).  Work is dispatched longest partition first when num_seqs <= 256.
  * out == NULL: every non-empty partition writes its partial.  out != NULL
  * ([num_seqs][num_q_heads][head_dim], q_dtype): sequences with
  * N_b <= partition_size get their final attention output in `out` (zeros for
@@ -182,7 +185,8 @@ pkv_status pkv_paged_attn_decode_partials(void* out, float* m_part, float* l_par
  * pkv_paged_attn_decode_partials (derived from the running-max / running-sum
  * rule of online softmax, caojiahao2 section 3.2):
  *    M = max_p m_p;  w_p = l_p exp(m_p - M);  out = sum_p w_p o_p / sum_p w_p
- * over the ceil(N_b / partition_size) partitions of sequence b.  N_b == 0
+ * over the ceil(N_b / partition_size) partitions of sequence b (the merge
+ * does not depend on where the partition boundaries lie).  N_b == 0
  * writes zeros.  skip_single_partition != 0 leaves `out` of sequences with at
  * most one partition untouched (phase 1 with an output pointer finished
  * them).  out is [num_seqs][num_q_heads][head_dim] in out_dtype (F32|F16|BF16),

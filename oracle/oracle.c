@@ -228,8 +228,10 @@ int oracle_paged_decode(double* out, const void* q, int q_dtype, const void* k_c
     return status;
 }
 
-/* Split-context partials over partitions of `partition_size` tokens:
- * for partition p of sequence b, tokens [p*P, min((p+1)*P, N_b)).
+/* Split-context partials.  A context of N tokens is cut into
+ * count = ceil(N / P) partitions (P = partition_size) of equal length, rounded
+ * up to whole blocks: span = block_size * ceil(ceil(N / count) / block_size);
+ * partition p holds tokens [p*span, min((p+1)*span, N)).
  * m, l: double [B][Hq][NP]; o: double [B][Hq][NP][D].  Partitions with no
  * token get m = -inf, l = 0, o = 0.  The max score m is in natural-log units
  * of the score s = scale * <q, k>. */
@@ -253,8 +255,14 @@ int oracle_paged_partials(double* m_part, double* l_part, double* o_part, const 
         long r = i / num_partitions;
         int b = (int)(r / Hq), h = (int)(r % Hq);
         int n = context_lens[b];
-        int t0 = p * partition_size;
-        int t1 = t0 + partition_size < n ? t0 + partition_size : n;
+        int count = n > 0 ? (n + partition_size - 1) / partition_size : 0;
+        int span = 0;
+        if (count > 0) {
+            int per = (n + count - 1) / count;
+            span = (per + block_size - 1) / block_size * block_size;
+        }
+        int t0 = p < count ? p * span : n;
+        int t1 = t0 + span < n ? t0 + span : n;
         int rc = attend(&P, b, h, t0, t1, m_part + i, l_part + i, o_part + (size_t)i * D);
         if (rc != 0) {
 #pragma omp critical

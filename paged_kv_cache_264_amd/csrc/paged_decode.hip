@@ -158,13 +158,29 @@ template <Elem CE, int E> __device__ __forceinline__ void widen(const uint4& c, 
     }
 }
 
-// 16-byte streaming load: every K/V byte is read exactly once per call, so
-// the loads carry the non-temporal hint and do not displace reusable lines
-// (q, block tables) from the caches.
+// K/V tiles are read through raw buffer loads.  A buffer resource covers one
+// (block, kv head) tile; a load whose offset lies outside the resource returns
+// zeros without touching memory, so a block that does not exist (past the end
+// of a wave's run, or an invalid id) is "loaded" from a zero-sized resource.
+// Every load is then issued without a branch and the compiler waits for
+// exactly the block being consumed.  The loads carry the non-temporal hint:
+// each K/V byte is used once per call.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 ld16_stream(const char* p) {
-    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+constexpr int kBufferWord3 = 0x00020000;  // gfx9 family: 32-bit data format, raw access
+constexpr int kNonTemporal = 2;           // cache-policy bit "nt" of the load
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes,
+                                             kBufferWord3);
+}
+
+__device__ __forceinline__ uint4 ld16_stream(__amdgpu_buffer_rsrc_t r, int offset) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, kNonTemporal);
     return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float ld_f32(__amdgpu_buffer_rsrc_t r, int offset) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, offset, 0, 0));
 }
 
 // The K and V bytes (and INT8 scales) of one 16-token block of one kv head as
@@ -174,7 +190,7 @@ template <Elem CE, int D> struct BlockRegs {
     uint4 k[G::STEPS][G::U], v[G::STEPS][G::U];
     float ks[G::STEPS][G::U], vs[G::STEPS][G::U];
     int jb;   // logical block index in the sequence
-    bool ok;  // the block id was inside the pool
+    bool ok;  // the block exists and its id was inside the pool
 };
 
 template <Elem QE, Elem CE, int D, int GT>
@@ -187,6 +203,8 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
     __shared__ float s_m[NW][GT];
     __shared__ float s_l[NW][GT];
     __shared__ float s_acc[NW][GT][D];
+    __shared__ int2 s_key[kScheduleMaxSeqs];  // (partition span, item count) per sequence
+    __shared__ int s_pick[2];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -194,18 +212,56 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
     const int row = lane / L;   // token row inside a wave load
     const int slice = lane % L; // which E elements of the row this lane holds
 
-    // work-group -> (partition, tile, sequence); partitions vary fastest
     const int NP = a.num_partitions;
-    const int part = blockIdx.x % NP;
-    const int rest = blockIdx.x / NP;
-    const int tile = rest % a.n_tiles;
-    const int b = rest / a.n_tiles;
-
     const int P = a.partition_size;
-    int n = a.context_lens[b];
     const int n_cap = a.max_blocks_per_seq * kBlockSize;
-    n = n < 0 ? 0 : (n > n_cap ? n_cap : n);
-    const int n_parts = (n + P - 1) / P;
+    auto clamp_len = [&](int v) { return v < 0 ? 0 : (v > n_cap ? n_cap : v); };
+
+    // ---- which (sequence, partition, q-head tile) this work-group takes ----
+    // Natural order: partitions fastest, then tiles, then sequences.
+    // Longest-first order: work items (partition x tile) of all sequences
+    // sorted by partition length, longest first, so that the work dispatched
+    // last is the shortest and the ragged tail of a batch is small.  Every
+    // work-group ranks the sequences itself (one per thread, in LDS).
+    int b, part, tile;
+    if (a.longest_first) {
+        const int item = blockIdx.x / a.n_tiles;
+        tile = blockIdx.x % a.n_tiles;
+        int my_span = -1, cnt = 0;
+        if (tid < a.num_seqs) {
+            const int nn = clamp_len(a.context_lens[tid]);
+            const int c = partition_count(nn, P);
+            my_span = c > 0 ? partition_span(nn, c) : 0;
+            cnt = c > 0 ? c : 1;  // an empty sequence still takes one item: it writes zeros
+        }
+        s_key[tid] = make_int2(my_span, cnt);
+        if (tid == 0) s_pick[0] = -1;
+        __syncthreads();
+        if (tid < a.num_seqs) {
+            int start = 0;
+            for (int j = 0; j < a.num_seqs; ++j) {
+                const int2 kj = s_key[j];
+                if (kj.x > my_span || (kj.x == my_span && j < tid)) start += kj.y;
+            }
+            if (item >= start && item < start + cnt) {
+                s_pick[0] = tid;
+                s_pick[1] = item - start;
+            }
+        }
+        __syncthreads();
+        b = s_pick[0];
+        part = s_pick[1];
+        if (b < 0) return;  // beyond the last item (uniform)
+    } else {
+        part = blockIdx.x % NP;
+        const int rest = blockIdx.x / NP;
+        tile = rest % a.n_tiles;
+        b = rest / a.n_tiles;
+    }
+
+    const int n = clamp_len(a.context_lens[b]);
+    const int n_parts = partition_count(n, P);
+    const int span = n_parts > 0 ? partition_span(n, n_parts) : 0;
     const int Hq = a.num_q_heads;
     const int h0 = tile * GT;
     const int g = Hq / a.num_kv_heads;
@@ -234,13 +290,12 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
         for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
     }
 
-    const int t_begin = part * P;
-    const int t_end = min(n, t_begin + P);
+    const int t_begin = part * span;
+    const int t_end = min(n, t_begin + span);
     const int blk_begin = t_begin / kBlockSize;
     const int blk_end = (t_end + kBlockSize - 1) / kBlockSize;
     const int32_t* table = a.block_tables + (size_t)b * a.max_blocks_per_seq;
     const float c = a.scale_log2;
-    const size_t tile_elems = (size_t)kBlockSize * D;
 
     // Each wave takes a contiguous run of the partition's blocks.  Block ids
     // are wave-uniform scalar loads, issued one block ahead of their use; they
@@ -251,26 +306,34 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
     const int my0 = blk_begin + wave * per_wave;
     const int n_my = max(0, min(per_wave, blk_end - my0));
     const int32_t* my_ids = table + my0;
+    const int last = max(n_my - 1, 0);
+    constexpr int kTileBytes = kBlockSize * G::ROW;
 
-    // Loads are issued without branches (a bad id reads block 0 and is masked
-    // out), so the compiler can count them and wait only for the block being
-    // consumed.
+    // block i of this wave's run; i >= n_my (or a bad id) gives an empty tile
     auto load_block = [&](BlockRegs<CE, D>& r, int phys, int i) {
         r.jb = my0 + i;
-        r.ok = phys >= 0 && (int64_t)phys < a.num_blocks;  // a bad id contributes nothing
+        r.ok = i < n_my && phys >= 0 && (int64_t)phys < a.num_blocks;
         const size_t tile_idx = (size_t)(r.ok ? phys : 0) * a.num_kv_heads + kvh;
-        const char* kt = static_cast<const char*>(a.k_cache) + tile_idx * tile_elems * G::EB;
-        const char* vt = static_cast<const char*>(a.v_cache) + tile_idx * tile_elems * G::EB;
+        const int bytes = r.ok ? kTileBytes : 0;
+        const __amdgpu_buffer_rsrc_t kr =
+            tile_rsrc(static_cast<const char*>(a.k_cache) + tile_idx * kTileBytes, bytes);
+        const __amdgpu_buffer_rsrc_t vr =
+            tile_rsrc(static_cast<const char*>(a.v_cache) + tile_idx * kTileBytes, bytes);
+        __amdgpu_buffer_rsrc_t ksr, vsr;
+        if constexpr (kInt8) {
+            ksr = tile_rsrc(a.k_scale + tile_idx * kBlockSize, r.ok ? kBlockSize * 4 : 0);
+            vsr = tile_rsrc(a.v_scale + tile_idx * kBlockSize, r.ok ? kBlockSize * 4 : 0);
+        }
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int tok = (st * U + u) * R;  // first token of this wave load
-                r.k[st][u] = ld16_stream(kt + (size_t)tok * G::ROW + lane * 16);
-                r.v[st][u] = ld16_stream(vt + (size_t)tok * G::ROW + lane * 16);
+                r.k[st][u] = ld16_stream(kr, tok * G::ROW + lane * 16);
+                r.v[st][u] = ld16_stream(vr, tok * G::ROW + lane * 16);
                 if constexpr (kInt8) {
-                    r.ks[st][u] = a.k_scale[tile_idx * kBlockSize + tok + row];
-                    r.vs[st][u] = a.v_scale[tile_idx * kBlockSize + tok + row];
+                    r.ks[st][u] = ld_f32(ksr, (tok + row) * 4);
+                    r.vs[st][u] = ld_f32(vsr, (tok + row) * 4);
                 }
             }
         }
@@ -337,27 +400,19 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
 
     // Two blocks in flight per wave: the loads of block i+1 are issued before
     // block i is consumed, and the id of block i+2 is requested meanwhile.
-    // The steady-state loop body has no conditional load.
+    // Loads past the run are empty, so only the consumption of the second
+    // block of the last pair sits behind a branch.
     if (n_my > 0) {
         BlockRegs<CE, D> ra, rb;
-        const int last = n_my - 1;
         load_block(ra, my_ids[0], 0);
         int next_id = my_ids[min(1, last)];
-        int i = 0;
-        for (; i + 2 < n_my; i += 2) {
+        for (int i = 0; i < n_my; i += 2) {
             load_block(rb, next_id, i + 1);
-            next_id = my_ids[i + 2];
+            next_id = my_ids[min(i + 2, last)];
             compute_block(ra);
             load_block(ra, next_id, i + 2);
             next_id = my_ids[min(i + 3, last)];
-            compute_block(rb);
-        }
-        if (i + 1 < n_my) {
-            load_block(rb, next_id, i + 1);
-            compute_block(ra);
-            compute_block(rb);
-        } else {
-            compute_block(ra);
+            if (i + 1 < n_my) compute_block(rb);
         }
     }
 

@@ -32,8 +32,21 @@ struct DecodeArgs {
     int partition_size;  // tokens, multiple of 16
     int num_partitions;  // NP: partial-array stride
     int n_tiles;         // num_q_heads / heads_per_tile
+    int longest_first;   // schedule work longest-first (needs num_seqs <= kScheduleMaxSeqs)
     float scale_log2;    // softmax scale * log2(e)
 };
+
+// Sequences ranked in LDS by the work-group scheduler (one per thread).
+constexpr int kScheduleMaxSeqs = kDecodeThreads;
+
+// Balanced split of an n-token context into ceil(n / P) partitions: every
+// partition but the last spans `partition_span` tokens, a multiple of the
+// block size and at most P, and no partition is empty.
+__host__ __device__ inline int partition_count(int n, int P) { return n <= 0 ? 0 : (n + P - 1) / P; }
+__host__ __device__ inline int partition_span(int n, int count) {
+    const int per = (n + count - 1) / count;
+    return (per + kBlockSize - 1) / kBlockSize * kBlockSize;
+}
 
 // Phase 1 of split-context decode.  With a.out set, sequences whose context
 // fits in one partition (or is empty) get their final output in a.out and

@@ -328,3 +328,14 @@ def test_workspace_reuse_across_shapes(pkv):
     for i, (lens, Hq, Hkv, D, P) in enumerate(shapes * 2):
         batch = W.make_batch(cfg=_cfg("f16", "f16", D, Hq, Hkv, lens, seed=i), device="cuda")
         _check_step(pkv, batch, partition_size=P)
+
+
+def test_large_batch_natural_order(pkv):
+    """More sequences than the longest-first scheduler ranks: natural order."""
+    g = np.random.default_rng(31)
+    lens = [int(x) for x in g.integers(0, 300, size=300)]
+    batch = W.make_batch(cfg=_cfg("f16", "f16", 64, 4, 2, lens, seed=31), device="cuda")
+    _check_step(pkv, batch, partition_size=64)
+    batch = W.make_batch(cfg=_cfg("bf16", "i8", 128, 8, 8, lens[:257], seed=32), device="cuda")
+    gpu_populate(pkv, batch)
+    _check_step(pkv, batch)

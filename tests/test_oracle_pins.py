@@ -262,11 +262,14 @@ def test_partials_merge_equals_full(P):
                                     NP)
     merged = oracle.merge_partials(m, l, o)
     np.testing.assert_allclose(merged, full, rtol=0, atol=1e-13)
-    # partitions that start past the context are empty
+    # ceil(N/P) balanced partitions, none of them empty; the rest are empty
     lens = b.context_lens.numpy()
     for s in range(b.B):
+        count = -(-int(lens[s]) // P)
         for p in range(NP):
-            if p * P >= lens[s]:
+            if p < count:
+                assert l[s, :, p].min() >= 1.0
+            else:
                 assert l[s, :, p].max() == 0.0 and np.isneginf(m[s, :, p]).all()
 
 
