@@ -53,6 +53,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", default="llama7b", choices=sorted(WORKLOAD_NAMES))
     p.add_argument("--partition-size", type=int, default=None)
+    p.add_argument("--step", choices=["fused", "separate"], default="fused",
+                   help="fused: one pkv_paged_attn_decode_append call per step; separate: "
+                        "pkv_kv_cache_write, then the two decode phases")
     p.add_argument("--seed", type=int, default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -73,7 +76,7 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
 
 
-def traffic_for(config: str, alg_bytes: int):
+def traffic_for(key: str, alg_bytes: int):
     """HBM bytes per decode launch from committed rocprofv3 counter runs, if
     they were taken on the current kernel source."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -81,7 +84,7 @@ def traffic_for(config: str, alg_bytes: int):
         return None, None
     with open(path) as f:
         data = json.load(f)
-    rec = data.get(config)
+    rec = data.get(key)
     if not rec or rec.get("kernel_sha") != kernel_sha():
         return None, None
     t = float(rec["fetch_bytes_per_launch"]) + float(rec["write_bytes_per_launch"])
@@ -124,10 +127,17 @@ def main():
     int8 = cfg["cache"] == "i8"
     dec_bytes = W.algorithmic_bytes(lens, batch.Hq, batch.Hkv, batch.D, e_kv, e_q, int8)
     n_new = int((batch.slot_new >= 0).sum())
-    # cache write: read new K/V rows, write them (codes + scales for INT8) and the slots
-    write_bytes = n_new * batch.Hkv * 2 * (batch.D * e_q + batch.D * e_kv + (4 if int8 else 0)) \
-        + n_new * 8
-    step_bytes = dec_bytes + write_bytes
+    # the new rows written into the cache (codes + scales for INT8)
+    store_bytes = n_new * batch.Hkv * 2 * (batch.D * e_kv + (4 if int8 else 0))
+    if args.step == "fused":
+        # the new token's K/V are read from the input instead of the cache: the
+        # decode byte count already holds them; add the stores
+        launch_bytes = dec_bytes + store_bytes
+        step_bytes = launch_bytes
+    else:
+        launch_bytes = dec_bytes
+        # separate cache write: read the new rows, store them, read the slots
+        step_bytes = dec_bytes + store_bytes + n_new * batch.Hkv * 2 * batch.D * e_q + n_new * 8
     kv_tokens = int(lens.sum())
     stream = torch.cuda.current_stream()
 
@@ -135,7 +145,20 @@ def main():
     # that HIP events bracket the decode kernel alone: cache write, phase 1
     # (split-context decode; single-partition sequences finish here), phase 2
     # (merge of the longer ones).
-    def step(ev0=None, ev1=None):
+    ws = torch.empty(pkv.decode_workspace_size(batch.B, batch.Hq, batch.Hkv, batch.D, mbs, P_eff),
+                     dtype=torch.uint8, device="cuda")
+
+    def step_fused(ev0=None, ev1=None):
+        if ev0 is not None:
+            ev0.record(stream)
+        pkv.paged_attn_decode_append(batch.q, batch.k_new, batch.v_new, batch.k_cache,
+                                     batch.v_cache, batch.block_tables, batch.context_lens,
+                                     batch.scale, out=out, k_scale=batch.k_scale,
+                                     v_scale=batch.v_scale, partition_size=P_eff, workspace=ws)
+        if ev1 is not None:
+            ev1.record(stream)
+
+    def step_separate(ev0=None, ev1=None):
         pkv.kv_cache_write(batch.k_new, batch.v_new, batch.k_cache, batch.v_cache,
                            batch.slot_new, batch.k_scale, batch.v_scale)
         if ev0 is not None:
@@ -149,6 +172,8 @@ def main():
         if NP > 1:
             pkv.paged_attn_reduce(*partials, batch.context_lens, P_eff, out=out,
                                   skip_single_partition=True)
+
+    step = step_fused if args.step == "fused" else step_separate
 
     for _ in range(args.warmup):
         step()
@@ -167,9 +192,9 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     dec_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
     dec_avg_ms = float(np.mean(dec_ms))
-    achieved = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
+    achieved = launch_bytes / (dec_avg_ms * 1e-3) / 1e9
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    traffic, traffic_ratio = traffic_for(args.config, dec_bytes)
+    traffic, traffic_ratio = traffic_for(f"{args.config}/{args.step}", launch_bytes)
 
     result = {
         "metric": METRIC,
@@ -193,11 +218,13 @@ def main():
                              f"{cfg['ctx'][0]} x {len(cfg['ctx'])}"),
             "sum_context_tokens": kv_tokens, "q_dtype": cfg["dtype"], "kv_dtype": cfg["cache"],
             "partition_size": P_eff, "seed": batch.seed, "parallelism": "single-gpu",
+            "step": args.step,
         },
         "kv_tokens_per_s": round(kv_tokens / (ms_per_step * 1e-3), 1),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "decode_kernel_us": round(dec_avg_ms * 1e3, 2),
         "decode_alg_bytes": dec_bytes,
+        "launch_alg_bytes": launch_bytes,
         "step_alg_bytes": step_bytes,
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -205,8 +232,11 @@ def main():
             "traffic": None if traffic is None else int(traffic),
             "traffic_unit": "bytes/launch",
             "traffic_over_alg": None if traffic_ratio is None else round(traffic_ratio, 4),
-            "kernel": "paged_decode_kernel", "kernel_sha": kernel_sha(),
-            "launches_per_step": {"kv_cache_write_kernel": 1, "paged_decode_kernel": 1,
+            "kernel": "paged_decode_kernel" + (" + paged_reduce_kernel (events span both)"
+                                                if (NP > 1 and args.step == "fused") else ""),
+            "kernel_sha": kernel_sha(),
+            "launches_per_step": {"kv_cache_write_kernel": 0 if args.step == "fused" else 1,
+                                  "paged_decode_kernel": 1,
                                   "paged_reduce_kernel": 1 if NP > 1 else 0},
         },
     }

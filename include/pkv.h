@@ -150,6 +150,30 @@ pkv_status pkv_paged_attn_decode(void* out, const void* q, const void* k_cache,
                                  pkv_dtype cache_dtype, hipStream_t stream);
 
 /*
+ * One decode step in one call: append each sequence's new token, then attend
+ * (the cache append of juejin "LLM Engineer's Handbook", section "KV cache",
+ * fused with the attention above).  For every sequence with N_b =
+ * context_lens[b] >= 1, position N_b - 1 is the new token: its rows
+ * k_new[b], v_new[b] ([num_seqs][num_kv_heads][head_dim], q_dtype) are
+ * written into slot (block_tables[b][(N_b - 1) / 16], (N_b - 1) % 16) —
+ * quantized exactly as pkv_kv_cache_write does for an INT8 cache — and the
+ * attention over positions 0..N_b-1 uses them.  Result and cache contents are
+ * those of pkv_kv_cache_write with those slots followed by
+ * pkv_paged_attn_decode; the attention does not wait for the stored copy.
+ * Other arguments as for pkv_paged_attn_decode.
+ */
+pkv_status pkv_paged_attn_decode_append(void* out, const void* q, const void* k_new,
+                                        const void* v_new, void* k_cache, void* v_cache,
+                                        float* k_scale, float* v_scale,
+                                        const int32_t* block_tables, int max_blocks_per_seq,
+                                        const int32_t* context_lens, int num_seqs,
+                                        int num_q_heads, int num_kv_heads, int head_dim,
+                                        int block_size, int64_t num_blocks, float scale,
+                                        int partition_size, void* workspace,
+                                        size_t workspace_bytes, pkv_dtype q_dtype,
+                                        pkv_dtype cache_dtype, hipStream_t stream);
+
+/*
  * Phase 1 of the split-context decode: per-partition partial results (for a
  * caller that merges them itself, e.g. partitions computed on several
  * devices, or that times the phases apart).  The N_b = context_lens[b] tokens

@@ -15,7 +15,8 @@ import os
 import torch
 
 __all__ = [
-    "kv_cache_write", "paged_attn_decode", "paged_attn_decode_partials", "paged_attn_reduce",
+    "kv_cache_write", "paged_attn_decode", "paged_attn_decode_append",
+    "paged_attn_decode_partials", "paged_attn_reduce",
     "decode_workspace_size", "default_partition_size", "num_partitions",
     "library_path", "PkvError", "BLOCK_SIZE",
 ]
@@ -61,6 +62,9 @@ def _load():
     L.pkv_paged_attn_decode.argtypes = [P, P, P, P, P, P, P, I, P, I, I, I, I, I, I64, F, I, P,
                                         SZ, I, I, P]
     L.pkv_paged_attn_decode.restype = I
+    L.pkv_paged_attn_decode_append.argtypes = [P, P, P, P, P, P, P, P, P, I, P, I, I, I, I, I,
+                                               I64, F, I, P, SZ, I, I, P]
+    L.pkv_paged_attn_decode_append.restype = I
     L.pkv_paged_attn_decode_partials.argtypes = [P, P, P, P, P, P, P, P, P, P, I, P, I, I, I, I,
                                                  I, I64, F, I, I, I, I, P]
     L.pkv_paged_attn_decode_partials.restype = I
@@ -200,6 +204,36 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, ou
         _ptr(block_tables), mbs, _ptr(context_lens), B, Hq, Hkv, D, bs, NB, float(scale),
         int(partition_size), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _code(q.dtype, "q"), _code(k_cache.dtype, "k_cache"), _stream(q))
+    _check_status(rc)
+    return out
+
+
+def paged_attn_decode_append(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,
+                             out=None, k_scale=None, v_scale=None, partition_size=0,
+                             workspace=None):
+    """One decode step: write each sequence's new token (k_new, v_new
+    [B][Hkv][D], q dtype) at position context_len-1, then attend."""
+    B, Hq, D, NB, Hkv, bs = _decode_common(q, k_cache, v_cache, block_tables, context_lens,
+                                           k_scale, v_scale)
+    _dev(k_new, "k_new", dtype=q.dtype, ndim=3)
+    _dev(v_new, "v_new", dtype=q.dtype, ndim=3)
+    if tuple(k_new.shape) != (B, Hkv, D) or v_new.shape != k_new.shape:
+        raise ValueError("k_new and v_new must be [num_seqs][num_kv_heads][head_dim]")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", dtype=q.dtype, ndim=3)
+    mbs = block_tables.shape[1]
+    need = decode_workspace_size(B, Hq, Hkv, D, mbs, partition_size)
+    if workspace is None:
+        workspace = _workspace(q.device, need)
+    else:
+        _dev(workspace, "workspace")
+    rc = _load().pkv_paged_attn_decode_append(
+        _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+        _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), mbs, _ptr(context_lens), B, Hq, Hkv,
+        D, bs, NB, float(scale), int(partition_size), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _code(q.dtype, "q"),
+        _code(k_cache.dtype, "k_cache"), _stream(q))
     _check_status(rc)
     return out
 

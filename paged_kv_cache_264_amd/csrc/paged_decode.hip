@@ -136,6 +136,35 @@ template <Elem QE> struct QSlice<QE, Elem::I8, 16> {
     }
 };
 
+// Component-wise select (keeps the 16-byte chunks in registers).
+__device__ __forceinline__ uint4 select4(bool c, const uint4& a, const uint4& b) {
+    return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
+}
+
+// INT8 codes of one row of the new token: this lane's 16 elements, whose row
+// spans L lanes.  Same arithmetic as the quantizing cache write: exact
+// absolute maximum, s = amax / 127 (IEEE division), round half to even.
+template <int L>
+__device__ __forceinline__ uint4 quantize16(const float (&x)[16], float& scale_out) {
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+    amax = group_max<L>(amax);
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    float s = 0.f;
+    if (amax > 0.f) {
+        s = amax / 127.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float cde = __builtin_rintf(x[i] / s);
+            cde = fminf(fmaxf(cde, -127.0f), 127.0f);
+            w[i / 4] |= ((uint32_t)(int32_t)cde & 0xffu) << (8 * (i % 4));
+        }
+    }
+    scale_out = s;
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // widen one 16-byte V chunk to E floats
 template <Elem CE, int E> __device__ __forceinline__ void widen(const uint4& c, float (&x)[E]) {
     const uint32_t w[4] = {c.x, c.y, c.z, c.w};
@@ -297,6 +326,53 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
     const int32_t* table = a.block_tables + (size_t)b * a.max_blocks_per_seq;
     const float c = a.scale_log2;
 
+    // ---- append of the step's new token (position n-1), when given --------
+    // The work-group owning the last partition takes the new K/V row from the
+    // input (quantized like the cache write for an INT8 cache), stores it
+    // into its slot (one writer per kv head) and uses it in registers, so the
+    // attention never waits for the stored copy.
+    const bool has_new = a.k_new != nullptr && n > 0 && t_end == n;
+    const int new_jb = (n - 1) / kBlockSize;
+    const int new_off = (n - 1) % kBlockSize;
+    uint4 knew = make_uint4(0, 0, 0, 0), vnew = make_uint4(0, 0, 0, 0);
+    float knew_s = 0.f, vnew_s = 0.f;
+    if (has_new) {
+        const size_t src = ((size_t)b * a.num_kv_heads + kvh) * D + (size_t)slice * E;
+        if constexpr (!kInt8) {
+            knew = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + src * G::EB);
+            vnew = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + src * G::EB);
+        } else {
+            float xk[16], xv[16];
+            const uint4* pk = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k_new) + src);
+            const uint4* pv = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v_new) + src);
+            const uint4 k0 = pk[0], k1 = pk[1], v0 = pv[0], v1 = pv[1];
+            const uint32_t wk[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+            const uint32_t wv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                xk[2 * i] = QE == Elem::F16 ? lo_h(wk[i]) : lo_bf(wk[i]);
+                xk[2 * i + 1] = QE == Elem::F16 ? hi_h(wk[i]) : hi_bf(wk[i]);
+                xv[2 * i] = QE == Elem::F16 ? lo_h(wv[i]) : lo_bf(wv[i]);
+                xv[2 * i + 1] = QE == Elem::F16 ? hi_h(wv[i]) : hi_bf(wv[i]);
+            }
+            knew = quantize16<L>(xk, knew_s);
+            vnew = quantize16<L>(xv, vnew_s);
+        }
+        const int phys = table[new_jb];
+        if (h0 % g == 0 && wave == 0 && row == 0 && phys >= 0 && (int64_t)phys < a.num_blocks) {
+            const size_t trow = ((size_t)phys * a.num_kv_heads + kvh) * kBlockSize + new_off;
+            const size_t dst = trow * D + (size_t)slice * E;  // elements of the cache type
+            *reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.k_cache)) + dst * G::EB) = knew;
+            *reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.v_cache)) + dst * G::EB) = vnew;
+            if constexpr (kInt8) {
+                if (slice == 0) {
+                    const_cast<float*>(a.k_scale)[trow] = knew_s;
+                    const_cast<float*>(a.v_scale)[trow] = vnew_s;
+                }
+            }
+        }
+    }
+
     // Each wave takes a contiguous run of the partition's blocks.  Block ids
     // are wave-uniform scalar loads, issued one block ahead of their use; they
     // are counted apart from the vector K/V loads (lgkmcnt vs vmcnt), so
@@ -339,8 +415,23 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
         }
     };
 
-    auto compute_block = [&](const BlockRegs<CE, D>& r) {
+    auto compute_block = [&](BlockRegs<CE, D>& r) {
         const int jb = r.jb;
+        if (has_new && jb == new_jb) {  // the new token's row comes from registers
+#pragma unroll
+            for (int st = 0; st < STEPS; ++st) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const bool mine = (st * U + u) * R + row == new_off;
+                    r.k[st][u] = select4(mine, knew, r.k[st][u]);
+                    r.v[st][u] = select4(mine, vnew, r.v[st][u]);
+                    if constexpr (kInt8) {
+                        r.ks[st][u] = mine ? knew_s : r.ks[st][u];
+                        r.vs[st][u] = mine ? vnew_s : r.vs[st][u];
+                    }
+                }
+            }
+        }
         const bool full = r.ok && (jb + 1) * kBlockSize <= n;
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {

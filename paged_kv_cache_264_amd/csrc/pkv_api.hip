@@ -202,16 +202,19 @@ pkv_status pkv_kv_cache_write(const void* k, const void* v, void* k_cache, void*
         "kv_cache_write launch");
 }
 
-pkv_status pkv_paged_attn_decode_partials(void* out, float* m_part, float* l_part, float* o_part,
-                                          const void* q, const void* k_cache, const void* v_cache,
-                                          const float* k_scale, const float* v_scale,
-                                          const int32_t* block_tables, int max_blocks_per_seq,
-                                          const int32_t* context_lens, int num_seqs,
-                                          int num_q_heads, int num_kv_heads, int head_dim,
-                                          int block_size, int64_t num_blocks, float scale,
-                                          int partition_size, int num_partitions_,
-                                          pkv_dtype q_dtype, pkv_dtype cache_dtype,
-                                          hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Phase 1, optionally with the append of each sequence's new token.
+pkv_status decode_phase1(void* out, float* m_part, float* l_part, float* o_part, const void* q,
+                         const void* k_new, const void* v_new, const void* k_cache,
+                         const void* v_cache, const float* k_scale, const float* v_scale,
+                         const int32_t* block_tables, int max_blocks_per_seq,
+                         const int32_t* context_lens, int num_seqs, int num_q_heads,
+                         int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+                         float scale, int partition_size, int num_partitions_, pkv_dtype q_dtype,
+                         pkv_dtype cache_dtype, hipStream_t stream) {
     pkv_status s = check_decode(q, k_cache, v_cache, k_scale, v_scale, block_tables,
                                 max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
                                 num_kv_heads, head_dim, block_size, num_blocks, q_dtype,
@@ -234,12 +237,78 @@ pkv_status pkv_paged_attn_decode_partials(void* out, float* m_part, float* l_par
                                   num_kv_heads, num_blocks, scale, partition_size,
                                   num_partitions_, num_q_heads / gt);
     a.out = out;
+    a.k_new = k_new;
+    a.v_new = v_new;
     a.m_part = m_part;
     a.l_part = l_part;
     a.o_part = o_part;
     return hip_status(pkv::launch_paged_decode(a, (int)q_dtype, (int)cache_dtype, head_dim, gt,
                                                stream),
-                      "paged_attn_decode_partials launch");
+                      "paged decode launch");
+}
+
+// Phase 1 with direct output, then the merge of sequences with > 1 partition.
+pkv_status decode_both_phases(void* out, const void* q, const void* k_new, const void* v_new,
+                              const void* k_cache, const void* v_cache, const float* k_scale,
+                              const float* v_scale, const int32_t* block_tables,
+                              int max_blocks_per_seq, const int32_t* context_lens, int num_seqs,
+                              int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                              int64_t num_blocks, float scale, int partition_size,
+                              void* workspace, size_t workspace_bytes, pkv_dtype q_dtype,
+                              pkv_dtype cache_dtype, hipStream_t stream) {
+    pkv_status s = check_decode(q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                                max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                                num_kv_heads, head_dim, block_size, num_blocks, q_dtype,
+                                cache_dtype);
+    if (s != PKV_OK) return s;
+    if (partition_size < 0 || partition_size % pkv::kBlockSize != 0)
+        return fail(PKV_ERR_SHAPE, "partition_size %d is not 0 or a positive multiple of 16",
+                    partition_size);
+    if (num_seqs == 0) return ok();
+    if (!out) return fail(PKV_ERR_NULL, "out is required");
+    if (!aligned16(out)) return fail(PKV_ERR_SHAPE, "out must be 16-byte aligned");
+    const int P = partition_size ? partition_size
+                                 : pkv_default_partition_size(num_seqs, num_q_heads, num_kv_heads,
+                                                              max_blocks_per_seq);
+    const int NP = num_partitions(max_blocks_per_seq, P);
+    const WorkspaceLayout w = layout(num_seqs, num_q_heads, head_dim, NP);
+    if (!workspace || workspace_bytes < w.total)
+        return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+        return fail(PKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    char* ws = static_cast<char*>(workspace);
+    float* m = reinterpret_cast<float*>(ws + w.m_off);
+    float* l = reinterpret_cast<float*>(ws + w.l_off);
+    float* o = reinterpret_cast<float*>(ws + w.o_off);
+    s = decode_phase1(out, m, l, o, q, k_new, v_new, k_cache, v_cache, k_scale, v_scale,
+                      block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                      num_kv_heads, head_dim, block_size, num_blocks, scale, P, NP, q_dtype,
+                      cache_dtype, stream);
+    if (s != PKV_OK) return s;
+    if (NP == 1) return ok();  // every sequence was finished in phase 1
+    return pkv_paged_attn_reduce(out, m, l, o, context_lens, num_seqs, num_q_heads, head_dim, P,
+                                 NP, 1, q_dtype, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_paged_attn_decode_partials(void* out, float* m_part, float* l_part, float* o_part,
+                                          const void* q, const void* k_cache, const void* v_cache,
+                                          const float* k_scale, const float* v_scale,
+                                          const int32_t* block_tables, int max_blocks_per_seq,
+                                          const int32_t* context_lens, int num_seqs,
+                                          int num_q_heads, int num_kv_heads, int head_dim,
+                                          int block_size, int64_t num_blocks, float scale,
+                                          int partition_size, int num_partitions_,
+                                          pkv_dtype q_dtype, pkv_dtype cache_dtype,
+                                          hipStream_t stream) {
+    return decode_phase1(out, m_part, l_part, o_part, q, nullptr, nullptr, k_cache, v_cache,
+                         k_scale, v_scale, block_tables, max_blocks_per_seq, context_lens,
+                         num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                         scale, partition_size, num_partitions_, q_dtype, cache_dtype, stream);
 }
 
 pkv_status pkv_paged_attn_reduce(void* out, const float* m_part, const float* l_part,
@@ -272,39 +341,32 @@ pkv_status pkv_paged_attn_decode(void* out, const void* q, const void* k_cache,
                                  int64_t num_blocks, float scale, int partition_size,
                                  void* workspace, size_t workspace_bytes, pkv_dtype q_dtype,
                                  pkv_dtype cache_dtype, hipStream_t stream) {
-    pkv_status s = check_decode(q, k_cache, v_cache, k_scale, v_scale, block_tables,
-                                max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
-                                num_kv_heads, head_dim, block_size, num_blocks, q_dtype,
-                                cache_dtype);
-    if (s != PKV_OK) return s;
-    if (partition_size < 0 || partition_size % pkv::kBlockSize != 0)
-        return fail(PKV_ERR_SHAPE, "partition_size %d is not 0 or a positive multiple of 16",
-                    partition_size);
-    if (num_seqs == 0) return ok();
-    if (!out) return fail(PKV_ERR_NULL, "out is required");
-    if (!aligned16(out)) return fail(PKV_ERR_SHAPE, "out must be 16-byte aligned");
-    const int P = partition_size ? partition_size
-                                 : pkv_default_partition_size(num_seqs, num_q_heads, num_kv_heads,
-                                                              max_blocks_per_seq);
-    const int NP = num_partitions(max_blocks_per_seq, P);
-    const WorkspaceLayout w = layout(num_seqs, num_q_heads, head_dim, NP);
-    if (!workspace || workspace_bytes < w.total)
-        return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
-                    workspace ? workspace_bytes : (size_t)0);
-    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
-        return fail(PKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-    char* ws = static_cast<char*>(workspace);
-    float* m = reinterpret_cast<float*>(ws + w.m_off);
-    float* l = reinterpret_cast<float*>(ws + w.l_off);
-    float* o = reinterpret_cast<float*>(ws + w.o_off);
-    s = pkv_paged_attn_decode_partials(out, m, l, o, q, k_cache, v_cache, k_scale, v_scale,
-                                       block_tables, max_blocks_per_seq, context_lens, num_seqs,
-                                       num_q_heads, num_kv_heads, head_dim, block_size,
-                                       num_blocks, scale, P, NP, q_dtype, cache_dtype, stream);
-    if (s != PKV_OK) return s;
-    if (NP == 1) return ok();  // every sequence was finished in phase 1
-    return pkv_paged_attn_reduce(out, m, l, o, context_lens, num_seqs, num_q_heads, head_dim, P,
-                                 NP, 1, q_dtype, stream);
+    return decode_both_phases(out, q, nullptr, nullptr, k_cache, v_cache, k_scale, v_scale,
+                              block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                              num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                              partition_size, workspace, workspace_bytes, q_dtype, cache_dtype,
+                              stream);
+}
+
+pkv_status pkv_paged_attn_decode_append(void* out, const void* q, const void* k_new,
+                                        const void* v_new, void* k_cache, void* v_cache,
+                                        float* k_scale, float* v_scale,
+                                        const int32_t* block_tables, int max_blocks_per_seq,
+                                        const int32_t* context_lens, int num_seqs,
+                                        int num_q_heads, int num_kv_heads, int head_dim,
+                                        int block_size, int64_t num_blocks, float scale,
+                                        int partition_size, void* workspace,
+                                        size_t workspace_bytes, pkv_dtype q_dtype,
+                                        pkv_dtype cache_dtype, hipStream_t stream) {
+    if (num_seqs > 0 && (!k_new || !v_new))
+        return fail(PKV_ERR_NULL, "k_new and v_new are required");
+    if (num_seqs > 0 && (!aligned16(k_new) || !aligned16(v_new)))
+        return fail(PKV_ERR_SHAPE, "k_new and v_new must be 16-byte aligned");
+    return decode_both_phases(out, q, k_new, v_new, k_cache, v_cache, k_scale, v_scale,
+                              block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                              num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                              partition_size, workspace, workspace_bytes, q_dtype, cache_dtype,
+                              stream);
 }
 
 }  // extern "C"

@@ -21,6 +21,8 @@ struct DecodeArgs {
     const float* v_scale;
     const int32_t* block_tables;
     const int32_t* context_lens;
+    const void* k_new;   // [B][Hkv][D] new token of each sequence (q dtype), or nullptr
+    const void* v_new;
     float* m_part;       // [B][Hq][NP]
     float* l_part;       // [B][Hq][NP]
     float* o_part;       // [B][Hq][NP][D]

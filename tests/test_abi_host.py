@@ -40,7 +40,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) >= 8
+    assert len(names) >= 9
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
                          check=True).stdout
     exported = set(re.findall(r"\sT\s(\S+)", out))
@@ -172,3 +172,24 @@ def test_binding_rejects_host_tensors():
         pkv.paged_attn_decode(q, torch.zeros((4, 4, 16, 64)), torch.zeros((4, 4, 16, 64)),
                               torch.zeros((1, 4), dtype=torch.int32),
                               torch.zeros((1,), dtype=torch.int32), 0.125)
+
+
+def test_append_argument_errors(lib):
+    f = lib.pkv_paged_attn_decode_append
+    I = ctypes.c_int
+    f.argtypes = [P, P, P, P, P, P, P, P, P, I, P, I, I, I, I, I, ctypes.c_int64, ctypes.c_float,
+                  I, P, ctypes.c_size_t, I, I, P]
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 8, FAKE, 2, 8, 2, 128, 16, 10,
+            0.1, 0, FAKE, 1 << 30, F16, F16, None]
+
+    def call(i, val):
+        a = list(base)
+        a[i] = val
+        return f(*a)
+
+    assert call(2, None) == ENULL           # k_new
+    assert call(3, None) == ENULL           # v_new
+    assert call(2, ctypes.c_void_p(0x1002)) == ESHAPE
+    assert call(14, 96) == EUNSUP
+    assert call(22, I8) == ENULL            # INT8 without scales
+    assert call(11, 0) == OK                # empty batch

@@ -339,3 +339,45 @@ def test_large_batch_natural_order(pkv):
     batch = W.make_batch(cfg=_cfg("bf16", "i8", 128, 8, 8, lens[:257], seed=32), device="cuda")
     gpu_populate(pkv, batch)
     _check_step(pkv, batch)
+
+
+@pytest.mark.parametrize("dtype,cache", PAIRS)
+@pytest.mark.parametrize("D,Hq,Hkv,P", [(128, 8, 8, 0), (64, 16, 2, 32), (256, 4, 1, 64)])
+def test_decode_append_matches_write_then_decode(pkv, dtype, cache, D, Hq, Hkv, P):
+    """The fused step equals the cache write of the new tokens followed by the
+    decode: cache bytes bit-exact against the oracle's write, outputs within
+    the dtype bound."""
+    lens = [1, 16, 17, 300, 33, 0, 129]
+    batch = W.make_batch(cfg=_cfg(dtype, cache, D, Hq, Hkv, lens, seed=D + P), device="cuda")
+    gpu_populate(pkv, batch)
+    view = OracleView(batch, np.arange(batch.B))
+    out = pkv.paged_attn_decode_append(batch.q, batch.k_new, batch.v_new, batch.k_cache,
+                                       batch.v_cache, batch.block_tables, batch.context_lens,
+                                       batch.scale, k_scale=batch.k_scale, v_scale=batch.v_scale,
+                                       partition_size=P)
+    torch.cuda.synchronize()
+    view.write_new_tokens(batch)
+    ref = view.decode()
+    err = max_abs_err(out, ref)
+    print(f"[append] {dtype}/{cache} D={D} Hq={Hq} Hkv={Hkv} P={P} max_abs_err={err:.3e}")
+    assert torch.isfinite(out.float()).all()
+    assert err <= tol_for(dtype, cache)
+    idx = torch.from_numpy(view.block_ids).cuda()
+    assert np.array_equal(host(batch.k_cache[idx]).view(np.uint8), view.k_cache.view(np.uint8)) \
+        if cache != "i8" else True
+    # every slot the oracle wrote holds the same bytes on the GPU
+    for i, (s_, n) in enumerate(zip(view.seqs, view.context_lens)):
+        if n == 0:
+            continue
+        t = n - 1
+        blk_o = view.block_tables[i, t // BS]
+        blk_g = int(batch.layout.block_tables[s_, t // BS])
+        assert np.array_equal(host(batch.k_cache[blk_g, :, t % BS]).view(np.uint8),
+                              view.k_cache[blk_o, :, t % BS].view(np.uint8))
+        assert np.array_equal(host(batch.v_cache[blk_g, :, t % BS]).view(np.uint8),
+                              view.v_cache[blk_o, :, t % BS].view(np.uint8))
+        if cache == "i8":
+            assert np.array_equal(host(batch.k_scale[blk_g, :, t % BS]).view(np.uint32),
+                                  view.k_scale[blk_o, :, t % BS].view(np.uint32))
+            assert np.array_equal(host(batch.v_scale[blk_g, :, t % BS]).view(np.uint32),
+                                  view.v_scale[blk_o, :, t % BS].view(np.uint32))
