@@ -136,11 +136,6 @@ template <Elem QE> struct QSlice<QE, Elem::I8, 16> {
     }
 };
 
-// Component-wise select (keeps the 16-byte chunks in registers).
-__device__ __forceinline__ uint4 select4(bool c, const uint4& a, const uint4& b) {
-    return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
-}
-
 // INT8 codes of one row of the new token: this lane's 16 elements, whose row
 // spans L lanes.  Same arithmetic as the quantizing cache write: exact
 // absolute maximum, s = amax / 127 (IEEE division), round half to even.
@@ -221,6 +216,21 @@ template <Elem CE, int D> struct BlockRegs {
     int jb;   // logical block index in the sequence
     bool ok;  // the block exists and its id was inside the pool
 };
+
+// Blocks in flight per wave (measured on MI355X: a third block in flight did
+// not help any tile size; it is kept selectable for experiments).
+#ifndef PKV_LAZY_RESCALE
+#define PKV_LAZY_RESCALE 1
+#endif
+#ifndef PKV_DEPTH_SMALL_TILE
+#define PKV_DEPTH_SMALL_TILE 2
+#endif
+#ifndef PKV_DEPTH_LARGE_TILE
+#define PKV_DEPTH_LARGE_TILE 2
+#endif
+template <Elem CE, int GT>
+constexpr int kPipelineDepth =
+    (GT == 4 && ElemInfo<CE>::bytes <= 2) ? PKV_DEPTH_LARGE_TILE : PKV_DEPTH_SMALL_TILE;
 
 template <Elem QE, Elem CE, int D, int GT>
 __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs a) {
@@ -327,51 +337,12 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
     const float c = a.scale_log2;
 
     // ---- append of the step's new token (position n-1), when given --------
-    // The work-group owning the last partition takes the new K/V row from the
-    // input (quantized like the cache write for an INT8 cache), stores it
-    // into its slot (one writer per kv head) and uses it in registers, so the
-    // attention never waits for the stored copy.
+    // The work-group owning the last partition leaves the new token's slot
+    // out of the block loop and folds the token in afterwards from the input
+    // row (quantized like the cache write for an INT8 cache), which it also
+    // stores into the slot.  Nothing of it is live during the loop.
     const bool has_new = a.k_new != nullptr && n > 0 && t_end == n;
-    const int new_jb = (n - 1) / kBlockSize;
-    const int new_off = (n - 1) % kBlockSize;
-    uint4 knew = make_uint4(0, 0, 0, 0), vnew = make_uint4(0, 0, 0, 0);
-    float knew_s = 0.f, vnew_s = 0.f;
-    if (has_new) {
-        const size_t src = ((size_t)b * a.num_kv_heads + kvh) * D + (size_t)slice * E;
-        if constexpr (!kInt8) {
-            knew = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + src * G::EB);
-            vnew = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + src * G::EB);
-        } else {
-            float xk[16], xv[16];
-            const uint4* pk = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k_new) + src);
-            const uint4* pv = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v_new) + src);
-            const uint4 k0 = pk[0], k1 = pk[1], v0 = pv[0], v1 = pv[1];
-            const uint32_t wk[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-            const uint32_t wv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                xk[2 * i] = QE == Elem::F16 ? lo_h(wk[i]) : lo_bf(wk[i]);
-                xk[2 * i + 1] = QE == Elem::F16 ? hi_h(wk[i]) : hi_bf(wk[i]);
-                xv[2 * i] = QE == Elem::F16 ? lo_h(wv[i]) : lo_bf(wv[i]);
-                xv[2 * i + 1] = QE == Elem::F16 ? hi_h(wv[i]) : hi_bf(wv[i]);
-            }
-            knew = quantize16<L>(xk, knew_s);
-            vnew = quantize16<L>(xv, vnew_s);
-        }
-        const int phys = table[new_jb];
-        if (h0 % g == 0 && wave == 0 && row == 0 && phys >= 0 && (int64_t)phys < a.num_blocks) {
-            const size_t trow = ((size_t)phys * a.num_kv_heads + kvh) * kBlockSize + new_off;
-            const size_t dst = trow * D + (size_t)slice * E;  // elements of the cache type
-            *reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.k_cache)) + dst * G::EB) = knew;
-            *reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.v_cache)) + dst * G::EB) = vnew;
-            if constexpr (kInt8) {
-                if (slice == 0) {
-                    const_cast<float*>(a.k_scale)[trow] = knew_s;
-                    const_cast<float*>(a.v_scale)[trow] = vnew_s;
-                }
-            }
-        }
-    }
+    const int n_loop = has_new ? n - 1 : n;  // tokens the block loop attends to
 
     // Each wave takes a contiguous run of the partition's blocks.  Block ids
     // are wave-uniform scalar loads, issued one block ahead of their use; they
@@ -415,30 +386,15 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
         }
     };
 
-    auto compute_block = [&](BlockRegs<CE, D>& r) {
+    auto compute_block = [&](const BlockRegs<CE, D>& r) {
         const int jb = r.jb;
-        if (has_new && jb == new_jb) {  // the new token's row comes from registers
-#pragma unroll
-            for (int st = 0; st < STEPS; ++st) {
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const bool mine = (st * U + u) * R + row == new_off;
-                    r.k[st][u] = select4(mine, knew, r.k[st][u]);
-                    r.v[st][u] = select4(mine, vnew, r.v[st][u]);
-                    if constexpr (kInt8) {
-                        r.ks[st][u] = mine ? knew_s : r.ks[st][u];
-                        r.vs[st][u] = mine ? vnew_s : r.vs[st][u];
-                    }
-                }
-            }
-        }
-        const bool full = r.ok && (jb + 1) * kBlockSize <= n;
+        const bool full = r.ok && (jb + 1) * kBlockSize <= n_loop;
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
             bool valid[U];
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                valid[u] = full || (r.ok && jb * kBlockSize + (st * U + u) * R + row < n);
+                valid[u] = full || (r.ok && jb * kBlockSize + (st * U + u) * R + row < n_loop);
 
             // scores of the U tokens this row sees, for every head of the tile,
             // then the online-softmax update of (m, l) and the rescale of acc
@@ -455,17 +411,24 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
                 float mx = m[h];
 #pragma unroll
                 for (int u = 0; u < U; ++u) mx = fmaxf(mx, s[u]);
-                const float alpha = fast_exp2(m[h] - mx);
                 float psum = 0.f;
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     p[h][u] = fast_exp2(s[u] - mx);
                     psum += p[h][u];
                 }
-                l[h] = fmaf(l[h], alpha, psum);
+                // Tiles of several heads rescale only when some row's running
+                // max grew (rare after the first blocks; otherwise the factor
+                // is exactly 1).  Measured: a win for GQA tiles, a loss for
+                // single-head tiles, which rescale unconditionally.
+                if (!(PKV_LAZY_RESCALE && GT > 1) || __builtin_amdgcn_ballot_w64(mx > m[h]) != 0) {
+                    const float alpha = fast_exp2(m[h] - mx);
+                    l[h] *= alpha;
 #pragma unroll
-                for (int e = 0; e < E; ++e) acc[h][e] *= alpha;
-                m[h] = mx;
+                    for (int e = 0; e < E; ++e) acc[h][e] *= alpha;
+                    m[h] = mx;
+                }
+                l[h] += psum;
             }
             // V: one wave load at a time, widened once and shared by the heads
 #pragma unroll
@@ -489,11 +452,12 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
         }
     };
 
-    // Two blocks in flight per wave: the loads of block i+1 are issued before
-    // block i is consumed, and the id of block i+2 is requested meanwhile.
-    // Loads past the run are empty, so only the consumption of the second
-    // block of the last pair sits behind a branch.
-    if (n_my > 0) {
+    // kDepth blocks in flight per wave: the loads of the next blocks are
+    // issued before block i is consumed, and the next id is requested
+    // meanwhile.  Loads past the run are empty, so only the consumption of the
+    // blocks of the last round sits behind a branch.
+    constexpr int kDepth = kPipelineDepth<CE, GT>;
+    if (n_my > 0 && kDepth == 2) {
         BlockRegs<CE, D> ra, rb;
         load_block(ra, my_ids[0], 0);
         int next_id = my_ids[min(1, last)];
@@ -504,6 +468,82 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
             load_block(ra, next_id, i + 2);
             next_id = my_ids[min(i + 3, last)];
             if (i + 1 < n_my) compute_block(rb);
+        }
+    } else if (n_my > 0) {  // three blocks in flight
+        BlockRegs<CE, D> ra, rb, rc;
+        load_block(ra, my_ids[0], 0);
+        load_block(rb, my_ids[min(1, last)], 1);
+        int next_id = my_ids[min(2, last)];
+        for (int i = 0; i < n_my; i += 3) {
+            load_block(rc, next_id, i + 2);
+            next_id = my_ids[min(i + 3, last)];
+            compute_block(ra);
+            load_block(ra, next_id, i + 3);
+            next_id = my_ids[min(i + 4, last)];
+            if (i + 1 < n_my) compute_block(rb);
+            load_block(rb, next_id, i + 4);
+            next_id = my_ids[min(i + 5, last)];
+            if (i + 2 < n_my) compute_block(rc);
+        }
+    }
+
+    if (has_new && wave == 0) {
+        // the new row: every lane loads its slice; row 0 of wave 0 folds it in
+        const size_t src = ((size_t)b * a.num_kv_heads + kvh) * D + (size_t)slice * E;
+        uint4 kc, vc;
+        float ks = 1.f, vs = 1.f;
+        if constexpr (!kInt8) {
+            kc = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + src * G::EB);
+            vc = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + src * G::EB);
+        } else {
+            float xk[16], xv[16];
+            const uint4* pk = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k_new) + src);
+            const uint4* pv = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v_new) + src);
+            const uint4 k0 = pk[0], k1 = pk[1], v0 = pv[0], v1 = pv[1];
+            const uint32_t wk[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+            const uint32_t wv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                xk[2 * i] = QE == Elem::F16 ? lo_h(wk[i]) : lo_bf(wk[i]);
+                xk[2 * i + 1] = QE == Elem::F16 ? hi_h(wk[i]) : hi_bf(wk[i]);
+                xv[2 * i] = QE == Elem::F16 ? lo_h(wv[i]) : lo_bf(wv[i]);
+                xv[2 * i + 1] = QE == Elem::F16 ? hi_h(wv[i]) : hi_bf(wv[i]);
+            }
+            kc = quantize16<L>(xk, ks);
+            vc = quantize16<L>(xv, vs);
+        }
+        const int new_jb = (n - 1) / kBlockSize, new_off = (n - 1) % kBlockSize;
+        const int phys = table[new_jb];
+        if (h0 % g == 0 && row == 0 && phys >= 0 && (int64_t)phys < a.num_blocks) {
+            // one writer per kv head: the first q-head tile's row 0 of wave 0
+            const size_t trow = ((size_t)phys * a.num_kv_heads + kvh) * kBlockSize + new_off;
+            const size_t dst = trow * D + (size_t)slice * E;  // elements of the cache type
+            *reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.k_cache)) + dst * G::EB) = kc;
+            *reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.v_cache)) + dst * G::EB) = vc;
+            if constexpr (kInt8) {
+                if (slice == 0) {
+                    const_cast<float*>(a.k_scale)[trow] = ks;
+                    const_cast<float*>(a.v_scale)[trow] = vs;
+                }
+            }
+        }
+        float vx[E];
+        widen<CE, E>(vc, vx);
+#pragma unroll
+        for (int h = 0; h < GT; ++h) {
+            float d = group_sum<L>(qs[h].dot(kc));
+            if constexpr (kInt8) d *= ks;
+            const float sn = d * c;
+            if (row == 0) {  // one row takes the token
+                const float mx = fmaxf(m[h], sn);
+                const float alpha = fast_exp2(m[h] - mx);
+                const float pn = fast_exp2(sn - mx);
+                l[h] = fmaf(l[h], alpha, pn);
+                const float pv = kInt8 ? pn * vs : pn;
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[h][e] = fmaf(pv, vx[e], acc[h][e] * alpha);
+                m[h] = mx;
+            }
         }
     }
 

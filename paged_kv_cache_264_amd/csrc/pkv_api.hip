@@ -5,7 +5,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
-#include "../../include/pkv.h"
+#include "pkv.h"
 #include "pkv_internal.h"
 
 namespace {

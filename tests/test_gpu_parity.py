@@ -342,7 +342,8 @@ def test_large_batch_natural_order(pkv):
 
 
 @pytest.mark.parametrize("dtype,cache", PAIRS)
-@pytest.mark.parametrize("D,Hq,Hkv,P", [(128, 8, 8, 0), (64, 16, 2, 32), (256, 4, 1, 64)])
+@pytest.mark.parametrize("D,Hq,Hkv,P", [(128, 8, 8, 0), (64, 16, 2, 32), (256, 4, 1, 64),
+                                        (128, 8, 2, 0), (128, 16, 2, 64)])
 def test_decode_append_matches_write_then_decode(pkv, dtype, cache, D, Hq, Hkv, P):
     """The fused step equals the cache write of the new tokens followed by the
     decode: cache bytes bit-exact against the oracle's write, outputs within
