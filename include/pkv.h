@@ -72,7 +72,9 @@ typedef enum {
     PKV_ERR_DTYPE = 3,       /* unsupported dtype or dtype pairing               */
     PKV_ERR_UNSUPPORTED = 4, /* head_dim / block_size outside the support set    */
     PKV_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required       */
-    PKV_ERR_HIP = 6          /* the HIP runtime reported an error                */
+    PKV_ERR_HIP = 6,         /* the HIP runtime reported an error                */
+    PKV_ERR_CAPACITY = 7,    /* the block pool has too few free blocks           */
+    PKV_ERR_SEQUENCE = 8     /* unknown sequence id, or one that already exists  */
 } pkv_status;
 
 typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_I8 = 3 } pkv_dtype;
@@ -221,6 +223,94 @@ pkv_status pkv_paged_attn_reduce(void* out, const float* m_part, const float* l_
                                  int num_q_heads, int head_dim, int partition_size,
                                  int num_partitions, int skip_single_partition,
                                  pkv_dtype out_dtype, hipStream_t stream);
+
+/*
+ * Host block manager: the pool of physical blocks and the block table of
+ * every sequence ("Efficient AI Lecture 13" notes, section "PagedAttention":
+ * blocks allocated on demand, stored anywhere, found through a block table;
+ * lazyllm lesson 4, section 4.2: a per-request page table over one global
+ * pool with dynamic allocation and release), with sharing of a common prefix
+ * between sequences that continue one prompt (lecture 13, the advantages of
+ * PagedAttention: shared prompt prefixes reuse physical blocks, for parallel
+ * sampling and beam search; juejin "LLM Engineer's Handbook", section
+ * "optimized attention").
+ *
+ * Sharing is by reference count.  pkv_bm_fork gives the child the parent's
+ * blocks (every count + 1).  A block whose count is above 1 is never written:
+ * when a sequence appends into a partly filled last block that it shares, the
+ * manager takes a fresh block, asks the caller to copy the shared block into
+ * it (a copy pair), and moves the sequence to the copy (copy-on-write).  A
+ * block returns to the free list when its count reaches 0.  With this rule the
+ * pool holds exactly one physical block per distinct (logical block, contents)
+ * pair over the live sequences, the least any manager can use.
+ *
+ * The manager lives in host memory and calls no HIP function; it is not
+ * thread-safe (one caller at a time per manager).  Sequence ids are any
+ * int64 the caller chooses.  Every function checks its arguments and leaves
+ * the manager unchanged when it returns an error.
+ */
+typedef struct pkv_block_manager pkv_block_manager;
+
+/* A manager of num_blocks (>= 1) free blocks of block_size (16) tokens.  The
+ * caller owns *out and releases it with pkv_bm_destroy. */
+pkv_status pkv_bm_create(int64_t num_blocks, int block_size, pkv_block_manager** out);
+void pkv_bm_destroy(pkv_block_manager* bm);
+
+/* A new sequence with no tokens.  PKV_ERR_SEQUENCE if seq_id exists. */
+pkv_status pkv_bm_add_sequence(pkv_block_manager* bm, int64_t seq_id);
+
+/* child_id starts as a copy of parent_id's table (shared blocks, no data
+ * moved).  PKV_ERR_SEQUENCE if the parent is unknown or the child exists. */
+pkv_status pkv_bm_fork(pkv_block_manager* bm, int64_t parent_id, int64_t child_id);
+
+/* Drop a sequence; blocks no other sequence holds become free. */
+pkv_status pkv_bm_free_sequence(pkv_block_manager* bm, int64_t seq_id);
+
+/*
+ * Reserve room for num_tokens[i] new tokens at the end of sequence
+ * seq_ids[i], for i in order (an id may repeat).  Host arrays:
+ *  slot_mapping  [sum num_tokens] int64 or NULL: the slot of each new token,
+ *                sequence by sequence, in position order (the layout
+ *                pkv_kv_cache_write reads)
+ *  copy_pairs    [max_copies][2] int32 (source block, destination block):
+ *                copies the caller must make, before writing the new tokens,
+ *                with pkv_copy_blocks; at most one per entry of seq_ids
+ *  num_copies    number of pairs written
+ * PKV_ERR_CAPACITY if the free blocks do not suffice, PKV_ERR_SHAPE if
+ * max_copies is too small; nothing changes then.
+ */
+pkv_status pkv_bm_append(pkv_block_manager* bm, const int64_t* seq_ids, const int32_t* num_tokens,
+                         int num_seqs, int64_t* slot_mapping, int32_t* copy_pairs,
+                         int64_t max_copies, int64_t* num_copies);
+
+/* Block tables and lengths of the listed sequences (host arrays):
+ * block_tables [num_seqs][max_blocks_per_seq] int32, entries past a
+ * sequence's last block set to -1; context_lens [num_seqs] int32.
+ * PKV_ERR_SHAPE if a sequence has more than max_blocks_per_seq blocks or more
+ * than INT32_MAX tokens. */
+pkv_status pkv_bm_block_tables(const pkv_block_manager* bm, const int64_t* seq_ids, int num_seqs,
+                               int max_blocks_per_seq, int32_t* block_tables,
+                               int32_t* context_lens);
+
+/* Free blocks left; -1 for a NULL manager. */
+int64_t pkv_bm_num_free_blocks(const pkv_block_manager* bm);
+
+/* Tokens held by a sequence; -1 if unknown. */
+int64_t pkv_bm_sequence_length(const pkv_block_manager* bm, int64_t seq_id);
+
+/*
+ * Copy whole blocks inside the pool, for the copy pairs of pkv_bm_append:
+ * for every pair (src, dst) of copy_pairs ([num_pairs][2] int32, device
+ * memory), the num_kv_heads tiles of block src in k_cache and v_cache (and
+ * their scale rows when cache_dtype == I8) are copied to block dst.  Pairs
+ * with an id outside [0, num_blocks) or src == dst are skipped.  A block may
+ * not be the destination of one pair and the source or destination of
+ * another in the same call.  Asynchronous on `stream` like the calls above.
+ */
+pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                           const int32_t* copy_pairs, int64_t num_pairs, int num_kv_heads,
+                           int head_dim, int block_size, int64_t num_blocks,
+                           pkv_dtype cache_dtype, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* pkv_status_string(pkv_status status);

@@ -18,6 +18,7 @@ __all__ = [
     "kv_cache_write", "paged_attn_decode", "paged_attn_decode_append",
     "paged_attn_decode_partials", "paged_attn_reduce",
     "decode_workspace_size", "default_partition_size", "num_partitions",
+    "BlockManager", "copy_blocks",
     "library_path", "PkvError", "BLOCK_SIZE",
 ]
 
@@ -70,6 +71,26 @@ def _load():
     L.pkv_paged_attn_decode_partials.restype = I
     L.pkv_paged_attn_reduce.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, P]
     L.pkv_paged_attn_reduce.restype = I
+    L.pkv_copy_blocks.argtypes = [P, P, P, P, P, I64, I, I, I, I64, I, P]
+    L.pkv_copy_blocks.restype = I
+    L.pkv_bm_create.argtypes = [I64, I, ctypes.POINTER(P)]
+    L.pkv_bm_create.restype = I
+    L.pkv_bm_destroy.argtypes = [P]
+    L.pkv_bm_destroy.restype = None
+    L.pkv_bm_add_sequence.argtypes = [P, I64]
+    L.pkv_bm_add_sequence.restype = I
+    L.pkv_bm_fork.argtypes = [P, I64, I64]
+    L.pkv_bm_fork.restype = I
+    L.pkv_bm_free_sequence.argtypes = [P, I64]
+    L.pkv_bm_free_sequence.restype = I
+    L.pkv_bm_append.argtypes = [P, P, P, I, P, P, I64, ctypes.POINTER(I64)]
+    L.pkv_bm_append.restype = I
+    L.pkv_bm_block_tables.argtypes = [P, P, I, I, P, P]
+    L.pkv_bm_block_tables.restype = I
+    L.pkv_bm_num_free_blocks.argtypes = [P]
+    L.pkv_bm_num_free_blocks.restype = I64
+    L.pkv_bm_sequence_length.argtypes = [P, I64]
+    L.pkv_bm_sequence_length.restype = I64
     L.pkv_status_string.argtypes = [I]
     L.pkv_status_string.restype = ctypes.c_char_p
     L.pkv_last_error.argtypes = []
@@ -290,3 +311,116 @@ def paged_attn_reduce(m_part, l_part, o_part, context_lens, partition_size, out=
                                        _code(out.dtype, "out"), _stream(o_part))
     _check_status(rc)
     return out
+
+
+def copy_blocks(k_cache, v_cache, copy_pairs, k_scale=None, v_scale=None):
+    """Copy whole pool blocks (all kv heads of K and V, and the scale rows of
+    an INT8 cache) for each (src, dst) row of copy_pairs ([n][2] int32 on the
+    GPU): the copy-on-write step of BlockManager.append."""
+    _dev(k_cache, "k_cache", ndim=4)
+    _dev(v_cache, "v_cache", dtype=k_cache.dtype, ndim=4)
+    _dev(copy_pairs, "copy_pairs", dtype=torch.int32, ndim=2)
+    if copy_pairs.shape[1] != 2:
+        raise ValueError("copy_pairs must be [n][2]")
+    NB, Hkv, bs, D = k_cache.shape
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache shapes disagree")
+    if k_cache.dtype == torch.int8:
+        _dev(k_scale, "k_scale", dtype=torch.float32, ndim=3)
+        _dev(v_scale, "v_scale", dtype=torch.float32, ndim=3)
+        if tuple(k_scale.shape) != (NB, Hkv, bs) or v_scale.shape != k_scale.shape:
+            raise ValueError("scale arrays must be [num_blocks][num_kv_heads][16]")
+    rc = _load().pkv_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                 _ptr(copy_pairs), copy_pairs.shape[0], Hkv, D, bs, NB,
+                                 _code(k_cache.dtype, "k_cache"), _stream(k_cache))
+    _check_status(rc)
+
+
+def _host(x, name, dtype):
+    """Pointer of a host buffer: a C-contiguous numpy array or CPU torch tensor
+    (pinned or not) of the given numpy dtype."""
+    import numpy as np
+    if isinstance(x, torch.Tensor):
+        if x.device.type != "cpu" or not x.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous host tensor")
+        if x.numpy().dtype != np.dtype(dtype):
+            raise TypeError(f"{name} must be {np.dtype(dtype)}")
+        return ctypes.c_void_p(x.data_ptr()), x.numel()
+    if not isinstance(x, np.ndarray) or not x.flags.c_contiguous or x.dtype != np.dtype(dtype):
+        raise TypeError(f"{name} must be a C-contiguous numpy {np.dtype(dtype)} array")
+    return ctypes.c_void_p(x.ctypes.data), x.size
+
+
+class BlockManager:
+    """The pool's block allocator and per-sequence block tables, with prefix
+    sharing (reference counts, copy-on-write of a shared partly filled last
+    block).  Host-side; wraps the pkv_bm_* functions of libpkv."""
+
+    def __init__(self, num_blocks: int, block_size: int = BLOCK_SIZE):
+        L = _load()
+        h = ctypes.c_void_p()
+        _check_status(L.pkv_bm_create(num_blocks, block_size, ctypes.byref(h)))
+        self._L = L
+        self._h = h
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._L.pkv_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def add_sequence(self, seq_id: int):
+        _check_status(self._L.pkv_bm_add_sequence(self._h, seq_id))
+
+    def fork(self, parent_id: int, child_id: int):
+        _check_status(self._L.pkv_bm_fork(self._h, parent_id, child_id))
+
+    def free_sequence(self, seq_id: int):
+        _check_status(self._L.pkv_bm_free_sequence(self._h, seq_id))
+
+    @property
+    def num_free_blocks(self) -> int:
+        return self._L.pkv_bm_num_free_blocks(self._h)
+
+    def sequence_length(self, seq_id: int) -> int:
+        return self._L.pkv_bm_sequence_length(self._h, seq_id)
+
+    def append(self, seq_ids, num_tokens):
+        """Room for num_tokens[i] new tokens at the end of seq_ids[i].  Returns
+        (slot_mapping int64 [sum], copy_pairs int32 [n][2]) as numpy arrays;
+        the copies must be made (copy_blocks) before the new tokens are
+        written."""
+        import numpy as np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        cnt = np.ascontiguousarray(num_tokens, dtype=np.int32)
+        if ids.ndim != 1 or cnt.shape != ids.shape:
+            raise ValueError("seq_ids and num_tokens must be 1-D of one length")
+        slots = np.empty(int(np.maximum(cnt, 0).sum()), dtype=np.int64)
+        pairs = np.empty((len(ids), 2), dtype=np.int32)
+        n = ctypes.c_int64(0)
+        _check_status(self._L.pkv_bm_append(
+            self._h, ctypes.c_void_p(ids.ctypes.data), ctypes.c_void_p(cnt.ctypes.data), len(ids),
+            ctypes.c_void_p(slots.ctypes.data), ctypes.c_void_p(pairs.ctypes.data), len(ids),
+            ctypes.byref(n)))
+        return slots, pairs[:n.value]
+
+    def block_tables(self, seq_ids, max_blocks_per_seq: int, out=None):
+        """(block_tables int32 [B][max_blocks_per_seq], context_lens int32 [B]);
+        `out` may give two host buffers (numpy or CPU torch, e.g. pinned) to
+        fill instead of new numpy arrays."""
+        import numpy as np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        B = len(ids)
+        if out is None:
+            out = (np.empty((B, max_blocks_per_seq), dtype=np.int32), np.empty(B, dtype=np.int32))
+        pt, nt = _host(out[0], "block_tables", np.int32)
+        pl, nl = _host(out[1], "context_lens", np.int32)
+        if nt < B * max_blocks_per_seq or nl < B:
+            raise ValueError("output buffers too small")
+        _check_status(self._L.pkv_bm_block_tables(self._h, ctypes.c_void_p(ids.ctypes.data), B,
+                                                  max_blocks_per_seq, pt, pl))
+        return out

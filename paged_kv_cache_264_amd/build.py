@@ -1,7 +1,7 @@
 """Build libpkv.so (HIP, gfx950) in-tree with hipcc.
 
 Usage: python -m paged_kv_cache_264_amd.build  (or call build_library()).
-Each .hip source compiles to an object in parallel, then one shared library
+Each source (.hip kernels, .cpp host code) compiles to an object in parallel, then one shared library
 is linked next to this file.  Always rebuilds.
 """
 from __future__ import annotations
@@ -17,7 +17,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpkv.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
-SOURCES = ["pkv_api.hip", "paged_decode.hip", "paged_reduce.hip", "kv_cache_write.hip"]
+SOURCES = ["pkv_api.hip", "paged_decode.hip", "paged_reduce.hip", "kv_cache_write.hip",
+           "copy_blocks.hip", "block_manager.cpp"]
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

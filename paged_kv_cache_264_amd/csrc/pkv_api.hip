@@ -8,9 +8,10 @@
 #include "pkv.h"
 #include "pkv_internal.h"
 
+namespace pkv {
 namespace {
-
 thread_local char g_err[512] = "";
+}  // namespace
 
 pkv_status fail(pkv_status s, const char* fmt, ...) {
     va_list ap;
@@ -24,6 +25,15 @@ pkv_status ok() {
     g_err[0] = '\0';
     return PKV_OK;
 }
+
+const char* last_error() { return g_err; }
+
+}  // namespace pkv
+
+namespace {
+
+using pkv::fail;
+using pkv::ok;
 
 pkv_status hip_status(hipError_t e, const char* what) {
     if (e == hipSuccess) return ok();
@@ -136,11 +146,13 @@ const char* pkv_status_string(pkv_status s) {
     case PKV_ERR_UNSUPPORTED: return "head_dim or block_size outside the supported set";
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_HIP: return "HIP runtime error";
+    case PKV_ERR_CAPACITY: return "too few free blocks in the pool";
+    case PKV_ERR_SEQUENCE: return "unknown or already existing sequence id";
     default: return "unknown status";
     }
 }
 
-const char* pkv_last_error(void) { return g_err; }
+const char* pkv_last_error(void) { return pkv::last_error(); }
 
 int pkv_default_partition_size(int num_seqs, int num_q_heads, int num_kv_heads,
                                int max_blocks_per_seq) {
@@ -200,6 +212,48 @@ pkv_status pkv_kv_cache_write(const void* k, const void* v, void* k_cache, void*
     return hip_status(
         pkv::launch_kv_cache_write(a, (int)src_dtype, (int)cache_dtype, head_dim, stream),
         "kv_cache_write launch");
+}
+
+pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                           const int32_t* copy_pairs, int64_t num_pairs, int num_kv_heads,
+                           int head_dim, int block_size, int64_t num_blocks,
+                           pkv_dtype cache_dtype, hipStream_t stream) {
+    if (num_pairs < 0 || num_kv_heads <= 0 || num_blocks <= 0)
+        return fail(PKV_ERR_SHAPE,
+                    "need num_pairs >= 0, num_kv_heads > 0 and num_blocks > 0 (got %lld, %d, %lld)",
+                    (long long)num_pairs, num_kv_heads, (long long)num_blocks);
+    if (block_size != pkv::kBlockSize)
+        return fail(PKV_ERR_UNSUPPORTED, "block_size %d unsupported (only 16)", block_size);
+    if (!head_dim_ok(head_dim))
+        return fail(PKV_ERR_UNSUPPORTED, "head_dim %d unsupported (64, 128, 256)", head_dim);
+    if (!is_float(cache_dtype) && cache_dtype != PKV_I8)
+        return fail(PKV_ERR_DTYPE, "unsupported cache_dtype %d", (int)cache_dtype);
+    if (num_pairs == 0) return ok();
+    if (!k_cache || !v_cache || !copy_pairs)
+        return fail(PKV_ERR_NULL, "k_cache, v_cache and copy_pairs are required");
+    if (cache_dtype == PKV_I8 && (!k_scale || !v_scale))
+        return fail(PKV_ERR_NULL, "k_scale and v_scale are required for an INT8 cache");
+    if (!aligned16(k_cache) || !aligned16(v_cache) ||
+        (cache_dtype == PKV_I8 && (!aligned16(k_scale) || !aligned16(v_scale))))
+        return fail(PKV_ERR_SHAPE, "caches and scales must be 16-byte aligned");
+    const int64_t elem = cache_dtype == PKV_F32 ? 4 : cache_dtype == PKV_I8 ? 1 : 2;
+    pkv::CopyBlocksArgs a{};
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.k_scale = cache_dtype == PKV_I8 ? k_scale : nullptr;
+    a.v_scale = cache_dtype == PKV_I8 ? v_scale : nullptr;
+    a.pairs = copy_pairs;
+    a.num_pairs = num_pairs;
+    a.num_blocks = num_blocks;
+    a.block_bytes = (int64_t)num_kv_heads * pkv::kBlockSize * head_dim * elem;
+    a.scale_bytes = cache_dtype == PKV_I8 ? (int64_t)num_kv_heads * pkv::kBlockSize * 4 : 0;
+    if (a.block_bytes > ((int64_t)1 << 40) / num_blocks)
+        return fail(PKV_ERR_SHAPE, "pool too large");
+    const hipError_t e = pkv::launch_copy_blocks(a, stream);
+    if (e == hipErrorInvalidValue)
+        return fail(PKV_ERR_SHAPE, "too many copy pairs for one launch (%lld)",
+                    (long long)num_pairs);
+    return hip_status(e, "copy_blocks launch");
 }
 
 }  // extern "C"

@@ -6,7 +6,15 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "pkv.h"
+
 namespace pkv {
+
+// Thread-local error reporting shared by every entry point: fail() records a
+// message and returns s; ok() clears it.
+pkv_status fail(pkv_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+pkv_status ok();
+const char* last_error();
 
 constexpr int kBlockSize = 16;   // tokens per KV block
 constexpr int kDecodeThreads = 256;
@@ -88,6 +96,21 @@ struct CacheWriteArgs {
 
 hipError_t launch_kv_cache_write(const CacheWriteArgs& a, int src_dtype, int cache_dtype,
                                  int head_dim, hipStream_t stream);
+
+struct CopyBlocksArgs {
+    void* k_cache;
+    void* v_cache;
+    float* k_scale;      // nullptr unless the cache holds INT8 codes
+    float* v_scale;
+    const int32_t* pairs;  // [num_pairs][2] (src, dst)
+    int64_t num_pairs;
+    int64_t num_blocks;
+    int64_t block_bytes;   // bytes of one block of one tensor (all kv heads), multiple of 16
+    int64_t scale_bytes;   // bytes of one block's scale row (all kv heads), or 0
+};
+
+// Returns hipErrorInvalidValue if the grid would not fit.
+hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
 
 
 }  // namespace pkv

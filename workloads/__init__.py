@@ -309,3 +309,34 @@ def algorithmic_bytes(context_lens, Hq, Hkv, D, e_kv, e_q, int8_scales=False) ->
     B = len(lens)
     return (tok * per_tok + B * Hq * D * 2 * e_q
             + int(sum(blocks_needed(n) for n in lens)) * 4 + 4 * B)
+
+
+# Parallel sampling over shared prompts (the prefix-sharing workload of the
+# block manager): `prompts` prompts with lengths U[lo, hi] are each continued
+# by `samples` sequences (parallel sampling / beams, lecture 13 notes,
+# "PagedAttention" advantages), which then decode `gen` tokens each.
+# LLaMA-7B shapes as above.
+SAMPLING = {
+    "sampling-small": dict(prompts=3, samples=3, prompt_len=[37, 16, 100], Hq=8, Hkv=2, D=128,
+                           dtype="f16", cache="f16", gen=20, seed=6),
+    "sampling": dict(prompts=16, samples=4, prompt_len=(512, 2048), Hq=32, Hkv=32, D=128,
+                     dtype="f16", cache="f16", gen=64, seed=7),
+}
+S_PROMPT, S_TOKEN_K, S_TOKEN_V, S_STEP_Q = 20, 21, 22, 23
+
+
+def sampling_prompt_lens(cfg: dict) -> np.ndarray:
+    pl = cfg["prompt_len"]
+    if isinstance(pl, (list, tuple)) and len(pl) == cfg["prompts"] and not (
+            isinstance(pl, tuple) and len(pl) == 2):
+        return np.asarray(pl, np.int64)
+    lo, hi = pl
+    return rng(cfg["seed"], S_PROMPT).integers(lo, hi, size=cfg["prompts"],
+                                               endpoint=True).astype(np.int64)
+
+
+def token_rows(n: int, Hkv: int, D: int, dtype: str, seed: int, stream: int,
+               device="cpu") -> torch.Tensor:
+    """[n][Hkv][D] N(0,1) rows rounded to dtype: the K (or V) row of token id
+    0..n-1.  Row values depend only on (seed, stream, n, device)."""
+    return _normal((n, Hkv, D), seed, stream, device, dtype)
