@@ -34,6 +34,7 @@ WORKLOAD_NAMES = {
     "gqa": "gqa-32q8kv-bf16-paged-decode",
     "long": "long-32k-fp16-split-decode",
     "int8": "llama7b-mha-int8kv-paged-decode",
+    "sampling": "llama7b-parallel-sampling-shared-prefix-decode",
 }
 KERNEL_SOURCES = ["paged_decode.hip", "pkv_device.h", "pkv_internal.h", "pkv_api.hip"]
 
@@ -99,6 +100,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.config == "sampling":
+        bench_sampling(args)
         return
 
     import numpy as np
@@ -243,6 +247,219 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = run_cpu_baseline(batch, args.config, args.cpu_seconds,
                                                   e_kv, e_q, int8)
+    print(json.dumps(result), flush=True)
+
+
+def bench_sampling(args):
+    """Decode with prefix sharing: 16 LLaMA-7B-shaped prompts (U[512, 2048]
+    tokens) continued by 4 samples each (64 sequences).  A step is what a
+    serving loop does per generated token: the native block manager reserves
+    one slot per sequence (copy-on-write of shared partial blocks on the first
+    step), its block tables go to the GPU through pinned double buffers, the
+    block copies run, then the fused append + decode kernel.  Also times
+    pkv_copy_blocks on 1024 block pairs, and reports the pool memory used
+    with and without sharing."""
+    import types
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_264_amd as pkv
+    import workloads as W
+
+    torch.cuda.set_device(0)
+    cfg = W.SAMPLING["sampling"]
+    BS = W.BLOCK_SIZE
+    Hq, Hkv, D = cfg["Hq"], cfg["Hkv"], cfg["D"]
+    n = cfg["samples"]
+    prompt_lens = W.sampling_prompt_lens(cfg)
+    B = len(prompt_lens) * n
+    gen = args.warmup + args.steps
+    NB = int(sum(n * -(-(int(L) + gen) // BS) for L in prompt_lens)) + 64
+    NB = max(NB, 2048 + 64)
+    mbs = max(-(-(int(L) + gen) // BS) for L in prompt_lens)
+    seed = cfg["seed"] if args.seed is None else args.seed
+    dt = W.TORCH_DTYPE[cfg["dtype"]]
+    kc = torch.zeros((NB, Hkv, BS, D), dtype=dt, device="cuda")
+    vc = torch.zeros_like(kc)
+    bm = pkv.BlockManager(NB)
+    for p, L in enumerate(prompt_lens):
+        sid = p * n
+        bm.add_sequence(sid)
+        slots, _ = bm.append([sid], [int(L)])
+        k = W.token_rows(int(L), Hkv, D, cfg["dtype"], seed * 100 + p, W.S_TOKEN_K, "cuda")
+        v = W.token_rows(int(L), Hkv, D, cfg["dtype"], seed * 100 + p, W.S_TOKEN_V, "cuda")
+        pkv.kv_cache_write(k, v, kc, vc, torch.from_numpy(slots).cuda())
+        for c in range(1, n):
+            bm.fork(sid, sid + c)
+    seqs = list(range(B))
+    ones = [1] * B
+    q = W.token_rows(B, Hq, D, cfg["dtype"], seed, W.S_STEP_Q, "cuda")
+    k_new = W.token_rows(B, Hkv, D, cfg["dtype"], seed, W.S_NEWK, "cuda")
+    v_new = W.token_rows(B, Hkv, D, cfg["dtype"], seed, W.S_NEWV, "cuda")
+    out = torch.empty_like(q)
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    P = pkv.default_partition_size(B, Hq, Hkv, mbs)
+    ws = torch.empty(pkv.decode_workspace_size(B, Hq, Hkv, D, mbs, P), dtype=torch.uint8,
+                     device="cuda")
+    pin_t = [torch.empty((B, mbs), dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    pin_l = [torch.empty((B,), dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    ev_up = [None, None]
+    tables = torch.empty((B, mbs), dtype=torch.int32, device="cuda")
+    lens_d = torch.empty((B,), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    e_kv = 2
+    state = dict(copies=0, host_s=0.0, lens_sum=0)
+    store_bytes = B * Hkv * 2 * D * e_kv
+
+    step_lens = []
+
+    def step(i, ev0=None, ev1=None, count=False):
+        t = time.perf_counter()
+        _, pairs = bm.append(seqs, ones)
+        t_mid = time.perf_counter()
+        buf = i % 2
+        if ev_up[buf] is not None:
+            ev_up[buf].synchronize()        # the pinned buffer's last upload is done
+        t_tab = time.perf_counter()
+        bm.block_tables(seqs, mbs, out=(pin_t[buf], pin_l[buf]))
+        state["host_s"] += (t_mid - t) + (time.perf_counter() - t_tab)
+        if len(pairs):
+            state["copies"] += len(pairs)
+            pkv.copy_blocks(kc, vc, torch.from_numpy(pairs).cuda())
+        tables.copy_(pin_t[buf], non_blocking=True)
+        lens_d.copy_(pin_l[buf], non_blocking=True)
+        ev_up[buf] = torch.cuda.Event()
+        ev_up[buf].record(stream)
+        if count:
+            step_lens.append(pin_l[buf].numpy().copy())
+        if ev0 is not None:
+            ev0.record(stream)
+        pkv.paged_attn_decode_append(q, k_new, v_new, kc, vc, tables, lens_d, scale, out=out,
+                                     partition_size=P, workspace=ws)
+        if ev1 is not None:
+            ev1.record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    state["host_s"] = 0.0
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j, (e0, e1) in enumerate(evs):
+        step(args.warmup + j, e0, e1, count=True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    assert torch.isfinite(out.float()).all()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    dec_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    # Bytes per step.  Per-sequence (the metric's count): every sequence's
+    # context K/V, as if nothing were shared.  Unique (the HBM minimum): each
+    # physical block once, for the tokens valid in it; the tables of a timed
+    # step are prefixes of the final tables (no copies after the first step).
+    final_tables, _ = bm.block_tables(seqs, mbs)
+    tok_bytes = Hkv * 2 * D * e_kv
+    side = B * Hq * D * 2 * 2 + 4 * B
+    seq_bytes, uniq_bytes = 0, 0
+    for lens_h in step_lens:
+        lens_h = lens_h.astype(np.int64)
+        seq_bytes += W.algorithmic_bytes(lens_h, Hq, Hkv, D, e_kv, 2) + store_bytes
+        nblk = -(-lens_h // BS)
+        ids, valid = [], []
+        for b in range(B):
+            if nblk[b] == 0:
+                continue
+            ids.append(final_tables[b, :nblk[b]])
+            v = np.full(nblk[b], BS, np.int64)
+            v[-1] = lens_h[b] - BS * (nblk[b] - 1)
+            valid.append(v)
+        ids = np.concatenate(ids)
+        valid = np.concatenate(valid)
+        best = np.zeros(NB, np.int64)
+        np.maximum.at(best, ids, valid)
+        uniq_bytes += int(best.sum()) * tok_bytes + side + 4 * len(ids) + store_bytes
+        state["lens_sum"] += int(lens_h.sum())
+    launch_bytes = seq_bytes / args.steps
+    unique_bytes = uniq_bytes / args.steps
+    value = launch_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = unique_bytes / (dec_ms * 1e-3) / 1e9
+
+    final_lens = np.asarray([bm.sequence_length(s) for s in seqs])
+    used = NB - bm.num_free_blocks
+    unshared = int(sum(-(-int(x) // BS) for x in final_lens))
+    block_bytes = Hkv * BS * D * e_kv * 2
+
+    # copy-on-write kernel alone: 1024 whole-block copies (K and V)
+    n_pairs = 1024
+    pairs = torch.from_numpy(np.stack([np.arange(n_pairs), np.arange(n_pairs, 2 * n_pairs)],
+                                      1).astype(np.int32)).cuda()
+    for _ in range(3):
+        pkv.copy_blocks(kc, vc, pairs)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    c0.record(stream)
+    for _ in range(reps):
+        pkv.copy_blocks(kc, vc, pairs)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_us = c0.elapsed_time(c1) * 1e3 / reps
+    copy_bytes = n_pairs * block_bytes * 2          # read + write
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg["dtype"],
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD_NAMES["sampling"], "prompts": len(prompt_lens),
+            "samples_per_prompt": n, "num_seqs": B, "num_q_heads": Hq, "num_kv_heads": Hkv,
+            "head_dim": D, "block_size": BS, "prompt_lens": "U[512,2048]",
+            "mean_context_tokens": round(state["lens_sum"] / args.steps / B, 1),
+            "partition_size": P, "seed": seed, "parallelism": "single-gpu",
+            "step": "block-manager append + table upload + fused decode",
+        },
+        "kv_tokens_per_s": round(state["lens_sum"] / args.steps / (ms_per_step * 1e-3), 1),
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "decode_kernel_us": round(dec_ms * 1e3, 2),
+        "launch_alg_bytes": int(launch_bytes),
+        "launch_unique_bytes": int(unique_bytes),
+        "per_sequence_gbs_in_kernel": round(launch_bytes / (dec_ms * 1e-3) / 1e9, 1),
+        "host_block_manager_us_per_step": round(state["host_s"] / args.steps * 1e6, 2),
+        "cow_copies_first_step": state["copies"],
+        "pool_blocks_used": used,
+        "pool_blocks_without_sharing": unshared,
+        "memory_saved_frac": round(1.0 - used / unshared, 4),
+        "copy_blocks": {"pairs": n_pairs, "us": round(copy_us, 2),
+                        "achieved": round(copy_bytes / (copy_us * 1e-6) / 1e9, 1),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(copy_bytes / (copy_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "paged_decode_kernel", "kernel_sha": kernel_sha(),
+            "note": "achieved = unique bytes (each physical block once) / kernel time; value "
+                    "counts every sequence's context, so shared prompt blocks count once per "
+                    "sample there",
+        },
+    }
+    if not args.no_cpu_baseline:
+        tb, lens = bm.block_tables(seqs, mbs)
+        fake = types.SimpleNamespace(
+            layout=types.SimpleNamespace(context_lens=lens.astype(np.int64), block_tables=tb),
+            num_blocks=NB, q=q, k_cache=kc, v_cache=vc, k_scale=None, v_scale=None, B=B, Hq=Hq,
+            Hkv=Hkv, D=D, scale=scale)
+        result["cpu_baseline"] = run_cpu_baseline(fake, "sampling", args.cpu_seconds, e_kv, 2,
+                                                  False)
     print(json.dumps(result), flush=True)
 
 

@@ -11,7 +11,11 @@
 // flat memcpy of that run.  One work-group moves one 16 KiB chunk of one run
 // with four 16-byte loads per lane in flight, then four stores; the launch is
 // pairs x chunks work-groups, a single extra work-group per pair moving the
-// scale rows.  Pure streaming: HBM bound.
+// scale rows.  Pure streaming: HBM bound.  Loads and stores are non-temporal
+// (measured on MI355X for 1024 LLaMA-7B block pairs: 6.27 TB/s moved vs 5.59
+// with ordinary accesses, 5.37 for a device-to-device memcpy of the same
+// bytes); more than four 16-byte accesses per lane, or a loop per work-group,
+// measured slower.
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -21,17 +25,19 @@ constexpr int kThreads = 256;
 constexpr int kUnroll = 4;
 constexpr int64_t kChunk = (int64_t)kThreads * 16 * kUnroll;   // bytes per work-group
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ void copy_run(const char* src, char* dst, int64_t begin, int64_t end) {
-    uint4 r[kUnroll];
+    u32x4 r[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
         const int64_t off = begin + ((int64_t)u * kThreads + threadIdx.x) * 16;
-        if (off < end) r[u] = *reinterpret_cast<const uint4*>(src + off);
+        if (off < end) r[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + off));
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
         const int64_t off = begin + ((int64_t)u * kThreads + threadIdx.x) * 16;
-        if (off < end) *reinterpret_cast<uint4*>(dst + off) = r[u];
+        if (off < end) __builtin_nontemporal_store(r[u], reinterpret_cast<u32x4*>(dst + off));
     }
 }
 
