@@ -7,7 +7,8 @@ inputs.
 
 Arrays are numpy arrays on the host.  16-bit floats are passed as their raw
 bits (``uint16``) together with an explicit dtype name, because numpy has no
-bfloat16.  Dtype names: ``"f32"``, ``"f16"``, ``"bf16"``, ``"i8"``.
+bfloat16; FP8 e4m3 codes are ``uint8``.  Dtype names: ``"f32"``, ``"f16"``,
+``"bf16"``, ``"i8"``, ``"f8"``.
 
 What the functions compute, and the pages they follow, is stated in the C
 source.  Parity status: every function here is pinned by the CPU tests in
@@ -26,8 +27,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3}
-_NP_OF = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "i8": np.int8}
+DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3, "f8": 4}
+_NP_OF = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "i8": np.int8, "f8": np.uint8}
 
 GCC_CMD = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-ffp-contract=off",
            "-fno-fast-math", "-Wall", "-Wextra", _SRC, "-o", _LIB, "-lm"]
@@ -55,6 +56,11 @@ def lib():
                                             I, F, I, I, I]
         L.oracle_merge_partials.argtypes = [P, P, P, P, L64, I, I]
         L.oracle_quantize_rows.argtypes = [P, P, P, I, L64, I]
+        L.oracle_quantize_rows_f8.argtypes = [P, P, P, I, L64, I]
+        L.oracle_f8_to_f64.argtypes = [ctypes.c_uint8]
+        L.oracle_f8_to_f64.restype = ctypes.c_double
+        L.oracle_f8_from_f32.argtypes = [ctypes.c_float]
+        L.oracle_f8_from_f32.restype = ctypes.c_uint8
         L.oracle_kv_cache_write.argtypes = [P, P, P, P, P, P, P, L64, I, I, I, I, I, I]
         L.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
         L.oracle_f16_to_f64.restype = ctypes.c_double
@@ -96,7 +102,7 @@ def paged_decode(q, q_dtype, k_cache, v_cache, cache_dtype, block_tables, contex
                  k_scale=None, v_scale=None, block_size=16, rows=None, nthreads=0):
     """fp64 gather-then-dense attention.  Shapes: q [B][Hq][D]; caches
     [NB][Hkv][block_size][D]; block_tables int32 [B][MBS]; context_lens int32 [B];
-    scales float32 [NB][Hkv][block_size] for "i8".  Returns float64 [B][Hq][D]
+    scales float32 [NB][Hkv][block_size] for "i8" and "f8".  Returns float64 [B][Hq][D]
     (rows not requested are NaN)."""
     q = _check(q, q_dtype, "q")
     k_cache = _check(k_cache, cache_dtype, "k_cache")
@@ -108,7 +114,7 @@ def paged_decode(q, q_dtype, k_cache, v_cache, cache_dtype, block_tables, contex
     B, Hq, D = q.shape
     NB, Hkv, bs, D2 = k_cache.shape
     assert D2 == D and bs == block_size and v_cache.shape == k_cache.shape
-    if cache_dtype == "i8":
+    if cache_dtype in ("i8", "f8"):
         assert ks is not None and vs is not None
     out = np.full((B, Hq, D), np.nan, dtype=np.float64)
     r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
@@ -160,16 +166,27 @@ def merge_partials(m, l, o):
     return out
 
 
-def quantize_rows(x, dtype):
-    """INT8 symmetric quantization of the rows of x ([..., D]).  Returns
-    (codes int8 [..., D], scales float32 [...])."""
+def quantize_rows(x, dtype, target="i8"):
+    """Symmetric per-row quantization of the rows of x ([..., D]) to INT8
+    (target "i8") or FP8 e4m3 (target "f8").  Returns (codes [..., D] int8 or
+    uint8, scales float32 [...])."""
     x = _check(x, dtype, "x")
     D = x.shape[-1]
     rows = int(np.prod(x.shape[:-1]))
-    codes = np.empty(x.shape, np.int8)
+    codes = np.empty(x.shape, _NP_OF[target])
     scales = np.empty(x.shape[:-1], np.float32)
-    lib().oracle_quantize_rows(_ptr(codes), _ptr(scales), _ptr(x), DTYPES[dtype], rows, D)
+    fn = lib().oracle_quantize_rows if target == "i8" else lib().oracle_quantize_rows_f8
+    fn(_ptr(codes), _ptr(scales), _ptr(x), DTYPES[dtype], rows, D)
     return codes, scales
+
+
+def f8_to_f64(code: int) -> float:
+    return lib().oracle_f8_to_f64(code)
+
+
+def f8_from_f32(x: float) -> int:
+    """Nearest e4m3 code (ties to even) to x, |x| <= 448."""
+    return lib().oracle_f8_from_f32(x)
 
 
 def kv_cache_write(k, v, k_cache, v_cache, slot_mapping, src_dtype, cache_dtype, k_scale=None,

@@ -20,7 +20,9 @@
  *    Attention(Q,K,V) = Softmax(Q K^T / sqrt(d)) V with Q of shape 1 x d and
  *    K, V of shape T x d; paging leaves that equation unchanged.
  *  - the same page, section 5.3 "KV Cache Quantization": symmetric INT8,
- *    K_q = round(K / s_K), s_K = max|K| / 127.
+ *    K_q = round(K / s_K), s_K = max|K| / 127; the same section names FP8 as
+ *    the alternative with a wider dynamic range, and the juejin page's
+ *    "latest developments" list names FP8 KV caches in serving engines.
  *  - juejin.cn "LLM Engineer's Handbook -- inference optimization", the
  *    absmax-quantization passage with its worked example (0.1 with absmax 3.2
  *    gives code 4, dequantized 0.1008) and its PyTorch snippet that rounds
@@ -32,7 +34,9 @@
  *
  * Readings where the pages are silent (each one is listed with its reason in
  * the design notes of the repository):
- *  - one INT8 scale per (slot, kv head), separately for K and V;
+ *  - one INT8 scale per (slot, kv head), separately for K and V; FP8 e4m3
+ *    caches take the same per-row scale with 448 (the format's largest
+ *    value) in place of 127;
  *  - quantizer form: s = fl32(amax / 127), code = clamp(rne(fl32(x / s)),
  *    -127, 127); amax == 0 gives s = 0 and all codes 0;
  *  - q head h reads kv head h / (Hq / Hkv) (contiguous GQA groups);
@@ -51,8 +55,14 @@
 #include <omp.h>
 #endif
 
-/* Element type codes, defined here and only here. */
-enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_I8 = 3 };
+/* Element type codes, defined here and only here.  OR_F8 is the 8-bit
+ * floating-point format e4m3 (OCP "E4M3FN": sign, 4 exponent bits with bias
+ * 7, 3 mantissa bits, no infinities, the all-ones exponent-and-mantissa
+ * pattern is NaN, largest finite value 448). */
+enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_I8 = 3, OR_F8 = 4 };
+
+/* Scaled 8-bit caches: one fp32 scale per (slot, kv head). */
+static int scaled(int dtype) { return dtype == OR_I8 || dtype == OR_F8; }
 
 /* ------------------------------------------------------------------------ */
 /* Exact widening of stored elements to double.                             */
@@ -82,18 +92,48 @@ double oracle_bf16_to_f64(uint16_t b) {
     return (double)f;
 }
 
+/* e4m3 code -> value, from the format's definition. */
+double oracle_f8_to_f64(uint8_t c) {
+    int sign = (c >> 7) & 1, e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7) return NAN;
+    double mag = e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -mag : mag;
+}
+
+/* Nearest e4m3 code to x, ties to the even code (mantissa bit 0 clear).
+ * Needs |x| <= 448 (callers clamp first).  Codes 0..126 hold the
+ * non-negative finite values in increasing order; a binary search finds the
+ * two neighbours of |x|. */
+uint8_t oracle_f8_from_f32(float x) {
+    const int neg = signbit(x) != 0;
+    const double a = fabs((double)x);
+    int lo = 0, hi = 126;                 /* invariant: value(lo) <= a */
+    if (a >= oracle_f8_to_f64(126)) {
+        lo = 126;
+    } else {
+        while (hi - lo > 1) {
+            int mid = (lo + hi) / 2;
+            if (oracle_f8_to_f64((uint8_t)mid) <= a) lo = mid; else hi = mid;
+        }
+        double dl = a - oracle_f8_to_f64((uint8_t)lo), dh = oracle_f8_to_f64((uint8_t)hi) - a;
+        if (dh < dl || (dh == dl && (hi & 1) == 0)) lo = hi;
+    }
+    return (uint8_t)(lo | (neg ? 0x80 : 0));
+}
+
 static double elem(const void* base, size_t i, int dtype) {
     switch (dtype) {
     case OR_F32: return (double)((const float*)base)[i];
     case OR_F16: return oracle_f16_to_f64(((const uint16_t*)base)[i]);
     case OR_BF16: return oracle_bf16_to_f64(((const uint16_t*)base)[i]);
     case OR_I8: return (double)((const int8_t*)base)[i];
+    case OR_F8: return oracle_f8_to_f64(((const uint8_t*)base)[i]);
     default: return NAN;
     }
 }
 
 static size_t elem_size(int dtype) {
-    return dtype == OR_F32 ? 4 : (dtype == OR_I8 ? 1 : 2);
+    return dtype == OR_F32 ? 4 : (dtype == OR_I8 || dtype == OR_F8 ? 1 : 2);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -131,7 +171,7 @@ static int gather(const problem* P, int b, int kvh, int t0, int t1, double* K, d
         long base = token_row(P, b, kvh, t, &si);
         if (base < 0) return -1;
         double ks = 1.0, vs = 1.0;
-        if (P->cache_dtype == OR_I8) {
+        if (scaled(P->cache_dtype)) {
             ks = (double)P->k_scale[si];
             vs = (double)P->v_scale[si];
         }
@@ -310,8 +350,8 @@ static float elem_f32(const void* base, size_t i, int dtype) {
 /* Quantize one row: amax = max |x|; s = amax / 127 in single precision;
  * code = clamp(round-half-even(x / s), -127, 127) with the division in single
  * precision.  amax == 0 gives s = 0 and codes 0. */
-static void quantize_row(int8_t* codes, float* scale_out, const void* x, size_t base, int D,
-                         int dtype) {
+static void quantize_row_i8(int8_t* codes, float* scale_out, const void* x, size_t base, int D,
+                            int dtype) {
     float amax = 0.0f;
     for (int d = 0; d < D; ++d) {
         float a = fabsf(elem_f32(x, base + d, dtype));
@@ -333,10 +373,53 @@ static void quantize_row(int8_t* codes, float* scale_out, const void* x, size_t 
     *scale_out = s;
 }
 
+/* FP8 e4m3 row, same shape of rule with the format's largest value in place
+ * of 127: s = amax / 448 in single precision; r = x / s in single precision,
+ * clamped to [-448, 448] (it can exceed 448 by a rounding of s); code = the
+ * nearest e4m3 value to r, ties to even.  amax == 0 gives s = 0 and codes 0. */
+static void quantize_row_f8(uint8_t* codes, float* scale_out, const void* x, size_t base, int D,
+                            int dtype) {
+    float amax = 0.0f;
+    for (int d = 0; d < D; ++d) {
+        float a = fabsf(elem_f32(x, base + d, dtype));
+        if (a > amax) amax = a;
+    }
+    if (amax == 0.0f) {
+        *scale_out = 0.0f;
+        for (int d = 0; d < D; ++d) codes[d] = 0;
+        return;
+    }
+    volatile float s = amax / 448.0f;
+    for (int d = 0; d < D; ++d) {
+        volatile float r = elem_f32(x, base + d, dtype) / s;
+        float c = r;
+        if (c > 448.0f) c = 448.0f;
+        if (c < -448.0f) c = -448.0f;
+        codes[d] = oracle_f8_from_f32(c);
+    }
+    *scale_out = s;
+}
+
+static void quantize_row(void* codes, float* scale_out, const void* x, size_t base, int D,
+                         int dtype, int cache_dtype) {
+    if (cache_dtype == OR_F8)
+        quantize_row_f8((uint8_t*)codes, scale_out, x, base, D, dtype);
+    else
+        quantize_row_i8((int8_t*)codes, scale_out, x, base, D, dtype);
+}
+
 /* x: [rows][D] of dtype; codes: int8 [rows][D]; scales: float [rows]. */
 int oracle_quantize_rows(int8_t* codes, float* scales, const void* x, int dtype, long rows, int D) {
     for (long r = 0; r < rows; ++r)
-        quantize_row(codes + (size_t)r * D, scales + r, x, (size_t)r * D, D, dtype);
+        quantize_row_i8(codes + (size_t)r * D, scales + r, x, (size_t)r * D, D, dtype);
+    return 0;
+}
+
+/* As oracle_quantize_rows, to e4m3 codes (uint8 [rows][D]). */
+int oracle_quantize_rows_f8(uint8_t* codes, float* scales, const void* x, int dtype, long rows,
+                            int D) {
+    for (long r = 0; r < rows; ++r)
+        quantize_row_f8(codes + (size_t)r * D, scales + r, x, (size_t)r * D, D, dtype);
     return 0;
 }
 
@@ -345,8 +428,8 @@ int oracle_quantize_rows(int8_t* codes, float* scales, const void* x, int dtype,
 /* ------------------------------------------------------------------------ */
 
 /* k, v: [T][Hkv][D] of src_dtype.  k_cache, v_cache: [num_blocks][Hkv][block_size][D]
- * of cache_dtype (equal to src_dtype, or OR_I8).  k_scale, v_scale: float
- * [num_blocks][Hkv][block_size], used only for OR_I8.  Token i with
+ * of cache_dtype (equal to src_dtype, or OR_I8 / OR_F8).  k_scale, v_scale:
+ * float [num_blocks][Hkv][block_size], used only for OR_I8 and OR_F8.  Token i with
  * slot = slot_mapping[i] >= 0 goes to block slot / block_size, offset
  * slot % block_size, for every kv head.  Negative slots are skipped.
  * Returns -1 if a slot is beyond the pool, -3 for an unsupported pairing. */
@@ -354,8 +437,8 @@ int oracle_kv_cache_write(const void* k, const void* v, void* k_cache, void* v_c
                           float* k_scale, float* v_scale, const int64_t* slot_mapping, long T,
                           int Hkv, int D, int block_size, int num_blocks, int src_dtype,
                           int cache_dtype) {
-    if (cache_dtype != src_dtype && cache_dtype != OR_I8) return -3;
-    if (cache_dtype == OR_I8 && src_dtype == OR_I8) return -3;
+    if (cache_dtype != src_dtype && !scaled(cache_dtype)) return -3;
+    if (scaled(src_dtype)) return -3;
     size_t es = elem_size(cache_dtype);
     for (long i = 0; i < T; ++i) {
         int64_t slot = slot_mapping[i];
@@ -365,9 +448,11 @@ int oracle_kv_cache_write(const void* k, const void* v, void* k_cache, void* v_c
         for (int h = 0; h < Hkv; ++h) {
             size_t src = ((size_t)i * Hkv + h) * D;
             size_t dst_row = ((size_t)blk * Hkv + h) * block_size + (size_t)off;
-            if (cache_dtype == OR_I8) {
-                quantize_row((int8_t*)k_cache + dst_row * D, k_scale + dst_row, k, src, D, src_dtype);
-                quantize_row((int8_t*)v_cache + dst_row * D, v_scale + dst_row, v, src, D, src_dtype);
+            if (scaled(cache_dtype)) {
+                quantize_row((int8_t*)k_cache + dst_row * D, k_scale + dst_row, k, src, D,
+                             src_dtype, cache_dtype);
+                quantize_row((int8_t*)v_cache + dst_row * D, v_scale + dst_row, v, src, D,
+                             src_dtype, cache_dtype);
             } else {
                 memcpy((char*)k_cache + dst_row * D * es, (const char*)k + src * es, D * es);
                 memcpy((char*)v_cache + dst_row * D * es, (const char*)v + src * es, D * es);
