@@ -34,6 +34,7 @@ WORKLOAD_NAMES = {
     "gqa": "gqa-32q8kv-bf16-paged-decode",
     "long": "long-32k-fp16-split-decode",
     "int8": "llama7b-mha-int8kv-paged-decode",
+    "fp8": "llama7b-mha-fp8e4m3kv-paged-decode",
     "sampling": "llama7b-parallel-sampling-shared-prefix-decode",
 }
 KERNEL_SOURCES = ["paged_decode.hip", "pkv_device.h", "pkv_internal.h", "pkv_api.hip"]
@@ -126,9 +127,9 @@ def main():
                 torch.empty((batch.B, batch.Hq, NP), dtype=torch.float32, device="cuda"),
                 torch.empty((batch.B, batch.Hq, NP, batch.D), dtype=torch.float32, device="cuda"))
     lens = batch.layout.context_lens
-    e_kv = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1}[cfg["cache"]]
+    e_kv = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "f8": 1}[cfg["cache"]]
     e_q = {"f32": 4, "f16": 2, "bf16": 2}[cfg["dtype"]]
-    int8 = cfg["cache"] == "i8"
+    int8 = cfg["cache"] in W.SCALED     # 1-byte codes + a 4-byte scale per row
     dec_bytes = W.algorithmic_bytes(lens, batch.Hq, batch.Hkv, batch.D, e_kv, e_q, int8)
     n_new = int((batch.slot_new >= 0).sum())
     # the new rows written into the cache (codes + scales for INT8)
@@ -211,7 +212,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cfg["cache"] if cfg["cache"] == "i8" else cfg["dtype"],
+        "dtype": cfg["cache"] if cfg["cache"] in W.SCALED else cfg["dtype"],
         "data": "synthetic",
         "config": {
             "workload": WORKLOAD_NAMES[args.config],
@@ -490,10 +491,12 @@ def run_cpu_baseline(batch, cfg_name, target_s, e_kv, e_q, int8):
             t = t.contiguous().cpu()
             if t.dtype in (torch.float16, torch.bfloat16):
                 return t.view(torch.int16).numpy().view(np.uint16)
+            if t.dtype == torch.float8_e4m3fn:
+                return t.view(torch.uint8).numpy()
             return t.numpy()
 
         dt = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16",
-              torch.int8: "i8"}
+              torch.int8: "i8", torch.float8_e4m3fn: "f8"}
         kw = {}
         if int8:
             kw = dict(k_scale=h(batch.k_scale[idx]), v_scale=h(batch.v_scale[idx]))

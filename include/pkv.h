@@ -23,11 +23,15 @@
  *  - Optional INT8 KV cache: symmetric quantization with one fp32 scale per
  *    (token slot, kv head), s = max|x| / 127, code = round(x / s)
  *    (lazyllm section 5.3; juejin absmax passage with its worked example).
+ *  - Optional FP8 (e4m3) KV cache, the wider-range alternative the same
+ *    section names (and the juejin page lists among serving-engine features):
+ *    the same per-(slot, kv head) scale with 448, the format's largest value,
+ *    in place of 127; code = e4m3 nearest to x / s.
  *
  * Tensor layouts (row-major, all device memory unless stated):
  *    q, out          [num_seqs][num_q_heads][head_dim]             q_dtype
  *    k_cache,v_cache [num_blocks][num_kv_heads][block_size][head_dim] cache_dtype
- *    k_scale,v_scale [num_blocks][num_kv_heads][block_size]        float (INT8 only)
+ *    k_scale,v_scale [num_blocks][num_kv_heads][block_size]        float (INT8 / FP8 only)
  *    block_tables    [num_seqs][max_blocks_per_seq]                int32
  *    context_lens    [num_seqs]                                    int32
  *    slot_mapping    [num_tokens]                                  int64
@@ -50,7 +54,8 @@
  *    are unspecified, but no access leaves the buffers described here.
  *  - Supported: block_size 16; head_dim 64, 128 or 256; (q_dtype,
  *    cache_dtype) in {(F32,F32), (F16,F16), (BF16,BF16), (F16,I8),
- *    (BF16,I8)}; num_q_heads a multiple of num_kv_heads.
+ *    (BF16,I8), (F16,F8_E4M3), (BF16,F8_E4M3)}; num_q_heads a multiple of
+ *    num_kv_heads.
  */
 #ifndef PKV_H
 #define PKV_H
@@ -77,7 +82,9 @@ typedef enum {
     PKV_ERR_SEQUENCE = 8     /* unknown sequence id, or one that already exists  */
 } pkv_status;
 
-typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_I8 = 3 } pkv_dtype;
+/* PKV_F8_E4M3: 8-bit floating point e4m3 (OCP "E4M3FN": bias 7, 3 mantissa
+ * bits, no infinities, largest finite value 448), one byte per element. */
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_I8 = 3, PKV_F8_E4M3 = 4 } pkv_dtype;
 
 /*
  * Slot-mapped cache append ("when a new token is generated only its keys and
@@ -86,14 +93,18 @@ typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_I8 = 3 } pkv_dtype;
  * (lazyllm lesson 4, section 5.3; juejin absmax passage).
  *
  *  k, v          [num_tokens][num_kv_heads][head_dim], src_dtype (F32|F16|BF16)
- *  k_cache/v_cache  pool (see layout above), cache_dtype == src_dtype or I8
- *  k_scale/v_scale  required iff cache_dtype == I8, else ignored (may be NULL)
+ *  k_cache/v_cache  pool (see layout above), cache_dtype == src_dtype, I8 or
+ *                F8_E4M3
+ *  k_scale/v_scale  required iff cache_dtype is I8 or F8_E4M3, else ignored
+ *                (may be NULL)
  *  slot_mapping  token i goes to block slot/16, offset slot%16 for every kv
  *                head; slot < 0 skips the token.  Slots must be distinct.
  *
  * INT8 rows: amax = max_d |x_d|; s = amax / 127 (IEEE single division);
  * code_d = clamp(round_half_even(x_d / s), -127, 127); amax == 0 stores s = 0
- * and zero codes.  Bytes of other slots are not touched.
+ * and zero codes.  FP8 rows: s = amax / 448; code_d = the e4m3 value nearest
+ * to clamp(x_d / s, -448, 448), ties to even.  Bytes of other slots are not
+ * touched.
  */
 pkv_status pkv_kv_cache_write(const void* k, const void* v, void* k_cache, void* v_cache,
                               float* k_scale, float* v_scale, const int64_t* slot_mapping,
@@ -130,7 +141,7 @@ size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads
  *
  *  out               [num_seqs][num_q_heads][head_dim], q_dtype, written
  *  q                 [num_seqs][num_q_heads][head_dim], q_dtype
- *  k_scale, v_scale  required iff cache_dtype == I8
+ *  k_scale, v_scale  required iff cache_dtype is I8 or F8_E4M3
  *  scale             the softmax scale, normally 1/sqrt(head_dim)
  *  partition_size    0 (library choice) or a positive multiple of 16
  *  workspace         >= pkv_decode_workspace_size(...) bytes, 256-byte aligned
@@ -158,7 +169,7 @@ pkv_status pkv_paged_attn_decode(void* out, const void* q, const void* k_cache,
  * context_lens[b] >= 1, position N_b - 1 is the new token: its rows
  * k_new[b], v_new[b] ([num_seqs][num_kv_heads][head_dim], q_dtype) are
  * written into slot (block_tables[b][(N_b - 1) / 16], (N_b - 1) % 16) —
- * quantized exactly as pkv_kv_cache_write does for an INT8 cache — and the
+ * quantized exactly as pkv_kv_cache_write does for an INT8 / FP8 cache — and the
  * attention over positions 0..N_b-1 uses them.  Result and cache contents are
  * those of pkv_kv_cache_write with those slots followed by
  * pkv_paged_attn_decode; the attention does not wait for the stored copy.
@@ -302,7 +313,7 @@ int64_t pkv_bm_sequence_length(const pkv_block_manager* bm, int64_t seq_id);
  * Copy whole blocks inside the pool, for the copy pairs of pkv_bm_append:
  * for every pair (src, dst) of copy_pairs ([num_pairs][2] int32, device
  * memory), the num_kv_heads tiles of block src in k_cache and v_cache (and
- * their scale rows when cache_dtype == I8) are copied to block dst.  Pairs
+ * their scale rows when cache_dtype is I8 or F8_E4M3) are copied to block dst.  Pairs
  * with an id outside [0, num_blocks) or src == dst are skipped.  A block may
  * not be the destination of one pair and the source or destination of
  * another in the same call.  Asynchronous on `stream` like the calls above.

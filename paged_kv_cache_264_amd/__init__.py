@@ -26,8 +26,11 @@ BLOCK_SIZE = 16
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
-F32, F16, BF16, I8 = 0, 1, 2, 3
-_DTYPE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16, torch.int8: I8}
+F32, F16, BF16, I8, F8_E4M3 = 0, 1, 2, 3, 4
+_DTYPE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16, torch.int8: I8,
+          torch.float8_e4m3fn: F8_E4M3}
+# caches of 1-byte codes with one float32 scale per (slot, kv head)
+SCALED_DTYPES = (torch.int8, torch.float8_e4m3fn)
 
 
 class PkvError(RuntimeError):
@@ -176,7 +179,7 @@ def kv_cache_write(k, v, k_cache, v_cache, slot_mapping, k_scale=None, v_scale=N
         raise ValueError("k/v and cache shapes disagree")
     if slot_mapping.shape[0] != T:
         raise ValueError("slot_mapping must have one entry per token")
-    if k_cache.dtype == torch.int8:
+    if k_cache.dtype in SCALED_DTYPES:
         _dev(k_scale, "k_scale", dtype=torch.float32, ndim=3)
         _dev(v_scale, "v_scale", dtype=torch.float32, ndim=3)
         if tuple(k_scale.shape) != (NB, Hkv, bs) or v_scale.shape != k_scale.shape:
@@ -200,7 +203,7 @@ def _decode_common(q, k_cache, v_cache, block_tables, context_lens, k_scale, v_s
         raise ValueError("q / cache shapes disagree")
     if block_tables.shape[0] != B or context_lens.shape[0] != B:
         raise ValueError("block_tables and context_lens need one row per sequence")
-    if k_cache.dtype == torch.int8:
+    if k_cache.dtype in SCALED_DTYPES:
         _dev(k_scale, "k_scale", dtype=torch.float32, ndim=3)
         _dev(v_scale, "v_scale", dtype=torch.float32, ndim=3)
     return B, Hq, D, NB, Hkv, bs
@@ -325,7 +328,7 @@ def copy_blocks(k_cache, v_cache, copy_pairs, k_scale=None, v_scale=None):
     NB, Hkv, bs, D = k_cache.shape
     if v_cache.shape != k_cache.shape:
         raise ValueError("k_cache and v_cache shapes disagree")
-    if k_cache.dtype == torch.int8:
+    if k_cache.dtype in SCALED_DTYPES:
         _dev(k_scale, "k_scale", dtype=torch.float32, ndim=3)
         _dev(v_scale, "v_scale", dtype=torch.float32, ndim=3)
         if tuple(k_scale.shape) != (NB, Hkv, bs) or v_scale.shape != k_scale.shape:

@@ -1,4 +1,4 @@
-// Slot-mapped cache append with optional INT8 quantize-on-write.
+// Slot-mapped cache append with optional INT8 / FP8 quantize-on-write.
 //
 // Each new token's K and V rows are written into the pool at the slot the
 // block manager assigned (block = slot / 16, offset = slot % 16), for every kv
@@ -44,18 +44,16 @@ template <Elem SE> struct Src8 {
             }
         }
     }
-    __device__ __forceinline__ void store_raw(void* base, size_t elem_off) const {
-        uint4* p = reinterpret_cast<uint4*>(static_cast<char*>(base) +
-                                            elem_off * ElemInfo<SE>::bytes);
-        p[0] = raw[0];
-        if constexpr (ElemInfo<SE>::bytes == 4) p[1] = raw[1];
-    }
 };
 
-// Quantize 8 elements of a row whose absolute maximum is `amax`; returns the
-// packed codes and the scale.
-template <int LPR>
+// Quantize 8 elements of a row (spread over LPR lanes); returns the packed
+// codes and the row's scale.  INT8: s = amax / 127, codes
+// clamp(rne(x / s), -127, 127).  FP8 e4m3: s = amax / 448, codes
+// e4m3(clamp(x / s, -448, 448)) with the hardware's round-to-nearest-even
+// convert.  Divisions are IEEE single precision.
+template <Elem CE, int LPR>
 __device__ __forceinline__ uint2 quantize8(const float (&x)[8], float& scale_out) {
+    constexpr float kQmax = CE == Elem::F8 ? 448.0f : 127.0f;
     float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
@@ -63,12 +61,23 @@ __device__ __forceinline__ uint2 quantize8(const float (&x)[8], float& scale_out
     uint32_t packed[2] = {0u, 0u};
     float s = 0.f;
     if (amax > 0.f) {
-        s = amax / 127.0f;
+        s = amax / kQmax;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float c = __builtin_rintf(x[i] / s);
-            c = fminf(fmaxf(c, -127.0f), 127.0f);
-            packed[i / 4] |= ((uint32_t)(int32_t)c & 0xffu) << (8 * (i % 4));
+        for (int i = 0; i < 2; ++i) {
+            float r[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                r[j] = x[4 * i + j] / s;
+                if constexpr (CE == Elem::I8) r[j] = __builtin_rintf(r[j]);
+                r[j] = fminf(fmaxf(r[j], -kQmax), kQmax);
+            }
+            if constexpr (CE == Elem::F8) {
+                packed[i] = f32x4_to_f8(r[0], r[1], r[2], r[3]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    packed[i] |= ((uint32_t)(int32_t)r[j] & 0xffu) << (8 * j);
+            }
         }
     }
     scale_out = s;
@@ -92,15 +101,15 @@ __global__ __launch_bounds__(kThreads) void kv_cache_write_kernel(CacheWriteArgs
     const size_t dst_row = ((size_t)blk * a.num_kv_heads + h) * kBlockSize + (size_t)off;
     const size_t dst = dst_row * D + (size_t)j * 8;
 
-    Src8<SE> k, v;
-    k.load(a.k, src);
-    v.load(a.v, src);
-    if constexpr (CE == Elem::I8) {
+    if constexpr (is_scaled(CE)) {
+        Src8<SE> k, v;
+        k.load(a.k, src);
+        v.load(a.v, src);
         k.widen();
         v.widen();
         float ks, vs;
-        const uint2 kc = quantize8<LPR>(k.x, ks);
-        const uint2 vc = quantize8<LPR>(v.x, vs);
+        const uint2 kc = quantize8<CE, LPR>(k.x, ks);
+        const uint2 vc = quantize8<CE, LPR>(v.x, vs);
         *reinterpret_cast<uint2*>(static_cast<int8_t*>(a.k_cache) + dst) = kc;
         *reinterpret_cast<uint2*>(static_cast<int8_t*>(a.v_cache) + dst) = vc;
         if (j == 0) {
@@ -108,8 +117,24 @@ __global__ __launch_bounds__(kThreads) void kv_cache_write_kernel(CacheWriteArgs
             a.v_scale[dst_row] = vs;
         }
     } else {
-        k.store_raw(a.k_cache, dst);
-        v.store_raw(a.v_cache, dst);
+        // plain copy of this lane's 8 elements (16 or 32 bytes)
+        constexpr int kChunks = ElemInfo<SE>::bytes * 8 / 16;
+        constexpr size_t EB = ElemInfo<SE>::bytes;
+        const uint4* ks = reinterpret_cast<const uint4*>(static_cast<const char*>(a.k) + src * EB);
+        const uint4* vs = reinterpret_cast<const uint4*>(static_cast<const char*>(a.v) + src * EB);
+        uint4* kd = reinterpret_cast<uint4*>(static_cast<char*>(a.k_cache) + dst * EB);
+        uint4* vd = reinterpret_cast<uint4*>(static_cast<char*>(a.v_cache) + dst * EB);
+        uint4 kx[kChunks], vx[kChunks];
+#pragma unroll
+        for (int i = 0; i < kChunks; ++i) {
+            kx[i] = ks[i];
+            vx[i] = vs[i];
+        }
+#pragma unroll
+        for (int i = 0; i < kChunks; ++i) {
+            kd[i] = kx[i];
+            vd[i] = vx[i];
+        }
     }
 }
 
@@ -148,6 +173,14 @@ hipError_t launch_kv_cache_write(const CacheWriteArgs& a, int src_dtype, int cac
         case Elem::F32: return launch_d<Elem::F32, Elem::I8>(a, head_dim, stream);
         case Elem::F16: return launch_d<Elem::F16, Elem::I8>(a, head_dim, stream);
         case Elem::BF16: return launch_d<Elem::BF16, Elem::I8>(a, head_dim, stream);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    if (ce == Elem::F8) {
+        switch (se) {
+        case Elem::F32: return launch_d<Elem::F32, Elem::F8>(a, head_dim, stream);
+        case Elem::F16: return launch_d<Elem::F16, Elem::F8>(a, head_dim, stream);
+        case Elem::BF16: return launch_d<Elem::BF16, Elem::F8>(a, head_dim, stream);
         default: return hipErrorInvalidValue;
         }
     }

@@ -104,8 +104,8 @@ __device__ __forceinline__ float i8_at(uint32_t w, int k) {
     return (float)(int8_t)(w >> (8 * k));
 }
 
-// INT8 cache: q widened to fp32 once; the codes are widened in the dot
-template <Elem QE> struct QSlice<QE, Elem::I8, 16> {
+// INT8 / FP8 cache: q widened to fp32 once; the codes are widened in the dot
+template <Elem QE, Elem CE> struct QSliceScaled {
     float v[16];
     __device__ __forceinline__ void load(const void* q, size_t elem_off) {
         const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) + elem_off);
@@ -127,20 +127,34 @@ template <Elem QE> struct QSlice<QE, Elem::I8, 16> {
         float d0 = 0.f, d1 = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            d0 = fmaf(v[4 * i + 0], i8_at(w[i], 0), d0);
-            d1 = fmaf(v[4 * i + 1], i8_at(w[i], 1), d1);
-            d0 = fmaf(v[4 * i + 2], i8_at(w[i], 2), d0);
-            d1 = fmaf(v[4 * i + 3], i8_at(w[i], 3), d1);
+            float x0, x1, x2, x3;
+            if constexpr (CE == Elem::F8) {
+                f8x4_to_f32(w[i], x0, x1, x2, x3);
+            } else {
+                x0 = i8_at(w[i], 0);
+                x1 = i8_at(w[i], 1);
+                x2 = i8_at(w[i], 2);
+                x3 = i8_at(w[i], 3);
+            }
+            d0 = fmaf(v[4 * i + 0], x0, d0);
+            d1 = fmaf(v[4 * i + 1], x1, d1);
+            d0 = fmaf(v[4 * i + 2], x2, d0);
+            d1 = fmaf(v[4 * i + 3], x3, d1);
         }
         return d0 + d1;
     }
 };
+template <Elem QE> struct QSlice<QE, Elem::I8, 16> : QSliceScaled<QE, Elem::I8> {};
+template <Elem QE> struct QSlice<QE, Elem::F8, 16> : QSliceScaled<QE, Elem::F8> {};
 
-// INT8 codes of one row of the new token: this lane's 16 elements, whose row
-// spans L lanes.  Same arithmetic as the quantizing cache write: exact
-// absolute maximum, s = amax / 127 (IEEE division), round half to even.
-template <int L>
+// Codes of one row of the new token: this lane's 16 elements, whose row spans
+// L lanes.  Same arithmetic as the quantizing cache write: exact absolute
+// maximum, s = amax / qmax (IEEE division; qmax 127 for INT8, 448 for FP8
+// e4m3), then x / s rounded half to even and clamped (INT8), or clamped to
+// +-448 and converted to e4m3 with round-to-nearest-even (FP8).
+template <Elem CE, int L>
 __device__ __forceinline__ uint4 quantize16(const float (&x)[16], float& scale_out) {
+    constexpr float kQmax = CE == Elem::F8 ? 448.0f : 127.0f;
     float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
@@ -148,12 +162,23 @@ __device__ __forceinline__ uint4 quantize16(const float (&x)[16], float& scale_o
     uint32_t w[4] = {0u, 0u, 0u, 0u};
     float s = 0.f;
     if (amax > 0.f) {
-        s = amax / 127.0f;
+        s = amax / kQmax;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float cde = __builtin_rintf(x[i] / s);
-            cde = fminf(fmaxf(cde, -127.0f), 127.0f);
-            w[i / 4] |= ((uint32_t)(int32_t)cde & 0xffu) << (8 * (i % 4));
+        for (int i = 0; i < 4; ++i) {
+            float r[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                r[j] = x[4 * i + j] / s;
+                if constexpr (CE == Elem::I8) r[j] = __builtin_rintf(r[j]);
+                r[j] = fminf(fmaxf(r[j], -kQmax), kQmax);
+            }
+            if constexpr (CE == Elem::F8) {
+                w[i] = f32x4_to_f8(r[0], r[1], r[2], r[3]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    w[i] |= ((uint32_t)(int32_t)r[j] & 0xffu) << (8 * j);
+            }
         }
     }
     scale_out = s;
@@ -173,6 +198,8 @@ template <Elem CE, int E> __device__ __forceinline__ void widen(const uint4& c, 
         } else if constexpr (CE == Elem::BF16) {
             x[2 * i] = lo_bf(w[i]);
             x[2 * i + 1] = hi_bf(w[i]);
+        } else if constexpr (CE == Elem::F8) {
+            f8x4_to_f32(w[i], x[4 * i + 0], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
         } else {
             x[4 * i + 0] = i8_at(w[i], 0);
             x[4 * i + 1] = i8_at(w[i], 1);
@@ -237,7 +264,7 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
     using G = Geom<CE, D>;
     constexpr int L = G::L, E = G::E, R = G::R, U = G::U, STEPS = G::STEPS;
     constexpr int NW = kDecodeWaves;
-    constexpr bool kInt8 = (CE == Elem::I8);
+    constexpr bool kInt8 = is_scaled(CE);  // 1-byte codes with a per-row scale
 
     __shared__ float s_m[NW][GT];
     __shared__ float s_l[NW][GT];
@@ -509,8 +536,8 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
                 xv[2 * i] = QE == Elem::F16 ? lo_h(wv[i]) : lo_bf(wv[i]);
                 xv[2 * i + 1] = QE == Elem::F16 ? hi_h(wv[i]) : hi_bf(wv[i]);
             }
-            kc = quantize16<L>(xk, ks);
-            vc = quantize16<L>(xv, vs);
+            kc = quantize16<CE, L>(xk, ks);
+            vc = quantize16<CE, L>(xv, vs);
         }
         const int new_jb = (n - 1) / kBlockSize, new_off = (n - 1) % kBlockSize;
         const int phys = table[new_jb];
@@ -620,9 +647,9 @@ hipError_t launch3(const DecodeArgs& a, int gt, hipStream_t s) {
     case 2: return launch4<QE, CE, D, 2>(a, s);
     case 4: return launch4<QE, CE, D, 4>(a, s);
     case 8:
-        // INT8 tiles stop at 4 heads: 8 would hold 8 x 16 fp32 accumulators
-        // per lane and spill
-        if constexpr (CE != Elem::I8) return launch4<QE, CE, D, 8>(a, s);
+        // 1-byte-code tiles stop at 4 heads: 8 would hold 8 x 16 fp32
+        // accumulators per lane and spill
+        if constexpr (!is_scaled(CE)) return launch4<QE, CE, D, 8>(a, s);
         return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
     }
@@ -653,6 +680,10 @@ hipError_t launch_paged_decode(const DecodeArgs& a, int q_dtype, int cache_dtype
         return launch2<Elem::F16, Elem::I8>(a, head_dim, heads_per_tile, stream);
     if (qe == Elem::BF16 && ce == Elem::I8)
         return launch2<Elem::BF16, Elem::I8>(a, head_dim, heads_per_tile, stream);
+    if (qe == Elem::F16 && ce == Elem::F8)
+        return launch2<Elem::F16, Elem::F8>(a, head_dim, heads_per_tile, stream);
+    if (qe == Elem::BF16 && ce == Elem::F8)
+        return launch2<Elem::BF16, Elem::F8>(a, head_dim, heads_per_tile, stream);
     return hipErrorInvalidValue;
 }
 

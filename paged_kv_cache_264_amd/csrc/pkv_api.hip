@@ -44,12 +44,15 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool is_float(pkv_dtype d) { return d == PKV_F32 || d == PKV_F16 || d == PKV_BF16; }
 
+// 1-byte codes with one fp32 scale per (slot, kv head)
+bool is_scaled(pkv_dtype d) { return d == PKV_I8 || d == PKV_F8_E4M3; }
+
 bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 int heads_per_tile(int g, pkv_dtype cache) {
-    const int cap = cache == PKV_I8 ? 4 : 8;
+    const int cap = is_scaled(cache) ? 4 : 8;
     for (int t = cap; t > 1; t >>= 1)
         if (g % t == 0) return t;
     return 1;
@@ -92,15 +95,15 @@ pkv_status check_decode(const void* q, const void* k_cache, const void* v_cache,
     if (!head_dim_ok(D))
         return fail(PKV_ERR_UNSUPPORTED, "head_dim %d unsupported (64, 128, 256)", D);
     const bool pair_ok = (is_float(q_dtype) && cache_dtype == q_dtype) ||
-                         ((q_dtype == PKV_F16 || q_dtype == PKV_BF16) && cache_dtype == PKV_I8);
+                         ((q_dtype == PKV_F16 || q_dtype == PKV_BF16) && is_scaled(cache_dtype));
     if (!pair_ok)
         return fail(PKV_ERR_DTYPE, "unsupported (q_dtype, cache_dtype) = (%d, %d)", (int)q_dtype,
                     (int)cache_dtype);
     if (B == 0) return ok();
     if (!q || !k_cache || !v_cache || !block_tables || !context_lens)
         return fail(PKV_ERR_NULL, "q, k_cache, v_cache, block_tables and context_lens are required");
-    if (cache_dtype == PKV_I8 && (!k_scale || !v_scale))
-        return fail(PKV_ERR_NULL, "k_scale and v_scale are required for an INT8 cache");
+    if (is_scaled(cache_dtype) && (!k_scale || !v_scale))
+        return fail(PKV_ERR_NULL, "k_scale and v_scale are required for an INT8 / FP8 cache");
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
         return fail(PKV_ERR_SHAPE, "q, k_cache and v_cache must be 16-byte aligned");
     if ((int64_t)Hkv * num_blocks * pkv::kBlockSize * D > (int64_t)1 << 62)
@@ -197,14 +200,14 @@ pkv_status pkv_kv_cache_write(const void* k, const void* v, void* k_cache, void*
         return fail(PKV_ERR_UNSUPPORTED, "block_size %d unsupported (only 16)", block_size);
     if (!head_dim_ok(head_dim))
         return fail(PKV_ERR_UNSUPPORTED, "head_dim %d unsupported (64, 128, 256)", head_dim);
-    if (!is_float(src_dtype) || !(cache_dtype == src_dtype || cache_dtype == PKV_I8))
+    if (!is_float(src_dtype) || !(cache_dtype == src_dtype || is_scaled(cache_dtype)))
         return fail(PKV_ERR_DTYPE, "unsupported (src_dtype, cache_dtype) = (%d, %d)",
                     (int)src_dtype, (int)cache_dtype);
     if (num_tokens == 0) return ok();
     if (!k || !v || !k_cache || !v_cache || !slot_mapping)
         return fail(PKV_ERR_NULL, "k, v, k_cache, v_cache and slot_mapping are required");
-    if (cache_dtype == PKV_I8 && (!k_scale || !v_scale))
-        return fail(PKV_ERR_NULL, "k_scale and v_scale are required for an INT8 cache");
+    if (is_scaled(cache_dtype) && (!k_scale || !v_scale))
+        return fail(PKV_ERR_NULL, "k_scale and v_scale are required for an INT8 / FP8 cache");
     if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
         return fail(PKV_ERR_SHAPE, "k, v, k_cache and v_cache must be 16-byte aligned");
     pkv::CacheWriteArgs a{k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping,
@@ -226,27 +229,27 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* 
         return fail(PKV_ERR_UNSUPPORTED, "block_size %d unsupported (only 16)", block_size);
     if (!head_dim_ok(head_dim))
         return fail(PKV_ERR_UNSUPPORTED, "head_dim %d unsupported (64, 128, 256)", head_dim);
-    if (!is_float(cache_dtype) && cache_dtype != PKV_I8)
+    if (!is_float(cache_dtype) && !is_scaled(cache_dtype))
         return fail(PKV_ERR_DTYPE, "unsupported cache_dtype %d", (int)cache_dtype);
     if (num_pairs == 0) return ok();
     if (!k_cache || !v_cache || !copy_pairs)
         return fail(PKV_ERR_NULL, "k_cache, v_cache and copy_pairs are required");
-    if (cache_dtype == PKV_I8 && (!k_scale || !v_scale))
-        return fail(PKV_ERR_NULL, "k_scale and v_scale are required for an INT8 cache");
+    if (is_scaled(cache_dtype) && (!k_scale || !v_scale))
+        return fail(PKV_ERR_NULL, "k_scale and v_scale are required for an INT8 / FP8 cache");
     if (!aligned16(k_cache) || !aligned16(v_cache) ||
-        (cache_dtype == PKV_I8 && (!aligned16(k_scale) || !aligned16(v_scale))))
+        (is_scaled(cache_dtype) && (!aligned16(k_scale) || !aligned16(v_scale))))
         return fail(PKV_ERR_SHAPE, "caches and scales must be 16-byte aligned");
-    const int64_t elem = cache_dtype == PKV_F32 ? 4 : cache_dtype == PKV_I8 ? 1 : 2;
+    const int64_t elem = cache_dtype == PKV_F32 ? 4 : is_scaled(cache_dtype) ? 1 : 2;
     pkv::CopyBlocksArgs a{};
     a.k_cache = k_cache;
     a.v_cache = v_cache;
-    a.k_scale = cache_dtype == PKV_I8 ? k_scale : nullptr;
-    a.v_scale = cache_dtype == PKV_I8 ? v_scale : nullptr;
+    a.k_scale = is_scaled(cache_dtype) ? k_scale : nullptr;
+    a.v_scale = is_scaled(cache_dtype) ? v_scale : nullptr;
     a.pairs = copy_pairs;
     a.num_pairs = num_pairs;
     a.num_blocks = num_blocks;
     a.block_bytes = (int64_t)num_kv_heads * pkv::kBlockSize * head_dim * elem;
-    a.scale_bytes = cache_dtype == PKV_I8 ? (int64_t)num_kv_heads * pkv::kBlockSize * 4 : 0;
+    a.scale_bytes = is_scaled(cache_dtype) ? (int64_t)num_kv_heads * pkv::kBlockSize * 4 : 0;
     if (a.block_bytes > ((int64_t)1 << 40) / num_blocks)
         return fail(PKV_ERR_SHAPE, "pool too large");
     const hipError_t e = pkv::launch_copy_blocks(a, stream);

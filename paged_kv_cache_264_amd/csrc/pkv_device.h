@@ -7,7 +7,9 @@
 
 namespace pkv {
 
-enum class Elem : int { F32 = 0, F16 = 1, BF16 = 2, I8 = 3 };
+// F8: 8-bit floating point e4m3 (OCP "E4M3FN", largest finite value 448),
+// the format of gfx950's fp8 convert instructions.
+enum class Elem : int { F32 = 0, F16 = 1, BF16 = 2, I8 = 3, F8 = 4 };
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
@@ -17,6 +19,10 @@ template <> struct ElemInfo<Elem::F32> { static constexpr int bytes = 4; };
 template <> struct ElemInfo<Elem::F16> { static constexpr int bytes = 2; };
 template <> struct ElemInfo<Elem::BF16> { static constexpr int bytes = 2; };
 template <> struct ElemInfo<Elem::I8> { static constexpr int bytes = 1; };
+template <> struct ElemInfo<Elem::F8> { static constexpr int bytes = 1; };
+
+// caches of 1-byte codes with one fp32 scale per (slot, kv head)
+constexpr bool is_scaled(Elem e) { return e == Elem::I8 || e == Elem::F8; }
 
 constexpr int kWave = 64;
 
@@ -35,6 +41,23 @@ __device__ __forceinline__ float hi_h(uint32_t w) { return h2f((uint16_t)(w >> 1
 __device__ __forceinline__ float lo_bf(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float hi_bf(uint32_t w) {
     return __builtin_bit_cast(float, w & 0xffff0000u);
+}
+
+// four e4m3 codes of a dword -> fp32 (exact), bytes 0..3 in order
+__device__ __forceinline__ void f8x4_to_f32(uint32_t w, float& x0, float& x1, float& x2,
+                                            float& x3) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    x0 = lo[0];
+    x1 = lo[1];
+    x2 = hi[0];
+    x3 = hi[1];
+}
+// four fp32 values (|x| <= 448) -> e4m3 codes, round to nearest even, bytes 0..3
+__device__ __forceinline__ uint32_t f32x4_to_f8(float x0, float x1, float x2, float x3) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
+    return (uint32_t)w;
 }
 
 // float -> storage with round-to-nearest-even

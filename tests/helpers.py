@@ -10,12 +10,15 @@ import oracle
 import workloads as W
 
 BS = W.BLOCK_SIZE
-DT = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16", torch.int8: "i8"}
+DT = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16", torch.int8: "i8",
+      torch.float8_e4m3fn: "f8"}
 # max-abs-error bounds by element type (fp32 is the proposed bound for the fp32
 # case).  A case is held to the looser bound of its cache type and its q/out
 # type: a bf16 output alone carries up to 2^-9 relative rounding error, which
 # exceeds 2e-3 for |out| > 1, so bf16 q with an INT8 cache takes the bf16 bound.
-TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 1.6e-2, "i8": 2e-3}
+# INT8 and FP8 caches are compared with the oracle on the same dequantized
+# values, so only accumulation order and output rounding differ: 2e-3.
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 1.6e-2, "i8": 2e-3, "f8": 2e-3}
 
 
 def tol_for(q_dtype: str, cache_dtype: str) -> float:
@@ -23,10 +26,12 @@ def tol_for(q_dtype: str, cache_dtype: str) -> float:
 
 
 def host(t: torch.Tensor) -> np.ndarray:
-    """Host numpy copy; 16-bit floats as their raw uint16 bits."""
+    """Host numpy copy; 16-bit floats as their raw uint16 bits, e4m3 as uint8."""
     t = t.detach().contiguous().cpu()
     if t.dtype in (torch.float16, torch.bfloat16):
         return t.view(torch.int16).numpy().view(np.uint16).copy()
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy().copy()
     return t.numpy().copy()
 
 
@@ -63,10 +68,11 @@ class OracleView:
         self.scale = batch.scale
         nb = max(len(self.block_ids), 1)
         idx = torch.from_numpy(self.block_ids).to(batch.k_cache.device)
-        if self.cache_dtype == "i8":
-            # the oracle builds its own INT8 pool from the fp source rows
+        if self.cache_dtype in W.SCALED:
+            # the oracle builds its own INT8 / FP8 pool from the fp source rows
             Hkv, D = batch.Hkv, batch.D
-            self.k_cache = np.zeros((nb, Hkv, BS, D), np.int8)
+            self.k_cache = np.zeros((nb, Hkv, BS, D), np.int8 if self.cache_dtype == "i8"
+                                    else np.uint8)
             self.v_cache = np.zeros_like(self.k_cache)
             self.k_scale = np.full((nb, Hkv, BS), np.nan, np.float32)
             self.v_scale = np.full_like(self.k_scale, np.nan)
@@ -76,7 +82,8 @@ class OracleView:
             ridx = torch.from_numpy(rows).to(batch.k_src.device)
             slots = batch.slot_src.cpu().numpy()[rows]
             oracle.kv_cache_write(host(batch.k_src[ridx]), host(batch.v_src[ridx]), self.k_cache,
-                                  self.v_cache, self.compact_slots(slots), self.src_dtype, "i8",
+                                  self.v_cache, self.compact_slots(slots), self.src_dtype,
+                                  self.cache_dtype,
                                   self.k_scale, self.v_scale)
         else:
             self.k_cache = host(batch.k_cache[idx]) if len(idx) else None
@@ -106,7 +113,7 @@ class OracleView:
 
 
 def gpu_populate(pkv, batch: W.Batch):
-    """INT8 batches: quantize the source rows into the pool with the library."""
+    """INT8 / FP8 batches: quantize the source rows into the pool with the library."""
     if batch.k_src is not None and batch.k_src.shape[0] > 0:
         pkv.kv_cache_write(batch.k_src, batch.v_src, batch.k_cache, batch.v_cache,
                            batch.slot_src, batch.k_scale, batch.v_scale)

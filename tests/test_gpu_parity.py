@@ -50,7 +50,8 @@ def _check_step(pkv, batch, seqs=None, partition_size=0, tol=None):
     return out, view
 
 
-PAIRS = [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"), ("f16", "i8"), ("bf16", "i8")]
+PAIRS = [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"), ("f16", "i8"), ("bf16", "i8"),
+         ("f16", "f8"), ("bf16", "f8")]
 LENS = [1, 15, 16, 17, 250, 700, 33]
 
 
@@ -64,7 +65,7 @@ def test_decode_matrix(pkv, dtype, cache, D, Hq, Hkv):
 
 
 @pytest.mark.parametrize("P", [16, 48, 64, 256, 1024])
-@pytest.mark.parametrize("dtype,cache", [("f16", "f16"), ("bf16", "i8")])
+@pytest.mark.parametrize("dtype,cache", [("f16", "f16"), ("bf16", "i8"), ("f16", "f8")])
 def test_partition_sizes(pkv, P, dtype, cache):
     batch = W.make_batch(cfg=_cfg(dtype, cache, 128, 8, 2, [5, 64, 129, 1000, 1500], seed=P),
                          device="cuda")
@@ -226,7 +227,8 @@ def test_reduce_on_synthetic_partials(pkv):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("src,cache", [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"),
-                                       ("f32", "i8"), ("f16", "i8"), ("bf16", "i8")])
+                                       ("f32", "i8"), ("f16", "i8"), ("bf16", "i8"),
+                                       ("f32", "f8"), ("f16", "f8"), ("bf16", "f8")])
 @pytest.mark.parametrize("D", [64, 128, 256])
 def test_cache_write_bit_exact(pkv, src, cache, D):
     NB, Hkv, T = 40, 4, 64
@@ -239,13 +241,21 @@ def test_cache_write_bit_exact(pkv, src, cache, D):
     if cache == "i8":
         k[0] = 0.0                                           # zero row -> s = 0
         k[1, :, :] = 0.5; k[1, :, 0] = 127.0                  # ties with s = 1
+    if cache == "f8":
+        k[0] = 0.0
+        # s = 1: the row holds 448 and e4m3 ties (midpoints between neighbours)
+        mids = torch.tensor([1.0625, 1.1875, 17.0, 0.0029296875, -2.25, 3.25, 0.013671875])
+        k[1, :, :] = 0.5; k[1, :, 0] = 448.0
+        k[1, :, 1:1 + len(mids)] = mids.to(k.dtype)
     # sentinel bytes everywhere in the pool
     kc = torch.from_numpy(g.integers(0, 256, (NB, Hkv, BS, D * (4 if cache == "f32" else
                                      2 if cache in ("f16", "bf16") else 1)), dtype=np.uint8))
+    if cache == "f8":                                        # sentinel codes, no NaN
+        kc[(kc & 0x7F) == 0x7F] = 0x3C
     vc = torch.from_numpy(g.integers(0, 256, kc.shape, dtype=np.uint8))
     kc = kc.view(tdt[cache]).contiguous(); vc = vc.view(tdt[cache]).contiguous()
     ks = vs = None
-    if cache == "i8":
+    if cache in W.SCALED:
         ks = torch.from_numpy(g.standard_normal((NB, Hkv, BS), dtype=np.float32))
         vs = torch.from_numpy(g.standard_normal((NB, Hkv, BS), dtype=np.float32))
     hk, hv = host(kc), host(vc)
@@ -259,7 +269,7 @@ def test_cache_write_bit_exact(pkv, src, cache, D):
     torch.cuda.synchronize()
     assert np.array_equal(host(gk).view(np.uint8), hk.view(np.uint8))
     assert np.array_equal(host(gv).view(np.uint8), hv.view(np.uint8))
-    if cache == "i8":
+    if cache in W.SCALED:
         assert np.array_equal(host(gks).view(np.uint32), hks.view(np.uint32))
         assert np.array_equal(host(gvs).view(np.uint32), hvs.view(np.uint32))
 
@@ -295,7 +305,7 @@ def test_int8_codes_bit_exact_many_rows(pkv):
 # the five workloads at full size, in the launch configuration the bench uses
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["tiny", "llama7b", "gqa", "long", "int8"])
+@pytest.mark.parametrize("name", ["tiny", "llama7b", "gqa", "long", "int8", "fp8"])
 def test_full_config(pkv, name):
     batch = W.make_batch(name, device="cuda", poison=True)
     gpu_populate(pkv, batch)
@@ -365,7 +375,7 @@ def test_decode_append_matches_write_then_decode(pkv, dtype, cache, D, Hq, Hkv, 
     assert err <= tol_for(dtype, cache)
     idx = torch.from_numpy(view.block_ids).cuda()
     assert np.array_equal(host(batch.k_cache[idx]).view(np.uint8), view.k_cache.view(np.uint8)) \
-        if cache != "i8" else True
+        if cache not in W.SCALED else True
     # every slot the oracle wrote holds the same bytes on the GPU
     for i, (s_, n) in enumerate(zip(view.seqs, view.context_lens)):
         if n == 0:
@@ -377,7 +387,7 @@ def test_decode_append_matches_write_then_decode(pkv, dtype, cache, D, Hq, Hkv, 
                               view.k_cache[blk_o, :, t % BS].view(np.uint8))
         assert np.array_equal(host(batch.v_cache[blk_g, :, t % BS]).view(np.uint8),
                               view.v_cache[blk_o, :, t % BS].view(np.uint8))
-        if cache == "i8":
+        if cache in W.SCALED:
             assert np.array_equal(host(batch.k_scale[blk_g, :, t % BS]).view(np.uint32),
                                   view.k_scale[blk_o, :, t % BS].view(np.uint32))
             assert np.array_equal(host(batch.v_scale[blk_g, :, t % BS]).view(np.uint32),

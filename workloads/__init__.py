@@ -50,10 +50,16 @@ CONFIGS = {
     # quantizing cache write.
     "int8": dict(B=64, ctx=(512, 4096), Hq=32, Hkv=32, D=128, dtype="f16", cache="i8",
                  pool=None, seed=5, max_ctx=4096),
+    # FP8 (e4m3) KV cache at the LLaMA-7B shape, populated the same way.
+    "fp8": dict(B=64, ctx=(512, 4096), Hq=32, Hkv=32, D=128, dtype="f16", cache="f8",
+                pool=None, seed=8, max_ctx=4096),
 }
 
 TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
-               "i8": torch.int8}
+               "i8": torch.int8, "f8": torch.float8_e4m3fn}
+# caches of 1-byte codes with one fp32 scale per (slot, kv head), populated by
+# the quantizing cache write
+SCALED = ("i8", "f8")
 
 
 def rng(seed: int, stream: int) -> np.random.Generator:
@@ -206,8 +212,8 @@ def make_batch(name: str | None = None, device="cpu", seed: int | None = None, p
 
     poison=True fills every pool slot that holds no token with NaN (K and V for
     float caches; the per-token scales for INT8 caches) so that a kernel which
-    reads outside the context cannot go unnoticed; poison=False fills them with
-    zeros (timing runs).
+    reads outside the context cannot go unnoticed (the per-token scales for
+    INT8 / FP8 caches); poison=False fills them with zeros (timing runs).
     """
     if cfg is None:
         cfg = CONFIGS[name]
@@ -247,9 +253,11 @@ def make_batch(name: str | None = None, device="cpu", seed: int | None = None, p
                          for b, n in enumerate(lens)], np.int64)
 
     k_scale = v_scale = k_src = v_src = slot_src = src_offsets = None
-    if cache == "i8":
-        k_cache = torch.zeros((nb, Hkv, BLOCK_SIZE, D), dtype=torch.int8, device=device)
-        v_cache = torch.zeros_like(k_cache)
+    if cache in SCALED:
+        k_cache = torch.zeros((nb, Hkv, BLOCK_SIZE, D), dtype=torch.uint8,
+                              device=device).view(TORCH_DTYPE[cache])
+        v_cache = torch.zeros((nb, Hkv, BLOCK_SIZE, D), dtype=torch.uint8,
+                              device=device).view(TORCH_DTYPE[cache])
         fill = float("nan") if poison else 0.0
         k_scale = torch.full((nb, Hkv, BLOCK_SIZE), fill, dtype=torch.float32, device=device)
         v_scale = torch.full_like(k_scale, fill)
