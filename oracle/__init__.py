@@ -52,6 +52,8 @@ def lib():
         P, I, L64, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_long, ctypes.c_float
         L.oracle_paged_decode.argtypes = [P, P, I, P, P, I, P, P, P, I, P, I, I, I, I, I, I, F,
                                           P, L64, I]
+        L.oracle_paged_decode_window.argtypes = [P, P, I, P, P, I, P, P, P, I, P, I, I, I, I, I, I,
+                                                 F, I, P, L64, I]
         L.oracle_paged_partials.argtypes = [P, P, P, P, I, P, P, I, P, P, P, I, P, I, I, I, I, I,
                                             I, F, I, I, I]
         L.oracle_merge_partials.argtypes = [P, P, P, P, L64, I, I]
@@ -99,11 +101,12 @@ def bf16_to_f64(bits: int) -> float:
 
 
 def paged_decode(q, q_dtype, k_cache, v_cache, cache_dtype, block_tables, context_lens, scale,
-                 k_scale=None, v_scale=None, block_size=16, rows=None, nthreads=0):
+                 k_scale=None, v_scale=None, block_size=16, rows=None, nthreads=0, window=0):
     """fp64 gather-then-dense attention.  Shapes: q [B][Hq][D]; caches
     [NB][Hkv][block_size][D]; block_tables int32 [B][MBS]; context_lens int32 [B];
     scales float32 [NB][Hkv][block_size] for "i8" and "f8".  Returns float64 [B][Hq][D]
-    (rows not requested are NaN)."""
+    (rows not requested are NaN).  window > 0: attend to the last `window`
+    positions of each sequence only (sliding window)."""
     q = _check(q, q_dtype, "q")
     k_cache = _check(k_cache, cache_dtype, "k_cache")
     v_cache = _check(v_cache, cache_dtype, "v_cache")
@@ -118,11 +121,11 @@ def paged_decode(q, q_dtype, k_cache, v_cache, cache_dtype, block_tables, contex
         assert ks is not None and vs is not None
     out = np.full((B, Hq, D), np.nan, dtype=np.float64)
     r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
-    rc = lib().oracle_paged_decode(_ptr(out), _ptr(q), DTYPES[q_dtype], _ptr(k_cache),
-                                   _ptr(v_cache), DTYPES[cache_dtype], _ptr(ks), _ptr(vs),
-                                   _ptr(bt), bt.shape[1], _ptr(cl), B, Hq, Hkv, D, block_size,
-                                   NB, float(scale), _ptr(r), 0 if r is None else len(r),
-                                   nthreads)
+    rc = lib().oracle_paged_decode_window(_ptr(out), _ptr(q), DTYPES[q_dtype], _ptr(k_cache),
+                                          _ptr(v_cache), DTYPES[cache_dtype], _ptr(ks), _ptr(vs),
+                                          _ptr(bt), bt.shape[1], _ptr(cl), B, Hq, Hkv, D,
+                                          block_size, NB, float(scale), int(window), _ptr(r),
+                                          0 if r is None else len(r), nthreads)
     if rc != 0:
         raise RuntimeError(f"oracle_paged_decode failed with {rc}")
     return out

@@ -29,11 +29,17 @@ physical blocks any manager can use is the number of distinct
 what it may and copies a shared block only when a sequence writes into it
 uses exactly that many.  ``blocks_in_use`` returns it.
 
+A sequence that attends through a sliding window (only the most recent
+window of its cache is kept: caojiahao2.github.io section 2.3, fixed memory)
+may release its positions before some p: whole blocks that end at or before p
+leave the physical count (the partly filled last block never does).
+
 Pinned by ``tests/test_oracle_block_manager.py`` against closed forms:
 independent sequences use sum(ceil(len / 16)) blocks; n samples of an
 L-token prompt, t new tokens each, use floor(L / 16) + n * ceil((L mod 16 +
 t) / 16) blocks (t >= 1, L mod 16 > 0); a fork without writes adds nothing;
-freeing every sequence leaves nothing.
+freeing every sequence leaves nothing; a sequence of N tokens that released
+everything before N - W holds ceil(N / 16) - floor((N - W) / 16) blocks.
 """
 from __future__ import annotations
 
@@ -46,6 +52,7 @@ class SequenceSet:
     def __init__(self, block_size: int = 16):
         self.block_size = block_size
         self.seqs: Dict[int, List[int]] = {}
+        self.released: Dict[int, int] = {}   # whole blocks released at the front
         self._next_token = 0
 
     def add(self, seq: int) -> None:
@@ -53,12 +60,21 @@ class SequenceSet:
         if seq in self.seqs:
             raise KeyError(f"sequence {seq} exists")
         self.seqs[seq] = []
+        self.released[seq] = 0
 
     def fork(self, parent: int, child: int) -> None:
         """The child continues from everything the parent holds now."""
         if child in self.seqs:
             raise KeyError(f"sequence {child} exists")
         self.seqs[child] = list(self.seqs[parent])
+        self.released[child] = self.released[parent]
+
+    def release_before(self, seq: int, position: int) -> None:
+        """Positions before `position` are no longer needed: every whole block
+        that ends at or before it (and before the last token) is dropped."""
+        full = len(self.seqs[seq]) // self.block_size
+        drop = min(max(position, 0) // self.block_size, full)
+        self.released[seq] = max(self.released[seq], drop)
 
     def append(self, seq: int, n: int) -> List[int]:
         """Write n new tokens at the end of seq; returns their ids."""
@@ -69,6 +85,7 @@ class SequenceSet:
 
     def free(self, seq: int) -> None:
         del self.seqs[seq]
+        del self.released[seq]
 
     def tokens(self, seq: int) -> List[int]:
         return self.seqs[seq]
@@ -80,8 +97,8 @@ class SequenceSet:
     def distinct_blocks(self) -> set:
         bs = self.block_size
         out = set()
-        for ids in self.seqs.values():
-            for j in range(0, len(ids), bs):
+        for seq, ids in self.seqs.items():
+            for j in range(self.released[seq] * bs, len(ids), bs):
                 out.add((j // bs, tuple(ids[j:j + bs])))
         return out
 
@@ -90,10 +107,11 @@ class SequenceSet:
         return len(self.distinct_blocks())
 
     def blocks_without_sharing(self) -> int:
-        return sum(self.blocks_of(s) for s in self.seqs)
+        return sum(self.blocks_of(s) - self.released[s] for s in self.seqs)
 
     def copy(self) -> "SequenceSet":
         c = SequenceSet(self.block_size)
         c.seqs = {k: list(v) for k, v in self.seqs.items()}
+        c.released = dict(self.released)
         c._next_token = self._next_token
         return c

@@ -239,14 +239,17 @@ static int set_threads(int nthreads) {
 
 /* Full decode attention.  out: double [B][Hq][D].  rows: optional list of
  * n_rows flattened (b * Hq + h) indices to compute; NULL computes all rows.
- * Rows not listed are left untouched.  Returns 0, or a negative code when a
+ * Rows not listed are left untouched.  window > 0 attends to the last
+ * `window` positions only, [max(0, N - window), N): the sliding window of the
+ * caojiahao2 page, section 2.3 (keep only the most recent window of the KV
+ * cache); window == 0 attends to all N.  Returns 0, or a negative code when a
  * block table entry points outside the pool (-1) or memory ran out (-2). */
-int oracle_paged_decode(double* out, const void* q, int q_dtype, const void* k_cache,
-                        const void* v_cache, int cache_dtype, const float* k_scale,
-                        const float* v_scale, const int32_t* block_tables,
-                        int max_blocks_per_seq, const int32_t* context_lens, int B, int Hq,
-                        int Hkv, int D, int block_size, int num_blocks, float scale,
-                        const int64_t* rows, long n_rows, int nthreads) {
+int oracle_paged_decode_window(double* out, const void* q, int q_dtype, const void* k_cache,
+                               const void* v_cache, int cache_dtype, const float* k_scale,
+                               const float* v_scale, const int32_t* block_tables,
+                               int max_blocks_per_seq, const int32_t* context_lens, int B, int Hq,
+                               int Hkv, int D, int block_size, int num_blocks, float scale,
+                               int window, const int64_t* rows, long n_rows, int nthreads) {
     problem P = {q, q_dtype, k_cache, v_cache, cache_dtype, k_scale, v_scale, block_tables,
                  max_blocks_per_seq, context_lens, B, Hq, Hkv, D, block_size, num_blocks,
                  (double)scale};
@@ -259,13 +262,27 @@ int oracle_paged_decode(double* out, const void* q, int q_dtype, const void* k_c
         long r = rows ? (long)rows[i] : i;
         int b = (int)(r / Hq), h = (int)(r % Hq);
         double m, l;
-        int rc = attend(&P, b, h, 0, context_lens[b], &m, &l, out + (size_t)r * D);
+        int n = context_lens[b];
+        int t0 = (window > 0 && n > window) ? n - window : 0;
+        int rc = attend(&P, b, h, t0, n, &m, &l, out + (size_t)r * D);
         if (rc != 0) {
 #pragma omp critical
             status = rc;
         }
     }
     return status;
+}
+
+int oracle_paged_decode(double* out, const void* q, int q_dtype, const void* k_cache,
+                        const void* v_cache, int cache_dtype, const float* k_scale,
+                        const float* v_scale, const int32_t* block_tables,
+                        int max_blocks_per_seq, const int32_t* context_lens, int B, int Hq,
+                        int Hkv, int D, int block_size, int num_blocks, float scale,
+                        const int64_t* rows, long n_rows, int nthreads) {
+    return oracle_paged_decode_window(out, q, q_dtype, k_cache, v_cache, cache_dtype, k_scale,
+                                      v_scale, block_tables, max_blocks_per_seq, context_lens, B,
+                                      Hq, Hkv, D, block_size, num_blocks, scale, 0, rows, n_rows,
+                                      nthreads);
 }
 
 /* Split-context partials.  A context of N tokens is cut into

@@ -99,3 +99,34 @@ def test_nested_forks_beam_like():
     # 2 prompt blocks + 2 generation blocks + 4 private partial blocks
     assert s.blocks_in_use() == 2 + 2 + 4
     assert s.blocks_without_sharing() == 4 * 4
+
+
+@pytest.mark.parametrize("N,W", [(100, 16), (100, 37), (4096, 1024), (5000, 4096), (30, 64),
+                                 (32, 16), (33, 1)])
+def test_sliding_window_memory_is_fixed(N, W):
+    s = SequenceSet(BS)
+    s.add(0)
+    peak = 0
+    for t in range(1, N + 1):            # one token per step, releasing as it goes
+        s.append(0, 1)
+        s.release_before(0, t - W)
+        peak = max(peak, s.blocks_in_use())
+    assert s.blocks_in_use() == math.ceil(N / BS) - max(N - W, 0) // BS
+    # a window of W tokens never needs more than ceil(W / 16) + 1 blocks
+    assert peak <= math.ceil(W / BS) + 1
+
+
+def test_release_keeps_shared_prefix_of_other_sequences():
+    s = SequenceSet(BS)
+    s.add(0)
+    s.append(0, 64)                      # 4 full blocks
+    s.fork(0, 1)
+    s.release_before(0, 40)              # sequence 0 drops blocks 0, 1; sequence 1 keeps them
+    assert s.blocks_in_use() == 4
+    s.release_before(1, 48)              # sequence 1 drops 0..2; sequence 0 still holds 2
+    assert s.blocks_in_use() == 2
+    s.release_before(0, 63)              # block 3 (the last full one) is still needed
+    assert s.blocks_in_use() == 1
+    s.append(0, 1)
+    s.append(1, 1)
+    assert s.blocks_in_use() == 3

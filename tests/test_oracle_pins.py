@@ -130,6 +130,30 @@ def test_attention_matches_sdpa(dtype, Hq, Hkv, D):
         np.testing.assert_allclose(out[b], ref, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("W", [1, 5, 16, 17, 40, 1000])
+def test_sliding_window_matches_sdpa_on_the_last_w_tokens(W):
+    """Sliding window (caojiahao2 section 2.3): attention over the most recent
+    W positions equals contiguous attention over exactly those tokens; W = 1
+    returns the last token's V exactly."""
+    g_ = np.random.default_rng(17)
+    lens = [1, 15, 16, 17, 40, 100]
+    Hq, Hkv, D = 8, 2, 64
+    K_list = [torch.from_numpy(g_.standard_normal((n, Hkv, D), dtype=np.float32)) for n in lens]
+    V_list = [torch.from_numpy(g_.standard_normal((n, Hkv, D), dtype=np.float32)) for n in lens]
+    q = torch.from_numpy(g_.standard_normal((len(lens), Hq, D), dtype=np.float32))
+    kp, vp, bt = _paged_from_contiguous(K_list, V_list, 32, 4, torch.float32)
+    scale = float(np.float32(1 / math.sqrt(D)))
+    out = oracle.paged_decode(q.numpy(), "f32", kp.numpy(), vp.numpy(), "f32", bt,
+                              np.array(lens, np.int32), scale, window=W)
+    for b, n in enumerate(lens):
+        lo = max(0, n - W)
+        ref = _sdpa(q[b], K_list[b][lo:], V_list[b][lo:], scale, Hq // Hkv).numpy()
+        np.testing.assert_allclose(out[b], ref, rtol=0, atol=1e-12)
+        if W == 1:
+            last = V_list[b][n - 1].to(torch.float64).numpy()       # [Hkv][D]
+            assert np.array_equal(out[b], np.repeat(last, Hq // Hkv, axis=0))
+
+
 def test_hand_placed_blocks():
     """20 tokens, logical block 0 in physical block 3 and logical block 1 in
     physical block 0, written element by element without any helper."""
