@@ -35,6 +35,7 @@ WORKLOAD_NAMES = {
     "long": "long-32k-fp16-split-decode",
     "int8": "llama7b-mha-int8kv-paged-decode",
     "fp8": "llama7b-mha-fp8e4m3kv-paged-decode",
+    "window": "llama7b-mha-fp16-sliding-window-4096-decode",
     "sampling": "llama7b-parallel-sampling-shared-prefix-decode",
 }
 KERNEL_SOURCES = ["paged_decode.hip", "pkv_device.h", "pkv_internal.h", "pkv_api.hip"]
@@ -120,13 +121,26 @@ def main():
                            batch.slot_src, batch.k_scale, batch.v_scale)
     P = args.partition_size if args.partition_size is not None else cfg.get("partition_size", 0)
     mbs = batch.block_tables.shape[1]
-    P_eff = P or pkv.default_partition_size(batch.B, batch.Hq, batch.Hkv, mbs)
+    mbs_eff = min(mbs, int(cfg.get("window", 0)) // W.BLOCK_SIZE + 2) if cfg.get("window") \
+        else mbs
+    P_eff = P or pkv.default_partition_size(batch.B, batch.Hq, batch.Hkv, mbs_eff)
     out = torch.empty_like(batch.q)
-    NP = pkv.num_partitions(mbs, P_eff)
+    NP = pkv.num_partitions(mbs_eff, P_eff)
     partials = (torch.empty((batch.B, batch.Hq, NP), dtype=torch.float32, device="cuda"),
                 torch.empty((batch.B, batch.Hq, NP), dtype=torch.float32, device="cuda"),
                 torch.empty((batch.B, batch.Hq, NP, batch.D), dtype=torch.float32, device="cuda"))
     lens = batch.layout.context_lens
+    window = int(cfg.get("window", 0))
+    block_tables = batch.block_tables
+    if window:
+        # tokens a sequence attends to; blocks wholly before the window are
+        # released (-1), as a block manager would have done
+        bt = batch.layout.block_tables.copy()
+        for b, n in enumerate(lens):
+            if n > window:
+                bt[b, :(int(n) - window) // W.BLOCK_SIZE] = -1
+        block_tables = torch.from_numpy(bt).cuda()
+        lens = np.minimum(lens, window)
     e_kv = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "f8": 1}[cfg["cache"]]
     e_q = {"f32": 4, "f16": 2, "bf16": 2}[cfg["dtype"]]
     int8 = cfg["cache"] in W.SCALED     # 1-byte codes + a 4-byte scale per row
@@ -150,16 +164,24 @@ def main():
     # that HIP events bracket the decode kernel alone: cache write, phase 1
     # (split-context decode; single-partition sequences finish here), phase 2
     # (merge of the longer ones).
-    ws = torch.empty(pkv.decode_workspace_size(batch.B, batch.Hq, batch.Hkv, batch.D, mbs, P_eff),
-                     dtype=torch.uint8, device="cuda")
+    ws = torch.empty(pkv.decode_workspace_size(batch.B, batch.Hq, batch.Hkv, batch.D, mbs_eff,
+                                               P_eff), dtype=torch.uint8, device="cuda")
 
     def step_fused(ev0=None, ev1=None):
         if ev0 is not None:
             ev0.record(stream)
-        pkv.paged_attn_decode_append(batch.q, batch.k_new, batch.v_new, batch.k_cache,
-                                     batch.v_cache, batch.block_tables, batch.context_lens,
-                                     batch.scale, out=out, k_scale=batch.k_scale,
-                                     v_scale=batch.v_scale, partition_size=P_eff, workspace=ws)
+        if window:
+            pkv.paged_attn_decode_sliding(batch.q, batch.k_cache, batch.v_cache, block_tables,
+                                          batch.context_lens, batch.scale, window,
+                                          k_new=batch.k_new, v_new=batch.v_new, out=out,
+                                          k_scale=batch.k_scale, v_scale=batch.v_scale,
+                                          partition_size=P_eff, workspace=ws)
+        else:
+            pkv.paged_attn_decode_append(batch.q, batch.k_new, batch.v_new, batch.k_cache,
+                                         batch.v_cache, batch.block_tables, batch.context_lens,
+                                         batch.scale, out=out, k_scale=batch.k_scale,
+                                         v_scale=batch.v_scale, partition_size=P_eff,
+                                         workspace=ws)
         if ev1 is not None:
             ev1.record(stream)
 
@@ -178,6 +200,9 @@ def main():
             pkv.paged_attn_reduce(*partials, batch.context_lens, P_eff, out=out,
                                   skip_single_partition=True)
 
+    if window and args.step != "fused":
+        print("the sliding-window workload runs the fused step only", file=sys.stderr)
+        sys.exit(2)
     step = step_fused if args.step == "fused" else step_separate
 
     for _ in range(args.warmup):
@@ -224,6 +249,7 @@ def main():
             "sum_context_tokens": kv_tokens, "q_dtype": cfg["dtype"], "kv_dtype": cfg["cache"],
             "partition_size": P_eff, "seed": batch.seed, "parallelism": "single-gpu",
             "step": args.step,
+            **({"sliding_window": window, "attended_tokens": kv_tokens} if window else {}),
         },
         "kv_tokens_per_s": round(kv_tokens / (ms_per_step * 1e-3), 1),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
@@ -247,7 +273,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = run_cpu_baseline(batch, args.config, args.cpu_seconds,
-                                                  e_kv, e_q, int8)
+                                                  e_kv, e_q, int8, window)
     print(json.dumps(result), flush=True)
 
 
@@ -464,7 +490,7 @@ def bench_sampling(args):
     print(json.dumps(result), flush=True)
 
 
-def run_cpu_baseline(batch, cfg_name, target_s, e_kv, e_q, int8):
+def run_cpu_baseline(batch, cfg_name, target_s, e_kv, e_q, int8, window=0):
     """Time the CPU oracle (as it stands) on the first sequences of the same
     batch, sized to about `target_s` seconds, and express it in the metric's
     unit (algorithmic GB/s)."""
@@ -503,22 +529,23 @@ def run_cpu_baseline(batch, cfg_name, target_s, e_kv, e_q, int8):
         return dict(q=h(batch.q[:n_seq]), q_dtype=dt[batch.q.dtype], k_cache=h(batch.k_cache[idx]),
                     v_cache=h(batch.v_cache[idx]), cache_dtype=dt[batch.k_cache.dtype],
                     block_tables=bt.astype(np.int32), context_lens=lens[:n_seq].astype(np.int32),
-                    scale=batch.scale, **kw)
+                    scale=batch.scale, window=window, **kw)
 
     # probe on one sequence, then size the sample
     v1 = view_for(1)
     t = time.perf_counter()
     oracle.paged_decode(**v1)
     t_one = max(time.perf_counter() - t, 1e-4)
-    per_tok = t_one / max(int(lens[0]), 1)
+    att = np.minimum(lens, window) if window else lens     # tokens attended to
+    per_tok = t_one / max(int(att[0]), 1)
     n_seq = 1
-    while n_seq < batch.B and per_tok * lens[:n_seq + 1].sum() < target_s:
+    while n_seq < batch.B and per_tok * att[:n_seq + 1].sum() < target_s:
         n_seq += 1
     v = view_for(n_seq)
     t = time.perf_counter()
     oracle.paged_decode(**v)
     t_s = time.perf_counter() - t
-    sub = lens[:n_seq]
+    sub = att[:n_seq]
     alg = W.algorithmic_bytes(sub, batch.Hq, batch.Hkv, batch.D, e_kv, e_q, int8)
     return {
         "value": round(alg / t_s / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",

@@ -187,6 +187,32 @@ pkv_status pkv_paged_attn_decode_append(void* out, const void* q, const void* k_
                                         pkv_dtype cache_dtype, hipStream_t stream);
 
 /*
+ * Sliding-window decode: as pkv_paged_attn_decode (k_new == v_new == NULL) or
+ * pkv_paged_attn_decode_append (both given), but each sequence attends only to
+ * its last `sliding_window` positions, [max(0, N_b - sliding_window), N_b)
+ * (caojiahao2.github.io section 2.3: keep only the most recent window of the
+ * KV cache, for a fixed memory footprint).  sliding_window == 0 means no
+ * window.  Only block-table entries from (N_b - sliding_window) / 16 on are
+ * read, so blocks before the window may already be released (entries -1;
+ * pkv_bm_release_before).  The partitions split the positions from the
+ * window's first block on.  Partition default and workspace are those of
+ * pkv_paged_attn_decode with max_blocks_per_seq replaced by
+ * min(max_blocks_per_seq, sliding_window / 16 + 2), the most blocks a window
+ * touches: workspace_bytes >= pkv_decode_workspace_size(num_seqs, num_q_heads,
+ * num_kv_heads, head_dim, that value, partition_size).
+ */
+pkv_status pkv_paged_attn_decode_sliding(void* out, const void* q, const void* k_new,
+                                         const void* v_new, void* k_cache, void* v_cache,
+                                         float* k_scale, float* v_scale,
+                                         const int32_t* block_tables, int max_blocks_per_seq,
+                                         const int32_t* context_lens, int num_seqs,
+                                         int num_q_heads, int num_kv_heads, int head_dim,
+                                         int block_size, int64_t num_blocks, float scale,
+                                         int sliding_window, int partition_size, void* workspace,
+                                         size_t workspace_bytes, pkv_dtype q_dtype,
+                                         pkv_dtype cache_dtype, hipStream_t stream);
+
+/*
  * Phase 1 of the split-context decode: per-partition partial results (for a
  * caller that merges them itself, e.g. partitions computed on several
  * devices, or that times the phases apart).  The N_b = context_lens[b] tokens
@@ -302,6 +328,12 @@ pkv_status pkv_bm_append(pkv_block_manager* bm, const int64_t* seq_ids, const in
 pkv_status pkv_bm_block_tables(const pkv_block_manager* bm, const int64_t* seq_ids, int num_seqs,
                                int max_blocks_per_seq, int32_t* block_tables,
                                int32_t* context_lens);
+
+/* A sequence decoded through a sliding window no longer needs its positions
+ * before `position`: every whole block that ends at or before `position` (and
+ * is not the sequence's last block) is released and its table entry becomes
+ * -1.  Blocks other sequences still hold stay allocated. */
+pkv_status pkv_bm_release_before(pkv_block_manager* bm, int64_t seq_id, int64_t position);
 
 /* Free blocks left; -1 for a NULL manager. */
 int64_t pkv_bm_num_free_blocks(const pkv_block_manager* bm);

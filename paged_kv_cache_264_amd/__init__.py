@@ -16,6 +16,7 @@ import torch
 
 __all__ = [
     "kv_cache_write", "paged_attn_decode", "paged_attn_decode_append",
+    "paged_attn_decode_sliding",
     "paged_attn_decode_partials", "paged_attn_reduce",
     "decode_workspace_size", "default_partition_size", "num_partitions",
     "BlockManager", "copy_blocks",
@@ -69,6 +70,11 @@ def _load():
     L.pkv_paged_attn_decode_append.argtypes = [P, P, P, P, P, P, P, P, P, I, P, I, I, I, I, I,
                                                I64, F, I, P, SZ, I, I, P]
     L.pkv_paged_attn_decode_append.restype = I
+    L.pkv_paged_attn_decode_sliding.argtypes = [P, P, P, P, P, P, P, P, P, I, P, I, I, I, I, I,
+                                                I64, F, I, I, P, SZ, I, I, P]
+    L.pkv_paged_attn_decode_sliding.restype = I
+    L.pkv_bm_release_before.argtypes = [P, I64, I64]
+    L.pkv_bm_release_before.restype = I
     L.pkv_paged_attn_decode_partials.argtypes = [P, P, P, P, P, P, P, P, P, P, I, P, I, I, I, I,
                                                  I, I64, F, I, I, I, I, P]
     L.pkv_paged_attn_decode_partials.restype = I
@@ -262,6 +268,41 @@ def paged_attn_decode_append(q, k_new, v_new, k_cache, v_cache, block_tables, co
     return out
 
 
+def paged_attn_decode_sliding(q, k_cache, v_cache, block_tables, context_lens, scale,
+                              sliding_window, k_new=None, v_new=None, out=None, k_scale=None,
+                              v_scale=None, partition_size=0, workspace=None):
+    """Decode over each sequence's last `sliding_window` positions only; with
+    k_new / v_new given, the new token is appended first (as in
+    paged_attn_decode_append)."""
+    B, Hq, D, NB, Hkv, bs = _decode_common(q, k_cache, v_cache, block_tables, context_lens,
+                                           k_scale, v_scale)
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    if k_new is not None:
+        _dev(k_new, "k_new", dtype=q.dtype, ndim=3)
+        _dev(v_new, "v_new", dtype=q.dtype, ndim=3)
+        if tuple(k_new.shape) != (B, Hkv, D) or v_new.shape != k_new.shape:
+            raise ValueError("k_new and v_new must be [num_seqs][num_kv_heads][head_dim]")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", dtype=q.dtype, ndim=3)
+    mbs = block_tables.shape[1]
+    mbs_eff = min(mbs, int(sliding_window) // BLOCK_SIZE + 2) if sliding_window > 0 else mbs
+    need = decode_workspace_size(B, Hq, Hkv, D, mbs_eff, partition_size)
+    if workspace is None:
+        workspace = _workspace(q.device, need)
+    else:
+        _dev(workspace, "workspace")
+    rc = _load().pkv_paged_attn_decode_sliding(
+        _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+        _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), mbs, _ptr(context_lens), B, Hq, Hkv,
+        D, bs, NB, float(scale), int(sliding_window), int(partition_size), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _code(q.dtype, "q"),
+        _code(k_cache.dtype, "k_cache"), _stream(q))
+    _check_status(rc)
+    return out
+
+
 def paged_attn_decode_partials(q, k_cache, v_cache, block_tables, context_lens, scale,
                                partition_size, num_partitions_=None, k_scale=None, v_scale=None,
                                out=None, partials=None):
@@ -384,6 +425,11 @@ class BlockManager:
 
     def free_sequence(self, seq_id: int):
         _check_status(self._L.pkv_bm_free_sequence(self._h, seq_id))
+
+    def release_before(self, seq_id: int, position: int):
+        """Release the whole blocks of seq_id that end at or before `position`
+        (sliding-window decode); their table entries become -1."""
+        _check_status(self._L.pkv_bm_release_before(self._h, seq_id, position))
 
     @property
     def num_free_blocks(self) -> int:

@@ -96,7 +96,8 @@ pkv_status pkv_bm_fork(pkv_block_manager* bm, int64_t parent_id, int64_t child_i
     if (bm->seqs.count(child_id))
         return fail(PKV_ERR_SEQUENCE, "sequence %lld exists", (long long)child_id);
     pkv_block_manager::Seq child = p->second;   // copy before emplace may rehash
-    for (int32_t b : child.blocks) ++bm->refs[b];
+    for (int32_t b : child.blocks)
+        if (b >= 0) ++bm->refs[b];
     bm->seqs.emplace(child_id, std::move(child));
     return ok();
 }
@@ -106,7 +107,8 @@ pkv_status pkv_bm_free_sequence(pkv_block_manager* bm, int64_t seq_id) {
     auto s = bm->seqs.find(seq_id);
     if (s == bm->seqs.end())
         return fail(PKV_ERR_SEQUENCE, "sequence %lld unknown", (long long)seq_id);
-    for (int32_t b : s->second.blocks) bm->release(b);
+    for (int32_t b : s->second.blocks)
+        if (b >= 0) bm->release(b);
     bm->seqs.erase(s);
     return ok();
 }
@@ -218,6 +220,25 @@ pkv_status pkv_bm_block_tables(const pkv_block_manager* bm, const int64_t* seq_i
         for (int j = 0; j < nb; ++j) row[j] = s.blocks[(size_t)j];
         for (int j = nb; j < max_blocks_per_seq; ++j) row[j] = -1;
         context_lens[i] = (int32_t)s.len;
+    }
+    return ok();
+}
+
+pkv_status pkv_bm_release_before(pkv_block_manager* bm, int64_t seq_id, int64_t position) {
+    if (!bm) return fail(PKV_ERR_NULL, "manager is NULL");
+    auto it = bm->seqs.find(seq_id);
+    if (it == bm->seqs.end())
+        return fail(PKV_ERR_SEQUENCE, "sequence %lld unknown", (long long)seq_id);
+    auto& s = it->second;
+    const int64_t full = s.len / bm->block_size;   // whole blocks; the last partial one stays
+    int64_t drop = position > 0 ? position / bm->block_size : 0;
+    if (drop > full) drop = full;
+    for (int64_t j = 0; j < drop; ++j) {
+        int32_t& b = s.blocks[(size_t)j];
+        if (b >= 0) {
+            bm->release(b);
+            b = -1;
+        }
     }
     return ok();
 }

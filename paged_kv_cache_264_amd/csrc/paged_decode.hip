@@ -295,7 +295,8 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
         tile = blockIdx.x % a.n_tiles;
         int my_span = -1, cnt = 0;
         if (tid < a.num_seqs) {
-            const int nn = clamp_len(a.context_lens[tid]);
+            int nn = clamp_len(a.context_lens[tid]);
+            nn -= window_base(nn, a.window);
             const int c = partition_count(nn, P);
             my_span = c > 0 ? partition_span(nn, c) : 0;
             cnt = c > 0 ? c : 1;  // an empty sequence still takes one item: it writes zeros
@@ -326,8 +327,12 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
     }
 
     const int n = clamp_len(a.context_lens[b]);
-    const int n_parts = partition_count(n, P);
-    const int span = n_parts > 0 ? partition_span(n, n_parts) : 0;
+    // sliding window: positions below `lo` are not attended to; the partitions
+    // split the positions from the block-aligned `base` on
+    const int lo = window_begin(n, a.window);
+    const int base = window_base(n, a.window);
+    const int n_parts = partition_count(n - base, P);
+    const int span = n_parts > 0 ? partition_span(n - base, n_parts) : 0;
     const int Hq = a.num_q_heads;
     const int h0 = tile * GT;
     const int g = Hq / a.num_kv_heads;
@@ -356,7 +361,7 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
         for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
     }
 
-    const int t_begin = part * span;
+    const int t_begin = base + part * span;
     const int t_end = min(n, t_begin + span);
     const int blk_begin = t_begin / kBlockSize;
     const int blk_end = (t_end + kBlockSize - 1) / kBlockSize;
@@ -415,13 +420,15 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
 
     auto compute_block = [&](const BlockRegs<CE, D>& r) {
         const int jb = r.jb;
-        const bool full = r.ok && (jb + 1) * kBlockSize <= n_loop;
+        const bool full = r.ok && jb * kBlockSize >= lo && (jb + 1) * kBlockSize <= n_loop;
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
             bool valid[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-                valid[u] = full || (r.ok && jb * kBlockSize + (st * U + u) * R + row < n_loop);
+            for (int u = 0; u < U; ++u) {
+                const int t = jb * kBlockSize + (st * U + u) * R + row;
+                valid[u] = full || (r.ok && t >= lo && t < n_loop);
+            }
 
             // scores of the U tokens this row sees, for every head of the tile,
             // then the online-softmax update of (m, l) and the rescale of acc

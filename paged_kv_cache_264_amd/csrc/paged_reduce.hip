@@ -28,7 +28,7 @@ __global__ __launch_bounds__(kReduceThreads) void paged_reduce_kernel(ReduceArgs
     const int P = a.partition_size;
     int n = a.context_lens[b];
     n = n < 0 ? 0 : n;
-    int n_parts = partition_count(n, P);
+    int n_parts = partition_count(n - window_base(n, a.window), P);
     n_parts = n_parts > a.num_partitions ? a.num_partitions : n_parts;
 
     if (a.skip_single && n_parts <= 1) return;  // phase 1 wrote these outputs

@@ -60,6 +60,15 @@ int heads_per_tile(int g, pkv_dtype cache) {
 
 int num_partitions(int mbs, int P) { return (int)(((int64_t)mbs * pkv::kBlockSize + P - 1) / P); }
 
+// Blocks of a sequence a decode can touch: all of them, or with a sliding
+// window of W positions at most W / 16 + 2 (the window's first block may start
+// mid-block and the partitions split from that block on).
+int window_blocks(int mbs, int window) {
+    if (window <= 0) return mbs;
+    const int64_t wb = (int64_t)window / pkv::kBlockSize + 2;
+    return wb < mbs ? (int)wb : mbs;
+}
+
 // Workspace layout: the fp32 partials m [B][Hq][NP], l [B][Hq][NP] and
 // o [B][Hq][NP][D], each region 256-byte aligned.
 struct WorkspaceLayout {
@@ -263,6 +272,29 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* 
 
 namespace {
 
+// Phase 2 (merge of partials) for a decode with the given sliding window.
+pkv_status reduce_impl(void* out, const float* m_part, const float* l_part, const float* o_part,
+                       const int32_t* context_lens, int num_seqs, int num_q_heads, int head_dim,
+                       int partition_size, int num_partitions_, int skip_single_partition,
+                       pkv_dtype out_dtype, int window, hipStream_t stream) {
+    if (num_seqs < 0 || num_q_heads <= 0 || num_partitions_ <= 0)
+        return fail(PKV_ERR_SHAPE, "need num_seqs >= 0, positive num_q_heads and num_partitions");
+    if (partition_size <= 0 || partition_size % pkv::kBlockSize != 0)
+        return fail(PKV_ERR_SHAPE, "partition_size %d is not a positive multiple of 16",
+                    partition_size);
+    if (!head_dim_ok(head_dim))
+        return fail(PKV_ERR_UNSUPPORTED, "head_dim %d unsupported (64, 128, 256)", head_dim);
+    if (!is_float(out_dtype)) return fail(PKV_ERR_DTYPE, "out_dtype must be F32, F16 or BF16");
+    if (num_seqs == 0) return ok();
+    if (!out || !m_part || !l_part || !o_part || !context_lens)
+        return fail(PKV_ERR_NULL, "out, m_part, l_part, o_part and context_lens are required");
+    pkv::ReduceArgs a{out,       m_part,         l_part,          o_part,
+                      context_lens, num_seqs,    num_q_heads,     partition_size,
+                      num_partitions_, skip_single_partition ? 1 : 0, window};
+    return hip_status(pkv::launch_paged_reduce(a, (int)out_dtype, head_dim, stream),
+                      "paged_attn_reduce launch");
+}
+
 // Phase 1, optionally with the append of each sequence's new token.
 pkv_status decode_phase1(void* out, float* m_part, float* l_part, float* o_part, const void* q,
                          const void* k_new, const void* v_new, const void* k_cache,
@@ -271,7 +303,7 @@ pkv_status decode_phase1(void* out, float* m_part, float* l_part, float* o_part,
                          const int32_t* context_lens, int num_seqs, int num_q_heads,
                          int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
                          float scale, int partition_size, int num_partitions_, pkv_dtype q_dtype,
-                         pkv_dtype cache_dtype, hipStream_t stream) {
+                         pkv_dtype cache_dtype, int window, hipStream_t stream) {
     pkv_status s = check_decode(q, k_cache, v_cache, k_scale, v_scale, block_tables,
                                 max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
                                 num_kv_heads, head_dim, block_size, num_blocks, q_dtype,
@@ -280,7 +312,7 @@ pkv_status decode_phase1(void* out, float* m_part, float* l_part, float* o_part,
     if (partition_size <= 0 || partition_size % pkv::kBlockSize != 0)
         return fail(PKV_ERR_SHAPE, "partition_size %d is not a positive multiple of 16",
                     partition_size);
-    const int NP = num_partitions(max_blocks_per_seq, partition_size);
+    const int NP = num_partitions(window_blocks(max_blocks_per_seq, window), partition_size);
     if (num_partitions_ < NP)
         return fail(PKV_ERR_SHAPE, "num_partitions %d < ceil(max_blocks_per_seq*16/P) = %d",
                     num_partitions_, NP);
@@ -299,6 +331,7 @@ pkv_status decode_phase1(void* out, float* m_part, float* l_part, float* o_part,
     a.m_part = m_part;
     a.l_part = l_part;
     a.o_part = o_part;
+    a.window = window;
     return hip_status(pkv::launch_paged_decode(a, (int)q_dtype, (int)cache_dtype, head_dim, gt,
                                                stream),
                       "paged decode launch");
@@ -312,7 +345,7 @@ pkv_status decode_both_phases(void* out, const void* q, const void* k_new, const
                               int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                               int64_t num_blocks, float scale, int partition_size,
                               void* workspace, size_t workspace_bytes, pkv_dtype q_dtype,
-                              pkv_dtype cache_dtype, hipStream_t stream) {
+                              pkv_dtype cache_dtype, int window, hipStream_t stream) {
     pkv_status s = check_decode(q, k_cache, v_cache, k_scale, v_scale, block_tables,
                                 max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
                                 num_kv_heads, head_dim, block_size, num_blocks, q_dtype,
@@ -324,10 +357,11 @@ pkv_status decode_both_phases(void* out, const void* q, const void* k_new, const
     if (num_seqs == 0) return ok();
     if (!out) return fail(PKV_ERR_NULL, "out is required");
     if (!aligned16(out)) return fail(PKV_ERR_SHAPE, "out must be 16-byte aligned");
+    const int mbs_eff = window_blocks(max_blocks_per_seq, window);
     const int P = partition_size ? partition_size
                                  : pkv_default_partition_size(num_seqs, num_q_heads, num_kv_heads,
-                                                              max_blocks_per_seq);
-    const int NP = num_partitions(max_blocks_per_seq, P);
+                                                              mbs_eff);
+    const int NP = num_partitions(mbs_eff, P);
     const WorkspaceLayout w = layout(num_seqs, num_q_heads, head_dim, NP);
     if (!workspace || workspace_bytes < w.total)
         return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
@@ -341,11 +375,11 @@ pkv_status decode_both_phases(void* out, const void* q, const void* k_new, const
     s = decode_phase1(out, m, l, o, q, k_new, v_new, k_cache, v_cache, k_scale, v_scale,
                       block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
                       num_kv_heads, head_dim, block_size, num_blocks, scale, P, NP, q_dtype,
-                      cache_dtype, stream);
+                      cache_dtype, window, stream);
     if (s != PKV_OK) return s;
     if (NP == 1) return ok();  // every sequence was finished in phase 1
-    return pkv_paged_attn_reduce(out, m, l, o, context_lens, num_seqs, num_q_heads, head_dim, P,
-                                 NP, 1, q_dtype, stream);
+    return reduce_impl(out, m, l, o, context_lens, num_seqs, num_q_heads, head_dim, P, NP, 1,
+                       q_dtype, window, stream);
 }
 
 }  // namespace
@@ -365,7 +399,7 @@ pkv_status pkv_paged_attn_decode_partials(void* out, float* m_part, float* l_par
     return decode_phase1(out, m_part, l_part, o_part, q, nullptr, nullptr, k_cache, v_cache,
                          k_scale, v_scale, block_tables, max_blocks_per_seq, context_lens,
                          num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                         scale, partition_size, num_partitions_, q_dtype, cache_dtype, stream);
+                         scale, partition_size, num_partitions_, q_dtype, cache_dtype, 0, stream);
 }
 
 pkv_status pkv_paged_attn_reduce(void* out, const float* m_part, const float* l_part,
@@ -373,21 +407,9 @@ pkv_status pkv_paged_attn_reduce(void* out, const float* m_part, const float* l_
                                  int num_q_heads, int head_dim, int partition_size,
                                  int num_partitions_, int skip_single_partition,
                                  pkv_dtype out_dtype, hipStream_t stream) {
-    if (num_seqs < 0 || num_q_heads <= 0 || num_partitions_ <= 0)
-        return fail(PKV_ERR_SHAPE, "need num_seqs >= 0, positive num_q_heads and num_partitions");
-    if (partition_size <= 0 || partition_size % pkv::kBlockSize != 0)
-        return fail(PKV_ERR_SHAPE, "partition_size %d is not a positive multiple of 16",
-                    partition_size);
-    if (!head_dim_ok(head_dim))
-        return fail(PKV_ERR_UNSUPPORTED, "head_dim %d unsupported (64, 128, 256)", head_dim);
-    if (!is_float(out_dtype)) return fail(PKV_ERR_DTYPE, "out_dtype must be F32, F16 or BF16");
-    if (num_seqs == 0) return ok();
-    if (!out || !m_part || !l_part || !o_part || !context_lens)
-        return fail(PKV_ERR_NULL, "out, m_part, l_part, o_part and context_lens are required");
-    pkv::ReduceArgs a{out, m_part, l_part, o_part, context_lens, num_seqs, num_q_heads,
-                      partition_size, num_partitions_, skip_single_partition ? 1 : 0};
-    return hip_status(pkv::launch_paged_reduce(a, (int)out_dtype, head_dim, stream),
-                      "paged_attn_reduce launch");
+    return reduce_impl(out, m_part, l_part, o_part, context_lens, num_seqs, num_q_heads,
+                       head_dim, partition_size, num_partitions_, skip_single_partition,
+                       out_dtype, 0, stream);
 }
 
 pkv_status pkv_paged_attn_decode(void* out, const void* q, const void* k_cache,
@@ -402,7 +424,7 @@ pkv_status pkv_paged_attn_decode(void* out, const void* q, const void* k_cache,
                               block_tables, max_blocks_per_seq, context_lens, num_seqs,
                               num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
                               partition_size, workspace, workspace_bytes, q_dtype, cache_dtype,
-                              stream);
+                              0, stream);
 }
 
 pkv_status pkv_paged_attn_decode_append(void* out, const void* q, const void* k_new,
@@ -423,7 +445,30 @@ pkv_status pkv_paged_attn_decode_append(void* out, const void* q, const void* k_
                               block_tables, max_blocks_per_seq, context_lens, num_seqs,
                               num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
                               partition_size, workspace, workspace_bytes, q_dtype, cache_dtype,
-                              stream);
+                              0, stream);
+}
+
+pkv_status pkv_paged_attn_decode_sliding(void* out, const void* q, const void* k_new,
+                                         const void* v_new, void* k_cache, void* v_cache,
+                                         float* k_scale, float* v_scale,
+                                         const int32_t* block_tables, int max_blocks_per_seq,
+                                         const int32_t* context_lens, int num_seqs,
+                                         int num_q_heads, int num_kv_heads, int head_dim,
+                                         int block_size, int64_t num_blocks, float scale,
+                                         int sliding_window, int partition_size, void* workspace,
+                                         size_t workspace_bytes, pkv_dtype q_dtype,
+                                         pkv_dtype cache_dtype, hipStream_t stream) {
+    if (sliding_window < 0)
+        return fail(PKV_ERR_SHAPE, "sliding_window %d < 0", sliding_window);
+    if ((k_new == nullptr) != (v_new == nullptr))
+        return fail(PKV_ERR_NULL, "k_new and v_new must both be given or both be NULL");
+    if (num_seqs > 0 && k_new && (!aligned16(k_new) || !aligned16(v_new)))
+        return fail(PKV_ERR_SHAPE, "k_new and v_new must be 16-byte aligned");
+    return decode_both_phases(out, q, k_new, v_new, k_cache, v_cache, k_scale, v_scale,
+                              block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                              num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                              partition_size, workspace, workspace_bytes, q_dtype, cache_dtype,
+                              sliding_window, stream);
 }
 
 }  // extern "C"

@@ -43,6 +43,7 @@ struct DecodeArgs {
     int num_partitions;  // NP: partial-array stride
     int n_tiles;         // num_q_heads / heads_per_tile
     int longest_first;   // schedule work longest-first (needs num_seqs <= kScheduleMaxSeqs)
+    int window;          // > 0: attend to the last `window` positions only
     float scale_log2;    // softmax scale * log2(e)
 };
 
@@ -56,6 +57,17 @@ __host__ __device__ inline int partition_count(int n, int P) { return n <= 0 ? 0
 __host__ __device__ inline int partition_span(int n, int count) {
     const int per = (n + count - 1) / count;
     return (per + kBlockSize - 1) / kBlockSize * kBlockSize;
+}
+
+// Sliding window of `window` positions (0: none) over an n-token context: the
+// first position attended to, and the block-aligned start of the tokens that
+// the partitions split (positions base..n-1; those below the first are
+// masked).
+__host__ __device__ inline int window_begin(int n, int window) {
+    return (window > 0 && n > window) ? n - window : 0;
+}
+__host__ __device__ inline int window_base(int n, int window) {
+    return window_begin(n, window) / kBlockSize * kBlockSize;
 }
 
 // Phase 1 of split-context decode.  With a.out set, sequences whose context
@@ -76,6 +88,7 @@ struct ReduceArgs {
     int partition_size;
     int num_partitions;
     int skip_single;     // sequences with <= 1 partition already hold their output
+    int window;          // sliding window of the decode that wrote the partials (0: none)
 };
 
 hipError_t launch_paged_reduce(const ReduceArgs& a, int out_dtype, int head_dim,

@@ -44,20 +44,22 @@ class OracleView:
     compacted to the blocks those sequences use and their tables renumbered
     (paging makes the result independent of where blocks sit)."""
 
-    def __init__(self, batch: W.Batch, seqs):
+    def __init__(self, batch: W.Batch, seqs, window: int = 0):
         self.seqs = np.asarray(seqs, np.int64)
+        self.window = window
         lay = batch.layout
         lens = lay.context_lens[self.seqs]
         blocks = []
         for s, n in zip(self.seqs, lens):
-            blocks.extend(int(x) for x in lay.block_tables[s, :W.blocks_needed(n)])
+            j0 = self.first_block(n)
+            blocks.extend(int(x) for x in lay.block_tables[s, j0:W.blocks_needed(n)])
         self.block_ids = np.asarray(blocks, np.int64)
         remap = {b: i for i, b in enumerate(self.block_ids)}
         self.remap = remap
         mbs = lay.block_tables.shape[1]
         bt = np.full((len(self.seqs), mbs), -1, np.int32)
         for i, (s, n) in enumerate(zip(self.seqs, lens)):
-            for j in range(W.blocks_needed(n)):
+            for j in range(self.first_block(n), W.blocks_needed(n)):
                 bt[i, j] = remap[int(lay.block_tables[s, j])]
         self.block_tables = bt
         self.context_lens = lens.astype(np.int32)
@@ -90,11 +92,19 @@ class OracleView:
             self.v_cache = host(batch.v_cache[idx]) if len(idx) else None
             self.k_scale = self.v_scale = None
 
+    def first_block(self, n: int) -> int:
+        """First block a sliding window of self.window positions reads (0: all)."""
+        n = int(n)
+        if self.window <= 0 or n <= self.window:
+            return 0
+        return (n - self.window) // BS
+
     def compact_slots(self, slots):
         slots = np.asarray(slots, np.int64)
         out = np.empty_like(slots)
         for i, s in enumerate(slots):
-            out[i] = -1 if s < 0 else self.remap[int(s) // BS] * BS + int(s) % BS
+            out[i] = (-1 if s < 0 or int(s) // BS not in self.remap
+                      else self.remap[int(s) // BS] * BS + int(s) % BS)
         return out
 
     def write_new_tokens(self, batch: W.Batch):
@@ -109,7 +119,7 @@ class OracleView:
         return oracle.paged_decode(self.q, self.q_dtype, self.k_cache, self.v_cache,
                                    self.cache_dtype, self.block_tables, self.context_lens,
                                    self.scale, k_scale=self.k_scale, v_scale=self.v_scale,
-                                   rows=rows, nthreads=nthreads)
+                                   rows=rows, nthreads=nthreads, window=self.window)
 
 
 def gpu_populate(pkv, batch: W.Batch):

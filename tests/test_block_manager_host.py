@@ -10,7 +10,8 @@ every operation:
   oracle's token list (so no write ever landed in a block another sequence
   still uses, and every copy was requested);
 - the pool holds exactly the oracle's least number of physical blocks
-  (num_blocks - free blocks == distinct (block, ids) pairs);
+  (num_blocks - free blocks == distinct (block, ids) pairs), also after
+  sliding-window releases of a sequence's front blocks;
 - a batch that needs more blocks than are free fails with the capacity status
   and changes nothing.
 
@@ -54,9 +55,12 @@ def check_all(bm, ref, pool, nb):
         toks = ref.tokens(s)
         assert lens[i] == len(toks) == bm.sequence_length(s)
         nblk = -(-len(toks) // BS)
+        r = ref.released[s]                       # whole blocks released at the front
         assert (tables[i, nblk:] == -1).all()
-        assert (tables[i, :nblk] >= 0).all() and (tables[i, :nblk] < nb).all()
-        assert np.array_equal(pool.read(tables[i], len(toks)), np.asarray(toks, dtype=np.int64))
+        assert (tables[i, :r] == -1).all()
+        assert (tables[i, r:nblk] >= 0).all() and (tables[i, r:nblk] < nb).all()
+        got = pool.read(tables[i, r:], len(toks) - r * BS)
+        assert np.array_equal(got, np.asarray(toks[r * BS:], dtype=np.int64))
 
 
 def run_history(seed, nb, steps, max_seqs=12):
@@ -68,7 +72,7 @@ def run_history(seed, nb, steps, max_seqs=12):
     n_capacity = n_copies = 0
     for _ in range(steps):
         live = sorted(ref.seqs)
-        op = rng.choice(["add", "fork", "append", "append", "append", "free"])
+        op = rng.choice(["add", "fork", "append", "append", "append", "free", "release"])
         if op == "add" or not live:
             if len(live) >= max_seqs:
                 continue
@@ -86,6 +90,11 @@ def run_history(seed, nb, steps, max_seqs=12):
             s = int(rng.choice(live))
             bm.free_sequence(s)
             ref.free(s)
+        elif op == "release":
+            s = int(rng.choice(live))
+            pos = int(rng.integers(-5, len(ref.tokens(s)) + 20))
+            bm.release_before(s, pos)
+            ref.release_before(s, pos)
         else:
             k = int(rng.integers(1, len(live) + 2))
             ids = [int(x) for x in rng.choice(live, size=k)]     # repeats allowed

@@ -50,6 +50,11 @@ CONFIGS = {
     # quantizing cache write.
     "int8": dict(B=64, ctx=(512, 4096), Hq=32, Hkv=32, D=128, dtype="f16", cache="i8",
                  pool=None, seed=5, max_ctx=4096),
+    # Sliding-window decode at the LLaMA-7B shape: contexts U[4096, 12288], each
+    # sequence attends to its last 4096 positions (blocks before the window are
+    # released: their table entries are -1).
+    "window": dict(B=64, ctx=(4096, 12288), Hq=32, Hkv=32, D=128, dtype="f16", cache="f16",
+                   pool=None, seed=9, max_ctx=12288, window=4096),
     # FP8 (e4m3) KV cache at the LLaMA-7B shape, populated the same way.
     "fp8": dict(B=64, ctx=(512, 4096), Hq=32, Hkv=32, D=128, dtype="f16", cache="f8",
                 pool=None, seed=8, max_ctx=4096),
