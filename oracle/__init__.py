@@ -54,6 +54,8 @@ def lib():
                                           P, L64, I]
         L.oracle_paged_decode_window.argtypes = [P, P, I, P, P, I, P, P, P, I, P, I, I, I, I, I, I,
                                                  F, I, P, L64, I]
+        L.oracle_paged_multi.argtypes = [P, P, I, P, P, I, P, P, P, I, P, P, I, I, I, I, I, I, F,
+                                         I]
         L.oracle_paged_partials.argtypes = [P, P, P, P, I, P, P, I, P, P, P, I, P, I, I, I, I, I,
                                             I, F, I, I, I]
         L.oracle_merge_partials.argtypes = [P, P, P, P, L64, I, I]
@@ -128,6 +130,32 @@ def paged_decode(q, q_dtype, k_cache, v_cache, cache_dtype, block_tables, contex
                                           0 if r is None else len(r), nthreads)
     if rc != 0:
         raise RuntimeError(f"oracle_paged_decode failed with {rc}")
+    return out
+
+
+def paged_multi(q, q_dtype, k_cache, v_cache, cache_dtype, block_tables, context_lens,
+                query_start_loc, scale, k_scale=None, v_scale=None, block_size=16, nthreads=0):
+    """Causal attention of several query tokens per sequence (see oracle.c).
+    q [T][Hq][D]; query_start_loc int32 [B+1].  Returns float64 [T][Hq][D]."""
+    q = _check(q, q_dtype, "q")
+    k_cache = _check(k_cache, cache_dtype, "k_cache")
+    v_cache = _check(v_cache, cache_dtype, "v_cache")
+    bt = _check(block_tables, np.int32, "block_tables")
+    cl = _check(context_lens, np.int32, "context_lens")
+    qsl = _check(query_start_loc, np.int32, "query_start_loc")
+    ks = _check(k_scale, np.float32, "k_scale")
+    vs = _check(v_scale, np.float32, "v_scale")
+    T, Hq, D = q.shape
+    NB, Hkv, bs, D2 = k_cache.shape
+    B = len(cl)
+    assert D2 == D and len(qsl) == B + 1 and qsl[-1] == T
+    out = np.full((T, Hq, D), np.nan, dtype=np.float64)
+    rc = lib().oracle_paged_multi(_ptr(out), _ptr(q), DTYPES[q_dtype], _ptr(k_cache),
+                                  _ptr(v_cache), DTYPES[cache_dtype], _ptr(ks), _ptr(vs), _ptr(bt),
+                                  bt.shape[1], _ptr(cl), _ptr(qsl), B, Hq, Hkv, D, block_size, NB,
+                                  float(scale), nthreads)
+    if rc != 0:
+        raise RuntimeError(f"oracle_paged_multi failed with {rc}")
     return out
 
 

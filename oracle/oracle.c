@@ -186,8 +186,17 @@ static int gather(const problem* P, int b, int kvh, int t0, int t1, double* K, d
 /* Softmax-weighted sum over tokens [t0, t1) of sequence b for q head h.
  * Outputs the max score m, the sum l of exp(s - m) and o = sum exp(s-m) V / l.
  * n == 0 gives m = -inf, l = 0, o = 0. */
+static int attend_q(const problem* P, int b, int h, size_t qbase, int t0, int t1, double* m_out,
+                    double* l_out, double* o);
+
 static int attend(const problem* P, int b, int h, int t0, int t1, double* m_out, double* l_out,
                   double* o) {
+    return attend_q(P, b, h, ((size_t)b * P->Hq + h) * P->D, t0, t1, m_out, l_out, o);
+}
+
+/* As attend, with the query vector at element qbase of P->q. */
+static int attend_q(const problem* P, int b, int h, size_t qbase, int t0, int t1, double* m_out,
+                    double* l_out, double* o) {
     int D = P->D;
     int g = P->Hq / P->Hkv;
     int kvh = h / g;
@@ -202,7 +211,6 @@ static int attend(const problem* P, int b, int h, int t0, int t1, double* m_out,
     if (!K || !V || !s || !qv) { free(K); free(V); free(s); free(qv); return -2; }
     if (gather(P, b, kvh, t0, t1, K, V) != 0) { free(K); free(V); free(s); free(qv); return -1; }
 
-    size_t qbase = ((size_t)b * P->Hq + h) * D;
     for (int d = 0; d < D; ++d) qv[d] = elem(P->q, qbase + d, P->q_dtype);
 
     /* scores s_t = scale * <q, K_t> */
@@ -283,6 +291,48 @@ int oracle_paged_decode(double* out, const void* q, int q_dtype, const void* k_c
                                       v_scale, block_tables, max_blocks_per_seq, context_lens, B,
                                       Hq, Hkv, D, block_size, num_blocks, scale, 0, rows, n_rows,
                                       nthreads);
+}
+
+/* Attention for several query tokens per sequence over the paged cache: the
+ * verification pass of speculative decoding, where the target model checks
+ * k draft tokens in one forward pass (caojiahao2.github.io section 6;
+ * lazyllm lesson 4, the speculative-decoding algorithm), or a prefill chunk.
+ * Sequence b has N_b = context_lens[b] cached tokens, the last
+ * q_len_b = query_start_loc[b + 1] - query_start_loc[b] of them being its
+ * queries; query row r = query_start_loc[b] + j (j < q_len_b) sits at position
+ * p = N_b - q_len_b + j and attends causally to positions 0..p.
+ * q, out: [T][Hq][D] with T = query_start_loc[B].  A query with p < 0 (more
+ * queries than tokens) gets a zero row. */
+int oracle_paged_multi(double* out, const void* q, int q_dtype, const void* k_cache,
+                       const void* v_cache, int cache_dtype, const float* k_scale,
+                       const float* v_scale, const int32_t* block_tables,
+                       int max_blocks_per_seq, const int32_t* context_lens,
+                       const int32_t* query_start_loc, int B, int Hq, int Hkv, int D,
+                       int block_size, int num_blocks, float scale, int nthreads) {
+    problem P = {q, q_dtype, k_cache, v_cache, cache_dtype, k_scale, v_scale, block_tables,
+                 max_blocks_per_seq, context_lens, B, Hq, Hkv, D, block_size, num_blocks,
+                 (double)scale};
+    if (Hkv <= 0 || Hq % Hkv != 0 || block_size <= 0) return -3;
+    long T = query_start_loc[B];
+    int status = 0;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long i = 0; i < T * Hq; ++i) {
+        long r = i / Hq;
+        int h = (int)(i % Hq);
+        int b = 0;
+        while (b + 1 < B && query_start_loc[b + 1] <= r) ++b;
+        int q_len = query_start_loc[b + 1] - query_start_loc[b];
+        int p = context_lens[b] - q_len + (int)(r - query_start_loc[b]);
+        double m, l;
+        int rc = attend_q(&P, b, h, ((size_t)r * Hq + h) * D, 0, p + 1, &m, &l,
+                          out + (size_t)i * D);
+        if (rc != 0) {
+#pragma omp critical
+            status = rc;
+        }
+    }
+    return status;
 }
 
 /* Split-context partials.  A context of N tokens is cut into
