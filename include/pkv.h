@@ -213,6 +213,48 @@ pkv_status pkv_paged_attn_decode_sliding(void* out, const void* q, const void* k
                                          pkv_dtype cache_dtype, hipStream_t stream);
 
 /*
+ * Causal attention of several query tokens per sequence: the verification
+ * pass of speculative decoding, in which the target model scores k draft
+ * tokens in one forward pass (caojiahao2.github.io section 6; lazyllm lesson
+ * 4, the speculative-decoding algorithm), or a prefill chunk.  The queries of
+ * sequence b are rows query_start_loc[b] .. query_start_loc[b+1]-1 of q
+ * ([T][num_q_heads][head_dim], T = num_query_tokens = query_start_loc[B]);
+ * they are its last q_len_b positions, already written into the cache, so
+ * query j sits at position p = N_b - q_len_b + j (N_b = context_lens[b]) and
+ *     out[row][h] = softmax(scale * q[row][h] . K[0..p]^T) V[0..p].
+ * A query with p < 0 (q_len_b > N_b, a caller error) gets a zero row.
+ *  query_start_loc  int32 [num_seqs + 1], device, non-decreasing
+ *  max_query_len    >= every q_len_b (sizes the grid; rows beyond a
+ *                   sequence's own count exit at once)
+ *  partition_size   0 = pkv_multi_default_partition_size(...)
+ *  workspace        >= pkv_multi_workspace_size(T, Hq, D, MBS, P) bytes,
+ *                   256-byte aligned, when the context splits into more than
+ *                   one partition (ceil(MBS * 16 / P) > 1); may be NULL
+ *                   otherwise
+ * Supported: (q_dtype, cache_dtype) in {(F16,F16), (BF16,BF16)}; head_dim 64,
+ * 128, 256.  Runs on the matrix cores; the softmax weights are rounded to the
+ * q dtype before they multiply V (one more rounding than
+ * pkv_paged_attn_decode; relative 2^-11 for F16, 2^-8 for BF16).
+ */
+pkv_status pkv_paged_attn_multi(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, int max_blocks_per_seq,
+                                const int32_t* context_lens, const int32_t* query_start_loc,
+                                int num_seqs, int num_query_tokens, int max_query_len,
+                                int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                                int64_t num_blocks, float scale, int partition_size,
+                                void* workspace, size_t workspace_bytes, pkv_dtype q_dtype,
+                                pkv_dtype cache_dtype, hipStream_t stream);
+
+/* Workspace bytes for pkv_paged_attn_multi (0 for invalid sizes). */
+size_t pkv_multi_workspace_size(int num_query_tokens, int num_q_heads, int head_dim,
+                                int max_blocks_per_seq, int partition_size);
+
+/* Partition size pkv_paged_attn_multi uses for partition_size == 0 (0 for
+ * invalid sizes). */
+int pkv_multi_default_partition_size(int num_seqs, int max_query_len, int num_q_heads,
+                                     int num_kv_heads, int max_blocks_per_seq);
+
+/*
  * Phase 1 of the split-context decode: per-partition partial results (for a
  * caller that merges them itself, e.g. partitions computed on several
  * devices, or that times the phases apart).  The N_b = context_lens[b] tokens

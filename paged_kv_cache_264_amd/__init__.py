@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "kv_cache_write", "paged_attn_decode", "paged_attn_decode_append",
-    "paged_attn_decode_sliding",
+    "paged_attn_decode_sliding", "paged_attn_multi",
     "paged_attn_decode_partials", "paged_attn_reduce",
     "decode_workspace_size", "default_partition_size", "num_partitions",
     "BlockManager", "copy_blocks",
@@ -75,6 +75,13 @@ def _load():
     L.pkv_paged_attn_decode_sliding.restype = I
     L.pkv_bm_release_before.argtypes = [P, I64, I64]
     L.pkv_bm_release_before.restype = I
+    L.pkv_paged_attn_multi.argtypes = [P, P, P, P, P, I, P, P, I, I, I, I, I, I, I, I64, F, I,
+                                       P, SZ, I, I, P]
+    L.pkv_paged_attn_multi.restype = I
+    L.pkv_multi_workspace_size.argtypes = [I, I, I, I, I]
+    L.pkv_multi_workspace_size.restype = SZ
+    L.pkv_multi_default_partition_size.argtypes = [I, I, I, I, I]
+    L.pkv_multi_default_partition_size.restype = I
     L.pkv_paged_attn_decode_partials.argtypes = [P, P, P, P, P, P, P, P, P, P, I, P, I, I, I, I,
                                                  I, I64, F, I, I, I, I, P]
     L.pkv_paged_attn_decode_partials.restype = I
@@ -297,6 +304,45 @@ def paged_attn_decode_sliding(q, k_cache, v_cache, block_tables, context_lens, s
         _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
         _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), mbs, _ptr(context_lens), B, Hq, Hkv,
         D, bs, NB, float(scale), int(sliding_window), int(partition_size), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _code(q.dtype, "q"),
+        _code(k_cache.dtype, "k_cache"), _stream(q))
+    _check_status(rc)
+    return out
+
+
+def paged_attn_multi(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale,
+                     max_query_len, out=None, partition_size=0, workspace=None):
+    """Causal attention of several query tokens per sequence (speculative
+    verification, prefill chunks): q [T][Hq][D]; the queries of sequence b are
+    rows query_start_loc[b] .. query_start_loc[b+1]-1 (int32 [B+1] on the GPU)
+    and sit at its last positions (their K/V already in the cache)."""
+    _dev(q, "q", ndim=3)
+    _dev(k_cache, "k_cache", dtype=q.dtype, ndim=4)
+    _dev(v_cache, "v_cache", dtype=q.dtype, ndim=4)
+    _dev(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _dev(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    _dev(query_start_loc, "query_start_loc", dtype=torch.int32, ndim=1)
+    T, Hq, D = q.shape
+    NB, Hkv, bs, D2 = k_cache.shape
+    B = context_lens.shape[0]
+    if D2 != D or v_cache.shape != k_cache.shape or query_start_loc.shape[0] != B + 1 or \
+            block_tables.shape[0] != B:
+        raise ValueError("q / cache / table / query_start_loc shapes disagree")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", dtype=q.dtype, ndim=3)
+    mbs = block_tables.shape[1]
+    L = _load()
+    P = partition_size or L.pkv_multi_default_partition_size(B, int(max_query_len), Hq, Hkv, mbs)
+    need = L.pkv_multi_workspace_size(T, Hq, D, mbs, P) if P else 0
+    if workspace is None:
+        workspace = _workspace(q.device, need)
+    else:
+        _dev(workspace, "workspace")
+    rc = L.pkv_paged_attn_multi(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), mbs,
+        _ptr(context_lens), _ptr(query_start_loc), B, T, int(max_query_len), Hq, Hkv, D, bs, NB,
+        float(scale), int(partition_size), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _code(q.dtype, "q"),
         _code(k_cache.dtype, "k_cache"), _stream(q))
     _check_status(rc)

@@ -23,7 +23,16 @@ __global__ __launch_bounds__(kReduceThreads) void paged_reduce_kernel(ReduceArgs
     __shared__ float s_red[kReduceThreads / kWave];
 
     const int bh = blockIdx.x;
-    const int b = bh / a.num_q_heads;
+    const int row = bh / a.num_q_heads;
+    int b = row;
+    if (a.query_start_loc) {  // sequence of query token `row`: binary search
+        int lo = 0, hi = a.num_seqs - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (a.query_start_loc[mid] <= row) lo = mid; else hi = mid - 1;
+        }
+        b = lo;
+    }
     const int tid = threadIdx.x;
     const int P = a.partition_size;
     int n = a.context_lens[b];
@@ -81,7 +90,7 @@ __global__ __launch_bounds__(kReduceThreads) void paged_reduce_kernel(ReduceArgs
 
 template <Elem OE>
 hipError_t launch_d(const ReduceArgs& a, int d, hipStream_t s) {
-    const int64_t n_wg = (int64_t)a.num_seqs * a.num_q_heads;
+    const int64_t n_wg = (int64_t)a.num_rows * a.num_q_heads;
     if (n_wg == 0) return hipSuccess;
     if (n_wg > 0x7fffffff) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)n_wg), block(kReduceThreads);

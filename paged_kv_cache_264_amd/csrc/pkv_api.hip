@@ -288,9 +288,20 @@ pkv_status reduce_impl(void* out, const float* m_part, const float* l_part, cons
     if (num_seqs == 0) return ok();
     if (!out || !m_part || !l_part || !o_part || !context_lens)
         return fail(PKV_ERR_NULL, "out, m_part, l_part, o_part and context_lens are required");
-    pkv::ReduceArgs a{out,       m_part,         l_part,          o_part,
-                      context_lens, num_seqs,    num_q_heads,     partition_size,
-                      num_partitions_, skip_single_partition ? 1 : 0, window};
+    pkv::ReduceArgs a{};
+    a.out = out;
+    a.m_part = m_part;
+    a.l_part = l_part;
+    a.o_part = o_part;
+    a.context_lens = context_lens;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.partition_size = partition_size;
+    a.num_partitions = num_partitions_;
+    a.skip_single = skip_single_partition ? 1 : 0;
+    a.window = window;
+    a.query_start_loc = nullptr;
+    a.num_rows = num_seqs;
     return hip_status(pkv::launch_paged_reduce(a, (int)out_dtype, head_dim, stream),
                       "paged_attn_reduce launch");
 }
@@ -469,6 +480,122 @@ pkv_status pkv_paged_attn_decode_sliding(void* out, const void* q, const void* k
                               num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
                               partition_size, workspace, workspace_bytes, q_dtype, cache_dtype,
                               sliding_window, stream);
+}
+
+size_t pkv_multi_workspace_size(int num_query_tokens, int num_q_heads, int head_dim,
+                                int max_blocks_per_seq, int partition_size) {
+    if (num_query_tokens < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0 ||
+        !head_dim_ok(head_dim) || partition_size <= 0 || partition_size % pkv::kBlockSize != 0)
+        return 0;
+    return layout(num_query_tokens, num_q_heads, head_dim,
+                  num_partitions(max_blocks_per_seq, partition_size))
+        .total;
+}
+
+int pkv_multi_default_partition_size(int num_seqs, int max_query_len, int num_q_heads,
+                                     int num_kv_heads, int max_blocks_per_seq) {
+    if (num_seqs < 0 || max_query_len <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+        num_q_heads % num_kv_heads != 0)
+        return 0;
+    const int64_t rows = (int64_t)max_query_len * (num_q_heads / num_kv_heads);
+    const int64_t tiles = (rows + 15) / 16;
+    const int64_t items = (int64_t)num_seqs * tiles;
+    return pkv_default_partition_size(items > 0x7fffffff ? 0x7fffffff : (int)items, num_q_heads,
+                                      num_kv_heads, max_blocks_per_seq);
+}
+
+pkv_status pkv_paged_attn_multi(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, int max_blocks_per_seq,
+                                const int32_t* context_lens, const int32_t* query_start_loc,
+                                int num_seqs, int num_query_tokens, int max_query_len,
+                                int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                                int64_t num_blocks, float scale, int partition_size,
+                                void* workspace, size_t workspace_bytes, pkv_dtype q_dtype,
+                                pkv_dtype cache_dtype, hipStream_t stream) {
+    if (num_seqs < 0 || num_query_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+        max_blocks_per_seq <= 0 || num_blocks <= 0)
+        return fail(PKV_ERR_SHAPE,
+                    "need num_seqs, num_query_tokens >= 0 and positive num_q_heads, num_kv_heads, "
+                    "max_blocks_per_seq, num_blocks");
+    if (num_q_heads % num_kv_heads != 0)
+        return fail(PKV_ERR_SHAPE, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
+                    num_q_heads, num_kv_heads);
+    if (block_size != pkv::kBlockSize)
+        return fail(PKV_ERR_UNSUPPORTED, "block_size %d unsupported (only 16)", block_size);
+    if (!head_dim_ok(head_dim))
+        return fail(PKV_ERR_UNSUPPORTED, "head_dim %d unsupported (64, 128, 256)", head_dim);
+    if (!((q_dtype == PKV_F16 || q_dtype == PKV_BF16) && cache_dtype == q_dtype))
+        return fail(PKV_ERR_DTYPE, "multi-query attention needs (F16,F16) or (BF16,BF16), got "
+                                   "(%d, %d)", (int)q_dtype, (int)cache_dtype);
+    if (partition_size < 0 || partition_size % pkv::kBlockSize != 0)
+        return fail(PKV_ERR_SHAPE, "partition_size %d is not 0 or a positive multiple of 16",
+                    partition_size);
+    if (num_seqs == 0 || num_query_tokens == 0) return ok();
+    if (max_query_len <= 0)
+        return fail(PKV_ERR_SHAPE, "max_query_len must be positive");
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start_loc)
+        return fail(PKV_ERR_NULL, "out, q, k_cache, v_cache, block_tables, context_lens and "
+                                  "query_start_loc are required");
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+        return fail(PKV_ERR_SHAPE, "q, out, k_cache and v_cache must be 16-byte aligned");
+    const int g = num_q_heads / num_kv_heads;
+    const int64_t row_tiles = ((int64_t)max_query_len * g + 15) / 16;
+    const int P = partition_size ? partition_size
+                                 : pkv_multi_default_partition_size(num_seqs, max_query_len,
+                                                                    num_q_heads, num_kv_heads,
+                                                                    max_blocks_per_seq);
+    const int NP = num_partitions(max_blocks_per_seq, P);
+    const WorkspaceLayout w = layout(num_query_tokens, num_q_heads, head_dim, NP);
+    if (NP > 1) {
+        if (!workspace || workspace_bytes < w.total)
+            return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
+                        workspace ? workspace_bytes : (size_t)0);
+        if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+            return fail(PKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    }
+    if ((int64_t)num_seqs * num_kv_heads * row_tiles * NP > 0x7fffffff)
+        return fail(PKV_ERR_SHAPE, "too many work items for one launch");
+    char* ws = static_cast<char*>(workspace);
+    pkv::MultiArgs a{};
+    a.out = out;
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.query_start_loc = query_start_loc;
+    a.m_part = NP > 1 ? reinterpret_cast<float*>(ws + w.m_off) : nullptr;
+    a.l_part = NP > 1 ? reinterpret_cast<float*>(ws + w.l_off) : nullptr;
+    a.o_part = NP > 1 ? reinterpret_cast<float*>(ws + w.o_off) : nullptr;
+    a.num_blocks = num_blocks;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.partition_size = P;
+    a.num_partitions = NP;
+    a.row_tiles = (int)row_tiles;
+    a.num_tokens = num_query_tokens;
+    a.scale_log2 = scale * 1.44269504088896340736f;
+    pkv_status s = hip_status(pkv::launch_paged_multi(a, (int)q_dtype, head_dim, stream),
+                              "paged multi-query launch");
+    if (s != PKV_OK || NP == 1) return s;
+    pkv::ReduceArgs r{};
+    r.out = out;
+    r.m_part = a.m_part;
+    r.l_part = a.l_part;
+    r.o_part = a.o_part;
+    r.context_lens = context_lens;
+    r.num_seqs = num_seqs;
+    r.num_q_heads = num_q_heads;
+    r.partition_size = P;
+    r.num_partitions = NP;
+    r.skip_single = 1;
+    r.window = 0;
+    r.query_start_loc = query_start_loc;
+    r.num_rows = num_query_tokens;
+    return hip_status(pkv::launch_paged_reduce(r, (int)q_dtype, head_dim, stream),
+                      "paged_attn_reduce launch");
 }
 
 }  // extern "C"

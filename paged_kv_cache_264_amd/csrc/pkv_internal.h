@@ -77,6 +77,33 @@ __host__ __device__ inline int window_base(int n, int window) {
 hipError_t launch_paged_decode(const DecodeArgs& a, int q_dtype, int cache_dtype, int head_dim,
                                int heads_per_tile, hipStream_t stream);
 
+struct MultiArgs {
+    void* out;                       // [T][Hq][D], written for sequences with one partition
+    const void* q;                   // [T][Hq][D]
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    const int32_t* query_start_loc;  // [B + 1]
+    float* m_part;                   // [T][Hq][NP]
+    float* l_part;
+    float* o_part;                   // [T][Hq][NP][D]
+    int64_t num_blocks;
+    int num_seqs;
+    int num_q_heads;
+    int num_kv_heads;
+    int max_blocks_per_seq;
+    int partition_size;
+    int num_partitions;
+    int row_tiles;                   // ceil(max_query_len * Hq / Hkv / 16)
+    int num_tokens;                  // T: rows of q / out (query rows outside are skipped)
+    float scale_log2;
+};
+
+// Multi-query causal attention (fp16 / bf16 caches).  Returns
+// hipErrorInvalidValue for a combination with no kernel.
+hipError_t launch_paged_multi(const MultiArgs& a, int dtype, int head_dim, hipStream_t stream);
+
 struct ReduceArgs {
     void* out;
     const float* m_part;
@@ -89,6 +116,11 @@ struct ReduceArgs {
     int num_partitions;
     int skip_single;     // sequences with <= 1 partition already hold their output
     int window;          // sliding window of the decode that wrote the partials (0: none)
+    // multi-query partials: rows are query tokens; the sequence of token r is
+    // the b with query_start_loc[b] <= r < query_start_loc[b + 1] (nullptr:
+    // row r belongs to sequence r)
+    const int32_t* query_start_loc;
+    int num_rows;        // output rows: num_seqs, or the number of query tokens
 };
 
 hipError_t launch_paged_reduce(const ReduceArgs& a, int out_dtype, int head_dim,

@@ -1,0 +1,111 @@
+"""GPU parity of multi-query causal attention (pkv_paged_attn_multi, MFMA)
+against the oracle.
+
+Every sequence of a NaN-poisoned pool gets q_len queries at its last
+positions (1 = plain decode, up to the whole context = prefill from empty);
+outputs are compared element by element with the fp64 oracle.  Bound: the
+decode bound of the dtype plus the rounding of the softmax weights to the q
+dtype before they multiply V on the matrix cores, u * max|V| (u = 2^-11 for
+fp16, 2^-8 for bf16): |sum_t (p_t + d_t) v_t - sum_t p_t v_t| / l <= u max|v|.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from helpers import BS, DT, TOL, OracleView, as_f64, host
+
+pytestmark = pytest.mark.gpu
+U_P = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    import paged_kv_cache_264_amd as m
+    m._load()
+    return m
+
+
+def _run(pkv, dtype, D, Hq, Hkv, lens, qlens, P=0, seed=0):
+    cfg = dict(B=len(lens), ctx=list(lens), Hq=Hq, Hkv=Hkv, D=D, dtype=dtype, cache=dtype,
+               pool=None, seed=seed, max_ctx=max(max(lens), 16))
+    batch = W.make_batch(cfg=cfg, device="cuda")
+    T = int(sum(qlens))
+    q = W.token_rows(T, Hq, D, dtype, seed, W.S_STEP_Q).cuda()
+    qsl = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    view = OracleView(batch, np.arange(batch.B))
+    out = pkv.paged_attn_multi(q, batch.k_cache, batch.v_cache, batch.block_tables,
+                               batch.context_lens, torch.from_numpy(qsl).cuda(), batch.scale,
+                               max(qlens), partition_size=P)
+    torch.cuda.synchronize()
+    ref = oracle.paged_multi(host(q), dtype, view.k_cache, view.v_cache, dtype,
+                             view.block_tables, view.context_lens, qsl, batch.scale)
+    vmax = float(np.nanmax(np.abs(as_f64(batch.v_cache).reshape(-1)[
+        np.isfinite(as_f64(batch.v_cache).reshape(-1))])))
+    tol = TOL[dtype] + U_P[dtype] * vmax
+    got = as_f64(out)
+    err = float(np.abs(got - ref).max()) if np.isfinite(got).all() else float("inf")
+    print(f"[multi] {dtype} D={D} Hq={Hq} Hkv={Hkv} qlens={qlens} P={P} "
+          f"max_abs_err={err:.3e} tol={tol:.2e}", flush=True)
+    assert np.isfinite(got).all()
+    assert err <= tol
+    return err
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 2), (32, 8), (4, 1)])
+def test_multi_matrix(pkv, dtype, D, Hq, Hkv):
+    lens = [1, 16, 17, 250, 700, 33, 100]
+    qlens = [1, 4, 8, 16, 5, 33, 100]          # the last one is a prefill from empty
+    _run(pkv, dtype, D, Hq, Hkv, lens, qlens, seed=D + Hq)
+
+
+@pytest.mark.parametrize("P", [16, 48, 64, 512])
+def test_multi_partitions(pkv, P):
+    lens = [5, 64, 129, 1000, 1500]
+    qlens = [5, 7, 16, 17, 64]
+    _run(pkv, "f16", 128, 8, 2, lens, qlens, P=P, seed=P)
+
+
+def test_multi_single_query_matches_decode(pkv):
+    lens = [1, 16, 17, 300, 33]
+    cfg = dict(B=5, ctx=lens, Hq=8, Hkv=2, D=128, dtype="f16", cache="f16", pool=None, seed=4,
+               max_ctx=300)
+    batch = W.make_batch(cfg=cfg, device="cuda")
+    qsl = torch.arange(6, dtype=torch.int32, device="cuda")
+    multi = pkv.paged_attn_multi(batch.q, batch.k_cache, batch.v_cache, batch.block_tables,
+                                 batch.context_lens, qsl, batch.scale, 1)
+    dec = pkv.paged_attn_decode(batch.q, batch.k_cache, batch.v_cache, batch.block_tables,
+                                batch.context_lens, batch.scale)
+    torch.cuda.synchronize()
+    # different rounding (P in fp16 on the matrix cores) but the same attention
+    assert float((multi.float() - dec.float()).abs().max()) <= 2e-3 + 2.0 ** -11 * 5
+
+
+def test_multi_verify_workload_sample(pkv):
+    """The speculative-verification shape at full size: 64 LLaMA-7B sequences,
+    8 queries each, U[512, 4096] contexts; 4 sequences checked by the oracle."""
+    batch = W.make_batch("verify", device="cuda", poison=True)
+    ql = batch.cfg["q_len"]
+    T = batch.B * ql
+    q = W.token_rows(T, batch.Hq, batch.D, "f16", batch.seed, W.S_STEP_Q).cuda()
+    qsl = (np.arange(batch.B + 1) * ql).astype(np.int32)
+    out = pkv.paged_attn_multi(q, batch.k_cache, batch.v_cache, batch.block_tables,
+                               batch.context_lens, torch.from_numpy(qsl).cuda(), batch.scale, ql)
+    torch.cuda.synchronize()
+    seqs = [0, 17, 40, 63]
+    view = OracleView(batch, seqs)
+    rows = np.concatenate([np.arange(s * ql, (s + 1) * ql) for s in seqs])
+    sub_qsl = (np.arange(len(seqs) + 1) * ql).astype(np.int32)
+    ref = oracle.paged_multi(host(q[torch.from_numpy(rows).cuda()]), "f16", view.k_cache,
+                             view.v_cache, "f16", view.block_tables, view.context_lens, sub_qsl,
+                             batch.scale)
+    got = as_f64(out)[rows]
+    assert np.isfinite(as_f64(out)).all()
+    err = float(np.abs(got - ref).max())
+    print(f"[multi verify] max_abs_err={err:.3e}", flush=True)
+    assert err <= TOL["f16"] + U_P["f16"] * 5.5

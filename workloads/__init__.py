@@ -55,6 +55,11 @@ CONFIGS = {
     # released: their table entries are -1).
     "window": dict(B=64, ctx=(4096, 12288), Hq=32, Hkv=32, D=128, dtype="f16", cache="f16",
                    pool=None, seed=9, max_ctx=12288, window=4096),
+    # Speculative-decoding verification at the LLaMA-7B shape: every sequence
+    # scores q_len = 8 tokens (7 drafts + 1) over U[512, 4096] cached tokens
+    # (the 8 included), in one multi-query pass.
+    "verify": dict(B=64, ctx=(512, 4096), Hq=32, Hkv=32, D=128, dtype="f16", cache="f16",
+                   pool=None, seed=10, max_ctx=4096, q_len=8),
     # FP8 (e4m3) KV cache at the LLaMA-7B shape, populated the same way.
     "fp8": dict(B=64, ctx=(512, 4096), Hq=32, Hkv=32, D=128, dtype="f16", cache="f8",
                 pool=None, seed=8, max_ctx=4096),
