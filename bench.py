@@ -36,6 +36,8 @@ WORKLOAD_NAMES = {
     "int8": "llama7b-mha-int8kv-paged-decode",
     "fp8": "llama7b-mha-fp8e4m3kv-paged-decode",
     "window": "llama7b-mha-fp16-sliding-window-4096-decode",
+    "verify": "llama7b-mha-fp16-speculative-verify-8-queries",
+    "prefill": "llama7b-mha-fp16-chunked-prefill-512",
     "sampling": "llama7b-parallel-sampling-shared-prefix-decode",
 }
 KERNEL_SOURCES = ["paged_decode.hip", "pkv_device.h", "pkv_internal.h", "pkv_api.hip"]
@@ -105,6 +107,9 @@ def main():
         return
     if args.config == "sampling":
         bench_sampling(args)
+        return
+    if "q_len" in __import__("workloads").CONFIGS[args.config]:
+        bench_multi(args)
         return
 
     import numpy as np
@@ -275,6 +280,147 @@ def main():
         result["cpu_baseline"] = run_cpu_baseline(batch, args.config, args.cpu_seconds,
                                                   e_kv, e_q, int8, window)
     print(json.dumps(result), flush=True)
+
+
+def bench_multi(args):
+    """Several query tokens per sequence (speculative verification, chunked
+    prefill).  A step: the cache write of the B * q_len new tokens' K/V, then
+    multi-query causal attention over the paged cache."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_264_amd as pkv
+    import workloads as W
+
+    torch.cuda.set_device(0)
+    cfg = W.CONFIGS[args.config]
+    batch = W.make_batch(args.config, device="cuda", seed=args.seed, poison=False)
+    ql = int(cfg["q_len"])
+    lens = batch.layout.context_lens.astype(np.int64)
+    qlens = np.minimum(lens, ql)
+    qsl_np = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    T = int(qsl_np[-1])
+    qsl = torch.from_numpy(qsl_np).cuda()
+    q = W.token_rows(T, batch.Hq, batch.D, cfg["dtype"], batch.seed, W.S_STEP_Q, "cuda")
+    k_new = W.token_rows(T, batch.Hkv, batch.D, cfg["dtype"], batch.seed, W.S_NEWK, "cuda")
+    v_new = W.token_rows(T, batch.Hkv, batch.D, cfg["dtype"], batch.seed, W.S_NEWV, "cuda")
+    slots = torch.from_numpy(np.concatenate(
+        [W.slots_for(batch.layout, b, np.arange(int(n) - int(k), int(n)))
+         for b, (n, k) in enumerate(zip(lens, qlens))])).cuda()
+    out = torch.empty_like(q)
+    mbs = batch.block_tables.shape[1]
+    P = args.partition_size or pkv._load().pkv_multi_default_partition_size(
+        batch.B, ql, batch.Hq, batch.Hkv, mbs)
+    ws = torch.empty(max(pkv._load().pkv_multi_workspace_size(T, batch.Hq, batch.D, mbs, P), 256),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    e = 2
+    kv_bytes = int(lens.sum()) * batch.Hkv * 2 * batch.D * e
+    launch_bytes = (kv_bytes + T * batch.Hq * batch.D * e * 2
+                    + int(sum(W.blocks_needed(int(n)) for n in lens)) * 4 + 8 * batch.B)
+    write_bytes = T * batch.Hkv * 2 * batch.D * e * 2 + T * 8
+    step_bytes = launch_bytes + write_bytes
+    flops = W.multi_query_flops(lens, ql, batch.Hq, batch.D)
+
+    def step(ev0=None, ev1=None):
+        pkv.kv_cache_write(k_new, v_new, batch.k_cache, batch.v_cache, slots)
+        if ev0 is not None:
+            ev0.record(stream)
+        pkv.paged_attn_multi(q, batch.k_cache, batch.v_cache, batch.block_tables,
+                             batch.context_lens, qsl, batch.scale, ql, out=out, partition_size=P,
+                             workspace=ws)
+        if ev1 is not None:
+            ev1.record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        step(e0, e1)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    assert torch.isfinite(out.float()).all()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    k_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    hbm = launch_bytes / (k_ms * 1e-3) / 1e9
+    tflops = flops / (k_ms * 1e-3) / 1e12
+    ridge = 2500.0 / HBM_PEAK_GBS * 1e3          # flop per byte where fp16 MFMA meets HBM
+    mfma_bound = flops / launch_bytes > ridge
+    roof = ({"bound": "mfma", "achieved": round(tflops, 2), "peak": 2500.0, "unit": "TFLOP/s",
+             "frac": round(tflops / 2500.0, 4)} if mfma_bound else
+            {"bound": "hbm", "achieved": round(hbm, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(hbm / HBM_PEAK_GBS, 4)})
+    roof.update({"traffic": None, "kernel": "paged_multi_kernel" + (
+        " + paged_reduce_kernel (events span both)" if pkv.num_partitions(mbs, P) > 1 else ""),
+        "kernel_sha": kernel_sha(), "flop_per_byte": round(flops / launch_bytes, 2)})
+    result = {
+        "metric": METRIC, "value": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg["dtype"], "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[args.config], "num_seqs": batch.B,
+                   "queries_per_seq": ql, "query_tokens": T, "num_q_heads": batch.Hq,
+                   "num_kv_heads": batch.Hkv, "head_dim": batch.D, "block_size": W.BLOCK_SIZE,
+                   "context_lens": f"U[{cfg['ctx'][0]},{cfg['ctx'][1]}]",
+                   "sum_context_tokens": int(lens.sum()), "partition_size": P,
+                   "seed": batch.seed, "parallelism": "single-gpu",
+                   "step": "kv_cache_write of the query tokens + multi-query attention"},
+        "query_tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
+        "multi_kernel_us": round(k_ms * 1e3, 2),
+        "kernel_hbm_gbs": round(hbm, 1), "kernel_tflops": round(tflops, 2),
+        "launch_alg_bytes": launch_bytes, "launch_flops": flops,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = run_multi_cpu_baseline(batch, q, qsl_np, ql, args.cpu_seconds,
+                                                        flops, launch_bytes)
+    print(json.dumps(result), flush=True)
+
+
+def run_multi_cpu_baseline(batch, q, qsl_np, ql, target_s, flops, launch_bytes):
+    """The multi-query oracle on the first sequences, sized to ~target_s."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads as W
+
+    lens = batch.layout.context_lens
+    threads = oracle.num_threads(len(os.sched_getaffinity(0)))
+
+    def h(t):
+        t = t.contiguous().cpu()
+        return t.view(torch.int16).numpy().view(np.uint16)
+
+    def run(n_seq):
+        blocks = np.concatenate([batch.layout.block_tables[s, :W.blocks_needed(lens[s])]
+                                 for s in range(n_seq)]).astype(np.int64)
+        remap = np.full(batch.num_blocks, -1, np.int64)
+        remap[blocks] = np.arange(len(blocks))
+        bt = batch.layout.block_tables[:n_seq].copy()
+        bt[bt >= 0] = remap[bt[bt >= 0]]
+        idx = torch.from_numpy(blocks).cuda()
+        T = int(qsl_np[n_seq])
+        args = (h(q[:T]), "f16", h(batch.k_cache[idx]), h(batch.v_cache[idx]), "f16",
+                bt.astype(np.int32), lens[:n_seq].astype(np.int32), qsl_np[:n_seq + 1],
+                batch.scale)
+        t = time.perf_counter()
+        oracle.paged_multi(*args)
+        return time.perf_counter() - t
+
+    t_one = max(run(1), 1e-4)
+    n_seq = max(1, min(batch.B, int(target_s / t_one)))
+    t_s = run(n_seq)
+    frac = float(lens[:n_seq].sum()) / float(lens.sum())
+    return {"value": round(launch_bytes * frac / t_s / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"first {n_seq} of {batch.B} sequences ({int(qsl_np[n_seq])} query tokens), "
+                      f"one fp64 oracle pass of {t_s:.2f} s",
+            "tflops": round(flops * frac / t_s / 1e12, 6), "seconds": round(t_s, 3)}
 
 
 def bench_sampling(args):

@@ -320,6 +320,231 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
     }
 }
 
+// Long runs of queries (prefill chunks): a work-group owns 4 waves x RW row
+// tiles of 16 rows and walks every block of its partition up to the last
+// position any of its rows attends to.  Each 16-token K/V block is fetched
+// once per work-group (one 16-byte chunk per thread), staged in
+// double-buffered padded LDS tiles, and every wave reads the K operand and the
+// V operand once per block and reuses them for its RW row tiles; one barrier
+// per block.  Each wave owns its rows for the whole partition, so there is no
+// merge between waves.
+template <Elem T, int D, int RW>
+__global__ __launch_bounds__(kThreads) void paged_multi_tiled_kernel(MultiArgs a) {
+    constexpr int KK = D / 32;
+    constexpr int NN = D / 16;
+    constexpr int ROW = D * 2;
+    constexpr int TILE = kRows * ROW;
+    constexpr int LS = ROW + 16;                    // padded LDS row stride
+    constexpr int CH = TILE / 16;                   // 16-byte chunks per tile
+    constexpr int CPT = (CH + kThreads - 1) / kThreads;
+    constexpr int WG_ROWS = kWaves * kRows * RW;
+
+    __shared__ __attribute__((aligned(16))) char s_k[2][kRows * LS];
+    __shared__ __attribute__((aligned(16))) char s_v[2][kRows * LS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = lane >> 4;
+    const int col = lane & 15;
+
+    const int NP = a.num_partitions;
+    int rest = blockIdx.x;
+    const int part = rest % NP;
+    rest /= NP;
+    const int rg = rest % a.row_tiles;
+    rest /= a.row_tiles;
+    const int kvh = rest % a.num_kv_heads;
+    const int b = rest / a.num_kv_heads;
+
+    const int Hq = a.num_q_heads;
+    const int g = Hq / a.num_kv_heads;
+    const int q0 = a.query_start_loc[b];
+    const int q1 = min(a.query_start_loc[b + 1], a.num_tokens);
+    const int qlen = a.query_start_loc[b + 1] - q0;
+    const int rows_total = q0 < 0 ? 0 : max(0, q1 - q0) * g;
+    const int wg_r0 = rg * WG_ROWS;
+    if (wg_r0 >= rows_total) return;
+    const int n_cap = a.max_blocks_per_seq * kBlockSize;
+    int n = a.context_lens[b];
+    n = n < 0 ? 0 : (n > n_cap ? n_cap : n);
+    const int n_parts = partition_count(n, a.partition_size);
+    const bool direct_out = n_parts <= 1;
+    if (part >= (n_parts > 0 ? n_parts : 1)) return;
+    const int span = n_parts > 0 ? partition_span(n, n_parts) : 0;
+    const int t_begin = part * span;
+    const int t_end = min(n, t_begin + span);
+    // the last position any row of this work-group attends to
+    const int r_last = min(wg_r0 + WG_ROWS, rows_total) - 1;
+    const int t_stop = min(t_end, max(n - qlen + r_last / g + 1, 0));
+    const int blk_begin = t_begin / kBlockSize;
+    const int blk_stop = t_stop > t_begin ? (t_stop + kBlockSize - 1) / kBlockSize : blk_begin;
+    const int32_t* table = a.block_tables + (size_t)b * a.max_blocks_per_seq;
+    const float c = a.scale_log2;
+
+    // this wave's row tiles
+    const int w_r0 = wg_r0 + wave * kRows * RW;
+    bool row_ok[RW];
+    int pos[RW];
+    uint4 qv[RW][KK];
+    float m[RW], l[RW];
+    f32x4_t o[RW][NN];
+#pragma unroll
+    for (int rr = 0; rr < RW; ++rr) {
+        const int R = w_r0 + rr * kRows + col;
+        row_ok[rr] = R < rows_total;
+        const int jq = row_ok[rr] ? R / g : 0;
+        const int hq = kvh * g + (row_ok[rr] ? R % g : 0);
+        pos[rr] = n - qlen + jq;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            qv[rr][kk] = make_uint4(0u, 0u, 0u, 0u);
+            if (row_ok[rr])
+                qv[rr][kk] = *reinterpret_cast<const uint4*>(
+                    static_cast<const char*>(a.q) +
+                    (((size_t)(q0 + jq) * Hq + hq) * D + kk * 32 + grp * 8) * 2);
+        }
+        m[rr] = kNegBig;
+        l[rr] = 0.f;
+#pragma unroll
+        for (int nn = 0; nn < NN; ++nn) o[rr][nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+    auto gload = [&](int jb, uint4 (&kc)[CPT], uint4 (&vc)[CPT]) {
+        const int phys = table[jb];
+        const bool ok = phys >= 0 && (int64_t)phys < a.num_blocks;
+        const size_t tile = (size_t)(ok ? phys : 0) * a.num_kv_heads + kvh;
+        const int bytes = ok ? TILE : 0;
+        const __amdgpu_buffer_rsrc_t kr = rsrc(static_cast<const char*>(a.k_cache) + tile * TILE, bytes);
+        const __amdgpu_buffer_rsrc_t vr = rsrc(static_cast<const char*>(a.v_cache) + tile * TILE, bytes);
+#pragma unroll
+        for (int cc = 0; cc < CPT; ++cc) {
+            const int ch = cc * kThreads + tid;
+            const int off = ch < CH ? ch * 16 : TILE;     // past the tile: reads zeros
+            kc[cc] = ld16(kr, off);
+            vc[cc] = ld16(vr, off);
+        }
+    };
+    auto lstore = [&](int buf, int jb, const uint4 (&kc)[CPT], const uint4 (&vc)[CPT]) {
+#pragma unroll
+        for (int cc = 0; cc < CPT; ++cc) {
+            const int ch = cc * kThreads + tid;
+            if (ch < CH) {
+                const int tok = ch / (ROW / 16), off = (ch % (ROW / 16)) * 16;
+                // rows past the partition are zeroed: weight 0 times NaN would not be 0
+                const bool keep = jb * kBlockSize + tok < t_end;
+                const uint4 kx = kc[cc], vx = vc[cc];
+                *reinterpret_cast<uint4*>(s_k[buf] + tok * LS + off) =
+                    make_uint4(keep ? kx.x : 0u, keep ? kx.y : 0u, keep ? kx.z : 0u,
+                               keep ? kx.w : 0u);
+                *reinterpret_cast<uint4*>(s_v[buf] + tok * LS + off) =
+                    make_uint4(keep ? vx.x : 0u, keep ? vx.y : 0u, keep ? vx.z : 0u,
+                               keep ? vx.w : 0u);
+            }
+        }
+    };
+    auto compute = [&](int buf, int jb) {
+        uint4 ka[KK];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            ka[kk] = *reinterpret_cast<const uint4*>(s_k[buf] + col * LS + (kk * 32 + grp * 8) * 2);
+        uint2 vb[NN];
+#pragma unroll
+        for (int nn = 0; nn < NN; ++nn) {
+            const char* base = s_v[buf] + (grp * 4) * LS + (nn * 16 + col) * 2;
+            const uint32_t v0 = *reinterpret_cast<const uint16_t*>(base);
+            const uint32_t v1 = *reinterpret_cast<const uint16_t*>(base + LS);
+            const uint32_t v2 = *reinterpret_cast<const uint16_t*>(base + 2 * LS);
+            const uint32_t v3 = *reinterpret_cast<const uint16_t*>(base + 3 * LS);
+            vb[nn] = make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
+        }
+#pragma unroll
+        for (int rr = 0; rr < RW; ++rr) {
+            f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) s = Mfma<T>::qk(ka[kk], qv[rr][kk], s);
+            float sv[4], mx = kNegBig;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = jb * kBlockSize + grp * 4 + i;
+                const bool valid = row_ok[rr] && t < t_end && t <= pos[rr];
+                sv[i] = valid ? s[i] * c : -INFINITY;
+                mx = fmaxf(mx, sv[i]);
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mn = fmaxf(m[rr], mx);
+            const float alpha = fast_exp2(m[rr] - mn);
+            float p[4], ps = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[i] = fast_exp2(sv[i] - mn);
+                ps += p[i];
+            }
+            ps += __shfl_xor(ps, 16);
+            ps += __shfl_xor(ps, 32);
+            l[rr] = fmaf(l[rr], alpha, ps);
+            m[rr] = mn;
+            float al[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, grp * 4 + i);
+            const uint2 pa = make_uint2(Mfma<T>::pack(p[0], p[1]), Mfma<T>::pack(p[2], p[3]));
+#pragma unroll
+            for (int nn = 0; nn < NN; ++nn) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[rr][nn][i] *= al[i];
+                o[rr][nn] = Mfma<T>::pv(pa, vb[nn], o[rr][nn]);
+            }
+        }
+    };
+
+    if (blk_begin < blk_stop) {
+        uint4 kc[CPT], vc[CPT];
+        gload(blk_begin, kc, vc);
+        lstore(0, blk_begin, kc, vc);
+        __syncthreads();
+        for (int jb = blk_begin; jb < blk_stop; ++jb) {
+            const int buf = (jb - blk_begin) & 1;
+            const bool more = jb + 1 < blk_stop;
+            if (more) gload(jb + 1, kc, vc);
+            compute(buf, jb);
+            if (more) lstore(buf ^ 1, jb + 1, kc, vc);
+            __syncthreads();
+        }
+    }
+
+    // ---- epilogue: each wave writes its own rows ---------------------------
+#pragma unroll
+    for (int rr = 0; rr < RW; ++rr) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int qr = grp * 4 + i;
+            const float lr = __shfl(l[rr], qr);
+            const float mr = __shfl(m[rr], qr);
+            const int R = w_r0 + rr * kRows + qr;
+            if (R >= rows_total) continue;
+            const float inv = lr > 0.f ? 1.f / lr : 0.f;
+            const size_t orow = (size_t)(q0 + R / g) * Hq + kvh * g + R % g;
+            const size_t pi = orow * NP + part;
+#pragma unroll
+            for (int nn = 0; nn < NN; ++nn) {
+                const int d = nn * 16 + col;
+                if (direct_out)
+                    store_elem<T>(a.out, orow * D + d, o[rr][nn][i] * inv);
+                else
+                    a.o_part[pi * D + d] = o[rr][nn][i] * inv;
+            }
+            if (!direct_out && col == 0) {
+                a.m_part[pi] = mr * kLn2;
+                a.l_part[pi] = lr;
+            }
+        }
+    }
+}
+
+constexpr int kTiledRW = 2;                 // row tiles per wave in the tiled kernel
+constexpr int kTiledMinRows = 64;           // rows per (sequence, kv head) that select it
+
 template <Elem T>
 hipError_t launch_d(const MultiArgs& a, int d, int64_t grid, hipStream_t s) {
     const dim3 g((unsigned)grid), blk(kThreads);
@@ -332,16 +557,40 @@ hipError_t launch_d(const MultiArgs& a, int d, int64_t grid, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <Elem T>
+hipError_t launch_tiled(const MultiArgs& a, int d, int64_t grid, hipStream_t s) {
+    const dim3 g((unsigned)grid), blk(kThreads);
+    switch (d) {
+    case 64: hipLaunchKernelGGL((paged_multi_tiled_kernel<T, 64, kTiledRW>), g, blk, 0, s, a); break;
+    case 128: hipLaunchKernelGGL((paged_multi_tiled_kernel<T, 128, kTiledRW>), g, blk, 0, s, a); break;
+    case 256: hipLaunchKernelGGL((paged_multi_tiled_kernel<T, 256, 1>), g, blk, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
+
+int64_t multi_row_groups(int max_rows, int head_dim) {
+    if (max_rows < kTiledMinRows) return (max_rows + kRows - 1) / kRows;
+    const int rw = head_dim == 256 ? 1 : kTiledRW;
+    const int per = kWaves * kRows * rw;
+    return (max_rows + per - 1) / per;
+}
 
 hipError_t launch_paged_multi(const MultiArgs& a, int dtype, int head_dim, hipStream_t stream) {
     const int64_t grid =
         (int64_t)a.num_seqs * a.num_kv_heads * a.row_tiles * a.num_partitions;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const bool tiled = a.max_rows >= kTiledMinRows;
     const Elem e = static_cast<Elem>(dtype);
-    if (e == Elem::F16) return launch_d<Elem::F16>(a, head_dim, grid, stream);
-    if (e == Elem::BF16) return launch_d<Elem::BF16>(a, head_dim, grid, stream);
+    if (e == Elem::F16)
+        return tiled ? launch_tiled<Elem::F16>(a, head_dim, grid, stream)
+                     : launch_d<Elem::F16>(a, head_dim, grid, stream);
+    if (e == Elem::BF16)
+        return tiled ? launch_tiled<Elem::BF16>(a, head_dim, grid, stream)
+                     : launch_d<Elem::BF16>(a, head_dim, grid, stream);
     return hipErrorInvalidValue;
 }
 

@@ -539,7 +539,10 @@ pkv_status pkv_paged_attn_multi(void* out, const void* q, const void* k_cache, c
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
         return fail(PKV_ERR_SHAPE, "q, out, k_cache and v_cache must be 16-byte aligned");
     const int g = num_q_heads / num_kv_heads;
-    const int64_t row_tiles = ((int64_t)max_query_len * g + 15) / 16;
+    if ((int64_t)max_query_len * g > 0x7fffffff)
+        return fail(PKV_ERR_SHAPE, "max_query_len * num_q_heads / num_kv_heads too large");
+    const int max_rows = max_query_len * g;
+    const int64_t row_tiles = pkv::multi_row_groups(max_rows, head_dim);
     const int P = partition_size ? partition_size
                                  : pkv_multi_default_partition_size(num_seqs, max_query_len,
                                                                     num_q_heads, num_kv_heads,
@@ -575,6 +578,7 @@ pkv_status pkv_paged_attn_multi(void* out, const void* q, const void* k_cache, c
     a.partition_size = P;
     a.num_partitions = NP;
     a.row_tiles = (int)row_tiles;
+    a.max_rows = max_rows;
     a.num_tokens = num_query_tokens;
     a.scale_log2 = scale * 1.44269504088896340736f;
     pkv_status s = hip_status(pkv::launch_paged_multi(a, (int)q_dtype, head_dim, stream),

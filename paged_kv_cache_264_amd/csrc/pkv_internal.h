@@ -95,10 +95,15 @@ struct MultiArgs {
     int max_blocks_per_seq;
     int partition_size;
     int num_partitions;
-    int row_tiles;                   // ceil(max_query_len * Hq / Hkv / 16)
+    int row_tiles;                   // row groups per (sequence, kv head): multi_row_groups()
+    int max_rows;                    // max_query_len * Hq / Hkv (selects the kernel)
     int num_tokens;                  // T: rows of q / out (query rows outside are skipped)
     float scale_log2;
 };
+
+// Work-groups along the query rows of one (sequence, kv head): 16-row tiles
+// for short query runs, 4 waves x 16 x RW rows for long ones.
+int64_t multi_row_groups(int max_rows, int head_dim);
 
 // Multi-query causal attention (fp16 / bf16 caches).  Returns
 // hipErrorInvalidValue for a combination with no kernel.

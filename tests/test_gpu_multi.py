@@ -109,3 +109,23 @@ def test_multi_verify_workload_sample(pkv):
     err = float(np.abs(got - ref).max())
     print(f"[multi verify] max_abs_err={err:.3e}", flush=True)
     assert err <= TOL["f16"] + U_P["f16"] * 5.5
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 2), (32, 8)])
+@pytest.mark.parametrize("P", [0, 32])
+def test_multi_short_query_runs(pkv, dtype, Hq, Hkv, P):
+    """Fewer than 64 rows per (sequence, kv head): the 16-row-tile kernel,
+    with several row tiles when the group is wide."""
+    lens = [3, 16, 17, 250, 700, 33]
+    qlens = [1, 2, 3, 4, 8, 7]
+    _run(pkv, dtype, 128, Hq, Hkv, lens, qlens, P=P, seed=Hq + P)
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_multi_prefill_chunks(pkv, D):
+    """Long query runs (the tiled kernel): 300-token chunks at the end of
+    longer contexts and a whole prompt, several work-groups per sequence."""
+    lens = [1000, 300, 777]
+    qlens = [300, 300, 129]
+    _run(pkv, "f16", D, 8, 4, lens, qlens, seed=D)

@@ -60,6 +60,10 @@ CONFIGS = {
     # (the 8 included), in one multi-query pass.
     "verify": dict(B=64, ctx=(512, 4096), Hq=32, Hkv=32, D=128, dtype="f16", cache="f16",
                    pool=None, seed=10, max_ctx=4096, q_len=8),
+    # Chunked prefill at the LLaMA-7B shape: every sequence adds a 512-token
+    # chunk of its prompt over U[1024, 4096] cached tokens (the chunk included).
+    "prefill": dict(B=16, ctx=(1024, 4096), Hq=32, Hkv=32, D=128, dtype="f16", cache="f16",
+                    pool=None, seed=11, max_ctx=4096, q_len=512),
     # FP8 (e4m3) KV cache at the LLaMA-7B shape, populated the same way.
     "fp8": dict(B=64, ctx=(512, 4096), Hq=32, Hkv=32, D=128, dtype="f16", cache="f8",
                 pool=None, seed=8, max_ctx=4096),
@@ -358,3 +362,14 @@ def token_rows(n: int, Hkv: int, D: int, dtype: str, seed: int, stream: int,
     """[n][Hkv][D] N(0,1) rows rounded to dtype: the K (or V) row of token id
     0..n-1.  Row values depend only on (seed, stream, n, device)."""
     return _normal((n, Hkv, D), seed, stream, device, dtype)
+
+
+def multi_query_flops(context_lens, q_len: int, Hq: int, D: int) -> int:
+    """Flops of causal multi-query attention: every query at position p scores
+    p + 1 keys and sums p + 1 values, 2 D flops each, per q head."""
+    total = 0
+    for n in np.asarray(context_lens, np.int64):
+        ql = min(int(q_len), int(n))
+        p = np.arange(int(n) - ql, int(n), dtype=np.int64)
+        total += int((p + 1).sum()) * 4 * D * Hq
+    return total
