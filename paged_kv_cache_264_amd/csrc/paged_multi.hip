@@ -22,10 +22,15 @@
 //     straight from the pool with raw buffer loads; the B operand is Q,
 //     loaded once.  The C layout puts a query's 16 scores in the 4 lanes
 //     l%16 = query, so the online-softmax max / sum need two lane swaps.
-//   * the same C layout is the A operand of v_mfma_f32_16x16x16 for P V, so
-//     P never leaves registers.  V is staged in a per-wave LDS tile (row
-//     stride 2D + 16 bytes: the 4 lane groups of a transposed read fall on
-//     different banks) and read back as the B operand.
+//   * the output is accumulated transposed, O^T = V^T P^T, on
+//     v_mfma_f32_16x16x16: the score C layout is then the B operand as it
+//     stands (P never leaves registers) and the accumulator column of a lane
+//     is its own query, so rescaling needs no lane exchange.  V is staged in a
+//     per-wave LDS tile (row stride 2D + 16 bytes: the 4 lane groups of a
+//     transposed read fall on different banks) and read back as the A operand.
+//   * the running max is shared by the 4 lanes of a query and reduced across
+//     them only when a score exceeds it; each lane sums its own tokens and
+//     the 4 partial sums are added once at the end.
 //   * tokens past a query's position, past the partition or past the context
 //     are masked by select; the 4 waves are merged through LDS at the end.
 //     Sequences with one partition write the output directly, longer ones
@@ -61,6 +66,9 @@ template <> struct Mfma<Elem::F16> {
         return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
                                                      __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
     }
+    static __device__ __forceinline__ f32x4_t pv32(const uint4& a, const uint4& b, f32x4_t c) {
+        return qk(a, b, c);
+    }
     static __device__ __forceinline__ uint32_t pack(float x, float y) {
         const _Float16 a = (_Float16)x, b = (_Float16)y;
         return (uint32_t)__builtin_bit_cast(uint16_t, a) |
@@ -78,6 +86,9 @@ template <> struct Mfma<Elem::BF16> {
                                                          __builtin_bit_cast(s16x4_t, b), c, 0, 0,
                                                          0);
     }
+    static __device__ __forceinline__ f32x4_t pv32(const uint4& a, const uint4& b, f32x4_t c) {
+        return qk(a, b, c);
+    }
     static __device__ __forceinline__ uint32_t pack(float x, float y) {
         const __bf16 a = (__bf16)x, b = (__bf16)y;
         return (uint32_t)__builtin_bit_cast(uint16_t, a) |
@@ -91,6 +102,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int byt
 }
 __device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, int off) {
     const u32x4_v v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+// cached load: blocks that several work-groups of a sequence read
+__device__ __forceinline__ uint4 ld16_cached(__amdgpu_buffer_rsrc_t r, int off) {
+    const u32x4_v v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -210,24 +226,24 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
             sv[i] = valid ? s[i] * c : -INFINITY;
             mx = fmaxf(mx, sv[i]);
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mn = fmaxf(m, mx);
-        const float alpha = fast_exp2(m - mn);
+        // shared running max, reduced across the query's 4 lanes only when
+        // some score exceeds it; l is this lane's share of the sum
+        const bool grew = __builtin_amdgcn_ballot_w64(mx > m) != 0;
+        float alpha = 1.f;
+        if (grew) {
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mn = fmaxf(m, mx);
+            alpha = fast_exp2(m - mn);
+            m = mn;
+        }
         float p[4], ps = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            p[i] = fast_exp2(sv[i] - mn);
+            p[i] = fast_exp2(sv[i] - m);
             ps += p[i];
         }
-        ps += __shfl_xor(ps, 16);
-        ps += __shfl_xor(ps, 32);
         l = fmaf(l, alpha, ps);
-        m = mn;
-        // rows of the O tile held by this lane are queries 4*grp + i
-        float al[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, grp * 4 + i);
         // stage V (natural layout) in this wave's LDS tile; rows past the
         // partition are zeroed (their weight is 0, but 0 * NaN would not be)
 #pragma unroll
@@ -250,9 +266,9 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
             const uint32_t v2 = *reinterpret_cast<const uint16_t*>(base + 2 * VS);
             const uint32_t v3 = *reinterpret_cast<const uint16_t*>(base + 3 * VS);
             const uint2 vb = make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o[nn][i] *= al[i];
-            o[nn] = Mfma<T>::pv(pa, vb, o[nn]);
+            // O^T = V^T P^T: the accumulator column is the lane's own query
+            if (grew) o[nn] *= alpha;
+            o[nn] = Mfma<T>::pv(vb, pa, o[nn]);
         }
         __asm__ volatile("" ::: "memory");
     };
@@ -269,8 +285,10 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
     }
 
     // ---- merge the 4 waves (wave 0 keeps its tile in registers) ------------
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
     __syncthreads();  // every wave is done with its V stage
-    float* s_o = reinterpret_cast<float*>(s_buf);  // [wave - 1][row][D]
+    float* s_o = reinterpret_cast<float*>(s_buf);  // [wave - 1][query][D]
     if (grp == 0) {
         s_m[wave][col] = m;
         s_l[wave][col] = l;
@@ -278,60 +296,72 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
     if (wave > 0) {
 #pragma unroll
         for (int nn = 0; nn < NN; ++nn)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                s_o[((wave - 1) * kRows + grp * 4 + i) * D + nn * 16 + col] = o[nn][i];
+            *reinterpret_cast<float4*>(&s_o[((wave - 1) * kRows + col) * D + nn * 16 + grp * 4]) =
+                make_float4(o[nn][0], o[nn][1], o[nn][2], o[nn][3]);
     }
     __syncthreads();
     if (wave != 0) return;
 
+    // lane: query col, channels 16 nn + 4 grp + i
+    const int Rr = rt * kRows + col;
+    if (Rr >= rows_total) return;
+    float M = kNegBig;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int qr = grp * 4 + i;                 // query row of o[.][i]
-        const int Rr = rt * kRows + qr;
-        if (Rr >= rows_total) continue;
-        float M = kNegBig;
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][col]);
+    float f[kWaves], L = 0.f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][qr]);
-        float f[kWaves], L = 0.f;
+    for (int w = 0; w < kWaves; ++w) {
+        f[w] = fast_exp2(s_m[w][col] - M);
+        L = fmaf(s_l[w][col], f[w], L);
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const size_t orow = (size_t)(q0 + Rr / g) * Hq + kvh * g + Rr % g;
+    const size_t pi = orow * NP + part;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            f[w] = fast_exp2(s_m[w][qr] - M);
-            L = fmaf(s_l[w][qr], f[w], L);
+    for (int nn = 0; nn < NN; ++nn) {
+        const int d0 = nn * 16 + grp * 4;
+        float O[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[i] = o[nn][i] * f[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) {
+            const float4 x = *reinterpret_cast<const float4*>(&s_o[((w - 1) * kRows + col) * D + d0]);
+            O[0] = fmaf(x.x, f[w], O[0]);
+            O[1] = fmaf(x.y, f[w], O[1]);
+            O[2] = fmaf(x.z, f[w], O[2]);
+            O[3] = fmaf(x.w, f[w], O[3]);
         }
-        const float inv = L > 0.f ? 1.f / L : 0.f;
-        const size_t orow = (size_t)(q0 + Rr / g) * Hq + kvh * g + Rr % g;
-        const size_t pi = orow * NP + part;
-#pragma unroll
-        for (int nn = 0; nn < NN; ++nn) {
-            const int d = nn * 16 + col;
-            float O = o[nn][i] * f[0];
-#pragma unroll
-            for (int w = 1; w < kWaves; ++w) O = fmaf(s_o[((w - 1) * kRows + qr) * D + d], f[w], O);
-            if (direct_out)
-                store_elem<T>(a.out, orow * D + d, O * inv);
-            else
-                a.o_part[pi * D + d] = O * inv;
+        if (direct_out) {
+            *reinterpret_cast<uint2*>(static_cast<char*>(a.out) + (orow * D + d0) * 2) =
+                make_uint2(Mfma<T>::pack(O[0] * inv, O[1] * inv), Mfma<T>::pack(O[2] * inv, O[3] * inv));
+        } else {
+            *reinterpret_cast<float4*>(a.o_part + pi * D + d0) =
+                make_float4(O[0] * inv, O[1] * inv, O[2] * inv, O[3] * inv);
         }
-        if (!direct_out && col == 0) {
-            a.m_part[pi] = M * kLn2;
-            a.l_part[pi] = L;
-        }
+    }
+    if (!direct_out && grp == 0) {
+        a.m_part[pi] = M * kLn2;
+        a.l_part[pi] = L;
     }
 }
 
 // Long runs of queries (prefill chunks): a work-group owns 4 waves x RW row
 // tiles of 16 rows and walks every block of its partition up to the last
-// position any of its rows attends to.  Each 16-token K/V block is fetched
-// once per work-group (one 16-byte chunk per thread), staged in
-// double-buffered padded LDS tiles, and every wave reads the K operand and the
-// V operand once per block and reuses them for its RW row tiles; one barrier
-// per block.  Each wave owns its rows for the whole partition, so there is no
-// merge between waves.
+// position any of its rows attends to, two 16-token blocks per step.  Each
+// K/V block is fetched once per work-group (a 16-byte chunk per thread),
+// staged in double-buffered padded LDS tiles, and every wave reads the K and
+// V operands once per step and reuses them for its RW row tiles; one barrier
+// and one softmax update per step.  The output is accumulated transposed,
+// O^T = V^T P^T: the P operand is then the score tile as it leaves the first
+// MFMA and each lane's accumulator column is its own query, so rescaling and
+// normalizing need no lane exchange.  Each wave owns its rows for the whole
+// partition, so there is no merge between waves.
 template <Elem T, int D, int RW>
-__global__ __launch_bounds__(kThreads) void paged_multi_tiled_kernel(MultiArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void paged_multi_tiled_kernel(MultiArgs a) {
     constexpr int KK = D / 32;
     constexpr int NN = D / 16;
+    constexpr int KB = D <= 128 ? 2 : 1;            // 16-token blocks per softmax step
     constexpr int ROW = D * 2;
     constexpr int TILE = kRows * ROW;
     constexpr int LS = ROW + 16;                    // padded LDS row stride
@@ -339,8 +369,8 @@ __global__ __launch_bounds__(kThreads) void paged_multi_tiled_kernel(MultiArgs a
     constexpr int CPT = (CH + kThreads - 1) / kThreads;
     constexpr int WG_ROWS = kWaves * kRows * RW;
 
-    __shared__ __attribute__((aligned(16))) char s_k[2][kRows * LS];
-    __shared__ __attribute__((aligned(16))) char s_v[2][kRows * LS];
+    __shared__ __attribute__((aligned(16))) char s_k[2][KB][kRows * LS];
+    __shared__ __attribute__((aligned(16))) char s_v[2][KB][kRows * LS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -382,13 +412,17 @@ __global__ __launch_bounds__(kThreads) void paged_multi_tiled_kernel(MultiArgs a
     const int32_t* table = a.block_tables + (size_t)b * a.max_blocks_per_seq;
     const float c = a.scale_log2;
 
-    // this wave's row tiles
+    // this wave's row tiles; lane column `col` is one query row of each tile
     const int w_r0 = wg_r0 + wave * kRows * RW;
     bool row_ok[RW];
     int pos[RW];
+    int tile_pos_min[RW];   // the earliest position of a tile's rows (its first row)
+#pragma unroll
+    for (int rr = 0; rr < RW; ++rr)
+        tile_pos_min[rr] = n - qlen + min(w_r0 + rr * kRows, rows_total - 1) / g;
     uint4 qv[RW][KK];
     float m[RW], l[RW];
-    f32x4_t o[RW][NN];
+    f32x4_t o[RW][NN];  // O^T: o[rr][nn][i] = O[row col][d = 16 nn + 4 grp + i]
 #pragma unroll
     for (int rr = 0; rr < RW; ++rr) {
         const int R = w_r0 + rr * kRows + col;
@@ -410,134 +444,225 @@ __global__ __launch_bounds__(kThreads) void paged_multi_tiled_kernel(MultiArgs a
         for (int nn = 0; nn < NN; ++nn) o[rr][nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    auto gload = [&](int jb, uint4 (&kc)[CPT], uint4 (&vc)[CPT]) {
-        const int phys = table[jb];
-        const bool ok = phys >= 0 && (int64_t)phys < a.num_blocks;
-        const size_t tile = (size_t)(ok ? phys : 0) * a.num_kv_heads + kvh;
-        const int bytes = ok ? TILE : 0;
-        const __amdgpu_buffer_rsrc_t kr = rsrc(static_cast<const char*>(a.k_cache) + tile * TILE, bytes);
-        const __amdgpu_buffer_rsrc_t vr = rsrc(static_cast<const char*>(a.v_cache) + tile * TILE, bytes);
-#pragma unroll
-        for (int cc = 0; cc < CPT; ++cc) {
-            const int ch = cc * kThreads + tid;
-            const int off = ch < CH ? ch * 16 : TILE;     // past the tile: reads zeros
-            kc[cc] = ld16(kr, off);
-            vc[cc] = ld16(vr, off);
-        }
+    // KB blocks starting at jb0: one 16-byte chunk (or two) per thread per
+    // tile; a block past the run reads zeros from an empty buffer window
+    struct Stage {
+        uint4 k[KB][CPT], v[KB][CPT];
     };
-    auto lstore = [&](int buf, int jb, const uint4 (&kc)[CPT], const uint4 (&vc)[CPT]) {
+    auto block_id = [&](int jb) { return jb < blk_stop ? table[jb] : -1; };
+    auto gload = [&](const int (&ids)[KB], uint4 (&kc)[KB][CPT], uint4 (&vc)[KB][CPT]) {
 #pragma unroll
-        for (int cc = 0; cc < CPT; ++cc) {
-            const int ch = cc * kThreads + tid;
-            if (ch < CH) {
-                const int tok = ch / (ROW / 16), off = (ch % (ROW / 16)) * 16;
-                // rows past the partition are zeroed: weight 0 times NaN would not be 0
-                const bool keep = jb * kBlockSize + tok < t_end;
-                const uint4 kx = kc[cc], vx = vc[cc];
-                *reinterpret_cast<uint4*>(s_k[buf] + tok * LS + off) =
-                    make_uint4(keep ? kx.x : 0u, keep ? kx.y : 0u, keep ? kx.z : 0u,
-                               keep ? kx.w : 0u);
-                *reinterpret_cast<uint4*>(s_v[buf] + tok * LS + off) =
-                    make_uint4(keep ? vx.x : 0u, keep ? vx.y : 0u, keep ? vx.z : 0u,
-                               keep ? vx.w : 0u);
+        for (int kb = 0; kb < KB; ++kb) {
+            const int phys = ids[kb];
+            const bool ok = phys >= 0 && (int64_t)phys < a.num_blocks;
+            const size_t tile = (size_t)(ok ? phys : 0) * a.num_kv_heads + kvh;
+            const int bytes = ok ? TILE : 0;
+            const __amdgpu_buffer_rsrc_t kr =
+                rsrc(static_cast<const char*>(a.k_cache) + tile * TILE, bytes);
+            const __amdgpu_buffer_rsrc_t vr =
+                rsrc(static_cast<const char*>(a.v_cache) + tile * TILE, bytes);
+#pragma unroll
+            for (int cc = 0; cc < CPT; ++cc) {
+                const int ch = cc * kThreads + tid;
+                const int off = ch < CH ? ch * 16 : TILE;   // past the tile: reads zeros
+                kc[kb][cc] = ld16_cached(kr, off);
+                vc[kb][cc] = ld16_cached(vr, off);
             }
         }
     };
-    auto compute = [&](int buf, int jb) {
-        uint4 ka[KK];
+    auto lstore = [&](int buf, int jb0, const uint4 (&kc)[KB][CPT], const uint4 (&vc)[KB][CPT]) {
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-            ka[kk] = *reinterpret_cast<const uint4*>(s_k[buf] + col * LS + (kk * 32 + grp * 8) * 2);
-        uint2 vb[NN];
+        for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-        for (int nn = 0; nn < NN; ++nn) {
-            const char* base = s_v[buf] + (grp * 4) * LS + (nn * 16 + col) * 2;
-            const uint32_t v0 = *reinterpret_cast<const uint16_t*>(base);
-            const uint32_t v1 = *reinterpret_cast<const uint16_t*>(base + LS);
-            const uint32_t v2 = *reinterpret_cast<const uint16_t*>(base + 2 * LS);
-            const uint32_t v3 = *reinterpret_cast<const uint16_t*>(base + 3 * LS);
-            vb[nn] = make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
+            for (int cc = 0; cc < CPT; ++cc) {
+                const int ch = cc * kThreads + tid;
+                if (ch < CH) {
+                    const int tok = ch / (ROW / 16), off = (ch % (ROW / 16)) * 16;
+                    // rows past the partition are zeroed: weight 0 times NaN would not be 0
+                    const bool keep = (jb0 + kb) * kBlockSize + tok < t_end;
+                    const uint4 kx = kc[kb][cc], vx = vc[kb][cc];
+                    *reinterpret_cast<uint4*>(s_k[buf][kb] + tok * LS + off) =
+                        make_uint4(keep ? kx.x : 0u, keep ? kx.y : 0u, keep ? kx.z : 0u,
+                                   keep ? kx.w : 0u);
+                    *reinterpret_cast<uint4*>(s_v[buf][kb] + tok * LS + off) =
+                        make_uint4(keep ? vx.x : 0u, keep ? vx.y : 0u, keep ? vx.z : 0u,
+                                   keep ? vx.w : 0u);
+                }
+            }
         }
+    };
+    auto compute = [&](int buf, int jb0) {
+        // 1. scores of every row tile: S^T[token 4 grp + i][query col]
+        f32x4_t s[RW][KB];
+        {
+            uint4 ka[KB][KK];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk)
+                    ka[kb][kk] = *reinterpret_cast<const uint4*>(s_k[buf][kb] + col * LS +
+                                                                 (kk * 32 + grp * 8) * 2);
+#pragma unroll
+            for (int rr = 0; rr < RW; ++rr)
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    s[rr][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kk = 0; kk < KK; ++kk)
+                        s[rr][kb] = Mfma<T>::qk(ka[kb][kk], qv[rr][kk], s[rr][kb]);
+                }
+        }
+        // 2. online softmax over the step's KB * 16 tokens, per row tile.
+        //    Masking only where the step reaches the partition end or the
+        //    causal diagonal of some row of the tile (uniform test).
+        uint2 pb[RW][KB];
+        float alpha[RW];
+        bool grew[RW];
+        const int t_hi = (jb0 + KB) * kBlockSize;       // one past the step's last token
 #pragma unroll
         for (int rr = 0; rr < RW; ++rr) {
-            f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+            const bool full = t_hi <= t_end && t_hi <= tile_pos_min[rr] + 1;
+            float sv[KB][4], mx = kNegBig;
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) s = Mfma<T>::qk(ka[kk], qv[rr][kk], s);
-            float sv[4], mx = kNegBig;
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = jb * kBlockSize + grp * 4 + i;
-                const bool valid = row_ok[rr] && t < t_end && t <= pos[rr];
-                sv[i] = valid ? s[i] * c : -INFINITY;
-                mx = fmaxf(mx, sv[i]);
+                for (int i = 0; i < 4; ++i) {
+                    const int t = (jb0 + kb) * kBlockSize + grp * 4 + i;
+                    const bool valid = full || (row_ok[rr] && t < t_end && t <= pos[rr]);
+                    sv[kb][i] = valid ? s[rr][kb][i] * c : -INFINITY;
+                    mx = fmaxf(mx, sv[kb][i]);
+                }
+            // The running max m is shared by a query's 4 lanes; the exact
+            // cross-lane max is needed only when some score exceeds it.
+            grew[rr] = __builtin_amdgcn_ballot_w64(mx > m[rr]) != 0;
+            float mn = m[rr];
+            alpha[rr] = 1.f;
+            if (grew[rr]) {
+                mx = fmaxf(mx, __shfl_xor(mx, 16));
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                mn = fmaxf(m[rr], mx);
+                alpha[rr] = fast_exp2(m[rr] - mn);
+                m[rr] = mn;
             }
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mn = fmaxf(m[rr], mx);
-            const float alpha = fast_exp2(m[rr] - mn);
-            float p[4], ps = 0.f;
+            // l is this lane's share of the sum (its own tokens), rescaled
+            // with the shared max and reduced across the 4 lanes at the end
+            float ps = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                p[i] = fast_exp2(sv[i] - mn);
-                ps += p[i];
+            for (int kb = 0; kb < KB; ++kb) {
+                float p[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    p[i] = fast_exp2(sv[kb][i] - mn);
+                    ps += p[i];
+                }
+                pb[rr][kb] = make_uint2(Mfma<T>::pack(p[0], p[1]), Mfma<T>::pack(p[2], p[3]));
             }
-            ps += __shfl_xor(ps, 16);
-            ps += __shfl_xor(ps, 32);
-            l[rr] = fmaf(l[rr], alpha, ps);
-            m[rr] = mn;
-            float al[4];
+            l[rr] = fmaf(l[rr], alpha[rr], ps);
+        }
+        // 3. O^T = V^T P^T, the lane's accumulator columns being its own query.
+        //    Rescale only when some running max grew (otherwise alpha is 1).
 #pragma unroll
-            for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, grp * 4 + i);
-            const uint2 pa = make_uint2(Mfma<T>::pack(p[0], p[1]), Mfma<T>::pack(p[2], p[3]));
+        for (int rr = 0; rr < RW; ++rr)
+            if (grew[rr]) {
 #pragma unroll
-            for (int nn = 0; nn < NN; ++nn) {
+                for (int nn = 0; nn < NN; ++nn) o[rr][nn] *= alpha[rr];
+            }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o[rr][nn][i] *= al[i];
-                o[rr][nn] = Mfma<T>::pv(pa, vb[nn], o[rr][nn]);
+        for (int nn = 0; nn < NN; ++nn) {
+            // V^T operand: row d = 16 nn + col; tokens 4 grp .. 4 grp + 3 of each block
+            uint32_t vw[KB][2];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const char* base = s_v[buf][kb] + (grp * 4) * LS + (nn * 16 + col) * 2;
+                const uint32_t v0 = *reinterpret_cast<const uint16_t*>(base);
+                const uint32_t v1 = *reinterpret_cast<const uint16_t*>(base + LS);
+                const uint32_t v2 = *reinterpret_cast<const uint16_t*>(base + 2 * LS);
+                const uint32_t v3 = *reinterpret_cast<const uint16_t*>(base + 3 * LS);
+                vw[kb][0] = v0 | (v1 << 16);
+                vw[kb][1] = v2 | (v3 << 16);
+            }
+            if constexpr (KB == 2) {
+                // one 16x16x32 MFMA over both blocks: contraction index 8 grp + j
+                // is token 4 grp + j of block 0 (j < 4) or 4 grp + j - 4 of
+                // block 1, in the A (V^T) and the B (P^T) operand alike
+                const uint4 va = make_uint4(vw[0][0], vw[0][1], vw[1][0], vw[1][1]);
+#pragma unroll
+                for (int rr = 0; rr < RW; ++rr) {
+                    const uint4 pbb = make_uint4(pb[rr][0].x, pb[rr][0].y, pb[rr][1].x, pb[rr][1].y);
+                    o[rr][nn] = Mfma<T>::pv32(va, pbb, o[rr][nn]);
+                }
+            } else {
+                const uint2 va = make_uint2(vw[0][0], vw[0][1]);
+#pragma unroll
+                for (int rr = 0; rr < RW; ++rr) o[rr][nn] = Mfma<T>::pv(va, pb[rr][0], o[rr][nn]);
             }
         }
     };
 
-    if (blk_begin < blk_stop) {
-        uint4 kc[CPT], vc[CPT];
-        gload(blk_begin, kc, vc);
-        lstore(0, blk_begin, kc, vc);
+    // Steps of KB blocks; global loads run two steps ahead of the step being
+    // computed (register sets A and B alternate), LDS holds the current and
+    // the next step, block ids are fetched a step before their loads.
+    const int n_steps = (blk_stop - blk_begin + KB - 1) / KB;
+    if (n_steps > 0) {
+        Stage A, B;
+        int ids[KB];
+        auto fetch_ids = [&](int step) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) ids[kb] = block_id(blk_begin + step * KB + kb);
+        };
+        fetch_ids(0);
+        gload(ids, A.k, A.v);
+        fetch_ids(1);
+        gload(ids, B.k, B.v);
+        fetch_ids(2);
+        lstore(0, blk_begin, A.k, A.v);
         __syncthreads();
-        for (int jb = blk_begin; jb < blk_stop; ++jb) {
-            const int buf = (jb - blk_begin) & 1;
-            const bool more = jb + 1 < blk_stop;
-            if (more) gload(jb + 1, kc, vc);
-            compute(buf, jb);
-            if (more) lstore(buf ^ 1, jb + 1, kc, vc);
+        for (int st = 0; st < n_steps; st += 2) {
+            const int jb = blk_begin + st * KB;
+            gload(ids, A.k, A.v);                       // step st + 2
+            fetch_ids(st + 3);
+            compute(0, jb);
+            lstore(1, jb + KB, B.k, B.v);               // step st + 1 (zeros past the run)
             __syncthreads();
+            if (st + 1 < n_steps) {
+                gload(ids, B.k, B.v);                   // step st + 3
+                fetch_ids(st + 4);
+                compute(1, jb + KB);
+                lstore(0, jb + 2 * KB, A.k, A.v);       // step st + 2
+                __syncthreads();
+            }
         }
     }
 
-    // ---- epilogue: each wave writes its own rows ---------------------------
+    // ---- epilogue: each lane writes 4 consecutive channels of its own row --
 #pragma unroll
     for (int rr = 0; rr < RW; ++rr) {
+        l[rr] += __shfl_xor(l[rr], 16);
+        l[rr] += __shfl_xor(l[rr], 32);
+    }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int qr = grp * 4 + i;
-            const float lr = __shfl(l[rr], qr);
-            const float mr = __shfl(m[rr], qr);
-            const int R = w_r0 + rr * kRows + qr;
-            if (R >= rows_total) continue;
-            const float inv = lr > 0.f ? 1.f / lr : 0.f;
-            const size_t orow = (size_t)(q0 + R / g) * Hq + kvh * g + R % g;
-            const size_t pi = orow * NP + part;
+    for (int rr = 0; rr < RW; ++rr) {
+        const int R = w_r0 + rr * kRows + col;
+        if (R >= rows_total) continue;
+        const float inv = l[rr] > 0.f ? 1.f / l[rr] : 0.f;
+        const size_t orow = (size_t)(q0 + R / g) * Hq + kvh * g + R % g;
+        const size_t pi = orow * NP + part;
 #pragma unroll
-            for (int nn = 0; nn < NN; ++nn) {
-                const int d = nn * 16 + col;
-                if (direct_out)
-                    store_elem<T>(a.out, orow * D + d, o[rr][nn][i] * inv);
-                else
-                    a.o_part[pi * D + d] = o[rr][nn][i] * inv;
+        for (int nn = 0; nn < NN; ++nn) {
+            const int d0 = nn * 16 + grp * 4;
+            if (direct_out) {
+                const uint2 w = make_uint2(Mfma<T>::pack(o[rr][nn][0] * inv, o[rr][nn][1] * inv),
+                                           Mfma<T>::pack(o[rr][nn][2] * inv, o[rr][nn][3] * inv));
+                *reinterpret_cast<uint2*>(static_cast<char*>(a.out) + (orow * D + d0) * 2) = w;
+            } else {
+                float4 w = make_float4(o[rr][nn][0] * inv, o[rr][nn][1] * inv,
+                                       o[rr][nn][2] * inv, o[rr][nn][3] * inv);
+                *reinterpret_cast<float4*>(a.o_part + pi * D + d0) = w;
             }
-            if (!direct_out && col == 0) {
-                a.m_part[pi] = mr * kLn2;
-                a.l_part[pi] = lr;
-            }
+        }
+        if (!direct_out && grp == 0) {
+            a.m_part[pi] = m[rr] * kLn2;
+            a.l_part[pi] = l[rr];
         }
     }
 }
