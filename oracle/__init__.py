@@ -7,8 +7,10 @@ inputs.
 
 Arrays are numpy arrays on the host.  16-bit floats are passed as their raw
 bits (``uint16``) together with an explicit dtype name, because numpy has no
-bfloat16; FP8 e4m3 codes are ``uint8``.  Dtype names: ``"f32"``, ``"f16"``,
-``"bf16"``, ``"i8"``, ``"f8"``.
+bfloat16; FP8 e4m3 codes are ``uint8``; 4-bit codes ("u4") are packed two
+per ``uint8`` (a u4 cache of head dim D has D / 2 bytes per row, and its
+scale arrays hold (x_min, range) pairs: [..., 2] float32).  Dtype names:
+``"f32"``, ``"f16"``, ``"bf16"``, ``"i8"``, ``"f8"``, ``"u4"``.
 
 What the functions compute, and the pages they follow, is stated in the C
 source.  Parity status: every function here is pinned by the CPU tests in
@@ -27,8 +29,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3, "f8": 4}
-_NP_OF = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "i8": np.int8, "f8": np.uint8}
+DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3, "f8": 4, "u4": 5}
+_NP_OF = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "i8": np.int8, "f8": np.uint8,
+          "u4": np.uint8}
 
 GCC_CMD = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-ffp-contract=off",
            "-fno-fast-math", "-Wall", "-Wextra", _SRC, "-o", _LIB, "-lm"]
@@ -61,6 +64,7 @@ def lib():
         L.oracle_merge_partials.argtypes = [P, P, P, P, L64, I, I]
         L.oracle_quantize_rows.argtypes = [P, P, P, I, L64, I]
         L.oracle_quantize_rows_f8.argtypes = [P, P, P, I, L64, I]
+        L.oracle_quantize_rows_u4.argtypes = [P, P, P, I, L64, I]
         L.oracle_f8_to_f64.argtypes = [ctypes.c_uint8]
         L.oracle_f8_to_f64.restype = ctypes.c_double
         L.oracle_f8_from_f32.argtypes = [ctypes.c_float]
@@ -118,8 +122,9 @@ def paged_decode(q, q_dtype, k_cache, v_cache, cache_dtype, block_tables, contex
     vs = _check(v_scale, np.float32, "v_scale")
     B, Hq, D = q.shape
     NB, Hkv, bs, D2 = k_cache.shape
-    assert D2 == D and bs == block_size and v_cache.shape == k_cache.shape
-    if cache_dtype in ("i8", "f8"):
+    assert D2 == (D // 2 if cache_dtype == "u4" else D)
+    assert bs == block_size and v_cache.shape == k_cache.shape
+    if cache_dtype in ("i8", "f8", "u4"):
         assert ks is not None and vs is not None
     out = np.full((B, Hq, D), np.nan, dtype=np.float64)
     r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
@@ -209,6 +214,21 @@ def quantize_rows(x, dtype, target="i8"):
     fn = lib().oracle_quantize_rows if target == "i8" else lib().oracle_quantize_rows_f8
     fn(_ptr(codes), _ptr(scales), _ptr(x), DTYPES[dtype], rows, D)
     return codes, scales
+
+
+def quantize_rows_u4(x, dtype):
+    """4-bit rows by the linear b-bit formula (b = 4) over each row's min and
+    max.  Returns (codes uint8 [..., D/2], meta float32 [..., 2] = (x_min,
+    range))."""
+    x = _check(x, dtype, "x")
+    D = x.shape[-1]
+    rows = int(np.prod(x.shape[:-1]))
+    codes = np.empty(x.shape[:-1] + (D // 2,), np.uint8)
+    meta = np.empty(x.shape[:-1] + (2,), np.float32)
+    rc = lib().oracle_quantize_rows_u4(_ptr(codes), _ptr(meta), _ptr(x), DTYPES[dtype], rows, D)
+    if rc != 0:
+        raise RuntimeError(f"oracle_quantize_rows_u4 failed with {rc}")
+    return codes, meta
 
 
 def f8_to_f64(code: int) -> float:

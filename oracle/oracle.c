@@ -34,6 +34,9 @@
  *
  * Readings where the pages are silent (each one is listed with its reason in
  * the design notes of the repository):
+ *  - 4-bit caches (caojiahao2 section 2.3 names INT4 KV quantization) take
+ *    the linear b-bit formula of the lazyllm page, section 3.2, with b = 4
+ *    over each (slot, kv head) row's own minimum and maximum;
  *  - one INT8 scale per (slot, kv head), separately for K and V; FP8 e4m3
  *    caches take the same per-row scale with 448 (the format's largest
  *    value) in place of 127;
@@ -59,7 +62,9 @@
  * floating-point format e4m3 (OCP "E4M3FN": sign, 4 exponent bits with bias
  * 7, 3 mantissa bits, no infinities, the all-ones exponent-and-mantissa
  * pattern is NaN, largest finite value 448). */
-enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_I8 = 3, OR_F8 = 4 };
+enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_I8 = 3, OR_F8 = 4, OR_U4 = 5 };
+/* OR_U4: 4-bit codes 0..15, two per byte, element 2i in the low nibble of
+ * byte i; each (slot, kv head) row carries two fp32 values (x_min, range). */
 
 /* Scaled 8-bit caches: one fp32 scale per (slot, kv head). */
 static int scaled(int dtype) { return dtype == OR_I8 || dtype == OR_F8; }
@@ -128,6 +133,10 @@ static double elem(const void* base, size_t i, int dtype) {
     case OR_BF16: return oracle_bf16_to_f64(((const uint16_t*)base)[i]);
     case OR_I8: return (double)((const int8_t*)base)[i];
     case OR_F8: return oracle_f8_to_f64(((const uint8_t*)base)[i]);
+    case OR_U4: {
+        const uint8_t byte = ((const uint8_t*)base)[i / 2];
+        return (double)((i % 2) ? (byte >> 4) : (byte & 15));
+    }
     default: return NAN;
     }
 }
@@ -171,6 +180,17 @@ static int gather(const problem* P, int b, int kvh, int t0, int t1, double* K, d
         long base = token_row(P, b, kvh, t, &si);
         if (base < 0) return -1;
         double ks = 1.0, vs = 1.0;
+        if (P->cache_dtype == OR_U4) {
+            /* dequantization of the linear b-bit formula (b = 4):
+             * x = x_min + code / (2^b - 1) * (x_max - x_min) */
+            const double kmin = P->k_scale[2 * si], krange = P->k_scale[2 * si + 1];
+            const double vmin = P->v_scale[2 * si], vrange = P->v_scale[2 * si + 1];
+            for (int d = 0; d < P->D; ++d) {
+                K[(size_t)(t - t0) * P->D + d] = kmin + elem(P->k_cache, base + d, OR_U4) / 15.0 * krange;
+                V[(size_t)(t - t0) * P->D + d] = vmin + elem(P->v_cache, base + d, OR_U4) / 15.0 * vrange;
+            }
+            continue;
+        }
         if (scaled(P->cache_dtype)) {
             ks = (double)P->k_scale[si];
             vs = (double)P->v_scale[si];
@@ -467,6 +487,36 @@ static void quantize_row_f8(uint8_t* codes, float* scale_out, const void* x, siz
     *scale_out = s;
 }
 
+/* 4-bit row by the linear b-bit formula with b = 4, over the row's own
+ * minimum and maximum: code = round((x - x_min) / (x_max - x_min) * 15),
+ * evaluated left to right in single precision (x - x_min, then the division,
+ * then the product), rounded half to even and clamped to [0, 15].
+ * meta = (x_min, x_max - x_min); a constant row gives range 0 and codes 0.
+ * codes: D / 2 bytes, element 2i in the low nibble of byte i. */
+static void quantize_row_u4(uint8_t* codes, float* meta, const void* x, size_t base, int D,
+                            int dtype) {
+    float lo = elem_f32(x, base, dtype), hi = lo;
+    for (int d = 1; d < D; ++d) {
+        float v = elem_f32(x, base + d, dtype);
+        if (v < lo) lo = v;
+        if (v > hi) hi = v;
+    }
+    volatile float range = hi - lo;
+    meta[0] = lo;
+    meta[1] = range;
+    for (int d = 0; d < D; d += 2) codes[d / 2] = 0;
+    if (range == 0.0f) return;
+    for (int d = 0; d < D; ++d) {
+        volatile float diff = elem_f32(x, base + d, dtype) - lo;
+        volatile float frac = diff / range;
+        volatile float r = frac * 15.0f;
+        float c = nearbyintf(r);
+        if (c < 0.0f) c = 0.0f;
+        if (c > 15.0f) c = 15.0f;
+        codes[d / 2] |= (uint8_t)((int)c << (4 * (d % 2)));
+    }
+}
+
 static void quantize_row(void* codes, float* scale_out, const void* x, size_t base, int D,
                          int dtype, int cache_dtype) {
     if (cache_dtype == OR_F8)
@@ -479,6 +529,15 @@ static void quantize_row(void* codes, float* scale_out, const void* x, size_t ba
 int oracle_quantize_rows(int8_t* codes, float* scales, const void* x, int dtype, long rows, int D) {
     for (long r = 0; r < rows; ++r)
         quantize_row_i8(codes + (size_t)r * D, scales + r, x, (size_t)r * D, D, dtype);
+    return 0;
+}
+
+/* 4-bit rows: codes uint8 [rows][D / 2], meta float [rows][2] = (x_min, range). */
+int oracle_quantize_rows_u4(uint8_t* codes, float* meta, const void* x, int dtype, long rows,
+                            int D) {
+    if (D % 2) return -3;
+    for (long r = 0; r < rows; ++r)
+        quantize_row_u4(codes + (size_t)r * (D / 2), meta + 2 * r, x, (size_t)r * D, D, dtype);
     return 0;
 }
 
@@ -504,8 +563,8 @@ int oracle_kv_cache_write(const void* k, const void* v, void* k_cache, void* v_c
                           float* k_scale, float* v_scale, const int64_t* slot_mapping, long T,
                           int Hkv, int D, int block_size, int num_blocks, int src_dtype,
                           int cache_dtype) {
-    if (cache_dtype != src_dtype && !scaled(cache_dtype)) return -3;
-    if (scaled(src_dtype)) return -3;
+    if (cache_dtype != src_dtype && !scaled(cache_dtype) && cache_dtype != OR_U4) return -3;
+    if (scaled(src_dtype) || src_dtype == OR_U4) return -3;
     size_t es = elem_size(cache_dtype);
     for (long i = 0; i < T; ++i) {
         int64_t slot = slot_mapping[i];
@@ -515,7 +574,12 @@ int oracle_kv_cache_write(const void* k, const void* v, void* k_cache, void* v_c
         for (int h = 0; h < Hkv; ++h) {
             size_t src = ((size_t)i * Hkv + h) * D;
             size_t dst_row = ((size_t)blk * Hkv + h) * block_size + (size_t)off;
-            if (scaled(cache_dtype)) {
+            if (cache_dtype == OR_U4) {
+                quantize_row_u4((uint8_t*)k_cache + dst_row * (D / 2), k_scale + 2 * dst_row, k,
+                                src, D, src_dtype);
+                quantize_row_u4((uint8_t*)v_cache + dst_row * (D / 2), v_scale + 2 * dst_row, v,
+                                src, D, src_dtype);
+            } else if (scaled(cache_dtype)) {
                 quantize_row((int8_t*)k_cache + dst_row * D, k_scale + dst_row, k, src, D,
                              src_dtype, cache_dtype);
                 quantize_row((int8_t*)v_cache + dst_row * D, v_scale + dst_row, v, src, D,
