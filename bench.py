@@ -35,6 +35,7 @@ WORKLOAD_NAMES = {
     "long": "long-32k-fp16-split-decode",
     "int8": "llama7b-mha-int8kv-paged-decode",
     "fp8": "llama7b-mha-fp8e4m3kv-paged-decode",
+    "int4": "llama7b-mha-int4kv-paged-decode",
     "window": "llama7b-mha-fp16-sliding-window-4096-decode",
     "verify": "llama7b-mha-fp16-speculative-verify-8-queries",
     "prefill": "llama7b-mha-fp16-chunked-prefill-512",
@@ -146,13 +147,14 @@ def main():
                 bt[b, :(int(n) - window) // W.BLOCK_SIZE] = -1
         block_tables = torch.from_numpy(bt).cuda()
         lens = np.minimum(lens, window)
-    e_kv = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "f8": 1}[cfg["cache"]]
+    e_kv = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "f8": 1, "u4": 0.5}[cfg["cache"]]
     e_q = {"f32": 4, "f16": 2, "bf16": 2}[cfg["dtype"]]
-    int8 = cfg["cache"] in W.SCALED     # 1-byte codes + a 4-byte scale per row
-    dec_bytes = W.algorithmic_bytes(lens, batch.Hq, batch.Hkv, batch.D, e_kv, e_q, int8)
+    int8 = cfg["cache"] in W.SCALED     # quantized codes + per-row scale (or min, range)
+    meta = {"i8": 4, "f8": 4, "u4": 8}.get(cfg["cache"], 0)
+    dec_bytes = W.algorithmic_bytes(lens, batch.Hq, batch.Hkv, batch.D, e_kv, e_q, int8, meta)
     n_new = int((batch.slot_new >= 0).sum())
-    # the new rows written into the cache (codes + scales for INT8)
-    store_bytes = n_new * batch.Hkv * 2 * (batch.D * e_kv + (4 if int8 else 0))
+    # the new rows written into the cache (codes + scales for quantized caches)
+    store_bytes = int(n_new * batch.Hkv * 2 * (batch.D * e_kv + meta))
     if args.step == "fused":
         # the new token's K/V are read from the input instead of the cache: the
         # decode byte count already holds them; add the stores
@@ -668,7 +670,7 @@ def run_cpu_baseline(batch, cfg_name, target_s, e_kv, e_q, int8, window=0):
             return t.numpy()
 
         dt = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16",
-              torch.int8: "i8", torch.float8_e4m3fn: "f8"}
+              torch.int8: "i8", torch.float8_e4m3fn: "f8", torch.uint8: "u4"}
         kw = {}
         if int8:
             kw = dict(k_scale=h(batch.k_scale[idx]), v_scale=h(batch.v_scale[idx]))
@@ -692,7 +694,8 @@ def run_cpu_baseline(batch, cfg_name, target_s, e_kv, e_q, int8, window=0):
     oracle.paged_decode(**v)
     t_s = time.perf_counter() - t
     sub = att[:n_seq]
-    alg = W.algorithmic_bytes(sub, batch.Hq, batch.Hkv, batch.D, e_kv, e_q, int8)
+    meta = 8 if e_kv == 0.5 else (4 if int8 else 0)
+    alg = W.algorithmic_bytes(sub, batch.Hq, batch.Hkv, batch.D, e_kv, e_q, int8, meta)
     return {
         "value": round(alg / t_s / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
         "sample": f"first {n_seq} of {batch.B} sequences (all {batch.Hq} q heads, "

@@ -27,6 +27,10 @@
  *    section names (and the juejin page lists among serving-engine features):
  *    the same per-(slot, kv head) scale with 448, the format's largest value,
  *    in place of 127; code = e4m3 nearest to x / s.
+ *  - Optional 4-bit KV cache (INT4 KV quantization, caojiahao2 section 2.3)
+ *    by the linear b-bit formula of lazyllm section 3.2 with b = 4 over each
+ *    (slot, kv head) row: code = round((x - x_min) / (x_max - x_min) * 15),
+ *    value = x_min + code / 15 * (x_max - x_min).
  *
  * Tensor layouts (row-major, all device memory unless stated):
  *    q, out          [num_seqs][num_q_heads][head_dim]             q_dtype
@@ -54,8 +58,8 @@
  *    are unspecified, but no access leaves the buffers described here.
  *  - Supported: block_size 16; head_dim 64, 128 or 256; (q_dtype,
  *    cache_dtype) in {(F32,F32), (F16,F16), (BF16,BF16), (F16,I8),
- *    (BF16,I8), (F16,F8_E4M3), (BF16,F8_E4M3)}; num_q_heads a multiple of
- *    num_kv_heads.
+ *    (BF16,I8), (F16,F8_E4M3), (BF16,F8_E4M3), (F16,U4), (BF16,U4)} (U4:
+ *    head_dim 128 or 256); num_q_heads a multiple of num_kv_heads.
  */
 #ifndef PKV_H
 #define PKV_H
@@ -83,8 +87,19 @@ typedef enum {
 } pkv_status;
 
 /* PKV_F8_E4M3: 8-bit floating point e4m3 (OCP "E4M3FN": bias 7, 3 mantissa
- * bits, no infinities, largest finite value 448), one byte per element. */
-typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_I8 = 3, PKV_F8_E4M3 = 4 } pkv_dtype;
+ * bits, no infinities, largest finite value 448), one byte per element.
+ * PKV_U4: 4-bit codes 0..15, two per byte (element 2i in the low nibble of
+ * byte i): a cache row of head_dim elements takes head_dim / 2 bytes, and the
+ * scale arrays hold two floats per (slot, kv head), (x_min, x_max - x_min):
+ * [num_blocks][num_kv_heads][block_size][2]. */
+typedef enum {
+    PKV_F32 = 0,
+    PKV_F16 = 1,
+    PKV_BF16 = 2,
+    PKV_I8 = 3,
+    PKV_F8_E4M3 = 4,
+    PKV_U4 = 5
+} pkv_dtype;
 
 /*
  * Slot-mapped cache append ("when a new token is generated only its keys and
@@ -95,16 +110,18 @@ typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_I8 = 3, PKV_F8_E4M3 =
  *  k, v          [num_tokens][num_kv_heads][head_dim], src_dtype (F32|F16|BF16)
  *  k_cache/v_cache  pool (see layout above), cache_dtype == src_dtype, I8 or
  *                F8_E4M3
- *  k_scale/v_scale  required iff cache_dtype is I8 or F8_E4M3, else ignored
- *                (may be NULL)
+ *  k_scale/v_scale  required iff cache_dtype is I8, F8_E4M3 or U4, else
+ *                ignored (may be NULL)
  *  slot_mapping  token i goes to block slot/16, offset slot%16 for every kv
  *                head; slot < 0 skips the token.  Slots must be distinct.
  *
  * INT8 rows: amax = max_d |x_d|; s = amax / 127 (IEEE single division);
  * code_d = clamp(round_half_even(x_d / s), -127, 127); amax == 0 stores s = 0
  * and zero codes.  FP8 rows: s = amax / 448; code_d = the e4m3 value nearest
- * to clamp(x_d / s, -448, 448), ties to even.  Bytes of other slots are not
- * touched.
+ * to clamp(x_d / s, -448, 448), ties to even.  U4 rows: range = max - min;
+ * code_d = clamp(round_half_even((x_d - min) / range * 15), 0, 15), each
+ * operation in IEEE single precision left to right; (min, range) stored;
+ * range == 0 stores zero codes.  Bytes of other slots are not touched.
  */
 pkv_status pkv_kv_cache_write(const void* k, const void* v, void* k_cache, void* v_cache,
                               float* k_scale, float* v_scale, const int64_t* slot_mapping,
@@ -141,7 +158,7 @@ size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads
  *
  *  out               [num_seqs][num_q_heads][head_dim], q_dtype, written
  *  q                 [num_seqs][num_q_heads][head_dim], q_dtype
- *  k_scale, v_scale  required iff cache_dtype is I8 or F8_E4M3
+ *  k_scale, v_scale  required iff cache_dtype is I8, F8_E4M3 or U4
  *  scale             the softmax scale, normally 1/sqrt(head_dim)
  *  partition_size    0 (library choice) or a positive multiple of 16
  *  workspace         >= pkv_decode_workspace_size(...) bytes, 256-byte aligned
@@ -387,7 +404,7 @@ int64_t pkv_bm_sequence_length(const pkv_block_manager* bm, int64_t seq_id);
  * Copy whole blocks inside the pool, for the copy pairs of pkv_bm_append:
  * for every pair (src, dst) of copy_pairs ([num_pairs][2] int32, device
  * memory), the num_kv_heads tiles of block src in k_cache and v_cache (and
- * their scale rows when cache_dtype is I8 or F8_E4M3) are copied to block dst.  Pairs
+ * their scale rows when cache_dtype is I8, F8_E4M3 or U4) are copied to block dst.  Pairs
  * with an id outside [0, num_blocks) or src == dst are skipped.  A block may
  * not be the destination of one pair and the source or destination of
  * another in the same call.  Asynchronous on `stream` like the calls above.

@@ -27,11 +27,30 @@ BLOCK_SIZE = 16
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
-F32, F16, BF16, I8, F8_E4M3 = 0, 1, 2, 3, 4
+F32, F16, BF16, I8, F8_E4M3, U4 = 0, 1, 2, 3, 4, 5
+# a 4-bit cache is a torch.uint8 tensor [NB][Hkv][16][D/2] (two codes per
+# byte) with scale arrays [NB][Hkv][16][2] float32 holding (x_min, range)
 _DTYPE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16, torch.int8: I8,
-          torch.float8_e4m3fn: F8_E4M3}
+          torch.float8_e4m3fn: F8_E4M3, torch.uint8: U4}
 # caches of 1-byte codes with one float32 scale per (slot, kv head)
 SCALED_DTYPES = (torch.int8, torch.float8_e4m3fn)
+
+
+def _head_dim(cache: torch.Tensor) -> int:
+    return cache.shape[3] * 2 if cache.dtype == torch.uint8 else cache.shape[3]
+
+
+def _check_scales(k_cache, k_scale, v_scale, NB, Hkv, bs):
+    if k_cache.dtype in SCALED_DTYPES:
+        _dev(k_scale, "k_scale", dtype=torch.float32, ndim=3)
+        _dev(v_scale, "v_scale", dtype=torch.float32, ndim=3)
+        if tuple(k_scale.shape) != (NB, Hkv, bs) or v_scale.shape != k_scale.shape:
+            raise ValueError("scale arrays must be [num_blocks][num_kv_heads][16]")
+    elif k_cache.dtype == torch.uint8:
+        _dev(k_scale, "k_scale", dtype=torch.float32, ndim=4)
+        _dev(v_scale, "v_scale", dtype=torch.float32, ndim=4)
+        if tuple(k_scale.shape) != (NB, Hkv, bs, 2) or v_scale.shape != k_scale.shape:
+            raise ValueError("4-bit scale arrays must be [num_blocks][num_kv_heads][16][2]")
 
 
 class PkvError(RuntimeError):
@@ -187,16 +206,13 @@ def kv_cache_write(k, v, k_cache, v_cache, slot_mapping, k_scale=None, v_scale=N
     _dev(v_cache, "v_cache", dtype=k_cache.dtype, ndim=4)
     _dev(slot_mapping, "slot_mapping", dtype=torch.int64, ndim=1)
     T, Hkv, D = k.shape
-    NB, Hkv2, bs, D2 = k_cache.shape
+    NB, Hkv2, bs, _ = k_cache.shape
+    D2 = _head_dim(k_cache)
     if v.shape != k.shape or v_cache.shape != k_cache.shape or (Hkv2, D2) != (Hkv, D):
         raise ValueError("k/v and cache shapes disagree")
     if slot_mapping.shape[0] != T:
         raise ValueError("slot_mapping must have one entry per token")
-    if k_cache.dtype in SCALED_DTYPES:
-        _dev(k_scale, "k_scale", dtype=torch.float32, ndim=3)
-        _dev(v_scale, "v_scale", dtype=torch.float32, ndim=3)
-        if tuple(k_scale.shape) != (NB, Hkv, bs) or v_scale.shape != k_scale.shape:
-            raise ValueError("scale arrays must be [num_blocks][num_kv_heads][16]")
+    _check_scales(k_cache, k_scale, v_scale, NB, Hkv, bs)
     rc = _load().pkv_kv_cache_write(_ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
                                     _ptr(v_scale), _ptr(slot_mapping), T, Hkv, D, bs, NB,
                                     _code(k.dtype, "k"), _code(k_cache.dtype, "k_cache"),
@@ -211,14 +227,12 @@ def _decode_common(q, k_cache, v_cache, block_tables, context_lens, k_scale, v_s
     _dev(block_tables, "block_tables", dtype=torch.int32, ndim=2)
     _dev(context_lens, "context_lens", dtype=torch.int32, ndim=1)
     B, Hq, D = q.shape
-    NB, Hkv, bs, D2 = k_cache.shape
-    if D2 != D or v_cache.shape != k_cache.shape:
+    NB, Hkv, bs, _ = k_cache.shape
+    if _head_dim(k_cache) != D or v_cache.shape != k_cache.shape:
         raise ValueError("q / cache shapes disagree")
     if block_tables.shape[0] != B or context_lens.shape[0] != B:
         raise ValueError("block_tables and context_lens need one row per sequence")
-    if k_cache.dtype in SCALED_DTYPES:
-        _dev(k_scale, "k_scale", dtype=torch.float32, ndim=3)
-        _dev(v_scale, "v_scale", dtype=torch.float32, ndim=3)
+    _check_scales(k_cache, k_scale, v_scale, NB, Hkv, bs)
     return B, Hq, D, NB, Hkv, bs
 
 
@@ -412,14 +426,11 @@ def copy_blocks(k_cache, v_cache, copy_pairs, k_scale=None, v_scale=None):
     _dev(copy_pairs, "copy_pairs", dtype=torch.int32, ndim=2)
     if copy_pairs.shape[1] != 2:
         raise ValueError("copy_pairs must be [n][2]")
-    NB, Hkv, bs, D = k_cache.shape
+    NB, Hkv, bs, _ = k_cache.shape
+    D = _head_dim(k_cache)
     if v_cache.shape != k_cache.shape:
         raise ValueError("k_cache and v_cache shapes disagree")
-    if k_cache.dtype in SCALED_DTYPES:
-        _dev(k_scale, "k_scale", dtype=torch.float32, ndim=3)
-        _dev(v_scale, "v_scale", dtype=torch.float32, ndim=3)
-        if tuple(k_scale.shape) != (NB, Hkv, bs) or v_scale.shape != k_scale.shape:
-            raise ValueError("scale arrays must be [num_blocks][num_kv_heads][16]")
+    _check_scales(k_cache, k_scale, v_scale, NB, Hkv, bs)
     rc = _load().pkv_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
                                  _ptr(copy_pairs), copy_pairs.shape[0], Hkv, D, bs, NB,
                                  _code(k_cache.dtype, "k_cache"), _stream(k_cache))

@@ -1,4 +1,4 @@
-// Slot-mapped cache append with optional INT8 / FP8 quantize-on-write.
+// Slot-mapped cache append with optional INT8 / FP8 / 4-bit quantize-on-write.
 //
 // Each new token's K and V rows are written into the pool at the slot the
 // block manager assigned (block = slot / 16, offset = slot % 16), for every kv
@@ -84,6 +84,36 @@ __device__ __forceinline__ uint2 quantize8(const float (&x)[8], float& scale_out
     return make_uint2(packed[0], packed[1]);
 }
 
+// 4-bit codes of 8 elements of a row (spread over LPR lanes) by the linear
+// b-bit formula with b = 4 over the row's min and max: code = rne((x - min)
+// / range * 15) clamped to [0, 15], range = max - min, each step in IEEE
+// single precision; element 2i goes to the low nibble of byte i.
+template <int LPR>
+__device__ __forceinline__ uint32_t quantize8_u4(const float (&x)[8], float& lo_out,
+                                                 float& range_out) {
+    float lo = x[0], hi = x[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) {
+        lo = fminf(lo, x[i]);
+        hi = fmaxf(hi, x[i]);
+    }
+    lo = -group_max<LPR>(-lo);
+    hi = group_max<LPR>(hi);
+    const float range = hi - lo;
+    uint32_t w = 0u;
+    if (range != 0.f) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float r = __builtin_rintf((x[i] - lo) / range * 15.0f);
+            r = fminf(fmaxf(r, 0.0f), 15.0f);
+            w |= (uint32_t)r << (4 * i);
+        }
+    }
+    lo_out = lo;
+    range_out = range;
+    return w;
+}
+
 template <Elem SE, Elem CE, int D>
 __global__ __launch_bounds__(kThreads) void kv_cache_write_kernel(CacheWriteArgs a) {
     constexpr int LPR = D / 8;  // lanes per row
@@ -101,7 +131,22 @@ __global__ __launch_bounds__(kThreads) void kv_cache_write_kernel(CacheWriteArgs
     const size_t dst_row = ((size_t)blk * a.num_kv_heads + h) * kBlockSize + (size_t)off;
     const size_t dst = dst_row * D + (size_t)j * 8;
 
-    if constexpr (is_scaled(CE)) {
+    if constexpr (CE == Elem::U4) {
+        Src8<SE> k, v;
+        k.load(a.k, src);
+        v.load(a.v, src);
+        k.widen();
+        v.widen();
+        float klo, kr, vlo, vr;
+        const uint32_t kc = quantize8_u4<LPR>(k.x, klo, kr);
+        const uint32_t vc = quantize8_u4<LPR>(v.x, vlo, vr);
+        *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(a.k_cache) + dst / 2) = kc;
+        *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(a.v_cache) + dst / 2) = vc;
+        if (j == 0) {
+            *reinterpret_cast<float2*>(a.k_scale + 2 * dst_row) = make_float2(klo, kr);
+            *reinterpret_cast<float2*>(a.v_scale + 2 * dst_row) = make_float2(vlo, vr);
+        }
+    } else if constexpr (is_scaled(CE)) {
         Src8<SE> k, v;
         k.load(a.k, src);
         v.load(a.v, src);
@@ -173,6 +218,14 @@ hipError_t launch_kv_cache_write(const CacheWriteArgs& a, int src_dtype, int cac
         case Elem::F32: return launch_d<Elem::F32, Elem::I8>(a, head_dim, stream);
         case Elem::F16: return launch_d<Elem::F16, Elem::I8>(a, head_dim, stream);
         case Elem::BF16: return launch_d<Elem::BF16, Elem::I8>(a, head_dim, stream);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    if (ce == Elem::U4) {
+        switch (se) {
+        case Elem::F32: return launch_d<Elem::F32, Elem::U4>(a, head_dim, stream);
+        case Elem::F16: return launch_d<Elem::F16, Elem::U4>(a, head_dim, stream);
+        case Elem::BF16: return launch_d<Elem::BF16, Elem::U4>(a, head_dim, stream);
         default: return hipErrorInvalidValue;
         }
     }

@@ -45,10 +45,10 @@ constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kNegBig = -3.0e38f;  // finite stand-in for -inf in running maxima
 
 template <Elem CE, int D> struct Geom {
-    static constexpr int EB = ElemInfo<CE>::bytes;
-    static constexpr int ROW = D * EB;           // bytes per token row
+    static constexpr int BITS = ElemInfo<CE>::bits;
+    static constexpr int ROW = D * BITS / 8;     // bytes per token row
     static constexpr int L = ROW / 16;           // lanes per token row
-    static constexpr int E = 16 / EB;            // cache elements per lane
+    static constexpr int E = 128 / BITS;         // cache elements per lane (16 bytes)
     static constexpr int R = kWave / L;          // token rows per wave load
     static constexpr int LPB = kBlockSize / R;   // wave loads per 16-token block
     static constexpr int U = LPB < 4 ? LPB : 4;  // wave loads per step
@@ -145,6 +145,46 @@ template <Elem QE, Elem CE> struct QSliceScaled {
     }
 };
 template <Elem QE> struct QSlice<QE, Elem::I8, 16> : QSliceScaled<QE, Elem::I8> {};
+
+// 4-bit cache: q widened to fp32 once, with the sum of its slice (the
+// x_min term of the dequantized dot); the dot runs on the raw codes:
+//   q . (x_min + c * step) = x_min * sum(q) + step * (q . c)
+template <Elem QE> struct QSlice<QE, Elem::U4, 32> {
+    float v[32];
+    float sum;
+    __device__ __forceinline__ void load(const void* q, size_t elem_off) {
+        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) + elem_off);
+        sum = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint4 a = p[c];
+            const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[8 * c + 2 * i] = QE == Elem::F16 ? lo_h(w[i]) : lo_bf(w[i]);
+                v[8 * c + 2 * i + 1] = QE == Elem::F16 ? hi_h(w[i]) : hi_bf(w[i]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 32; ++i) sum += v[i];
+    }
+    // sum_e q_e * code_e over the 32 codes of a 16-byte chunk
+    __device__ __forceinline__ float dot(const uint4& k) const {
+        const uint32_t w[4] = {k.x, k.y, k.z, k.w};
+        float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t lo = w[i] & 0x0F0F0F0Fu;          // elements 8i, 8i+2, 8i+4, 8i+6
+            const uint32_t hi = (w[i] >> 4) & 0x0F0F0F0Fu;   // elements 8i+1, 8i+3, ...
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                d0 = fmaf(v[8 * i + 2 * j], (float)((lo >> (8 * j)) & 0xffu), d0);
+                d1 = fmaf(v[8 * i + 2 * j + 1], (float)((hi >> (8 * j)) & 0xffu), d1);
+            }
+        }
+        return d0 + d1;
+    }
+};
 template <Elem QE> struct QSlice<QE, Elem::F8, 16> : QSliceScaled<QE, Elem::F8> {};
 
 // Codes of one row of the new token: this lane's 16 elements, whose row spans
@@ -185,6 +225,36 @@ __device__ __forceinline__ uint4 quantize16(const float (&x)[16], float& scale_o
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// 4-bit codes of one row of the new token: this lane's 32 elements, whose
+// row spans L lanes.  Same arithmetic as the quantizing cache write: the
+// row's exact min and max, range = max - min, code = rne((x - min) / range
+// * 15) clamped to [0, 15], each step in IEEE single precision.
+template <int L>
+__device__ __forceinline__ uint4 quantize32_u4(const float (&x)[32], float& lo_out,
+                                               float& range_out) {
+    float lo = x[0], hi = x[0];
+#pragma unroll
+    for (int i = 1; i < 32; ++i) {
+        lo = fminf(lo, x[i]);
+        hi = fmaxf(hi, x[i]);
+    }
+    lo = -group_max<L>(-lo);
+    hi = group_max<L>(hi);
+    const float range = hi - lo;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (range != 0.f) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            float r = __builtin_rintf((x[i] - lo) / range * 15.0f);
+            r = fminf(fmaxf(r, 0.0f), 15.0f);
+            w[i / 8] |= (uint32_t)r << (4 * (i % 8));
+        }
+    }
+    lo_out = lo;
+    range_out = range;
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // widen one 16-byte V chunk to E floats
 template <Elem CE, int E> __device__ __forceinline__ void widen(const uint4& c, float (&x)[E]) {
     const uint32_t w[4] = {c.x, c.y, c.z, c.w};
@@ -200,6 +270,9 @@ template <Elem CE, int E> __device__ __forceinline__ void widen(const uint4& c, 
             x[2 * i + 1] = hi_bf(w[i]);
         } else if constexpr (CE == Elem::F8) {
             f8x4_to_f32(w[i], x[4 * i + 0], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+        } else if constexpr (CE == Elem::U4) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x[8 * i + j] = (float)((w[i] >> (4 * j)) & 15u);
         } else {
             x[4 * i + 0] = i8_at(w[i], 0);
             x[4 * i + 1] = i8_at(w[i], 1);
@@ -239,7 +312,8 @@ __device__ __forceinline__ float ld_f32(__amdgpu_buffer_rsrc_t r, int offset) {
 template <Elem CE, int D> struct BlockRegs {
     using G = Geom<CE, D>;
     uint4 k[G::STEPS][G::U], v[G::STEPS][G::U];
-    float ks[G::STEPS][G::U], vs[G::STEPS][G::U];
+    float ks[G::STEPS][G::U], vs[G::STEPS][G::U];  // INT8 / FP8 scale, 4-bit range
+    float kz[G::STEPS][G::U], vz[G::STEPS][G::U];  // 4-bit x_min
     int jb;   // logical block index in the sequence
     bool ok;  // the block exists and its id was inside the pool
 };
@@ -257,7 +331,7 @@ template <Elem CE, int D> struct BlockRegs {
 #endif
 template <Elem CE, int GT>
 constexpr int kPipelineDepth =
-    (GT == 4 && ElemInfo<CE>::bytes <= 2) ? PKV_DEPTH_LARGE_TILE : PKV_DEPTH_SMALL_TILE;
+    (GT == 4 && ElemInfo<CE>::bits <= 16) ? PKV_DEPTH_LARGE_TILE : PKV_DEPTH_SMALL_TILE;
 
 template <Elem QE, Elem CE, int D, int GT>
 __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs a) {
@@ -265,6 +339,8 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
     constexpr int L = G::L, E = G::E, R = G::R, U = G::U, STEPS = G::STEPS;
     constexpr int NW = kDecodeWaves;
     constexpr bool kInt8 = is_scaled(CE);  // 1-byte codes with a per-row scale
+    constexpr bool kU4 = CE == Elem::U4;    // 4-bit codes with a per-row (x_min, range)
+    constexpr float kInv15 = 1.0f / 15.0f;
 
     __shared__ float s_m[NW][GT];
     __shared__ float s_l[NW][GT];
@@ -353,10 +429,12 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
     for (int h = 0; h < GT; ++h) qs[h].load(a.q, ((size_t)b * Hq + h0 + h) * D + slice * E);
 
     float m[GT], l[GT], acc[GT][E];
+    float zacc[GT];  // 4-bit caches: sum of p * x_min, added to every channel at the end
 #pragma unroll
     for (int h = 0; h < GT; ++h) {
         m[h] = kNegBig;
         l[h] = 0.f;
+        zacc[h] = 0.f;
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
     }
@@ -403,6 +481,10 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
             ksr = tile_rsrc(a.k_scale + tile_idx * kBlockSize, r.ok ? kBlockSize * 4 : 0);
             vsr = tile_rsrc(a.v_scale + tile_idx * kBlockSize, r.ok ? kBlockSize * 4 : 0);
         }
+        if constexpr (kU4) {
+            ksr = tile_rsrc(a.k_scale + tile_idx * kBlockSize * 2, r.ok ? kBlockSize * 8 : 0);
+            vsr = tile_rsrc(a.v_scale + tile_idx * kBlockSize * 2, r.ok ? kBlockSize * 8 : 0);
+        }
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
 #pragma unroll
@@ -413,6 +495,12 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
                 if constexpr (kInt8) {
                     r.ks[st][u] = ld_f32(ksr, (tok + row) * 4);
                     r.vs[st][u] = ld_f32(vsr, (tok + row) * 4);
+                }
+                if constexpr (kU4) {
+                    r.kz[st][u] = ld_f32(ksr, (tok + row) * 8);
+                    r.ks[st][u] = ld_f32(ksr, (tok + row) * 8 + 4);
+                    r.vz[st][u] = ld_f32(vsr, (tok + row) * 8);
+                    r.vs[st][u] = ld_f32(vsr, (tok + row) * 8 + 4);
                 }
             }
         }
@@ -438,7 +526,12 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
                 float s[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    float d = group_sum<L>(qs[h].dot(r.k[st][u]));
+                    float d;
+                    if constexpr (kU4)
+                        d = group_sum<L>(fmaf(qs[h].dot(r.k[st][u]), r.ks[st][u] * kInv15,
+                                              r.kz[st][u] * qs[h].sum));
+                    else
+                        d = group_sum<L>(qs[h].dot(r.k[st][u]));
                     if constexpr (kInt8) d *= r.ks[st][u];
                     s[u] = valid[u] ? d * c : -INFINITY;
                 }
@@ -458,6 +551,7 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
                 if (!(PKV_LAZY_RESCALE && GT > 1) || __builtin_amdgcn_ballot_w64(mx > m[h]) != 0) {
                     const float alpha = fast_exp2(m[h] - mx);
                     l[h] *= alpha;
+                    if constexpr (kU4) zacc[h] *= alpha;
 #pragma unroll
                     for (int e = 0; e < E; ++e) acc[h][e] *= alpha;
                     m[h] = mx;
@@ -469,16 +563,29 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
             for (int u = 0; u < U; ++u) {
                 float vx[E];
                 widen<CE, E>(r.v[st][u], vx);
-                if constexpr (!kInt8) {
+                if constexpr (kU4) {
+                    // p (x_min + step c) = (p step) c + p x_min: the codes take
+                    // one FMA each, p x_min a running scalar.  Masked rows get
+                    // step = x_min = 0 (their values may be anything, NaN too).
+                } else if constexpr (!kInt8) {
                     if (!full) {
 #pragma unroll
                         for (int e = 0; e < E; ++e) vx[e] = valid[u] ? vx[e] : 0.f;
                     }
                 }
+                float vstep = 0.f, vmin = 0.f;
+                if constexpr (kU4) {
+                    vstep = valid[u] ? r.vs[st][u] * kInv15 : 0.f;
+                    vmin = valid[u] ? r.vz[st][u] : 0.f;
+                }
 #pragma unroll
                 for (int h = 0; h < GT; ++h) {
                     float pv = p[h][u];
                     if constexpr (kInt8) pv = valid[u] ? pv * r.vs[st][u] : 0.f;
+                    if constexpr (kU4) {
+                        zacc[h] = fmaf(pv, vmin, zacc[h]);
+                        pv *= vstep;
+                    }
 #pragma unroll
                     for (int e = 0; e < E; ++e) acc[h][e] = fmaf(pv, vx[e], acc[h][e]);
                 }
@@ -526,9 +633,29 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
         const size_t src = ((size_t)b * a.num_kv_heads + kvh) * D + (size_t)slice * E;
         uint4 kc, vc;
         float ks = 1.f, vs = 1.f;
-        if constexpr (!kInt8) {
-            kc = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + src * G::EB);
-            vc = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + src * G::EB);
+        float kz = 0.f, vz = 0.f;
+        if constexpr (kU4) {
+            float xk[32], xv[32];
+            const uint4* pk = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k_new) + src);
+            const uint4* pv = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v_new) + src);
+#pragma unroll
+            for (int cix = 0; cix < 4; ++cix) {
+                const uint4 k4 = pk[cix], v4 = pv[cix];
+                const uint32_t wk[4] = {k4.x, k4.y, k4.z, k4.w};
+                const uint32_t wv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    xk[8 * cix + 2 * i] = QE == Elem::F16 ? lo_h(wk[i]) : lo_bf(wk[i]);
+                    xk[8 * cix + 2 * i + 1] = QE == Elem::F16 ? hi_h(wk[i]) : hi_bf(wk[i]);
+                    xv[8 * cix + 2 * i] = QE == Elem::F16 ? lo_h(wv[i]) : lo_bf(wv[i]);
+                    xv[8 * cix + 2 * i + 1] = QE == Elem::F16 ? hi_h(wv[i]) : hi_bf(wv[i]);
+                }
+            }
+            kc = quantize32_u4<L>(xk, kz, ks);
+            vc = quantize32_u4<L>(xv, vz, vs);
+        } else if constexpr (!kInt8) {
+            kc = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + src * G::BITS / 8);
+            vc = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + src * G::BITS / 8);
         } else {
             float xk[16], xv[16];
             const uint4* pk = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k_new) + src);
@@ -552,12 +679,20 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
             // one writer per kv head: the first q-head tile's row 0 of wave 0
             const size_t trow = ((size_t)phys * a.num_kv_heads + kvh) * kBlockSize + new_off;
             const size_t dst = trow * D + (size_t)slice * E;  // elements of the cache type
-            *reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.k_cache)) + dst * G::EB) = kc;
-            *reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.v_cache)) + dst * G::EB) = vc;
+            *reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.k_cache)) + dst * G::BITS / 8) = kc;
+            *reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(a.v_cache)) + dst * G::BITS / 8) = vc;
             if constexpr (kInt8) {
                 if (slice == 0) {
                     const_cast<float*>(a.k_scale)[trow] = ks;
                     const_cast<float*>(a.v_scale)[trow] = vs;
+                }
+            }
+            if constexpr (kU4) {
+                if (slice == 0) {
+                    const_cast<float*>(a.k_scale)[2 * trow] = kz;
+                    const_cast<float*>(a.k_scale)[2 * trow + 1] = ks;
+                    const_cast<float*>(a.v_scale)[2 * trow] = vz;
+                    const_cast<float*>(a.v_scale)[2 * trow + 1] = vs;
                 }
             }
         }
@@ -565,7 +700,11 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
         widen<CE, E>(vc, vx);
 #pragma unroll
         for (int h = 0; h < GT; ++h) {
-            float d = group_sum<L>(qs[h].dot(kc));
+            float d;
+            if constexpr (kU4)
+                d = group_sum<L>(fmaf(qs[h].dot(kc), ks * kInv15, kz * qs[h].sum));
+            else
+                d = group_sum<L>(qs[h].dot(kc));
             if constexpr (kInt8) d *= ks;
             const float sn = d * c;
             if (row == 0) {  // one row takes the token
@@ -573,12 +712,23 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
                 const float alpha = fast_exp2(m[h] - mx);
                 const float pn = fast_exp2(sn - mx);
                 l[h] = fmaf(l[h], alpha, pn);
-                const float pv = kInt8 ? pn * vs : pn;
+                float pv = kInt8 ? pn * vs : pn;
+                if constexpr (kU4) {
+                    zacc[h] = fmaf(pn, vz, zacc[h] * alpha);
+                    pv = pn * (vs * kInv15);
+                }
 #pragma unroll
                 for (int e = 0; e < E; ++e) acc[h][e] = fmaf(pv, vx[e], acc[h][e] * alpha);
                 m[h] = mx;
             }
         }
+    }
+
+    if constexpr (kU4) {
+#pragma unroll
+        for (int h = 0; h < GT; ++h)
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[h][e] += zacc[h];
     }
 
     // ---- merge the R rows of each wave (lanes with equal `slice`) ----------
@@ -652,11 +802,14 @@ hipError_t launch3(const DecodeArgs& a, int gt, hipStream_t s) {
     switch (gt) {
     case 1: return launch4<QE, CE, D, 1>(a, s);
     case 2: return launch4<QE, CE, D, 2>(a, s);
-    case 4: return launch4<QE, CE, D, 4>(a, s);
+    case 4:
+        // 4-bit tiles stop at 2 heads (32 fp32 q and accumulator values per head)
+        if constexpr (CE != Elem::U4) return launch4<QE, CE, D, 4>(a, s);
+        return hipErrorInvalidValue;
     case 8:
         // 1-byte-code tiles stop at 4 heads: 8 would hold 8 x 16 fp32
         // accumulators per lane and spill
-        if constexpr (!is_scaled(CE)) return launch4<QE, CE, D, 8>(a, s);
+        if constexpr (!is_scaled(CE) && CE != Elem::U4) return launch4<QE, CE, D, 8>(a, s);
         return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
     }
@@ -665,7 +818,10 @@ hipError_t launch3(const DecodeArgs& a, int gt, hipStream_t s) {
 template <Elem QE, Elem CE>
 hipError_t launch2(const DecodeArgs& a, int d, int gt, hipStream_t s) {
     switch (d) {
-    case 64: return launch3<QE, CE, 64>(a, gt, s);
+    case 64:
+        // a 32-byte 4-bit row would put two blocks in one wave load
+        if constexpr (CE != Elem::U4) return launch3<QE, CE, 64>(a, gt, s);
+        return hipErrorInvalidValue;
     case 128: return launch3<QE, CE, 128>(a, gt, s);
     case 256: return launch3<QE, CE, 256>(a, gt, s);
     default: return hipErrorInvalidValue;
@@ -691,6 +847,10 @@ hipError_t launch_paged_decode(const DecodeArgs& a, int q_dtype, int cache_dtype
         return launch2<Elem::F16, Elem::F8>(a, head_dim, heads_per_tile, stream);
     if (qe == Elem::BF16 && ce == Elem::F8)
         return launch2<Elem::BF16, Elem::F8>(a, head_dim, heads_per_tile, stream);
+    if (qe == Elem::F16 && ce == Elem::U4)
+        return launch2<Elem::F16, Elem::U4>(a, head_dim, heads_per_tile, stream);
+    if (qe == Elem::BF16 && ce == Elem::U4)
+        return launch2<Elem::BF16, Elem::U4>(a, head_dim, heads_per_tile, stream);
     return hipErrorInvalidValue;
 }
 

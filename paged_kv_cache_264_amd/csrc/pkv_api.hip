@@ -47,12 +47,20 @@ bool is_float(pkv_dtype d) { return d == PKV_F32 || d == PKV_F16 || d == PKV_BF1
 // 1-byte codes with one fp32 scale per (slot, kv head)
 bool is_scaled(pkv_dtype d) { return d == PKV_I8 || d == PKV_F8_E4M3; }
 
+// quantized caches: per-row scale arrays required (4-bit: (x_min, range) pairs)
+bool is_quantized(pkv_dtype d) { return is_scaled(d) || d == PKV_U4; }
+
+// bytes of one cache row of head_dim elements
+int64_t row_bytes(pkv_dtype d, int head_dim) {
+    return d == PKV_F32 ? 4LL * head_dim : d == PKV_U4 ? head_dim / 2 : is_scaled(d) ? head_dim : 2LL * head_dim;
+}
+
 bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 int heads_per_tile(int g, pkv_dtype cache) {
-    const int cap = is_scaled(cache) ? 4 : 8;
+    const int cap = cache == PKV_U4 ? 2 : is_scaled(cache) ? 4 : 8;
     for (int t = cap; t > 1; t >>= 1)
         if (g % t == 0) return t;
     return 1;
@@ -104,15 +112,17 @@ pkv_status check_decode(const void* q, const void* k_cache, const void* v_cache,
     if (!head_dim_ok(D))
         return fail(PKV_ERR_UNSUPPORTED, "head_dim %d unsupported (64, 128, 256)", D);
     const bool pair_ok = (is_float(q_dtype) && cache_dtype == q_dtype) ||
-                         ((q_dtype == PKV_F16 || q_dtype == PKV_BF16) && is_scaled(cache_dtype));
+                         ((q_dtype == PKV_F16 || q_dtype == PKV_BF16) && is_quantized(cache_dtype));
+    if (cache_dtype == PKV_U4 && D == 64)
+        return fail(PKV_ERR_UNSUPPORTED, "4-bit caches need head_dim 128 or 256");
     if (!pair_ok)
         return fail(PKV_ERR_DTYPE, "unsupported (q_dtype, cache_dtype) = (%d, %d)", (int)q_dtype,
                     (int)cache_dtype);
     if (B == 0) return ok();
     if (!q || !k_cache || !v_cache || !block_tables || !context_lens)
         return fail(PKV_ERR_NULL, "q, k_cache, v_cache, block_tables and context_lens are required");
-    if (is_scaled(cache_dtype) && (!k_scale || !v_scale))
-        return fail(PKV_ERR_NULL, "k_scale and v_scale are required for an INT8 / FP8 cache");
+    if (is_quantized(cache_dtype) && (!k_scale || !v_scale))
+        return fail(PKV_ERR_NULL, "k_scale and v_scale are required for an INT8 / FP8 / 4-bit cache");
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
         return fail(PKV_ERR_SHAPE, "q, k_cache and v_cache must be 16-byte aligned");
     if ((int64_t)Hkv * num_blocks * pkv::kBlockSize * D > (int64_t)1 << 62)
@@ -209,14 +219,16 @@ pkv_status pkv_kv_cache_write(const void* k, const void* v, void* k_cache, void*
         return fail(PKV_ERR_UNSUPPORTED, "block_size %d unsupported (only 16)", block_size);
     if (!head_dim_ok(head_dim))
         return fail(PKV_ERR_UNSUPPORTED, "head_dim %d unsupported (64, 128, 256)", head_dim);
-    if (!is_float(src_dtype) || !(cache_dtype == src_dtype || is_scaled(cache_dtype)))
+    if (cache_dtype == PKV_U4 && head_dim == 64)
+        return fail(PKV_ERR_UNSUPPORTED, "4-bit caches need head_dim 128 or 256");
+    if (!is_float(src_dtype) || !(cache_dtype == src_dtype || is_quantized(cache_dtype)))
         return fail(PKV_ERR_DTYPE, "unsupported (src_dtype, cache_dtype) = (%d, %d)",
                     (int)src_dtype, (int)cache_dtype);
     if (num_tokens == 0) return ok();
     if (!k || !v || !k_cache || !v_cache || !slot_mapping)
         return fail(PKV_ERR_NULL, "k, v, k_cache, v_cache and slot_mapping are required");
-    if (is_scaled(cache_dtype) && (!k_scale || !v_scale))
-        return fail(PKV_ERR_NULL, "k_scale and v_scale are required for an INT8 / FP8 cache");
+    if (is_quantized(cache_dtype) && (!k_scale || !v_scale))
+        return fail(PKV_ERR_NULL, "k_scale and v_scale are required for an INT8 / FP8 / 4-bit cache");
     if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
         return fail(PKV_ERR_SHAPE, "k, v, k_cache and v_cache must be 16-byte aligned");
     pkv::CacheWriteArgs a{k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping,
@@ -238,27 +250,28 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* 
         return fail(PKV_ERR_UNSUPPORTED, "block_size %d unsupported (only 16)", block_size);
     if (!head_dim_ok(head_dim))
         return fail(PKV_ERR_UNSUPPORTED, "head_dim %d unsupported (64, 128, 256)", head_dim);
-    if (!is_float(cache_dtype) && !is_scaled(cache_dtype))
+    if (!is_float(cache_dtype) && !is_quantized(cache_dtype))
         return fail(PKV_ERR_DTYPE, "unsupported cache_dtype %d", (int)cache_dtype);
     if (num_pairs == 0) return ok();
     if (!k_cache || !v_cache || !copy_pairs)
         return fail(PKV_ERR_NULL, "k_cache, v_cache and copy_pairs are required");
-    if (is_scaled(cache_dtype) && (!k_scale || !v_scale))
-        return fail(PKV_ERR_NULL, "k_scale and v_scale are required for an INT8 / FP8 cache");
+    if (is_quantized(cache_dtype) && (!k_scale || !v_scale))
+        return fail(PKV_ERR_NULL, "k_scale and v_scale are required for an INT8 / FP8 / 4-bit cache");
     if (!aligned16(k_cache) || !aligned16(v_cache) ||
-        (is_scaled(cache_dtype) && (!aligned16(k_scale) || !aligned16(v_scale))))
+        (is_quantized(cache_dtype) && (!aligned16(k_scale) || !aligned16(v_scale))))
         return fail(PKV_ERR_SHAPE, "caches and scales must be 16-byte aligned");
-    const int64_t elem = cache_dtype == PKV_F32 ? 4 : is_scaled(cache_dtype) ? 1 : 2;
     pkv::CopyBlocksArgs a{};
     a.k_cache = k_cache;
     a.v_cache = v_cache;
-    a.k_scale = is_scaled(cache_dtype) ? k_scale : nullptr;
-    a.v_scale = is_scaled(cache_dtype) ? v_scale : nullptr;
+    a.k_scale = is_quantized(cache_dtype) ? k_scale : nullptr;
+    a.v_scale = is_quantized(cache_dtype) ? v_scale : nullptr;
     a.pairs = copy_pairs;
     a.num_pairs = num_pairs;
     a.num_blocks = num_blocks;
-    a.block_bytes = (int64_t)num_kv_heads * pkv::kBlockSize * head_dim * elem;
-    a.scale_bytes = is_scaled(cache_dtype) ? (int64_t)num_kv_heads * pkv::kBlockSize * 4 : 0;
+    a.block_bytes = (int64_t)num_kv_heads * pkv::kBlockSize * row_bytes(cache_dtype, head_dim);
+    a.scale_bytes = is_quantized(cache_dtype)
+                        ? (int64_t)num_kv_heads * pkv::kBlockSize * (cache_dtype == PKV_U4 ? 8 : 4)
+                        : 0;
     if (a.block_bytes > ((int64_t)1 << 40) / num_blocks)
         return fail(PKV_ERR_SHAPE, "pool too large");
     const hipError_t e = pkv::launch_copy_blocks(a, stream);

@@ -9,17 +9,20 @@ namespace pkv {
 
 // F8: 8-bit floating point e4m3 (OCP "E4M3FN", largest finite value 448),
 // the format of gfx950's fp8 convert instructions.
-enum class Elem : int { F32 = 0, F16 = 1, BF16 = 2, I8 = 3, F8 = 4 };
+// U4: 4-bit codes 0..15, two per byte (element 2i in the low nibble of byte
+// i), with two fp32 values (x_min, x_max - x_min) per (slot, kv head) row.
+enum class Elem : int { F32 = 0, F16 = 1, BF16 = 2, I8 = 3, F8 = 4, U4 = 5 };
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
 
 template <Elem E> struct ElemInfo;
-template <> struct ElemInfo<Elem::F32> { static constexpr int bytes = 4; };
-template <> struct ElemInfo<Elem::F16> { static constexpr int bytes = 2; };
-template <> struct ElemInfo<Elem::BF16> { static constexpr int bytes = 2; };
-template <> struct ElemInfo<Elem::I8> { static constexpr int bytes = 1; };
-template <> struct ElemInfo<Elem::F8> { static constexpr int bytes = 1; };
+template <> struct ElemInfo<Elem::F32> { static constexpr int bytes = 4, bits = 32; };
+template <> struct ElemInfo<Elem::F16> { static constexpr int bytes = 2, bits = 16; };
+template <> struct ElemInfo<Elem::BF16> { static constexpr int bytes = 2, bits = 16; };
+template <> struct ElemInfo<Elem::I8> { static constexpr int bytes = 1, bits = 8; };
+template <> struct ElemInfo<Elem::F8> { static constexpr int bytes = 1, bits = 8; };
+template <> struct ElemInfo<Elem::U4> { static constexpr int bytes = 1, bits = 4; };  // bytes: rounded up
 
 // caches of 1-byte codes with one fp32 scale per (slot, kv head)
 constexpr bool is_scaled(Elem e) { return e == Elem::I8 || e == Elem::F8; }

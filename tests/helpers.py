@@ -11,14 +11,15 @@ import workloads as W
 
 BS = W.BLOCK_SIZE
 DT = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16", torch.int8: "i8",
-      torch.float8_e4m3fn: "f8"}
+      torch.float8_e4m3fn: "f8", torch.uint8: "u4"}
 # max-abs-error bounds by element type (fp32 is the proposed bound for the fp32
 # case).  A case is held to the looser bound of its cache type and its q/out
 # type: a bf16 output alone carries up to 2^-9 relative rounding error, which
 # exceeds 2e-3 for |out| > 1, so bf16 q with an INT8 cache takes the bf16 bound.
-# INT8 and FP8 caches are compared with the oracle on the same dequantized
-# values, so only accumulation order and output rounding differ: 2e-3.
-TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 1.6e-2, "i8": 2e-3, "f8": 2e-3}
+# INT8, FP8 and 4-bit caches are compared with the oracle on the same
+# dequantized values, so only accumulation order and output rounding differ:
+# 2e-3.
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 1.6e-2, "i8": 2e-3, "f8": 2e-3, "u4": 2e-3}
 
 
 def tol_for(q_dtype: str, cache_dtype: str) -> float:
@@ -73,10 +74,11 @@ class OracleView:
         if self.cache_dtype in W.SCALED:
             # the oracle builds its own INT8 / FP8 pool from the fp source rows
             Hkv, D = batch.Hkv, batch.D
-            self.k_cache = np.zeros((nb, Hkv, BS, D), np.int8 if self.cache_dtype == "i8"
-                                    else np.uint8)
+            u4 = self.cache_dtype == "u4"
+            self.k_cache = np.zeros((nb, Hkv, BS, D // 2 if u4 else D),
+                                    np.int8 if self.cache_dtype == "i8" else np.uint8)
             self.v_cache = np.zeros_like(self.k_cache)
-            self.k_scale = np.full((nb, Hkv, BS), np.nan, np.float32)
+            self.k_scale = np.full((nb, Hkv, BS, 2) if u4 else (nb, Hkv, BS), np.nan, np.float32)
             self.v_scale = np.full_like(self.k_scale, np.nan)
             offs = batch.extra["src_offsets"]
             rows = np.concatenate([np.arange(offs[s], offs[s + 1]) for s in self.seqs]) \

@@ -18,7 +18,7 @@ HEADER = os.path.join(ROOT, "include", "pkv.h")
 LIB = os.path.join(ROOT, "paged_kv_cache_264_amd", "libpkv.so")
 
 OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EWS, EHIP, ECAP, ESEQ = range(9)
-F32, F16, BF16, I8, F8 = range(5)
+F32, F16, BF16, I8, F8, U4 = range(6)
 
 
 def declared_functions():
@@ -88,7 +88,10 @@ def decode(lib, **kw):
     (dict(cd=F8), ENULL),                 # FP8 cache without scales
     (dict(qd=F32, cd=F8), EDTYPE),
     (dict(qd=F8, cd=F8), EDTYPE),
-    (dict(cd=5), EDTYPE),
+    (dict(cd=6), EDTYPE),
+    (dict(cd=U4), ENULL),                 # 4-bit cache without (min, range) arrays
+    (dict(cd=U4, D=64, ks=FAKE, vs=FAKE), EUNSUP),
+    (dict(qd=F32, cd=U4), EDTYPE),
     (dict(out=None), ENULL),
     (dict(P=24), ESHAPE),
     (dict(P=-16), ESHAPE),

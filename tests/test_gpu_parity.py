@@ -51,7 +51,7 @@ def _check_step(pkv, batch, seqs=None, partition_size=0, tol=None):
 
 
 PAIRS = [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"), ("f16", "i8"), ("bf16", "i8"),
-         ("f16", "f8"), ("bf16", "f8")]
+         ("f16", "f8"), ("bf16", "f8"), ("f16", "u4"), ("bf16", "u4")]
 LENS = [1, 15, 16, 17, 250, 700, 33]
 
 
@@ -59,6 +59,9 @@ LENS = [1, 15, 16, 17, 250, 700, 33]
 @pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 2), (16, 2), (6, 3)])
 def test_decode_matrix(pkv, dtype, cache, D, Hq, Hkv):
+    if cache == "u4" and D == 64:
+        pytest.skip("4-bit caches support head_dim 128 and 256 (a 32-byte row would put two "
+                    "blocks in one wave load)")
     batch = W.make_batch(cfg=_cfg(dtype, cache, D, Hq, Hkv, LENS, seed=D + Hq), device="cuda")
     gpu_populate(pkv, batch)
     _check_step(pkv, batch)
@@ -228,9 +231,12 @@ def test_reduce_on_synthetic_partials(pkv):
 
 @pytest.mark.parametrize("src,cache", [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"),
                                        ("f32", "i8"), ("f16", "i8"), ("bf16", "i8"),
-                                       ("f32", "f8"), ("f16", "f8"), ("bf16", "f8")])
+                                       ("f32", "f8"), ("f16", "f8"), ("bf16", "f8"),
+                                       ("f32", "u4"), ("f16", "u4"), ("bf16", "u4")])
 @pytest.mark.parametrize("D", [64, 128, 256])
 def test_cache_write_bit_exact(pkv, src, cache, D):
+    if cache == "u4" and D == 64:
+        pytest.skip("4-bit caches support head_dim 128 and 256")
     NB, Hkv, T = 40, 4, 64
     g = np.random.default_rng(D)
     slots = W.random_slots(NB, T, seed=D)
@@ -248,16 +254,21 @@ def test_cache_write_bit_exact(pkv, src, cache, D):
         k[1, :, :] = 0.5; k[1, :, 0] = 448.0
         k[1, :, 1:1 + len(mids)] = mids.to(k.dtype)
     # sentinel bytes everywhere in the pool
-    kc = torch.from_numpy(g.integers(0, 256, (NB, Hkv, BS, D * (4 if cache == "f32" else
-                                     2 if cache in ("f16", "bf16") else 1)), dtype=np.uint8))
+    row = {"f32": 4 * D, "f16": 2 * D, "bf16": 2 * D, "u4": D // 2}.get(cache, D)
+    kc = torch.from_numpy(g.integers(0, 256, (NB, Hkv, BS, row), dtype=np.uint8))
     if cache == "f8":                                        # sentinel codes, no NaN
         kc[(kc & 0x7F) == 0x7F] = 0x3C
     vc = torch.from_numpy(g.integers(0, 256, kc.shape, dtype=np.uint8))
     kc = kc.view(tdt[cache]).contiguous(); vc = vc.view(tdt[cache]).contiguous()
     ks = vs = None
+    if cache == "u4":
+        k[0] = 0.7                                           # constant row -> range 0
+        # a row with ties: min 0, max 15 -> range 15, (x - 0) / 15 * 15 = x
+        k[1, :, :] = 7.5; k[1, :, 0] = 0.0; k[1, :, 1] = 15.0; k[1, :, 2] = 2.5
     if cache in W.SCALED:
-        ks = torch.from_numpy(g.standard_normal((NB, Hkv, BS), dtype=np.float32))
-        vs = torch.from_numpy(g.standard_normal((NB, Hkv, BS), dtype=np.float32))
+        shape = (NB, Hkv, BS, 2) if cache == "u4" else (NB, Hkv, BS)
+        ks = torch.from_numpy(g.standard_normal(shape, dtype=np.float32))
+        vs = torch.from_numpy(g.standard_normal(shape, dtype=np.float32))
     hk, hv = host(kc), host(vc)
     hks = None if ks is None else ks.numpy().copy()
     hvs = None if vs is None else vs.numpy().copy()
@@ -305,7 +316,7 @@ def test_int8_codes_bit_exact_many_rows(pkv):
 # the five workloads at full size, in the launch configuration the bench uses
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["tiny", "llama7b", "gqa", "long", "int8", "fp8"])
+@pytest.mark.parametrize("name", ["tiny", "llama7b", "gqa", "long", "int8", "fp8", "int4"])
 def test_full_config(pkv, name):
     batch = W.make_batch(name, device="cuda", poison=True)
     gpu_populate(pkv, batch)
@@ -355,6 +366,8 @@ def test_large_batch_natural_order(pkv):
 @pytest.mark.parametrize("D,Hq,Hkv,P", [(128, 8, 8, 0), (64, 16, 2, 32), (256, 4, 1, 64),
                                         (128, 8, 2, 0), (128, 16, 2, 64)])
 def test_decode_append_matches_write_then_decode(pkv, dtype, cache, D, Hq, Hkv, P):
+    if cache == "u4" and D == 64:
+        pytest.skip("4-bit caches support head_dim 128 and 256")
     """The fused step equals the cache write of the new tokens followed by the
     decode: cache bytes bit-exact against the oracle's write, outputs within
     the dtype bound."""

@@ -64,16 +64,20 @@ CONFIGS = {
     # chunk of its prompt over U[1024, 4096] cached tokens (the chunk included).
     "prefill": dict(B=16, ctx=(1024, 4096), Hq=32, Hkv=32, D=128, dtype="f16", cache="f16",
                     pool=None, seed=11, max_ctx=4096, q_len=512),
+    # 4-bit KV cache at the LLaMA-7B shape (per-row min/max, two codes a byte).
+    "int4": dict(B=64, ctx=(512, 4096), Hq=32, Hkv=32, D=128, dtype="f16", cache="u4",
+                 pool=None, seed=12, max_ctx=4096),
     # FP8 (e4m3) KV cache at the LLaMA-7B shape, populated the same way.
     "fp8": dict(B=64, ctx=(512, 4096), Hq=32, Hkv=32, D=128, dtype="f16", cache="f8",
                 pool=None, seed=8, max_ctx=4096),
 }
 
 TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
-               "i8": torch.int8, "f8": torch.float8_e4m3fn}
-# caches of 1-byte codes with one fp32 scale per (slot, kv head), populated by
-# the quantizing cache write
-SCALED = ("i8", "f8")
+               "i8": torch.int8, "f8": torch.float8_e4m3fn, "u4": torch.uint8}
+# quantized caches, populated by the quantizing cache write: 1-byte codes with
+# one fp32 scale per (slot, kv head) ("i8", "f8"), or 4-bit codes two per byte
+# with an fp32 (x_min, range) pair per (slot, kv head) ("u4")
+SCALED = ("i8", "f8", "u4")
 
 
 def rng(seed: int, stream: int) -> np.random.Generator:
@@ -268,12 +272,14 @@ def make_batch(name: str | None = None, device="cpu", seed: int | None = None, p
 
     k_scale = v_scale = k_src = v_src = slot_src = src_offsets = None
     if cache in SCALED:
-        k_cache = torch.zeros((nb, Hkv, BLOCK_SIZE, D), dtype=torch.uint8,
+        row = D // 2 if cache == "u4" else D
+        k_cache = torch.zeros((nb, Hkv, BLOCK_SIZE, row), dtype=torch.uint8,
                               device=device).view(TORCH_DTYPE[cache])
-        v_cache = torch.zeros((nb, Hkv, BLOCK_SIZE, D), dtype=torch.uint8,
+        v_cache = torch.zeros((nb, Hkv, BLOCK_SIZE, row), dtype=torch.uint8,
                               device=device).view(TORCH_DTYPE[cache])
         fill = float("nan") if poison else 0.0
-        k_scale = torch.full((nb, Hkv, BLOCK_SIZE), fill, dtype=torch.float32, device=device)
+        meta = (nb, Hkv, BLOCK_SIZE, 2) if cache == "u4" else (nb, Hkv, BLOCK_SIZE)
+        k_scale = torch.full(meta, fill, dtype=torch.float32, device=device)
         v_scale = torch.full_like(k_scale, fill)
         # prefill rows: positions 0..N_b-2 of every sequence, in sequence order
         slots = [slots_for(layout, b, np.arange(max(int(n) - 1, 0))) for b, n in enumerate(lens)]
@@ -321,13 +327,16 @@ def random_slots(num_blocks: int, T: int, seed: int) -> np.ndarray:
         np.int64)
 
 
-def algorithmic_bytes(context_lens, Hq, Hkv, D, e_kv, e_q, int8_scales=False) -> int:
+def algorithmic_bytes(context_lens, Hq, Hkv, D, e_kv, e_q, int8_scales=False,
+                      meta_bytes=None) -> int:
     """Bytes a decode step over this batch must move at least: every context
-    token's K and V rows (plus a 4-byte scale each for INT8), q and out, the
+    token's K and V rows (e_kv bytes per element, 0.5 for 4-bit codes; plus a
+    4-byte scale each for INT8 / FP8, or meta_bytes per row), q and out, the
     block-table entries actually used and the context lengths."""
     lens = np.asarray(context_lens, np.int64)
     tok = int(lens.sum())
-    per_tok = Hkv * 2 * (D * e_kv + (4 if int8_scales else 0))
+    meta = meta_bytes if meta_bytes is not None else (4 if int8_scales else 0)
+    per_tok = int(Hkv * 2 * (D * e_kv + meta))
     B = len(lens)
     return (tok * per_tok + B * Hq * D * 2 * e_q
             + int(sum(blocks_needed(n) for n in lens)) * 4 + 4 * B)
