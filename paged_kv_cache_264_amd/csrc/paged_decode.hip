@@ -145,47 +145,70 @@ template <Elem QE, Elem CE> struct QSliceScaled {
     }
 };
 template <Elem QE> struct QSlice<QE, Elem::I8, 16> : QSliceScaled<QE, Elem::I8> {};
+template <Elem QE> struct QSlice<QE, Elem::F8, 16> : QSliceScaled<QE, Elem::F8> {};
 
-// 4-bit cache: q widened to fp32 once, with the sum of its slice (the
-// x_min term of the dequantized dot); the dot runs on the raw codes:
-//   q . (x_min + c * step) = x_min * sum(q) + step * (q . c)
+// 4-bit cache: q kept packed in its own 16-bit format, paired as the codes
+// come out of a 32-bit word: pair k of word i is (q[8i+k], q[8i+k+4]),
+// matching (nibble k, nibble k+4).  A pair of codes becomes a pair of 16-bit
+// floats of value 16 + code by OR-ing the nibbles, shifted into the mantissa,
+// with the bits of 16.0 (exact in fp16 and bf16), so one v_dot2 takes two
+// codes:  q . (x_min + step c) = step * sum q (16 + c) + (x_min - 16 step) sum q.
 template <Elem QE> struct QSlice<QE, Elem::U4, 32> {
-    float v[32];
+    uint32_t v[16];  // [word i][pair k] -> v[4 i + k]
     float sum;
     __device__ __forceinline__ void load(const void* q, size_t elem_off) {
-        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) + elem_off);
-        sum = 0.f;
+        const uint16_t* p = static_cast<const uint16_t*>(q) + elem_off;
+        uint16_t x[32];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const uint4 a = p[c];
+            const uint4 a = reinterpret_cast<const uint4*>(p)[c];
             const uint32_t w[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                v[8 * c + 2 * i] = QE == Elem::F16 ? lo_h(w[i]) : lo_bf(w[i]);
-                v[8 * c + 2 * i + 1] = QE == Elem::F16 ? hi_h(w[i]) : hi_bf(w[i]);
+            for (int t = 0; t < 4; ++t) {
+                x[8 * c + 2 * t] = (uint16_t)(w[t] & 0xffffu);
+                x[8 * c + 2 * t + 1] = (uint16_t)(w[t] >> 16);
             }
         }
+        sum = 0.f;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) sum += v[i];
+        for (int i = 0; i < 32; ++i) sum += QE == Elem::F16 ? h2f(x[i]) : bf2f(x[i]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                v[4 * i + k] = (uint32_t)x[8 * i + k] | ((uint32_t)x[8 * i + k + 4] << 16);
     }
-    // sum_e q_e * code_e over the 32 codes of a 16-byte chunk
-    __device__ __forceinline__ float dot(const uint4& k) const {
+    // sum over the chunk's 32 codes of q * (16 + code)
+    __device__ __forceinline__ float dot16(const uint4& k) const {
         const uint32_t w[4] = {k.x, k.y, k.z, k.w};
+        // fp16 16.0 = 0x4C00, mantissa step 1/64 at that exponent: code << 6;
+        // bf16 16.0 = 0x4180, mantissa step 1/8: code << 3
+        constexpr uint32_t kMagic = QE == Elem::F16 ? 0x4C004C00u : 0x41804180u;
+        constexpr int kSh = QE == Elem::F16 ? 6 : 3;
+        constexpr uint32_t kMask = 0x000F000Fu << kSh;
         float d0 = 0.f, d1 = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint32_t lo = w[i] & 0x0F0F0F0Fu;          // elements 8i, 8i+2, 8i+4, 8i+6
-            const uint32_t hi = (w[i] >> 4) & 0x0F0F0F0Fu;   // elements 8i+1, 8i+3, ...
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                d0 = fmaf(v[8 * i + 2 * j], (float)((lo >> (8 * j)) & 0xffu), d0);
-                d1 = fmaf(v[8 * i + 2 * j + 1], (float)((hi >> (8 * j)) & 0xffu), d1);
+            for (int kq = 0; kq < 4; ++kq) {
+                const int sh = kSh - 4 * kq;   // nibble kq (and kq + 4) to the mantissa
+                const uint32_t bits = ((sh >= 0 ? (w[i] << sh) : (w[i] >> -sh)) & kMask) | kMagic;
+                float& d = (kq & 1) ? d1 : d0;
+                if constexpr (QE == Elem::F16)
+                    d = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, v[4 * i + kq]),
+                                               __builtin_bit_cast(half2_t, bits), d, false);
+                else
+                    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, v[4 * i + kq]),
+                                                        __builtin_bit_cast(bf162_t, bits), d, false);
             }
         }
         return d0 + d1;
     }
+    // this lane's share of q . dequantized K row
+    __device__ __forceinline__ float score(const uint4& k, float step, float zmin) const {
+        return fmaf(dot16(k), step, fmaf(-16.0f, step, zmin) * sum);
+    }
 };
-template <Elem QE> struct QSlice<QE, Elem::F8, 16> : QSliceScaled<QE, Elem::F8> {};
 
 // Codes of one row of the new token: this lane's 16 elements, whose row spans
 // L lanes.  Same arithmetic as the quantizing cache write: exact absolute
@@ -271,8 +294,14 @@ template <Elem CE, int E> __device__ __forceinline__ void widen(const uint4& c, 
         } else if constexpr (CE == Elem::F8) {
             f8x4_to_f32(w[i], x[4 * i + 0], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
         } else if constexpr (CE == Elem::U4) {
+            // low nibbles are elements 8i, 8i+2, 8i+4, 8i+6, high ones the odd
+            // elements: byte-select converts of the two masked words
+            const uint32_t lo = w[i] & 0x0F0F0F0Fu, hi = (w[i] >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) x[8 * i + j] = (float)((w[i] >> (4 * j)) & 15u);
+            for (int j = 0; j < 4; ++j) {
+                x[8 * i + 2 * j] = (float)((lo >> (8 * j)) & 0xffu);
+                x[8 * i + 2 * j + 1] = (float)((hi >> (8 * j)) & 0xffu);
+            }
         } else {
             x[4 * i + 0] = i8_at(w[i], 0);
             x[4 * i + 1] = i8_at(w[i], 1);
@@ -334,7 +363,9 @@ constexpr int kPipelineDepth =
     (GT == 4 && ElemInfo<CE>::bits <= 16) ? PKV_DEPTH_LARGE_TILE : PKV_DEPTH_SMALL_TILE;
 
 template <Elem QE, Elem CE, int D, int GT>
-__global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kDecodeThreads)
+__attribute__((amdgpu_waves_per_eu(CE == Elem::U4 && GT == 1 && D == 128 ? 4 : 1)))
+void paged_decode_kernel(DecodeArgs a) {
     using G = Geom<CE, D>;
     constexpr int L = G::L, E = G::E, R = G::R, U = G::U, STEPS = G::STEPS;
     constexpr int NW = kDecodeWaves;
@@ -344,7 +375,11 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
 
     __shared__ float s_m[NW][GT];
     __shared__ float s_l[NW][GT];
-    __shared__ float s_acc[NW][GT][D];
+    // rows of a wave kept apart for the final LDS merge (the rest are added
+    // by lane shuffles first): as many as 4, within 32 KiB of LDS
+    constexpr int kKeepCap = 32768 / (NW * GT * D * 4);
+    constexpr int RK = kKeepCap >= 4 ? (R < 4 ? R : 4) : kKeepCap >= 2 ? (R < 2 ? R : 2) : 1;
+    __shared__ float s_acc[NW][RK][GT][D];
     __shared__ int2 s_key[kScheduleMaxSeqs];  // (partition span, item count) per sequence
     __shared__ int s_pick[2];
 
@@ -528,8 +563,8 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
                 for (int u = 0; u < U; ++u) {
                     float d;
                     if constexpr (kU4)
-                        d = group_sum<L>(fmaf(qs[h].dot(r.k[st][u]), r.ks[st][u] * kInv15,
-                                              r.kz[st][u] * qs[h].sum));
+                        d = group_sum<L>(qs[h].score(r.k[st][u], r.ks[st][u] * kInv15,
+                                                     r.kz[st][u]));
                     else
                         d = group_sum<L>(qs[h].dot(r.k[st][u]));
                     if constexpr (kInt8) d *= r.ks[st][u];
@@ -702,7 +737,7 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
         for (int h = 0; h < GT; ++h) {
             float d;
             if constexpr (kU4)
-                d = group_sum<L>(fmaf(qs[h].dot(kc), ks * kInv15, kz * qs[h].sum));
+                d = group_sum<L>(qs[h].score(kc, ks * kInv15, kz));
             else
                 d = group_sum<L>(qs[h].dot(kc));
             if constexpr (kInt8) d *= ks;
@@ -745,16 +780,16 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
         for (int e = 0; e < E; ++e) {
             float x = acc[h][e] * f;
 #pragma unroll
-            for (int off = L; off < kWave; off <<= 1) x += __shfl_xor(x, off);
+            for (int off = L * RK; off < kWave; off <<= 1) x += __shfl_xor(x, off);
             acc[h][e] = x;
         }
         if (lane == 0) {
             s_m[wave][h] = M;
             s_l[wave][h] = lh;
         }
-        if (row == 0) {
+        if (row < RK) {
 #pragma unroll
-            for (int e = 0; e < E; ++e) s_acc[wave][h][slice * E + e] = acc[h][e];
+            for (int e = 0; e < E; ++e) s_acc[wave][row][h][slice * E + e] = acc[h][e];
         }
     }
     __syncthreads();
@@ -771,7 +806,10 @@ __global__ __launch_bounds__(kDecodeThreads) void paged_decode_kernel(DecodeArgs
         for (int w = 0; w < NW; ++w) {
             const float f = fast_exp2(s_m[w][h] - M);
             lsum = fmaf(s_l[w][h], f, lsum);
-            o = fmaf(s_acc[w][h][d], f, o);
+            float ow = s_acc[w][0][h][d];
+#pragma unroll
+            for (int rk = 1; rk < RK; ++rk) ow += s_acc[w][rk][h][d];
+            o = fmaf(ow, f, o);
         }
         const size_t bh = (size_t)b * Hq + h0 + h;
         if (single) {
