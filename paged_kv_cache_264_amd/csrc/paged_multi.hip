@@ -46,6 +46,7 @@ typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_v __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_v __attribute__((ext_vector_type(4)));
 
 constexpr int kRows = 16;
@@ -354,7 +355,13 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
 // and one softmax update per step.  The output is accumulated transposed,
 // O^T = V^T P^T: the P operand is then the score tile as it leaves the first
 // MFMA and each lane's accumulator column is its own query, so rescaling and
-// normalizing need no lane exchange.  Each wave owns its rows for the whole
+// normalizing need no lane exchange.  The V^T operand comes from the
+// token-major V tile through the LDS transpose read (ds_read_b64_tr_b16):
+// in each 16-lane group, lane 16 G + 4 a + c receives, as its element e,
+// element c of the 8 bytes that lane 16 G + a + 4 e addresses.  So when lane
+// 16 G + a + 4 e addresses channels 16 nn + 4 a .. + 3 of token 4 G + e,
+// lane 16 G + col receives channel 16 nn + col of tokens 4 G .. 4 G + 3:
+// one read per block and 16 channels.  Each wave owns its rows for the whole
 // partition, so there is no merge between waves.
 template <Elem T, int D, int RW>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
@@ -364,13 +371,16 @@ void paged_multi_tiled_kernel(MultiArgs a) {
     constexpr int KB = D <= 128 ? 2 : 1;            // 16-token blocks per softmax step
     constexpr int ROW = D * 2;
     constexpr int TILE = kRows * ROW;
-    constexpr int LS = ROW + 16;                    // padded LDS row stride
+    constexpr int LS = ROW + 16;                    // padded LDS row stride (K)
+    // V row stride: the 16 lanes of a transpose read address 4 tokens x 4
+    // channel quads; rows 8 words apart mod 64 put them on distinct banks
+    constexpr int LSV = ROW + 32;
     constexpr int CH = TILE / 16;                   // 16-byte chunks per tile
     constexpr int CPT = (CH + kThreads - 1) / kThreads;
     constexpr int WG_ROWS = kWaves * kRows * RW;
 
     __shared__ __attribute__((aligned(16))) char s_k[2][KB][kRows * LS];
-    __shared__ __attribute__((aligned(16))) char s_v[2][KB][kRows * LS];
+    __shared__ __attribute__((aligned(16))) char s_v[2][KB][kRows * LSV];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -484,7 +494,7 @@ void paged_multi_tiled_kernel(MultiArgs a) {
                     *reinterpret_cast<uint4*>(s_k[buf][kb] + tok * LS + off) =
                         make_uint4(keep ? kx.x : 0u, keep ? kx.y : 0u, keep ? kx.z : 0u,
                                    keep ? kx.w : 0u);
-                    *reinterpret_cast<uint4*>(s_v[buf][kb] + tok * LS + off) =
+                    *reinterpret_cast<uint4*>(s_v[buf][kb] + tok * LSV + off) =
                         make_uint4(keep ? vx.x : 0u, keep ? vx.y : 0u, keep ? vx.z : 0u,
                                    keep ? vx.w : 0u);
                 }
@@ -567,34 +577,33 @@ void paged_multi_tiled_kernel(MultiArgs a) {
 #pragma unroll
                 for (int nn = 0; nn < NN; ++nn) o[rr][nn] *= alpha[rr];
             }
+        // the LDS address this lane gives the transpose read: token
+        // 4 grp + (lane / 4) % 4, channels 4 (lane % 4) .. + 3 of each 16
+        const int v_off = (4 * grp + ((lane >> 2) & 3)) * LSV + (lane & 3) * 8;
 #pragma unroll
         for (int nn = 0; nn < NN; ++nn) {
             // V^T operand: row d = 16 nn + col; tokens 4 grp .. 4 grp + 3 of each block
-            uint32_t vw[KB][2];
+            uint2 vw[KB];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                const char* base = s_v[buf][kb] + (grp * 4) * LS + (nn * 16 + col) * 2;
-                const uint32_t v0 = *reinterpret_cast<const uint16_t*>(base);
-                const uint32_t v1 = *reinterpret_cast<const uint16_t*>(base + LS);
-                const uint32_t v2 = *reinterpret_cast<const uint16_t*>(base + 2 * LS);
-                const uint32_t v3 = *reinterpret_cast<const uint16_t*>(base + 3 * LS);
-                vw[kb][0] = v0 | (v1 << 16);
-                vw[kb][1] = v2 | (v3 << 16);
+                typedef __attribute__((address_space(3))) s16x4_v lds_s16x4;
+                const s16x4_v t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4*)(s_v[buf][kb] + v_off + nn * 32));
+                vw[kb] = __builtin_bit_cast(uint2, t);
             }
             if constexpr (KB == 2) {
                 // one 16x16x32 MFMA over both blocks: contraction index 8 grp + j
                 // is token 4 grp + j of block 0 (j < 4) or 4 grp + j - 4 of
                 // block 1, in the A (V^T) and the B (P^T) operand alike
-                const uint4 va = make_uint4(vw[0][0], vw[0][1], vw[1][0], vw[1][1]);
+                const uint4 va = make_uint4(vw[0].x, vw[0].y, vw[1].x, vw[1].y);
 #pragma unroll
                 for (int rr = 0; rr < RW; ++rr) {
                     const uint4 pbb = make_uint4(pb[rr][0].x, pb[rr][0].y, pb[rr][1].x, pb[rr][1].y);
                     o[rr][nn] = Mfma<T>::pv32(va, pbb, o[rr][nn]);
                 }
             } else {
-                const uint2 va = make_uint2(vw[0][0], vw[0][1]);
 #pragma unroll
-                for (int rr = 0; rr < RW; ++rr) o[rr][nn] = Mfma<T>::pv(va, pb[rr][0], o[rr][nn]);
+                for (int rr = 0; rr < RW; ++rr) o[rr][nn] = Mfma<T>::pv(vw[0], pb[rr][0], o[rr][nn]);
             }
         }
     };
