@@ -56,6 +56,7 @@ constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kNegBig = -3.0e38f;
 constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer access
 constexpr int kNonTemporal = 2;
+constexpr unsigned kXcds = 8;              // accelerator complex dies of the chip
 
 template <Elem T> struct Mfma;
 template <> struct Mfma<Elem::F16> {
@@ -388,12 +389,26 @@ void paged_multi_tiled_kernel(MultiArgs a) {
     const int grp = lane >> 4;
     const int col = lane & 15;
 
+    // Work-groups go to the XCDs round-robin in launch order.  Renumbered so
+    // that the row groups of one (sequence, partition, kv head), which read
+    // the same K/V blocks, go to one XCD one after the other and share its
+    // L2, while successive (sequence, partition, kv head) groups still go
+    // round-robin (the XCDs stay balanced when sequence lengths differ).
     const int NP = a.num_partitions;
-    int rest = blockIdx.x;
-    const int part = rest % NP;
-    rest /= NP;
+    unsigned item = blockIdx.x;
+    {
+        const unsigned R = (unsigned)a.row_tiles;
+        const unsigned whole = gridDim.x / R / kXcds * kXcds;  // groups in whole rounds
+        if (item < whole * R) {
+            const unsigned x = item % kXcds, y = item / kXcds;
+            item = ((y / R) * kXcds + x) * R + y % R;
+        }
+    }
+    int rest = (int)item;
     const int rg = rest % a.row_tiles;
     rest /= a.row_tiles;
+    const int part = rest % NP;
+    rest /= NP;
     const int kvh = rest % a.num_kv_heads;
     const int b = rest / a.num_kv_heads;
 
@@ -522,40 +537,67 @@ void paged_multi_tiled_kernel(MultiArgs a) {
                         s[rr][kb] = Mfma<T>::qk(ka[kb][kk], qv[rr][kk], s[rr][kb]);
                 }
         }
-        // 2. online softmax over the step's KB * 16 tokens, per row tile.
-        //    Masking only where the step reaches the partition end or the
-        //    causal diagonal of some row of the tile (uniform test).
-        uint2 pb[RW][KB];
-        float alpha[RW];
-        bool grew[RW];
+        // V^T operands of the step, read once for every row tile.  In each
+        // 16-lane group the lane addresses token 4 grp + (lane / 4) % 4,
+        // channels 4 (lane % 4) .. + 3 of each 16; it receives channel
+        // 16 nn + col of tokens 4 grp .. 4 grp + 3.
+        const int v_off = (4 * grp + ((lane >> 2) & 3)) * LSV + (lane & 3) * 8;
+        uint2 vw[NN][KB];
+#pragma unroll
+        for (int nn = 0; nn < NN; ++nn)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                typedef __attribute__((address_space(3))) s16x4_v lds_s16x4;
+                const s16x4_v t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4*)(s_v[buf][kb] + v_off + nn * 32));
+                vw[nn][kb] = __builtin_bit_cast(uint2, t);
+            }
+        // 2. per row tile: online softmax over the step's KB * 16 tokens, then
+        //    O^T += V^T P^T.  The P·V products of one tile run on the matrix
+        //    cores while the next tile's softmax is computed.
         const int t_hi = (jb0 + KB) * kBlockSize;       // one past the step's last token
 #pragma unroll
         for (int rr = 0; rr < RW; ++rr) {
+            // Masking only where the step reaches the partition end or the
+            // causal diagonal of some row of the tile (uniform test).
             const bool full = t_hi <= t_end && t_hi <= tile_pos_min[rr] + 1;
             float sv[KB][4], mx = kNegBig;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = (jb0 + kb) * kBlockSize + grp * 4 + i;
-                    const bool valid = full || (row_ok[rr] && t < t_end && t <= pos[rr]);
-                    sv[kb][i] = valid ? s[rr][kb][i] * c : -INFINITY;
-                    mx = fmaxf(mx, sv[kb][i]);
-                }
+                for (int i = 0; i < 4; ++i) sv[kb][i] = s[rr][kb][i] * c;
+            if (!full) {
+                // a lane's tokens lie below t_lim: its row's position + 1 and the partition end
+                const int t_lim = row_ok[rr] ? min(t_end, pos[rr] + 1) : 0;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = (jb0 + kb) * kBlockSize + grp * 4 + i;
+                        sv[kb][i] = t < t_lim ? sv[kb][i] : -INFINITY;
+                    }
+            }
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sv[kb][i]);
             // The running max m is shared by a query's 4 lanes; the exact
-            // cross-lane max is needed only when some score exceeds it.
-            grew[rr] = __builtin_amdgcn_ballot_w64(mx > m[rr]) != 0;
+            // cross-lane max is needed only when some score exceeds it, and
+            // then acc is rescaled (otherwise alpha is 1).
             float mn = m[rr];
-            alpha[rr] = 1.f;
-            if (grew[rr]) {
+            if (__builtin_amdgcn_ballot_w64(mx > m[rr]) != 0) {
                 mx = fmaxf(mx, __shfl_xor(mx, 16));
                 mx = fmaxf(mx, __shfl_xor(mx, 32));
                 mn = fmaxf(m[rr], mx);
-                alpha[rr] = fast_exp2(m[rr] - mn);
+                const float alpha = fast_exp2(m[rr] - mn);
                 m[rr] = mn;
+                l[rr] *= alpha;
+#pragma unroll
+                for (int nn = 0; nn < NN; ++nn) o[rr][nn] *= alpha;
             }
-            // l is this lane's share of the sum (its own tokens), rescaled
-            // with the shared max and reduced across the 4 lanes at the end
+            // l is this lane's share of the sum (its own tokens), reduced
+            // across the 4 lanes at the end
+            uint2 pb[KB];
             float ps = 0.f;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
@@ -565,45 +607,21 @@ void paged_multi_tiled_kernel(MultiArgs a) {
                     p[i] = fast_exp2(sv[kb][i] - mn);
                     ps += p[i];
                 }
-                pb[rr][kb] = make_uint2(Mfma<T>::pack(p[0], p[1]), Mfma<T>::pack(p[2], p[3]));
+                pb[kb] = make_uint2(Mfma<T>::pack(p[0], p[1]), Mfma<T>::pack(p[2], p[3]));
             }
-            l[rr] = fmaf(l[rr], alpha[rr], ps);
-        }
-        // 3. O^T = V^T P^T, the lane's accumulator columns being its own query.
-        //    Rescale only when some running max grew (otherwise alpha is 1).
+            l[rr] += ps;
 #pragma unroll
-        for (int rr = 0; rr < RW; ++rr)
-            if (grew[rr]) {
-#pragma unroll
-                for (int nn = 0; nn < NN; ++nn) o[rr][nn] *= alpha[rr];
-            }
-        // the LDS address this lane gives the transpose read: token
-        // 4 grp + (lane / 4) % 4, channels 4 (lane % 4) .. + 3 of each 16
-        const int v_off = (4 * grp + ((lane >> 2) & 3)) * LSV + (lane & 3) * 8;
-#pragma unroll
-        for (int nn = 0; nn < NN; ++nn) {
-            // V^T operand: row d = 16 nn + col; tokens 4 grp .. 4 grp + 3 of each block
-            uint2 vw[KB];
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                typedef __attribute__((address_space(3))) s16x4_v lds_s16x4;
-                const s16x4_v t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4*)(s_v[buf][kb] + v_off + nn * 32));
-                vw[kb] = __builtin_bit_cast(uint2, t);
-            }
-            if constexpr (KB == 2) {
-                // one 16x16x32 MFMA over both blocks: contraction index 8 grp + j
-                // is token 4 grp + j of block 0 (j < 4) or 4 grp + j - 4 of
-                // block 1, in the A (V^T) and the B (P^T) operand alike
-                const uint4 va = make_uint4(vw[0].x, vw[0].y, vw[1].x, vw[1].y);
-#pragma unroll
-                for (int rr = 0; rr < RW; ++rr) {
-                    const uint4 pbb = make_uint4(pb[rr][0].x, pb[rr][0].y, pb[rr][1].x, pb[rr][1].y);
+            for (int nn = 0; nn < NN; ++nn) {
+                if constexpr (KB == 2) {
+                    // one 16x16x32 MFMA over both blocks: contraction index 8 grp + j
+                    // is token 4 grp + j of block 0 (j < 4) or 4 grp + j - 4 of
+                    // block 1, in the A (V^T) and the B (P^T) operand alike
+                    const uint4 va = make_uint4(vw[nn][0].x, vw[nn][0].y, vw[nn][1].x, vw[nn][1].y);
+                    const uint4 pbb = make_uint4(pb[0].x, pb[0].y, pb[1].x, pb[1].y);
                     o[rr][nn] = Mfma<T>::pv32(va, pbb, o[rr][nn]);
+                } else {
+                    o[rr][nn] = Mfma<T>::pv(vw[nn][0], pb[0], o[rr][nn]);
                 }
-            } else {
-#pragma unroll
-                for (int rr = 0; rr < RW; ++rr) o[rr][nn] = Mfma<T>::pv(vw[0], pb[rr][0], o[rr][nn]);
             }
         }
     };
