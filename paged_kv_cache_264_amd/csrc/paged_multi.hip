@@ -410,7 +410,35 @@ void paged_multi_tiled_kernel(MultiArgs a) {
     const int part = rest % NP;
     rest /= NP;
     const int kvh = rest % a.num_kv_heads;
-    const int b = rest / a.num_kv_heads;
+    // Sequences in longest-first order (by partition length), so that the
+    // work-groups dispatched last are the shortest and the ragged tail of
+    // the launch is small.  Every work-group ranks the sequences itself
+    // (one per thread, in LDS).
+    static_assert(kThreads <= kScheduleMaxSeqs, "one LDS key per thread");
+    __shared__ int s_key[kScheduleMaxSeqs];
+    __shared__ int s_order[kScheduleMaxSeqs];
+    int b = rest / a.num_kv_heads;
+    if (a.num_seqs <= kScheduleMaxSeqs) {
+        const int n_cap0 = a.max_blocks_per_seq * kBlockSize;
+        int key = -1;
+        if (tid < a.num_seqs) {
+            const int nn = min(max(a.context_lens[tid], 0), n_cap0);
+            const int c = partition_count(nn, a.partition_size);
+            key = c > 0 ? partition_span(nn, c) : 0;
+        }
+        s_key[tid] = key;
+        __syncthreads();
+        if (tid < a.num_seqs) {
+            int r = 0;
+            for (int j = 0; j < a.num_seqs; ++j) {
+                const int kj = s_key[j];
+                r += (kj > key || (kj == key && j < tid)) ? 1 : 0;
+            }
+            s_order[r] = tid;
+        }
+        __syncthreads();
+        b = s_order[b];
+    }
 
     const int Hq = a.num_q_heads;
     const int g = Hq / a.num_kv_heads;
@@ -435,7 +463,12 @@ void paged_multi_tiled_kernel(MultiArgs a) {
     const int blk_begin = t_begin / kBlockSize;
     const int blk_stop = t_stop > t_begin ? (t_stop + kBlockSize - 1) / kBlockSize : blk_begin;
     const int32_t* table = a.block_tables + (size_t)b * a.max_blocks_per_seq;
-    const float c = a.scale_log2;
+    // Scores stay in raw units (q . k); the softmax works on c * s with
+    // c = scale * log2(e), applied inside the exponent by one FMA.  A
+    // negative scale is taken as |scale| on negated queries (exact), and c
+    // is kept above zero so that a masked score (-inf) still gives weight 0.
+    const bool neg_scale = a.scale_log2 < 0.f;
+    const float c = fmaxf(fabsf(a.scale_log2), 1.17549435e-38f);
 
     // this wave's row tiles; lane column `col` is one query row of each tile
     const int w_r0 = wg_r0 + wave * kRows * RW;
@@ -446,7 +479,7 @@ void paged_multi_tiled_kernel(MultiArgs a) {
     for (int rr = 0; rr < RW; ++rr)
         tile_pos_min[rr] = n - qlen + min(w_r0 + rr * kRows, rows_total - 1) / g;
     uint4 qv[RW][KK];
-    float m[RW], l[RW];
+    float m[RW], cm[RW], l[RW];  // running max of raw scores, c times it, sum
     f32x4_t o[RW][NN];  // O^T: o[rr][nn][i] = O[row col][d = 16 nn + 4 grp + i]
 #pragma unroll
     for (int rr = 0; rr < RW; ++rr) {
@@ -462,8 +495,14 @@ void paged_multi_tiled_kernel(MultiArgs a) {
                 qv[rr][kk] = *reinterpret_cast<const uint4*>(
                     static_cast<const char*>(a.q) +
                     (((size_t)(q0 + jq) * Hq + hq) * D + kk * 32 + grp * 8) * 2);
+            if (neg_scale) {
+                const uint32_t sg = 0x80008000u;  // sign bits of both 16-bit elements
+                qv[rr][kk] = make_uint4(qv[rr][kk].x ^ sg, qv[rr][kk].y ^ sg, qv[rr][kk].z ^ sg,
+                                        qv[rr][kk].w ^ sg);
+            }
         }
         m[rr] = kNegBig;
+        cm[rr] = c * kNegBig;
         l[rr] = 0.f;
 #pragma unroll
         for (int nn = 0; nn < NN; ++nn) o[rr][nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -496,6 +535,9 @@ void paged_multi_tiled_kernel(MultiArgs a) {
         }
     };
     auto lstore = [&](int buf, int jb0, const uint4 (&kc)[KB][CPT], const uint4 (&vc)[KB][CPT]) {
+        // rows past the partition are zeroed (weight 0 times NaN would not be
+        // 0); only the step that reaches the partition end has such rows
+        const bool tail = (jb0 + KB) * kBlockSize > t_end;  // uniform
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -503,15 +545,13 @@ void paged_multi_tiled_kernel(MultiArgs a) {
                 const int ch = cc * kThreads + tid;
                 if (ch < CH) {
                     const int tok = ch / (ROW / 16), off = (ch % (ROW / 16)) * 16;
-                    // rows past the partition are zeroed: weight 0 times NaN would not be 0
-                    const bool keep = (jb0 + kb) * kBlockSize + tok < t_end;
-                    const uint4 kx = kc[kb][cc], vx = vc[kb][cc];
-                    *reinterpret_cast<uint4*>(s_k[buf][kb] + tok * LS + off) =
-                        make_uint4(keep ? kx.x : 0u, keep ? kx.y : 0u, keep ? kx.z : 0u,
-                                   keep ? kx.w : 0u);
-                    *reinterpret_cast<uint4*>(s_v[buf][kb] + tok * LSV + off) =
-                        make_uint4(keep ? vx.x : 0u, keep ? vx.y : 0u, keep ? vx.z : 0u,
-                                   keep ? vx.w : 0u);
+                    uint4 kx = kc[kb][cc], vx = vc[kb][cc];
+                    if (tail && (jb0 + kb) * kBlockSize + tok >= t_end) {
+                        kx = make_uint4(0u, 0u, 0u, 0u);
+                        vx = kx;
+                    }
+                    *reinterpret_cast<uint4*>(s_k[buf][kb] + tok * LS + off) = kx;
+                    *reinterpret_cast<uint4*>(s_v[buf][kb] + tok * LSV + off) = vx;
                 }
             }
         }
@@ -565,7 +605,7 @@ void paged_multi_tiled_kernel(MultiArgs a) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sv[kb][i] = s[rr][kb][i] * c;
+                for (int i = 0; i < 4; ++i) sv[kb][i] = s[rr][kb][i];
             if (!full) {
                 // a lane's tokens lie below t_lim: its row's position + 1 and the partition end
                 const int t_lim = row_ok[rr] ? min(t_end, pos[rr] + 1) : 0;
@@ -584,13 +624,13 @@ void paged_multi_tiled_kernel(MultiArgs a) {
             // The running max m is shared by a query's 4 lanes; the exact
             // cross-lane max is needed only when some score exceeds it, and
             // then acc is rescaled (otherwise alpha is 1).
-            float mn = m[rr];
             if (__builtin_amdgcn_ballot_w64(mx > m[rr]) != 0) {
                 mx = fmaxf(mx, __shfl_xor(mx, 16));
                 mx = fmaxf(mx, __shfl_xor(mx, 32));
-                mn = fmaxf(m[rr], mx);
-                const float alpha = fast_exp2(m[rr] - mn);
+                const float mn = fmaxf(m[rr], mx);
+                const float alpha = fast_exp2((m[rr] - mn) * c);
                 m[rr] = mn;
+                cm[rr] = c * mn;
                 l[rr] *= alpha;
 #pragma unroll
                 for (int nn = 0; nn < NN; ++nn) o[rr][nn] *= alpha;
@@ -604,7 +644,7 @@ void paged_multi_tiled_kernel(MultiArgs a) {
                 float p[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    p[i] = fast_exp2(sv[kb][i] - mn);
+                    p[i] = fast_exp2(fmaf(sv[kb][i], c, -cm[rr]));
                     ps += p[i];
                 }
                 pb[kb] = make_uint2(Mfma<T>::pack(p[0], p[1]), Mfma<T>::pack(p[2], p[3]));
@@ -688,7 +728,7 @@ void paged_multi_tiled_kernel(MultiArgs a) {
             }
         }
         if (!direct_out && grp == 0) {
-            a.m_part[pi] = m[rr] * kLn2;
+            a.m_part[pi] = cm[rr] * kLn2;
             a.l_part[pi] = l[rr];
         }
     }

@@ -29,7 +29,7 @@ def pkv():
     return m
 
 
-def _run(pkv, dtype, D, Hq, Hkv, lens, qlens, P=0, seed=0):
+def _run(pkv, dtype, D, Hq, Hkv, lens, qlens, P=0, seed=0, scale=None):
     cfg = dict(B=len(lens), ctx=list(lens), Hq=Hq, Hkv=Hkv, D=D, dtype=dtype, cache=dtype,
                pool=None, seed=seed, max_ctx=max(max(lens), 16))
     batch = W.make_batch(cfg=cfg, device="cuda")
@@ -37,12 +37,13 @@ def _run(pkv, dtype, D, Hq, Hkv, lens, qlens, P=0, seed=0):
     q = W.token_rows(T, Hq, D, dtype, seed, W.S_STEP_Q).cuda()
     qsl = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
     view = OracleView(batch, np.arange(batch.B))
+    scale = batch.scale if scale is None else scale
     out = pkv.paged_attn_multi(q, batch.k_cache, batch.v_cache, batch.block_tables,
-                               batch.context_lens, torch.from_numpy(qsl).cuda(), batch.scale,
+                               batch.context_lens, torch.from_numpy(qsl).cuda(), scale,
                                max(qlens), partition_size=P)
     torch.cuda.synchronize()
     ref = oracle.paged_multi(host(q), dtype, view.k_cache, view.v_cache, dtype,
-                             view.block_tables, view.context_lens, qsl, batch.scale)
+                             view.block_tables, view.context_lens, qsl, scale)
     vmax = float(np.nanmax(np.abs(as_f64(batch.v_cache).reshape(-1)[
         np.isfinite(as_f64(batch.v_cache).reshape(-1))])))
     tol = TOL[dtype] + U_P[dtype] * vmax
@@ -129,3 +130,14 @@ def test_multi_prefill_chunks(pkv, D):
     lens = [1000, 300, 777]
     qlens = [300, 300, 129]
     _run(pkv, "f16", D, 8, 4, lens, qlens, seed=D)
+
+
+@pytest.mark.parametrize("scale", [-0.088388346, 0.0])
+@pytest.mark.parametrize("qlens", [[300, 129, 64], [3, 8, 1]])
+@pytest.mark.parametrize("P", [0, 256])
+def test_multi_negative_and_zero_scale(pkv, scale, qlens, P):
+    """The scale is any fp32 value: a negative one reverses the order of the
+    scores (the softmax then favours the smallest q . k), zero gives the
+    plain mean of V over each query's positions.  Long query runs (the tiled
+    kernel) and short ones, whole and split contexts."""
+    _run(pkv, "f16", 128, 8, 4, [1000, 300, 777], qlens, P=P, seed=7, scale=scale)
