@@ -57,6 +57,10 @@ constexpr float kNegBig = -3.0e38f;
 constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer access
 constexpr int kNonTemporal = 2;
 constexpr unsigned kXcds = 8;              // accelerator complex dies of the chip
+// s_waitcnt immediate that waits for at most n outstanding vector memory
+// operations and for nothing else (gfx9 layout: vmcnt in bits 3:0 and 15:14,
+// expcnt 6:4, lgkmcnt 11:8)
+constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 template <Elem T> struct Mfma;
 template <> struct Mfma<Elem::F16> {
@@ -106,10 +110,12 @@ __device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, int off) {
     const u32x4_v v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
-// cached load: blocks that several work-groups of a sequence read
-__device__ __forceinline__ uint4 ld16_cached(__amdgpu_buffer_rsrc_t r, int off) {
-    const u32x4_v v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-    return make_uint4(v.x, v.y, v.z, v.w);
+// 16 bytes per lane from the buffer straight into LDS: lane l's land at
+// lds + 16 l (lds is wave-uniform); bytes outside the buffer window arrive
+// as zeros.  Counted by vmcnt, like any vector memory load.
+__device__ __forceinline__ void load_to_lds16(__amdgpu_buffer_rsrc_t r, char* lds, int voffset) {
+    typedef __attribute__((address_space(3))) void lds_void;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voffset, 0, 0, 0);
 }
 
 template <Elem T, int D>
@@ -364,24 +370,25 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
 // lane 16 G + col receives channel 16 nn + col of tokens 4 G .. 4 G + 3:
 // one read per block and 16 channels.  Each wave owns its rows for the whole
 // partition, so there is no merge between waves.
-template <Elem T, int D, int RW>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+template <Elem T, int D, int RW, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void paged_multi_tiled_kernel(MultiArgs a) {
     constexpr int KK = D / 32;
     constexpr int NN = D / 16;
     constexpr int KB = D <= 128 ? 2 : 1;            // 16-token blocks per softmax step
     constexpr int ROW = D * 2;
     constexpr int TILE = kRows * ROW;
-    constexpr int LS = ROW + 16;                    // padded LDS row stride (K)
-    // V row stride: the 16 lanes of a transpose read address 4 tokens x 4
-    // channel quads; rows 8 words apart mod 64 put them on distinct banks
-    constexpr int LSV = ROW + 32;
-    constexpr int CH = TILE / 16;                   // 16-byte chunks per tile
-    constexpr int CPT = (CH + kThreads - 1) / kThreads;
-    constexpr int WG_ROWS = kWaves * kRows * RW;
+    constexpr int SUBS = TILE / 1024;               // 1 KiB wave loads per tile
+    constexpr int IPW = 2 * KB * SUBS / NW;         // wave loads per step and wave
+    static_assert((2 * KB * SUBS) % NW == 0, "the loads of a step split evenly over the waves");
+    constexpr int STAGE = 2 * KB * TILE;            // the K tiles, then the V tiles, of one step
+    constexpr int WG_ROWS = NW * kRows * RW;
 
-    __shared__ __attribute__((aligned(16))) char s_k[2][KB][kRows * LS];
-    __shared__ __attribute__((aligned(16))) char s_v[2][KB][kRows * LSV];
+    // three stages: the step being computed, the next one (loads landed or
+    // landing), the one after (loads issued at the top of this step)
+    __shared__ __attribute__((aligned(16))) char s_b0[STAGE];
+    __shared__ __attribute__((aligned(16))) char s_b1[STAGE];
+    __shared__ __attribute__((aligned(16))) char s_b2[STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -414,7 +421,7 @@ void paged_multi_tiled_kernel(MultiArgs a) {
     // work-groups dispatched last are the shortest and the ragged tail of
     // the launch is small.  Every work-group ranks the sequences itself
     // (one per thread, in LDS).
-    static_assert(kThreads <= kScheduleMaxSeqs, "one LDS key per thread");
+    static_assert(NW * 64 >= kScheduleMaxSeqs, "one thread per ranked sequence");
     __shared__ int s_key[kScheduleMaxSeqs];
     __shared__ int s_order[kScheduleMaxSeqs];
     int b = rest / a.num_kv_heads;
@@ -426,7 +433,7 @@ void paged_multi_tiled_kernel(MultiArgs a) {
             const int c = partition_count(nn, a.partition_size);
             key = c > 0 ? partition_span(nn, c) : 0;
         }
-        s_key[tid] = key;
+        if (tid < kScheduleMaxSeqs) s_key[tid] = key;
         __syncthreads();
         if (tid < a.num_seqs) {
             int r = 0;
@@ -508,55 +515,62 @@ void paged_multi_tiled_kernel(MultiArgs a) {
         for (int nn = 0; nn < NN; ++nn) o[rr][nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    // KB blocks starting at jb0: one 16-byte chunk (or two) per thread per
-    // tile; a block past the run reads zeros from an empty buffer window
-    struct Stage {
-        uint4 k[KB][CPT], v[KB][CPT];
+    // LDS tiles are token rows of ROW bytes without padding.  The 16-byte
+    // chunk c of token t's row sits in chunk slot c ^ swz(t) of that row:
+    // the 16 lanes that read one K operand chunk of tokens 0..15 then hit 16
+    // different bank groups, and so do the 32 lanes of a transpose read (8
+    // tokens x 2 chunks).  Rows of 128 bytes pair up in one 256-byte bank
+    // line, so swz permutes t / 2 there.
+    auto swz = [](int t) {
+        return ROW == 128 ? 2 * ((t >> 1) & 3) | (t >> 3) : 2 * (t & 7) | (t >> 3);
     };
-    auto block_id = [&](int jb) { return jb < blk_stop ? table[jb] : -1; };
-    auto gload = [&](const int (&ids)[KB], uint4 (&kc)[KB][CPT], uint4 (&vc)[KB][CPT]) {
+    // this lane's LDS offsets inside a tile: the K operand (token col,
+    // channels 32 kk + 8 grp .. + 7) and the address it gives the V^T
+    // transpose read (token 4 grp + (lane / 4) % 4, channels 16 nn + 4 (lane
+    // % 4) .. + 3: in each 16-lane group, lane 16 G + 4 a + c receives as its
+    // element e element c of what lane 16 G + a + 4 e addresses)
+    int k_off[KK], v_off[NN];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            const int phys = ids[kb];
+    for (int kk = 0; kk < KK; ++kk) k_off[kk] = col * ROW + 16 * ((kk * 4 + grp) ^ swz(col));
+    {
+        const int tv = 4 * grp + ((lane >> 2) & 3), qa = lane & 3;
+#pragma unroll
+        for (int nn = 0; nn < NN; ++nn)
+            v_off[nn] = tv * ROW + 16 * ((2 * nn + (qa >> 1)) ^ swz(tv)) + 8 * (qa & 1);
+    }
+
+    // Loads of the KB blocks from jb0 on, straight from the pool into the LDS
+    // stage dst: 2 KB tiles of 1 KiB wave loads, IPW per wave.  Lane l of a
+    // wave load fills bytes 16 l .. 16 l + 15 of its kilobyte, so it fetches
+    // the chunk that the swizzle puts there.  The buffer window ends at the
+    // partition end: rows past it (and a block past the run, or a bad block
+    // id) arrive as zeros, so no score or weight meets a stale or NaN value.
+    const __attribute__((address_space(4))) int32_t* table_c =
+        (const __attribute__((address_space(4))) int32_t*)table;
+    auto issue = [&](char* dst, int jb0) {
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+            const int u = wave * IPW + i;            // wave-uniform
+            const int tt = u / SUBS, r = u % SUBS;   // tile (K tiles first), kilobyte
+            const int jb = jb0 + tt % KB;
+            // a scalar load (constant address space: the table is not written
+            // here), so that waiting for it never waits for the K/V loads
+            const int id = table_c[min(jb, blk_stop - 1)];
+            const int phys = jb < blk_stop ? id : -1;
             const bool ok = phys >= 0 && (int64_t)phys < a.num_blocks;
+            // wave-uniform by construction; said so, or the descriptor is
+            // built in vector registers and the load wrapped in a loop
+            const int rows =
+                __builtin_amdgcn_readfirstlane(ok ? min(max(t_end - jb * kBlockSize, 0), kRows) : 0);
             const size_t tile = (size_t)(ok ? phys : 0) * a.num_kv_heads + kvh;
-            const int bytes = ok ? TILE : 0;
-            const __amdgpu_buffer_rsrc_t kr =
-                rsrc(static_cast<const char*>(a.k_cache) + tile * TILE, bytes);
-            const __amdgpu_buffer_rsrc_t vr =
-                rsrc(static_cast<const char*>(a.v_cache) + tile * TILE, bytes);
-#pragma unroll
-            for (int cc = 0; cc < CPT; ++cc) {
-                const int ch = cc * kThreads + tid;
-                const int off = ch < CH ? ch * 16 : TILE;   // past the tile: reads zeros
-                kc[kb][cc] = ld16_cached(kr, off);
-                vc[kb][cc] = ld16_cached(vr, off);
-            }
+            const char* pool = static_cast<const char*>(tt < KB ? a.k_cache : a.v_cache);
+            const __amdgpu_buffer_rsrc_t rs = rsrc(pool + tile * TILE, rows * ROW);
+            const int at = r * 1024 + lane * 16;
+            const int t = at / ROW, slot = (at % ROW) / 16;
+            load_to_lds16(rs, dst + tt * TILE + r * 1024, t * ROW + 16 * (slot ^ swz(t)));
         }
     };
-    auto lstore = [&](int buf, int jb0, const uint4 (&kc)[KB][CPT], const uint4 (&vc)[KB][CPT]) {
-        // rows past the partition are zeroed (weight 0 times NaN would not be
-        // 0); only the step that reaches the partition end has such rows
-        const bool tail = (jb0 + KB) * kBlockSize > t_end;  // uniform
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-            for (int cc = 0; cc < CPT; ++cc) {
-                const int ch = cc * kThreads + tid;
-                if (ch < CH) {
-                    const int tok = ch / (ROW / 16), off = (ch % (ROW / 16)) * 16;
-                    uint4 kx = kc[kb][cc], vx = vc[kb][cc];
-                    if (tail && (jb0 + kb) * kBlockSize + tok >= t_end) {
-                        kx = make_uint4(0u, 0u, 0u, 0u);
-                        vx = kx;
-                    }
-                    *reinterpret_cast<uint4*>(s_k[buf][kb] + tok * LS + off) = kx;
-                    *reinterpret_cast<uint4*>(s_v[buf][kb] + tok * LSV + off) = vx;
-                }
-            }
-        }
-    };
-    auto compute = [&](int buf, int jb0) {
+    auto compute = [&](const char* buf, int jb0) {
         // 1. scores of every row tile: S^T[token 4 grp + i][query col]
         f32x4_t s[RW][KB];
         {
@@ -565,8 +579,7 @@ void paged_multi_tiled_kernel(MultiArgs a) {
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk)
-                    ka[kb][kk] = *reinterpret_cast<const uint4*>(s_k[buf][kb] + col * LS +
-                                                                 (kk * 32 + grp * 8) * 2);
+                    ka[kb][kk] = *reinterpret_cast<const uint4*>(buf + kb * TILE + k_off[kk]);
 #pragma unroll
             for (int rr = 0; rr < RW; ++rr)
 #pragma unroll
@@ -577,11 +590,8 @@ void paged_multi_tiled_kernel(MultiArgs a) {
                         s[rr][kb] = Mfma<T>::qk(ka[kb][kk], qv[rr][kk], s[rr][kb]);
                 }
         }
-        // V^T operands of the step, read once for every row tile.  In each
-        // 16-lane group the lane addresses token 4 grp + (lane / 4) % 4,
-        // channels 4 (lane % 4) .. + 3 of each 16; it receives channel
-        // 16 nn + col of tokens 4 grp .. 4 grp + 3.
-        const int v_off = (4 * grp + ((lane >> 2) & 3)) * LSV + (lane & 3) * 8;
+        // V^T operands of the step, read once for every row tile (the lane
+        // receives channel 16 nn + col of tokens 4 grp .. 4 grp + 3)
         uint2 vw[NN][KB];
 #pragma unroll
         for (int nn = 0; nn < NN; ++nn)
@@ -589,7 +599,7 @@ void paged_multi_tiled_kernel(MultiArgs a) {
             for (int kb = 0; kb < KB; ++kb) {
                 typedef __attribute__((address_space(3))) s16x4_v lds_s16x4;
                 const s16x4_v t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4*)(s_v[buf][kb] + v_off + nn * 32));
+                    (lds_s16x4*)(buf + (KB + kb) * TILE + v_off[nn]));
                 vw[nn][kb] = __builtin_bit_cast(uint2, t);
             }
         // 2. per row tile: online softmax over the step's KB * 16 tokens, then
@@ -666,39 +676,29 @@ void paged_multi_tiled_kernel(MultiArgs a) {
         }
     };
 
-    // Steps of KB blocks; global loads run two steps ahead of the step being
-    // computed (register sets A and B alternate), LDS holds the current and
-    // the next step, block ids are fetched a step before their loads.
+    // Steps of KB blocks over three LDS stages, loads two steps ahead.  At
+    // the top of a step a wave waits for its own loads of the step (the next
+    // step's IPW may still run); after the barrier every wave's have landed
+    // and no wave still reads the stage of the step before, which then takes
+    // the loads of two steps on.  A plain s_barrier: a fence would also wait
+    // for those newer loads.  Past the run the loads fetch zeros.
     const int n_steps = (blk_stop - blk_begin + KB - 1) / KB;
     if (n_steps > 0) {
-        Stage A, B;
-        int ids[KB];
-        auto fetch_ids = [&](int step) {
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) ids[kb] = block_id(blk_begin + step * KB + kb);
+        issue(s_b0, blk_begin);
+        issue(s_b1, blk_begin + KB);
+        auto step = [&](const char* cur, char* nxt, int st) {
+            __builtin_amdgcn_s_waitcnt(vmcnt_only(IPW));
+            __builtin_amdgcn_s_barrier();
+            issue(nxt, blk_begin + (st + 2) * KB);
+            compute(cur, blk_begin + st * KB);
         };
-        fetch_ids(0);
-        gload(ids, A.k, A.v);
-        fetch_ids(1);
-        gload(ids, B.k, B.v);
-        fetch_ids(2);
-        lstore(0, blk_begin, A.k, A.v);
-        __syncthreads();
-        for (int st = 0; st < n_steps; st += 2) {
-            const int jb = blk_begin + st * KB;
-            gload(ids, A.k, A.v);                       // step st + 2
-            fetch_ids(st + 3);
-            compute(0, jb);
-            lstore(1, jb + KB, B.k, B.v);               // step st + 1 (zeros past the run)
-            __syncthreads();
-            if (st + 1 < n_steps) {
-                gload(ids, B.k, B.v);                   // step st + 3
-                fetch_ids(st + 4);
-                compute(1, jb + KB);
-                lstore(0, jb + 2 * KB, A.k, A.v);       // step st + 2
-                __syncthreads();
-            }
+        for (int st = 0; st < n_steps; st += 3) {
+            step(s_b0, s_b2, st);
+            if (st + 1 < n_steps) step(s_b1, s_b0, st + 1);
+            if (st + 2 < n_steps) step(s_b2, s_b1, st + 2);
         }
+        // no load may still write this work-group's LDS when its waves end
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
     }
 
     // ---- epilogue: each lane writes 4 consecutive channels of its own row --
@@ -734,7 +734,8 @@ void paged_multi_tiled_kernel(MultiArgs a) {
     }
 }
 
-constexpr int kTiledRW = 2;                 // row tiles per wave in the tiled kernel
+constexpr int kTiledRW = 1;                 // row tiles per wave in the tiled kernel
+constexpr int kTiledWaves = 8;              // waves per work-group of the tiled kernel
 constexpr int kTiledMinRows = 64;           // rows per (sequence, kv head) that select it
 
 template <Elem T>
@@ -751,11 +752,11 @@ hipError_t launch_d(const MultiArgs& a, int d, int64_t grid, hipStream_t s) {
 
 template <Elem T>
 hipError_t launch_tiled(const MultiArgs& a, int d, int64_t grid, hipStream_t s) {
-    const dim3 g((unsigned)grid), blk(kThreads);
+    const dim3 g((unsigned)grid), blk(kTiledWaves * 64);
     switch (d) {
-    case 64: hipLaunchKernelGGL((paged_multi_tiled_kernel<T, 64, kTiledRW>), g, blk, 0, s, a); break;
-    case 128: hipLaunchKernelGGL((paged_multi_tiled_kernel<T, 128, kTiledRW>), g, blk, 0, s, a); break;
-    case 256: hipLaunchKernelGGL((paged_multi_tiled_kernel<T, 256, 1>), g, blk, 0, s, a); break;
+    case 64: hipLaunchKernelGGL((paged_multi_tiled_kernel<T, 64, kTiledRW, kTiledWaves>), g, blk, 0, s, a); break;
+    case 128: hipLaunchKernelGGL((paged_multi_tiled_kernel<T, 128, kTiledRW, kTiledWaves>), g, blk, 0, s, a); break;
+    case 256: hipLaunchKernelGGL((paged_multi_tiled_kernel<T, 256, 1, kTiledWaves>), g, blk, 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -766,7 +767,7 @@ hipError_t launch_tiled(const MultiArgs& a, int d, int64_t grid, hipStream_t s) 
 int64_t multi_row_groups(int max_rows, int head_dim) {
     if (max_rows < kTiledMinRows) return (max_rows + kRows - 1) / kRows;
     const int rw = head_dim == 256 ? 1 : kTiledRW;
-    const int per = kWaves * kRows * rw;
+    const int per = kTiledWaves * kRows * rw;
     return (max_rows + per - 1) / per;
 }
 
