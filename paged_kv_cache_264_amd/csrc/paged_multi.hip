@@ -125,7 +125,10 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
     constexpr int VL = D / 32;          // 16-byte V loads per lane per block
     constexpr int ROW = D * 2;          // bytes per token row
     constexpr int TILE = kRows * ROW;   // bytes per (block, kv head) tile
-    constexpr int VS = ROW + 16;        // LDS row stride of the staged V tile
+    // LDS row stride of the staged V tile: the 16 lanes of a transpose read
+    // address 4 tokens x 4 channel quads; rows 8 words apart (mod 64) put
+    // them on distinct banks
+    constexpr int VS = ROW + 32;
 
     // LDS: the per-wave V stage during the loop, then (same bytes) the output
     // tiles of waves 1..3 for the final merge
@@ -176,6 +179,12 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
     const int hq = kvh * g + (row_ok ? R % g : 0);
     const int pos = n - qlen + jq;      // the query attends to positions 0..pos
 
+    // Scores stay in raw units (q . k); the softmax works on c * s with
+    // c = scale * log2(e), applied inside the exponent by one FMA.  A
+    // negative scale is taken as |scale| on negated queries (exact), and c
+    // is kept above zero so that a masked score (-inf) still gives weight 0.
+    const bool neg_scale = a.scale_log2 < 0.f;
+    const float c = fmaxf(fabsf(a.scale_log2), 1.17549435e-38f);
     uint4 qv[KK];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
@@ -184,9 +193,13 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
             qv[kk] = *reinterpret_cast<const uint4*>(
                 static_cast<const char*>(a.q) +
                 (((size_t)(q0 + jq) * Hq + hq) * D + kk * 32 + grp * 8) * 2);
+        if (neg_scale) {
+            const uint32_t sg = 0x80008000u;  // sign bits of both 16-bit elements
+            qv[kk] = make_uint4(qv[kk].x ^ sg, qv[kk].y ^ sg, qv[kk].z ^ sg, qv[kk].w ^ sg);
+        }
     }
 
-    float m = kNegBig, l = 0.f;
+    float m = kNegBig, cm = c * kNegBig, l = 0.f;  // max of raw scores, c times it, sum
     f32x4_t o[NN];
 #pragma unroll
     for (int nn = 0; nn < NN; ++nn) o[nn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -199,8 +212,15 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
     const int my0 = blk_begin + wave * per_wave;
     const int n_my = max(0, min(per_wave, blk_end - my0));
     const int32_t* table = a.block_tables + (size_t)b * a.max_blocks_per_seq;
-    const float c = a.scale_log2;
     char* vst = s_buf + wave * kRows * VS;
+    // the last position any row of this tile attends to, and the first
+    const int pos_min = n - qlen + min(rt * kRows, rows_total - 1) / g;
+    // the address this lane gives the V^T transpose read: token 4 grp +
+    // (lane / 4) % 4, channels 4 (lane % 4) .. + 3 of each 16 (in each
+    // 16-lane group, lane 16 G + 4 a + c receives as its element e element c
+    // of what lane 16 G + a + 4 e addresses, so lane 16 grp + col receives
+    // channel 16 nn + col of tokens 4 grp .. 4 grp + 3)
+    const int v_off = (4 * grp + ((lane >> 2) & 3)) * VS + (lane & 3) * 8;
 
     struct Regs {
         uint4 k[KK], v[VL];
@@ -225,15 +245,20 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
         f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) s = Mfma<T>::qk(r.k[kk], qv[kk], s);
-        float sv[4];
+        float sv[4] = {s[0], s[1], s[2], s[3]};
+        // masks only where the block reaches the partition end or the causal
+        // diagonal of some row of the tile (uniform test)
+        const int t_hi = (r.jb + 1) * kBlockSize;
+        const bool full = r.ok && t_hi <= t_end && t_hi <= pos_min + 1;
+        if (!full) {
+            const int t_lim = (r.ok && row_ok) ? min(t_end, pos + 1) : 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                sv[i] = r.jb * kBlockSize + grp * 4 + i < t_lim ? sv[i] : -INFINITY;
+        }
         float mx = kNegBig;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = r.jb * kBlockSize + grp * 4 + i;
-            const bool valid = r.ok && row_ok && t < t_end && t <= pos;
-            sv[i] = valid ? s[i] * c : -INFINITY;
-            mx = fmaxf(mx, sv[i]);
-        }
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sv[i]);
         // shared running max, reduced across the query's 4 lanes only when
         // some score exceeds it; l is this lane's share of the sum
         const bool grew = __builtin_amdgcn_ballot_w64(mx > m) != 0;
@@ -242,41 +267,41 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
             const float mn = fmaxf(m, mx);
-            alpha = fast_exp2(m - mn);
+            alpha = fast_exp2((m - mn) * c);
             m = mn;
+            cm = c * mn;
         }
         float p[4], ps = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            p[i] = fast_exp2(sv[i] - m);
+            p[i] = fast_exp2(fmaf(sv[i], c, -cm));
             ps += p[i];
         }
         l = fmaf(l, alpha, ps);
         // stage V (natural layout) in this wave's LDS tile; rows past the
         // partition are zeroed (their weight is 0, but 0 * NaN would not be)
+        const bool tail = t_hi > t_end;  // uniform
 #pragma unroll
         for (int u = 0; u < VL; ++u) {
             const int ch = u * 64 + lane;                  // 16-byte chunk of the tile
             const int tok = ch / (D / 8), d0 = (ch % (D / 8)) * 8;
-            const bool keep = r.jb * kBlockSize + tok < t_end;
-            const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-            const uint4 v = r.v[u];
-            *reinterpret_cast<uint4*>(vst + tok * VS + d0 * 2) =
-                make_uint4(keep ? v.x : z.x, keep ? v.y : z.y, keep ? v.z : z.z, keep ? v.w : z.w);
+            uint4 v = r.v[u];
+            if (tail && r.jb * kBlockSize + tok >= t_end) v = make_uint4(0u, 0u, 0u, 0u);
+            *reinterpret_cast<uint4*>(vst + tok * VS + d0 * 2) = v;
         }
         __asm__ volatile("" ::: "memory");
         const uint2 pa = make_uint2(Mfma<T>::pack(p[0], p[1]), Mfma<T>::pack(p[2], p[3]));
+        if (grew) {
+#pragma unroll
+            for (int nn = 0; nn < NN; ++nn) o[nn] *= alpha;
+        }
 #pragma unroll
         for (int nn = 0; nn < NN; ++nn) {
-            const char* base = vst + (grp * 4) * VS + (nn * 16 + col) * 2;
-            const uint32_t v0 = *reinterpret_cast<const uint16_t*>(base);
-            const uint32_t v1 = *reinterpret_cast<const uint16_t*>(base + VS);
-            const uint32_t v2 = *reinterpret_cast<const uint16_t*>(base + 2 * VS);
-            const uint32_t v3 = *reinterpret_cast<const uint16_t*>(base + 3 * VS);
-            const uint2 vb = make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
+            typedef __attribute__((address_space(3))) s16x4_v lds_s16x4;
+            const s16x4_v vt =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vst + v_off + nn * 32));
             // O^T = V^T P^T: the accumulator column is the lane's own query
-            if (grew) o[nn] *= alpha;
-            o[nn] = Mfma<T>::pv(vb, pa, o[nn]);
+            o[nn] = Mfma<T>::pv(__builtin_bit_cast(uint2, vt), pa, o[nn]);
         }
         __asm__ volatile("" ::: "memory");
     };
@@ -298,7 +323,7 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
     __syncthreads();  // every wave is done with its V stage
     float* s_o = reinterpret_cast<float*>(s_buf);  // [wave - 1][query][D]
     if (grp == 0) {
-        s_m[wave][col] = m;
+        s_m[wave][col] = cm;  // in log2 units
         s_l[wave][col] = l;
     }
     if (wave > 0) {
