@@ -261,6 +261,8 @@ def main():
         "kv_tokens_per_s": round(kv_tokens / (ms_per_step * 1e-3), 1),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "decode_kernel_us": round(dec_avg_ms * 1e3, 2),
+        "decode_kernel_us_p10_p50_p90": [round(float(np.percentile(dec_ms, q)) * 1e3, 2)
+                                         for q in (10, 50, 90)],
         "decode_alg_bytes": dec_bytes,
         "launch_alg_bytes": launch_bytes,
         "step_alg_bytes": step_bytes,
@@ -347,7 +349,8 @@ def bench_multi(args):
     t1 = time.perf_counter()
     assert torch.isfinite(out.float()).all()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    k_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    k_list = [e0.elapsed_time(e1) for e0, e1 in evs]
+    k_ms = float(np.mean(k_list))
     hbm = launch_bytes / (k_ms * 1e-3) / 1e9
     tflops = flops / (k_ms * 1e-3) / 1e12
     ridge = 2500.0 / HBM_PEAK_GBS * 1e3          # flop per byte where fp16 MFMA meets HBM
@@ -373,6 +376,8 @@ def bench_multi(args):
                    "step": "kv_cache_write of the query tokens + multi-query attention"},
         "query_tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
         "multi_kernel_us": round(k_ms * 1e3, 2),
+        "multi_kernel_us_p10_p50_p90": [round(float(np.percentile(k_list, q)) * 1e3, 2)
+                                        for q in (10, 50, 90)],
         "kernel_hbm_gbs": round(hbm, 1), "kernel_tflops": round(tflops, 2),
         "launch_alg_bytes": launch_bytes, "launch_flops": flops,
         "roofline": roof,
