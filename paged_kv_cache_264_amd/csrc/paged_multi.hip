@@ -129,10 +129,13 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
     // address 4 tokens x 4 channel quads; rows 8 words apart (mod 64) put
     // them on distinct banks
     constexpr int VS = ROW + 32;
+    // LDS row stride of the staged K tile: 16 lanes reading 16 bytes of 16
+    // token rows fall on distinct banks
+    constexpr int KS = ROW + 16;
 
-    // LDS: the per-wave V stage during the loop, then (same bytes) the output
-    // tiles of waves 1..3 for the final merge
-    constexpr int kStage = kWaves * kRows * VS;
+    // LDS: the per-wave K and V stages during the loop, then (same bytes) the
+    // output tiles of waves 1..3 for the final merge
+    constexpr int kStage = kWaves * kRows * (VS + KS);
     constexpr int kMerge = (kWaves - 1) * kRows * D * 4;
     __shared__ __attribute__((aligned(16))) char s_buf[kStage > kMerge ? kStage : kMerge];
     __shared__ float s_m[kWaves][kRows];
@@ -213,6 +216,7 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
     const int n_my = max(0, min(per_wave, blk_end - my0));
     const int32_t* table = a.block_tables + (size_t)b * a.max_blocks_per_seq;
     char* vst = s_buf + wave * kRows * VS;
+    char* kst = s_buf + kWaves * kRows * VS + wave * kRows * KS;
     // the last position any row of this tile attends to, and the first
     const int pos_min = n - qlen + min(rt * kRows, rows_total - 1) / g;
     // the address this lane gives the V^T transpose read: token 4 grp +
@@ -223,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
     const int v_off = (4 * grp + ((lane >> 2) & 3)) * VS + (lane & 3) * 8;
 
     struct Regs {
-        uint4 k[KK], v[VL];
+        uint4 k[VL], v[VL];
         int jb;
         bool ok;
     };
@@ -235,16 +239,28 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
         const int bytes = r.ok ? TILE : 0;
         const __amdgpu_buffer_rsrc_t kr = rsrc(static_cast<const char*>(a.k_cache) + tile * TILE, bytes);
         const __amdgpu_buffer_rsrc_t vr = rsrc(static_cast<const char*>(a.v_cache) + tile * TILE, bytes);
+        // both tiles in token order, 1 KiB per wave load (the MFMA operand
+        // order, 16 rows x 64 bytes per load, streams less well from HBM)
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) r.k[kk] = ld16(kr, col * ROW + (kk * 32 + grp * 8) * 2);
+        for (int u = 0; u < VL; ++u) r.k[u] = ld16(kr, (u * 64 + lane) * 16);
 #pragma unroll
         for (int u = 0; u < VL; ++u) r.v[u] = ld16(vr, (u * 64 + lane) * 16);
     };
     auto compute = [&](const Regs& r) {
+        // K through this wave's LDS tile into the MFMA A operand (lane:
+        // token col, channels 32 kk + 8 grp .. + 7)
+#pragma unroll
+        for (int u = 0; u < VL; ++u) {
+            const int ch = u * 64 + lane;
+            *reinterpret_cast<uint4*>(kst + (ch / (D / 8)) * KS + (ch % (D / 8)) * 16) = r.k[u];
+        }
+        __asm__ volatile("" ::: "memory");
         // S^T[token 4*grp + i][query col]
         f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) s = Mfma<T>::qk(r.k[kk], qv[kk], s);
+        for (int kk = 0; kk < KK; ++kk)
+            s = Mfma<T>::qk(*reinterpret_cast<const uint4*>(kst + col * KS + (kk * 32 + grp * 8) * 2),
+                            qv[kk], s);
         float sv[4] = {s[0], s[1], s[2], s[3]};
         // masks only where the block reaches the partition end or the causal
         // diagonal of some row of the tile (uniform test)
