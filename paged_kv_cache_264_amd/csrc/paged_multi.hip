@@ -557,13 +557,15 @@ void paged_multi_tiled_kernel(MultiArgs a) {
     }
 
     // LDS tiles are token rows of ROW bytes without padding.  The 16-byte
-    // chunk c of token t's row sits in chunk slot c ^ swz(t) of that row:
-    // the 16 lanes that read one K operand chunk of tokens 0..15 then hit 16
-    // different bank groups, and so do the 32 lanes of a transpose read (8
-    // tokens x 2 chunks).  Rows of 128 bytes pair up in one 256-byte bank
-    // line, so swz permutes t / 2 there.
+    // chunk c of token t's row sits in chunk slot c ^ swz(t) of that row,
+    // chosen so that every group of lanes the LDS serves together (8 lanes
+    // of a 16-byte read or 16 of an 8-byte read per 128-byte bank line, as
+    // well as twice that per 256 bytes) hits distinct banks: the K operand
+    // reads (tokens 0..15, one chunk) and the transpose reads (4 tokens x 2
+    // chunks per 16 lanes).
     auto swz = [](int t) {
-        return ROW == 128 ? 2 * ((t >> 1) & 3) | (t >> 3) : 2 * (t & 7) | (t >> 3);
+        return ROW == 128 ? ((2 * t) ^ (3 * (t >> 2))) & 7
+                          : 2 * (t & 7) + (((t & 7) >> 2) ^ (t >> 3));
     };
     // this lane's LDS offsets inside a tile: the K operand (token col,
     // channels 32 kk + 8 grp .. + 7) and the address it gives the V^T
