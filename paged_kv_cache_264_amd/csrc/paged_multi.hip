@@ -18,16 +18,17 @@
 //     tile; a work-group is one (sequence, kv head, row tile, partition) with
 //     4 waves, each streaming a contiguous run of the partition's blocks.
 //   * scores: S^T = K Q^T, one v_mfma_f32_16x16x32 per 32 channels.  The A
-//     operand is the K tile itself (lane l: token l%16, 8 channels), loaded
-//     straight from the pool with raw buffer loads; the B operand is Q,
-//     loaded once.  The C layout puts a query's 16 scores in the 4 lanes
-//     l%16 = query, so the online-softmax max / sum need two lane swaps.
+//     operand is the K tile (lane l: token l%16, 8 channels), fetched from
+//     the pool in token order and staged in a per-wave LDS tile; the B
+//     operand is Q, loaded once.  The C layout puts a query's 16 scores in
+//     the 4 lanes l%16 = query, so the online-softmax max / sum need two
+//     lane swaps.
 //   * the output is accumulated transposed, O^T = V^T P^T, on
 //     v_mfma_f32_16x16x16: the score C layout is then the B operand as it
 //     stands (P never leaves registers) and the accumulator column of a lane
-//     is its own query, so rescaling needs no lane exchange.  V is staged in a
-//     per-wave LDS tile (row stride 2D + 16 bytes: the 4 lane groups of a
-//     transposed read fall on different banks) and read back as the A operand.
+//     is its own query, so rescaling needs no lane exchange.  V is staged in
+//     a per-wave LDS tile in token order and read back as the V^T operand by
+//     the LDS transpose read (see the long-run kernel below).
 //   * the running max is shared by the 4 lanes of a query and reduced across
 //     them only when a score exceeds it; each lane sums its own tokens and
 //     the 4 partial sums are added once at the end.
@@ -394,13 +395,13 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
     }
 }
 
-// Long runs of queries (prefill chunks): a work-group owns 4 waves x RW row
-// tiles of 16 rows and walks every block of its partition up to the last
+// Long runs of queries (prefill chunks): a work-group owns NW waves x RW
+// row tiles of 16 rows and walks every block of its partition up to the last
 // position any of its rows attends to, two 16-token blocks per step.  Each
-// K/V block is fetched once per work-group (a 16-byte chunk per thread),
-// staged in double-buffered padded LDS tiles, and every wave reads the K and
-// V operands once per step and reuses them for its RW row tiles; one barrier
-// and one softmax update per step.  The output is accumulated transposed,
+// K/V block is fetched once per work-group, straight from the pool into one
+// of three LDS stages, and every wave reads the K and V operands once per
+// step and uses them for its RW row tiles; one barrier and one softmax
+// update per step.  The output is accumulated transposed,
 // O^T = V^T P^T: the P operand is then the score tile as it leaves the first
 // MFMA and each lane's accumulator column is its own query, so rescaling and
 // normalizing need no lane exchange.  The V^T operand comes from the
