@@ -141,3 +141,34 @@ def test_multi_negative_and_zero_scale(pkv, scale, qlens, P):
     plain mean of V over each query's positions.  Long query runs (the tiled
     kernel) and short ones, whole and split contexts."""
     _run(pkv, "f16", 128, 8, 4, [1000, 300, 777], qlens, P=P, seed=7, scale=scale)
+
+
+def test_multi_prefill_workload_sample(pkv):
+    """The chunked-prefill shape at full size (the tiled kernel as the bench
+    launches it): 16 LLaMA-7B sequences, the last 512 of U[1024, 4096]
+    positions being queries; the shortest and the longest sequence checked
+    against the oracle on every query row and head."""
+    batch = W.make_batch("prefill", device="cuda", poison=True)
+    ql = batch.cfg["q_len"]
+    lens = batch.layout.context_lens.astype(np.int64)
+    qlens = np.minimum(lens, ql)
+    qsl = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    T = int(qsl[-1])
+    q = W.token_rows(T, batch.Hq, batch.D, "f16", batch.seed, W.S_STEP_Q).cuda()
+    out = pkv.paged_attn_multi(q, batch.k_cache, batch.v_cache, batch.block_tables,
+                               batch.context_lens, torch.from_numpy(qsl).cuda(), batch.scale, ql)
+    torch.cuda.synchronize()
+    assert np.isfinite(as_f64(out)).all()
+    seqs = [int(np.argmin(lens)), int(np.argmax(lens))]
+    view = OracleView(batch, seqs)
+    rows = np.concatenate([np.arange(qsl[s], qsl[s + 1]) for s in seqs])
+    sub_qsl = np.concatenate([[0], np.cumsum(qlens[seqs])]).astype(np.int32)
+    ref = oracle.paged_multi(host(q[torch.from_numpy(rows).cuda()]), "f16", view.k_cache,
+                             view.v_cache, "f16", view.block_tables, view.context_lens, sub_qsl,
+                             batch.scale)
+    err = float(np.abs(as_f64(out)[rows] - ref).max())
+    vals = as_f64(batch.v_cache[torch.from_numpy(view.block_ids).cuda()]).reshape(-1)
+    vmax = float(np.abs(vals[np.isfinite(vals)]).max())
+    print(f"[multi prefill] seqs={seqs} lens={lens[seqs].tolist()} max_abs_err={err:.3e}",
+          flush=True)
+    assert err <= TOL["f16"] + U_P["f16"] * vmax
