@@ -272,6 +272,56 @@ int pkv_multi_default_partition_size(int num_seqs, int max_query_len, int num_q_
                                      int num_kv_heads, int max_blocks_per_seq);
 
 /*
+ * Single-query decode of groups of sequences that continue one prompt (the
+ * samples of parallel sampling or beam search share the prompt's blocks:
+ * "Efficient AI Lecture 13" notes, section "PagedAttention", on sharing
+ * between sequences of one request; docs.lazyllm.ai lesson 4, section 4.2):
+ * each shared prefix block is read once for all the group's queries instead
+ * of once per sequence.  The result is the decode of pkv_paged_attn_decode
+ * (with the new token appended when k_new / v_new are given, as
+ * pkv_paged_attn_decode_append): attention over positions
+ * 0 .. context_lens[b] - 1.  It is computed as two exact pieces merged by the
+ * online-softmax rule (caojiahao2.github.io section 3.2): the prefix
+ * 0 .. prefix_lens[b] - 1 for all queries of a group at once on the matrix
+ * cores (the group's rows of one kv head form one operand tile), and each
+ * sequence's own positions prefix_lens[b] .. context_lens[b] - 1.
+ *  group_start   [num_groups + 1] int32 on the device: the sequences of group
+ *                g are group_start[g] .. group_start[g + 1] - 1 (consecutive;
+ *                group_start[0] = 0, group_start[num_groups] = num_seqs)
+ *  prefix_lens   [num_seqs] int32 on the device: the group's shared prefix
+ *                length, equal for all members; the prefix is read through
+ *                the block table of the group's first sequence, so the
+ *                members' table entries for those positions must be the same
+ *                physical blocks (as after pkv_bm_fork), and the prefix must
+ *                end before the appended token (prefix_lens[b] <
+ *                context_lens[b] with k_new)
+ *  max_group_size >= every group's size (sizes the prefix launch)
+ *  workspace     >= pkv_shared_prefix_workspace_size(...) bytes, 256-byte
+ *                aligned (fp32 partials of both pieces)
+ * Other arguments as pkv_paged_attn_decode_append (k_new, v_new may be NULL).
+ * Supported: (q_dtype, cache_dtype) in {(F16,F16), (BF16,BF16)}; head_dim 64,
+ * 128, 256.  The prefix piece rounds its softmax weights to the q dtype before
+ * they multiply V (as pkv_paged_attn_multi).  A group of one sequence, or a
+ * prefix of 0, is the plain decode.  Violated contracts (groups that do not
+ * share the first member's prefix blocks, prefix_lens beyond the context)
+ * give wrong results, not faults: every position read is bounds-checked
+ * against the pool.
+ */
+pkv_status pkv_paged_attn_decode_shared_prefix(
+    void* out, const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+    const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+    const int32_t* prefix_lens, const int32_t* group_start, int num_groups, int max_group_size,
+    int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+    int64_t num_blocks, float scale, void* workspace, size_t workspace_bytes, pkv_dtype q_dtype,
+    pkv_dtype cache_dtype, hipStream_t stream);
+
+/* Workspace bytes for pkv_paged_attn_decode_shared_prefix (0 for invalid
+ * sizes). */
+size_t pkv_shared_prefix_workspace_size(int num_seqs, int num_groups, int max_group_size,
+                                        int num_q_heads, int num_kv_heads, int head_dim,
+                                        int max_blocks_per_seq);
+
+/*
  * Phase 1 of the split-context decode: per-partition partial results (for a
  * caller that merges them itself, e.g. partitions computed on several
  * devices, or that times the phases apart).  The N_b = context_lens[b] tokens

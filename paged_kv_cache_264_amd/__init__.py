@@ -97,6 +97,11 @@ def _load():
     L.pkv_paged_attn_multi.argtypes = [P, P, P, P, P, I, P, P, I, I, I, I, I, I, I, I64, F, I,
                                        P, SZ, I, I, P]
     L.pkv_paged_attn_multi.restype = I
+    L.pkv_paged_attn_decode_shared_prefix.argtypes = [P, P, P, P, P, P, P, I, P, P, P, I, I, I, I,
+                                                      I, I, I, I64, F, P, SZ, I, I, P]
+    L.pkv_paged_attn_decode_shared_prefix.restype = I
+    L.pkv_shared_prefix_workspace_size.argtypes = [I, I, I, I, I, I, I]
+    L.pkv_shared_prefix_workspace_size.restype = SZ
     L.pkv_multi_workspace_size.argtypes = [I, I, I, I, I]
     L.pkv_multi_workspace_size.restype = SZ
     L.pkv_multi_default_partition_size.argtypes = [I, I, I, I, I]
@@ -283,6 +288,54 @@ def paged_attn_decode_append(q, k_new, v_new, k_cache, v_cache, block_tables, co
         _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
         _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), mbs, _ptr(context_lens), B, Hq, Hkv,
         D, bs, NB, float(scale), int(partition_size), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _code(q.dtype, "q"),
+        _code(k_cache.dtype, "k_cache"), _stream(q))
+    _check_status(rc)
+    return out
+
+
+def shared_prefix_workspace_size(num_seqs, num_groups, max_group_size, num_q_heads, num_kv_heads,
+                                 head_dim, max_blocks_per_seq):
+    return int(_load().pkv_shared_prefix_workspace_size(num_seqs, num_groups, max_group_size,
+                                                        num_q_heads, num_kv_heads, head_dim,
+                                                        max_blocks_per_seq))
+
+
+def paged_attn_decode_shared_prefix(q, k_cache, v_cache, block_tables, context_lens, prefix_lens,
+                                    group_start, scale, max_group_size, k_new=None, v_new=None,
+                                    out=None, workspace=None):
+    """Decode of groups of sequences that continue one prompt: sequences
+    group_start[g] .. group_start[g+1]-1 (int32 [G+1] on the GPU) share their
+    first prefix_lens[b] positions (int32 [B], equal within a group, the same
+    physical blocks), which are read once per group.  Same result as
+    paged_attn_decode (or paged_attn_decode_append with k_new / v_new)."""
+    B, Hq, D, NB, Hkv, bs = _decode_common(q, k_cache, v_cache, block_tables, context_lens,
+                                           None, None)
+    _dev(prefix_lens, "prefix_lens", dtype=torch.int32, ndim=1)
+    _dev(group_start, "group_start", dtype=torch.int32, ndim=1)
+    if prefix_lens.shape[0] != B:
+        raise ValueError("prefix_lens needs one entry per sequence")
+    G = group_start.shape[0] - 1
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    if k_new is not None:
+        _dev(k_new, "k_new", dtype=q.dtype, ndim=3)
+        _dev(v_new, "v_new", dtype=q.dtype, ndim=3)
+        if tuple(k_new.shape) != (B, Hkv, D) or v_new.shape != k_new.shape:
+            raise ValueError("k_new and v_new must be [num_seqs][num_kv_heads][head_dim]")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", dtype=q.dtype, ndim=3)
+    mbs = block_tables.shape[1]
+    need = shared_prefix_workspace_size(B, G, int(max_group_size), Hq, Hkv, D, mbs)
+    if workspace is None:
+        workspace = _workspace(q.device, need)
+    else:
+        _dev(workspace, "workspace")
+    rc = _load().pkv_paged_attn_decode_shared_prefix(
+        _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+        _ptr(block_tables), mbs, _ptr(context_lens), _ptr(prefix_lens), _ptr(group_start), G,
+        int(max_group_size), B, Hq, Hkv, D, bs, NB, float(scale), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _code(q.dtype, "q"),
         _code(k_cache.dtype, "k_cache"), _stream(q))
     _check_status(rc)

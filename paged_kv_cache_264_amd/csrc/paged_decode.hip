@@ -407,7 +407,7 @@ void paged_decode_kernel(DecodeArgs a) {
         int my_span = -1, cnt = 0;
         if (tid < a.num_seqs) {
             int nn = clamp_len(a.context_lens[tid]);
-            nn -= window_base(nn, a.window);
+            nn -= attend_begin(nn, a.window, a.seq_start, tid) / kBlockSize * kBlockSize;
             const int c = partition_count(nn, P);
             my_span = c > 0 ? partition_span(nn, c) : 0;
             cnt = c > 0 ? c : 1;  // an empty sequence still takes one item: it writes zeros
@@ -438,10 +438,11 @@ void paged_decode_kernel(DecodeArgs a) {
     }
 
     const int n = clamp_len(a.context_lens[b]);
-    // sliding window: positions below `lo` are not attended to; the partitions
-    // split the positions from the block-aligned `base` on
-    const int lo = window_begin(n, a.window);
-    const int base = window_base(n, a.window);
+    // sliding window or per-sequence start: positions below `lo` are not
+    // attended to; the partitions split the positions from the block-aligned
+    // `base` on
+    const int lo = attend_begin(n, a.window, a.seq_start, b);
+    const int base = lo / kBlockSize * kBlockSize;
     const int n_parts = partition_count(n - base, P);
     const int span = n_parts > 0 ? partition_span(n - base, n_parts) : 0;
     const int Hq = a.num_q_heads;
@@ -451,9 +452,22 @@ void paged_decode_kernel(DecodeArgs a) {
 
     const bool direct_out = a.out != nullptr;
     if (part >= n_parts) {
-        if (direct_out && n == 0 && part == 0) {  // empty context: the output is zero
-            for (int i = tid; i < GT * D; i += kDecodeThreads)
-                store_elem<QE>(a.out, ((size_t)b * Hq + h0 + i / D) * D + i % D, 0.0f);
+        if (part == 0 && n_parts == 0) {  // no position to attend to
+            if (direct_out) {  // the output is zero
+                for (int i = tid; i < GT * D; i += kDecodeThreads)
+                    store_elem<QE>(a.out, ((size_t)b * Hq + h0 + i / D) * D + i % D, 0.0f);
+            } else if (a.seq_start != nullptr) {
+                // an empty partial (weight 0) for the merge with the positions
+                // attended to elsewhere
+                for (int i = tid; i < GT * D; i += kDecodeThreads) {
+                    const size_t pi = ((size_t)b * Hq + h0 + i / D) * NP;
+                    a.o_part[pi * D + i % D] = 0.f;
+                    if (i % D == 0) {
+                        a.m_part[pi] = kNegBig;
+                        a.l_part[pi] = 0.f;
+                    }
+                }
+            }
         }
         return;
     }

@@ -166,22 +166,28 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
     const int qlen = a.query_start_loc[b + 1] - q0;  // positions follow the given count
     const int rows_total = q0 < 0 ? 0 : max(0, q1 - q0) * g;
     if (rt * kRows >= rows_total) return;
+    // the sequence whose length and block table the rows read (a group's
+    // first member; q0 < num_tokens here, as the tile has rows)
+    const int seq0 = a.group_rows ? q0 : b;
     const int n_cap = a.max_blocks_per_seq * kBlockSize;
-    int n = a.context_lens[b];
+    int n = a.context_lens[seq0];
     n = n < 0 ? 0 : (n > n_cap ? n_cap : n);
     const int n_parts = partition_count(n, a.partition_size);
-    const bool direct_out = n_parts <= 1;
+    const bool direct_out = n_parts <= 1 && !a.partials_only;
     if (part >= (n_parts > 0 ? n_parts : 1)) return;
     const int span = n_parts > 0 ? partition_span(n, n_parts) : 0;
     const int t_begin = part * span;
     const int t_end = min(n, t_begin + span);
+    // the last query of the sequence sits at position n - 1 (causal), or every
+    // query sees the whole context
+    const int pos_of_last = a.causal ? n - 1 : 0x3fffffff;
 
     // this lane's query row (B operand and softmax state)
     const int R = rt * kRows + col;
     const bool row_ok = R < rows_total;
     const int jq = row_ok ? R / g : 0;
     const int hq = kvh * g + (row_ok ? R % g : 0);
-    const int pos = n - qlen + jq;      // the query attends to positions 0..pos
+    const int pos = pos_of_last - (qlen - 1) + jq;  // the query attends to positions 0..pos
 
     // Scores stay in raw units (q . k); the softmax works on c * s with
     // c = scale * log2(e), applied inside the exponent by one FMA.  A
@@ -215,11 +221,11 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
     const int per_wave = (nblk + kWaves - 1) / kWaves;
     const int my0 = blk_begin + wave * per_wave;
     const int n_my = max(0, min(per_wave, blk_end - my0));
-    const int32_t* table = a.block_tables + (size_t)b * a.max_blocks_per_seq;
+    const int32_t* table = a.block_tables + (size_t)seq0 * a.max_blocks_per_seq;
     char* vst = s_buf + wave * kRows * VS;
     char* kst = s_buf + kWaves * kRows * VS + wave * kRows * KS;
     // the last position any row of this tile attends to, and the first
-    const int pos_min = n - qlen + min(rt * kRows, rows_total - 1) / g;
+    const int pos_min = pos_of_last - (qlen - 1) + min(rt * kRows, rows_total - 1) / g;
     // the address this lane gives the V^T transpose read: token 4 grp +
     // (lane / 4) % 4, channels 4 (lane % 4) .. + 3 of each 16 (in each
     // 16-lane group, lane 16 G + 4 a + c receives as its element e element c
@@ -471,7 +477,12 @@ void paged_multi_tiled_kernel(MultiArgs a) {
         const int n_cap0 = a.max_blocks_per_seq * kBlockSize;
         int key = -1;
         if (tid < a.num_seqs) {
-            const int nn = min(max(a.context_lens[tid], 0), n_cap0);
+            int s0 = tid;
+            if (a.group_rows) {  // a group's context is its first member's
+                s0 = a.query_start_loc[tid];
+                s0 = s0 >= 0 && s0 < a.num_tokens ? s0 : -1;
+            }
+            const int nn = s0 < 0 ? 0 : min(max(a.context_lens[s0], 0), n_cap0);
             const int c = partition_count(nn, a.partition_size);
             key = c > 0 ? partition_span(nn, c) : 0;
         }
@@ -497,21 +508,27 @@ void paged_multi_tiled_kernel(MultiArgs a) {
     const int rows_total = q0 < 0 ? 0 : max(0, q1 - q0) * g;
     const int wg_r0 = rg * WG_ROWS;
     if (wg_r0 >= rows_total) return;
+    // the sequence whose length and block table the rows read (a group's
+    // first member; q0 < num_tokens here, as the work-group has rows)
+    const int seq0 = a.group_rows ? q0 : b;
     const int n_cap = a.max_blocks_per_seq * kBlockSize;
-    int n = a.context_lens[b];
+    int n = a.context_lens[seq0];
     n = n < 0 ? 0 : (n > n_cap ? n_cap : n);
     const int n_parts = partition_count(n, a.partition_size);
-    const bool direct_out = n_parts <= 1;
+    const bool direct_out = n_parts <= 1 && !a.partials_only;
     if (part >= (n_parts > 0 ? n_parts : 1)) return;
     const int span = n_parts > 0 ? partition_span(n, n_parts) : 0;
     const int t_begin = part * span;
     const int t_end = min(n, t_begin + span);
+    // the last query of the sequence sits at position n - 1 (causal), or every
+    // query sees the whole context
+    const int pos_of_last = a.causal ? n - 1 : 0x3fffffff;
     // the last position any row of this work-group attends to
     const int r_last = min(wg_r0 + WG_ROWS, rows_total) - 1;
-    const int t_stop = min(t_end, max(n - qlen + r_last / g + 1, 0));
+    const int t_stop = min(t_end, max(pos_of_last - (qlen - 1) + r_last / g + 1, 0));
     const int blk_begin = t_begin / kBlockSize;
     const int blk_stop = t_stop > t_begin ? (t_stop + kBlockSize - 1) / kBlockSize : blk_begin;
-    const int32_t* table = a.block_tables + (size_t)b * a.max_blocks_per_seq;
+    const int32_t* table = a.block_tables + (size_t)seq0 * a.max_blocks_per_seq;
     // Scores stay in raw units (q . k); the softmax works on c * s with
     // c = scale * log2(e), applied inside the exponent by one FMA.  A
     // negative scale is taken as |scale| on negated queries (exact), and c
@@ -526,7 +543,7 @@ void paged_multi_tiled_kernel(MultiArgs a) {
     int tile_pos_min[RW];   // the earliest position of a tile's rows (its first row)
 #pragma unroll
     for (int rr = 0; rr < RW; ++rr)
-        tile_pos_min[rr] = n - qlen + min(w_r0 + rr * kRows, rows_total - 1) / g;
+        tile_pos_min[rr] = pos_of_last - (qlen - 1) + min(w_r0 + rr * kRows, rows_total - 1) / g;
     uint4 qv[RW][KK];
     float m[RW], cm[RW], l[RW];  // running max of raw scores, c times it, sum
     f32x4_t o[RW][NN];  // O^T: o[rr][nn][i] = O[row col][d = 16 nn + 4 grp + i]
@@ -536,7 +553,7 @@ void paged_multi_tiled_kernel(MultiArgs a) {
         row_ok[rr] = R < rows_total;
         const int jq = row_ok[rr] ? R / g : 0;
         const int hq = kvh * g + (row_ok[rr] ? R % g : 0);
-        pos[rr] = n - qlen + jq;
+        pos[rr] = pos_of_last - (qlen - 1) + jq;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
             qv[rr][kk] = make_uint4(0u, 0u, 0u, 0u);

@@ -517,6 +517,39 @@ int pkv_multi_default_partition_size(int num_seqs, int max_query_len, int num_q_
                                       num_kv_heads, max_blocks_per_seq);
 }
 
+}  // extern "C"
+
+namespace {
+
+// The prefix piece of a shared-prefix decode: its partition size and count,
+// and the workspace: fp32 partials of the prefix (m, l [B][Hq][NP],
+// o [B][Hq][NP][D]) and of the own positions (m, l [B][Hq], o [B][Hq][D]),
+// each region 256-byte aligned.
+struct SharedPrefixLayout {
+    int P, NP;
+    size_t m0, l0, o0, m1, l1, o1, total;
+};
+
+bool shared_prefix_layout(int B, int G, int max_group, int Hq, int Hkv, int D, int mbs,
+                          SharedPrefixLayout& w) {
+    w.P = pkv_multi_default_partition_size(G, max_group, Hq, Hkv, mbs);
+    if (w.P <= 0) return false;
+    w.NP = num_partitions(mbs, w.P);
+    const size_t pre = (size_t)B * Hq * w.NP, own = (size_t)B * Hq;
+    w.m0 = 0;
+    w.l0 = align256(w.m0 + pre * sizeof(float));
+    w.o0 = align256(w.l0 + pre * sizeof(float));
+    w.m1 = align256(w.o0 + pre * D * sizeof(float));
+    w.l1 = align256(w.m1 + own * sizeof(float));
+    w.o1 = align256(w.l1 + own * sizeof(float));
+    w.total = align256(w.o1 + own * D * sizeof(float));
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
 pkv_status pkv_paged_attn_multi(void* out, const void* q, const void* k_cache, const void* v_cache,
                                 const int32_t* block_tables, int max_blocks_per_seq,
                                 const int32_t* context_lens, const int32_t* query_start_loc,
@@ -593,6 +626,7 @@ pkv_status pkv_paged_attn_multi(void* out, const void* q, const void* k_cache, c
     a.row_tiles = (int)row_tiles;
     a.max_rows = max_rows;
     a.num_tokens = num_query_tokens;
+    a.causal = 1;
     a.scale_log2 = scale * 1.44269504088896340736f;
     pkv_status s = hip_status(pkv::launch_paged_multi(a, (int)q_dtype, head_dim, stream),
                               "paged multi-query launch");
@@ -613,6 +647,142 @@ pkv_status pkv_paged_attn_multi(void* out, const void* q, const void* k_cache, c
     r.num_rows = num_query_tokens;
     return hip_status(pkv::launch_paged_reduce(r, (int)q_dtype, head_dim, stream),
                       "paged_attn_reduce launch");
+}
+
+size_t pkv_shared_prefix_workspace_size(int num_seqs, int num_groups, int max_group_size,
+                                        int num_q_heads, int num_kv_heads, int head_dim,
+                                        int max_blocks_per_seq) {
+    if (num_seqs < 0 || num_groups < 0 || max_group_size <= 0 || num_q_heads <= 0 ||
+        num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || !head_dim_ok(head_dim) ||
+        max_blocks_per_seq <= 0)
+        return 0;
+    SharedPrefixLayout w;
+    if (!shared_prefix_layout(num_seqs, num_groups, max_group_size, num_q_heads, num_kv_heads,
+                              head_dim, max_blocks_per_seq, w))
+        return 0;
+    return w.total;
+}
+
+pkv_status pkv_paged_attn_decode_shared_prefix(
+    void* out, const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+    const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+    const int32_t* prefix_lens, const int32_t* group_start, int num_groups, int max_group_size,
+    int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+    int64_t num_blocks, float scale, void* workspace, size_t workspace_bytes, pkv_dtype q_dtype,
+    pkv_dtype cache_dtype, hipStream_t stream) {
+    pkv_status s = check_decode(q, k_cache, v_cache, nullptr, nullptr, block_tables,
+                                max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                                num_kv_heads, head_dim, block_size, num_blocks, q_dtype,
+                                cache_dtype);
+    if (s != PKV_OK) return s;
+    if (!((q_dtype == PKV_F16 || q_dtype == PKV_BF16) && cache_dtype == q_dtype))
+        return fail(PKV_ERR_DTYPE, "shared-prefix decode needs (F16,F16) or (BF16,BF16), got "
+                                   "(%d, %d)", (int)q_dtype, (int)cache_dtype);
+    if (num_groups < 0 || max_group_size <= 0)
+        return fail(PKV_ERR_SHAPE, "need num_groups >= 0 and max_group_size > 0 (got %d, %d)",
+                    num_groups, max_group_size);
+    if ((k_new == nullptr) != (v_new == nullptr))
+        return fail(PKV_ERR_NULL, "k_new and v_new must both be given or both be NULL");
+    if (num_seqs == 0) return ok();
+    if (num_groups == 0 || num_groups > num_seqs)
+        return fail(PKV_ERR_SHAPE, "need 1 <= num_groups <= num_seqs (got %d, %d)", num_groups,
+                    num_seqs);
+    if (!out || !prefix_lens || !group_start)
+        return fail(PKV_ERR_NULL, "out, prefix_lens and group_start are required");
+    if (!aligned16(out) || (k_new && (!aligned16(k_new) || !aligned16(v_new))))
+        return fail(PKV_ERR_SHAPE, "out, k_new and v_new must be 16-byte aligned");
+    const int g = num_q_heads / num_kv_heads;
+    if ((int64_t)max_group_size * g > 0x7fffffff)
+        return fail(PKV_ERR_SHAPE, "max_group_size * num_q_heads / num_kv_heads too large");
+    SharedPrefixLayout w;
+    if (!shared_prefix_layout(num_seqs, num_groups, max_group_size, num_q_heads, num_kv_heads,
+                              head_dim, max_blocks_per_seq, w))
+        return fail(PKV_ERR_SHAPE, "no partition size for these sizes");
+    if (!workspace || workspace_bytes < w.total)
+        return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes,
+                    w.total);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(PKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    const int max_rows = max_group_size * g;
+    const int64_t row_tiles = pkv::multi_row_groups(max_rows, head_dim);
+    if ((int64_t)num_groups * num_kv_heads * row_tiles * w.NP > 0x7fffffff)
+        return fail(PKV_ERR_SHAPE, "too many work items for one launch");
+    char* ws = static_cast<char*>(workspace);
+    float* m0 = reinterpret_cast<float*>(ws + w.m0);
+    float* l0 = reinterpret_cast<float*>(ws + w.l0);
+    float* o0 = reinterpret_cast<float*>(ws + w.o0);
+    float* m1 = reinterpret_cast<float*>(ws + w.m1);
+    float* l1 = reinterpret_cast<float*>(ws + w.l1);
+    float* o1 = reinterpret_cast<float*>(ws + w.o1);
+    const float scale_log2 = scale * 1.44269504088896340736f;
+
+    // the shared prefix: a group's queries are the rows of one tile per kv
+    // head; no causal mask (every query follows the whole prefix)
+    pkv::MultiArgs a{};
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.context_lens = prefix_lens;
+    a.query_start_loc = group_start;
+    a.m_part = m0;
+    a.l_part = l0;
+    a.o_part = o0;
+    a.num_blocks = num_blocks;
+    a.num_seqs = num_groups;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.partition_size = w.P;
+    a.num_partitions = w.NP;
+    a.row_tiles = (int)row_tiles;
+    a.max_rows = max_rows;
+    a.num_tokens = num_seqs;
+    a.causal = 0;
+    a.partials_only = 1;
+    a.group_rows = 1;
+    a.scale_log2 = scale_log2;
+    s = hip_status(pkv::launch_paged_multi(a, (int)q_dtype, head_dim, stream),
+                   "shared-prefix launch");
+    if (s != PKV_OK) return s;
+
+    // each sequence's own positions (with the append), one partition
+    const int gt = heads_per_tile(g, cache_dtype);
+    const int own_p = (max_blocks_per_seq < 0x7fffffff / pkv::kBlockSize ? max_blocks_per_seq
+                                                                         : 0x7fffffff /
+                                                                               pkv::kBlockSize) *
+                      pkv::kBlockSize;
+    pkv::DecodeArgs d = make_args(q, k_cache, v_cache, nullptr, nullptr, block_tables,
+                                  max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                                  num_kv_heads, num_blocks, scale, own_p, 1, num_q_heads / gt);
+    d.out = nullptr;
+    d.k_new = k_new;
+    d.v_new = v_new;
+    d.m_part = m1;
+    d.l_part = l1;
+    d.o_part = o1;
+    d.seq_start = prefix_lens;
+    s = hip_status(pkv::launch_paged_decode(d, (int)q_dtype, (int)cache_dtype, head_dim, gt,
+                                            stream),
+                   "own-positions decode launch");
+    if (s != PKV_OK) return s;
+
+    pkv::PrefixMergeArgs mg{};
+    mg.out = out;
+    mg.m_pre = m0;
+    mg.l_pre = l0;
+    mg.o_pre = o0;
+    mg.m_suf = m1;
+    mg.l_suf = l1;
+    mg.o_suf = o1;
+    mg.prefix_lens = prefix_lens;
+    mg.num_seqs = num_seqs;
+    mg.num_q_heads = num_q_heads;
+    mg.partition_size = w.P;
+    mg.num_partitions = w.NP;
+    mg.max_tokens = own_p;
+    return hip_status(pkv::launch_prefix_merge(mg, (int)q_dtype, head_dim, stream),
+                      "shared-prefix merge launch");
 }
 
 }  // extern "C"

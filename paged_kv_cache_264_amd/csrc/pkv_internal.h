@@ -44,6 +44,7 @@ struct DecodeArgs {
     int n_tiles;         // num_q_heads / heads_per_tile
     int longest_first;   // schedule work longest-first (needs num_seqs <= kScheduleMaxSeqs)
     int window;          // > 0: attend to the last `window` positions only
+    const int32_t* seq_start;  // [B] first position attended, or nullptr (0)
     float scale_log2;    // softmax scale * log2(e)
 };
 
@@ -68,6 +69,17 @@ __host__ __device__ inline int window_begin(int n, int window) {
 }
 __host__ __device__ inline int window_base(int n, int window) {
     return window_begin(n, window) / kBlockSize * kBlockSize;
+}
+// The first position sequence b attends to: the window's, or a later start
+// given per sequence (the positions before it are attended to elsewhere, as
+// a shared prefix is).
+__device__ inline int attend_begin(int n, int window, const int32_t* seq_start, int b) {
+    int lo = window_begin(n, window);
+    if (seq_start != nullptr) {
+        const int s = min(max(seq_start[b], 0), n);
+        lo = max(lo, s);
+    }
+    return lo;
 }
 
 // Phase 1 of split-context decode.  With a.out set, sequences whose context
@@ -98,6 +110,13 @@ struct MultiArgs {
     int row_tiles;                   // row groups per (sequence, kv head): multi_row_groups()
     int max_rows;                    // max_query_len * Hq / Hkv (selects the kernel)
     int num_tokens;                  // T: rows of q / out (query rows outside are skipped)
+    int causal;                      // 0: every query row attends to the whole context
+    int partials_only;               // 1: (m, l, o) partials even for one partition
+    // 1: b indexes groups of sequences (rows query_start_loc[b] .. are the
+    // group's sequences, one query each); the group's context is the length
+    // context_lens[query_start_loc[b]] and the block table of that first
+    // sequence, shared by all its members
+    int group_rows;
     float scale_log2;
 };
 
@@ -129,6 +148,28 @@ struct ReduceArgs {
 };
 
 hipError_t launch_paged_reduce(const ReduceArgs& a, int out_dtype, int head_dim,
+                               hipStream_t stream);
+
+// Merge, per (sequence, q head), of the partials over a shared prefix
+// (partitions of the prefix length, stride num_partitions) with the one
+// partial over the sequence's own positions after it.
+struct PrefixMergeArgs {
+    void* out;                 // [B][Hq][D]
+    const float* m_pre;        // [B][Hq][NP]
+    const float* l_pre;
+    const float* o_pre;        // [B][Hq][NP][D]
+    const float* m_suf;        // [B][Hq]
+    const float* l_suf;
+    const float* o_suf;        // [B][Hq][D]
+    const int32_t* prefix_lens;  // [B]
+    int num_seqs;
+    int num_q_heads;
+    int partition_size;
+    int num_partitions;
+    int max_tokens;            // max_blocks_per_seq * 16 (prefix lengths are clamped to it)
+};
+
+hipError_t launch_prefix_merge(const PrefixMergeArgs& a, int out_dtype, int head_dim,
                                hipStream_t stream);
 
 struct CacheWriteArgs {

@@ -237,3 +237,40 @@ def test_block_manager_null_handle(lib):
     assert lib.pkv_bm_num_free_blocks(None) == -1
     assert lib.pkv_bm_sequence_length(None, 1) == -1
     assert lib.pkv_bm_create(10, 16, None) == ENULL
+
+
+def test_shared_prefix_argument_errors(lib):
+    f = lib.pkv_paged_attn_decode_shared_prefix
+    I = ctypes.c_int
+    f.argtypes = [P, P, P, P, P, P, P, I, P, P, P, I, I, I, I, I, I, I, ctypes.c_int64,
+                  ctypes.c_float, P, ctypes.c_size_t, I, I, P]
+    # out q k_new v_new k v bt mbs cl prefix group_start G maxg B Hq Hkv D bs NB scale ws wsb qd cd
+    base = [FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 8, FAKE, FAKE, FAKE, 2, 4, 8, 8, 2, 128, 16,
+            10, 0.1, FAKE, 1 << 30, F16, F16, None]
+
+    def call(**kw):
+        a = list(base)
+        for i, val in kw.items():
+            a[int(i[1:])] = val
+        return f(*a)
+
+    assert call(a22=F32, a23=F32) == EDTYPE      # fp32: the prefix piece runs on MFMA (16-bit)
+    assert call(a23=I8) == ENULL                 # INT8 cache (no scales taken): rejected
+    assert call(a22=BF16, a23=F16) == EDTYPE
+    assert call(a2=FAKE) == ENULL                # k_new without v_new
+    assert call(a11=0) == ESHAPE                 # no groups for 8 sequences
+    assert call(a11=9) == ESHAPE                 # more groups than sequences
+    assert call(a12=0) == ESHAPE                 # max_group_size
+    assert call(a9=None) == ENULL                # prefix_lens
+    assert call(a10=None) == ENULL               # group_start
+    assert call(a0=None) == ENULL                # out
+    assert call(a21=100) == EWS
+    assert call(a20=None) == EWS
+    assert call(a20=ctypes.c_void_p(0x1010)) == EWS   # not 256-byte aligned
+    assert call(a16=96) == EUNSUP
+    assert call(a13=0, a0=None, a9=None, a10=None) == OK   # empty batch, no launch
+    g = lib.pkv_shared_prefix_workspace_size
+    g.argtypes = [I] * 7
+    assert g(64, 16, 4, 32, 32, 128, 256) >= 2 * 64 * 32 * (128 + 2) * 4
+    assert g(64, 16, 0, 32, 32, 128, 256) == 0
+    assert g(64, 16, 4, 32, 32, 96, 256) == 0
