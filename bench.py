@@ -66,6 +66,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time of the oracle baseline sample")
+    p.add_argument("--sampling-decode", choices=["shared", "plain"], default="shared",
+                   help="sampling workload: shared = pkv_paged_attn_decode_shared_prefix (each "
+                        "prompt's shared blocks read once per group), plain = the fused decode "
+                        "of every sequence over its whole context")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain 1 GiB device copy (for HBM counter calibration)")
     return p.parse_args()
@@ -482,6 +486,14 @@ def bench_sampling(args):
     P = pkv.default_partition_size(B, Hq, Hkv, mbs)
     ws = torch.empty(pkv.decode_workspace_size(B, Hq, Hkv, D, mbs, P), dtype=torch.uint8,
                      device="cuda")
+    shared = args.sampling_decode == "shared"
+    # the shared prefix of a prompt's samples: its whole blocks (the partial
+    # last block is copied on write at the first step)
+    prefix_d = torch.from_numpy(np.repeat((prompt_lens // BS * BS).astype(np.int32), n)).cuda()
+    group_d = torch.from_numpy((np.arange(len(prompt_lens) + 1) * n).astype(np.int32)).cuda()
+    ws_sp = torch.empty(max(pkv.shared_prefix_workspace_size(B, len(prompt_lens), n, Hq, Hkv, D,
+                                                             mbs), 256),
+                        dtype=torch.uint8, device="cuda")
     pin_t = [torch.empty((B, mbs), dtype=torch.int32, pin_memory=True) for _ in range(2)]
     pin_l = [torch.empty((B,), dtype=torch.int32, pin_memory=True) for _ in range(2)]
     ev_up = [None, None]
@@ -515,8 +527,13 @@ def bench_sampling(args):
             step_lens.append(pin_l[buf].numpy().copy())
         if ev0 is not None:
             ev0.record(stream)
-        pkv.paged_attn_decode_append(q, k_new, v_new, kc, vc, tables, lens_d, scale, out=out,
-                                     partition_size=P, workspace=ws)
+        if shared:
+            pkv.paged_attn_decode_shared_prefix(q, kc, vc, tables, lens_d, prefix_d, group_d,
+                                                scale, n, k_new=k_new, v_new=v_new, out=out,
+                                                workspace=ws_sp)
+        else:
+            pkv.paged_attn_decode_append(q, k_new, v_new, kc, vc, tables, lens_d, scale,
+                                         out=out, partition_size=P, workspace=ws)
         if ev1 is not None:
             ev1.record(stream)
 
@@ -607,6 +624,8 @@ def bench_sampling(args):
             "mean_context_tokens": round(state["lens_sum"] / args.steps / B, 1),
             "partition_size": P, "seed": seed, "parallelism": "single-gpu",
             "step": "block-manager append + table upload + fused decode",
+            "decode": ("shared-prefix (prompt blocks once per group, own positions per "
+                       "sequence, merge)" if shared else "plain (every sequence's whole context)"),
         },
         "kv_tokens_per_s": round(state["lens_sum"] / args.steps / (ms_per_step * 1e-3), 1),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
@@ -626,7 +645,9 @@ def bench_sampling(args):
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "paged_decode_kernel", "kernel_sha": kernel_sha(),
+            "kernel": ("paged_multi_kernel + paged_decode_kernel + prefix_merge_kernel (events "
+                       "span the three)" if shared else "paged_decode_kernel"),
+            "kernel_sha": kernel_sha(),
             "note": "achieved = unique bytes (each physical block once) / kernel time; value "
                     "counts every sequence's context, so shared prompt blocks count once per "
                     "sample there",
