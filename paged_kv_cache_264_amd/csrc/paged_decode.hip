@@ -362,6 +362,111 @@ template <Elem CE, int GT>
 constexpr int kPipelineDepth =
     (GT == 4 && ElemInfo<CE>::bits <= 16) ? PKV_DEPTH_LARGE_TILE : PKV_DEPTH_SMALL_TILE;
 
+// ---- scores by a transposed (reduce-scatter) butterfly -------------------
+// When a token row spans exactly one 16-lane DPP row and a block is four wave
+// loads (16-bit caches at D = 128: token group g = 0..3 holds rows 4g..4g+3),
+// every lane has GT x 4 partial dot products (GT heads x 4 groups) that must
+// be summed over its row.  Summing each one over all 16 lanes costs 4 DPP adds
+// per value and leaves 16 copies of every score, each of which then takes its
+// own exponential.  Here each exchange step instead hands half of the
+// remaining values to the partner lane and keeps the other half (partners
+// lane ^ 8, ^ 7, ^ 2, ^ 1: row_ror:8, row_half_mirror and quad_perm), so
+// after four steps a lane holds the complete score of one (head, group)
+// pair: GT x 4 - 1 adds in all for GT = 4, and one exponential per lane.
+// The half a lane keeps is the same slot index in every lane because lanes
+// take their q heads and their K token groups in a lane-dependent order
+// (slot s holds head s ^ head_xor(lane), slot u holds group u ^ 2 b3, b3 =
+// bit 3 of the lane's place in the row); one split of the groups is done by a
+// per-lane select instead, since a K group that depends on lane bits below 3
+// would break the 128-byte lines a wave load reads.  The scores then go back
+// to all lanes of the row by DPP row broadcasts, one per (head, group).
+#ifndef PKV_SCATTER_MIN_GT
+#define PKV_SCATTER_MIN_GT 2
+#endif
+template <int GT> struct Scatter;
+template <> struct Scatter<4> {
+    // lane bits b3 b2 b1 b0 = place in the row; head 2 b2 + (b1 ^ b2),
+    // group 2 b3 + (b0 ^ b2)
+    static constexpr int kPartnerA = kDppQuadXor1, kPartnerB = kDppRowXor8;  // same head
+    __device__ static int head_xor(int s) { return (s & 4) >> 1 | (((s >> 1) ^ (s >> 2)) & 1); }
+    __device__ static bool sel(int s) { return ((s ^ (s >> 2)) & 1) != 0; }
+    static constexpr int src(int h, int g) {
+        return 8 * (g >> 1) + 4 * (h >> 1) + 2 * ((h & 1) ^ (h >> 1)) + ((g & 1) ^ (h >> 1));
+    }
+    __device__ static float reduce(const float (&x)[4][4], bool sl) {
+        float y[4][2], z[2][2], w[2];
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) y[h][u] = x[h][u] + dpp<kDppRowXor8>(x[h][u + 2]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) z[h][u] = y[h][u] + dpp<kDppRowHalfMirror>(y[h + 2][u]);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) w[u] = z[0][u] + dpp<kDppQuadXor2>(z[1][u]);
+        const float keep = sl ? w[1] : w[0], send = sl ? w[0] : w[1];
+        return keep + dpp<kDppQuadXor1>(send);
+    }
+};
+template <> struct Scatter<2> {
+    // head b2, group 2 b3 + (b1 ^ b2); lanes i and i ^ 1 hold the same score
+    static constexpr int kPartnerA = kDppQuadXor2, kPartnerB = kDppRowXor8;
+    __device__ static int head_xor(int s) { return (s >> 2) & 1; }
+    __device__ static bool sel(int s) { return (((s >> 1) ^ (s >> 2)) & 1) != 0; }
+    static constexpr int src(int h, int g) { return 8 * (g >> 1) + 4 * h + 2 * ((g & 1) ^ h); }
+    __device__ static float reduce(const float (&x)[2][4], bool sl) {
+        float y[2][2], z[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) y[h][u] = x[h][u] + dpp<kDppRowXor8>(x[h][u + 2]);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) z[u] = y[0][u] + dpp<kDppRowHalfMirror>(y[1][u]);
+        const float keep = sl ? z[1] : z[0], send = sl ? z[0] : z[1];
+        const float w = keep + dpp<kDppQuadXor2>(send);
+        return w + dpp<kDppQuadXor1>(w);
+    }
+};
+template <> struct Scatter<1> {
+    // group 2 b3 + b2; lanes i, i ^ 1, i ^ 2, i ^ 3 hold the same score
+    static constexpr int kPartnerA = kDppRowHalfMirror, kPartnerB = kDppRowXor8;
+    __device__ static int head_xor(int) { return 0; }
+    __device__ static bool sel(int s) { return ((s >> 2) & 1) != 0; }
+    static constexpr int src(int, int g) { return 8 * (g >> 1) + 4 * (g & 1); }
+    __device__ static float reduce(const float (&x)[1][4], bool sl) {
+        float y[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) y[u] = x[0][u] + dpp<kDppRowXor8>(x[0][u + 2]);
+        const float keep = sl ? y[1] : y[0], send = sl ? y[0] : y[1];
+        float w = keep + dpp<kDppRowHalfMirror>(send);
+        w += dpp<kDppQuadXor2>(w);
+        return w + dpp<kDppQuadXor1>(w);
+    }
+};
+// lane `src` of each row of 16 to the whole row; `src` is a constant once the
+// loops around the call are unrolled, so the switch folds away
+__device__ __forceinline__ float row_bcast(float x, int src) {
+    switch (src & 15) {
+    case 0: return dpp<kDppRowBcast + 0>(x);
+    case 1: return dpp<kDppRowBcast + 1>(x);
+    case 2: return dpp<kDppRowBcast + 2>(x);
+    case 3: return dpp<kDppRowBcast + 3>(x);
+    case 4: return dpp<kDppRowBcast + 4>(x);
+    case 5: return dpp<kDppRowBcast + 5>(x);
+    case 6: return dpp<kDppRowBcast + 6>(x);
+    case 7: return dpp<kDppRowBcast + 7>(x);
+    case 8: return dpp<kDppRowBcast + 8>(x);
+    case 9: return dpp<kDppRowBcast + 9>(x);
+    case 10: return dpp<kDppRowBcast + 10>(x);
+    case 11: return dpp<kDppRowBcast + 11>(x);
+    case 12: return dpp<kDppRowBcast + 12>(x);
+    case 13: return dpp<kDppRowBcast + 13>(x);
+    case 14: return dpp<kDppRowBcast + 14>(x);
+    default: return dpp<kDppRowBcast + 15>(x);
+    }
+}
+
 template <Elem QE, Elem CE, int D, int GT>
 __global__ __launch_bounds__(kDecodeThreads)
 __attribute__((amdgpu_waves_per_eu(CE == Elem::U4 && GT == 1 && D == 128 ? 4 : 1)))
@@ -372,6 +477,11 @@ void paged_decode_kernel(DecodeArgs a) {
     constexpr bool kInt8 = is_scaled(CE);  // 1-byte codes with a per-row scale
     constexpr bool kU4 = CE == Elem::U4;    // 4-bit codes with a per-row (x_min, range)
     constexpr float kInv15 = 1.0f / 15.0f;
+    // scores by the reduce-scatter butterfly (16-bit caches, one DPP row per
+    // token row, four wave loads per block)
+    constexpr bool kScatter = (CE == Elem::F16 || CE == Elem::BF16) && QE == CE && L == 16 &&
+                              U == 4 && STEPS == 1 && GT >= PKV_SCATTER_MIN_GT && GT <= 4;
+    using SC = Scatter<(GT <= 4 ? GT : 1)>;
 
     __shared__ float s_m[NW][GT];
     __shared__ float s_l[NW][GT];
@@ -475,7 +585,15 @@ void paged_decode_kernel(DecodeArgs a) {
     // q slices of the GT heads, and the running state of this lane's row
     QSlice<QE, CE, E> qs[GT];
 #pragma unroll
-    for (int h = 0; h < GT; ++h) qs[h].load(a.q, ((size_t)b * Hq + h0 + h) * D + slice * E);
+    for (int h = 0; h < GT; ++h) {
+        const int hq = kScatter ? (h ^ SC::head_xor(slice)) : h;
+        qs[h].load(a.q, ((size_t)b * Hq + h0 + hq) * D + slice * E);
+    }
+    // scatter mode: K slot u of this lane holds token group u ^ kflip
+    const int kflip = kScatter ? (slice & 8) >> 2 : 0;
+    const bool ssel = kScatter && SC::sel(slice);
+    const int sgroup = 2 * (kflip >> 1) + (ssel ? 1 : 0);  // group of the lane's score
+    float ms = kNegBig, ls = 0.f;  // running max / this lane's share of the sum
 
     float m[GT], l[GT], acc[GT][E];
     float zacc[GT];  // 4-bit caches: sum of p * x_min, added to every channel at the end
@@ -520,26 +638,31 @@ void paged_decode_kernel(DecodeArgs a) {
         r.jb = my0 + i;
         r.ok = i < n_my && phys >= 0 && (int64_t)phys < a.num_blocks;
         const size_t tile_idx = (size_t)(r.ok ? phys : 0) * a.num_kv_heads + kvh;
-        const int bytes = r.ok ? kTileBytes : 0;
+        // the window ends at the last token the loop attends to: rows past it
+        // (the unused tail of a last block, the new token's slot) load as zeros
+        // (uniform in the work-group; said so, or the loads get per-lane descriptors)
+        const int rows = __builtin_amdgcn_readfirstlane(
+            r.ok ? min(max(n_loop - r.jb * kBlockSize, 0), kBlockSize) : 0);
+        const int bytes = rows * G::ROW;
         const __amdgpu_buffer_rsrc_t kr =
             tile_rsrc(static_cast<const char*>(a.k_cache) + tile_idx * kTileBytes, bytes);
         const __amdgpu_buffer_rsrc_t vr =
             tile_rsrc(static_cast<const char*>(a.v_cache) + tile_idx * kTileBytes, bytes);
         __amdgpu_buffer_rsrc_t ksr, vsr;
         if constexpr (kInt8) {
-            ksr = tile_rsrc(a.k_scale + tile_idx * kBlockSize, r.ok ? kBlockSize * 4 : 0);
-            vsr = tile_rsrc(a.v_scale + tile_idx * kBlockSize, r.ok ? kBlockSize * 4 : 0);
+            ksr = tile_rsrc(a.k_scale + tile_idx * kBlockSize, rows * 4);
+            vsr = tile_rsrc(a.v_scale + tile_idx * kBlockSize, rows * 4);
         }
         if constexpr (kU4) {
-            ksr = tile_rsrc(a.k_scale + tile_idx * kBlockSize * 2, r.ok ? kBlockSize * 8 : 0);
-            vsr = tile_rsrc(a.v_scale + tile_idx * kBlockSize * 2, r.ok ? kBlockSize * 8 : 0);
+            ksr = tile_rsrc(a.k_scale + tile_idx * kBlockSize * 2, rows * 8);
+            vsr = tile_rsrc(a.v_scale + tile_idx * kBlockSize * 2, rows * 8);
         }
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int tok = (st * U + u) * R;  // first token of this wave load
-                r.k[st][u] = ld16_stream(kr, tok * G::ROW + lane * 16);
+                r.k[st][u] = ld16_stream(kr, (st * U + (u ^ kflip)) * R * G::ROW + lane * 16);
                 r.v[st][u] = ld16_stream(vr, tok * G::ROW + lane * 16);
                 if constexpr (kInt8) {
                     r.ks[st][u] = ld_f32(ksr, (tok + row) * 4);
@@ -558,6 +681,57 @@ void paged_decode_kernel(DecodeArgs a) {
     auto compute_block = [&](const BlockRegs<CE, D>& r) {
         const int jb = r.jb;
         const bool full = r.ok && jb * kBlockSize >= lo && (jb + 1) * kBlockSize <= n_loop;
+        // V rows past the loop's last token arrive as zeros (buffer window);
+        // only a block that starts before the first attended position (a
+        // sliding window or a per-sequence start) must zero rows itself
+        const bool below_lo = r.ok && jb * kBlockSize < lo;
+        if constexpr (kScatter) {
+            // one score per lane: head h0 + head_xor(slice), token group sgroup
+            float x[GT][U];
+#pragma unroll
+            for (int h = 0; h < GT; ++h)
+#pragma unroll
+                for (int u = 0; u < U; ++u) x[h][u] = qs[h].dot(r.k[0][u]);
+            const float sc = SC::reduce(x, ssel);
+            const int t_own = jb * kBlockSize + sgroup * R + row;
+            const bool v_own = full || (r.ok && t_own >= lo && t_own < n_loop);
+            const float s = v_own ? sc * c : -INFINITY;
+            // the running max of the lane's head over the row's four groups
+            float mx = fmaxf(s, dpp<SC::kPartnerA>(s));
+            mx = fmaxf(mx, dpp<SC::kPartnerB>(mx));
+            mx = fmaxf(mx, ms);
+            const float p = fast_exp2(s - mx);
+            if (__builtin_amdgcn_ballot_w64(mx > ms) != 0) {
+                const float alpha = fast_exp2(ms - mx);
+                ls *= alpha;
+                float ah[GT];
+#pragma unroll
+                for (int h = 0; h < GT; ++h) ah[h] = row_bcast(alpha, SC::src(h, 0));
+#pragma unroll
+                for (int h = 0; h < GT; ++h)
+#pragma unroll
+                    for (int e = 0; e < E; ++e) acc[h][e] *= ah[h];
+                ms = mx;
+            }
+            ls += p;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float vx[E];
+                widen<CE, E>(r.v[0][u], vx);
+                if (below_lo) {  // rows before the first attended position
+                    const bool ok_u = jb * kBlockSize + u * R + row >= lo;
+#pragma unroll
+                    for (int e = 0; e < E; ++e) vx[e] = ok_u ? vx[e] : 0.f;
+                }
+#pragma unroll
+                for (int h = 0; h < GT; ++h) {
+                    const float pv = row_bcast(p, SC::src(h, u));
+#pragma unroll
+                    for (int e = 0; e < E; ++e) acc[h][e] = fmaf(pv, vx[e], acc[h][e]);
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
             bool valid[U];
@@ -617,7 +791,7 @@ void paged_decode_kernel(DecodeArgs a) {
                     // one FMA each, p x_min a running scalar.  Masked rows get
                     // step = x_min = 0 (their values may be anything, NaN too).
                 } else if constexpr (!kInt8) {
-                    if (!full) {
+                    if (below_lo) {
 #pragma unroll
                         for (int e = 0; e < E; ++e) vx[e] = valid[u] ? vx[e] : 0.f;
                     }
@@ -674,6 +848,18 @@ void paged_decode_kernel(DecodeArgs a) {
             load_block(rb, next_id, i + 4);
             next_id = my_ids[min(i + 5, last)];
             if (i + 2 < n_my) compute_block(rc);
+        }
+    }
+
+    if constexpr (kScatter) {
+        // back to one (m, l) per head in every lane of the row: the head's sum
+        // is spread over the lanes of its four groups
+        float lh = ls + dpp<SC::kPartnerA>(ls);
+        lh += dpp<SC::kPartnerB>(lh);
+#pragma unroll
+        for (int h = 0; h < GT; ++h) {
+            m[h] = row_bcast(ms, SC::src(h, 0));
+            l[h] = row_bcast(lh, SC::src(h, 0));
         }
     }
 
@@ -752,7 +938,17 @@ void paged_decode_kernel(DecodeArgs a) {
             float d;
             if constexpr (kU4)
                 d = group_sum<L>(qs[h].score(kc, ks * kInv15, kz));
-            else
+            else if constexpr (kScatter) {
+                // this lane holds head h in slot h ^ head_xor(slice)
+                const int want = h ^ SC::head_xor(slice);
+                float mine = qs[0].dot(kc);
+#pragma unroll
+                for (int s2 = 1; s2 < GT; ++s2) {
+                    const float t2 = qs[s2].dot(kc);
+                    mine = want == s2 ? t2 : mine;
+                }
+                d = group_sum<L>(mine);
+            } else
                 d = group_sum<L>(qs[h].dot(kc));
             if constexpr (kInt8) d *= ks;
             const float sn = d * c;

@@ -94,6 +94,8 @@ enum : int {
     kDppQuadXor2 = 0x4E,       // quad_perm [2,3,0,1]
     kDppRowHalfMirror = 0x141, // lane i <-> 7-i inside each group of 8
     kDppRowMirror = 0x140,     // lane i <-> 15-i inside each row of 16
+    kDppRowXor8 = 0x128,       // row_ror:8, i.e. lane i <-> i ^ 8 inside each row of 16
+    kDppRowBcast = 0x150,      // + n: row_newbcast:n, lane n of each row of 16 to the whole row
 };
 
 template <int CTRL> __device__ __forceinline__ float dpp(float x) {
