@@ -380,6 +380,9 @@ constexpr int kPipelineDepth =
 // per-lane select instead, since a K group that depends on lane bits below 3
 // would break the 128-byte lines a wave load reads.  The scores then go back
 // to all lanes of the row by DPP row broadcasts, one per (head, group).
+#ifndef PKV_WAVES_16BIT
+#define PKV_WAVES_16BIT 1
+#endif
 #ifndef PKV_SCATTER_MIN_GT
 #define PKV_SCATTER_MIN_GT 2
 #endif
@@ -467,9 +470,20 @@ __device__ __forceinline__ float row_bcast(float x, int src) {
     }
 }
 
+// Waves per SIMD asked of the register allocator where the default falls
+// just short of a step: 4-bit single-head tiles at D = 128 (4).  16-bit
+// single-head tiles at D = 128 take 100 VGPRs (4 waves); asking for 5 gives
+// 96 with one spill reloaded in the block loop, measured slower on MI355X
+// (LLaMA-7B batch 404 -> 412 us, 16 x 32k 1407 -> 1434 us), so it is off.
+template <Elem CE, int D, int GT>
+constexpr int kMinWavesPerEU = (GT == 1 && D == 128 && CE == Elem::U4) ? 4
+                               : (GT == 1 && D == 128 && (CE == Elem::F16 || CE == Elem::BF16))
+                                   ? PKV_WAVES_16BIT
+                                   : 1;
+
 template <Elem QE, Elem CE, int D, int GT>
 __global__ __launch_bounds__(kDecodeThreads)
-__attribute__((amdgpu_waves_per_eu(CE == Elem::U4 && GT == 1 && D == 128 ? 4 : 1)))
+__attribute__((amdgpu_waves_per_eu(kMinWavesPerEU<CE, D, GT>)))
 void paged_decode_kernel(DecodeArgs a) {
     using G = Geom<CE, D>;
     constexpr int L = G::L, E = G::E, R = G::R, U = G::U, STEPS = G::STEPS;
@@ -491,7 +505,7 @@ void paged_decode_kernel(DecodeArgs a) {
     constexpr int RK = kKeepCap >= 4 ? (R < 4 ? R : 4) : kKeepCap >= 2 ? (R < 2 ? R : 2) : 1;
     __shared__ float s_acc[NW][RK][GT][D];
     __shared__ int2 s_key[kScheduleMaxSeqs];  // (partition span, item count) per sequence
-    __shared__ int s_pick[2];
+    __shared__ int s_pick[3];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -510,44 +524,58 @@ void paged_decode_kernel(DecodeArgs a) {
     // sorted by partition length, longest first, so that the work dispatched
     // last is the shortest and the ragged tail of a batch is small.  Every
     // work-group ranks the sequences itself (one per thread, in LDS).
-    int b, part, tile;
+    // The ranking sits on the path from kernel start to the first K/V load:
+    // the keys are read eight at a time (one LDS round trip per eight
+    // sequences instead of one per sequence), and the picked sequence's
+    // length comes back through LDS rather than from memory again.
+    int b, part, tile, n;
     if (a.longest_first) {
         const int item = blockIdx.x / a.n_tiles;
         tile = blockIdx.x % a.n_tiles;
-        int my_span = -1, cnt = 0;
+        int my_span = -1, cnt = 0, my_n = 0;
         if (tid < a.num_seqs) {
-            int nn = clamp_len(a.context_lens[tid]);
-            nn -= attend_begin(nn, a.window, a.seq_start, tid) / kBlockSize * kBlockSize;
+            my_n = clamp_len(a.context_lens[tid]);
+            const int nn =
+                my_n - attend_begin(my_n, a.window, a.seq_start, tid) / kBlockSize * kBlockSize;
             const int c = partition_count(nn, P);
             my_span = c > 0 ? partition_span(nn, c) : 0;
             cnt = c > 0 ? c : 1;  // an empty sequence still takes one item: it writes zeros
         }
+        // every one of the kScheduleMaxSeqs entries is written; those past the
+        // batch hold count 0 and so add nothing to a rank
         s_key[tid] = make_int2(my_span, cnt);
         if (tid == 0) s_pick[0] = -1;
         __syncthreads();
         if (tid < a.num_seqs) {
             int start = 0;
-            for (int j = 0; j < a.num_seqs; ++j) {
-                const int2 kj = s_key[j];
-                if (kj.x > my_span || (kj.x == my_span && j < tid)) start += kj.y;
+            const int nj = (a.num_seqs + 7) & ~7;  // <= kScheduleMaxSeqs
+            for (int j = 0; j < nj; j += 8) {
+                int2 kj[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) kj[q] = s_key[j + q];
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    if (kj[q].x > my_span || (kj[q].x == my_span && j + q < tid)) start += kj[q].y;
             }
             if (item >= start && item < start + cnt) {
                 s_pick[0] = tid;
                 s_pick[1] = item - start;
+                s_pick[2] = my_n;
             }
         }
         __syncthreads();
         b = s_pick[0];
         part = s_pick[1];
+        n = s_pick[2];
         if (b < 0) return;  // beyond the last item (uniform)
     } else {
         part = blockIdx.x % NP;
         const int rest = blockIdx.x / NP;
         tile = rest % a.n_tiles;
         b = rest / a.n_tiles;
+        n = clamp_len(a.context_lens[b]);
     }
 
-    const int n = clamp_len(a.context_lens[b]);
     // sliding window or per-sequence start: positions below `lo` are not
     // attended to; the partitions split the positions from the block-aligned
     // `base` on
