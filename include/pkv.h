@@ -362,7 +362,8 @@ pkv_status pkv_paged_attn_decode_partials(void* out, float* m_part, float* l_par
  * writes zeros.  skip_single_partition != 0 leaves `out` of sequences with at
  * most one partition untouched (phase 1 with an output pointer finished
  * them).  out is [num_seqs][num_q_heads][head_dim] in out_dtype (F32|F16|BF16),
- * rounded to nearest even.
+ * rounded to nearest even.  o_part must be 16-byte aligned (PKV_ERR_SHAPE
+ * otherwise): its rows are read as 16-byte pieces.
  */
 pkv_status pkv_paged_attn_reduce(void* out, const float* m_part, const float* l_part,
                                  const float* o_part, const int32_t* context_lens, int num_seqs,

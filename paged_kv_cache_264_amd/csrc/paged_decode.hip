@@ -433,7 +433,8 @@ template <> struct Scatter<2> {
 };
 template <> struct Scatter<1> {
     // group 2 b3 + b2; lanes i, i ^ 1, i ^ 2, i ^ 3 hold the same score
-    static constexpr int kPartnerA = kDppRowHalfMirror, kPartnerB = kDppRowXor8;
+    [[maybe_unused]] static constexpr int kPartnerA = kDppRowHalfMirror;
+    [[maybe_unused]] static constexpr int kPartnerB = kDppRowXor8;
     __device__ static int head_xor(int) { return 0; }
     __device__ static bool sel(int s) { return ((s >> 2) & 1) != 0; }
     static constexpr int src(int, int g) { return 8 * (g >> 1) + 4 * (g & 1); }

@@ -6,7 +6,7 @@
 // section 3.2) applied to whole partitions:
 //     M = max_p m_p,  w_p = l_p exp(m_p - M),  out = sum_p w_p o_p / sum_p w_p.
 // One work-group per (sequence, q head); the weights are computed once into
-// LDS and every lane then owns output channels.
+// LDS, then the threads split the partitions' rows between them.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -61,30 +61,62 @@ __global__ __launch_bounds__(kReduceThreads) void paged_reduce_kernel(ReduceArgs
 #pragma unroll
     for (int w = 1; w < kReduceThreads / kWave; ++w) M = fmaxf(M, s_red[w]);
 
-    float o[(D + kReduceThreads - 1) / kReduceThreads];
-#pragma unroll
-    for (int i = 0; i < (D + kReduceThreads - 1) / kReduceThreads; ++i) o[i] = 0.f;
+    // sum_p w_p o_p over all threads: CPL = D / 4 threads read one partition's
+    // row as 16-byte pieces, RP = 256 / CPL rows side by side, four rows in
+    // flight per thread; the RP row groups then meet in LDS.
+    constexpr int CPL = D / 4;
+    constexpr int RP = kReduceThreads / CPL;
+    static_assert(CPL * RP == kReduceThreads, "rows must tile the work-group");
+    __shared__ float4 s_o[kReduceThreads];
+    __shared__ float s_ws[RP];
+    const int c4 = tid % CPL, r0 = tid / CPL;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float wsum = 0.f;
+    auto add_row = [&](float w, const float4& x) {
+        acc.x = fmaf(w, x.x, acc.x);
+        acc.y = fmaf(w, x.y, acc.y);
+        acc.z = fmaf(w, x.z, acc.z);
+        acc.w = fmaf(w, x.w, acc.w);
+        wsum += w;
+    };
     for (int c0 = 0; c0 < n_parts; c0 += kWeightChunk) {
         const int c1 = min(n_parts, c0 + kWeightChunk);
         __syncthreads();
         for (int p = c0 + tid; p < c1; p += kReduceThreads)
             s_w[p - c0] = lp[p] * fast_exp2((mp[p] - M) * kLog2e);
         __syncthreads();
-        for (int p = c0; p < c1; ++p) {
-            const float w = s_w[p - c0];
-            wsum += w;
+        int p = c0 + r0;
+        for (; p + 3 * RP < c1; p += 4 * RP) {
+            float4 x[4];
 #pragma unroll
-            for (int i = 0; i < (D + kReduceThreads - 1) / kReduceThreads; ++i) {
-                const int d = tid + i * kReduceThreads;
-                if (d < D) o[i] = fmaf(w, op[(size_t)p * D + d], o[i]);
-            }
+            for (int k = 0; k < 4; ++k)
+                x[k] = *reinterpret_cast<const float4*>(op + (size_t)(p + k * RP) * D + 4 * c4);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) add_row(s_w[p + k * RP - c0], x[k]);
         }
+        for (; p < c1; p += RP)
+            add_row(s_w[p - c0], *reinterpret_cast<const float4*>(op + (size_t)p * D + 4 * c4));
     }
+    s_o[tid] = acc;
+    if (c4 == 0) s_ws[r0] = wsum;
+    __syncthreads();
+    if (tid < CPL) {
+        float4 o = s_o[tid];
+        float W = s_ws[0];
 #pragma unroll
-    for (int i = 0; i < (D + kReduceThreads - 1) / kReduceThreads; ++i) {
-        const int d = tid + i * kReduceThreads;
-        if (d < D) store_elem<OE>(a.out, (size_t)bh * D + d, o[i] / wsum);
+        for (int r = 1; r < RP; ++r) {
+            const float4 x = s_o[r * CPL + tid];
+            o.x += x.x;
+            o.y += x.y;
+            o.z += x.z;
+            o.w += x.w;
+            W += s_ws[r];
+        }
+        const size_t d0 = (size_t)bh * D + 4 * tid;
+        store_elem<OE>(a.out, d0 + 0, o.x / W);
+        store_elem<OE>(a.out, d0 + 1, o.y / W);
+        store_elem<OE>(a.out, d0 + 2, o.z / W);
+        store_elem<OE>(a.out, d0 + 3, o.w / W);
     }
 }
 

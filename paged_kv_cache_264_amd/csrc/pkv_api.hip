@@ -301,6 +301,7 @@ pkv_status reduce_impl(void* out, const float* m_part, const float* l_part, cons
     if (num_seqs == 0) return ok();
     if (!out || !m_part || !l_part || !o_part || !context_lens)
         return fail(PKV_ERR_NULL, "out, m_part, l_part, o_part and context_lens are required");
+    if (!aligned16(o_part)) return fail(PKV_ERR_SHAPE, "o_part must be 16-byte aligned");
     pkv::ReduceArgs a{};
     a.out = out;
     a.m_part = m_part;

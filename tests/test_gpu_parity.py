@@ -76,6 +76,21 @@ def test_partition_sizes(pkv, P, dtype, cache):
     _check_step(pkv, batch, partition_size=P)
 
 
+@pytest.mark.parametrize("P", [16, 64, 0])
+@pytest.mark.parametrize("dtype,cache,Hq,Hkv", [("f16", "f16", 4, 4), ("bf16", "bf16", 8, 2),
+                                                ("f16", "f16", 8, 4), ("bf16", "i8", 4, 4)])
+def test_schedule_ties_and_ragged_batch(pkv, P, dtype, cache, Hq, Hkv):
+    """Longest-first ranking with many equal partition lengths, empty
+    sequences and a batch size (21) that is not a multiple of the eight keys
+    a rank step reads: every work item must be taken exactly once (a
+    duplicated or skipped item leaves a wrong or unwritten output row)."""
+    lens = [100, 100, 0, 100, 37, 100, 1, 100, 100, 250, 100, 37, 37, 16, 17, 100, 250, 0, 100,
+            64, 100]
+    batch = W.make_batch(cfg=_cfg(dtype, cache, 128, Hq, Hkv, lens, seed=77 + P), device="cuda")
+    gpu_populate(pkv, batch)
+    _check_step(pkv, batch, partition_size=P)
+
+
 def test_tiny_config(pkv):
     batch = W.make_batch("tiny", device="cuda")
     _check_step(pkv, batch)
