@@ -98,9 +98,13 @@ enum : int {
     kDppRowBcast = 0x150,      // + n: row_newbcast:n, lane n of each row of 16 to the whole row
 };
 
+// Every pattern used here gives each lane a source inside its own row, so
+// the bound control (a lane without a source reads 0) never acts; it lets the
+// compiler fold the lane move into the add that consumes it (one
+// v_add_f32_dpp instead of a v_mov_b32_dpp and a v_add_f32).
 template <int CTRL> __device__ __forceinline__ float dpp(float x) {
     return __builtin_bit_cast(
-        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 
 // Sum over aligned groups of N lanes (N a power of two, 1..64); every lane of
