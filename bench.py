@@ -716,18 +716,27 @@ def run_cpu_baseline(batch, cfg_name, target_s, e_kv, e_q, int8, window=0):
     while n_seq < batch.B and per_tok * att[:n_seq + 1].sum() < target_s:
         n_seq += 1
     v = view_for(n_seq)
-    t = time.perf_counter()
-    oracle.paged_decode(**v)
-    t_s = time.perf_counter() - t
+    # passes over the sample until about target_s seconds of oracle work (the
+    # whole batch can take well under a second); the median pass is reported
+    passes = []
+    while True:
+        t = time.perf_counter()
+        oracle.paged_decode(**v)
+        passes.append(time.perf_counter() - t)
+        if sum(passes) >= target_s or len(passes) >= 50:
+            break
+    t_s = float(np.median(passes))
     sub = att[:n_seq]
     meta = 8 if e_kv == 0.5 else (4 if int8 else 0)
     alg = W.algorithmic_bytes(sub, batch.Hq, batch.Hkv, batch.D, e_kv, e_q, int8, meta)
     return {
         "value": round(alg / t_s / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
         "sample": f"first {n_seq} of {batch.B} sequences (all {batch.Hq} q heads, "
-                  f"{int(sub.sum())} context tokens), one fp64 oracle pass of {t_s:.2f} s",
+                  f"{int(sub.sum())} context tokens), median of {len(passes)} fp64 oracle passes "
+                  f"({sum(passes):.1f} s in all)",
         "kv_tokens_per_s": round(float(sub.sum()) / t_s, 1),
         "seconds": round(t_s, 3),
+        "passes": len(passes),
     }
 
 
