@@ -295,12 +295,18 @@ template <Elem CE, int E> __device__ __forceinline__ void widen(const uint4& c, 
             f8x4_to_f32(w[i], x[4 * i + 0], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
         } else if constexpr (CE == Elem::U4) {
             // low nibbles are elements 8i, 8i+2, 8i+4, 8i+6, high ones the odd
-            // elements: byte-select converts of the two masked words
+            // elements.  A byte c <= 15 read as an e4m3 code is exactly
+            // c * 2^-9 (codes 1..7 are the subnormals m * 2^-9, 8..15 the
+            // normals (8 + m) * 2^-9), so one packed fp8 convert widens two
+            // codes; the values come out scaled by 2^-9 (kU4Widen undoes it)
             const uint32_t lo = w[i] & 0x0F0F0F0Fu, hi = (w[i] >> 4) & 0x0F0F0F0Fu;
+            float l[4], h[4];
+            f8x4_to_f32(lo, l[0], l[1], l[2], l[3]);
+            f8x4_to_f32(hi, h[0], h[1], h[2], h[3]);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                x[8 * i + 2 * j] = (float)((lo >> (8 * j)) & 0xffu);
-                x[8 * i + 2 * j + 1] = (float)((hi >> (8 * j)) & 0xffu);
+                x[8 * i + 2 * j] = l[j];
+                x[8 * i + 2 * j + 1] = h[j];
             }
         } else {
             x[4 * i + 0] = i8_at(w[i], 0);
@@ -310,6 +316,10 @@ template <Elem CE, int E> __device__ __forceinline__ void widen(const uint4& c, 
         }
     }
 }
+
+// 4-bit V codes are widened to code * 2^-9 (see widen); their weights carry
+// the 2^9 back (a power of two: the products are the same as with the codes)
+constexpr float kU4Widen = 512.0f;
 
 // K/V tiles are read through raw buffer loads.  A buffer resource covers one
 // (block, kv head) tile; a load whose offset lies outside the resource returns
@@ -799,8 +809,11 @@ void paged_decode_kernel(DecodeArgs a) {
                 // Tiles of several heads rescale only when some row's running
                 // max grew (rare after the first blocks; otherwise the factor
                 // is exactly 1).  Measured: a win for GQA tiles, a loss for
-                // single-head tiles, which rescale unconditionally.
-                if (!(PKV_LAZY_RESCALE && GT > 1) || __builtin_amdgcn_ballot_w64(mx > m[h]) != 0) {
+                // 16-bit single-head tiles (8 accumulators per lane), which
+                // rescale unconditionally; 4-bit tiles hold 32 per lane and
+                // rescale lazily too.
+                if (!(PKV_LAZY_RESCALE && (GT > 1 || kU4)) ||
+                    __builtin_amdgcn_ballot_w64(mx > m[h]) != 0) {
                     const float alpha = fast_exp2(m[h] - mx);
                     l[h] *= alpha;
                     if constexpr (kU4) zacc[h] *= alpha;
@@ -827,7 +840,7 @@ void paged_decode_kernel(DecodeArgs a) {
                 }
                 float vstep = 0.f, vmin = 0.f;
                 if constexpr (kU4) {
-                    vstep = valid[u] ? r.vs[st][u] * kInv15 : 0.f;
+                    vstep = valid[u] ? r.vs[st][u] * kInv15 * kU4Widen : 0.f;
                     vmin = valid[u] ? r.vz[st][u] : 0.f;
                 }
 #pragma unroll
@@ -989,7 +1002,7 @@ void paged_decode_kernel(DecodeArgs a) {
                 float pv = kInt8 ? pn * vs : pn;
                 if constexpr (kU4) {
                     zacc[h] = fmaf(pn, vz, zacc[h] * alpha);
-                    pv = pn * (vs * kInv15);
+                    pv = pn * (vs * kInv15 * kU4Widen);
                 }
 #pragma unroll
                 for (int e = 0; e < E; ++e) acc[h][e] = fmaf(pv, vx[e], acc[h][e] * alpha);
