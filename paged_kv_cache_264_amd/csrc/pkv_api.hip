@@ -185,12 +185,19 @@ int pkv_default_partition_size(int num_seqs, int num_q_heads, int num_kv_heads,
     // round trips (context length, block ids, first K/V tiles) before it
     // streams, so long partitions stream best; they are cut only as far as
     // needed to give the 256 CUs about 8 work-groups each at the maximum
-    // context (one tile per kv head).  Power of two in [256, 4096].
+    // context (one tile per kv head), at most 4096 tokens.  A batch that
+    // already has 1024 (sequence, kv head) items fills the chip with about 4
+    // per CU and partitions of up to 8192 tokens (the GQA batch of 128
+    // sequences x 8 kv heads at contexts up to 8192: 397 -> 389 us without
+    // the split and its merge).  Power of two in [256, 8192].
     const int64_t seq_tiles = (int64_t)num_seqs * num_kv_heads;
     const int64_t max_tokens = (int64_t)max_blocks_per_seq * pkv::kBlockSize;
-    const int64_t want = (max_tokens * seq_tiles + 2047) / 2048;  // tokens per work-group
+    const bool wide = seq_tiles >= 1024;
+    const int64_t per = wide ? 1024 : 2048;                             // work-groups wanted
+    const int64_t want = (max_tokens * seq_tiles + per - 1) / per;      // tokens per work-group
+    const int cap = wide ? 8192 : 4096;
     int P = 256;
-    while (P < 4096 && P < want) P <<= 1;
+    while (P < cap && P < want) P <<= 1;
     return P;
 }
 
