@@ -119,6 +119,15 @@ def test_workspace_size(lib):
     for args in [(64, 32, 32, 256), (1, 32, 8, 2048), (16, 32, 32, 2048), (128, 32, 8, 512)]:
         p = lib.pkv_default_partition_size(*args)
         assert p >= 64 and p % 16 == 0
+    d = lib.pkv_default_partition_size
+    # fewer than 1024 (sequence, kv head) items: about 8 work-groups per CU at
+    # the longest context, at most 4096 tokens
+    assert d(16, 32, 32, 2048) == 4096      # 512 items, 32k tokens
+    assert d(2, 32, 32, 1024) == 512        # 64 items, 16k tokens
+    # >= 1024 items already fill the chip: up to 8192 tokens, about 4 per CU
+    assert d(128, 32, 8, 512) == 8192       # the GQA batch: no sequence split
+    assert d(64, 32, 32, 256) == 8192       # 4096-token contexts stay whole
+    assert d(256, 32, 8, 64) == 2048        # 2048 items of at most 1024 tokens
 
 
 def test_cache_write_argument_errors(lib):
@@ -152,6 +161,10 @@ def test_reduce_argument_errors(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 128, 16, 4, 0, I8, None) == EDTYPE
     assert f(None, FAKE, FAKE, FAKE, FAKE, 2, 4, 128, 16, 4, 1, F16, None) == ENULL
     assert f(None, None, None, None, None, 0, 4, 128, 16, 4, 0, F16, None) == OK
+    # o_part rows are read as 16-byte pieces: a misaligned pointer is refused
+    # before anything is enqueued
+    odd = ctypes.c_void_p(0x1004)
+    assert f(FAKE, FAKE, FAKE, odd, FAKE, 2, 4, 128, 16, 4, 0, F16, None) == ESHAPE
 
 
 def test_partials_argument_errors(lib):
