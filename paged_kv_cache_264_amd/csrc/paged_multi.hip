@@ -148,7 +148,11 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
     const int grp = lane >> 4;          // lane group 0..3
     const int col = lane & 15;          // query row (B / C column) of this lane
 
-    // (partition fastest, then row tile, then kv head, then sequence)
+    // (partition fastest, then row tile, then kv head, then sequence), the
+    // sequences in longest-first order (by partition length) so that the
+    // work-groups dispatched last are the shortest; every work-group ranks
+    // the sequences itself (one per thread, keys read eight per LDS round
+    // trip)
     const int NP = a.num_partitions;
     int rest = blockIdx.x;
     const int part = rest % NP;
@@ -156,7 +160,42 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
     const int rt = rest % a.row_tiles;
     rest /= a.row_tiles;
     const int kvh = rest % a.num_kv_heads;
-    const int b = rest / a.num_kv_heads;
+    int b = rest / a.num_kv_heads;
+    static_assert(kThreads >= kScheduleMaxSeqs, "one thread per ranked sequence");
+    __shared__ int s_key[kScheduleMaxSeqs];
+    __shared__ int s_order[kScheduleMaxSeqs];
+    if (a.num_seqs <= kScheduleMaxSeqs) {
+        const int n_cap0 = a.max_blocks_per_seq * kBlockSize;
+        int key = -1;
+        if (threadIdx.x < a.num_seqs) {
+            int s0 = threadIdx.x;
+            if (a.group_rows) {  // a group's context is its first member's
+                s0 = a.query_start_loc[threadIdx.x];
+                s0 = s0 >= 0 && s0 < a.num_tokens ? s0 : -1;
+            }
+            const int nn = s0 < 0 ? 0 : min(max(a.context_lens[s0], 0), n_cap0);
+            const int c = partition_count(nn, a.partition_size);
+            key = c > 0 ? partition_span(nn, c) : 0;
+        }
+        // every entry is written; those past the batch (key -1) rank nothing
+        if (threadIdx.x < kScheduleMaxSeqs) s_key[threadIdx.x] = key;
+        __syncthreads();
+        if (threadIdx.x < a.num_seqs) {
+            const int me = threadIdx.x;
+            int r = 0;
+            const int nj = (a.num_seqs + 7) & ~7;  // <= kScheduleMaxSeqs
+            for (int j = 0; j < nj; j += 8) {
+                int kj[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) kj[q] = s_key[j + q];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) r += (kj[q] > key || (kj[q] == key && j + q < me)) ? 1 : 0;
+            }
+            s_order[r] = me;
+        }
+        __syncthreads();
+        b = s_order[b];
+    }
 
     const int Hq = a.num_q_heads;
     const int g = Hq / a.num_kv_heads;
