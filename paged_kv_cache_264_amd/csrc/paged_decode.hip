@@ -22,13 +22,16 @@
 //     reads 1 KiB of consecutive bytes (whole 128-byte lines).
 //   * a token row (D * elem bytes) is owned by L = row_bytes / 16 consecutive
 //     lanes; q.k is a per-lane partial dot (packed dot2 instructions for
-//     fp16 / bf16) finished by a DPP butterfly inside the row.
+//     fp16 / bf16) finished by a DPP butterfly inside the row; tiles of 2 or 4
+//     heads with 16-bit caches at D = 128 use a reduce-scatter butterfly that
+//     leaves one complete score (and one exponential) per lane (Scatter).
 //   * every row of lanes keeps its own online-softmax state (m, l, acc) for
 //     the tokens it sees, so the loop has no cross-row traffic; rows and waves
 //     are merged once at the end (shuffles, then LDS).
 //   * the exponential is exp2 with log2(e) folded into the scale.
-//   * tokens past the context are masked with selects (never a multiply), so
-//     whatever bytes sit in unused slots (NaN included) cannot leak.
+//   * tokens past the context are masked with selects (never a multiply), and
+//     the K/V rows past it are outside the tile's buffer window, so they load
+//     as zeros: whatever bytes sit in unused slots (NaN included) cannot leak.
 //   * a sequence whose context fits in one partition gets its final output
 //     here (when an output pointer is given); longer ones leave a partial
 //     (m, l, o) per partition for the merge kernel.  The merge runs as a
