@@ -45,6 +45,7 @@ namespace pkv {
 namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kNegBig = -3.0e38f;  // finite stand-in for -inf in running maxima
 
 template <Elem CE, int D> struct Geom {
@@ -603,9 +604,33 @@ void paged_decode_kernel(DecodeArgs a) {
     const int kvh = h0 / g;
 
     const bool direct_out = a.out != nullptr;
+    // The output of a sequence whose earlier positions were attended to
+    // elsewhere (a shared prefix, partials pre_*): this work-group's result
+    // (max M in log2 units, sum L, unnormalized O) merged with those partials
+    // by the running-max / running-sum rule; nothing attended at all gives 0.
+    const bool pre = a.pre_m != nullptr && a.seq_start != nullptr && direct_out;
+    auto merge_pre = [&](int h, int d, float M2, float L, float O) -> float {
+        const size_t pb = ((size_t)b * Hq + h0 + h) * a.pre_np;
+        const int n0 = min(max(a.seq_start[b], 0), n_cap);
+        const int np = min(max(partition_count(n0, a.pre_partition_size), 1), a.pre_np);
+        float Mx = M2;
+        for (int p = 0; p < np; ++p) Mx = fmaxf(Mx, a.pre_m[pb + p] * kLog2e);
+        const float f = fast_exp2(M2 - Mx);
+        float LL = L * f, OO = O * f;
+        for (int p = 0; p < np; ++p) {
+            const float w = a.pre_l[pb + p] * fast_exp2(fmaf(a.pre_m[pb + p], kLog2e, -Mx));
+            LL += w;
+            OO = fmaf(w, a.pre_o[(pb + p) * D + d], OO);
+        }
+        return LL > 0.f ? OO / LL : 0.f;
+    };
     if (part >= n_parts) {
         if (part == 0 && n_parts == 0) {  // no position to attend to
-            if (direct_out) {  // the output is zero
+            if (pre) {  // the prefix alone
+                for (int i = tid; i < GT * D; i += kDecodeThreads)
+                    store_elem<QE>(a.out, ((size_t)b * Hq + h0 + i / D) * D + i % D,
+                                   merge_pre(i / D, i % D, kNegBig, 0.f, 0.f));
+            } else if (direct_out) {  // the output is zero
                 for (int i = tid; i < GT * D; i += kDecodeThreads)
                     store_elem<QE>(a.out, ((size_t)b * Hq + h0 + i / D) * D + i % D, 0.0f);
             } else if (a.seq_start != nullptr) {
@@ -1068,7 +1093,7 @@ void paged_decode_kernel(DecodeArgs a) {
         }
         const size_t bh = (size_t)b * Hq + h0 + h;
         if (single) {
-            store_elem<QE>(a.out, bh * D + d, o / lsum);
+            store_elem<QE>(a.out, bh * D + d, pre ? merge_pre(h, d, M, lsum, o) : o / lsum);
         } else {
             const size_t pi = bh * NP + part;
             a.o_part[pi * D + d] = o / lsum;

@@ -120,52 +120,6 @@ __global__ __launch_bounds__(kReduceThreads) void paged_reduce_kernel(ReduceArgs
     }
 }
 
-// One wave per (sequence, q head): the prefix partitions' weights are
-// recomputed by every lane (a few per sequence); each lane owns D / 64
-// output channels.  A partition or suffix with l = 0 (nothing attended)
-// weighs nothing; with nothing attended at all the output is zero.
-template <Elem OE, int D>
-__global__ __launch_bounds__(kWave) void prefix_merge_kernel(PrefixMergeArgs a) {
-    constexpr int C = D / kWave;
-    const size_t bh = blockIdx.x;
-    const int b = (int)(bh / a.num_q_heads);
-    const int lane = threadIdx.x;
-    const int n0 = min(max(a.prefix_lens[b], 0), a.max_tokens);
-    const int np = min(max(partition_count(n0, a.partition_size), 1), a.num_partitions);
-    const size_t pre = bh * a.num_partitions;
-    float M = a.m_suf[bh];
-    for (int p = 0; p < np; ++p) M = fmaxf(M, a.m_pre[pre + p]);
-    float o[C];
-    const float ws = a.l_suf[bh] * fast_exp2((a.m_suf[bh] - M) * kLog2e);
-#pragma unroll
-    for (int i = 0; i < C; ++i) o[i] = ws * a.o_suf[bh * D + lane + i * kWave];
-    float L = ws;
-    for (int p = 0; p < np; ++p) {
-        const float w = a.l_pre[pre + p] * fast_exp2((a.m_pre[pre + p] - M) * kLog2e);
-        L += w;
-#pragma unroll
-        for (int i = 0; i < C; ++i) o[i] = fmaf(w, a.o_pre[(pre + p) * D + lane + i * kWave], o[i]);
-    }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-#pragma unroll
-    for (int i = 0; i < C; ++i) store_elem<OE>(a.out, bh * D + lane + i * kWave, o[i] * inv);
-}
-
-template <Elem OE>
-hipError_t launch_merge_d(const PrefixMergeArgs& a, int d, hipStream_t s) {
-    const int64_t n_wg = (int64_t)a.num_seqs * a.num_q_heads;
-    if (n_wg == 0) return hipSuccess;
-    if (n_wg > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const dim3 grid((unsigned)n_wg), block(kWave);
-    switch (d) {
-    case 64: hipLaunchKernelGGL((prefix_merge_kernel<OE, 64>), grid, block, 0, s, a); break;
-    case 128: hipLaunchKernelGGL((prefix_merge_kernel<OE, 128>), grid, block, 0, s, a); break;
-    case 256: hipLaunchKernelGGL((prefix_merge_kernel<OE, 256>), grid, block, 0, s, a); break;
-    default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-}
-
 template <Elem OE>
 hipError_t launch_d(const ReduceArgs& a, int d, hipStream_t s) {
     const int64_t n_wg = (int64_t)a.num_rows * a.num_q_heads;
@@ -182,15 +136,6 @@ hipError_t launch_d(const ReduceArgs& a, int d, hipStream_t s) {
 }
 
 }  // namespace
-
-hipError_t launch_prefix_merge(const PrefixMergeArgs& a, int out_dtype, int head_dim,
-                               hipStream_t stream) {
-    switch (static_cast<Elem>(out_dtype)) {
-    case Elem::F16: return launch_merge_d<Elem::F16>(a, head_dim, stream);
-    case Elem::BF16: return launch_merge_d<Elem::BF16>(a, head_dim, stream);
-    default: return hipErrorInvalidValue;
-    }
-}
 
 hipError_t launch_paged_reduce(const ReduceArgs& a, int out_dtype, int head_dim,
                                hipStream_t stream) {

@@ -531,8 +531,10 @@ namespace {
 
 // The prefix piece of a shared-prefix decode: its partition size and count,
 // and the workspace: fp32 partials of the prefix (m, l [B][Hq][NP],
-// o [B][Hq][NP][D]) and of the own positions (m, l [B][Hq], o [B][Hq][D]),
-// each region 256-byte aligned.
+// o [B][Hq][NP][D]) and a region for the own positions' partials (m, l
+// [B][Hq], o [B][Hq][D]) that the decode launch is given but, with its one
+// partition and an output to merge into, never writes; each region 256-byte
+// aligned.
 struct SharedPrefixLayout {
     int P, NP;
     size_t m0, l0, o0, m1, l1, o1, total;
@@ -768,34 +770,22 @@ pkv_status pkv_paged_attn_decode_shared_prefix(
     pkv::DecodeArgs d = make_args(q, k_cache, v_cache, nullptr, nullptr, block_tables,
                                   max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
                                   num_kv_heads, num_blocks, scale, own_p, 1, num_q_heads / gt);
-    d.out = nullptr;
+    // ... which merges its result with the prefix partials into `out` itself
+    d.out = out;
     d.k_new = k_new;
     d.v_new = v_new;
     d.m_part = m1;
     d.l_part = l1;
     d.o_part = o1;
     d.seq_start = prefix_lens;
-    s = hip_status(pkv::launch_paged_decode(d, (int)q_dtype, (int)cache_dtype, head_dim, gt,
-                                            stream),
-                   "own-positions decode launch");
-    if (s != PKV_OK) return s;
-
-    pkv::PrefixMergeArgs mg{};
-    mg.out = out;
-    mg.m_pre = m0;
-    mg.l_pre = l0;
-    mg.o_pre = o0;
-    mg.m_suf = m1;
-    mg.l_suf = l1;
-    mg.o_suf = o1;
-    mg.prefix_lens = prefix_lens;
-    mg.num_seqs = num_seqs;
-    mg.num_q_heads = num_q_heads;
-    mg.partition_size = w.P;
-    mg.num_partitions = w.NP;
-    mg.max_tokens = own_p;
-    return hip_status(pkv::launch_prefix_merge(mg, (int)q_dtype, head_dim, stream),
-                      "shared-prefix merge launch");
+    d.pre_m = m0;
+    d.pre_l = l0;
+    d.pre_o = o0;
+    d.pre_np = w.NP;
+    d.pre_partition_size = w.P;
+    return hip_status(pkv::launch_paged_decode(d, (int)q_dtype, (int)cache_dtype, head_dim, gt,
+                                               stream),
+                      "own-positions decode launch");
 }
 
 }  // extern "C"

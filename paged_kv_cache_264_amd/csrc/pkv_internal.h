@@ -45,6 +45,13 @@ struct DecodeArgs {
     int longest_first;   // schedule work longest-first (needs num_seqs <= kScheduleMaxSeqs)
     int window;          // > 0: attend to the last `window` positions only
     const int32_t* seq_start;  // [B] first position attended, or nullptr (0)
+    // With seq_start and an output: the partials of the positions before the
+    // start ([B][Hq][pre_np], natural-log m), merged into the output here
+    const float* pre_m;
+    const float* pre_l;
+    const float* pre_o;  // [B][Hq][pre_np][D]
+    int pre_np;
+    int pre_partition_size;
     float scale_log2;    // softmax scale * log2(e)
 };
 
@@ -153,24 +160,6 @@ hipError_t launch_paged_reduce(const ReduceArgs& a, int out_dtype, int head_dim,
 // Merge, per (sequence, q head), of the partials over a shared prefix
 // (partitions of the prefix length, stride num_partitions) with the one
 // partial over the sequence's own positions after it.
-struct PrefixMergeArgs {
-    void* out;                 // [B][Hq][D]
-    const float* m_pre;        // [B][Hq][NP]
-    const float* l_pre;
-    const float* o_pre;        // [B][Hq][NP][D]
-    const float* m_suf;        // [B][Hq]
-    const float* l_suf;
-    const float* o_suf;        // [B][Hq][D]
-    const int32_t* prefix_lens;  // [B]
-    int num_seqs;
-    int num_q_heads;
-    int partition_size;
-    int num_partitions;
-    int max_tokens;            // max_blocks_per_seq * 16 (prefix lengths are clamped to it)
-};
-
-hipError_t launch_prefix_merge(const PrefixMergeArgs& a, int out_dtype, int head_dim,
-                               hipStream_t stream);
 
 struct CacheWriteArgs {
     const void* k;
