@@ -158,7 +158,8 @@ size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads
  *
  *  out               [num_seqs][num_q_heads][head_dim], q_dtype, written
  *  q                 [num_seqs][num_q_heads][head_dim], q_dtype
- *  k_scale, v_scale  required iff cache_dtype is I8, F8_E4M3 or U4
+ *  k_scale, v_scale  required iff cache_dtype is I8, F8_E4M3 or U4; for U4
+ *                    8-byte aligned (PKV_ERR_SHAPE otherwise)
  *  scale             the softmax scale, normally 1/sqrt(head_dim)
  *  partition_size    0 (library choice) or a positive multiple of 16
  *  workspace         >= pkv_decode_workspace_size(...) bytes, 256-byte aligned
@@ -166,7 +167,9 @@ size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads
  * context_lens[b] == 0 writes zeros for sequence b.  Only block-table entries
  * j < ceil(context_lens[b] / 16) are read, and only slots of those blocks that
  * lie below context_lens[b]; everything else in the pool may hold any bytes,
- * NaN included.  Outputs are rounded to q_dtype with round-to-nearest-even.
+ * NaN included.  (For a U4 cache the scale pairs of the other slots of those
+ * blocks, and of block 0, may be loaded too; they never reach the result.)
+ * Outputs are rounded to q_dtype with round-to-nearest-even.
  * The result does not depend on where blocks sit in the pool (bit for bit),
  * and repeated calls give bit-identical results.
  */

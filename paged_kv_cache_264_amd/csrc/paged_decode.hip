@@ -720,9 +720,14 @@ void paged_decode_kernel(DecodeArgs a) {
             ksr = tile_rsrc(a.k_scale + tile_idx * kBlockSize, rows * 4);
             vsr = tile_rsrc(a.v_scale + tile_idx * kBlockSize, rows * 4);
         }
+        // 4-bit rows: one 8-byte (x_min, range) pair per row, read in place
+        // from the row's slot (every slot of the tile exists; values of rows
+        // outside the window may be anything and every use selects them away)
+        const float2* kzs = nullptr;
+        const float2* vzs = nullptr;
         if constexpr (kU4) {
-            ksr = tile_rsrc(a.k_scale + tile_idx * kBlockSize * 2, rows * 8);
-            vsr = tile_rsrc(a.v_scale + tile_idx * kBlockSize * 2, rows * 8);
+            kzs = reinterpret_cast<const float2*>(a.k_scale) + tile_idx * kBlockSize;
+            vzs = reinterpret_cast<const float2*>(a.v_scale) + tile_idx * kBlockSize;
         }
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
@@ -736,10 +741,12 @@ void paged_decode_kernel(DecodeArgs a) {
                     r.vs[st][u] = ld_f32(vsr, (tok + row) * 4);
                 }
                 if constexpr (kU4) {
-                    r.kz[st][u] = ld_f32(ksr, (tok + row) * 8);
-                    r.ks[st][u] = ld_f32(ksr, (tok + row) * 8 + 4);
-                    r.vz[st][u] = ld_f32(vsr, (tok + row) * 8);
-                    r.vs[st][u] = ld_f32(vsr, (tok + row) * 8 + 4);
+                    const float2 kp = kzs[tok + row];
+                    const float2 vp = vzs[tok + row];
+                    r.kz[st][u] = kp.x;
+                    r.ks[st][u] = kp.y;
+                    r.vz[st][u] = vp.x;
+                    r.vs[st][u] = vp.y;
                 }
             }
         }

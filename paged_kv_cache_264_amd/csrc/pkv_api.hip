@@ -125,6 +125,10 @@ pkv_status check_decode(const void* q, const void* k_cache, const void* v_cache,
         return fail(PKV_ERR_NULL, "k_scale and v_scale are required for an INT8 / FP8 / 4-bit cache");
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
         return fail(PKV_ERR_SHAPE, "q, k_cache and v_cache must be 16-byte aligned");
+    // a 4-bit row's (x_min, range) pair is read as one 8-byte word
+    if (cache_dtype == PKV_U4 &&
+        ((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 7u))
+        return fail(PKV_ERR_SHAPE, "4-bit k_scale and v_scale must be 8-byte aligned");
     if ((int64_t)Hkv * num_blocks * pkv::kBlockSize * D > (int64_t)1 << 62)
         return fail(PKV_ERR_SHAPE, "pool too large");
     return ok();

@@ -98,6 +98,9 @@ def decode(lib, **kw):
     (dict(ws=None), EWS),
     (dict(wsb=100), EWS),
     (dict(q=ctypes.c_void_p(0x1004)), ESHAPE),   # misaligned
+    # a 4-bit row's (x_min, range) pair is one 8-byte load
+    (dict(cd=U4, ks=ctypes.c_void_p(0x1004), vs=FAKE), ESHAPE),
+    (dict(cd=U4, ks=FAKE, vs=ctypes.c_void_p(0x100c)), ESHAPE),
 ])
 def test_decode_argument_errors(lib, kw, status):
     assert decode(lib, **kw) == status
