@@ -153,10 +153,12 @@ template <Elem QE> struct QSlice<QE, Elem::F8, 16> : QSliceScaled<QE, Elem::F8> 
 
 // 4-bit cache: q kept packed in its own 16-bit format, paired as the codes
 // come out of a 32-bit word: pair k of word i is (q[8i+k], q[8i+k+4]),
-// matching (nibble k, nibble k+4).  A pair of codes becomes a pair of 16-bit
-// floats of value 16 + code by OR-ing the nibbles, shifted into the mantissa,
-// with the bits of 16.0 (exact in fp16 and bf16), so one v_dot2 takes two
-// codes:  q . (x_min + step c) = step * sum q (16 + c) + (x_min - 16 step) sum q.
+// matching (nibble k, nibble k+4), so one v_dot2 takes two codes and
+// q . (x_min + step c) = step * sum q c + x_min * sum q.  For fp16 q a code
+// pair is a pair of fp16 subnormals (masking only, below); bf16 subnormal
+// products would fall under fp32's normal range, so for bf16 q a pair becomes
+// two bf16 values 16 + code by OR-ing the nibbles, shifted into the mantissa,
+// with the bits of 16.0, and the 16 sum q is taken off again.
 template <Elem QE> struct QSlice<QE, Elem::U4, 32> {
     uint32_t v[16];  // [word i][pair k] -> v[4 i + k]
     float sum;
@@ -182,13 +184,12 @@ template <Elem QE> struct QSlice<QE, Elem::U4, 32> {
             for (int k = 0; k < 4; ++k)
                 v[4 * i + k] = (uint32_t)x[8 * i + k] | ((uint32_t)x[8 * i + k + 4] << 16);
     }
-    // sum over the chunk's 32 codes of q * (16 + code)
+    // bf16 q: sum over the chunk's 32 codes of q * (16 + code); bf16 16.0 is
+    // 0x4180 and the mantissa step at that exponent is 1/8, so code << 3
     __device__ __forceinline__ float dot16(const uint4& k) const {
         const uint32_t w[4] = {k.x, k.y, k.z, k.w};
-        // fp16 16.0 = 0x4C00, mantissa step 1/64 at that exponent: code << 6;
-        // bf16 16.0 = 0x4180, mantissa step 1/8: code << 3
-        constexpr uint32_t kMagic = QE == Elem::F16 ? 0x4C004C00u : 0x41804180u;
-        constexpr int kSh = QE == Elem::F16 ? 6 : 3;
+        constexpr uint32_t kMagic = 0x41804180u;
+        constexpr int kSh = 3;
         constexpr uint32_t kMask = 0x000F000Fu << kSh;
         float d0 = 0.f, d1 = 0.f;
 #pragma unroll
@@ -198,19 +199,44 @@ template <Elem QE> struct QSlice<QE, Elem::U4, 32> {
                 const int sh = kSh - 4 * kq;   // nibble kq (and kq + 4) to the mantissa
                 const uint32_t bits = ((sh >= 0 ? (w[i] << sh) : (w[i] >> -sh)) & kMask) | kMagic;
                 float& d = (kq & 1) ? d1 : d0;
-                if constexpr (QE == Elem::F16)
-                    d = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, v[4 * i + kq]),
-                                               __builtin_bit_cast(half2_t, bits), d, false);
-                else
-                    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, v[4 * i + kq]),
-                                                        __builtin_bit_cast(bf162_t, bits), d, false);
+                d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, v[4 * i + kq]),
+                                                    __builtin_bit_cast(bf162_t, bits), d, false);
             }
         }
         return d0 + d1;
     }
+    // fp16 q: a nibble masked into the low mantissa bits of a half whose
+    // exponent bits are zero is the subnormal code * 2^-24 (code * 2^-20 at
+    // bits 4..7), exact, so a mask alone makes the v_dot2 operand: nibbles 0
+    // and 2 of each half land at bits 0..3, nibbles 1 and 3 at bits 4..7.
+    // Returns the sums over pairs 0, 2 and over pairs 1, 3 of q * code * 2^-24
+    // and q * code * 2^-20.
+    __device__ __forceinline__ void dot_sub(const uint4& k, float& d0, float& d1) const {
+        const uint32_t w[4] = {k.x, k.y, k.z, k.w};
+        d0 = 0.f;
+        d1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t w8 = w[i] >> 8;
+            const uint32_t b[4] = {w[i] & 0x000F000Fu, w[i] & 0x00F000F0u, w8 & 0x000F000Fu,
+                                   w8 & 0x00F000F0u};
+#pragma unroll
+            for (int kq = 0; kq < 4; ++kq) {
+                float& d = (kq & 1) ? d1 : d0;
+                d = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, v[4 * i + kq]),
+                                           __builtin_bit_cast(half2_t, b[kq]), d, false);
+            }
+        }
+    }
     // this lane's share of q . dequantized K row
     __device__ __forceinline__ float score(const uint4& k, float step, float zmin) const {
-        return fmaf(dot16(k), step, fmaf(-16.0f, step, zmin) * sum);
+        if constexpr (QE == Elem::F16) {
+            float d0, d1;
+            dot_sub(k, d0, d1);
+            return fmaf(fmaf(d1, 0x1p20f, d0 * 0x1p24f), step, zmin * sum);
+        } else {
+            return fmaf(dot16(k), step, fmaf(-16.0f, step, zmin) * sum);
+        }
     }
 };
 
@@ -361,8 +387,10 @@ template <Elem CE, int D> struct BlockRegs {
     bool ok;  // the block exists and its id was inside the pool
 };
 
-// Blocks in flight per wave (measured on MI355X: a third block in flight did
-// not help any tile size; it is kept selectable for experiments).
+// Blocks in flight per wave.  Measured on MI355X: a third block in flight
+// helps the single-head 4-bit tile only (its blocks are a quarter of an fp16
+// block's bytes for a similar amount of work: 134.3 -> 131.3 us on a 64 x
+// U[512, 4096] batch) and no other tile; the depths stay selectable.
 #ifndef PKV_LAZY_RESCALE
 #define PKV_LAZY_RESCALE 1
 #endif
@@ -372,9 +400,14 @@ template <Elem CE, int D> struct BlockRegs {
 #ifndef PKV_DEPTH_LARGE_TILE
 #define PKV_DEPTH_LARGE_TILE 2
 #endif
+#ifndef PKV_DEPTH_U4_SINGLE
+#define PKV_DEPTH_U4_SINGLE 3
+#endif
 template <Elem CE, int GT>
 constexpr int kPipelineDepth =
-    (GT == 4 && ElemInfo<CE>::bits <= 16) ? PKV_DEPTH_LARGE_TILE : PKV_DEPTH_SMALL_TILE;
+    (CE == Elem::U4 && GT == 1)             ? PKV_DEPTH_U4_SINGLE
+    : (GT == 4 && ElemInfo<CE>::bits <= 16) ? PKV_DEPTH_LARGE_TILE
+                                            : PKV_DEPTH_SMALL_TILE;
 
 // ---- scores by a transposed (reduce-scatter) butterfly -------------------
 // When a token row spans exactly one 16-lane DPP row and a block is four wave
