@@ -547,9 +547,11 @@ struct SharedPrefixLayout {
 bool shared_prefix_layout(int B, int G, int max_group, int Hq, int Hkv, int D, int mbs,
                           SharedPrefixLayout& w) {
     // a group's rows share one tile, so the prefix has few work items (groups
-    // x kv heads): split it 4x finer than the multi-query default (measured
-    // on the 16-prompt x 4-sample workload: 108.6 / 99.9 / 97.5 us for 1x /
-    // 2x / 4x)
+    // x kv heads); the default rule would cut them into short partitions,
+    // yet each split adds partials and a merge.  Counting every group four
+    // times gives longer partitions (measured on the 16-prompt x 4-sample
+    // workload with 1x / 2x / 4x the groups: 3 / 2 / 1 partitions, 108.6 /
+    // 99.9 / 97.5 us)
     w.P = pkv_multi_default_partition_size(G > 0x7fffffff / 4 ? 0x7fffffff : G * 4, max_group,
                                            Hq, Hkv, mbs);
     if (w.P <= 0) return false;
