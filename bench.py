@@ -645,8 +645,9 @@ def bench_sampling(args):
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": ("paged_multi_kernel + paged_decode_kernel + prefix_merge_kernel (events "
-                       "span the three)" if shared else "paged_decode_kernel"),
+            "kernel": ("paged_multi_kernel + paged_decode_kernel (events span the two; the "
+                       "decode merges the prompt partials in its epilogue)" if shared
+                       else "paged_decode_kernel"),
             "kernel_sha": kernel_sha(),
             "note": "achieved = unique bytes (each physical block once) / kernel time; value "
                     "counts every sequence's context, so shared prompt blocks count once per "

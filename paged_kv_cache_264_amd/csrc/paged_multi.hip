@@ -51,7 +51,12 @@ typedef short s16x4_v __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_v __attribute__((ext_vector_type(4)));
 
 constexpr int kRows = 16;
-constexpr int kWaves = 4;
+#ifndef PKV_MULTI_WAVES
+#define PKV_MULTI_WAVES 4
+#endif
+// waves per work-group of the short-run kernel (8 measured slower on MI355X:
+// verify 409.5 -> 425.0 us, shared-prefix sampling decode 97.0 -> 98.8 us)
+constexpr int kWaves = PKV_MULTI_WAVES;
 constexpr int kThreads = kWaves * 64;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kNegBig = -3.0e38f;
