@@ -2,8 +2,9 @@
 
 A step is one pass of the whole hot path over one synthetic batch: the
 slot-mapped cache write of every sequence's new token (INT8 quantize-on-write
-for the INT8 cache), then split-context paged decode attention with its
-in-kernel partition merge.  Inputs are resident in HBM before timing starts.
+for the INT8 cache), then split-context paged decode attention, then (for
+sequences cut into more than one partition) the merge of the partial softmax
+results in a second launch.  Inputs are resident in HBM before timing starts.
 
 Prints ONE JSON line.  `value` is algorithmic bytes moved per step / wall time
 per step (GB/s); `roofline` reports the dominant kernel (paged decode) from HIP

@@ -108,10 +108,12 @@ typedef enum {
  * (lazyllm lesson 4, section 5.3; juejin absmax passage).
  *
  *  k, v          [num_tokens][num_kv_heads][head_dim], src_dtype (F32|F16|BF16)
- *  k_cache/v_cache  pool (see layout above), cache_dtype == src_dtype, I8 or
- *                F8_E4M3
+ *  k_cache/v_cache  pool (see layout above), cache_dtype == src_dtype, I8,
+ *                F8_E4M3 or U4
  *  k_scale/v_scale  required iff cache_dtype is I8, F8_E4M3 or U4, else
- *                ignored (may be NULL)
+ *                ignored (may be NULL); U4: 8-byte aligned (each row's
+ *                (x_min, range) pair is stored as one 8-byte word), else
+ *                PKV_ERR_SHAPE
  *  slot_mapping  token i goes to block slot/16, offset slot%16 for every kv
  *                head; slot < 0 skips the token.  Slots must be distinct.
  *

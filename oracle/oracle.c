@@ -358,7 +358,12 @@ int oracle_paged_multi(double* out, const void* q, int q_dtype, const void* k_ca
 /* Split-context partials.  A context of N tokens is cut into
  * count = ceil(N / P) partitions (P = partition_size) of equal length, rounded
  * up to whole blocks: span = block_size * ceil(ceil(N / count) / block_size);
- * partition p holds tokens [p*span, min((p+1)*span, N)).
+ * partition p holds tokens [p*span, min((p+1)*span, N)).  The pages fix no
+ * split (the merge of running maxima and sums is exact whatever the split:
+ * caojiahao2.github.io section 3.2), so this is a reading: the same number
+ * of partitions as cutting at multiples of P, but of equal length, so that
+ * no partition is a short stub.  The boundaries are pinned by hand-computed
+ * spans in the tests; the final output does not depend on them.
  * m, l: double [B][Hq][NP]; o: double [B][Hq][NP][D].  Partitions with no
  * token get m = -inf, l = 0, o = 0.  The max score m is in natural-log units
  * of the score s = scale * <q, k>. */

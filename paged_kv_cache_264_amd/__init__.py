@@ -188,18 +188,25 @@ def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blo
                                              max_blocks_per_seq, partition_size)
 
 
-_ws_cache: dict = {}
-
-
 def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
-    """A workspace of at least nbytes on `device`, reused by later calls on
-    the same device (calls on one stream run one after another)."""
-    key = (device.type, device.index)
-    ws = _ws_cache.get(key)
-    if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
-        _ws_cache[key] = ws
-    return ws
+    """A workspace of at least nbytes for one call, from torch's caching
+    allocator on the current stream.  The allocator hands a freed block to
+    another allocation only on the stream it was allocated on (in stream
+    order), so calls on different streams never share partials, and the
+    buffer stays valid until the call's kernels have run."""
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def _out(out, q, name="out"):
+    """The caller's output buffer (same dtype and shape as q), or a new one."""
+    if out is None:
+        return torch.empty_like(q)
+    _dev(out, name, dtype=q.dtype, ndim=3)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError(f"{name} must have q's shape {tuple(q.shape)} (got {tuple(out.shape)})")
+    if out.device != q.device:
+        raise ValueError(f"{name} must be on q's device")
+    return out
 
 
 def kv_cache_write(k, v, k_cache, v_cache, slot_mapping, k_scale=None, v_scale=None):
@@ -246,15 +253,15 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, ou
     """softmax(scale * q K^T) V per sequence and q head over the paged cache."""
     B, Hq, D, NB, Hkv, bs = _decode_common(q, k_cache, v_cache, block_tables, context_lens,
                                            k_scale, v_scale)
-    if out is None:
-        out = torch.empty_like(q)
-    _dev(out, "out", dtype=q.dtype, ndim=3)
+    out = _out(out, q)
     mbs = block_tables.shape[1]
     need = decode_workspace_size(B, Hq, Hkv, D, mbs, partition_size)
     if workspace is None:
         workspace = _workspace(q.device, need)
     else:
         _dev(workspace, "workspace")
+        if workspace.device != q.device:
+            raise ValueError("workspace must be on q's device")
     rc = _load().pkv_paged_attn_decode(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
         _ptr(block_tables), mbs, _ptr(context_lens), B, Hq, Hkv, D, bs, NB, float(scale),
@@ -275,15 +282,15 @@ def paged_attn_decode_append(q, k_new, v_new, k_cache, v_cache, block_tables, co
     _dev(v_new, "v_new", dtype=q.dtype, ndim=3)
     if tuple(k_new.shape) != (B, Hkv, D) or v_new.shape != k_new.shape:
         raise ValueError("k_new and v_new must be [num_seqs][num_kv_heads][head_dim]")
-    if out is None:
-        out = torch.empty_like(q)
-    _dev(out, "out", dtype=q.dtype, ndim=3)
+    out = _out(out, q)
     mbs = block_tables.shape[1]
     need = decode_workspace_size(B, Hq, Hkv, D, mbs, partition_size)
     if workspace is None:
         workspace = _workspace(q.device, need)
     else:
         _dev(workspace, "workspace")
+        if workspace.device != q.device:
+            raise ValueError("workspace must be on q's device")
     rc = _load().pkv_paged_attn_decode_append(
         _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
         _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), mbs, _ptr(context_lens), B, Hq, Hkv,
@@ -323,15 +330,15 @@ def paged_attn_decode_shared_prefix(q, k_cache, v_cache, block_tables, context_l
         _dev(v_new, "v_new", dtype=q.dtype, ndim=3)
         if tuple(k_new.shape) != (B, Hkv, D) or v_new.shape != k_new.shape:
             raise ValueError("k_new and v_new must be [num_seqs][num_kv_heads][head_dim]")
-    if out is None:
-        out = torch.empty_like(q)
-    _dev(out, "out", dtype=q.dtype, ndim=3)
+    out = _out(out, q)
     mbs = block_tables.shape[1]
     need = shared_prefix_workspace_size(B, G, int(max_group_size), Hq, Hkv, D, mbs)
     if workspace is None:
         workspace = _workspace(q.device, need)
     else:
         _dev(workspace, "workspace")
+        if workspace.device != q.device:
+            raise ValueError("workspace must be on q's device")
     rc = _load().pkv_paged_attn_decode_shared_prefix(
         _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
         _ptr(block_tables), mbs, _ptr(context_lens), _ptr(prefix_lens), _ptr(group_start), G,
@@ -357,9 +364,7 @@ def paged_attn_decode_sliding(q, k_cache, v_cache, block_tables, context_lens, s
         _dev(v_new, "v_new", dtype=q.dtype, ndim=3)
         if tuple(k_new.shape) != (B, Hkv, D) or v_new.shape != k_new.shape:
             raise ValueError("k_new and v_new must be [num_seqs][num_kv_heads][head_dim]")
-    if out is None:
-        out = torch.empty_like(q)
-    _dev(out, "out", dtype=q.dtype, ndim=3)
+    out = _out(out, q)
     mbs = block_tables.shape[1]
     mbs_eff = min(mbs, int(sliding_window) // BLOCK_SIZE + 2) if sliding_window > 0 else mbs
     need = decode_workspace_size(B, Hq, Hkv, D, mbs_eff, partition_size)
@@ -367,6 +372,8 @@ def paged_attn_decode_sliding(q, k_cache, v_cache, block_tables, context_lens, s
         workspace = _workspace(q.device, need)
     else:
         _dev(workspace, "workspace")
+        if workspace.device != q.device:
+            raise ValueError("workspace must be on q's device")
     rc = _load().pkv_paged_attn_decode_sliding(
         _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
         _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), mbs, _ptr(context_lens), B, Hq, Hkv,
@@ -395,9 +402,7 @@ def paged_attn_multi(q, k_cache, v_cache, block_tables, context_lens, query_star
     if D2 != D or v_cache.shape != k_cache.shape or query_start_loc.shape[0] != B + 1 or \
             block_tables.shape[0] != B:
         raise ValueError("q / cache / table / query_start_loc shapes disagree")
-    if out is None:
-        out = torch.empty_like(q)
-    _dev(out, "out", dtype=q.dtype, ndim=3)
+    out = _out(out, q)
     mbs = block_tables.shape[1]
     L = _load()
     P = partition_size or L.pkv_multi_default_partition_size(B, int(max_query_len), Hq, Hkv, mbs)
@@ -406,6 +411,8 @@ def paged_attn_multi(q, k_cache, v_cache, block_tables, context_lens, query_star
         workspace = _workspace(q.device, need)
     else:
         _dev(workspace, "workspace")
+        if workspace.device != q.device:
+            raise ValueError("workspace must be on q's device")
     rc = L.pkv_paged_attn_multi(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), mbs,
         _ptr(context_lens), _ptr(query_start_loc), B, T, int(max_query_len), Hq, Hkv, D, bs, NB,
@@ -440,7 +447,7 @@ def paged_attn_decode_partials(q, k_cache, v_cache, block_tables, context_lens, 
         if tuple(m.shape) != (B, Hq, NP) or l.shape != m.shape or tuple(o.shape) != (B, Hq, NP, D):
             raise ValueError("partials must be [B][Hq][NP] and [B][Hq][NP][D]")
     if out is not None:
-        _dev(out, "out", dtype=q.dtype, ndim=3)
+        out = _out(out, q)
     rc = _load().pkv_paged_attn_decode_partials(
         _ptr(out), _ptr(m), _ptr(l), _ptr(o), _ptr(q), _ptr(k_cache), _ptr(v_cache),
         _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), mbs, _ptr(context_lens), B, Hq, Hkv, D,
@@ -459,9 +466,16 @@ def paged_attn_reduce(m_part, l_part, o_part, context_lens, partition_size, out=
     _dev(o_part, "o_part", dtype=torch.float32, ndim=4)
     _dev(context_lens, "context_lens", dtype=torch.int32, ndim=1)
     B, Hq, NP, D = o_part.shape
+    if tuple(m_part.shape) != (B, Hq, NP) or l_part.shape != m_part.shape:
+        raise ValueError(f"m_part and l_part must be [B][Hq][NP] = {(B, Hq, NP)} (got "
+                         f"{tuple(m_part.shape)}, {tuple(l_part.shape)})")
+    if context_lens.shape[0] != B:
+        raise ValueError(f"context_lens needs one entry per sequence ({B})")
     if out is None:
         out = torch.empty((B, Hq, D), dtype=out_dtype, device=o_part.device)
     _dev(out, "out", ndim=3)
+    if tuple(out.shape) != (B, Hq, D):
+        raise ValueError(f"out must be [B][Hq][D] = {(B, Hq, D)} (got {tuple(out.shape)})")
     rc = _load().pkv_paged_attn_reduce(_ptr(out), _ptr(m_part), _ptr(l_part), _ptr(o_part),
                                        _ptr(context_lens), B, Hq, D, int(partition_size), NP,
                                        1 if skip_single_partition else 0,

@@ -900,7 +900,12 @@ void paged_decode_kernel(DecodeArgs a) {
                     // p (x_min + step c) = (p step) c + p x_min: the codes take
                     // one FMA each, p x_min a running scalar.  Masked rows get
                     // step = x_min = 0 (their values may be anything, NaN too).
-                } else if constexpr (!kInt8) {
+                } else if constexpr (!kInt8 || CE == Elem::F8) {
+                    // rows before the first attended position are selected
+                    // away: their bytes may be anything (an e4m3 NaN code too),
+                    // and a zero weight times NaN would still be NaN.  INT8
+                    // codes always widen to finite values, which the zero
+                    // weight of an invalid row cancels.
                     if (below_lo) {
 #pragma unroll
                         for (int e = 0; e < E; ++e) vx[e] = valid[u] ? vx[e] : 0.f;

@@ -242,6 +242,10 @@ pkv_status pkv_kv_cache_write(const void* k, const void* v, void* k_cache, void*
         return fail(PKV_ERR_NULL, "k_scale and v_scale are required for an INT8 / FP8 / 4-bit cache");
     if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
         return fail(PKV_ERR_SHAPE, "k, v, k_cache and v_cache must be 16-byte aligned");
+    // a 4-bit row's (x_min, range) pair is stored as one 8-byte word
+    if (cache_dtype == PKV_U4 &&
+        ((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 7u))
+        return fail(PKV_ERR_SHAPE, "4-bit k_scale and v_scale must be 8-byte aligned");
     pkv::CacheWriteArgs a{k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping,
                           num_tokens, num_blocks, num_kv_heads};
     return hip_status(

@@ -157,10 +157,6 @@ struct ReduceArgs {
 hipError_t launch_paged_reduce(const ReduceArgs& a, int out_dtype, int head_dim,
                                hipStream_t stream);
 
-// Merge, per (sequence, q head), of the partials over a shared prefix
-// (partitions of the prefix length, stride num_partitions) with the one
-// partial over the sequence's own positions after it.
-
 struct CacheWriteArgs {
     const void* k;
     const void* v;

@@ -55,13 +55,14 @@ class OracleView:
             j0 = self.first_block(n)
             blocks.extend(int(x) for x in lay.block_tables[s, j0:W.blocks_needed(n)])
         self.block_ids = np.asarray(blocks, np.int64)
-        remap = {b: i for i, b in enumerate(self.block_ids)}
-        self.remap = remap
+        # pool id -> compacted id (-1: not used by these sequences)
+        self.remap = np.full(batch.num_blocks, -1, np.int64)
+        self.remap[self.block_ids] = np.arange(len(self.block_ids))
         mbs = lay.block_tables.shape[1]
         bt = np.full((len(self.seqs), mbs), -1, np.int32)
         for i, (s, n) in enumerate(zip(self.seqs, lens)):
-            for j in range(self.first_block(n), W.blocks_needed(n)):
-                bt[i, j] = remap[int(lay.block_tables[s, j])]
+            j0, j1 = self.first_block(n), W.blocks_needed(n)
+            bt[i, j0:j1] = self.remap[lay.block_tables[s, j0:j1]]
         self.block_tables = bt
         self.context_lens = lens.astype(np.int32)
         self.q = host(batch.q[torch.from_numpy(self.seqs).to(batch.q.device)])
@@ -90,8 +91,10 @@ class OracleView:
                                   self.cache_dtype,
                                   self.k_scale, self.v_scale)
         else:
-            self.k_cache = host(batch.k_cache[idx]) if len(idx) else None
-            self.v_cache = host(batch.v_cache[idx]) if len(idx) else None
+            # (no block used at all: one pool block that no table entry names)
+            idx = idx if len(idx) else torch.zeros(1, dtype=torch.int64, device=idx.device)
+            self.k_cache = host(batch.k_cache[idx])
+            self.v_cache = host(batch.v_cache[idx])
             self.k_scale = self.v_scale = None
 
     def first_block(self, n: int) -> int:
@@ -103,11 +106,9 @@ class OracleView:
 
     def compact_slots(self, slots):
         slots = np.asarray(slots, np.int64)
-        out = np.empty_like(slots)
-        for i, s in enumerate(slots):
-            out[i] = (-1 if s < 0 or int(s) // BS not in self.remap
-                      else self.remap[int(s) // BS] * BS + int(s) % BS)
-        return out
+        ok = (slots >= 0) & (slots < len(self.remap) * BS)
+        blk = np.where(ok, self.remap[np.where(ok, slots // BS, 0)], -1)
+        return np.where(blk >= 0, blk * BS + slots % BS, -1).astype(np.int64)
 
     def write_new_tokens(self, batch: W.Batch):
         """The decode step's cache write of the new tokens, on the host image."""
@@ -147,3 +148,53 @@ def max_abs_err(gpu_out: torch.Tensor, ref: np.ndarray) -> float:
     if not np.isfinite(g).all():
         return float("inf")
     return float(np.abs(g - ref).max()) if g.size else 0.0
+
+
+def hide_before_window(batch: W.Batch, window: int, n_of) -> torch.Tensor:
+    """Block tables with the entries of whole blocks before the window set to
+    -1 (as after pkv_bm_release_before), and the positions before the window
+    inside its first block poisoned on the GPU: NaN K/V for float caches, NaN
+    scales for quantized ones, and for FP8 also the NaN code 0x7F in K and V,
+    so that a zero weight times such a value cannot pass.  n_of[b] is the
+    context length the decode will see."""
+    bt = batch.block_tables.clone()
+    for b in range(batch.B):
+        n = int(n_of[b])
+        if window <= 0 or n <= window:
+            continue
+        lo = n - window
+        j0 = lo // BS
+        bt[b, :j0] = -1
+        if lo % BS:
+            blk = int(batch.layout.block_tables[b, j0])
+            if batch.k_scale is not None:
+                batch.k_scale[blk, :, :lo % BS] = float("nan")
+                batch.v_scale[blk, :, :lo % BS] = float("nan")
+                if batch.k_cache.dtype == torch.float8_e4m3fn:
+                    batch.k_cache.view(torch.uint8)[blk, :, :lo % BS] = 0x7F
+                    batch.v_cache.view(torch.uint8)[blk, :, :lo % BS] = 0x7F
+            else:
+                batch.k_cache[blk, :, :lo % BS] = float("nan")
+                batch.v_cache[blk, :, :lo % BS] = float("nan")
+    return bt
+
+
+def guarded(shape, dtype: torch.dtype, device="cuda", guard_bytes: int = 512):
+    """A contiguous tensor of `shape` inside a larger buffer whose first and
+    last guard_bytes hold a sentinel bit pattern (0xA5 bytes).  Returns
+    (tensor, check) where check() asserts the guard bands are untouched."""
+    el = torch.empty((), dtype=dtype).element_size()
+    g = guard_bytes // el
+    n = int(np.prod(shape)) if len(shape) else 1
+    raw = torch.full((guard_bytes * 2 + n * el,), 0xA5, dtype=torch.uint8, device=device)
+    t = raw[guard_bytes:guard_bytes + n * el].view(dtype).view(*shape)
+    assert t.data_ptr() % 256 == 0 or guard_bytes % 256 != 0
+
+    def check():
+        head = raw[:guard_bytes].cpu().numpy()
+        tail = raw[guard_bytes + n * el:].cpu().numpy()
+        assert (head == 0xA5).all(), "write before the buffer"
+        assert (tail == 0xA5).all(), "write past the buffer"
+        assert g >= 0
+
+    return t, check

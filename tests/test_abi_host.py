@@ -153,6 +153,16 @@ def test_cache_write_argument_errors(lib):
     assert call(13, F8) == ENULL            # FP8 without scales
     assert call(0, None) == ENULL
     assert call(13, I8) == ENULL            # INT8 without scales
+    # 4-bit rows store (x_min, range) as one 8-byte word: scales must be
+    # 8-byte aligned (the decode entry points ask the same)
+    u4 = list(base)
+    u4[13] = U4
+    u4[4], u4[5] = ctypes.c_void_p(0x1004), FAKE
+    assert f(*u4) == ESHAPE
+    u4[4], u4[5] = FAKE, ctypes.c_void_p(0x100c)
+    assert f(*u4) == ESHAPE
+    u4[9] = 64                              # 4-bit rows need head_dim 128 or 256
+    assert f(*u4) == EUNSUP
     assert call(7, 0) == OK                 # nothing to write: no launch
 
 

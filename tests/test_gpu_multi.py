@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import workloads as W
-from helpers import BS, DT, TOL, OracleView, as_f64, host
+from helpers import BS, DT, TOL, OracleView, as_f64, guarded, host
 
 pytestmark = pytest.mark.gpu
 U_P = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
@@ -87,29 +87,72 @@ def test_multi_single_query_matches_decode(pkv):
     assert float((multi.float() - dec.float()).abs().max()) <= 2e-3 + 2.0 ** -11 * 5
 
 
-def test_multi_verify_workload_sample(pkv):
-    """The speculative-verification shape at full size: 64 LLaMA-7B sequences,
-    8 queries each, U[512, 4096] contexts; 4 sequences checked by the oracle."""
-    batch = W.make_batch("verify", device="cuda", poison=True)
+_FULL_RUNS: dict = {}
+
+
+def _full_multi_run(pkv, name):
+    """A multi-query workload at full size as bench.py launches it (the cache
+    write of the query tokens' K/V, then pkv_paged_attn_multi with the default
+    partition size), output inside sentinel guard bands; run once per module
+    and kept for the checks that follow."""
+    if name in _FULL_RUNS:
+        return _FULL_RUNS[name]
+    batch = W.make_batch(name, device="cuda", poison=True)
     ql = batch.cfg["q_len"]
-    T = batch.B * ql
-    q = W.token_rows(T, batch.Hq, batch.D, "f16", batch.seed, W.S_STEP_Q).cuda()
-    qsl = (np.arange(batch.B + 1) * ql).astype(np.int32)
-    out = pkv.paged_attn_multi(q, batch.k_cache, batch.v_cache, batch.block_tables,
-                               batch.context_lens, torch.from_numpy(qsl).cuda(), batch.scale, ql)
+    lens = batch.layout.context_lens.astype(np.int64)
+    qlens = np.minimum(lens, ql)
+    qsl = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    T = int(qsl[-1])
+    q = W.token_rows(T, batch.Hq, batch.D, "f16", batch.seed, W.S_STEP_Q, "cuda")
+    k_new = W.token_rows(T, batch.Hkv, batch.D, "f16", batch.seed, W.S_NEWK, "cuda")
+    v_new = W.token_rows(T, batch.Hkv, batch.D, "f16", batch.seed, W.S_NEWV, "cuda")
+    slots = np.concatenate([W.slots_for(batch.layout, b, np.arange(int(n) - int(k), int(n)))
+                            for b, (n, k) in enumerate(zip(lens, qlens))])
+    pkv.kv_cache_write(k_new, v_new, batch.k_cache, batch.v_cache, torch.from_numpy(slots).cuda())
+    out, out_guard = guarded((T, batch.Hq, batch.D), torch.float16)
+    pkv.paged_attn_multi(q, batch.k_cache, batch.v_cache, batch.block_tables,
+                         batch.context_lens, torch.from_numpy(qsl).cuda(), batch.scale, ql,
+                         out=out)
     torch.cuda.synchronize()
-    seqs = [0, 17, 40, 63]
-    view = OracleView(batch, seqs)
-    rows = np.concatenate([np.arange(s * ql, (s + 1) * ql) for s in seqs])
-    sub_qsl = (np.arange(len(seqs) + 1) * ql).astype(np.int32)
+    out_guard()
+    got = as_f64(out)
+    assert np.isfinite(got).all()
+    _FULL_RUNS[name] = (batch, q, qsl, qlens, got)
+    return _FULL_RUNS[name]
+
+
+def _full_multi_check(pkv, name, seqs):
+    """Every query row and head of the given sequences against the oracle."""
+    batch, q, qsl, qlens, got = _full_multi_run(pkv, name)
+    seqs = np.asarray(seqs, np.int64)
+    view = OracleView(batch, seqs)        # the pool with the queries' K/V
+    rows = np.concatenate([np.arange(qsl[s], qsl[s + 1]) for s in seqs])
+    sub_qsl = np.concatenate([[0], np.cumsum(qlens[seqs])]).astype(np.int32)
     ref = oracle.paged_multi(host(q[torch.from_numpy(rows).cuda()]), "f16", view.k_cache,
                              view.v_cache, "f16", view.block_tables, view.context_lens, sub_qsl,
                              batch.scale)
-    got = as_f64(out)[rows]
-    assert np.isfinite(as_f64(out)).all()
-    err = float(np.abs(got - ref).max())
-    print(f"[multi verify] max_abs_err={err:.3e}", flush=True)
-    assert err <= TOL["f16"] + U_P["f16"] * 5.5
+    vals = view.v_cache.view(np.float16).astype(np.float64).reshape(-1)
+    vmax = float(np.abs(vals[np.isfinite(vals)]).max())
+    err = float(np.abs(got[rows] - ref).max())
+    tol = TOL["f16"] + U_P["f16"] * vmax
+    print(f"[multi {name}] sequences {seqs.tolist()} query rows={len(rows)} "
+          f"max_abs_err={err:.3e} tol={tol:.2e}", flush=True)
+    assert err <= tol
+
+
+def test_multi_verify_workload_full(pkv):
+    """The speculative-verification shape: 64 LLaMA-7B sequences, 8 queries
+    each, U[512, 4096] contexts (the short-run kernel); every sequence."""
+    _full_multi_check(pkv, "verify", np.arange(W.CONFIGS["verify"]["B"]))
+
+
+@pytest.mark.parametrize("part", range(4))
+def test_multi_prefill_workload_full(pkv, part):
+    """The chunked-prefill shape: 16 LLaMA-7B sequences, the last 512 of
+    U[1024, 4096] positions being queries (the tiled kernel).  One launch;
+    the oracle checks a quarter of the sequences per case (every query row
+    and head of each), all 16 over the four cases."""
+    _full_multi_check(pkv, "prefill", np.arange(part, W.CONFIGS["prefill"]["B"], 4))
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
@@ -141,34 +184,3 @@ def test_multi_negative_and_zero_scale(pkv, scale, qlens, P):
     plain mean of V over each query's positions.  Long query runs (the tiled
     kernel) and short ones, whole and split contexts."""
     _run(pkv, "f16", 128, 8, 4, [1000, 300, 777], qlens, P=P, seed=7, scale=scale)
-
-
-def test_multi_prefill_workload_sample(pkv):
-    """The chunked-prefill shape at full size (the tiled kernel as the bench
-    launches it): 16 LLaMA-7B sequences, the last 512 of U[1024, 4096]
-    positions being queries; the shortest and the longest sequence checked
-    against the oracle on every query row and head."""
-    batch = W.make_batch("prefill", device="cuda", poison=True)
-    ql = batch.cfg["q_len"]
-    lens = batch.layout.context_lens.astype(np.int64)
-    qlens = np.minimum(lens, ql)
-    qsl = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
-    T = int(qsl[-1])
-    q = W.token_rows(T, batch.Hq, batch.D, "f16", batch.seed, W.S_STEP_Q).cuda()
-    out = pkv.paged_attn_multi(q, batch.k_cache, batch.v_cache, batch.block_tables,
-                               batch.context_lens, torch.from_numpy(qsl).cuda(), batch.scale, ql)
-    torch.cuda.synchronize()
-    assert np.isfinite(as_f64(out)).all()
-    seqs = [int(np.argmin(lens)), int(np.argmax(lens))]
-    view = OracleView(batch, seqs)
-    rows = np.concatenate([np.arange(qsl[s], qsl[s + 1]) for s in seqs])
-    sub_qsl = np.concatenate([[0], np.cumsum(qlens[seqs])]).astype(np.int32)
-    ref = oracle.paged_multi(host(q[torch.from_numpy(rows).cuda()]), "f16", view.k_cache,
-                             view.v_cache, "f16", view.block_tables, view.context_lens, sub_qsl,
-                             batch.scale)
-    err = float(np.abs(as_f64(out)[rows] - ref).max())
-    vals = as_f64(batch.v_cache[torch.from_numpy(view.block_ids).cuda()]).reshape(-1)
-    vmax = float(np.abs(vals[np.isfinite(vals)]).max())
-    print(f"[multi prefill] seqs={seqs} lens={lens[seqs].tolist()} max_abs_err={err:.3e}",
-          flush=True)
-    assert err <= TOL["f16"] + U_P["f16"] * vmax

@@ -14,8 +14,8 @@ import torch
 
 import oracle
 import workloads as W
-from helpers import (BS, DT, TOL, OracleView, as_f64, gpu_populate, gpu_step, host,
-                     max_abs_err, tol_for)
+from helpers import (BS, DT, TOL, OracleView, as_f64, gpu_populate, gpu_step, guarded,
+                     hide_before_window, host, max_abs_err, tol_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -328,32 +328,116 @@ def test_int8_codes_bit_exact_many_rows(pkv):
 
 
 # ---------------------------------------------------------------------------
-# the five workloads at full size, in the launch configuration the bench uses
+# the workloads at full size, through the call and the launch configuration
+# the bench times, every sequence and every head compared
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["tiny", "llama7b", "gqa", "long", "int8", "fp8", "int4"])
+FULL = ["tiny", "llama7b", "gqa", "long", "int8", "fp8", "int4", "window"]
+
+
+def bench_partition(pkv, batch):
+    """(partition size, effective max blocks per sequence) as bench.py picks
+    them: the workload's own partition size, else the library default over
+    the blocks a sequence can touch (a window's blocks only)."""
+    mbs = batch.block_tables.shape[1]
+    window = int(batch.cfg.get("window", 0))
+    mbs_eff = min(mbs, window // BS + 2) if window else mbs
+    P = batch.cfg.get("partition_size", 0)
+    return (P or pkv.default_partition_size(batch.B, batch.Hq, batch.Hkv, mbs_eff)), mbs_eff
+
+
+def _slot_rows(t, blk, off):
+    """Rows [B][Hkv][...] of a pool tensor at (block blk[i], offset off[i])."""
+    if isinstance(t, torch.Tensor):
+        return host(t[torch.from_numpy(blk).to(t.device), :, torch.from_numpy(off).to(t.device)])
+    return t[blk, :, off]
+
+
+@pytest.mark.parametrize("name", FULL)
 def test_full_config(pkv, name):
+    """The fused step (pkv_paged_attn_decode_append; the sliding-window entry
+    with its append for the window workload) with the bench's partition size,
+    against the oracle's cache write of the new tokens followed by its decode,
+    on every sequence and head; the appended slots' bytes (and scales) bit for
+    bit; output and workspace inside sentinel guard bands.  Then the separate
+    path (cache write, decode) on the same batch, against the same result."""
     batch = W.make_batch(name, device="cuda", poison=True)
     gpu_populate(pkv, batch)
+    window = int(batch.cfg.get("window", 0))
+    view = OracleView(batch, np.arange(batch.B), window=window)  # host copies before the step
     lens = batch.layout.context_lens
-    order = np.argsort(lens)
-    seqs = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2])})
-    P = batch.cfg.get("partition_size", 0)
-    out, view = _check_step(pkv, batch, seqs=seqs, partition_size=P)
-    if name == "int8":
-        # the library's INT8 pool equals the oracle's, byte for byte, on the
-        # blocks of the sampled sequences
+    bt = hide_before_window(batch, window, lens) if window else batch.block_tables
+    P, mbs_eff = bench_partition(pkv, batch)
+    NP = pkv.num_partitions(mbs_eff, P)
+    out, out_guard = guarded(tuple(batch.q.shape), batch.q.dtype)
+    need = pkv.decode_workspace_size(batch.B, batch.Hq, batch.Hkv, batch.D, mbs_eff, P)
+    ws, ws_guard = guarded((need,), torch.uint8)
+    kw = dict(k_scale=batch.k_scale, v_scale=batch.v_scale, partition_size=P, workspace=ws)
+    if window:
+        pkv.paged_attn_decode_sliding(batch.q, batch.k_cache, batch.v_cache, bt,
+                                      batch.context_lens, batch.scale, window, k_new=batch.k_new,
+                                      v_new=batch.v_new, out=out, **kw)
+    else:
+        pkv.paged_attn_decode_append(batch.q, batch.k_new, batch.v_new, batch.k_cache,
+                                     batch.v_cache, bt, batch.context_lens, batch.scale,
+                                     out=out, **kw)
+    torch.cuda.synchronize()
+    out_guard()
+    ws_guard()
+    view.write_new_tokens(batch)
+    ref = view.decode()
+    err = max_abs_err(out, ref)
+    tol = tol_for(DT[batch.q.dtype], DT[batch.k_cache.dtype])
+    print(f"[full fused] {name} B={batch.B} P={P} NP={NP} sequences={batch.B} "
+          f"max_abs_err={err:.3e} tol={tol:.1e}", flush=True)
+    assert torch.isfinite(out.float()).all(), "non-finite output (poisoned slot read?)"
+    assert err <= tol
+
+    # the appended slot (position N-1) of every sequence, every kv head
+    has = lens > 0
+    t = (lens[has] - 1).astype(np.int64)
+    rows = np.arange(batch.B)[has]
+    blk_g = batch.layout.block_tables[rows, t // BS].astype(np.int64)
+    blk_o = view.block_tables[rows, t // BS].astype(np.int64)
+    off = t % BS
+    for g_t, o_t in ((batch.k_cache, view.k_cache), (batch.v_cache, view.v_cache)):
+        assert np.array_equal(_slot_rows(g_t, blk_g, off).view(np.uint8),
+                              _slot_rows(o_t, blk_o, off).view(np.uint8))
+    if batch.k_scale is not None:
+        for g_t, o_t in ((batch.k_scale, view.k_scale), (batch.v_scale, view.v_scale)):
+            assert np.array_equal(_slot_rows(g_t, blk_g, off).view(np.uint32),
+                                  _slot_rows(o_t, blk_o, off).view(np.uint32))
+        # the whole quantized pool of the batch equals the oracle's, codes byte
+        # for byte and the scales of every attended slot bit for bit
         idx = torch.from_numpy(view.block_ids).cuda()
-        assert np.array_equal(host(batch.k_cache[idx]), view.k_cache)
-        assert np.array_equal(host(batch.v_cache[idx]), view.v_cache)
-        used = np.zeros((len(view.block_ids), batch.Hkv, BS), bool)
-        for i, (s, n) in enumerate(zip(view.seqs, view.context_lens)):
-            for t in range(n):
-                used[view.block_tables[i, t // BS], :, t % BS] = True
-        assert np.array_equal(host(batch.k_scale[idx])[used].view(np.uint32),
-                              view.k_scale[used].view(np.uint32))
-        assert np.array_equal(host(batch.v_scale[idx])[used].view(np.uint32),
-                              view.v_scale[used].view(np.uint32))
+        assert np.array_equal(host(batch.k_cache[idx]).view(np.uint8), view.k_cache.view(np.uint8))
+        assert np.array_equal(host(batch.v_cache[idx]).view(np.uint8), view.v_cache.view(np.uint8))
+        used = np.zeros((len(view.block_ids), BS), bool)
+        for i, n in enumerate(view.context_lens):
+            n = int(n)
+            j0 = view.first_block(n)
+            pos = np.arange(j0 * BS, n)
+            used[view.block_tables[i, pos // BS], pos % BS] = True
+        for g_t, o_t in ((batch.k_scale, view.k_scale), (batch.v_scale, view.v_scale)):
+            g_h = host(g_t[idx]).transpose(0, 2, 1, *range(3, g_t.dim()))
+            o_h = o_t.transpose(0, 2, 1, *range(3, o_t.ndim))
+            assert np.array_equal(g_h[used].view(np.uint32), o_h[used].view(np.uint32))
+
+    # the separate path: the cache write stores the same bytes again
+    pkv.kv_cache_write(batch.k_new, batch.v_new, batch.k_cache, batch.v_cache, batch.slot_new,
+                       batch.k_scale, batch.v_scale)
+    out2 = torch.empty_like(batch.q)
+    if window:
+        pkv.paged_attn_decode_sliding(batch.q, batch.k_cache, batch.v_cache, bt,
+                                      batch.context_lens, batch.scale, window, out=out2, **kw)
+    else:
+        pkv.paged_attn_decode(batch.q, batch.k_cache, batch.v_cache, bt, batch.context_lens,
+                              batch.scale, out=out2, **kw)
+    torch.cuda.synchronize()
+    ws_guard()
+    err2 = max_abs_err(out2, ref)
+    print(f"[full separate] {name} max_abs_err={err2:.3e}", flush=True)
+    assert err2 <= tol
 
 
 def test_workspace_reuse_across_shapes(pkv):

@@ -16,7 +16,8 @@ import torch
 
 import oracle
 import workloads as W
-from helpers import BS, DT, OracleView, as_f64, gpu_populate, host, max_abs_err, tol_for
+from helpers import (BS, DT, OracleView, as_f64, gpu_populate, hide_before_window, host,
+                     max_abs_err, tol_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -31,29 +32,6 @@ def pkv():
 def _cfg(dtype, cache, D, Hq, Hkv, lens, seed):
     return dict(B=len(lens), ctx=list(lens), Hq=Hq, Hkv=Hkv, D=D, dtype=dtype, cache=cache,
                 pool=None, seed=seed, max_ctx=max(max(lens), 16))
-
-
-def _hide_before_window(batch, window, n_of):
-    """Tables before the window -> -1; positions before it in its first block
-    -> NaN (K/V, or the scales of a scaled cache).  n_of[b] is the context
-    length the decode will see."""
-    bt = batch.block_tables.clone()
-    for b in range(batch.B):
-        n = int(n_of[b])
-        if window <= 0 or n <= window:
-            continue
-        lo = n - window
-        j0 = lo // BS
-        bt[b, :j0] = -1
-        if lo % BS:
-            blk = int(batch.layout.block_tables[b, j0])
-            if batch.k_scale is not None:
-                batch.k_scale[blk, :, :lo % BS] = float("nan")
-                batch.v_scale[blk, :, :lo % BS] = float("nan")
-            else:
-                batch.k_cache[blk, :, :lo % BS] = float("nan")
-                batch.v_cache[blk, :, :lo % BS] = float("nan")
-    return bt
 
 
 PAIRS = [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"), ("f16", "i8"), ("bf16", "f8")]
@@ -71,7 +49,7 @@ def test_window_decode_matches_oracle(pkv, dtype, cache, window, P):
     pkv.kv_cache_write(batch.k_new, batch.v_new, batch.k_cache, batch.v_cache, batch.slot_new,
                        batch.k_scale, batch.v_scale)
     view.write_new_tokens(batch)
-    bt = _hide_before_window(batch, window, batch.layout.context_lens)
+    bt = hide_before_window(batch, window, batch.layout.context_lens)
     out = pkv.paged_attn_decode_sliding(batch.q, batch.k_cache, batch.v_cache, bt,
                                         batch.context_lens, batch.scale, window,
                                         k_scale=batch.k_scale, v_scale=batch.v_scale,
@@ -94,7 +72,7 @@ def test_window_decode_with_append(pkv, dtype, cache, window):
     batch = W.make_batch(cfg=_cfg(dtype, cache, 128, 16, 2, lens, seed=window), device="cuda")
     gpu_populate(pkv, batch)
     view = OracleView(batch, np.arange(batch.B), window=window)
-    bt = _hide_before_window(batch, window, batch.layout.context_lens)
+    bt = hide_before_window(batch, window, batch.layout.context_lens)
     out = pkv.paged_attn_decode_sliding(batch.q, batch.k_cache, batch.v_cache, bt,
                                         batch.context_lens, batch.scale, window,
                                         k_new=batch.k_new, v_new=batch.v_new,
