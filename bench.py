@@ -41,6 +41,7 @@ WORKLOAD_NAMES = {
     "verify": "llama7b-mha-fp16-speculative-verify-8-queries",
     "prefill": "llama7b-mha-fp16-chunked-prefill-512",
     "sampling": "llama7b-parallel-sampling-shared-prefix-decode",
+    "int8-write": "llama7b-int8kv-cache-write-64-new-tokens",
 }
 KERNEL_SOURCES = ["paged_decode.hip", "pkv_device.h", "pkv_internal.h", "pkv_api.hip"]
 
@@ -102,6 +103,40 @@ def traffic_for(key: str, alg_bytes: int):
     return t, t / alg_bytes
 
 
+def timed_steps(step, steps, stream):
+    """The contract's timed region: `steps` steps bracketed by
+    torch.cuda.synchronize() on both sides, wall clock around it, plus two
+    HIP events on the launch stream at its ends (nothing is recorded between
+    the steps, so the region holds the launches alone).  Returns (wall ms per
+    step, GPU ms per step)."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) * 1e3 / steps, e0.elapsed_time(e1) / steps
+
+
+def per_launch_events(step, steps):
+    """A pass after the timed region with HIP events around the measured
+    launch of every step (its distribution; recording events between launches
+    adds a few microseconds to each step, so this pass is not the timed one).
+    `step(ev0, ev1)` records ev0 / ev1 around the launch.  Returns ms list."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        step(a, b)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -114,7 +149,10 @@ def main():
     if args.config == "sampling":
         bench_sampling(args)
         return
-    if "q_len" in __import__("workloads").CONFIGS[args.config]:
+    if args.config == "int8-write":
+        bench_cache_write(args)
+        return
+    if "q_len" in __import__("workloads").CONFIGS.get(args.config, {}):
         bench_multi(args)
         return
 
@@ -221,19 +259,26 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for e0, e1 in evs:
-        step(e0, e1)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    if args.step == "fused":
+        # one decode launch per step (plus the merge launch when NP > 1): the
+        # events at the ends of the timed region give the average launch
+        ms_per_step, gpu_ms = timed_steps(step, args.steps, stream)
+        dec_avg_ms = gpu_ms
+        timing = ("HIP events at the ends of the timed region on the launch stream, divided by "
+                  "the steps (one decode launch per step" +
+                  (" and one merge launch" if NP > 1 else "") + "; gaps between launches "
+                  "included)")
+    else:
+        # three launches per step: events around the decode launch inside the
+        # timed region
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        it = iter(evs)
+        ms_per_step, gpu_ms = timed_steps(lambda: step(*next(it)), args.steps, stream)
+        dec_avg_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        timing = "HIP events around every decode launch of the timed region"
     assert torch.isfinite(out.float()).all()
-
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    dec_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
-    dec_avg_ms = float(np.mean(dec_ms))
+    dec_ms = per_launch_events(step, args.steps)
     achieved = launch_bytes / (dec_avg_ms * 1e-3) / 1e9
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     traffic, traffic_ratio = traffic_for(f"{args.config}/{args.step}", launch_bytes)
@@ -265,9 +310,12 @@ def main():
         },
         "kv_tokens_per_s": round(kv_tokens / (ms_per_step * 1e-3), 1),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "ms_per_step_gpu_events": round(gpu_ms, 5),
         "decode_kernel_us": round(dec_avg_ms * 1e3, 2),
-        "decode_kernel_us_p10_p50_p90": [round(float(np.percentile(dec_ms, q)) * 1e3, 2)
-                                         for q in (10, 50, 90)],
+        "decode_kernel_timing": timing,
+        "per_launch_events_us_mean_p10_p50_p90": (
+            [round(float(np.mean(dec_ms)) * 1e3, 2)] +
+            [round(float(np.percentile(dec_ms, q)) * 1e3, 2) for q in (10, 50, 90)]),
         "decode_alg_bytes": dec_bytes,
         "launch_alg_bytes": launch_bytes,
         "step_alg_bytes": step_bytes,
@@ -731,6 +779,20 @@ def run_cpu_baseline(batch, cfg_name, target_s, e_kv, e_q, int8, window=0):
     sub = att[:n_seq]
     meta = 8 if e_kv == 0.5 else (4 if int8 else 0)
     alg = W.algorithmic_bytes(sub, batch.Hq, batch.Hkv, batch.D, e_kv, e_q, int8, meta)
+
+    # the same oracle on one thread, on a sample sized to about a third of
+    # target_s (the first sequences, whole)
+    n1 = 1
+    per_tok1 = per_tok * threads
+    while n1 < n_seq and per_tok1 * att[:n1 + 1].sum() < target_s / 3:
+        n1 += 1
+    v1 = view_for(n1) if n1 != n_seq else v
+    t = time.perf_counter()
+    oracle.paged_decode(**v1, nthreads=1)
+    t1_s = time.perf_counter() - t
+    oracle.num_threads(threads)
+    sub1 = att[:n1]
+    alg1 = W.algorithmic_bytes(sub1, batch.Hq, batch.Hkv, batch.D, e_kv, e_q, int8, meta)
     return {
         "value": round(alg / t_s / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
         "sample": f"first {n_seq} of {batch.B} sequences (all {batch.Hq} q heads, "
@@ -739,7 +801,70 @@ def run_cpu_baseline(batch, cfg_name, target_s, e_kv, e_q, int8, window=0):
         "kv_tokens_per_s": round(float(sub.sum()) / t_s, 1),
         "seconds": round(t_s, 3),
         "passes": len(passes),
+        "single_thread": {
+            "value": round(alg1 / t1_s / 1e9, 5), "unit": "GB/s", "cores": 1,
+            "sample": f"first {n1} of {batch.B} sequences ({int(sub1.sum())} context tokens), "
+                      f"one fp64 oracle pass on one thread",
+            "kv_tokens_per_s": round(float(sub1.sum()) / t1_s, 1), "seconds": round(t1_s, 3)},
     }
+
+
+def bench_cache_write(args):
+    """The INT8 workload's cache write alone: the decode step's 64 new tokens
+    (one per sequence, at position context_len - 1, slots from the block
+    tables) quantized on write into the INT8 pool (absmax per (slot, kv head),
+    round half to even).  A step is one pkv_kv_cache_write launch."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_264_amd as pkv
+    import workloads as W
+
+    torch.cuda.set_device(0)
+    cfg = W.CONFIGS["int8"]
+    batch = W.make_batch("int8", device="cuda", seed=args.seed, poison=False)
+    stream = torch.cuda.current_stream()
+    T = int((batch.slot_new >= 0).sum())
+    e_src = 2
+    # read the fp16 rows and the slots, write the codes and one fp32 scale per row
+    alg = T * batch.Hkv * 2 * (batch.D * e_src + batch.D * 1 + 4) + T * 8
+
+    def step(ev0=None, ev1=None):
+        if ev0 is not None:
+            ev0.record(stream)
+        pkv.kv_cache_write(batch.k_new, batch.v_new, batch.k_cache, batch.v_cache,
+                           batch.slot_new, batch.k_scale, batch.v_scale)
+        if ev1 is not None:
+            ev1.record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    ms_per_step, gpu_ms = timed_steps(step, args.steps, stream)
+    per = per_launch_events(step, args.steps)
+    achieved = alg / (gpu_ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC, "value": round(alg / (ms_per_step * 1e-3) / 1e9, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "i8", "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES["int8-write"], "new_tokens": T,
+                   "num_kv_heads": batch.Hkv, "head_dim": batch.D, "block_size": W.BLOCK_SIZE,
+                   "src_dtype": cfg["dtype"], "kv_dtype": "i8", "seed": batch.seed,
+                   "slot_mapping": "position context_len-1 of each sequence, from its block "
+                                   "table", "parallelism": "single-gpu"},
+        "write_kernel_us": round(gpu_ms * 1e3, 3),
+        "per_launch_events_us_mean_p10_p50_p90": (
+            [round(float(np.mean(per)) * 1e3, 3)] +
+            [round(float(np.percentile(per, q)) * 1e3, 3) for q in (10, 50, 90)]),
+        "launch_alg_bytes": alg,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "kv_cache_write_kernel",
+                     "note": "1.6 MB per launch: the launch is bound by its fixed latency, not "
+                             "by HBM; in the decode step the same write is fused into the "
+                             "decode launch"},
+    }
+    print(json.dumps(result), flush=True)
 
 
 if __name__ == "__main__":
