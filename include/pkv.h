@@ -209,6 +209,36 @@ pkv_status pkv_paged_attn_decode_append(void* out, const void* q, const void* k_
                                         pkv_dtype cache_dtype, hipStream_t stream);
 
 /*
+ * pkv_paged_attn_decode_append without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, serving loops
+ * that must not call an allocator, harnesses that forbid it.  The caller
+ * passes inputs and outputs only.  The split-context partials go to a static
+ * device array of PKV_STATIC_SCRATCH_BYTES (32 MiB) that every GPU the library
+ * runs on holds from the first call on that GPU until the process ends; its
+ * address is looked up on that first call (the GPU of `stream`).  The entry
+ * point calls no allocator.
+ *  - A call whose partials need more than PKV_STATIC_SCRATCH_BYTES
+ *    (pkv_decode_workspace_size > PKV_STATIC_SCRATCH_BYTES) returns
+ *    PKV_ERR_WORKSPACE before enqueueing anything.
+ *  - Every call on one GPU uses the same array and it keeps the last call's
+ *    contents: calls that overlap in time on one GPU (different streams, or
+ *    host threads) race and must be serialized by the caller.  Nothing needs
+ *    clearing between calls.
+ * Other arguments, results and errors as for pkv_paged_attn_decode_append.
+ */
+#define PKV_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+pkv_status pkv_paged_attn_decode_append_static(void* out, const void* q, const void* k_new,
+                                               const void* v_new, void* k_cache, void* v_cache,
+                                               float* k_scale, float* v_scale,
+                                               const int32_t* block_tables,
+                                               int max_blocks_per_seq,
+                                               const int32_t* context_lens, int num_seqs,
+                                               int num_q_heads, int num_kv_heads, int head_dim,
+                                               int block_size, int64_t num_blocks, float scale,
+                                               int partition_size, pkv_dtype q_dtype,
+                                               pkv_dtype cache_dtype, hipStream_t stream);
+
+/*
  * Sliding-window decode: as pkv_paged_attn_decode (k_new == v_new == NULL) or
  * pkv_paged_attn_decode_append (both given), but each sequence attends only to
  * its last `sliding_window` positions, [max(0, N_b - sliding_window), N_b)

@@ -16,6 +16,7 @@ import torch
 
 __all__ = [
     "kv_cache_write", "paged_attn_decode", "paged_attn_decode_append",
+    "paged_attn_decode_append_static", "STATIC_SCRATCH_BYTES",
     "paged_attn_decode_sliding", "paged_attn_multi",
     "paged_attn_decode_partials", "paged_attn_reduce",
     "decode_workspace_size", "default_partition_size", "num_partitions",
@@ -89,6 +90,9 @@ def _load():
     L.pkv_paged_attn_decode_append.argtypes = [P, P, P, P, P, P, P, P, P, I, P, I, I, I, I, I,
                                                I64, F, I, P, SZ, I, I, P]
     L.pkv_paged_attn_decode_append.restype = I
+    L.pkv_paged_attn_decode_append_static.argtypes = [P, P, P, P, P, P, P, P, P, I, P, I, I, I,
+                                                      I, I, I64, F, I, I, I, P]
+    L.pkv_paged_attn_decode_append_static.restype = I
     L.pkv_paged_attn_decode_sliding.argtypes = [P, P, P, P, P, P, P, P, P, I, P, I, I, I, I, I,
                                                 I64, F, I, I, P, SZ, I, I, P]
     L.pkv_paged_attn_decode_sliding.restype = I
@@ -297,6 +301,34 @@ def paged_attn_decode_append(q, k_new, v_new, k_cache, v_cache, block_tables, co
         D, bs, NB, float(scale), int(partition_size), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _code(q.dtype, "q"),
         _code(k_cache.dtype, "k_cache"), _stream(q))
+    _check_status(rc)
+    return out
+
+
+STATIC_SCRATCH_BYTES = 32 << 20   # PKV_STATIC_SCRATCH_BYTES of include/pkv.h
+
+
+def paged_attn_decode_append_static(q, k_new, v_new, k_cache, v_cache, block_tables,
+                                    context_lens, scale, out, k_scale=None, v_scale=None,
+                                    partition_size=0):
+    """paged_attn_decode_append with the partials in the library's static
+    per-GPU scratch array (STATIC_SCRATCH_BYTES) instead of a workspace: the
+    C entry point allocates nothing.  `out` is required (this wrapper does not
+    allocate either).  Calls that overlap on one GPU race."""
+    B, Hq, D, NB, Hkv, bs = _decode_common(q, k_cache, v_cache, block_tables, context_lens,
+                                           k_scale, v_scale)
+    _dev(k_new, "k_new", dtype=q.dtype, ndim=3)
+    _dev(v_new, "v_new", dtype=q.dtype, ndim=3)
+    if tuple(k_new.shape) != (B, Hkv, D) or v_new.shape != k_new.shape:
+        raise ValueError("k_new and v_new must be [num_seqs][num_kv_heads][head_dim]")
+    if out is None:
+        raise ValueError("out is required")
+    out = _out(out, q)
+    rc = _load().pkv_paged_attn_decode_append_static(
+        _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+        _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), block_tables.shape[1],
+        _ptr(context_lens), B, Hq, Hkv, D, bs, NB, float(scale), int(partition_size),
+        _code(q.dtype, "q"), _code(k_cache.dtype, "k_cache"), _stream(q))
     _check_status(rc)
     return out
 

@@ -5,6 +5,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "pkv.h"
 #include "pkv_internal.h"
 
@@ -796,6 +798,106 @@ pkv_status pkv_paged_attn_decode_shared_prefix(
     return hip_status(pkv::launch_paged_decode(d, (int)q_dtype, (int)cache_dtype, head_dim, gt,
                                                stream),
                       "own-positions decode launch");
+}
+
+}  // extern "C"
+
+// ---- decode with the fused append into a library-owned scratch array -------
+// For callers that cannot allocate device memory.  The partials of a split
+// decode live in `scratch`, a static device array of kStaticScratchBytes that
+// every GPU the library runs on holds from the load of this code until the
+// process ends.  In host code `scratch` names a host-side stand-in, not the
+// device array: its device address is looked up once per GPU with
+// hipGetSymbolAddress (that GPU current) and only that address is handed to
+// kernels.  Calls on one GPU share the array (overlapping calls race); the
+// decode writes every partial it later reads, so nothing is cleared.
+
+namespace {
+
+constexpr size_t kStaticScratchBytes = PKV_STATIC_SCRATCH_BYTES;
+constexpr int kMaxScratchDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of `scratch` on the GPU that `stream` runs on.
+pkv_status scratch_on(hipStream_t stream, void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    if (stream != nullptr) {
+        hipDevice_t sd = 0;
+        e = hipStreamGetDevice(stream, &sd);
+        if (e != hipSuccess) return hip_status(e, "hipStreamGetDevice");
+        dev = sd;
+    }
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(PKV_ERR_UNSUPPORTED, "device %d beyond the %d the static scratch serves", dev,
+                    kMaxScratchDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        int cur = -1;
+        e = hipGetDevice(&cur);
+        if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+            return hip_status(e, "hipSetDevice");
+        void* p = nullptr;
+        const hipError_t es = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev && (e = hipSetDevice(cur)) != hipSuccess)
+            return hip_status(e, "hipSetDevice");
+        if (es != hipSuccess) return hip_status(es, "hipGetSymbolAddress(scratch)");
+        if (p == nullptr || (reinterpret_cast<uintptr_t>(p) & 255u))
+            return fail(PKV_ERR_HIP, "static scratch address %p is not 256-byte aligned", p);
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_paged_attn_decode_append_static(
+    void* out, const void* q, const void* k_new, const void* v_new, void* k_cache,
+    void* v_cache, float* k_scale, float* v_scale, const int32_t* block_tables,
+    int max_blocks_per_seq, const int32_t* context_lens, int num_seqs, int num_q_heads,
+    int num_kv_heads, int head_dim, int block_size, int64_t num_blocks, float scale,
+    int partition_size, pkv_dtype q_dtype, pkv_dtype cache_dtype, hipStream_t stream) {
+    pkv_status s = check_decode(q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                                max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                                num_kv_heads, head_dim, block_size, num_blocks, q_dtype,
+                                cache_dtype);
+    if (s != PKV_OK) return s;
+    if (partition_size < 0 || partition_size % pkv::kBlockSize != 0)
+        return fail(PKV_ERR_SHAPE, "partition_size %d is not 0 or a positive multiple of 16",
+                    partition_size);
+    if (num_seqs == 0) return ok();
+    if (!k_new || !v_new) return fail(PKV_ERR_NULL, "k_new and v_new are required");
+    if (!aligned16(k_new) || !aligned16(v_new))
+        return fail(PKV_ERR_SHAPE, "k_new and v_new must be 16-byte aligned");
+    const size_t need = pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                  max_blocks_per_seq, partition_size);
+    if (need > kStaticScratchBytes)
+        return fail(PKV_ERR_WORKSPACE,
+                    "the partials of this call need %zu bytes, more than the %zu-byte static "
+                    "scratch (fewer sequences or partitions per call, or the workspace entry "
+                    "point)",
+                    need, kStaticScratchBytes);
+    void* ws = nullptr;
+    s = scratch_on(stream, &ws);
+    if (s != PKV_OK) return s;
+    return decode_both_phases(out, q, k_new, v_new, k_cache, v_cache, k_scale, v_scale,
+                              block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                              num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                              partition_size, ws, kStaticScratchBytes, q_dtype, cache_dtype, 0,
+                              stream);
 }
 
 }  // extern "C"

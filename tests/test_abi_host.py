@@ -300,3 +300,23 @@ def test_shared_prefix_argument_errors(lib):
     assert g(64, 16, 4, 32, 32, 128, 256) >= 2 * 64 * 32 * (128 + 2) * 4
     assert g(64, 16, 0, 32, 32, 128, 256) == 0
     assert g(64, 16, 4, 32, 32, 96, 256) == 0
+
+
+def test_static_scratch_entry_refuses_oversized_partials(lib):
+    """The no-allocation decode refuses, before any HIP call, a batch whose
+    partials would not fit its static scratch (256 sequences x 32 heads x
+    2048 partitions of 16 tokens: ~8.7 GB of partials)."""
+    f = lib.pkv_paged_attn_decode_append_static
+    I = ctypes.c_int
+    f.argtypes = [P] * 9 + [I, P, I, I, I, I, I, ctypes.c_int64, ctypes.c_float, I, I, I, P]
+    args = [FAKE] * 9 + [2048, FAKE, 256, 32, 32, 128, 16, 40000, 0.1, 16, F16, F16, None]
+    assert f(*args) == EWS
+    assert b"static scratch" in lib.pkv_last_error()
+    args[14] = 96                              # head_dim checked first
+    assert f(*args) == EUNSUP
+    args[14] = 128
+    args[2] = None                             # k_new required
+    args[11] = 2
+    assert f(*args) == ENULL
+    args[11] = 0                               # no sequence: nothing to do
+    assert f(*args) == OK
