@@ -529,13 +529,27 @@ constexpr int kMinWavesPerEU = (GT == 1 && D == 128 && CE == Elem::U4) ? 4
                                    ? PKV_WAVES_16BIT
                                    : 1;
 
+// Waves per work-group; each streams its share of the item's blocks.
+// Measured on MI355X (same-box A/B, steps of the fused decode): eight waves
+// against four, LLaMA-7B-shaped fp16 batch 392.5 vs 393.1 us, INT8 184.2 vs
+// 186.4, FP8 179.8 vs 180.8, GQA 32/8 bf16 364.3 vs 369.9, 16 x 32k
+// 1342.6 vs 1353.9; the 4-bit tiles measured slower with eight (123.5 vs
+// 117.7 us) and keep four, as do the tiles whose registers pass 256 per lane
+// (head_dim 256, and 8 fp32 heads): with eight waves (two per SIMD) those
+// would spill to memory instead of to accumulation registers.
+template <Elem CE, int D, int GT>
+constexpr int kDecodeWaves =
+    (CE == Elem::U4 || D > 128 || (CE == Elem::F32 && GT == 8)) ? 4 : 8;
+
 template <Elem QE, Elem CE, int D, int GT>
-__global__ __launch_bounds__(kDecodeThreads)
+__global__ __launch_bounds__((kDecodeWaves<CE, D, GT> * 64))
 __attribute__((amdgpu_waves_per_eu(kMinWavesPerEU<CE, D, GT>)))
 void paged_decode_kernel(DecodeArgs a) {
     using G = Geom<CE, D>;
     constexpr int L = G::L, E = G::E, R = G::R, U = G::U, STEPS = G::STEPS;
-    constexpr int NW = kDecodeWaves;
+    constexpr int NW = kDecodeWaves<CE, D, GT>;
+    constexpr int kDecodeThreads = NW * 64;
+    static_assert(kDecodeThreads >= kScheduleMaxSeqs, "one thread per ranked sequence");
     constexpr bool kInt8 = is_scaled(CE);  // 1-byte codes with a per-row scale
     constexpr bool kU4 = CE == Elem::U4;    // 4-bit codes with a per-row (x_min, range)
     constexpr float kInv15 = 1.0f / 15.0f;
@@ -552,7 +566,8 @@ void paged_decode_kernel(DecodeArgs a) {
     constexpr int kKeepCap = 32768 / (NW * GT * D * 4);
     constexpr int RK = kKeepCap >= 4 ? (R < 4 ? R : 4) : kKeepCap >= 2 ? (R < 2 ? R : 2) : 1;
     __shared__ float s_acc[NW][RK][GT][D];
-    __shared__ int2 s_key[kScheduleMaxSeqs];  // (partition span, item count) per sequence
+    // (rank key, item count) per sequence, read two sequences per 16-byte LDS load
+    __shared__ __align__(16) int2 s_key[kScheduleMaxSeqs];
     __shared__ int s_pick[3];
 
     const int tid = threadIdx.x;
@@ -571,39 +586,39 @@ void paged_decode_kernel(DecodeArgs a) {
     // Longest-first order: work items (partition x tile) of all sequences
     // sorted by partition length, longest first, so that the work dispatched
     // last is the shortest and the ragged tail of a batch is small.  Every
-    // work-group ranks the sequences itself (one per thread, in LDS).
-    // The ranking sits on the path from kernel start to the first K/V load:
-    // the keys are read eight at a time (one LDS round trip per eight
-    // sequences instead of one per sequence), and the picked sequence's
-    // length comes back through LDS rather than from memory again.
+    // work-group ranks the sequences itself (one per thread, in LDS), on the
+    // path from kernel start to its first K/V load, so the ranking is kept
+    // branch-free: a sequence's key packs its partition span (in blocks) above
+    // 255 - index (longer first, then lower index), and a rank is the sum of
+    // the item counts of the larger keys, two keys per LDS load.
     int b, part, tile, n;
     if (a.longest_first) {
         const int item = blockIdx.x / a.n_tiles;
         tile = blockIdx.x % a.n_tiles;
-        int my_span = -1, cnt = 0, my_n = 0;
+        int my_key = -1, cnt = 0, my_n = 0;
         if (tid < a.num_seqs) {
             my_n = clamp_len(a.context_lens[tid]);
             const int nn =
                 my_n - attend_begin(my_n, a.window, a.seq_start, tid) / kBlockSize * kBlockSize;
             const int c = partition_count(nn, P);
-            my_span = c > 0 ? partition_span(nn, c) : 0;
+            const int span_blocks = c > 0 ? partition_span(nn, c) / kBlockSize : 0;
+            static_assert(kScheduleMaxSeqs <= 256, "sequence index must fit 8 key bits");
+            my_key = span_blocks << 8 | (255 - tid);
             cnt = c > 0 ? c : 1;  // an empty sequence still takes one item: it writes zeros
         }
-        // every one of the kScheduleMaxSeqs entries is written; those past the
-        // batch hold count 0 and so add nothing to a rank
-        s_key[tid] = make_int2(my_span, cnt);
+        // every one of the kScheduleMaxSeqs entries is written; those
+        // past the batch hold count 0 and so add nothing to a rank
+        if (tid < kScheduleMaxSeqs) s_key[tid] = make_int2(my_key, cnt);
         if (tid == 0) s_pick[0] = -1;
         __syncthreads();
         if (tid < a.num_seqs) {
             int start = 0;
-            const int nj = (a.num_seqs + 7) & ~7;  // <= kScheduleMaxSeqs
-            for (int j = 0; j < nj; j += 8) {
-                int2 kj[8];
-#pragma unroll
-                for (int q = 0; q < 8; ++q) kj[q] = s_key[j + q];
-#pragma unroll
-                for (int q = 0; q < 8; ++q)
-                    if (kj[q].x > my_span || (kj[q].x == my_span && j + q < tid)) start += kj[q].y;
+            const int nj = (a.num_seqs + 1) & ~1;  // <= kScheduleMaxSeqs
+#pragma unroll 4
+            for (int j = 0; j < nj; j += 2) {
+                const int4 kk = *reinterpret_cast<const int4*>(&s_key[j]);
+                start += kk.x > my_key ? kk.y : 0;
+                start += kk.z > my_key ? kk.w : 0;
             }
             if (item >= start && item < start + cnt) {
                 s_pick[0] = tid;
@@ -1156,7 +1171,7 @@ hipError_t launch4(const DecodeArgs& a, hipStream_t stream) {
     if (n_wg <= 0) return hipSuccess;
     if (n_wg > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((paged_decode_kernel<QE, CE, D, GT>), dim3((unsigned)n_wg),
-                       dim3(kDecodeThreads), 0, stream, a);
+                       dim3(kDecodeWaves<CE, D, GT> * 64), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -167,9 +167,11 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
     const int kvh = rest % a.num_kv_heads;
     int b = rest / a.num_kv_heads;
     static_assert(kThreads >= kScheduleMaxSeqs, "one thread per ranked sequence");
-    __shared__ int s_key[kScheduleMaxSeqs];
+    __shared__ __align__(16) int s_key[kScheduleMaxSeqs];
     __shared__ int s_order[kScheduleMaxSeqs];
-    if (a.num_seqs <= kScheduleMaxSeqs) {
+    // a key packs the partition span in blocks above 255 - index (longer
+    // first, then lower index): distinct keys, and a branch-free rank
+    if (a.num_seqs <= kScheduleMaxSeqs && a.max_blocks_per_seq < (1 << 23)) {
         const int n_cap0 = a.max_blocks_per_seq * kBlockSize;
         int key = -1;
         if (threadIdx.x < a.num_seqs) {
@@ -180,23 +182,20 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
             }
             const int nn = s0 < 0 ? 0 : min(max(a.context_lens[s0], 0), n_cap0);
             const int c = partition_count(nn, a.partition_size);
-            key = c > 0 ? partition_span(nn, c) : 0;
+            key = (c > 0 ? partition_span(nn, c) / kBlockSize : 0) << 8 | (255 - threadIdx.x);
         }
         // every entry is written; those past the batch (key -1) rank nothing
         if (threadIdx.x < kScheduleMaxSeqs) s_key[threadIdx.x] = key;
         __syncthreads();
         if (threadIdx.x < a.num_seqs) {
-            const int me = threadIdx.x;
             int r = 0;
-            const int nj = (a.num_seqs + 7) & ~7;  // <= kScheduleMaxSeqs
-            for (int j = 0; j < nj; j += 8) {
-                int kj[8];
-#pragma unroll
-                for (int q = 0; q < 8; ++q) kj[q] = s_key[j + q];
-#pragma unroll
-                for (int q = 0; q < 8; ++q) r += (kj[q] > key || (kj[q] == key && j + q < me)) ? 1 : 0;
+            const int nj = (a.num_seqs + 3) & ~3;  // <= kScheduleMaxSeqs
+#pragma unroll 2
+            for (int j = 0; j < nj; j += 4) {
+                const int4 kk = *reinterpret_cast<const int4*>(&s_key[j]);
+                r += (kk.x > key) + (kk.y > key) + (kk.z > key) + (kk.w > key);
             }
-            s_order[r] = me;
+            s_order[r] = threadIdx.x;
         }
         __syncthreads();
         b = s_order[b];
@@ -514,10 +513,11 @@ void paged_multi_tiled_kernel(MultiArgs a) {
     // the launch is small.  Every work-group ranks the sequences itself
     // (one per thread, in LDS).
     static_assert(NW * 64 >= kScheduleMaxSeqs, "one thread per ranked sequence");
-    __shared__ int s_key[kScheduleMaxSeqs];
+    __shared__ __align__(16) int s_key[kScheduleMaxSeqs];
     __shared__ int s_order[kScheduleMaxSeqs];
     int b = rest / a.num_kv_heads;
-    if (a.num_seqs <= kScheduleMaxSeqs) {
+    // (keys as in the short-run kernel: span in blocks above 255 - index)
+    if (a.num_seqs <= kScheduleMaxSeqs && a.max_blocks_per_seq < (1 << 23)) {
         const int n_cap0 = a.max_blocks_per_seq * kBlockSize;
         int key = -1;
         if (tid < a.num_seqs) {
@@ -528,15 +528,16 @@ void paged_multi_tiled_kernel(MultiArgs a) {
             }
             const int nn = s0 < 0 ? 0 : min(max(a.context_lens[s0], 0), n_cap0);
             const int c = partition_count(nn, a.partition_size);
-            key = c > 0 ? partition_span(nn, c) : 0;
+            key = (c > 0 ? partition_span(nn, c) / kBlockSize : 0) << 8 | (255 - tid);
         }
         if (tid < kScheduleMaxSeqs) s_key[tid] = key;
         __syncthreads();
         if (tid < a.num_seqs) {
             int r = 0;
-            for (int j = 0; j < a.num_seqs; ++j) {
-                const int kj = s_key[j];
-                r += (kj > key || (kj == key && j < tid)) ? 1 : 0;
+            const int nj = (a.num_seqs + 3) & ~3;  // <= kScheduleMaxSeqs
+            for (int j = 0; j < nj; j += 4) {
+                const int4 kk = *reinterpret_cast<const int4*>(&s_key[j]);
+                r += (kk.x > key) + (kk.y > key) + (kk.z > key) + (kk.w > key);
             }
             s_order[r] = tid;
         }

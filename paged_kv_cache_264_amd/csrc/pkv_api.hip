@@ -156,7 +156,7 @@ pkv::DecodeArgs make_args(const void* q, const void* k_cache, const void* v_cach
     a.partition_size = P;
     a.num_partitions = NP;
     a.n_tiles = n_tiles;
-    a.longest_first = B <= pkv::kScheduleMaxSeqs ? 1 : 0;
+    a.longest_first = B <= pkv::kScheduleMaxSeqs && mbs < (1 << 23) ? 1 : 0;
     a.scale_log2 = scale * 1.44269504088896340736f;
     return a;
 }

@@ -17,8 +17,6 @@ pkv_status ok();
 const char* last_error();
 
 constexpr int kBlockSize = 16;   // tokens per KV block
-constexpr int kDecodeThreads = 256;
-constexpr int kDecodeWaves = kDecodeThreads / 64;
 
 struct DecodeArgs {
     void* out;
@@ -42,7 +40,8 @@ struct DecodeArgs {
     int partition_size;  // tokens, multiple of 16
     int num_partitions;  // NP: partial-array stride
     int n_tiles;         // num_q_heads / heads_per_tile
-    int longest_first;   // schedule work longest-first (needs num_seqs <= kScheduleMaxSeqs)
+    int longest_first;   // schedule work longest-first (needs num_seqs <= kScheduleMaxSeqs
+                         // and max_blocks_per_seq < 2^23, for the packed rank key)
     int window;          // > 0: attend to the last `window` positions only
     const int32_t* seq_start;  // [B] first position attended, or nullptr (0)
     // With seq_start and an output: the partials of the positions before the
@@ -55,8 +54,9 @@ struct DecodeArgs {
     float scale_log2;    // softmax scale * log2(e)
 };
 
-// Sequences ranked in LDS by the work-group scheduler (one per thread).
-constexpr int kScheduleMaxSeqs = kDecodeThreads;
+// Sequences ranked in LDS by the work-group schedulers (one per thread; the
+// work-groups that rank have at least this many threads).
+constexpr int kScheduleMaxSeqs = 256;
 
 // Balanced split of an n-token context into ceil(n / P) partitions: every
 // partition but the last spans `partition_span` tokens, a multiple of the
