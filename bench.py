@@ -44,11 +44,12 @@ WORKLOAD_NAMES = {
     "int8-write": "llama7b-int8kv-cache-write-64-new-tokens",
 }
 KERNEL_SOURCES = ["paged_decode.hip", "pkv_device.h", "pkv_internal.h", "pkv_api.hip"]
+MULTI_SOURCES = ["paged_multi.hip", "pkv_device.h", "pkv_internal.h", "pkv_api.hip"]
 
 
-def kernel_sha() -> str:
+def kernel_sha(sources=None) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, "paged_kv_cache_264_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -414,7 +415,7 @@ def bench_multi(args):
              "frac": round(hbm / HBM_PEAK_GBS, 4)})
     roof.update({"traffic": None, "kernel": "paged_multi_kernel" + (
         " + paged_reduce_kernel (events span both)" if pkv.num_partitions(mbs, P) > 1 else ""),
-        "kernel_sha": kernel_sha(), "flop_per_byte": round(flops / launch_bytes, 2)})
+        "kernel_sha": kernel_sha(MULTI_SOURCES), "flop_per_byte": round(flops / launch_bytes, 2)})
     result = {
         "metric": METRIC, "value": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 2),
         "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

@@ -47,6 +47,9 @@ typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_v __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_v __attribute__((ext_vector_type(4)));
 
@@ -60,6 +63,14 @@ constexpr int kWaves = PKV_MULTI_WAVES;
 constexpr int kThreads = kWaves * 64;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kNegBig = -3.0e38f;
+// The running max of a row is the reference the weights are taken against,
+// exp2(c s - c m): any reference gives the same softmax once the sum and the
+// output use the same one.  It is moved (and the sum and output rescaled)
+// only when a score exceeds it by more than kSlack in exp2 units, so a weight
+// is at most 2^kSlack (exact in fp32 and in the 16-bit P operand's range), and
+// the rescale, which touches every output accumulator of the wave, runs about
+// once per row after the first blocks instead of whenever a row's max grows.
+constexpr float kSlack = 8.0f;
 constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer access
 constexpr int kNonTemporal = 2;
 constexpr unsigned kXcds = 8;              // accelerator complex dies of the chip
@@ -81,10 +92,9 @@ template <> struct Mfma<Elem::F16> {
     static __device__ __forceinline__ f32x4_t pv32(const uint4& a, const uint4& b, f32x4_t c) {
         return qk(a, b, c);
     }
+    // two floats to a pair of fp16, nearest even (one v_cvt_pk_f16_f32)
     static __device__ __forceinline__ uint32_t pack(float x, float y) {
-        const _Float16 a = (_Float16)x, b = (_Float16)y;
-        return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{x, y}, f16x2_t));
     }
 };
 template <> struct Mfma<Elem::BF16> {
@@ -101,10 +111,9 @@ template <> struct Mfma<Elem::BF16> {
     static __device__ __forceinline__ f32x4_t pv32(const uint4& a, const uint4& b, f32x4_t c) {
         return qk(a, b, c);
     }
+    // two floats to a pair of bf16, nearest even (one v_cvt_pk_bf16_f32)
     static __device__ __forceinline__ uint32_t pack(float x, float y) {
-        const __bf16 a = (__bf16)x, b = (__bf16)y;
-        return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{x, y}, bf16x2_t));
     }
 };
 
@@ -325,9 +334,10 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
         float mx = kNegBig;
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sv[i]);
-        // shared running max, reduced across the query's 4 lanes only when
-        // some score exceeds it; l is this lane's share of the sum
-        const bool grew = __builtin_amdgcn_ballot_w64(mx > m) != 0;
+        // shared reference max, reduced across the query's 4 lanes only
+        // when some score exceeds it by more than kSlack; l is this lane's
+        // share of the sum
+        const bool grew = __builtin_amdgcn_ballot_w64(fmaf(mx, c, -cm) > kSlack) != 0;
         float alpha = 1.f;
         if (grew) {
             mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -653,15 +663,20 @@ void paged_multi_tiled_kernel(MultiArgs a) {
     // id) arrive as zeros, so no score or weight meets a stale or NaN value.
     const __attribute__((address_space(4))) int32_t* table_c =
         (const __attribute__((address_space(4))) int32_t*)table;
-    auto issue = [&](char* dst, int jb0) {
+    // The IPW loads of a wave fall in one tile, so each wave needs one block
+    // id per step; it is a scalar load (constant address space: the table is
+    // not written here, and waiting for it never waits for the K/V loads),
+    // issued a step before the loads that use it.
+    static_assert(SUBS % IPW == 0, "a wave's loads of a step lie in one tile");
+    auto load_id = [&](int jb0) {
+        return table_c[min(jb0 + (wave * IPW / SUBS) % KB, blk_stop - 1)];
+    };
+    auto issue = [&](char* dst, int jb0, int id) {
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
             const int u = wave * IPW + i;            // wave-uniform
             const int tt = u / SUBS, r = u % SUBS;   // tile (K tiles first), kilobyte
             const int jb = jb0 + tt % KB;
-            // a scalar load (constant address space: the table is not written
-            // here), so that waiting for it never waits for the K/V loads
-            const int id = table_c[min(jb, blk_stop - 1)];
             const int phys = jb < blk_stop ? id : -1;
             const bool ok = phys >= 0 && (int64_t)phys < a.num_blocks;
             // wave-uniform by construction; said so, or the descriptor is
@@ -737,10 +752,10 @@ void paged_multi_tiled_kernel(MultiArgs a) {
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sv[kb][i]);
-            // The running max m is shared by a query's 4 lanes; the exact
-            // cross-lane max is needed only when some score exceeds it, and
-            // then acc is rescaled (otherwise alpha is 1).
-            if (__builtin_amdgcn_ballot_w64(mx > m[rr]) != 0) {
+            // The reference max m is shared by a query's 4 lanes; the
+            // cross-lane max is needed only when some score exceeds it by
+            // more than kSlack, and then acc is rescaled (otherwise alpha is 1).
+            if (__builtin_amdgcn_ballot_w64(fmaf(mx, c, -cm[rr]) > kSlack) != 0) {
                 mx = fmaxf(mx, __shfl_xor(mx, 16));
                 mx = fmaxf(mx, __shfl_xor(mx, 32));
                 const float mn = fmaxf(m[rr], mx);
@@ -790,12 +805,15 @@ void paged_multi_tiled_kernel(MultiArgs a) {
     // for those newer loads.  Past the run the loads fetch zeros.
     const int n_steps = (blk_stop - blk_begin + KB - 1) / KB;
     if (n_steps > 0) {
-        issue(s_b0, blk_begin);
-        issue(s_b1, blk_begin + KB);
+        issue(s_b0, blk_begin, load_id(blk_begin));
+        issue(s_b1, blk_begin + KB, load_id(blk_begin + KB));
+        int id_next = load_id(blk_begin + 2 * KB);  // for the loads issued at step 0
         auto step = [&](const char* cur, char* nxt, int st) {
             __builtin_amdgcn_s_waitcnt(vmcnt_only(IPW));
             __builtin_amdgcn_s_barrier();
-            issue(nxt, blk_begin + (st + 2) * KB);
+            const int id = id_next;
+            id_next = load_id(blk_begin + (st + 3) * KB);
+            issue(nxt, blk_begin + (st + 2) * KB, id);
             compute(cur, blk_begin + st * KB);
         };
         for (int st = 0; st < n_steps; st += 3) {
