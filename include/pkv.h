@@ -507,6 +507,33 @@ const char* pkv_status_string(pkv_status status);
  * none).  The pointer stays valid until the thread's next pkv_* call. */
 const char* pkv_last_error(void);
 
+/*
+ * Read-only measurement helpers: the HBM read rate the decode's bytes can be
+ * fetched at on this GPU, reported beside the decode's own rate as context.
+ * Neither computes anything; a word of `sink` (device, 4 bytes) is written
+ * only in the practically impossible case that the bytes read fold to a fixed
+ * constant, which keeps the loads from being optimized away.
+ *
+ * pkv_stream_read: a plain streaming read of `bytes` bytes from `src`
+ * (device, 16-byte aligned), contiguous chunks per work-group, non-temporal
+ * 16-byte loads.
+ *
+ * pkv_tile_read: the decode's access pattern without its arithmetic: one
+ * work-group per entry of `items` (device int32 [num_items][2], (sequence,
+ * kv head), 8-byte aligned; entries outside [0, num_seqs) x [0, num_kv_heads)
+ * are skipped), which reads the K and V (block, kv head) tiles of that
+ * sequence's context_lens[b] tokens through its block table, up to the last
+ * token, in the order the items are listed.  4 KiB tiles only (16 tokens x
+ * head_dim x element size = 4096 bytes, e.g. fp16 at head_dim 128), else
+ * PKV_ERR_UNSUPPORTED.  Other arguments as for pkv_paged_attn_decode.
+ */
+pkv_status pkv_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
+pkv_status pkv_tile_read(const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                         int max_blocks_per_seq, const int32_t* context_lens, int num_seqs,
+                         const int32_t* items, int num_items, int num_kv_heads, int head_dim,
+                         int64_t num_blocks, pkv_dtype cache_dtype, uint32_t* sink,
+                         hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,7 +20,7 @@ __all__ = [
     "paged_attn_decode_sliding", "paged_attn_multi",
     "paged_attn_decode_partials", "paged_attn_reduce",
     "decode_workspace_size", "default_partition_size", "num_partitions",
-    "BlockManager", "copy_blocks",
+    "BlockManager", "copy_blocks", "stream_read", "tile_read",
     "library_path", "PkvError", "BLOCK_SIZE",
 ]
 
@@ -135,6 +135,10 @@ def _load():
     L.pkv_bm_num_free_blocks.restype = I64
     L.pkv_bm_sequence_length.argtypes = [P, I64]
     L.pkv_bm_sequence_length.restype = I64
+    L.pkv_stream_read.argtypes = [P, I64, P, P]
+    L.pkv_stream_read.restype = I
+    L.pkv_tile_read.argtypes = [P, P, P, I, P, I, P, I, I, I, I64, I, P, P]
+    L.pkv_tile_read.restype = I
     L.pkv_status_string.argtypes = [I]
     L.pkv_status_string.restype = ctypes.c_char_p
     L.pkv_last_error.argtypes = []
@@ -533,6 +537,36 @@ def copy_blocks(k_cache, v_cache, copy_pairs, k_scale=None, v_scale=None):
     rc = _load().pkv_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
                                  _ptr(copy_pairs), copy_pairs.shape[0], Hkv, D, bs, NB,
                                  _code(k_cache.dtype, "k_cache"), _stream(k_cache))
+    _check_status(rc)
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor):
+    """Measurement helper: read every byte of `src` once (plain streaming
+    read, no arithmetic).  `sink` is a 1-element int32 device tensor."""
+    _dev(src, "src")
+    _dev(sink, "sink", dtype=torch.int32)
+    rc = _load().pkv_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                                 _stream(src))
+    _check_status(rc)
+
+
+def tile_read(k_cache, v_cache, block_tables, context_lens, items, sink):
+    """Measurement helper: the decode's K/V tile reads without arithmetic, one
+    work-group per (sequence, kv head) row of `items` (int32 [n][2] on the
+    GPU), in that order.  4 KiB tiles only."""
+    _dev(k_cache, "k_cache", ndim=4)
+    _dev(v_cache, "v_cache", dtype=k_cache.dtype, ndim=4)
+    _dev(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _dev(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    _dev(items, "items", dtype=torch.int32, ndim=2)
+    _dev(sink, "sink", dtype=torch.int32)
+    if items.shape[1] != 2 or block_tables.shape[0] != context_lens.shape[0]:
+        raise ValueError("items must be [n][2] and the tables one row per sequence")
+    NB, Hkv, bs, _ = k_cache.shape
+    rc = _load().pkv_tile_read(_ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                               block_tables.shape[1], _ptr(context_lens), context_lens.shape[0],
+                               _ptr(items), items.shape[0], Hkv, _head_dim(k_cache), NB,
+                               _code(k_cache.dtype, "k_cache"), _ptr(sink), _stream(k_cache))
     _check_status(rc)
 
 

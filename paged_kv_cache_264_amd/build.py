@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libpkv.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 SOURCES = ["pkv_api.hip", "paged_decode.hip", "paged_reduce.hip", "kv_cache_write.hip",
-           "copy_blocks.hip", "block_manager.cpp", "paged_multi.hip"]
+           "copy_blocks.hip", "block_manager.cpp", "paged_multi.hip", "read_ceiling.hip"]
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

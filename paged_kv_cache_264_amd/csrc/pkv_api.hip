@@ -901,3 +901,53 @@ pkv_status pkv_paged_attn_decode_append_static(
 }
 
 }  // extern "C"
+
+// ---- read-only measurement helpers ------------------------------------------
+
+extern "C" {
+
+pkv_status pkv_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream) {
+    if (bytes < 0) return fail(PKV_ERR_SHAPE, "bytes %lld < 0", (long long)bytes);
+    if (bytes == 0) return ok();
+    if (!src || !sink) return fail(PKV_ERR_NULL, "src and sink are required");
+    if (!aligned16(src)) return fail(PKV_ERR_SHAPE, "src must be 16-byte aligned");
+    return hip_status(pkv::launch_stream_read(src, bytes, sink, stream), "stream_read launch");
+}
+
+pkv_status pkv_tile_read(const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                         int max_blocks_per_seq, const int32_t* context_lens, int num_seqs,
+                         const int32_t* items, int num_items, int num_kv_heads, int head_dim,
+                         int64_t num_blocks, pkv_dtype cache_dtype, uint32_t* sink,
+                         hipStream_t stream) {
+    if (num_items < 0 || num_seqs < 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
+        num_blocks <= 0)
+        return fail(PKV_ERR_SHAPE, "need num_items, num_seqs >= 0 and positive num_kv_heads, "
+                                   "max_blocks_per_seq, num_blocks");
+    if (!is_float(cache_dtype) && !is_quantized(cache_dtype))
+        return fail(PKV_ERR_DTYPE, "unsupported cache_dtype %d", (int)cache_dtype);
+    if (!head_dim_ok(head_dim) || pkv::kBlockSize * row_bytes(cache_dtype, head_dim) != 4096)
+        return fail(PKV_ERR_UNSUPPORTED, "tile_read reads 4 KiB (block, kv head) tiles only");
+    if (num_items == 0) return ok();
+    if (!k_cache || !v_cache || !block_tables || !context_lens || !items || !sink)
+        return fail(PKV_ERR_NULL, "every pointer is required");
+    if (!aligned16(k_cache) || !aligned16(v_cache) ||
+        (reinterpret_cast<uintptr_t>(items) & 7u))
+        return fail(PKV_ERR_SHAPE, "caches must be 16-byte and items 8-byte aligned");
+    pkv::TileReadArgs a{};
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.items = reinterpret_cast<const int2*>(items);
+    a.num_items = num_items;
+    a.num_seqs = num_seqs;
+    a.num_kv_heads = num_kv_heads;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.tile_bytes = 4096;
+    a.num_blocks = num_blocks;
+    a.sink = sink;
+    return hip_status(pkv::launch_tile_read(a, stream), "tile_read launch");
+}
+
+}  // extern "C"
+

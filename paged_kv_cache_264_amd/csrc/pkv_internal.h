@@ -188,5 +188,23 @@ struct CopyBlocksArgs {
 // Returns hipErrorInvalidValue if the grid would not fit.
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
 
+// Read-only measurement kernels (read_ceiling.hip).
+struct TileReadArgs {
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    const int2* items;     // (sequence, kv head) per work-group
+    int num_items;
+    int num_seqs;
+    int num_kv_heads;
+    int max_blocks_per_seq;
+    int tile_bytes;        // bytes of one (block, kv head) tile: 4096
+    int64_t num_blocks;
+    unsigned* sink;
+};
+hipError_t launch_stream_read(const void* src, int64_t bytes, unsigned* sink, hipStream_t stream);
+hipError_t launch_tile_read(const TileReadArgs& a, hipStream_t stream);
+
 
 }  // namespace pkv

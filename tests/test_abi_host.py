@@ -320,3 +320,30 @@ def test_static_scratch_entry_refuses_oversized_partials(lib):
     assert f(*args) == ENULL
     args[11] = 0                               # no sequence: nothing to do
     assert f(*args) == OK
+
+
+def test_read_helpers_argument_errors(lib):
+    """The measurement helpers refuse what the host can see to be wrong,
+    before any launch."""
+    I, I64 = ctypes.c_int, ctypes.c_int64
+    f = lib.pkv_stream_read
+    f.argtypes = [P, I64, P, P]
+    assert f(FAKE, -1, FAKE, None) == ESHAPE
+    assert f(None, 64, FAKE, None) == ENULL
+    assert f(ctypes.c_void_p(0x1004), 64, FAKE, None) == ESHAPE
+    assert f(None, 0, None, None) == OK
+    g = lib.pkv_tile_read
+    g.argtypes = [P, P, P, I, P, I, P, I, I, I, I64, I, P, P]
+    base = [FAKE, FAKE, FAKE, 8, FAKE, 2, FAKE, 4, 2, 128, 10, F16, FAKE, None]
+
+    def call(i, val):
+        a = list(base)
+        a[i] = val
+        return g(*a)
+
+    assert call(9, 64) == EUNSUP            # 2 KiB tiles
+    assert call(11, I8) == EUNSUP           # 1-byte codes at head_dim 128: 2 KiB tiles
+    assert call(8, 0) == ESHAPE             # num_kv_heads
+    assert call(6, None) == ENULL           # items
+    assert call(6, ctypes.c_void_p(0x1004)) == ESHAPE
+    assert call(7, 0) == OK                 # no item: no launch

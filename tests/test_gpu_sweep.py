@@ -179,3 +179,18 @@ def test_binding_refuses_misshaped_outputs(pkv):
     ref = OracleView(b, np.arange(b.B)).decode()
     assert max_abs_err(good, ref) <= 2e-3
     assert host(b.q).shape == tuple(b.q.shape)
+
+
+@pytest.mark.gpu
+def test_read_helpers_run(pkv):
+    """The read-only measurement helpers run over a NaN-poisoned batch and a
+    list of items that includes out-of-range entries (skipped) without
+    error."""
+    b = W.make_batch(cfg=dict(B=3, ctx=[40, 0, 300], Hq=4, Hkv=4, D=128, dtype="f16", cache="f16",
+                              pool=None, seed=9, max_ctx=300), device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    items = torch.tensor([[s, h] for s in range(3) for h in range(4)] + [[3, 0], [0, 4], [-1, 0]],
+                         dtype=torch.int32, device="cuda")
+    pkv.tile_read(b.k_cache, b.v_cache, b.block_tables, b.context_lens, items, sink)
+    pkv.stream_read(b.k_cache.view(-1)[:1000], sink)
+    torch.cuda.synchronize()
