@@ -456,11 +456,11 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
 
 // Long runs of queries (prefill chunks): a work-group owns NW waves x RW
 // row tiles of 16 rows and walks every block of its partition up to the last
-// position any of its rows attends to, two 16-token blocks per step.  Each
-// K/V block is fetched once per work-group, straight from the pool into one
-// of three LDS stages, and every wave reads the K and V operands once per
-// step and uses them for its RW row tiles; one barrier and one softmax
-// update per step.  The output is accumulated transposed,
+// position any of its rows attends to.  The K/V blocks are fetched once per
+// work-group, four at a time (one load step), straight from the pool into
+// one of two LDS stages; the step is computed as two halves of two blocks,
+// each one softmax update, and every wave reads the K and V operands once
+// and uses them for its RW row tiles.  One barrier per load step.  The output is accumulated transposed,
 // O^T = V^T P^T: the P operand is then the score tile as it leaves the first
 // MFMA and each lane's accumulator column is its own query, so rescaling and
 // normalizing need no lane exchange.  The V^T operand comes from the
@@ -472,24 +472,24 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
 // one read per block and 16 channels.  Each wave owns its rows for the whole
 // partition, so there is no merge between waves.
 template <Elem T, int D, int RW, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RW == 1 && D <= 128 ? 4 : 2)))
 void paged_multi_tiled_kernel(MultiArgs a) {
     constexpr int KK = D / 32;
     constexpr int NN = D / 16;
-    constexpr int KB = D <= 128 ? 2 : 1;            // 16-token blocks per softmax step
+    constexpr int KB = D <= 128 ? 2 : 1;            // 16-token blocks per softmax update
+    constexpr int KL = 2 * KB;                      // 16-token blocks per load step
     constexpr int ROW = D * 2;
     constexpr int TILE = kRows * ROW;
     constexpr int SUBS = TILE / 1024;               // 1 KiB wave loads per tile
-    constexpr int IPW = 2 * KB * SUBS / NW;         // wave loads per step and wave
-    static_assert((2 * KB * SUBS) % NW == 0, "the loads of a step split evenly over the waves");
-    constexpr int STAGE = 2 * KB * TILE;            // the K tiles, then the V tiles, of one step
+    constexpr int IPW = 2 * KL * SUBS / NW;         // wave loads per step and wave
+    static_assert((2 * KL * SUBS) % NW == 0, "the loads of a step split evenly over the waves");
+    constexpr int STAGE = 2 * KL * TILE;            // the K tiles, then the V tiles, of one step
     constexpr int WG_ROWS = NW * kRows * RW;
 
-    // three stages: the step being computed, the next one (loads landed or
-    // landing), the one after (loads issued at the top of this step)
+    // two stages: the step being computed, and the next one (its loads are
+    // issued at the top of this step and waited for at the top of the next)
     __shared__ __attribute__((aligned(16))) char s_b0[STAGE];
     __shared__ __attribute__((aligned(16))) char s_b1[STAGE];
-    __shared__ __attribute__((aligned(16))) char s_b2[STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -630,16 +630,23 @@ void paged_multi_tiled_kernel(MultiArgs a) {
     }
 
     // LDS tiles are token rows of ROW bytes without padding.  The 16-byte
-    // chunk c of token t's row sits in chunk slot c ^ swz(t) of that row,
-    // chosen so that every group of lanes the LDS serves together (8 lanes
-    // of a 16-byte read or 16 of an 8-byte read per 128-byte bank line, as
-    // well as twice that per 256 bytes) hits distinct banks: the K operand
-    // reads (tokens 0..15, one chunk) and the transpose reads (4 tokens x 2
-    // chunks per 16 lanes).
-    auto swz = [](int t) {
+    // chunk c of token t's row sits in chunk slot c ^ swz(t) of that row
+    // (swz_k in K tiles, swz_v in V tiles), chosen so that the lanes the LDS
+    // serves in one cycle hit distinct banks (64 banks of 4 bytes).  Measured
+    // on gfx950 with read-only kernels: a 16-byte read serves lanes 0-7
+    // together with 24-31 (and 8-15 with 16-23, likewise in the upper half),
+    // which for the K operand read (lane: token col, chunk 4 kk + grp) asks
+    // for distinct swz_k(t) over 16 rows and no collision between swz_k(t)
+    // and swz_k(t + 8) ^ 1; the transpose read serves lanes 0-31 together (8
+    // tokens x one 32-byte piece each), which asks for distinct swz_v(t) / 2
+    // over each 8 tokens.  The two conditions exclude each other, hence two
+    // layouts: with one swizzle for both the K reads ran at 0.63 of the
+    // conflict-free rate.
+    auto swz_v = [](int t) {
         return ROW == 128 ? ((2 * t) ^ (3 * (t >> 2))) & 7
                           : 2 * (t & 7) + (((t & 7) >> 2) ^ (t >> 3));
     };
+    auto swz_k = [](int t) { return ROW == 128 ? ((2 * t) ^ (3 * (t >> 2))) & 7 : t & 15; };
     // this lane's LDS offsets inside a tile: the K operand (token col,
     // channels 32 kk + 8 grp .. + 7) and the address it gives the V^T
     // transpose read (token 4 grp + (lane / 4) % 4, channels 16 nn + 4 (lane
@@ -647,16 +654,16 @@ void paged_multi_tiled_kernel(MultiArgs a) {
     // element e element c of what lane 16 G + a + 4 e addresses)
     int k_off[KK], v_off[NN];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) k_off[kk] = col * ROW + 16 * ((kk * 4 + grp) ^ swz(col));
+    for (int kk = 0; kk < KK; ++kk) k_off[kk] = col * ROW + 16 * ((kk * 4 + grp) ^ swz_k(col));
     {
         const int tv = 4 * grp + ((lane >> 2) & 3), qa = lane & 3;
 #pragma unroll
         for (int nn = 0; nn < NN; ++nn)
-            v_off[nn] = tv * ROW + 16 * ((2 * nn + (qa >> 1)) ^ swz(tv)) + 8 * (qa & 1);
+            v_off[nn] = tv * ROW + 16 * ((2 * nn + (qa >> 1)) ^ swz_v(tv)) + 8 * (qa & 1);
     }
 
-    // Loads of the KB blocks from jb0 on, straight from the pool into the LDS
-    // stage dst: 2 KB tiles of 1 KiB wave loads, IPW per wave.  Lane l of a
+    // Loads of the KL blocks from jb0 on, straight from the pool into the LDS
+    // stage dst: 2 KL tiles of 1 KiB wave loads, IPW per wave.  Lane l of a
     // wave load fills bytes 16 l .. 16 l + 15 of its kilobyte, so it fetches
     // the chunk that the swizzle puts there.  The buffer window ends at the
     // partition end: rows past it (and a block past the run, or a bad block
@@ -669,29 +676,39 @@ void paged_multi_tiled_kernel(MultiArgs a) {
     // issued a step before the loads that use it.
     static_assert(SUBS % IPW == 0, "a wave's loads of a step lie in one tile");
     auto load_id = [&](int jb0) {
-        return table_c[min(jb0 + (wave * IPW / SUBS) % KB, blk_stop - 1)];
+        return table_c[min(jb0 + (wave * IPW / SUBS) % KL, blk_stop - 1)];
     };
+    // Block ids at or past nb_lim are refused (the pool's block count, capped
+    // to the int range); the K and V bases of this kv head's tiles and the
+    // stride from one block to the next.  The descriptor arithmetic is all
+    // scalar and branch-free.
+    const unsigned nb_lim = (unsigned)(a.num_blocks < 0x7fffffff ? a.num_blocks : 0x7fffffff);
+    const char* const k_base = static_cast<const char*>(a.k_cache) + (size_t)kvh * TILE;
+    const char* const v_base = static_cast<const char*>(a.v_cache) + (size_t)kvh * TILE;
+    const size_t blk_stride = (size_t)a.num_kv_heads * TILE;
     auto issue = [&](char* dst, int jb0, int id) {
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
             const int u = wave * IPW + i;            // wave-uniform
             const int tt = u / SUBS, r = u % SUBS;   // tile (K tiles first), kilobyte
-            const int jb = jb0 + tt % KB;
-            const int phys = jb < blk_stop ? id : -1;
-            const bool ok = phys >= 0 && (int64_t)phys < a.num_blocks;
+            const int jb = jb0 + tt % KL;
+            const bool ok = (jb < blk_stop) & ((unsigned)id < nb_lim);
+            int rows = t_end - jb * kBlockSize;
+            rows = rows < 0 ? 0 : rows;
+            rows = rows > kRows ? kRows : rows;
             // wave-uniform by construction; said so, or the descriptor is
             // built in vector registers and the load wrapped in a loop
-            const int rows =
-                __builtin_amdgcn_readfirstlane(ok ? min(max(t_end - jb * kBlockSize, 0), kRows) : 0);
-            const size_t tile = (size_t)(ok ? phys : 0) * a.num_kv_heads + kvh;
-            const char* pool = static_cast<const char*>(tt < KB ? a.k_cache : a.v_cache);
-            const __amdgpu_buffer_rsrc_t rs = rsrc(pool + tile * TILE, rows * ROW);
+            rows = __builtin_amdgcn_readfirstlane(ok ? rows : 0);
+            const char* base = (tt < KL ? k_base : v_base) + (size_t)(ok ? (unsigned)id : 0u) * blk_stride;
+            const __amdgpu_buffer_rsrc_t rs = rsrc(base, rows * ROW);
             const int at = r * 1024 + lane * 16;
             const int t = at / ROW, slot = (at % ROW) / 16;
-            load_to_lds16(rs, dst + tt * TILE + r * 1024, t * ROW + 16 * (slot ^ swz(t)));
+            load_to_lds16(rs, dst + tt * TILE + r * 1024,
+                          t * ROW + 16 * (slot ^ (tt < KL ? swz_k(t) : swz_v(t))));
         }
     };
-    auto compute = [&](const char* buf, int jb0) {
+    // KB blocks from jb0 on: K tiles at kbuf, V tiles at vbuf
+    auto compute = [&](const char* kbuf, const char* vbuf, int jb0) {
         // 1. scores of every row tile: S^T[token 4 grp + i][query col]
         f32x4_t s[RW][KB];
         {
@@ -700,7 +717,7 @@ void paged_multi_tiled_kernel(MultiArgs a) {
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk)
-                    ka[kb][kk] = *reinterpret_cast<const uint4*>(buf + kb * TILE + k_off[kk]);
+                    ka[kb][kk] = *reinterpret_cast<const uint4*>(kbuf + kb * TILE + k_off[kk]);
 #pragma unroll
             for (int rr = 0; rr < RW; ++rr)
 #pragma unroll
@@ -720,7 +737,7 @@ void paged_multi_tiled_kernel(MultiArgs a) {
             for (int kb = 0; kb < KB; ++kb) {
                 typedef __attribute__((address_space(3))) s16x4_v lds_s16x4;
                 const s16x4_v t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4*)(buf + (KB + kb) * TILE + v_off[nn]));
+                    (lds_s16x4*)(vbuf + kb * TILE + v_off[nn]));
                 vw[nn][kb] = __builtin_bit_cast(uint2, t);
             }
         // 2. per row tile: online softmax over the step's KB * 16 tokens, then
@@ -797,29 +814,31 @@ void paged_multi_tiled_kernel(MultiArgs a) {
         }
     };
 
-    // Steps of KB blocks over three LDS stages, loads two steps ahead.  At
-    // the top of a step a wave waits for its own loads of the step (the next
-    // step's IPW may still run); after the barrier every wave's have landed
-    // and no wave still reads the stage of the step before, which then takes
-    // the loads of two steps on.  A plain s_barrier: a fence would also wait
-    // for those newer loads.  Past the run the loads fetch zeros.
-    const int n_steps = (blk_stop - blk_begin + KB - 1) / KB;
+    // Load steps of KL blocks over two LDS stages.  At the top of a step a
+    // wave waits for all its loads (those of this step); after the barrier
+    // every wave's have landed and no wave still reads the other stage, which
+    // then takes the loads of the next step, issued before this step's
+    // compute.  (With deeper prefetch the compiler, which cannot tell the LDS
+    // stages apart, waits for every load issued earlier before the first LDS
+    // read anyway.)  A plain s_barrier: a fence would also wait for the newer
+    // loads.  Past the run the loads fetch zeros.
+    const int n_steps = (blk_stop - blk_begin + KL - 1) / KL;
     if (n_steps > 0) {
         issue(s_b0, blk_begin, load_id(blk_begin));
-        issue(s_b1, blk_begin + KB, load_id(blk_begin + KB));
-        int id_next = load_id(blk_begin + 2 * KB);  // for the loads issued at step 0
+        int id_next = load_id(blk_begin + KL);  // for the loads issued at step 0
         auto step = [&](const char* cur, char* nxt, int st) {
-            __builtin_amdgcn_s_waitcnt(vmcnt_only(IPW));
+            __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
             __builtin_amdgcn_s_barrier();
             const int id = id_next;
-            id_next = load_id(blk_begin + (st + 3) * KB);
-            issue(nxt, blk_begin + (st + 2) * KB, id);
-            compute(cur, blk_begin + st * KB);
+            id_next = load_id(blk_begin + (st + 2) * KL);
+            issue(nxt, blk_begin + (st + 1) * KL, id);
+#pragma unroll
+            for (int h = 0; h < KL / KB; ++h)
+                compute(cur + h * KB * TILE, cur + (KL + h * KB) * TILE, blk_begin + st * KL + h * KB);
         };
-        for (int st = 0; st < n_steps; st += 3) {
-            step(s_b0, s_b2, st);
+        for (int st = 0; st < n_steps; st += 2) {
+            step(s_b0, s_b1, st);
             if (st + 1 < n_steps) step(s_b1, s_b0, st + 1);
-            if (st + 2 < n_steps) step(s_b2, s_b1, st + 2);
         }
         // no load may still write this work-group's LDS when its waves end
         __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
