@@ -398,6 +398,51 @@ def practical_ceiling(batch, stream, dec_bytes, reps=10):
                     "arithmetic, HIP events over 10 launches after 3"}
 
 
+def matrix_core_ceiling(stream, kernel_tflops, reps=5):
+    """Context for the chunked-prefill kernel's rate, measured on this GPU in
+    this run: the rate the matrix cores sustain on back-to-back independent
+    16x16x32 fp16 MFMAs (4 waves per SIMD on every CU, no memory traffic),
+    and the LDS read rate of the kernel's two operand reads on each of its
+    tile layouts (the K layout serves the 16-byte K reads, the V layout the
+    V^T transpose reads; either read on the other layout meets bank
+    conflicts)."""
+    import torch
+
+    import paged_kv_cache_264_amd as pkv
+
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+
+    def run(fn):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    groups, rounds = 4 * cus, 2000
+    t = run(lambda: pkv.mfma_rate(groups, rounds, sink))
+    mfma_tflops = groups * 4 * rounds * 8 * 16384 / t / 1e12
+    lds = {}
+    names = ["k_read_k_layout", "k_read_v_layout", "vt_read_v_layout", "vt_read_k_layout"]
+    for pattern, name in enumerate(names):
+        lgroups, lrounds = 2 * cus, 4000
+        t = run(lambda: pkv.lds_read_rate(pattern, lgroups, lrounds, sink))
+        lds[name] = round(lgroups * 8 * lrounds * 8192 / t / 1e9 / cus, 1)
+    return {"mfma_f16_tflops": round(mfma_tflops, 1),
+            "kernel_frac_of_mfma_rate": round(kernel_tflops / mfma_tflops, 4),
+            "lds_read_gbs_per_cu": lds,
+            "note": "pkv_mfma_rate (8 independent 16x16x32 fp16 MFMAs per wave and round, 4 waves "
+                    "per SIMD, no memory traffic) and pkv_lds_read_rate (the kernel's operand "
+                    "reads, 8 KiB per wave and round, 4 waves per SIMD); HIP events over 5 "
+                    "launches after 2"}
+
+
 def bench_multi(args):
     """Several query tokens per sequence (speculative verification, chunked
     prefill).  A step: the cache write of the B * q_len new tokens' K/V, then
@@ -494,6 +539,8 @@ def bench_multi(args):
         "launch_alg_bytes": launch_bytes, "launch_flops": flops,
         "roofline": roof,
     }
+    if mfma_bound:
+        result["practical_ceiling"] = matrix_core_ceiling(stream, tflops)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = run_multi_cpu_baseline(batch, q, qsl_np, ql, args.cpu_seconds,
                                                         flops, launch_bytes)

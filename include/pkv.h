@@ -534,6 +534,28 @@ pkv_status pkv_tile_read(const void* k_cache, const void* v_cache, const int32_t
                          int64_t num_blocks, pkv_dtype cache_dtype, uint32_t* sink,
                          hipStream_t stream);
 
+/*
+ * Rate measurement helpers for the matrix-core kernels, reported beside the
+ * chunked-prefill kernel's rate as context.  `sink` as above; `groups`
+ * work-groups (1 .. 2^20), `rounds` > 0, else PKV_ERR_SHAPE.
+ *
+ * pkv_mfma_rate: work-groups of 256 threads; every wave issues `rounds`
+ * rounds of 8 independent v_mfma_f32_16x16x32_f16 (16,384 flops each) into
+ * its own accumulators, with no memory traffic: flops = groups x 4 x rounds
+ * x 8 x 16384.  The rate the matrix cores sustain at the clock the chip holds
+ * under that load.
+ *
+ * pkv_lds_read_rate: work-groups of 512 threads over 32 KiB of LDS; every
+ * wave reads 8 KiB per round with one of the chunked-prefill kernel's operand
+ * reads: pattern 0 the 16-byte K operand read on the K tile layout, 1 the same
+ * read on the V tile layout, 2 the V^T transpose read (ds_read_b64_tr_b16) on
+ * the V layout, 3 the transpose read on the K layout; bytes = groups x 8 x
+ * rounds x 8192.  Other patterns: PKV_ERR_SHAPE.
+ */
+pkv_status pkv_mfma_rate(int groups, int rounds, uint32_t* sink, hipStream_t stream);
+pkv_status pkv_lds_read_rate(int pattern, int groups, int rounds, uint32_t* sink,
+                             hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,7 +20,7 @@ __all__ = [
     "paged_attn_decode_sliding", "paged_attn_multi",
     "paged_attn_decode_partials", "paged_attn_reduce",
     "decode_workspace_size", "default_partition_size", "num_partitions",
-    "BlockManager", "copy_blocks", "stream_read", "tile_read",
+    "BlockManager", "copy_blocks", "stream_read", "tile_read", "mfma_rate", "lds_read_rate",
     "library_path", "PkvError", "BLOCK_SIZE",
 ]
 
@@ -139,6 +139,10 @@ def _load():
     L.pkv_stream_read.restype = I
     L.pkv_tile_read.argtypes = [P, P, P, I, P, I, P, I, I, I, I64, I, P, P]
     L.pkv_tile_read.restype = I
+    L.pkv_mfma_rate.argtypes = [I, I, P, P]
+    L.pkv_mfma_rate.restype = I
+    L.pkv_lds_read_rate.argtypes = [I, I, I, P, P]
+    L.pkv_lds_read_rate.restype = I
     L.pkv_status_string.argtypes = [I]
     L.pkv_status_string.restype = ctypes.c_char_p
     L.pkv_last_error.argtypes = []
@@ -568,6 +572,24 @@ def tile_read(k_cache, v_cache, block_tables, context_lens, items, sink):
                                _ptr(items), items.shape[0], Hkv, _head_dim(k_cache), NB,
                                _code(k_cache.dtype, "k_cache"), _ptr(sink), _stream(k_cache))
     _check_status(rc)
+
+
+def mfma_rate(groups: int, rounds: int, sink: torch.Tensor):
+    """Measurement helper: `groups` work-groups of 4 waves, each wave `rounds`
+    rounds of 8 independent 16x16x32 fp16 MFMAs (16,384 flops each), no
+    memory traffic.  `sink` is a 1-element int32 device tensor."""
+    _dev(sink, "sink", dtype=torch.int32)
+    _check_status(_load().pkv_mfma_rate(int(groups), int(rounds), _ptr(sink), _stream(sink)))
+
+
+def lds_read_rate(pattern: int, groups: int, rounds: int, sink: torch.Tensor):
+    """Measurement helper: the prefill kernel's LDS operand reads, 8 KiB per
+    wave and round over `groups` work-groups of 8 waves (pattern 0: K reads on
+    the K layout, 1: K reads on the V layout, 2: V^T transpose reads on the V
+    layout, 3: transpose reads on the K layout)."""
+    _dev(sink, "sink", dtype=torch.int32)
+    _check_status(_load().pkv_lds_read_rate(int(pattern), int(groups), int(rounds), _ptr(sink),
+                                            _stream(sink)))
 
 
 def _host(x, name, dtype):

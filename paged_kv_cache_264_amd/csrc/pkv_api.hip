@@ -949,5 +949,21 @@ pkv_status pkv_tile_read(const void* k_cache, const void* v_cache, const int32_t
     return hip_status(pkv::launch_tile_read(a, stream), "tile_read launch");
 }
 
+pkv_status pkv_mfma_rate(int groups, int rounds, uint32_t* sink, hipStream_t stream) {
+    if (groups <= 0 || rounds <= 0 || groups > (1 << 20))
+        return fail(PKV_ERR_SHAPE, "need 0 < groups <= 2^20 and rounds > 0");
+    if (!sink) return fail(PKV_ERR_NULL, "sink is required");
+    return hip_status(pkv::launch_mfma_rate(groups, rounds, sink, stream), "mfma_rate launch");
+}
+
+pkv_status pkv_lds_read_rate(int pattern, int groups, int rounds, uint32_t* sink,
+                             hipStream_t stream) {
+    if (pattern < 0 || pattern > 3) return fail(PKV_ERR_SHAPE, "pattern %d is not 0..3", pattern);
+    if (groups <= 0 || rounds <= 0 || groups > (1 << 20))
+        return fail(PKV_ERR_SHAPE, "need 0 < groups <= 2^20 and rounds > 0");
+    if (!sink) return fail(PKV_ERR_NULL, "sink is required");
+    return hip_status(pkv::launch_lds_rate(pattern, groups, rounds, sink, stream), "lds_read_rate launch");
+}
+
 }  // extern "C"
 

@@ -205,6 +205,8 @@ struct TileReadArgs {
 };
 hipError_t launch_stream_read(const void* src, int64_t bytes, unsigned* sink, hipStream_t stream);
 hipError_t launch_tile_read(const TileReadArgs& a, hipStream_t stream);
+hipError_t launch_mfma_rate(int groups, int rounds, unsigned* sink, hipStream_t stream);
+hipError_t launch_lds_rate(int pattern, int groups, int rounds, unsigned* sink, hipStream_t stream);
 
 
 }  // namespace pkv

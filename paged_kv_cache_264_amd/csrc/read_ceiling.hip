@@ -1,6 +1,6 @@
-// Read-only kernels that measure the HBM rate the decode's bytes can be
-// fetched at on this GPU, as context for its bandwidth fraction: no
-// arithmetic, no output beyond a word that keeps the loads alive.
+// Kernels that measure the rates this GPU reaches on the resources the
+// attention kernels are bound by, as context for their roofline fractions:
+// no attention arithmetic, no output beyond a word that keeps the work alive.
 //   * stream_read_kernel: a plain streaming read of one contiguous buffer,
 //     each work-group a contiguous chunk, four 16-byte non-temporal loads
 //     per lane in flight.
@@ -10,6 +10,11 @@
 //     through its block table with two blocks in flight, each block one
 //     (block, kv head) tile of K and one of V, read up to the context's last
 //     token (buffer windows, as in the decode).
+//   * mfma_rate_kernel: back-to-back independent 16x16x32 fp16 MFMAs, eight
+//     accumulators per wave, no memory traffic: the sustained matrix-core
+//     rate (clock included) under a load like the prefill kernel's.
+//   * lds_rate_kernel: the prefill kernel's LDS operand reads (the 16-byte K
+//     reads and the V^T transpose reads) on either of its two tile layouts.
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -89,7 +94,105 @@ __global__ __launch_bounds__(kThreads) void tile_read_kernel(TileReadArgs a) {
     if (f == kMagic) a.sink[0] = f;
 }
 
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// The MFMAs are written as instructions, so that the eight accumulators stay
+// in place from round to round (the compiler moves builtin accumulators
+// between register files here, three moves per MFMA).  No memory access; the
+// drain before the accumulators are read covers the MFMA result latency.
+__global__ __launch_bounds__(256) void mfma_rate_kernel(int rounds, unsigned* sink) {
+    const int lane = threadIdx.x & 63;
+    f16x8_t a, b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        a[i] = (_Float16)(lane * 0.01f + i);
+        b[i] = (_Float16)(i * 0.02f - lane * 0.001f);
+    }
+    f32x4_t c0 = {0.f, 0.5f, 0.25f, 0.125f}, c1 = c0 + 1.f, c2 = c0 + 2.f, c3 = c0 + 3.f,
+            c4 = c0 + 4.f, c5 = c0 + 5.f, c6 = c0 + 6.f, c7 = c0 + 7.f;
+#pragma unroll 1
+    for (int r = 0; r < rounds; ++r) {
+        asm volatile(
+            "v_mfma_f32_16x16x32_f16 %0, %8, %9, %0\n"
+            "v_mfma_f32_16x16x32_f16 %1, %8, %9, %1\n"
+            "v_mfma_f32_16x16x32_f16 %2, %8, %9, %2\n"
+            "v_mfma_f32_16x16x32_f16 %3, %8, %9, %3\n"
+            "v_mfma_f32_16x16x32_f16 %4, %8, %9, %4\n"
+            "v_mfma_f32_16x16x32_f16 %5, %8, %9, %5\n"
+            "v_mfma_f32_16x16x32_f16 %6, %8, %9, %6\n"
+            "v_mfma_f32_16x16x32_f16 %7, %8, %9, %7"
+            : "+v"(c0), "+v"(c1), "+v"(c2), "+v"(c3), "+v"(c4), "+v"(c5), "+v"(c6), "+v"(c7)
+            : "v"(a), "v"(b));
+    }
+    asm volatile("s_nop 7\n s_nop 7\n s_nop 7" ::: "memory");
+    const f32x4_t s = c0 + c1 + c2 + c3 + c4 + c5 + c6 + c7;
+    const unsigned f = __float_as_uint(s[0] + s[1] + s[2] + s[3]);
+    if (f == kMagic) sink[0] = f;
+}
+
+// 512 threads over 32 KiB of LDS: eight 4 KiB tiles of 16 rows x 256 bytes
+// (the prefill kernel's fp16 tile at head_dim 128).  Each wave reads 8 KiB
+// per round, at its own tile offset.  Patterns: 0 the K operand read on the K
+// layout (16-byte chunk c of row t at slot c ^ t), 1 the same read on the V
+// layout (slot c ^ (2 (t & 7) + (((t & 7) >> 2) ^ (t >> 3)))), 2 the V^T
+// transpose read on the V layout, 3 the transpose read on the K layout.
+template <bool TR>
+__global__ __launch_bounds__(512) void lds_rate_kernel(int rounds, int k_layout, unsigned* sink) {
+    __shared__ __attribute__((aligned(16))) char lds[32768];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int i = tid; i < 32768 / 4; i += 512) reinterpret_cast<unsigned*>(lds)[i] = i * 2654435761u;
+    __syncthreads();
+    auto swz = [&](int t) {
+        return k_layout ? (t & 15) : 2 * (t & 7) + (((t & 7) >> 2) ^ (t >> 3));
+    };
+    int off[8];
+    if (!TR) {  // lane: token col, chunks 4 kk + grp; two tiles, kk = 0..3
+        const int col = lane & 15, grp = lane >> 4;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) off[j] = (j >> 2) * 4096 + col * 256 + 16 * (((j & 3) * 4 + grp) ^ swz(col));
+    } else {    // lane: token 4 grp + (lane / 4) % 4, 8 bytes of chunks 2 nn, 2 nn + 1
+        const int g = lane >> 4, t = 4 * g + ((lane >> 2) & 3), qa = lane & 3;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) off[j] = t * 256 + 16 * ((2 * j + (qa >> 1)) ^ swz(t)) + 8 * (qa & 1);
+    }
+    unsigned acc = 0u;
+#pragma unroll 1
+    for (int r = 0; r < rounds; ++r) {
+        const int base = ((r + wave) & 3) * 8192;  // <= 24576; offsets < 8192
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (!TR) {
+                const uint4 x = *reinterpret_cast<const uint4*>(lds + base + off[j]);
+                acc ^= x.x ^ x.y ^ x.z ^ x.w;
+            } else {
+                typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+                const s16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + base + off[j]));
+                const s16x4_t y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + base + 4096 + off[j]));
+                acc ^= __builtin_bit_cast(uint2, x).x ^ __builtin_bit_cast(uint2, x).y ^
+                       __builtin_bit_cast(uint2, y).x ^ __builtin_bit_cast(uint2, y).y;
+            }
+        }
+    }
+    if (acc == kMagic) sink[0] = acc;
+}
+
 }  // namespace
+
+hipError_t launch_mfma_rate(int groups, int rounds, unsigned* sink, hipStream_t stream) {
+    hipLaunchKernelGGL(mfma_rate_kernel, dim3((unsigned)groups), dim3(256), 0, stream, rounds, sink);
+    return hipGetLastError();
+}
+
+hipError_t launch_lds_rate(int pattern, int groups, int rounds, unsigned* sink, hipStream_t stream) {
+    const int k_layout = pattern == 0 || pattern == 3;
+    if (pattern < 2)
+        hipLaunchKernelGGL(lds_rate_kernel<false>, dim3((unsigned)groups), dim3(512), 0, stream, rounds, k_layout, sink);
+    else
+        hipLaunchKernelGGL(lds_rate_kernel<true>, dim3((unsigned)groups), dim3(512), 0, stream, rounds, k_layout, sink);
+    return hipGetLastError();
+}
 
 hipError_t launch_stream_read(const void* src, int64_t bytes, unsigned* sink, hipStream_t stream) {
     if (bytes <= 0) return hipSuccess;

@@ -347,3 +347,16 @@ def test_read_helpers_argument_errors(lib):
     assert call(6, None) == ENULL           # items
     assert call(6, ctypes.c_void_p(0x1004)) == ESHAPE
     assert call(7, 0) == OK                 # no item: no launch
+    m = lib.pkv_mfma_rate
+    m.argtypes = [I, I, P, P]
+    assert m(0, 10, FAKE, None) == ESHAPE
+    assert m(4, 0, FAKE, None) == ESHAPE
+    assert m((1 << 20) + 1, 10, FAKE, None) == ESHAPE
+    assert m(4, 10, None, None) == ENULL
+    r = lib.pkv_lds_read_rate
+    r.argtypes = [I, I, I, P, P]
+    assert r(4, 4, 10, FAKE, None) == ESHAPE   # patterns are 0..3
+    assert r(-1, 4, 10, FAKE, None) == ESHAPE
+    assert r(0, 0, 10, FAKE, None) == ESHAPE
+    assert r(2, 4, -3, FAKE, None) == ESHAPE
+    assert r(1, 4, 10, None, None) == ENULL

@@ -183,9 +183,9 @@ def test_binding_refuses_misshaped_outputs(pkv):
 
 @pytest.mark.gpu
 def test_read_helpers_run(pkv):
-    """The read-only measurement helpers run over a NaN-poisoned batch and a
-    list of items that includes out-of-range entries (skipped) without
-    error."""
+    """The measurement helpers run without error: the read-only ones over a
+    NaN-poisoned batch and a list of items that includes out-of-range entries
+    (skipped), the matrix-core and LDS rate kernels on a few work-groups."""
     b = W.make_batch(cfg=dict(B=3, ctx=[40, 0, 300], Hq=4, Hkv=4, D=128, dtype="f16", cache="f16",
                               pool=None, seed=9, max_ctx=300), device="cuda")
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -193,4 +193,7 @@ def test_read_helpers_run(pkv):
                          dtype=torch.int32, device="cuda")
     pkv.tile_read(b.k_cache, b.v_cache, b.block_tables, b.context_lens, items, sink)
     pkv.stream_read(b.k_cache.view(-1)[:1000], sink)
+    pkv.mfma_rate(8, 3, sink)
+    for pattern in range(4):
+        pkv.lds_read_rate(pattern, 4, 3, sink)
     torch.cuda.synchronize()
