@@ -460,7 +460,8 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
 // work-group, four at a time (one load step), straight from the pool into
 // one of two LDS stages; the step is computed as two halves of two blocks,
 // each one softmax update, and every wave reads the K and V operands once
-// and uses them for its RW row tiles.  One barrier per load step.  The output is accumulated transposed,
+// and uses them for its RW row tiles.  One barrier per load step.  The
+// output is accumulated transposed,
 // O^T = V^T P^T: the P operand is then the score tile as it leaves the first
 // MFMA and each lane's accumulator column is its own query, so rescaling and
 // normalizing need no lane exchange.  The V^T operand comes from the
@@ -641,7 +642,8 @@ void paged_multi_tiled_kernel(MultiArgs a) {
     // tokens x one 32-byte piece each), which asks for distinct swz_v(t) / 2
     // over each 8 tokens.  The two conditions exclude each other, hence two
     // layouts: with one swizzle for both the K reads ran at 0.63 of the
-    // conflict-free rate.
+    // conflict-free rate.  (The 128-byte rows of head_dim 64 keep one layout
+    // for both tiles.)
     auto swz_v = [](int t) {
         return ROW == 128 ? ((2 * t) ^ (3 * (t >> 2))) & 7
                           : 2 * (t & 7) + (((t & 7) >> 2) ^ (t >> 3));
