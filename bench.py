@@ -359,7 +359,7 @@ def practical_ceiling(batch, stream, dec_bytes, reps=10):
     run, of (1) a plain streaming read of the same number of bytes from the
     pool and (2) the decode's own tile reads (the batch's K/V tiles through
     its block tables, longest sequences first, one work-group per (sequence,
-    kv head)) without any arithmetic."""
+    kv head), in the decode's order of work-groups) without any arithmetic."""
     import numpy as np
     import torch
 
@@ -367,7 +367,15 @@ def practical_ceiling(batch, stream, dec_bytes, reps=10):
 
     lens = batch.layout.context_lens
     order = np.argsort(-lens, kind="stable")
-    items = torch.from_numpy(np.array([(s, h) for s in order for h in range(batch.Hkv)],
+
+    def head(t):
+        # the decode's order of a sequence's kv heads (with a multiple of 16
+        # heads, the 8 XCDs read adjacent pairs of them)
+        if batch.Hkv % 16:
+            return t
+        return (t & ~15) | ((t >> 3) & 1) | ((t & 7) << 1)
+
+    items = torch.from_numpy(np.array([(s, head(t)) for s in order for t in range(batch.Hkv)],
                                       np.int32)).cuda()
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     half = min(dec_bytes // 2, batch.k_cache.numel() * batch.k_cache.element_size())

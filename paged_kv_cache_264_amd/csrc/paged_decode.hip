@@ -595,6 +595,19 @@ void paged_decode_kernel(DecodeArgs a) {
     if (a.longest_first) {
         const int item = blockIdx.x / a.n_tiles;
         tile = blockIdx.x % a.n_tiles;
+        // Work-groups go to the 8 XCDs round-robin, so with a multiple of 16
+        // tiles XCD x would get tiles x, x + 8, ... of every sequence.  Taken
+        // through this bijection (per 16 tiles: bit 3 of t to bit 0, bits
+        // 0-2 to bits 1-3), XCD x reads tiles 2 x and 2 x + 1, whose K (and
+        // V) rows of a block lie next to each other in the pool.  Measured
+        // (same box, bit-identical output): LLaMA-7B-shaped batch 391.7
+        // against 398.0 us per launch, INT8 cache 194.5 against 197.3; maps
+        // in which no XCD reads two adjacent tiles (tiles 2, 4 or 8 apart)
+        // stayed at 396-398 us.
+        if ((a.n_tiles & 15) == 0) {
+            const int t = tile;
+            tile = (t & ~15) | ((t >> 3) & 1) | ((t & 7) << 1);
+        }
         int my_key = -1, cnt = 0, my_n = 0;
         if (tid < a.num_seqs) {
             my_n = clamp_len(a.context_lens[tid]);
