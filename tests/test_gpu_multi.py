@@ -65,6 +65,16 @@ def test_multi_matrix(pkv, dtype, D, Hq, Hkv):
     _run(pkv, dtype, D, Hq, Hkv, lens, qlens, seed=D + Hq)
 
 
+@pytest.mark.parametrize("Hkv", [16, 32, 48])
+def test_multi_xcd_head_order(pkv, Hkv):
+    """Short query runs with one work-group per (sequence, kv head) and a
+    multiple of 16 kv heads: the kernel takes the kv heads in its XCD order;
+    every head of every query row must still come from its own kv head."""
+    lens = [1, 16, 17, 250, 33]
+    qlens = [1, 4, 8, 16, 5]
+    _run(pkv, "f16", 64, Hkv, Hkv, lens, qlens, seed=Hkv)
+
+
 @pytest.mark.parametrize("P", [16, 48, 64, 512])
 def test_multi_partitions(pkv, P):
     lens = [5, 64, 129, 1000, 1500]

@@ -95,6 +95,22 @@ def test_schedule_ties_and_ragged_batch(pkv, P, dtype, cache, Hq, Hkv):
     _check_step(pkv, batch, partition_size=P)
 
 
+@pytest.mark.parametrize("dtype,cache,D,Hq,Hkv", [("f16", "f16", 64, 16, 16),
+                                                   ("bf16", "bf16", 64, 48, 48),
+                                                   ("f16", "i8", 128, 32, 32),
+                                                   ("f16", "u4", 128, 32, 8)])
+def test_xcd_head_order(pkv, dtype, cache, D, Hq, Hkv):
+    """With a multiple of 16 q-head tiles per sequence (16, 48 and 32 one-head
+    tiles; 16 two-head tiles of a 4-bit GQA batch, two per kv head) the decode
+    takes the tiles in its XCD order: every head of every sequence must still
+    be computed once, from its own kv head."""
+    lens = [1, 37, 300, 16, 129, 0, 70]
+    batch = W.make_batch(cfg=_cfg(dtype, cache, D, Hq, Hkv, lens, seed=Hq + D), device="cuda")
+    gpu_populate(pkv, batch)
+    _check_step(pkv, batch)
+    _check_step(pkv, batch, partition_size=64)
+
+
 def test_tiny_config(pkv):
     batch = W.make_batch("tiny", device="cuda")
     _check_step(pkv, batch)
