@@ -42,6 +42,9 @@ WORKLOAD_NAMES = {
     "prefill": "llama7b-mha-fp16-chunked-prefill-512",
     "sampling": "llama7b-parallel-sampling-shared-prefix-decode",
     "int8-write": "llama7b-int8kv-cache-write-64-new-tokens",
+    "tp8": "llama7b-mha-fp16-decode-one-gpu-share-of-8-by-kv-head",
+    "dp8": "llama7b-mha-fp16-decode-one-gpu-share-of-8-by-sequence",
+    "cp8": "long-32k-fp16-decode-one-gpu-share-of-8-by-context",
 }
 # the device code of a kernel: its source file, the device helpers and the
 # argument struct it is launched with (host-side edits elsewhere leave the

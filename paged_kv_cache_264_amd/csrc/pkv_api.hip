@@ -189,17 +189,27 @@ int pkv_default_partition_size(int num_seqs, int num_q_heads, int num_kv_heads,
         return 0;
     // Measured on MI355X: a work-group pays a chain of dependent memory
     // round trips (context length, block ids, first K/V tiles) before it
-    // streams, so long partitions stream best; they are cut only as far as
-    // needed to give the 256 CUs about 8 work-groups each at the maximum
-    // context (one tile per kv head), at most 4096 tokens.  A batch that
-    // already has 1024 (sequence, kv head) items fills the chip with about 4
-    // per CU and partitions of up to 8192 tokens (the GQA batch of 128
-    // sequences x 8 kv heads at contexts up to 8192: 397 -> 389 us without
-    // the split and its merge).  Power of two in [256, 8192].
+    // streams, and a split adds the merge launch, so long partitions stream
+    // best; they are cut only as far as needed to give the chip about as
+    // many work-groups as it holds at once, counted at the maximum context:
+    // 1024 for one-head tiles (two 8-wave work-groups per CU), 256 for tiles
+    // of several q heads (their registers leave room for one per CU).
+    // Partitions of at most 4096 tokens, or 8192 once the batch has 1024
+    // (sequence, kv head) items.  Sweeps of the fused step over powers of
+    // two (same box), µs at the size this picks, and in brackets at the size
+    // the rule before picked (2048 work-groups whatever the tile): GQA 32/8
+    // 4 x 32k 85.9 (109.1), 8 x 32k 169.9 (182.0), 1 x 32k 26.4 (40.3),
+    // 16 x U[1024, 8192] 59.9 (68.1), 64 x U[512, 4096] 90.0 (119.2), each
+    // the best size or within 1.1% of it; one-head tiles: 64 sequences x 4
+    // heads 55.0 (57.0), 16 x U[512, 4096] 89.0 (91.4), 32 x U[1024, 8192]
+    // x 8 heads 106.0 (106.3), 16 x U[4096, 16384] x 16 heads 203.2 (204.5),
+    // 2 x 16k and 1 x 32k within 0.3% of the rule before; 8 x U[512, 4096]
+    // measured 61.0 unsplit against 64.9 (64.7) here.  Power of two in
+    // [256, 8192].
     const int64_t seq_tiles = (int64_t)num_seqs * num_kv_heads;
     const int64_t max_tokens = (int64_t)max_blocks_per_seq * pkv::kBlockSize;
     const bool wide = seq_tiles >= 1024;
-    const int64_t per = wide ? 1024 : 2048;                             // work-groups wanted
+    const int64_t per = num_q_heads == num_kv_heads ? 1024 : 256;      // work-groups wanted
     const int64_t want = (max_tokens * seq_tiles + per - 1) / per;      // tokens per work-group
     const int cap = wide ? 8192 : 4096;
     int P = 256;

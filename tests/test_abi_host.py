@@ -123,14 +123,20 @@ def test_workspace_size(lib):
         p = lib.pkv_default_partition_size(*args)
         assert p >= 64 and p % 16 == 0
     d = lib.pkv_default_partition_size
-    # fewer than 1024 (sequence, kv head) items: about 8 work-groups per CU at
-    # the longest context, at most 4096 tokens
+    # about 1024 work-groups at the longest context for one-head tiles, 256
+    # for tiles of several q heads; fewer than 1024 (sequence, kv head) items:
+    # at most 4096 tokens
     assert d(16, 32, 32, 2048) == 4096      # 512 items, 32k tokens
-    assert d(2, 32, 32, 1024) == 512        # 64 items, 16k tokens
-    # >= 1024 items already fill the chip: up to 8192 tokens, about 4 per CU
+    assert d(2, 32, 32, 1024) == 1024       # 64 items, 16k tokens
+    assert d(64, 4, 4, 256) == 1024         # 256 items, 4k tokens
+    assert d(4, 32, 8, 2048) == 4096        # GQA: 32 items, 32k tokens
+    assert d(1, 32, 8, 2048) == 1024        # GQA: 8 items, 32k tokens
+    assert d(64, 32, 8, 256) == 4096        # GQA: 512 items, 4k tokens (cap)
+    # >= 1024 items already fill the chip: up to 8192 tokens
     assert d(128, 32, 8, 512) == 8192       # the GQA batch: no sequence split
     assert d(64, 32, 32, 256) == 8192       # 4096-token contexts stay whole
-    assert d(256, 32, 8, 64) == 2048        # 2048 items of at most 1024 tokens
+    assert d(256, 32, 8, 64) == 8192        # 2048 GQA items of at most 1024 tokens
+    assert d(256, 32, 32, 4) == 512         # 8192 items of at most 64 tokens
 
 
 def test_cache_write_argument_errors(lib):

@@ -70,6 +70,19 @@ CONFIGS = {
     # FP8 (e4m3) KV cache at the LLaMA-7B shape, populated the same way.
     "fp8": dict(B=64, ctx=(512, 4096), Hq=32, Hkv=32, D=128, dtype="f16", cache="f8",
                 pool=None, seed=8, max_ctx=4096),
+    # One GPU's share of the LLaMA-7B batch when 8 GPUs split it: by kv head
+    # (4 of the 32 heads, every sequence; the same context lengths), by
+    # sequence (8 sequences of the same length distribution, all heads), and
+    # one GPU's share of the Long batch split by context (4,096 of each
+    # sequence's 32,768 positions, 512-token partitions whose merge stands in
+    # for the one after the all-gather of the partials).
+    "tp8": dict(B=64, ctx=(512, 4096), Hq=4, Hkv=4, D=128, dtype="f16", cache="f16",
+                pool=None, seed=2, max_ctx=4096),
+    "dp8": dict(B=8, ctx=(512, 4096), Hq=32, Hkv=32, D=128, dtype="f16", cache="f16",
+                pool=None, seed=13, max_ctx=4096),
+    "cp8": dict(B=16, ctx=[4096] * 16, Hq=32, Hkv=32, D=128, dtype="f16", cache="f16",
+                pool=None, seed=4, max_ctx=4096, outlier_frac=0.01, outlier_mult=20.0,
+                partition_size=512),
 }
 
 TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
