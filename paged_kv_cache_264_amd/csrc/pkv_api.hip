@@ -182,6 +182,23 @@ const char* pkv_status_string(pkv_status s) {
 
 const char* pkv_last_error(void) { return pkv::last_error(); }
 
+}  // extern "C"
+
+namespace {
+// The smallest power of two in [256, cap] that cuts the longest context of
+// `items` work items into about `wgs` work-groups in all; cap = 8192 once
+// there are 1024 items, else 4096.
+int pow2_partition(int64_t items, int64_t max_tokens, int64_t wgs) {
+    const int cap = items >= 1024 ? 8192 : 4096;
+    const int64_t want = (max_tokens * items + wgs - 1) / wgs;  // tokens per work-group
+    int P = 256;
+    while (P < cap && P < want) P <<= 1;
+    return P;
+}
+}  // namespace
+
+extern "C" {
+
 int pkv_default_partition_size(int num_seqs, int num_q_heads, int num_kv_heads,
                                int max_blocks_per_seq) {
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
@@ -207,14 +224,8 @@ int pkv_default_partition_size(int num_seqs, int num_q_heads, int num_kv_heads,
     // measured 61.0 unsplit against 64.9 (64.7) here.  Power of two in
     // [256, 8192].
     const int64_t seq_tiles = (int64_t)num_seqs * num_kv_heads;
-    const int64_t max_tokens = (int64_t)max_blocks_per_seq * pkv::kBlockSize;
-    const bool wide = seq_tiles >= 1024;
-    const int64_t per = num_q_heads == num_kv_heads ? 1024 : 256;      // work-groups wanted
-    const int64_t want = (max_tokens * seq_tiles + per - 1) / per;      // tokens per work-group
-    const int cap = wide ? 8192 : 4096;
-    int P = 256;
-    while (P < cap && P < want) P <<= 1;
-    return P;
+    return pow2_partition(seq_tiles, (int64_t)max_blocks_per_seq * pkv::kBlockSize,
+                          num_q_heads == num_kv_heads ? 1024 : 256);
 }
 
 size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
@@ -540,9 +551,12 @@ int pkv_multi_default_partition_size(int num_seqs, int max_query_len, int num_q_
         return 0;
     const int64_t rows = (int64_t)max_query_len * (num_q_heads / num_kv_heads);
     const int64_t tiles = (rows + 15) / 16;
-    const int64_t items = (int64_t)num_seqs * tiles;
-    return pkv_default_partition_size(items > 0x7fffffff ? 0x7fffffff : (int)items, num_q_heads,
-                                      num_kv_heads, max_blocks_per_seq);
+    const int64_t items = (int64_t)num_seqs * tiles * num_kv_heads;
+    // about 2048 work-groups at the longest context (1024 once the items
+    // fill the chip), for every head grouping: the multi-query kernels'
+    // own rule, not re-measured with the decode's
+    return pow2_partition(items, (int64_t)max_blocks_per_seq * pkv::kBlockSize,
+                          items >= 1024 ? 1024 : 2048);
 }
 
 }  // extern "C"
