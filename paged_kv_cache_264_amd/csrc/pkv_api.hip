@@ -552,11 +552,15 @@ int pkv_multi_default_partition_size(int num_seqs, int max_query_len, int num_q_
     const int64_t rows = (int64_t)max_query_len * (num_q_heads / num_kv_heads);
     const int64_t tiles = (rows + 15) / 16;
     const int64_t items = (int64_t)num_seqs * tiles * num_kv_heads;
-    // about 2048 work-groups at the longest context (1024 once the items
-    // fill the chip), for every head grouping: the multi-query kernels'
-    // own rule, not re-measured with the decode's
+    // About 512 work-groups of 4 waves at the longest context (1024 once
+    // the items fill the chip).  Sweeps over all powers of two (same box),
+    // 8 or 4 queries per sequence: the size this picks was the best on all
+    // six shapes; µs, and in brackets at the size a 2048-work-group rule
+    // picked: 8 x U[512, 4096] 32 heads 63.4 (84.3), 2 x 16k 88.3 (101.8),
+    // GQA 32/8 16 x U[1024, 8192] 109.3 (122.5), 4 x 32k 90.0 (110.4);
+    // 64 x U[512, 4096] GQA and MHA unchanged (within 0.1% of the best).
     return pow2_partition(items, (int64_t)max_blocks_per_seq * pkv::kBlockSize,
-                          items >= 1024 ? 1024 : 2048);
+                          items >= 1024 ? 1024 : 512);
 }
 
 }  // extern "C"

@@ -137,6 +137,16 @@ def test_workspace_size(lib):
     assert d(64, 32, 32, 256) == 8192       # 4096-token contexts stay whole
     assert d(256, 32, 8, 64) == 8192        # 2048 GQA items of at most 1024 tokens
     assert d(256, 32, 32, 4) == 512         # 8192 items of at most 64 tokens
+    m = lib.pkv_multi_default_partition_size
+    m.argtypes = [ctypes.c_int] * 5
+    # multi-query: about 512 work-groups at the longest context, 1024 once
+    # the (sequence, row tile, kv head) items reach 1024
+    assert m(8, 8, 32, 32, 256) == 2048     # 256 items, 4k tokens
+    assert m(4, 4, 32, 8, 2048) == 2048     # GQA, 16 rows: 32 items, 32k tokens
+    assert m(16, 8, 32, 8, 512) == 4096     # GQA, 32 rows: 256 items, 8k tokens
+    assert m(64, 8, 32, 32, 256) == 8192    # the verify batch: 2048 items
+    assert m(16, 512, 32, 32, 256) == 8192  # the prefill batch
+    assert m(4, 0, 32, 8, 16) == 0 and m(4, 8, 32, 6, 16) == 0
 
 
 def test_cache_write_argument_errors(lib):
