@@ -224,8 +224,13 @@ int pkv_default_partition_size(int num_seqs, int num_q_heads, int num_kv_heads,
     // measured 61.0 unsplit against 64.9 (64.7) here.  Power of two in
     // [256, 8192].
     const int64_t seq_tiles = (int64_t)num_seqs * num_kv_heads;
-    return pow2_partition(seq_tiles, (int64_t)max_blocks_per_seq * pkv::kBlockSize,
-                          num_q_heads == num_kv_heads ? 1024 : 256);
+    const int64_t max_tokens = (int64_t)max_blocks_per_seq * pkv::kBlockSize;
+    const int P = pow2_partition(seq_tiles, max_tokens, num_q_heads == num_kv_heads ? 1024 : 256);
+    // one-head tiles over at most 1024 tokens: no split (the merge launch
+    // costs more than it parallelizes: 1 x 1k 16.3 -> 14.2 us, 4 x 1k 16.0
+    // -> 15.3, 16 x 1k 44.7 -> 41.3)
+    if (num_q_heads == num_kv_heads && max_tokens <= 1024 && P < max_tokens) return 1024;
+    return P;
 }
 
 size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,

@@ -137,6 +137,10 @@ def test_workspace_size(lib):
     assert d(64, 32, 32, 256) == 8192       # 4096-token contexts stay whole
     assert d(256, 32, 8, 64) == 8192        # 2048 GQA items of at most 1024 tokens
     assert d(256, 32, 32, 4) == 512         # 8192 items of at most 64 tokens
+    assert d(1, 32, 32, 64) == 1024         # one-head tiles of at most 1024 tokens: no split
+    assert d(16, 32, 32, 64) == 1024
+    assert d(1, 32, 32, 256) == 256         # 4096 tokens: split
+    assert d(1, 32, 8, 64) == 256           # GQA tiles keep the rule
     m = lib.pkv_multi_default_partition_size
     m.argtypes = [ctypes.c_int] * 5
     # multi-query: about 512 work-groups at the longest context, 1024 once
