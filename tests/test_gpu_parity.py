@@ -111,6 +111,18 @@ def test_xcd_head_order(pkv, dtype, cache, D, Hq, Hkv):
     _check_step(pkv, batch, partition_size=64)
 
 
+@pytest.mark.parametrize("dtype,cache,D", [("f16", "f16", 128), ("bf16", "i8", 128),
+                                           ("f16", "f8", 64), ("bf16", "u4", 256)])
+def test_multi_query_attention_heads(pkv, dtype, cache, D):
+    """MQA: 32 q heads over one kv head (four 8-head tiles, or 4-head and
+    2-head tiles for 8-bit and 4-bit caches, all reading the same K/V)."""
+    lens = [1, 300, 16, 77, 1000]
+    batch = W.make_batch(cfg=_cfg(dtype, cache, D, 32, 1, lens, seed=D + 1), device="cuda")
+    gpu_populate(pkv, batch)
+    _check_step(pkv, batch)
+    _check_step(pkv, batch, partition_size=128)
+
+
 def test_tiny_config(pkv):
     batch = W.make_batch("tiny", device="cuda")
     _check_step(pkv, batch)
