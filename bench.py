@@ -186,7 +186,8 @@ def main():
     mbs = batch.block_tables.shape[1]
     mbs_eff = min(mbs, int(cfg.get("window", 0)) // W.BLOCK_SIZE + 2) if cfg.get("window") \
         else mbs
-    P_eff = P or pkv.default_partition_size(batch.B, batch.Hq, batch.Hkv, mbs_eff)
+    P_eff = P or pkv.default_partition_size(batch.B, batch.Hq, batch.Hkv, mbs_eff,
+                                            batch.k_cache.dtype)
     out = torch.empty_like(batch.q)
     NP = pkv.num_partitions(mbs_eff, P_eff)
     partials = (torch.empty((batch.B, batch.Hq, NP), dtype=torch.float32, device="cuda"),
@@ -229,7 +230,8 @@ def main():
     # (split-context decode; single-partition sequences finish here), phase 2
     # (merge of the longer ones).
     ws = torch.empty(pkv.decode_workspace_size(batch.B, batch.Hq, batch.Hkv, batch.D, mbs_eff,
-                                               P_eff), dtype=torch.uint8, device="cuda")
+                                               P_eff, batch.k_cache.dtype),
+                     dtype=torch.uint8, device="cuda")
 
     def step_fused(ev0=None, ev1=None):
         if ev0 is not None:
@@ -657,9 +659,9 @@ def bench_sampling(args):
     v_new = W.token_rows(B, Hkv, D, cfg["dtype"], seed, W.S_NEWV, "cuda")
     out = torch.empty_like(q)
     scale = float(np.float32(1.0 / math.sqrt(D)))
-    P = pkv.default_partition_size(B, Hq, Hkv, mbs)
-    ws = torch.empty(pkv.decode_workspace_size(B, Hq, Hkv, D, mbs, P), dtype=torch.uint8,
-                     device="cuda")
+    P = pkv.default_partition_size(B, Hq, Hkv, mbs, kc.dtype)
+    ws = torch.empty(pkv.decode_workspace_size(B, Hq, Hkv, D, mbs, P, kc.dtype),
+                     dtype=torch.uint8, device="cuda")
     shared = args.sampling_decode == "shared"
     # the shared prefix of a prompt's samples: its whole blocks (the partial
     # last block is copied on write at the first step)

@@ -132,22 +132,28 @@ pkv_status pkv_kv_cache_write(const void* k, const void* v, void* k_cache, void*
                               hipStream_t stream);
 
 /*
- * Partition size (tokens, a multiple of 16) that pkv_paged_attn_decode uses
- * when it is passed partition_size == 0.  Returns 0 for invalid arguments.
+ * Partition size (tokens, a multiple of 16) that pkv_paged_attn_decode (and
+ * the other decode entry points) use when passed partition_size == 0, for a
+ * cache of cache_dtype.  A power of two in [256, 8192], chosen from the sizes
+ * and the tile the decode takes (one q head, several q heads of a kv head,
+ * or the matrix-core path of 8 to 63 q heads per kv head over a 16-bit
+ * cache).  Returns 0 for invalid arguments.
  */
 int pkv_default_partition_size(int num_seqs, int num_q_heads, int num_kv_heads,
-                               int max_blocks_per_seq);
+                               int max_blocks_per_seq, pkv_dtype cache_dtype);
 
 /*
- * Bytes of workspace pkv_paged_attn_decode needs for these sizes
- * (partition_size 0 means the default above).  Returns 0 for invalid sizes.
+ * Bytes of workspace pkv_paged_attn_decode needs for these sizes and cache
+ * dtype (partition_size 0 means the default above).  Returns 0 for invalid
+ * sizes.
  * The workspace holds the fp32 partial results of sequences longer than one
  * partition; it needs no initialization and its contents after a call are
  * unspecified.  Two decode calls that may run at the same time must not share
  * a workspace.
  */
 size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                                 int max_blocks_per_seq, int partition_size);
+                                 int max_blocks_per_seq, int partition_size,
+                                 pkv_dtype cache_dtype);
 
 /*
  * Single-query decode attention over the paged cache (lazyllm lesson 4,
@@ -251,7 +257,7 @@ pkv_status pkv_paged_attn_decode_append_static(void* out, const void* q, const v
  * pkv_paged_attn_decode with max_blocks_per_seq replaced by
  * min(max_blocks_per_seq, sliding_window / 16 + 2), the most blocks a window
  * touches: workspace_bytes >= pkv_decode_workspace_size(num_seqs, num_q_heads,
- * num_kv_heads, head_dim, that value, partition_size).
+ * num_kv_heads, head_dim, that value, partition_size, cache_dtype).
  */
 pkv_status pkv_paged_attn_decode_sliding(void* out, const void* q, const void* k_new,
                                          const void* v_new, void* k_cache, void* v_cache,

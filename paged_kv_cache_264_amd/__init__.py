@@ -80,9 +80,9 @@ def _load():
                         ctypes.c_size_t)
     L.pkv_kv_cache_write.argtypes = [P, P, P, P, P, P, P, I64, I, I, I, I64, I, I, P]
     L.pkv_kv_cache_write.restype = I
-    L.pkv_default_partition_size.argtypes = [I, I, I, I]
+    L.pkv_default_partition_size.argtypes = [I, I, I, I, I]
     L.pkv_default_partition_size.restype = I
-    L.pkv_decode_workspace_size.argtypes = [I, I, I, I, I, I]
+    L.pkv_decode_workspace_size.argtypes = [I, I, I, I, I, I, I]
     L.pkv_decode_workspace_size.restype = SZ
     L.pkv_paged_attn_decode.argtypes = [P, P, P, P, P, P, P, I, P, I, I, I, I, I, I64, F, I, P,
                                         SZ, I, I, P]
@@ -185,9 +185,12 @@ def _code(dtype: torch.dtype, name: str) -> int:
     return _DTYPE[dtype]
 
 
-def default_partition_size(num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq) -> int:
+def default_partition_size(num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq,
+                           cache_dtype: torch.dtype) -> int:
+    """The partition size the decode entry points use when passed 0, for a
+    cache of cache_dtype (the torch dtype of k_cache)."""
     return _load().pkv_default_partition_size(num_seqs, num_q_heads, num_kv_heads,
-                                              max_blocks_per_seq)
+                                              max_blocks_per_seq, _code(cache_dtype, "cache_dtype"))
 
 
 def num_partitions(max_blocks_per_seq: int, partition_size: int) -> int:
@@ -195,9 +198,12 @@ def num_partitions(max_blocks_per_seq: int, partition_size: int) -> int:
 
 
 def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
-                          partition_size=0) -> int:
+                          partition_size, cache_dtype: torch.dtype) -> int:
+    """Workspace bytes of a decode over a cache of cache_dtype (partition_size
+    0: the default size)."""
     return _load().pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                             max_blocks_per_seq, partition_size)
+                                             max_blocks_per_seq, partition_size,
+                                             _code(cache_dtype, "cache_dtype"))
 
 
 def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
@@ -267,7 +273,7 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, ou
                                            k_scale, v_scale)
     out = _out(out, q)
     mbs = block_tables.shape[1]
-    need = decode_workspace_size(B, Hq, Hkv, D, mbs, partition_size)
+    need = decode_workspace_size(B, Hq, Hkv, D, mbs, partition_size, k_cache.dtype)
     if workspace is None:
         workspace = _workspace(q.device, need)
     else:
@@ -296,7 +302,7 @@ def paged_attn_decode_append(q, k_new, v_new, k_cache, v_cache, block_tables, co
         raise ValueError("k_new and v_new must be [num_seqs][num_kv_heads][head_dim]")
     out = _out(out, q)
     mbs = block_tables.shape[1]
-    need = decode_workspace_size(B, Hq, Hkv, D, mbs, partition_size)
+    need = decode_workspace_size(B, Hq, Hkv, D, mbs, partition_size, k_cache.dtype)
     if workspace is None:
         workspace = _workspace(q.device, need)
     else:
@@ -407,7 +413,7 @@ def paged_attn_decode_sliding(q, k_cache, v_cache, block_tables, context_lens, s
     out = _out(out, q)
     mbs = block_tables.shape[1]
     mbs_eff = min(mbs, int(sliding_window) // BLOCK_SIZE + 2) if sliding_window > 0 else mbs
-    need = decode_workspace_size(B, Hq, Hkv, D, mbs_eff, partition_size)
+    need = decode_workspace_size(B, Hq, Hkv, D, mbs_eff, partition_size, k_cache.dtype)
     if workspace is None:
         workspace = _workspace(q.device, need)
     else:

@@ -124,7 +124,17 @@ __global__ __launch_bounds__(kThreads) void kv_cache_write_kernel(CacheWriteArgs
     if (row >= n_rows) return;  // whole rows leave together (rows are lane-aligned)
     const int64_t tok = row / a.num_kv_heads;
     const int h = (int)(row % a.num_kv_heads);
-    const int64_t slot = a.slot_mapping[tok];
+    int64_t slot = -1;
+    if (a.slot_mapping) {
+        slot = a.slot_mapping[tok];
+    } else {
+        const int n_cap = a.max_blocks_per_seq * kBlockSize;
+        const int n = min(a.context_lens[tok], n_cap);
+        if (n >= 1) {
+            const int phys = a.block_tables[tok * a.max_blocks_per_seq + (n - 1) / kBlockSize];
+            slot = phys < 0 ? -1 : (int64_t)phys * kBlockSize + (n - 1) % kBlockSize;
+        }
+    }
     if (slot < 0 || slot >= a.num_blocks * kBlockSize) return;
     const int64_t blk = slot / kBlockSize, off = slot % kBlockSize;
     const size_t src = (size_t)row * D + (size_t)j * 8;

@@ -96,6 +96,12 @@ template <> struct Mfma<Elem::F16> {
     static __device__ __forceinline__ uint32_t pack(float x, float y) {
         return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{x, y}, f16x2_t));
     }
+    // the pair back to floats (exact)
+    static __device__ __forceinline__ void unpack(uint32_t w, float& x, float& y) {
+        const f16x2_t h = __builtin_bit_cast(f16x2_t, w);
+        x = (float)h[0];
+        y = (float)h[1];
+    }
 };
 template <> struct Mfma<Elem::BF16> {
     static __device__ __forceinline__ f32x4_t qk(const uint4& a, const uint4& b, f32x4_t c) {
@@ -114,6 +120,11 @@ template <> struct Mfma<Elem::BF16> {
     // two floats to a pair of bf16, nearest even (one v_cvt_pk_bf16_f32)
     static __device__ __forceinline__ uint32_t pack(float x, float y) {
         return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{x, y}, bf16x2_t));
+    }
+    // the pair back to floats (exact: a bf16 is the top half of an fp32)
+    static __device__ __forceinline__ void unpack(uint32_t w, float& x, float& y) {
+        x = __builtin_bit_cast(float, w << 16);
+        y = __builtin_bit_cast(float, w & 0xffff0000u);
     }
 };
 
@@ -219,10 +230,11 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
 
     const int Hq = a.num_q_heads;
     const int g = Hq / a.num_kv_heads;
-    const int q0 = a.query_start_loc[b];
+    const int q0 = a.one_query ? b : a.query_start_loc[b];
     // query rows must lie in [0, T): a malformed query_start_loc skips rows
-    const int q1 = min(a.query_start_loc[b + 1], a.num_tokens);
-    const int qlen = a.query_start_loc[b + 1] - q0;  // positions follow the given count
+    const int q1 = min(a.one_query ? b + 1 : a.query_start_loc[b + 1], a.num_tokens);
+    // positions follow the given count
+    const int qlen = a.one_query ? 1 : a.query_start_loc[b + 1] - q0;
     const int rows_total = q0 < 0 ? 0 : max(0, q1 - q0) * g;
     if (rt * kRows >= rows_total) return;
     // the sequence whose length and block table the rows read (a group's
@@ -374,6 +386,17 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
         }
         __asm__ volatile("" ::: "memory");
         const uint2 pa = make_uint2(Mfma<T>::pack(p[0], p[1]), Mfma<T>::pack(p[2], p[3]));
+        // with exact_p the rest of each weight, lo = p - hi, as a second
+        // 16-bit operand: |lo| <= 2^-8 |p| (bf16) or 2^-11 |p| (fp16), and
+        // its own rounding leaves 2^-16 |p| or 2^-22 |p| (2^-25 absolute for
+        // an fp16 subnormal lo)
+        uint2 pl = make_uint2(0u, 0u);
+        if (a.exact_p) {
+            float h0, h1, h2, h3;
+            Mfma<T>::unpack(pa.x, h0, h1);
+            Mfma<T>::unpack(pa.y, h2, h3);
+            pl = make_uint2(Mfma<T>::pack(p[0] - h0, p[1] - h1), Mfma<T>::pack(p[2] - h2, p[3] - h3));
+        }
         if (grew) {
 #pragma unroll
             for (int nn = 0; nn < NN; ++nn) o[nn] *= alpha;
@@ -385,6 +408,7 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
                 __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vst + v_off + nn * 32));
             // O^T = V^T P^T: the accumulator column is the lane's own query
             o[nn] = Mfma<T>::pv(__builtin_bit_cast(uint2, vt), pa, o[nn]);
+            if (a.exact_p) o[nn] = Mfma<T>::pv(__builtin_bit_cast(uint2, vt), pl, o[nn]);
         }
         __asm__ volatile("" ::: "memory");
     };
@@ -565,9 +589,9 @@ void paged_multi_tiled_kernel(MultiArgs a) {
 
     const int Hq = a.num_q_heads;
     const int g = Hq / a.num_kv_heads;
-    const int q0 = a.query_start_loc[b];
-    const int q1 = min(a.query_start_loc[b + 1], a.num_tokens);
-    const int qlen = a.query_start_loc[b + 1] - q0;
+    const int q0 = a.one_query ? b : a.query_start_loc[b];
+    const int q1 = min(a.one_query ? b + 1 : a.query_start_loc[b + 1], a.num_tokens);
+    const int qlen = a.one_query ? 1 : a.query_start_loc[b + 1] - q0;
     const int rows_total = q0 < 0 ? 0 : max(0, q1 - q0) * g;
     const int wg_r0 = rg * WG_ROWS;
     if (wg_r0 >= rows_total) return;

@@ -185,63 +185,87 @@ const char* pkv_last_error(void) { return pkv::last_error(); }
 }  // extern "C"
 
 namespace {
-// The smallest power of two in [256, cap] that cuts the longest context of
-// `items` work items into about `wgs` work-groups in all; cap = 8192 once
-// there are 1024 items, else 4096.
-int pow2_partition(int64_t items, int64_t max_tokens, int64_t wgs) {
-    const int cap = items >= 1024 ? 8192 : 4096;
-    const int64_t want = (max_tokens * items + wgs - 1) / wgs;  // tokens per work-group
+// The smallest power of two in [256, cap] that cuts the longest context of a
+// launch with `count` work-groups per partition into about `wgs` in all.
+int pow2_partition(int64_t count, int64_t max_tokens, int64_t wgs, int cap) {
+    const int64_t want = (max_tokens * count + wgs - 1) / wgs;  // tokens per work-group
     int P = 256;
     while (P < cap && P < want) P <<= 1;
     return P;
+}
+
+// Decodes of 8 to 63 q heads per kv head over a 16-bit cache run on the
+// matrix cores (the short-run multi-query kernel; see decode_mfma).
+bool decode_on_matrix_cores(int g, int window, pkv_dtype q_dtype, pkv_dtype cache_dtype) {
+    return window == 0 && g >= 8 && g < 64 && q_dtype == cache_dtype &&
+           (cache_dtype == PKV_F16 || cache_dtype == PKV_BF16);
+}
+
+// Measured on MI355X: a work-group pays a chain of dependent memory round
+// trips (context length, block ids, first K/V tiles) before it streams, and
+// a split adds the merge launch, so long partitions stream best; they are cut
+// only as far as needed to give the chip about as many work-groups as it
+// holds at once, counted at the maximum context: 1024 for one-head tiles
+// (two 8-wave work-groups per CU), 256 for tiles of several q heads (their
+// registers leave room for one per CU; work-groups counted as the decode
+// launches them, num_seqs x num_q_heads / heads per tile), and for the
+// decodes on the matrix cores the multi-query kernel's rule.  Partitions of
+// at most 4096 tokens, or 8192 once the batch has 1024 (sequence, kv head)
+// items.  Sweeps of the fused step over powers of two (same box), µs at the
+// size this picks, and in brackets at the size a rule of 2048 work-groups
+// per (sequence, kv head) item picked: GQA 32/8 4 x 32k 85.9 (109.1), 8 x
+// 32k 169.9 (182.0), 1 x 32k 26.4 (40.3), 16 x U[1024, 8192] 59.9 (68.1),
+// 64 x U[512, 4096] 90.0 (119.2); one-head tiles: 64 sequences x 4 heads
+// 55.0 (57.0), 16 x U[512, 4096] 89.0 (91.4), 32 x U[1024, 8192] x 8 heads
+// 106.0 (106.3), 16 x U[4096, 16384] x 16 heads 203.2 (204.5); 32 q / 4 kv
+// heads x 64 sequences, INT8 83.1 (102.5 at half the size), 32 q / 2 kv
+// heads x 32 sequences, 4-bit 53.8 (71.1); on the matrix cores 32 q / 4 kv
+// heads 69.7 (88.7), 32 q / 1 kv head 42.2.  Each the best size or within
+// 1.2% of it, but for 8 x U[512, 4096]: 61.0 unsplit against 64.9 here.
+int decode_default_partition(int num_seqs, int num_q_heads, int num_kv_heads,
+                             int max_blocks_per_seq, pkv_dtype cache_dtype) {
+    const int g = num_q_heads / num_kv_heads;
+    const int64_t items = (int64_t)num_seqs * num_kv_heads;
+    const int64_t max_tokens = (int64_t)max_blocks_per_seq * pkv::kBlockSize;
+    const int cap = items >= 1024 ? 8192 : 4096;
+    if (decode_on_matrix_cores(g, 0, cache_dtype, cache_dtype)) {
+        const int64_t rows = items * ((g + 15) / 16);  // 16-row tiles
+        return pow2_partition(rows, max_tokens, rows >= 1024 ? 1024 : 512,
+                              rows >= 1024 ? 8192 : 4096);
+    }
+    if (g == 1) {
+        const int P = pow2_partition(items, max_tokens, 1024, cap);
+        // over at most 1024 tokens: no split (the merge launch costs more
+        // than it parallelizes: 1 x 1k 16.3 -> 14.2 us, 16 x 1k 44.7 -> 41.3)
+        return max_tokens <= 1024 && P < max_tokens ? 1024 : P;
+    }
+    const int64_t wgs = (int64_t)num_seqs * (num_q_heads / heads_per_tile(g, cache_dtype));
+    return pow2_partition(wgs, max_tokens, 256, cap);
 }
 }  // namespace
 
 extern "C" {
 
 int pkv_default_partition_size(int num_seqs, int num_q_heads, int num_kv_heads,
-                               int max_blocks_per_seq) {
+                               int max_blocks_per_seq, pkv_dtype cache_dtype) {
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
-        num_q_heads % num_kv_heads != 0)
+        num_q_heads % num_kv_heads != 0 || !(is_float(cache_dtype) || is_quantized(cache_dtype)))
         return 0;
-    // Measured on MI355X: a work-group pays a chain of dependent memory
-    // round trips (context length, block ids, first K/V tiles) before it
-    // streams, and a split adds the merge launch, so long partitions stream
-    // best; they are cut only as far as needed to give the chip about as
-    // many work-groups as it holds at once, counted at the maximum context:
-    // 1024 for one-head tiles (two 8-wave work-groups per CU), 256 for tiles
-    // of several q heads (their registers leave room for one per CU).
-    // Partitions of at most 4096 tokens, or 8192 once the batch has 1024
-    // (sequence, kv head) items.  Sweeps of the fused step over powers of
-    // two (same box), µs at the size this picks, and in brackets at the size
-    // the rule before picked (2048 work-groups whatever the tile): GQA 32/8
-    // 4 x 32k 85.9 (109.1), 8 x 32k 169.9 (182.0), 1 x 32k 26.4 (40.3),
-    // 16 x U[1024, 8192] 59.9 (68.1), 64 x U[512, 4096] 90.0 (119.2), each
-    // the best size or within 1.1% of it; one-head tiles: 64 sequences x 4
-    // heads 55.0 (57.0), 16 x U[512, 4096] 89.0 (91.4), 32 x U[1024, 8192]
-    // x 8 heads 106.0 (106.3), 16 x U[4096, 16384] x 16 heads 203.2 (204.5),
-    // 2 x 16k and 1 x 32k within 0.3% of the rule before; 8 x U[512, 4096]
-    // measured 61.0 unsplit against 64.9 (64.7) here.  Power of two in
-    // [256, 8192].
-    const int64_t seq_tiles = (int64_t)num_seqs * num_kv_heads;
-    const int64_t max_tokens = (int64_t)max_blocks_per_seq * pkv::kBlockSize;
-    const int P = pow2_partition(seq_tiles, max_tokens, num_q_heads == num_kv_heads ? 1024 : 256);
-    // one-head tiles over at most 1024 tokens: no split (the merge launch
-    // costs more than it parallelizes: 1 x 1k 16.3 -> 14.2 us, 4 x 1k 16.0
-    // -> 15.3, 16 x 1k 44.7 -> 41.3)
-    if (num_q_heads == num_kv_heads && max_tokens <= 1024 && P < max_tokens) return 1024;
-    return P;
+    return decode_default_partition(num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq,
+                                    cache_dtype);
 }
 
 size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                                 int max_blocks_per_seq, int partition_size) {
+                                 int max_blocks_per_seq, int partition_size,
+                                 pkv_dtype cache_dtype) {
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
         num_q_heads % num_kv_heads != 0 || !head_dim_ok(head_dim) || partition_size < 0 ||
-        partition_size % pkv::kBlockSize != 0)
+        partition_size % pkv::kBlockSize != 0 ||
+        !(is_float(cache_dtype) || is_quantized(cache_dtype)))
         return 0;
     const int P = partition_size ? partition_size
-                                 : pkv_default_partition_size(num_seqs, num_q_heads, num_kv_heads,
-                                                              max_blocks_per_seq);
+                                 : decode_default_partition(num_seqs, num_q_heads, num_kv_heads,
+                                                            max_blocks_per_seq, cache_dtype);
     return layout(num_seqs, num_q_heads, head_dim, num_partitions(max_blocks_per_seq, P)).total;
 }
 
@@ -274,8 +298,8 @@ pkv_status pkv_kv_cache_write(const void* k, const void* v, void* k_cache, void*
     if (cache_dtype == PKV_U4 &&
         ((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 7u))
         return fail(PKV_ERR_SHAPE, "4-bit k_scale and v_scale must be 8-byte aligned");
-    pkv::CacheWriteArgs a{k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping,
-                          num_tokens, num_blocks, num_kv_heads};
+    pkv::CacheWriteArgs a{k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping, nullptr,
+                          nullptr, 0, num_tokens, num_blocks, num_kv_heads};
     return hip_status(
         pkv::launch_kv_cache_write(a, (int)src_dtype, (int)cache_dtype, head_dim, stream),
         "kv_cache_write launch");
@@ -405,6 +429,66 @@ pkv_status decode_phase1(void* out, float* m_part, float* l_part, float* o_part,
                       "paged decode launch");
 }
 
+// The decode of q-head groups of 8 to 63 per kv head (16-bit caches, no
+// window) on the matrix cores: the decode kernel's tiles of 8 heads keep 8
+// dot products per K row in vector registers and run at about half the HBM
+// rate, while the short-run multi-query kernel takes a kv head's 8..63 heads
+// as MFMA rows.  Its softmax weights enter P.V as two 16-bit parts (exact_p),
+// so the result keeps the decode's precision.  With new tokens, the cache
+// write stores them first (each sequence's slot at its context end) and the
+// attention reads them from the cache.  Measured (decode of U[512, 4096]
+// contexts, fp16 / bf16): 64 q / 8 kv heads x 64 sequences 145-147 ->
+// 103 us, x 256 sequences 585-591 -> 367 us, 32 q / 4 kv heads x 64
+// sequences 113-115 -> 63 us (the multi-query kernel with 16-bit weights);
+// 4 q heads per kv head stay on the decode kernel (368 us either way).
+pkv_status decode_mfma(void* out, float* m, float* l, float* o, const void* q, const void* k_new,
+                       const void* v_new, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, int max_blocks_per_seq,
+                       const int32_t* context_lens, int num_seqs, int num_q_heads,
+                       int num_kv_heads, int head_dim, int64_t num_blocks, float scale, int P,
+                       int NP, pkv_dtype dtype, hipStream_t stream) {
+    if (k_new) {
+        pkv::CacheWriteArgs w{k_new, v_new, const_cast<void*>(k_cache),
+                              const_cast<void*>(v_cache), nullptr, nullptr, nullptr,
+                              block_tables, context_lens, max_blocks_per_seq, num_seqs,
+                              num_blocks, num_kv_heads};
+        pkv_status s = hip_status(
+            pkv::launch_kv_cache_write(w, (int)dtype, (int)dtype, head_dim, stream),
+            "new-token store launch");
+        if (s != PKV_OK) return s;
+    }
+    const int g = num_q_heads / num_kv_heads;
+    pkv::MultiArgs a{};
+    a.out = out;
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.query_start_loc = nullptr;
+    a.m_part = m;
+    a.l_part = l;
+    a.o_part = o;
+    a.num_blocks = num_blocks;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.partition_size = P;
+    a.num_partitions = NP;
+    a.row_tiles = (int)pkv::multi_row_groups(g, head_dim);
+    a.max_rows = g;
+    a.num_tokens = num_seqs;
+    a.causal = 1;
+    a.one_query = 1;
+    a.exact_p = 1;
+    a.scale_log2 = scale * 1.44269504088896340736f;
+    if ((int64_t)num_seqs * num_kv_heads * a.row_tiles * NP > 0x7fffffff)
+        return fail(PKV_ERR_SHAPE, "too many work items for one launch");
+    return hip_status(pkv::launch_paged_multi(a, (int)dtype, head_dim, stream),
+                      "paged decode (matrix cores) launch");
+}
+
 // Phase 1 with direct output, then the merge of sequences with > 1 partition.
 pkv_status decode_both_phases(void* out, const void* q, const void* k_new, const void* v_new,
                               const void* k_cache, const void* v_cache, const float* k_scale,
@@ -427,8 +511,8 @@ pkv_status decode_both_phases(void* out, const void* q, const void* k_new, const
     if (!aligned16(out)) return fail(PKV_ERR_SHAPE, "out must be 16-byte aligned");
     const int mbs_eff = window_blocks(max_blocks_per_seq, window);
     const int P = partition_size ? partition_size
-                                 : pkv_default_partition_size(num_seqs, num_q_heads, num_kv_heads,
-                                                              mbs_eff);
+                                 : decode_default_partition(num_seqs, num_q_heads, num_kv_heads,
+                                                            mbs_eff, cache_dtype);
     const int NP = num_partitions(mbs_eff, P);
     const WorkspaceLayout w = layout(num_seqs, num_q_heads, head_dim, NP);
     if (!workspace || workspace_bytes < w.total)
@@ -440,10 +524,15 @@ pkv_status decode_both_phases(void* out, const void* q, const void* k_new, const
     float* m = reinterpret_cast<float*>(ws + w.m_off);
     float* l = reinterpret_cast<float*>(ws + w.l_off);
     float* o = reinterpret_cast<float*>(ws + w.o_off);
-    s = decode_phase1(out, m, l, o, q, k_new, v_new, k_cache, v_cache, k_scale, v_scale,
-                      block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
-                      num_kv_heads, head_dim, block_size, num_blocks, scale, P, NP, q_dtype,
-                      cache_dtype, window, stream);
+    if (decode_on_matrix_cores(num_q_heads / num_kv_heads, window, q_dtype, cache_dtype))
+        s = decode_mfma(out, m, l, o, q, k_new, v_new, k_cache, v_cache, block_tables,
+                        max_blocks_per_seq, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                        head_dim, num_blocks, scale, P, NP, q_dtype, stream);
+    else
+        s = decode_phase1(out, m, l, o, q, k_new, v_new, k_cache, v_cache, k_scale, v_scale,
+                          block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                          num_kv_heads, head_dim, block_size, num_blocks, scale, P, NP, q_dtype,
+                          cache_dtype, window, stream);
     if (s != PKV_OK) return s;
     if (NP == 1) return ok();  // every sequence was finished in phase 1
     return reduce_impl(out, m, l, o, context_lens, num_seqs, num_q_heads, head_dim, P, NP, 1,
@@ -565,7 +654,7 @@ int pkv_multi_default_partition_size(int num_seqs, int max_query_len, int num_q_
     // GQA 32/8 16 x U[1024, 8192] 109.3 (122.5), 4 x 32k 90.0 (110.4);
     // 64 x U[512, 4096] GQA and MHA unchanged (within 0.1% of the best).
     return pow2_partition(items, (int64_t)max_blocks_per_seq * pkv::kBlockSize,
-                          items >= 1024 ? 1024 : 512);
+                          items >= 1024 ? 1024 : 512, items >= 1024 ? 8192 : 4096);
 }
 
 }  // extern "C"
@@ -916,7 +1005,7 @@ pkv_status pkv_paged_attn_decode_append_static(
     if (!aligned16(k_new) || !aligned16(v_new))
         return fail(PKV_ERR_SHAPE, "k_new and v_new must be 16-byte aligned");
     const size_t need = pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                                  max_blocks_per_seq, partition_size);
+                                                  max_blocks_per_seq, partition_size, cache_dtype);
     if (need > kStaticScratchBytes)
         return fail(PKV_ERR_WORKSPACE,
                     "the partials of this call need %zu bytes, more than the %zu-byte static "

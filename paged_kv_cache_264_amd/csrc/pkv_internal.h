@@ -124,6 +124,13 @@ struct MultiArgs {
     // context_lens[query_start_loc[b]] and the block table of that first
     // sequence, shared by all its members
     int group_rows;
+    // 1: sequence b has one query, row b of q (a decode; query_start_loc is
+    // not read)
+    int one_query;
+    // 1: the softmax weights enter the P.V products as two 16-bit parts,
+    // p = hi + lo (hi = p rounded, lo = the rest rounded), so the products
+    // carry fp32-level weights instead of weights rounded to 16 bits
+    int exact_p;
     float scale_log2;
 };
 
@@ -165,6 +172,12 @@ struct CacheWriteArgs {
     float* k_scale;
     float* v_scale;
     const int64_t* slot_mapping;
+    // used when slot_mapping is null: token b is sequence b's new token, at
+    // position context_lens[b] - 1 of its block table (no store when the
+    // length is 0 or the block id is out of range)
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    int max_blocks_per_seq;
     int64_t num_tokens;
     int64_t num_blocks;
     int num_kv_heads;

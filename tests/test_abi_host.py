@@ -113,34 +113,48 @@ def test_empty_batch_is_ok_without_launch(lib):
 
 def test_workspace_size(lib):
     f = lib.pkv_decode_workspace_size
-    f.argtypes = [ctypes.c_int] * 6
-    assert f(64, 32, 32, 128, 256, 512) > 64 * 32 * 8 * 128 * 4
-    assert f(64, 32, 32, 96, 256, 512) == 0
-    assert f(64, 32, 32, 128, 256, 24) == 0
-    assert f(4, 8, 3, 64, 8, 0) == 0
-    lib.pkv_default_partition_size.argtypes = [ctypes.c_int] * 4
-    for args in [(64, 32, 32, 256), (1, 32, 8, 2048), (16, 32, 32, 2048), (128, 32, 8, 512)]:
-        p = lib.pkv_default_partition_size(*args)
-        assert p >= 64 and p % 16 == 0
+    f.argtypes = [ctypes.c_int] * 7
+    assert f(64, 32, 32, 128, 256, 512, F16) > 64 * 32 * 8 * 128 * 4
+    assert f(64, 32, 32, 96, 256, 512, F16) == 0
+    assert f(64, 32, 32, 128, 256, 24, F16) == 0
+    assert f(4, 8, 3, 64, 8, 0, F16) == 0
+    assert f(64, 32, 32, 128, 256, 512, 9) == 0      # no such cache dtype
+    # the default size's partials: a split batch needs room, one that is not
+    # split needs none beyond the alignment
+    assert f(1, 32, 8, 128, 2048, 0, BF16) > 8 * 32 * 128 * 4
+    lib.pkv_default_partition_size.argtypes = [ctypes.c_int] * 5
     d = lib.pkv_default_partition_size
+    for args in [(64, 32, 32, 256), (1, 32, 8, 2048), (16, 32, 32, 2048), (128, 32, 8, 512)]:
+        for dt in (F32, F16, BF16, I8, F8, U4):
+            p = d(*args, dt)
+            assert p >= 256 and p % 16 == 0 and p & (p - 1) == 0
+    assert d(64, 32, 32, 256, 9) == 0
     # about 1024 work-groups at the longest context for one-head tiles, 256
-    # for tiles of several q heads; fewer than 1024 (sequence, kv head) items:
-    # at most 4096 tokens
-    assert d(16, 32, 32, 2048) == 4096      # 512 items, 32k tokens
-    assert d(2, 32, 32, 1024) == 1024       # 64 items, 16k tokens
-    assert d(64, 4, 4, 256) == 1024         # 256 items, 4k tokens
-    assert d(4, 32, 8, 2048) == 4096        # GQA: 32 items, 32k tokens
-    assert d(1, 32, 8, 2048) == 1024        # GQA: 8 items, 32k tokens
-    assert d(64, 32, 8, 256) == 4096        # GQA: 512 items, 4k tokens (cap)
+    # for tiles of several q heads (counted as launched: num_seqs x num_q_heads
+    # / heads per tile); fewer than 1024 (sequence, kv head) items: at most
+    # 4096 tokens
+    assert d(16, 32, 32, 2048, F16) == 4096      # 512 items, 32k tokens
+    assert d(2, 32, 32, 1024, F16) == 1024       # 64 items, 16k tokens
+    assert d(64, 4, 4, 256, F16) == 1024         # 256 items, 4k tokens
+    assert d(4, 32, 8, 2048, BF16) == 4096       # GQA: 32 items, 32k tokens
+    assert d(1, 32, 8, 2048, BF16) == 1024       # GQA: 8 items, 32k tokens
+    assert d(64, 32, 8, 256, BF16) == 4096       # GQA: 512 items, 4k tokens (cap)
+    assert d(64, 32, 4, 256, I8) == 4096         # 8 heads per kv head in 2 tiles of 4
+    assert d(32, 32, 2, 256, U4) == 4096         # 16 per kv head in 8 tiles of 2
     # >= 1024 items already fill the chip: up to 8192 tokens
-    assert d(128, 32, 8, 512) == 8192       # the GQA batch: no sequence split
-    assert d(64, 32, 32, 256) == 8192       # 4096-token contexts stay whole
-    assert d(256, 32, 8, 64) == 8192        # 2048 GQA items of at most 1024 tokens
-    assert d(256, 32, 32, 4) == 512         # 8192 items of at most 64 tokens
-    assert d(1, 32, 32, 64) == 1024         # one-head tiles of at most 1024 tokens: no split
-    assert d(16, 32, 32, 64) == 1024
-    assert d(1, 32, 32, 256) == 256         # 4096 tokens: split
-    assert d(1, 32, 8, 64) == 256           # GQA tiles keep the rule
+    assert d(128, 32, 8, 512, BF16) == 8192      # the GQA batch: no sequence split
+    assert d(64, 32, 32, 256, F16) == 8192       # 4096-token contexts stay whole
+    assert d(256, 32, 8, 64, BF16) == 8192       # 2048 GQA items of at most 1024 tokens
+    assert d(256, 32, 32, 4, F16) == 512         # 8192 items of at most 64 tokens
+    assert d(1, 32, 32, 64, F16) == 1024         # one-head tiles of at most 1024 tokens: no split
+    assert d(16, 32, 32, 64, I8) == 1024
+    assert d(1, 32, 32, 256, F16) == 256         # 4096 tokens: split
+    assert d(1, 32, 8, 64, BF16) == 256          # GQA tiles keep the rule
+    # 8 to 63 q heads per kv head over a 16-bit cache (the matrix cores): the
+    # multi-query rule over (sequence, kv head, 16-row tile) items
+    assert d(64, 32, 4, 256, F16) == 2048        # 256 items, 4k tokens
+    assert d(64, 64, 8, 256, BF16) == 4096       # 512 items
+    assert d(64, 32, 1, 256, BF16) == 1024       # 32 per kv head: 2 row tiles, 128 items
     m = lib.pkv_multi_default_partition_size
     m.argtypes = [ctypes.c_int] * 5
     # multi-query: about 512 work-groups at the longest context, 1024 once

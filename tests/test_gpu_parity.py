@@ -373,7 +373,8 @@ def bench_partition(pkv, batch):
     window = int(batch.cfg.get("window", 0))
     mbs_eff = min(mbs, window // BS + 2) if window else mbs
     P = batch.cfg.get("partition_size", 0)
-    return (P or pkv.default_partition_size(batch.B, batch.Hq, batch.Hkv, mbs_eff)), mbs_eff
+    return (P or pkv.default_partition_size(batch.B, batch.Hq, batch.Hkv, mbs_eff,
+                                            batch.k_cache.dtype)), mbs_eff
 
 
 def _slot_rows(t, blk, off):
@@ -400,7 +401,8 @@ def test_full_config(pkv, name):
     P, mbs_eff = bench_partition(pkv, batch)
     NP = pkv.num_partitions(mbs_eff, P)
     out, out_guard = guarded(tuple(batch.q.shape), batch.q.dtype)
-    need = pkv.decode_workspace_size(batch.B, batch.Hq, batch.Hkv, batch.D, mbs_eff, P)
+    need = pkv.decode_workspace_size(batch.B, batch.Hq, batch.Hkv, batch.D, mbs_eff, P,
+                                     batch.k_cache.dtype)
     ws, ws_guard = guarded((need,), torch.uint8)
     kw = dict(k_scale=batch.k_scale, v_scale=batch.v_scale, partition_size=P, workspace=ws)
     if window:

@@ -62,7 +62,8 @@ def run_case(pkv, c: dict):
     out, out_guard = guarded(tuple(batch.q.shape), batch.q.dtype)
     mbs = batch.block_tables.shape[1]
     mbs_eff = min(mbs, window // BS + 2) if window else mbs
-    need = pkv.decode_workspace_size(batch.B, batch.Hq, batch.Hkv, batch.D, mbs_eff, c["P"])
+    need = pkv.decode_workspace_size(batch.B, batch.Hq, batch.Hkv, batch.D, mbs_eff, c["P"],
+                                     batch.k_cache.dtype)
     ws, ws_guard = guarded((max(need, 256),), torch.uint8)
     kw = dict(k_scale=batch.k_scale, v_scale=batch.v_scale, partition_size=c["P"], workspace=ws,
               out=out)
