@@ -144,7 +144,8 @@ __device__ __forceinline__ void load_to_lds16(__amdgpu_buffer_rsrc_t r, char* ld
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voffset, 0, 0, 0);
 }
 
-template <Elem T, int D>
+// XP: the weights enter P.V as two 16-bit parts (MultiArgs::exact_p)
+template <Elem T, int D, bool XP>
 __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
     constexpr int KK = D / 32;          // 16x16x32 MFMAs per score tile
     constexpr int NN = D / 16;          // 16x16x16 MFMAs (output column tiles) per block
@@ -391,7 +392,7 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
         // its own rounding leaves 2^-16 |p| or 2^-22 |p| (2^-25 absolute for
         // an fp16 subnormal lo)
         uint2 pl = make_uint2(0u, 0u);
-        if (a.exact_p) {
+        if constexpr (XP) {
             float h0, h1, h2, h3;
             Mfma<T>::unpack(pa.x, h0, h1);
             Mfma<T>::unpack(pa.y, h2, h3);
@@ -408,7 +409,7 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
                 __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vst + v_off + nn * 32));
             // O^T = V^T P^T: the accumulator column is the lane's own query
             o[nn] = Mfma<T>::pv(__builtin_bit_cast(uint2, vt), pa, o[nn]);
-            if (a.exact_p) o[nn] = Mfma<T>::pv(__builtin_bit_cast(uint2, vt), pl, o[nn]);
+            if constexpr (XP) o[nn] = Mfma<T>::pv(__builtin_bit_cast(uint2, vt), pl, o[nn]);
         }
         __asm__ volatile("" ::: "memory");
     };
@@ -918,9 +919,18 @@ template <Elem T>
 hipError_t launch_d(const MultiArgs& a, int d, int64_t grid, hipStream_t s) {
     const dim3 g((unsigned)grid), blk(kThreads);
     switch (d) {
-    case 64: hipLaunchKernelGGL((paged_multi_kernel<T, 64>), g, blk, 0, s, a); break;
-    case 128: hipLaunchKernelGGL((paged_multi_kernel<T, 128>), g, blk, 0, s, a); break;
-    case 256: hipLaunchKernelGGL((paged_multi_kernel<T, 256>), g, blk, 0, s, a); break;
+    case 64:
+        if (a.exact_p) hipLaunchKernelGGL((paged_multi_kernel<T, 64, true>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((paged_multi_kernel<T, 64, false>), g, blk, 0, s, a);
+        break;
+    case 128:
+        if (a.exact_p) hipLaunchKernelGGL((paged_multi_kernel<T, 128, true>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((paged_multi_kernel<T, 128, false>), g, blk, 0, s, a);
+        break;
+    case 256:
+        if (a.exact_p) hipLaunchKernelGGL((paged_multi_kernel<T, 256, true>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((paged_multi_kernel<T, 256, false>), g, blk, 0, s, a);
+        break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
