@@ -42,6 +42,7 @@ WORKLOAD_NAMES = {
     "prefill": "llama7b-mha-fp16-chunked-prefill-512",
     "sampling": "llama7b-parallel-sampling-shared-prefix-decode",
     "int8-write": "llama7b-int8kv-cache-write-64-new-tokens",
+    "gqa8": "gqa-64q8kv-bf16-paged-decode",
     "tp8": "llama7b-mha-fp16-decode-one-gpu-share-of-8-by-kv-head",
     "dp8": "llama7b-mha-fp16-decode-one-gpu-share-of-8-by-sequence",
     "cp8": "long-32k-fp16-decode-one-gpu-share-of-8-by-context",
@@ -102,7 +103,7 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
 
 
-def traffic_for(key: str, alg_bytes: int):
+def traffic_for(key: str, alg_bytes: int, sources=None):
     """HBM bytes per decode launch from committed rocprofv3 counter runs, if
     they were taken on the current kernel source."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -111,7 +112,7 @@ def traffic_for(key: str, alg_bytes: int):
     with open(path) as f:
         data = json.load(f)
     rec = data.get(key)
-    if not rec or rec.get("kernel_sha") != kernel_sha():
+    if not rec or rec.get("kernel_sha") != kernel_sha(sources):
         return None, None
     t = float(rec["fetch_bytes_per_launch"]) + float(rec["write_bytes_per_launch"])
     return t, t / alg_bytes
@@ -297,7 +298,25 @@ def main():
     dec_ms = per_launch_events(step, args.steps)
     achieved = launch_bytes / (dec_avg_ms * 1e-3) / 1e9
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    traffic, traffic_ratio = traffic_for(f"{args.config}/{args.step}", launch_bytes)
+    # The library runs decodes of 8 to 63 q heads per kv head over a 16-bit
+    # cache (q in the cache's dtype, no window) on the matrix cores: a cache
+    # write launch, then the multi-query kernel (phase 1 alone keeps the
+    # decode kernel).
+    g = batch.Hq // batch.Hkv
+    mfma_route = (args.step == "fused" and not window and 8 <= g < 64 and
+                  cfg["cache"] == cfg["dtype"] and cfg["cache"] in ("f16", "bf16"))
+    sources = MULTI_SOURCES if mfma_route else KERNEL_SOURCES
+    traffic, traffic_ratio = traffic_for(f"{args.config}/{args.step}", launch_bytes, sources)
+    if mfma_route:
+        kernel_label = "kv_cache_write_kernel + paged_multi_kernel" + (
+            " + paged_reduce_kernel" if NP > 1 else "") + " (events span the step)"
+        launches = {"kv_cache_write_kernel": 1, "paged_multi_kernel": 1,
+                    "paged_reduce_kernel": 1 if NP > 1 else 0}
+    else:
+        kernel_label = "paged_decode_kernel" + (" + paged_reduce_kernel (events span both)"
+                                                if (NP > 1 and args.step == "fused") else "")
+        launches = {"kv_cache_write_kernel": 0 if args.step == "fused" else 1,
+                    "paged_decode_kernel": 1, "paged_reduce_kernel": 1 if NP > 1 else 0}
 
     result = {
         "metric": METRIC,
@@ -341,12 +360,9 @@ def main():
             "traffic": None if traffic is None else int(traffic),
             "traffic_unit": "bytes/launch",
             "traffic_over_alg": None if traffic_ratio is None else round(traffic_ratio, 4),
-            "kernel": "paged_decode_kernel" + (" + paged_reduce_kernel (events span both)"
-                                                if (NP > 1 and args.step == "fused") else ""),
-            "kernel_sha": kernel_sha(),
-            "launches_per_step": {"kv_cache_write_kernel": 0 if args.step == "fused" else 1,
-                                  "paged_decode_kernel": 1,
-                                  "paged_reduce_kernel": 1 if NP > 1 else 0},
+            "kernel": kernel_label,
+            "kernel_sha": kernel_sha(sources),
+            "launches_per_step": launches,
         },
     }
     if batch.k_cache.element_size() * batch.D * W.BLOCK_SIZE == 4096 and not window:

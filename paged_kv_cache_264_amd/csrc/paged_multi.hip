@@ -16,7 +16,7 @@
 // dense contraction, so it runs on the matrix cores.
 //   * rows: the (query token, q head) pairs that read one kv head, 16 per
 //     tile; a work-group is one (sequence, kv head, row tile, partition) with
-//     4 waves, each streaming a contiguous run of the partition's blocks.
+//     4 waves (8 for one query per sequence), each streaming a contiguous run of the partition's blocks.
 //   * scores: S^T = K Q^T, one v_mfma_f32_16x16x32 per 32 channels.  The A
 //     operand is the K tile (lane l: token l%16, 8 channels), fetched from
 //     the pool in token order and staged in a per-wave LDS tile; the B
@@ -33,7 +33,7 @@
 //     them only when a score exceeds it; each lane sums its own tokens and
 //     the 4 partial sums are added once at the end.
 //   * tokens past a query's position, past the partition or past the context
-//     are masked by select; the 4 waves are merged through LDS at the end.
+//     are masked by select; the waves are merged through LDS at the end.
 //     Sequences with one partition write the output directly, longer ones
 //     write (m, l, o) partials for the merge kernel.
 #include "pkv_device.h"
@@ -54,13 +54,15 @@ typedef short s16x4_v __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_v __attribute__((ext_vector_type(4)));
 
 constexpr int kRows = 16;
-#ifndef PKV_MULTI_WAVES
-#define PKV_MULTI_WAVES 4
-#endif
-// waves per work-group of the short-run kernel (8 measured slower on MI355X:
-// verify 409.5 -> 425.0 us, shared-prefix sampling decode 97.0 -> 98.8 us)
-constexpr int kWaves = PKV_MULTI_WAVES;
-constexpr int kThreads = kWaves * 64;
+// Waves per work-group of the short-run kernel.  Runs of several queries use
+// 4 (8 measured slower on MI355X: verify 381.7 -> 389.2 us per launch,
+// shared-prefix sampling decode 97.0 -> 98.8 us).  A single query per
+// sequence (decode of 8-63 q heads per kv head) fills at most one 16-row
+// tile, so its work-groups are few and short of loads in flight: 8 waves
+// there took a 64-sequence, 64 q / 8 kv head bf16 decode from 127.1 to
+// 118.0 us.
+constexpr int kWavesRuns = 4;
+constexpr int kWavesOneQuery = 8;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kNegBig = -3.0e38f;
 // The running max of a row is the reference the weights are taken against,
@@ -145,8 +147,9 @@ __device__ __forceinline__ void load_to_lds16(__amdgpu_buffer_rsrc_t r, char* ld
 }
 
 // XP: the weights enter P.V as two 16-bit parts (MultiArgs::exact_p)
-template <Elem T, int D, bool XP>
-__global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
+template <Elem T, int D, bool XP, int kWaves>
+__global__ __launch_bounds__(kWaves * 64) void paged_multi_kernel(MultiArgs a) {
+    constexpr int kThreads = kWaves * 64;
     constexpr int KK = D / 32;          // 16x16x32 MFMAs per score tile
     constexpr int NN = D / 16;          // 16x16x16 MFMAs (output column tiles) per block
     constexpr int VL = D / 32;          // 16-byte V loads per lane per block
@@ -161,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
     constexpr int KS = ROW + 16;
 
     // LDS: the per-wave K and V stages during the loop, then (same bytes) the
-    // output tiles of waves 1..3 for the final merge
+    // output tiles of waves 1.. for the final merge
     constexpr int kStage = kWaves * kRows * (VS + KS);
     constexpr int kMerge = (kWaves - 1) * kRows * D * 4;
     __shared__ __attribute__((aligned(16))) char s_buf[kStage > kMerge ? kStage : kMerge];
@@ -425,7 +428,7 @@ __global__ __launch_bounds__(kThreads) void paged_multi_kernel(MultiArgs a) {
         }
     }
 
-    // ---- merge the 4 waves (wave 0 keeps its tile in registers) ------------
+    // ---- merge the waves (wave 0 keeps its tile in registers) --------------
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
     __syncthreads();  // every wave is done with its V stage
@@ -915,22 +918,26 @@ constexpr int kTiledRW = 1;                 // row tiles per wave in the tiled k
 constexpr int kTiledWaves = 8;              // waves per work-group of the tiled kernel
 constexpr int kTiledMinRows = 64;           // rows per (sequence, kv head) that select it
 
+template <Elem T, int D>
+void launch_dw(const MultiArgs& a, int64_t grid, hipStream_t s) {
+    const dim3 g((unsigned)grid);
+    if (a.one_query) {
+        const dim3 blk(kWavesOneQuery * 64);
+        if (a.exact_p) hipLaunchKernelGGL((paged_multi_kernel<T, D, true, kWavesOneQuery>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((paged_multi_kernel<T, D, false, kWavesOneQuery>), g, blk, 0, s, a);
+    } else {
+        const dim3 blk(kWavesRuns * 64);
+        if (a.exact_p) hipLaunchKernelGGL((paged_multi_kernel<T, D, true, kWavesRuns>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((paged_multi_kernel<T, D, false, kWavesRuns>), g, blk, 0, s, a);
+    }
+}
+
 template <Elem T>
 hipError_t launch_d(const MultiArgs& a, int d, int64_t grid, hipStream_t s) {
-    const dim3 g((unsigned)grid), blk(kThreads);
     switch (d) {
-    case 64:
-        if (a.exact_p) hipLaunchKernelGGL((paged_multi_kernel<T, 64, true>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((paged_multi_kernel<T, 64, false>), g, blk, 0, s, a);
-        break;
-    case 128:
-        if (a.exact_p) hipLaunchKernelGGL((paged_multi_kernel<T, 128, true>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((paged_multi_kernel<T, 128, false>), g, blk, 0, s, a);
-        break;
-    case 256:
-        if (a.exact_p) hipLaunchKernelGGL((paged_multi_kernel<T, 256, true>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((paged_multi_kernel<T, 256, false>), g, blk, 0, s, a);
-        break;
+    case 64: launch_dw<T, 64>(a, grid, s); break;
+    case 128: launch_dw<T, 128>(a, grid, s); break;
+    case 256: launch_dw<T, 256>(a, grid, s); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

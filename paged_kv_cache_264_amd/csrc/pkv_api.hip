@@ -209,7 +209,7 @@ bool decode_on_matrix_cores(int g, int window, pkv_dtype q_dtype, pkv_dtype cach
 // (two 8-wave work-groups per CU), 256 for tiles of several q heads (their
 // registers leave room for one per CU; work-groups counted as the decode
 // launches them, num_seqs x num_q_heads / heads per tile), and for the
-// decodes on the matrix cores the multi-query kernel's rule.  Partitions of
+// decodes on the matrix cores their own (below).  Partitions of
 // at most 4096 tokens, or 8192 once the batch has 1024 (sequence, kv head)
 // items.  Sweeps of the fused step over powers of two (same box), µs at the
 // size this picks, and in brackets at the size a rule of 2048 work-groups
@@ -219,8 +219,7 @@ bool decode_on_matrix_cores(int g, int window, pkv_dtype q_dtype, pkv_dtype cach
 // 55.0 (57.0), 16 x U[512, 4096] 89.0 (91.4), 32 x U[1024, 8192] x 8 heads
 // 106.0 (106.3), 16 x U[4096, 16384] x 16 heads 203.2 (204.5); 32 q / 4 kv
 // heads x 64 sequences, INT8 83.1 (102.5 at half the size), 32 q / 2 kv
-// heads x 32 sequences, 4-bit 53.8 (71.1); on the matrix cores 32 q / 4 kv
-// heads 69.7 (88.7), 32 q / 1 kv head 42.2.  Each the best size or within
+// heads x 32 sequences, 4-bit 53.8 (71.1).  Each the best size or within
 // 1.2% of it, but for 8 x U[512, 4096]: 61.0 unsplit against 64.9 here.
 int decode_default_partition(int num_seqs, int num_q_heads, int num_kv_heads,
                              int max_blocks_per_seq, pkv_dtype cache_dtype) {
@@ -229,8 +228,16 @@ int decode_default_partition(int num_seqs, int num_q_heads, int num_kv_heads,
     const int64_t max_tokens = (int64_t)max_blocks_per_seq * pkv::kBlockSize;
     const int cap = items >= 1024 ? 8192 : 4096;
     if (decode_on_matrix_cores(g, 0, cache_dtype, cache_dtype)) {
+        // 8-wave work-groups, one per 16-row tile and partition: about 256
+        // of them (512 once there are 1024 tiles) at the longest context.
+        // Sweeps of the step over powers of two, µs at the size this picks
+        // and in brackets at the size of the 4-wave multi-query rule: 64 q /
+        // 8 kv heads bf16, 64 x U[512, 4096] 105.9 (105.9), 8 x U[8k, 16k]
+        // 73.5 (81.9), 256 x U[512, 4096] 399.3 (399.3); 32 q / 1 kv head
+        // bf16 64 x U[512, 4096] 42.6 (46.0); 32 q / 2 kv heads 16 x U[512,
+        // 4096] 21.6; 32 q / 4 kv heads 64 x U[512, 4096] 67.1 (66.5).
         const int64_t rows = items * ((g + 15) / 16);  // 16-row tiles
-        return pow2_partition(rows, max_tokens, rows >= 1024 ? 1024 : 512,
+        return pow2_partition(rows, max_tokens, rows >= 1024 ? 512 : 256,
                               rows >= 1024 ? 8192 : 4096);
     }
     if (g == 1) {

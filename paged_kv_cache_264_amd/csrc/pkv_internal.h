@@ -135,7 +135,7 @@ struct MultiArgs {
 };
 
 // Work-groups along the query rows of one (sequence, kv head): 16-row tiles
-// for short query runs, 4 waves x 16 x RW rows for long ones.
+// for short query runs, 8 waves x 16 x RW rows for long ones.
 int64_t multi_row_groups(int max_rows, int head_dim);
 
 // Multi-query causal attention (fp16 / bf16 caches).  Returns

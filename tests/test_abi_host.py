@@ -151,10 +151,13 @@ def test_workspace_size(lib):
     assert d(1, 32, 32, 256, F16) == 256         # 4096 tokens: split
     assert d(1, 32, 8, 64, BF16) == 256          # GQA tiles keep the rule
     # 8 to 63 q heads per kv head over a 16-bit cache (the matrix cores): the
-    # multi-query rule over (sequence, kv head, 16-row tile) items
-    assert d(64, 32, 4, 256, F16) == 2048        # 256 items, 4k tokens
-    assert d(64, 64, 8, 256, BF16) == 4096       # 512 items
-    assert d(64, 32, 1, 256, BF16) == 1024       # 32 per kv head: 2 row tiles, 128 items
+    # own rule over (sequence, kv head, 16-row tile) items
+    assert d(64, 32, 4, 256, F16) == 4096        # 256 row tiles, 4k tokens
+    assert d(64, 64, 8, 256, BF16) == 4096       # 512 row tiles (cap)
+    assert d(64, 32, 1, 256, BF16) == 2048       # 32 per kv head: 2 row tiles, 128 in all
+    assert d(8, 64, 8, 1024, F16) == 4096        # 64 row tiles, 16k tokens
+    assert d(16, 32, 2, 256, F16) == 512         # 32 row tiles, 4k tokens
+    assert d(256, 64, 8, 256, BF16) == 8192      # 2048 row tiles (cap)
     m = lib.pkv_multi_default_partition_size
     m.argtypes = [ctypes.c_int] * 5
     # multi-query: about 512 work-groups at the longest context, 1024 once

@@ -70,6 +70,10 @@ CONFIGS = {
     # FP8 (e4m3) KV cache at the LLaMA-7B shape, populated the same way.
     "fp8": dict(B=64, ctx=(512, 4096), Hq=32, Hkv=32, D=128, dtype="f16", cache="f8",
                 pool=None, seed=8, max_ctx=4096),
+    # GQA with 8 q heads per kv head (64 q / 8 kv heads, D=128, bf16: the
+    # attention of a LLaMA-70B-shaped layer), B=64, ctx U[512,4096].
+    "gqa8": dict(B=64, ctx=(512, 4096), Hq=64, Hkv=8, D=128, dtype="bf16", cache="bf16",
+                 pool=None, seed=14, max_ctx=4096),
     # One GPU's share of the LLaMA-7B batch when 8 GPUs split it: by kv head
     # (4 of the 32 heads, every sequence; the same context lengths), by
     # sequence (8 sequences of the same length distribution, all heads), and
