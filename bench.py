@@ -299,18 +299,18 @@ def main():
     achieved = launch_bytes / (dec_avg_ms * 1e-3) / 1e9
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     # The library runs decodes of 8 to 63 q heads per kv head over a 16-bit
-    # cache (q in the cache's dtype, no window) on the matrix cores: a cache
-    # write launch, then the multi-query kernel (phase 1 alone keeps the
-    # decode kernel).
+    # cache (q in the cache's dtype, no window) on the matrix cores: the
+    # multi-query kernel, which also stores the new token (phase 1 alone
+    # keeps the decode kernel).
     g = batch.Hq // batch.Hkv
     mfma_route = (args.step == "fused" and not window and 8 <= g < 64 and
                   cfg["cache"] == cfg["dtype"] and cfg["cache"] in ("f16", "bf16"))
     sources = MULTI_SOURCES if mfma_route else KERNEL_SOURCES
     traffic, traffic_ratio = traffic_for(f"{args.config}/{args.step}", launch_bytes, sources)
     if mfma_route:
-        kernel_label = "kv_cache_write_kernel + paged_multi_kernel" + (
-            " + paged_reduce_kernel" if NP > 1 else "") + " (events span the step)"
-        launches = {"kv_cache_write_kernel": 1, "paged_multi_kernel": 1,
+        kernel_label = "paged_multi_kernel" + (" + paged_reduce_kernel (events span both)"
+                                               if NP > 1 else "")
+        launches = {"kv_cache_write_kernel": 0, "paged_multi_kernel": 1,
                     "paged_reduce_kernel": 1 if NP > 1 else 0}
     else:
         kernel_label = "paged_decode_kernel" + (" + paged_reduce_kernel (events span both)"

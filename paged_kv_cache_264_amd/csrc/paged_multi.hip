@@ -59,8 +59,8 @@ constexpr int kRows = 16;
 // shared-prefix sampling decode 97.0 -> 98.8 us).  A single query per
 // sequence (decode of 8-63 q heads per kv head) fills at most one 16-row
 // tile, so its work-groups are few and short of loads in flight: 8 waves
-// there took a 64-sequence, 64 q / 8 kv head bf16 decode from 127.1 to
-// 118.0 us.
+// there (head_dim up to 128) took a 64-sequence, 64 q / 8 kv head bf16
+// decode from 127.1 to 118.0 us.
 constexpr int kWavesRuns = 4;
 constexpr int kWavesOneQuery = 8;
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -253,6 +253,24 @@ __global__ __launch_bounds__(kWaves * 64) void paged_multi_kernel(MultiArgs a) {
     const int span = n_parts > 0 ? partition_span(n, n_parts) : 0;
     const int t_begin = part * span;
     const int t_end = min(n, t_begin + span);
+    // The step's new token (one query per sequence, k_new given): position
+    // n - 1, row row_new of block jb_new.  If this partition holds it, lane l
+    // keeps 16 bytes of its K and V rows (chunk l % (D / 8)), which replace
+    // the cache's bytes for that row when the block is computed; so no
+    // work-group depends on another's store, and row tile 0 makes the store.
+    const bool append = a.one_query && !a.group_rows && a.k_new != nullptr && n >= 1 &&
+                        t_end == n;  // uniform: the last partition
+    const int jb_new = append ? (n - 1) / kBlockSize : -1;
+    const int row_new = (n - 1) & (kBlockSize - 1);
+    constexpr int kChunks = D / 8;                  // 16-byte chunks per row
+    constexpr int kRowsPerLoad = 64 / kChunks;      // rows per 1 KiB wave load
+    const bool new_lane = lane / kChunks == row_new % kRowsPerLoad;
+    uint4 k_nw = make_uint4(0u, 0u, 0u, 0u), v_nw = make_uint4(0u, 0u, 0u, 0u);
+    if (append) {
+        const size_t at = (((size_t)b * a.num_kv_heads + kvh) * D + (lane % kChunks) * 8) * 2;
+        k_nw = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + at);
+        v_nw = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + at);
+    }
     // the last query of the sequence sits at position n - 1 (causal), or every
     // query sees the whole context
     const int pos_of_last = a.causal ? n - 1 : 0x3fffffff;
@@ -310,13 +328,14 @@ __global__ __launch_bounds__(kWaves * 64) void paged_multi_kernel(MultiArgs a) {
 
     struct Regs {
         uint4 k[VL], v[VL];
-        int jb;
+        int jb, phys;
         bool ok;
     };
     auto load = [&](Regs& r, int i) {
         r.jb = my0 + i;
         const int phys = i < n_my ? table[my0 + i] : -1;
         r.ok = i < n_my && phys >= 0 && (int64_t)phys < a.num_blocks;
+        r.phys = phys;
         const size_t tile = (size_t)(r.ok ? phys : 0) * a.num_kv_heads + kvh;
         const int bytes = r.ok ? TILE : 0;
         const __amdgpu_buffer_rsrc_t kr = rsrc(static_cast<const char*>(a.k_cache) + tile * TILE, bytes);
@@ -328,7 +347,21 @@ __global__ __launch_bounds__(kWaves * 64) void paged_multi_kernel(MultiArgs a) {
 #pragma unroll
         for (int u = 0; u < VL; ++u) r.v[u] = ld16(vr, (u * 64 + lane) * 16);
     };
-    auto compute = [&](const Regs& r) {
+    auto compute = [&](Regs& r) {
+        if (append && r.ok && r.jb == jb_new) {  // uniform: the new token's block
+#pragma unroll
+            for (int u = 0; u < VL; ++u)
+                if (new_lane && u == row_new / kRowsPerLoad) {
+                    r.k[u] = k_nw;
+                    r.v[u] = v_nw;
+                }
+            if (rt == 0 && new_lane) {
+                const size_t at = (((size_t)r.phys * a.num_kv_heads + kvh) * kRows + row_new) * ROW +
+                                  (lane % kChunks) * 16;
+                *reinterpret_cast<uint4*>(static_cast<char*>(a.k_cache_w) + at) = k_nw;
+                *reinterpret_cast<uint4*>(static_cast<char*>(a.v_cache_w) + at) = v_nw;
+            }
+        }
         // K through this wave's LDS tile into the MFMA A operand (lane:
         // token col, channels 32 kk + 8 grp .. + 7)
 #pragma unroll
@@ -921,10 +954,12 @@ constexpr int kTiledMinRows = 64;           // rows per (sequence, kv head) that
 template <Elem T, int D>
 void launch_dw(const MultiArgs& a, int64_t grid, hipStream_t s) {
     const dim3 g((unsigned)grid);
-    if (a.one_query) {
-        const dim3 blk(kWavesOneQuery * 64);
-        if (a.exact_p) hipLaunchKernelGGL((paged_multi_kernel<T, D, true, kWavesOneQuery>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((paged_multi_kernel<T, D, false, kWavesOneQuery>), g, blk, 0, s, a);
+    // (at head_dim 256 eight waves would spill registers to memory)
+    if (D <= 128 && a.one_query) {
+        constexpr int W = D <= 128 ? kWavesOneQuery : kWavesRuns;
+        const dim3 blk(W * 64);
+        if (a.exact_p) hipLaunchKernelGGL((paged_multi_kernel<T, D, true, W>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((paged_multi_kernel<T, D, false, W>), g, blk, 0, s, a);
     } else {
         const dim3 blk(kWavesRuns * 64);
         if (a.exact_p) hipLaunchKernelGGL((paged_multi_kernel<T, D, true, kWavesRuns>), g, blk, 0, s, a);

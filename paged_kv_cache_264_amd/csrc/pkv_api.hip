@@ -441,9 +441,9 @@ pkv_status decode_phase1(void* out, float* m_part, float* l_part, float* o_part,
 // dot products per K row in vector registers and run at about half the HBM
 // rate, while the short-run multi-query kernel takes a kv head's 8..63 heads
 // as MFMA rows.  Its softmax weights enter P.V as two 16-bit parts (exact_p),
-// so the result keeps the decode's precision.  With new tokens, the cache
-// write stores them first (each sequence's slot at its context end) and the
-// attention reads them from the cache.  Measured (decode of U[512, 4096]
+// so the result keeps the decode's precision.  With new tokens, the launch
+// stores each sequence's row at its context end and computes with the given
+// row (one launch, as the decode kernel's append).  Measured (decode of U[512, 4096]
 // contexts, fp16 / bf16): 64 q / 8 kv heads x 64 sequences 145-147 ->
 // 103 us, x 256 sequences 585-591 -> 367 us, 32 q / 4 kv heads x 64
 // sequences 113-115 -> 63 us (the multi-query kernel with 16-bit weights);
@@ -454,16 +454,6 @@ pkv_status decode_mfma(void* out, float* m, float* l, float* o, const void* q, c
                        const int32_t* context_lens, int num_seqs, int num_q_heads,
                        int num_kv_heads, int head_dim, int64_t num_blocks, float scale, int P,
                        int NP, pkv_dtype dtype, hipStream_t stream) {
-    if (k_new) {
-        pkv::CacheWriteArgs w{k_new, v_new, const_cast<void*>(k_cache),
-                              const_cast<void*>(v_cache), nullptr, nullptr, nullptr,
-                              block_tables, context_lens, max_blocks_per_seq, num_seqs,
-                              num_blocks, num_kv_heads};
-        pkv_status s = hip_status(
-            pkv::launch_kv_cache_write(w, (int)dtype, (int)dtype, head_dim, stream),
-            "new-token store launch");
-        if (s != PKV_OK) return s;
-    }
     const int g = num_q_heads / num_kv_heads;
     pkv::MultiArgs a{};
     a.out = out;
@@ -489,6 +479,10 @@ pkv_status decode_mfma(void* out, float* m, float* l, float* o, const void* q, c
     a.causal = 1;
     a.one_query = 1;
     a.exact_p = 1;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_cache_w = k_new ? const_cast<void*>(k_cache) : nullptr;
+    a.v_cache_w = k_new ? const_cast<void*>(v_cache) : nullptr;
     a.scale_log2 = scale * 1.44269504088896340736f;
     if ((int64_t)num_seqs * num_kv_heads * a.row_tiles * NP > 0x7fffffff)
         return fail(PKV_ERR_SHAPE, "too many work items for one launch");
