@@ -43,6 +43,7 @@ WORKLOAD_NAMES = {
     "sampling": "llama7b-parallel-sampling-shared-prefix-decode",
     "int8-write": "llama7b-int8kv-cache-write-64-new-tokens",
     "gqa8": "gqa-64q8kv-bf16-paged-decode",
+    "gqa8-int8": "gqa-64q8kv-int8kv-paged-decode",
     "tp8": "llama7b-mha-fp16-decode-one-gpu-share-of-8-by-kv-head",
     "dp8": "llama7b-mha-fp16-decode-one-gpu-share-of-8-by-sequence",
     "cp8": "long-32k-fp16-decode-one-gpu-share-of-8-by-context",
@@ -298,19 +299,22 @@ def main():
     dec_ms = per_launch_events(step, args.steps)
     achieved = launch_bytes / (dec_avg_ms * 1e-3) / 1e9
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    # The library runs decodes of 8 to 63 q heads per kv head over a 16-bit
-    # cache (q in the cache's dtype, no window) on the matrix cores: the
-    # multi-query kernel, which also stores the new token (phase 1 alone
-    # keeps the decode kernel).
+    # The library runs decodes of 8 to 63 q heads per kv head with 16-bit q
+    # over a cache of q's dtype, INT8 or FP8 (no window) on the matrix cores:
+    # the multi-query kernel, which also stores the new token of a 16-bit
+    # cache (an 8-bit cache gets it from a cache-write launch first); phase
+    # 1 alone keeps the decode kernel.
     g = batch.Hq // batch.Hkv
     mfma_route = (args.step == "fused" and not window and 8 <= g < 64 and
-                  cfg["cache"] == cfg["dtype"] and cfg["cache"] in ("f16", "bf16"))
+                  cfg["dtype"] in ("f16", "bf16") and cfg["cache"] in (cfg["dtype"], "i8", "f8"))
+    q8_write = mfma_route and cfg["cache"] in ("i8", "f8")
     sources = MULTI_SOURCES if mfma_route else KERNEL_SOURCES
     traffic, traffic_ratio = traffic_for(f"{args.config}/{args.step}", launch_bytes, sources)
     if mfma_route:
-        kernel_label = "paged_multi_kernel" + (" + paged_reduce_kernel (events span both)"
-                                               if NP > 1 else "")
-        launches = {"kv_cache_write_kernel": 0, "paged_multi_kernel": 1,
+        kernel_label = (("kv_cache_write_kernel + " if q8_write else "") + "paged_multi_kernel" +
+                        (" + paged_reduce_kernel" if NP > 1 else "") +
+                        (" (events span the step)" if q8_write or NP > 1 else ""))
+        launches = {"kv_cache_write_kernel": 1 if q8_write else 0, "paged_multi_kernel": 1,
                     "paged_reduce_kernel": 1 if NP > 1 else 0}
     else:
         kernel_label = "paged_decode_kernel" + (" + paged_reduce_kernel (events span both)"

@@ -146,15 +146,47 @@ __device__ __forceinline__ void load_to_lds16(__amdgpu_buffer_rsrc_t r, char* ld
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voffset, 0, 0, 0);
 }
 
-// XP: the weights enter P.V as two 16-bit parts (MultiArgs::exact_p)
-template <Elem T, int D, bool XP, int kWaves>
+// 16 codes of an 8-bit cache (INT8, or e4m3 FP8) as 16 values of the 16-bit
+// MFMA type T, in order: both formats' values are exact in fp16 and in bf16
+// (integers up to 127; e4m3's 4 significant bits and exponents 2^-9..2^8)
+template <Elem T, Elem CE>
+__device__ __forceinline__ void widen16(const uint4& w, uint4& lo, uint4& hi) {
+    const uint32_t in[4] = {w.x, w.y, w.z, w.w};
+    uint32_t out[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float x0, x1, x2, x3;
+        if constexpr (CE == Elem::F8) {
+            f8x4_to_f32(in[i], x0, x1, x2, x3);
+        } else {
+            x0 = (float)(int8_t)(in[i] & 0xffu);
+            x1 = (float)(int8_t)((in[i] >> 8) & 0xffu);
+            x2 = (float)(int8_t)((in[i] >> 16) & 0xffu);
+            x3 = (float)(int8_t)(in[i] >> 24);
+        }
+        out[2 * i] = Mfma<T>::pack(x0, x1);
+        out[2 * i + 1] = Mfma<T>::pack(x2, x3);
+    }
+    lo = make_uint4(out[0], out[1], out[2], out[3]);
+    hi = make_uint4(out[4], out[5], out[6], out[7]);
+}
+
+// T: the q (and MFMA operand) type; CE: the cache's, T itself or an 8-bit
+// format with an fp32 scale per (slot, kv head), widened to T as the tiles
+// are staged.  XP: the weights enter P.V as two 16-bit parts
+// (MultiArgs::exact_p)
+template <Elem T, Elem CE, int D, bool XP, int kWaves>
 __global__ __launch_bounds__(kWaves * 64) void paged_multi_kernel(MultiArgs a) {
     constexpr int kThreads = kWaves * 64;
+    constexpr bool kQ8 = CE == Elem::I8 || CE == Elem::F8;
+    static_assert(CE == T || kQ8, "cache of the q type or an 8-bit cache");
     constexpr int KK = D / 32;          // 16x16x32 MFMAs per score tile
     constexpr int NN = D / 16;          // 16x16x16 MFMAs (output column tiles) per block
-    constexpr int VL = D / 32;          // 16-byte V loads per lane per block
-    constexpr int ROW = D * 2;          // bytes per token row
-    constexpr int TILE = kRows * ROW;   // bytes per (block, kv head) tile
+    constexpr int ROW = D * 2;          // bytes per staged (16-bit) token row
+    constexpr int CROW = kQ8 ? D : ROW; // bytes per token row in the cache
+    constexpr int CTILE = kRows * CROW; // cache bytes per (block, kv head) tile
+    constexpr int VL = CTILE / 1024;    // 16-byte loads per lane per tile
+    constexpr int CPR = CROW / 16;      // 16-byte chunks per cache row
     // LDS row stride of the staged V tile: the 16 lanes of a transpose read
     // address 4 tokens x 4 channel quads; rows 8 words apart (mod 64) put
     // them on distinct banks
@@ -328,18 +360,37 @@ __global__ __launch_bounds__(kWaves * 64) void paged_multi_kernel(MultiArgs a) {
 
     struct Regs {
         uint4 k[VL], v[VL];
+        float4 ks, vs;  // 8-bit caches: the scales of tokens 4 grp .. 4 grp + 3
         int jb, phys;
         bool ok;
     };
+    // The block ids of this wave's run, 64 at a time in one register (lane j
+    // holds id j of the current 64) and taken out with readlane.  A table
+    // read per block is a vector load, and waiting for it would also wait
+    // for the K/V loads of the blocks in flight.
+    int ids = -1;
+    auto fetch_ids = [&](int i0) {
+        const int j = i0 + lane;
+        ids = j < n_my ? table[my0 + j] : -1;
+    };
+    fetch_ids(0);
     auto load = [&](Regs& r, int i) {
         r.jb = my0 + i;
-        const int phys = i < n_my ? table[my0 + i] : -1;
+        if ((i & 63) == 0 && i > 0 && i < n_my) fetch_ids(i);  // uniform
+        const int phys = i < n_my ? __builtin_amdgcn_readlane(ids, i & 63) : -1;
         r.ok = i < n_my && phys >= 0 && (int64_t)phys < a.num_blocks;
         r.phys = phys;
         const size_t tile = (size_t)(r.ok ? phys : 0) * a.num_kv_heads + kvh;
-        const int bytes = r.ok ? TILE : 0;
-        const __amdgpu_buffer_rsrc_t kr = rsrc(static_cast<const char*>(a.k_cache) + tile * TILE, bytes);
-        const __amdgpu_buffer_rsrc_t vr = rsrc(static_cast<const char*>(a.v_cache) + tile * TILE, bytes);
+        const int bytes = r.ok ? CTILE : 0;
+        const __amdgpu_buffer_rsrc_t kr = rsrc(static_cast<const char*>(a.k_cache) + tile * CTILE, bytes);
+        const __amdgpu_buffer_rsrc_t vr = rsrc(static_cast<const char*>(a.v_cache) + tile * CTILE, bytes);
+        if constexpr (kQ8) {
+            const int sb = r.ok ? kRows * 4 : 0;
+            const uint4 ks = ld16(rsrc(a.k_scale + tile * kRows, sb), grp * 16);
+            const uint4 vs = ld16(rsrc(a.v_scale + tile * kRows, sb), grp * 16);
+            r.ks = __builtin_bit_cast(float4, ks);
+            r.vs = __builtin_bit_cast(float4, vs);
+        }
         // both tiles in token order, 1 KiB per wave load (the MFMA operand
         // order, 16 rows x 64 bytes per load, streams less well from HBM)
 #pragma unroll
@@ -348,7 +399,7 @@ __global__ __launch_bounds__(kWaves * 64) void paged_multi_kernel(MultiArgs a) {
         for (int u = 0; u < VL; ++u) r.v[u] = ld16(vr, (u * 64 + lane) * 16);
     };
     auto compute = [&](Regs& r) {
-        if (append && r.ok && r.jb == jb_new) {  // uniform: the new token's block
+        if (!kQ8 && append && r.ok && r.jb == jb_new) {  // uniform: the new token's block
 #pragma unroll
             for (int u = 0; u < VL; ++u)
                 if (new_lane && u == row_new / kRowsPerLoad) {
@@ -366,8 +417,16 @@ __global__ __launch_bounds__(kWaves * 64) void paged_multi_kernel(MultiArgs a) {
         // token col, channels 32 kk + 8 grp .. + 7)
 #pragma unroll
         for (int u = 0; u < VL; ++u) {
-            const int ch = u * 64 + lane;
-            *reinterpret_cast<uint4*>(kst + (ch / (D / 8)) * KS + (ch % (D / 8)) * 16) = r.k[u];
+            const int ch = u * 64 + lane;  // 16-byte chunk ch % CPR of token ch / CPR
+            char* dst = kst + (ch / CPR) * KS + (ch % CPR) * (kQ8 ? 32 : 16);
+            if constexpr (kQ8) {
+                uint4 lo, hi;
+                widen16<T, CE>(r.k[u], lo, hi);
+                *reinterpret_cast<uint4*>(dst) = lo;
+                *reinterpret_cast<uint4*>(dst + 16) = hi;
+            } else {
+                *reinterpret_cast<uint4*>(dst) = r.k[u];
+            }
         }
         __asm__ volatile("" ::: "memory");
         // S^T[token 4*grp + i][query col]
@@ -377,6 +436,12 @@ __global__ __launch_bounds__(kWaves * 64) void paged_multi_kernel(MultiArgs a) {
             s = Mfma<T>::qk(*reinterpret_cast<const uint4*>(kst + col * KS + (kk * 32 + grp * 8) * 2),
                             qv[kk], s);
         float sv[4] = {s[0], s[1], s[2], s[3]};
+        if constexpr (kQ8) {  // q . (code * scale) = scale * (q . code)
+            sv[0] *= r.ks.x;
+            sv[1] *= r.ks.y;
+            sv[2] *= r.ks.z;
+            sv[3] *= r.ks.w;
+        }
         // masks only where the block reaches the partition end or the causal
         // diagonal of some row of the tile (uniform test)
         const int t_hi = (r.jb + 1) * kBlockSize;
@@ -416,12 +481,28 @@ __global__ __launch_bounds__(kWaves * 64) void paged_multi_kernel(MultiArgs a) {
 #pragma unroll
         for (int u = 0; u < VL; ++u) {
             const int ch = u * 64 + lane;                  // 16-byte chunk of the tile
-            const int tok = ch / (D / 8), d0 = (ch % (D / 8)) * 8;
+            const int tok = ch / CPR;
+            char* dst = vst + tok * VS + (ch % CPR) * (kQ8 ? 32 : 16);
             uint4 v = r.v[u];
             if (tail && r.jb * kBlockSize + tok >= t_end) v = make_uint4(0u, 0u, 0u, 0u);
-            *reinterpret_cast<uint4*>(vst + tok * VS + d0 * 2) = v;
+            if constexpr (kQ8) {
+                uint4 lo, hi;
+                widen16<T, CE>(v, lo, hi);
+                *reinterpret_cast<uint4*>(dst) = lo;
+                *reinterpret_cast<uint4*>(dst + 16) = hi;
+            } else {
+                *reinterpret_cast<uint4*>(dst) = v;
+            }
         }
         __asm__ volatile("" ::: "memory");
+        if constexpr (kQ8) {
+            // the weight of a token's codes is p times its V scale; a token
+            // past the partition keeps weight 0 whatever its scale slot holds
+            const float vs4[4] = {r.vs.x, r.vs.y, r.vs.z, r.vs.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                p[i] = r.jb * kBlockSize + grp * 4 + i < t_end ? p[i] * vs4[i] : 0.f;
+        }
         const uint2 pa = make_uint2(Mfma<T>::pack(p[0], p[1]), Mfma<T>::pack(p[2], p[3]));
         // with exact_p the rest of each weight, lo = p - hi, as a second
         // 16-bit operand: |lo| <= 2^-8 |p| (bf16) or 2^-11 |p| (fp16), and
@@ -951,31 +1032,40 @@ constexpr int kTiledRW = 1;                 // row tiles per wave in the tiled k
 constexpr int kTiledWaves = 8;              // waves per work-group of the tiled kernel
 constexpr int kTiledMinRows = 64;           // rows per (sequence, kv head) that select it
 
-template <Elem T, int D>
-void launch_dw(const MultiArgs& a, int64_t grid, hipStream_t s) {
+template <Elem T, Elem CE, int D>
+hipError_t launch_dw(const MultiArgs& a, int64_t grid, hipStream_t s) {
     const dim3 g((unsigned)grid);
-    // (at head_dim 256 eight waves would spill registers to memory)
-    if (D <= 128 && a.one_query) {
-        constexpr int W = D <= 128 ? kWavesOneQuery : kWavesRuns;
-        const dim3 blk(W * 64);
-        if (a.exact_p) hipLaunchKernelGGL((paged_multi_kernel<T, D, true, W>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((paged_multi_kernel<T, D, false, W>), g, blk, 0, s, a);
-    } else {
-        const dim3 blk(kWavesRuns * 64);
-        if (a.exact_p) hipLaunchKernelGGL((paged_multi_kernel<T, D, true, kWavesRuns>), g, blk, 0, s, a);
-        else hipLaunchKernelGGL((paged_multi_kernel<T, D, false, kWavesRuns>), g, blk, 0, s, a);
+    if constexpr (CE != T) {
+        // 8-bit caches: the decode route only (one query, two-part weights)
+        if (!a.one_query || !a.exact_p) return hipErrorInvalidValue;
     }
+    // (at head_dim 256 eight waves would spill registers to memory; four
+    // measured slower at 128 for 16-bit and 8-bit caches alike)
+    constexpr int WQ = kWavesOneQuery;
+    if constexpr (D <= 128) {
+        if (a.one_query) {
+            const dim3 blk(WQ * 64);
+            if (a.exact_p) hipLaunchKernelGGL((paged_multi_kernel<T, CE, D, true, WQ>), g, blk, 0, s, a);
+            else if constexpr (CE == T)
+                hipLaunchKernelGGL((paged_multi_kernel<T, T, D, false, WQ>), g, blk, 0, s, a);
+            return hipGetLastError();
+        }
+    }
+    const dim3 blk(kWavesRuns * 64);
+    if (a.exact_p) hipLaunchKernelGGL((paged_multi_kernel<T, CE, D, true, kWavesRuns>), g, blk, 0, s, a);
+    else if constexpr (CE == T)
+        hipLaunchKernelGGL((paged_multi_kernel<T, T, D, false, kWavesRuns>), g, blk, 0, s, a);
+    return hipGetLastError();
 }
 
-template <Elem T>
+template <Elem T, Elem CE>
 hipError_t launch_d(const MultiArgs& a, int d, int64_t grid, hipStream_t s) {
     switch (d) {
-    case 64: launch_dw<T, 64>(a, grid, s); break;
-    case 128: launch_dw<T, 128>(a, grid, s); break;
-    case 256: launch_dw<T, 256>(a, grid, s); break;
+    case 64: return launch_dw<T, CE, 64>(a, grid, s);
+    case 128: return launch_dw<T, CE, 128>(a, grid, s);
+    case 256: return launch_dw<T, CE, 256>(a, grid, s);
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 template <Elem T>
@@ -999,19 +1089,28 @@ int64_t multi_row_groups(int max_rows, int head_dim) {
     return (max_rows + per - 1) / per;
 }
 
-hipError_t launch_paged_multi(const MultiArgs& a, int dtype, int head_dim, hipStream_t stream) {
+hipError_t launch_paged_multi(const MultiArgs& a, int dtype, int cache_dtype, int head_dim,
+                              hipStream_t stream) {
     const int64_t grid =
         (int64_t)a.num_seqs * a.num_kv_heads * a.row_tiles * a.num_partitions;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     const bool tiled = a.max_rows >= kTiledMinRows;
-    const Elem e = static_cast<Elem>(dtype);
-    if (e == Elem::F16)
-        return tiled ? launch_tiled<Elem::F16>(a, head_dim, grid, stream)
-                     : launch_d<Elem::F16>(a, head_dim, grid, stream);
-    if (e == Elem::BF16)
-        return tiled ? launch_tiled<Elem::BF16>(a, head_dim, grid, stream)
-                     : launch_d<Elem::BF16>(a, head_dim, grid, stream);
+    const Elem e = static_cast<Elem>(dtype), ce = static_cast<Elem>(cache_dtype);
+    if (ce == e) {
+        if (e == Elem::F16)
+            return tiled ? launch_tiled<Elem::F16>(a, head_dim, grid, stream)
+                         : launch_d<Elem::F16, Elem::F16>(a, head_dim, grid, stream);
+        if (e == Elem::BF16)
+            return tiled ? launch_tiled<Elem::BF16>(a, head_dim, grid, stream)
+                         : launch_d<Elem::BF16, Elem::BF16>(a, head_dim, grid, stream);
+        return hipErrorInvalidValue;
+    }
+    if (tiled || !(a.k_scale && a.v_scale)) return hipErrorInvalidValue;
+    if (e == Elem::F16 && ce == Elem::I8) return launch_d<Elem::F16, Elem::I8>(a, head_dim, grid, stream);
+    if (e == Elem::F16 && ce == Elem::F8) return launch_d<Elem::F16, Elem::F8>(a, head_dim, grid, stream);
+    if (e == Elem::BF16 && ce == Elem::I8) return launch_d<Elem::BF16, Elem::I8>(a, head_dim, grid, stream);
+    if (e == Elem::BF16 && ce == Elem::F8) return launch_d<Elem::BF16, Elem::F8>(a, head_dim, grid, stream);
     return hipErrorInvalidValue;
 }
 

@@ -194,11 +194,12 @@ int pow2_partition(int64_t count, int64_t max_tokens, int64_t wgs, int cap) {
     return P;
 }
 
-// Decodes of 8 to 63 q heads per kv head over a 16-bit cache run on the
-// matrix cores (the short-run multi-query kernel; see decode_mfma).
+// Decodes of 8 to 63 q heads per kv head with 16-bit q over a cache of q's
+// dtype or an 8-bit one run on the matrix cores (the short-run multi-query
+// kernel; see decode_mfma).
 bool decode_on_matrix_cores(int g, int window, pkv_dtype q_dtype, pkv_dtype cache_dtype) {
-    return window == 0 && g >= 8 && g < 64 && q_dtype == cache_dtype &&
-           (cache_dtype == PKV_F16 || cache_dtype == PKV_BF16);
+    return window == 0 && g >= 8 && g < 64 && (q_dtype == PKV_F16 || q_dtype == PKV_BF16) &&
+           (cache_dtype == q_dtype || cache_dtype == PKV_I8 || cache_dtype == PKV_F8_E4M3);
 }
 
 // Measured on MI355X: a work-group pays a chain of dependent memory round
@@ -227,7 +228,8 @@ int decode_default_partition(int num_seqs, int num_q_heads, int num_kv_heads,
     const int64_t items = (int64_t)num_seqs * num_kv_heads;
     const int64_t max_tokens = (int64_t)max_blocks_per_seq * pkv::kBlockSize;
     const int cap = items >= 1024 ? 8192 : 4096;
-    if (decode_on_matrix_cores(g, 0, cache_dtype, cache_dtype)) {
+    // (q's dtype is not an argument: an 8-bit cache is taken with 16-bit q)
+    if (decode_on_matrix_cores(g, 0, is_float(cache_dtype) ? cache_dtype : PKV_F16, cache_dtype)) {
         // 8-wave work-groups, one per 16-row tile and partition: about 256
         // of them (512 once there are 1024 tiles) at the longest context.
         // Sweeps of the step over powers of two, µs at the size this picks
@@ -436,24 +438,42 @@ pkv_status decode_phase1(void* out, float* m_part, float* l_part, float* o_part,
                       "paged decode launch");
 }
 
-// The decode of q-head groups of 8 to 63 per kv head (16-bit caches, no
-// window) on the matrix cores: the decode kernel's tiles of 8 heads keep 8
-// dot products per K row in vector registers and run at about half the HBM
-// rate, while the short-run multi-query kernel takes a kv head's 8..63 heads
-// as MFMA rows.  Its softmax weights enter P.V as two 16-bit parts (exact_p),
-// so the result keeps the decode's precision.  With new tokens, the launch
-// stores each sequence's row at its context end and computes with the given
-// row (one launch, as the decode kernel's append).  Measured (decode of U[512, 4096]
+// The decode of q-head groups of 8 to 63 per kv head (16-bit q; a cache of
+// q's dtype, INT8 or FP8; no window) on the matrix cores: the decode
+// kernel's tiles of 8 heads keep 8 dot products per K row in vector
+// registers and run at about half the HBM rate, while the short-run
+// multi-query kernel takes a kv head's 8..63 heads as MFMA rows (8-bit codes
+// widened to q's dtype as they are staged, exactly; the K scale multiplies
+// the score, the V scale the weight).  Its softmax weights enter P.V as two
+// 16-bit parts (exact_p), so the result keeps the decode's precision.  With
+// new tokens over a 16-bit cache, the launch stores each sequence's row at
+// its context end and computes with the given row (one launch, as the decode
+// kernel's append); an 8-bit cache gets its quantized rows from a cache-write
+// launch first.  Measured (decode of U[512, 4096]
 // contexts, fp16 / bf16): 64 q / 8 kv heads x 64 sequences 145-147 ->
 // 103 us, x 256 sequences 585-591 -> 367 us, 32 q / 4 kv heads x 64
 // sequences 113-115 -> 63 us (the multi-query kernel with 16-bit weights);
 // 4 q heads per kv head stay on the decode kernel (368 us either way).
 pkv_status decode_mfma(void* out, float* m, float* l, float* o, const void* q, const void* k_new,
                        const void* v_new, const void* k_cache, const void* v_cache,
+                       const float* k_scale, const float* v_scale,
                        const int32_t* block_tables, int max_blocks_per_seq,
                        const int32_t* context_lens, int num_seqs, int num_q_heads,
                        int num_kv_heads, int head_dim, int64_t num_blocks, float scale, int P,
-                       int NP, pkv_dtype dtype, hipStream_t stream) {
+                       int NP, pkv_dtype dtype, pkv_dtype cache_dtype, hipStream_t stream) {
+    const bool q8 = cache_dtype != dtype;  // INT8 / FP8 codes with scales
+    if (q8 && k_new) {
+        // the new rows are quantized into their slots first (bit-exact as
+        // pkv_kv_cache_write), then read back with the cache
+        pkv::CacheWriteArgs w{k_new, v_new, const_cast<void*>(k_cache),
+                              const_cast<void*>(v_cache), const_cast<float*>(k_scale),
+                              const_cast<float*>(v_scale), nullptr, block_tables, context_lens,
+                              max_blocks_per_seq, num_seqs, num_blocks, num_kv_heads};
+        pkv_status s = hip_status(
+            pkv::launch_kv_cache_write(w, (int)dtype, (int)cache_dtype, head_dim, stream),
+            "new-token store launch");
+        if (s != PKV_OK) return s;
+    }
     const int g = num_q_heads / num_kv_heads;
     pkv::MultiArgs a{};
     a.out = out;
@@ -479,14 +499,16 @@ pkv_status decode_mfma(void* out, float* m, float* l, float* o, const void* q, c
     a.causal = 1;
     a.one_query = 1;
     a.exact_p = 1;
-    a.k_new = k_new;
-    a.v_new = v_new;
-    a.k_cache_w = k_new ? const_cast<void*>(k_cache) : nullptr;
-    a.v_cache_w = k_new ? const_cast<void*>(v_cache) : nullptr;
+    a.k_new = q8 ? nullptr : k_new;
+    a.v_new = q8 ? nullptr : v_new;
+    a.k_cache_w = q8 || !k_new ? nullptr : const_cast<void*>(k_cache);
+    a.v_cache_w = q8 || !k_new ? nullptr : const_cast<void*>(v_cache);
+    a.k_scale = q8 ? k_scale : nullptr;
+    a.v_scale = q8 ? v_scale : nullptr;
     a.scale_log2 = scale * 1.44269504088896340736f;
     if ((int64_t)num_seqs * num_kv_heads * a.row_tiles * NP > 0x7fffffff)
         return fail(PKV_ERR_SHAPE, "too many work items for one launch");
-    return hip_status(pkv::launch_paged_multi(a, (int)dtype, head_dim, stream),
+    return hip_status(pkv::launch_paged_multi(a, (int)dtype, (int)cache_dtype, head_dim, stream),
                       "paged decode (matrix cores) launch");
 }
 
@@ -526,9 +548,10 @@ pkv_status decode_both_phases(void* out, const void* q, const void* k_new, const
     float* l = reinterpret_cast<float*>(ws + w.l_off);
     float* o = reinterpret_cast<float*>(ws + w.o_off);
     if (decode_on_matrix_cores(num_q_heads / num_kv_heads, window, q_dtype, cache_dtype))
-        s = decode_mfma(out, m, l, o, q, k_new, v_new, k_cache, v_cache, block_tables,
-                        max_blocks_per_seq, context_lens, num_seqs, num_q_heads, num_kv_heads,
-                        head_dim, num_blocks, scale, P, NP, q_dtype, stream);
+        s = decode_mfma(out, m, l, o, q, k_new, v_new, k_cache, v_cache, k_scale, v_scale,
+                        block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+                        num_kv_heads, head_dim, num_blocks, scale, P, NP, q_dtype, cache_dtype,
+                        stream);
     else
         s = decode_phase1(out, m, l, o, q, k_new, v_new, k_cache, v_cache, k_scale, v_scale,
                           block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
@@ -778,7 +801,7 @@ pkv_status pkv_paged_attn_multi(void* out, const void* q, const void* k_cache, c
     a.num_tokens = num_query_tokens;
     a.causal = 1;
     a.scale_log2 = scale * 1.44269504088896340736f;
-    pkv_status s = hip_status(pkv::launch_paged_multi(a, (int)q_dtype, head_dim, stream),
+    pkv_status s = hip_status(pkv::launch_paged_multi(a, (int)q_dtype, (int)q_dtype, head_dim, stream),
                               "paged multi-query launch");
     if (s != PKV_OK || NP == 1) return s;
     pkv::ReduceArgs r{};
@@ -892,7 +915,7 @@ pkv_status pkv_paged_attn_decode_shared_prefix(
     a.partials_only = 1;
     a.group_rows = 1;
     a.scale_log2 = scale_log2;
-    s = hip_status(pkv::launch_paged_multi(a, (int)q_dtype, head_dim, stream),
+    s = hip_status(pkv::launch_paged_multi(a, (int)q_dtype, (int)q_dtype, head_dim, stream),
                    "shared-prefix launch");
     if (s != PKV_OK) return s;
 

@@ -362,7 +362,7 @@ def test_int8_codes_bit_exact_many_rows(pkv):
 # the bench times, every sequence and every head compared
 # ---------------------------------------------------------------------------
 
-FULL = ["tiny", "llama7b", "gqa", "gqa8", "long", "int8", "fp8", "int4", "window", "tp8", "dp8",
+FULL = ["tiny", "llama7b", "gqa", "gqa8", "gqa8-int8", "long", "int8", "fp8", "int4", "window", "tp8", "dp8",
         "cp8"]
 
 

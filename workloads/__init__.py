@@ -74,6 +74,10 @@ CONFIGS = {
     # attention of a LLaMA-70B-shaped layer), B=64, ctx U[512,4096].
     "gqa8": dict(B=64, ctx=(512, 4096), Hq=64, Hkv=8, D=128, dtype="bf16", cache="bf16",
                  pool=None, seed=14, max_ctx=4096),
+    # The same layer shape over an INT8 cache (codes + fp32 scale per row,
+    # quantized on write; bf16 q).
+    "gqa8-int8": dict(B=64, ctx=(512, 4096), Hq=64, Hkv=8, D=128, dtype="bf16", cache="i8",
+                      pool=None, seed=15, max_ctx=4096),
     # One GPU's share of the LLaMA-7B batch when 8 GPUs split it: by kv head
     # (4 of the 32 heads, every sequence; the same context lengths), by
     # sequence (8 sequences of the same length distribution, all heads), and
