@@ -290,7 +290,7 @@ __global__ __launch_bounds__(kWaves * 64) void paged_multi_kernel(MultiArgs a) {
     // keeps 16 bytes of its K and V rows (chunk l % (D / 8)), which replace
     // the cache's bytes for that row when the block is computed; so no
     // work-group depends on another's store, and row tile 0 makes the store.
-    const bool append = a.one_query && !a.group_rows && a.k_new != nullptr && n >= 1 &&
+    const bool append = !kQ8 && a.one_query && !a.group_rows && a.k_new != nullptr && n >= 1 &&
                         t_end == n;  // uniform: the last partition
     const int jb_new = append ? (n - 1) / kBlockSize : -1;
     const int row_new = (n - 1) & (kBlockSize - 1);
