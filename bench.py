@@ -300,14 +300,14 @@ def main():
     achieved = launch_bytes / (dec_avg_ms * 1e-3) / 1e9
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     # The library runs decodes of 8 to 63 q heads per kv head with 16-bit q
-    # over a cache of q's dtype, INT8 or FP8 (no window) on the matrix cores:
+    # over a cache of q's dtype, INT8, FP8 or 4-bit (no window) on the matrix cores:
     # the multi-query kernel, which also stores the new token of a 16-bit
-    # cache (an 8-bit cache gets it from a cache-write launch first); phase
+    # cache (a quantized cache gets it from a cache-write launch first); phase
     # 1 alone keeps the decode kernel.
     g = batch.Hq // batch.Hkv
     mfma_route = (args.step == "fused" and not window and 8 <= g < 64 and
-                  cfg["dtype"] in ("f16", "bf16") and cfg["cache"] in (cfg["dtype"], "i8", "f8"))
-    q8_write = mfma_route and cfg["cache"] in ("i8", "f8")
+                  cfg["dtype"] in ("f16", "bf16") and cfg["cache"] in (cfg["dtype"], "i8", "f8", "u4"))
+    q8_write = mfma_route and cfg["cache"] in ("i8", "f8", "u4")
     sources = MULTI_SOURCES if mfma_route else KERNEL_SOURCES
     traffic, traffic_ratio = traffic_for(f"{args.config}/{args.step}", launch_bytes, sources)
     if mfma_route:

@@ -138,6 +138,15 @@ __device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, int off) {
     const u32x4_v v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
+// two 8-byte loads at off and off + 8 (arrays that are only 8-byte aligned)
+// (the builtin returns a generic two-element vector; its elements are taken
+// by subscript, as assigning it to an ext_vector_type would splat its first)
+__device__ __forceinline__ float4 ld8x2(__amdgpu_buffer_rsrc_t r, int off) {
+    const auto a = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    const auto b = __builtin_amdgcn_raw_buffer_load_b64(r, off + 8, 0, 0);
+    return make_float4(__builtin_bit_cast(float, (unsigned)a[0]), __builtin_bit_cast(float, (unsigned)a[1]),
+                       __builtin_bit_cast(float, (unsigned)b[0]), __builtin_bit_cast(float, (unsigned)b[1]));
+}
 // 16 bytes per lane from the buffer straight into LDS: lane l's land at
 // lds + 16 l (lds is wave-uniform); bytes outside the buffer window arrive
 // as zeros.  Counted by vmcnt, like any vector memory load.
@@ -171,22 +180,45 @@ __device__ __forceinline__ void widen16(const uint4& w, uint4& lo, uint4& hi) {
     hi = make_uint4(out[4], out[5], out[6], out[7]);
 }
 
-// T: the q (and MFMA operand) type; CE: the cache's, T itself or an 8-bit
-// format with an fp32 scale per (slot, kv head), widened to T as the tiles
-// are staged.  XP: the weights enter P.V as two 16-bit parts
+// 32 codes of a 4-bit cache (two per byte, element 2k in the low nibble of
+// byte k) as 32 values code * 2^-9 of the 16-bit type T, in order: a byte c
+// <= 15 read as an e4m3 code is exactly c * 2^-9 (1..7 the subnormals, 8..15
+// the normals of exponent -6), so one packed fp8 convert widens two codes
+template <Elem T>
+__device__ __forceinline__ void widen32_u4(const uint4& w, uint4 out[4]) {
+    const uint32_t in[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float l0, l1, l2, l3, h0, h1, h2, h3;
+        f8x4_to_f32(in[i] & 0x0F0F0F0Fu, l0, l1, l2, l3);         // elements 8i, 8i+2, ..
+        f8x4_to_f32((in[i] >> 4) & 0x0F0F0F0Fu, h0, h1, h2, h3);  // elements 8i+1, 8i+3, ..
+        out[i] = make_uint4(Mfma<T>::pack(l0, h0), Mfma<T>::pack(l1, h1), Mfma<T>::pack(l2, h2),
+                            Mfma<T>::pack(l3, h3));
+    }
+}
+constexpr float kU4Unscale = 512.0f;        // undoes widen32_u4's 2^-9
+constexpr float kInv15 = 1.0f / 15.0f;      // 4-bit step = range / 15
+
+// T: the q (and MFMA operand) type; CE: the cache's, T itself, an 8-bit
+// format with an fp32 scale per (slot, kv head), or 4-bit codes with an
+// fp32 (x_min, range) per (slot, kv head), widened to T as the tiles are
+// staged.  XP: the weights enter P.V as two 16-bit parts
 // (MultiArgs::exact_p)
 template <Elem T, Elem CE, int D, bool XP, int kWaves>
 __global__ __launch_bounds__(kWaves * 64) void paged_multi_kernel(MultiArgs a) {
     constexpr int kThreads = kWaves * 64;
     constexpr bool kQ8 = CE == Elem::I8 || CE == Elem::F8;
-    static_assert(CE == T || kQ8, "cache of the q type or an 8-bit cache");
+    constexpr bool kU4 = CE == Elem::U4;
+    static_assert(CE == T || kQ8 || kU4, "cache of the q type, 8-bit or 4-bit");
     constexpr int KK = D / 32;          // 16x16x32 MFMAs per score tile
     constexpr int NN = D / 16;          // 16x16x16 MFMAs (output column tiles) per block
     constexpr int ROW = D * 2;          // bytes per staged (16-bit) token row
-    constexpr int CROW = kQ8 ? D : ROW; // bytes per token row in the cache
+    constexpr int CROW = kU4 ? D / 2 : kQ8 ? D : ROW;  // bytes per token row in the cache
     constexpr int CTILE = kRows * CROW; // cache bytes per (block, kv head) tile
     constexpr int VL = CTILE / 1024;    // 16-byte loads per lane per tile
+    static_assert(VL >= 1, "a tile is at least one 1 KiB wave load");
     constexpr int CPR = CROW / 16;      // 16-byte chunks per cache row
+    constexpr int WID = kU4 ? 64 : kQ8 ? 32 : 16;  // staged bytes per 16-byte cache chunk
     // LDS row stride of the staged V tile: the 16 lanes of a transpose read
     // address 4 tokens x 4 channel quads; rows 8 words apart (mod 64) put
     // them on distinct banks
@@ -290,7 +322,7 @@ __global__ __launch_bounds__(kWaves * 64) void paged_multi_kernel(MultiArgs a) {
     // keeps 16 bytes of its K and V rows (chunk l % (D / 8)), which replace
     // the cache's bytes for that row when the block is computed; so no
     // work-group depends on another's store, and row tile 0 makes the store.
-    const bool append = !kQ8 && a.one_query && !a.group_rows && a.k_new != nullptr && n >= 1 &&
+    const bool append = CE == T && a.one_query && !a.group_rows && a.k_new != nullptr && n >= 1 &&
                         t_end == n;  // uniform: the last partition
     const int jb_new = append ? (n - 1) / kBlockSize : -1;
     const int row_new = (n - 1) & (kBlockSize - 1);
@@ -333,6 +365,23 @@ __global__ __launch_bounds__(kWaves * 64) void paged_multi_kernel(MultiArgs a) {
             qv[kk] = make_uint4(qv[kk].x ^ sg, qv[kk].y ^ sg, qv[kk].z ^ sg, qv[kk].w ^ sg);
         }
     }
+    // 4-bit caches: q . (x_min + step c) = step (q . c) + x_min sum(q), and
+    // the weights' x_min part, sum over tokens of p x_min, kept per lane
+    float qsum = 0.f, pxm = 0.f;
+    if constexpr (kU4) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            const uint32_t w4[4] = {qv[kk].x, qv[kk].y, qv[kk].z, qv[kk].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float x, y;
+                Mfma<T>::unpack(w4[j], x, y);
+                qsum += x + y;
+            }
+        }
+        qsum += __shfl_xor(qsum, 16);
+        qsum += __shfl_xor(qsum, 32);
+    }
 
     float m = kNegBig, cm = c * kNegBig, l = 0.f;  // max of raw scores, c times it, sum
     f32x4_t o[NN];
@@ -360,7 +409,10 @@ __global__ __launch_bounds__(kWaves * 64) void paged_multi_kernel(MultiArgs a) {
 
     struct Regs {
         uint4 k[VL], v[VL];
-        float4 ks, vs;  // 8-bit caches: the scales of tokens 4 grp .. 4 grp + 3
+        // 8-bit caches: the scales of tokens 4 grp .. 4 grp + 3; 4-bit: their
+        // (x_min, range) pairs, tokens 4 grp, 4 grp + 1 in ks / vs, the
+        // other two in ks2 / vs2
+        float4 ks, vs, ks2, vs2;
         int jb, phys;
         bool ok;
     };
@@ -391,6 +443,16 @@ __global__ __launch_bounds__(kWaves * 64) void paged_multi_kernel(MultiArgs a) {
             r.ks = __builtin_bit_cast(float4, ks);
             r.vs = __builtin_bit_cast(float4, vs);
         }
+        if constexpr (kU4) {
+            const int sb = r.ok ? kRows * 8 : 0;
+            const __amdgpu_buffer_rsrc_t kq = rsrc(a.k_scale + tile * kRows * 2, sb);
+            const __amdgpu_buffer_rsrc_t vq = rsrc(a.v_scale + tile * kRows * 2, sb);
+            // (the pairs are 8-byte aligned: 8-byte loads)
+            r.ks = ld8x2(kq, grp * 32);
+            r.ks2 = ld8x2(kq, grp * 32 + 16);
+            r.vs = ld8x2(vq, grp * 32);
+            r.vs2 = ld8x2(vq, grp * 32 + 16);
+        }
         // both tiles in token order, 1 KiB per wave load (the MFMA operand
         // order, 16 rows x 64 bytes per load, streams less well from HBM)
 #pragma unroll
@@ -418,8 +480,13 @@ __global__ __launch_bounds__(kWaves * 64) void paged_multi_kernel(MultiArgs a) {
 #pragma unroll
         for (int u = 0; u < VL; ++u) {
             const int ch = u * 64 + lane;  // 16-byte chunk ch % CPR of token ch / CPR
-            char* dst = kst + (ch / CPR) * KS + (ch % CPR) * (kQ8 ? 32 : 16);
-            if constexpr (kQ8) {
+            char* dst = kst + (ch / CPR) * KS + (ch % CPR) * WID;
+            if constexpr (kU4) {
+                uint4 w4[4];
+                widen32_u4<T>(r.k[u], w4);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(dst + 16 * j) = w4[j];
+            } else if constexpr (kQ8) {
                 uint4 lo, hi;
                 widen16<T, CE>(r.k[u], lo, hi);
                 *reinterpret_cast<uint4*>(dst) = lo;
@@ -441,6 +508,13 @@ __global__ __launch_bounds__(kWaves * 64) void paged_multi_kernel(MultiArgs a) {
             sv[1] *= r.ks.y;
             sv[2] *= r.ks.z;
             sv[3] *= r.ks.w;
+        }
+        if constexpr (kU4) {  // step (q . code) + x_min sum(q), step = range / 15
+            const float xm[4] = {r.ks.x, r.ks.z, r.ks2.x, r.ks2.z};
+            const float rg[4] = {r.ks.y, r.ks.w, r.ks2.y, r.ks2.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                sv[i] = fmaf(sv[i], rg[i] * kInv15 * kU4Unscale, xm[i] * qsum);
         }
         // masks only where the block reaches the partition end or the causal
         // diagonal of some row of the tile (uniform test)
@@ -482,10 +556,15 @@ __global__ __launch_bounds__(kWaves * 64) void paged_multi_kernel(MultiArgs a) {
         for (int u = 0; u < VL; ++u) {
             const int ch = u * 64 + lane;                  // 16-byte chunk of the tile
             const int tok = ch / CPR;
-            char* dst = vst + tok * VS + (ch % CPR) * (kQ8 ? 32 : 16);
+            char* dst = vst + tok * VS + (ch % CPR) * WID;
             uint4 v = r.v[u];
             if (tail && r.jb * kBlockSize + tok >= t_end) v = make_uint4(0u, 0u, 0u, 0u);
-            if constexpr (kQ8) {
+            if constexpr (kU4) {
+                uint4 w4[4];
+                widen32_u4<T>(v, w4);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(dst + 16 * j) = w4[j];
+            } else if constexpr (kQ8) {
                 uint4 lo, hi;
                 widen16<T, CE>(v, lo, hi);
                 *reinterpret_cast<uint4*>(dst) = lo;
@@ -502,6 +581,21 @@ __global__ __launch_bounds__(kWaves * 64) void paged_multi_kernel(MultiArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 p[i] = r.jb * kBlockSize + grp * 4 + i < t_end ? p[i] * vs4[i] : 0.f;
+        }
+        if constexpr (kU4) {
+            // the codes' weight is p step (times 2^9 for the widening), and
+            // p x_min adds to every channel; tokens past the partition add
+            // nothing whatever their pair holds
+            const float xm[4] = {r.vs.x, r.vs.z, r.vs2.x, r.vs2.z};
+            const float rg[4] = {r.vs.y, r.vs.w, r.vs2.y, r.vs2.w};
+            float add = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool in = r.jb * kBlockSize + grp * 4 + i < t_end;
+                add = in ? fmaf(p[i], xm[i], add) : add;
+                p[i] = in ? p[i] * (rg[i] * kInv15 * kU4Unscale) : 0.f;
+            }
+            pxm = fmaf(pxm, alpha, add);
         }
         const uint2 pa = make_uint2(Mfma<T>::pack(p[0], p[1]), Mfma<T>::pack(p[2], p[3]));
         // with exact_p the rest of each weight, lo = p - hi, as a second
@@ -545,6 +639,12 @@ __global__ __launch_bounds__(kWaves * 64) void paged_multi_kernel(MultiArgs a) {
     // ---- merge the waves (wave 0 keeps its tile in registers) --------------
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
+    if constexpr (kU4) {  // the x_min part of every channel of the lane's query
+        pxm += __shfl_xor(pxm, 16);
+        pxm += __shfl_xor(pxm, 32);
+#pragma unroll
+        for (int nn = 0; nn < NN; ++nn) o[nn] += pxm;
+    }
     __syncthreads();  // every wave is done with its V stage
     float* s_o = reinterpret_cast<float*>(s_buf);  // [wave - 1][query][D]
     if (grp == 0) {
@@ -1036,9 +1136,13 @@ template <Elem T, Elem CE, int D>
 hipError_t launch_dw(const MultiArgs& a, int64_t grid, hipStream_t s) {
     const dim3 g((unsigned)grid);
     if constexpr (CE != T) {
-        // 8-bit caches: the decode route only (one query, two-part weights)
+        // 8- and 4-bit caches: the decode route only (one query, two-part
+        // weights); a 4-bit tile at head_dim 64 is half a wave load
         if (!a.one_query || !a.exact_p) return hipErrorInvalidValue;
     }
+    if constexpr (CE == Elem::U4 && D < 128) {
+        return hipErrorInvalidValue;
+    } else {
     // (at head_dim 256 eight waves would spill registers to memory; four
     // measured slower at 128 for 16-bit and 8-bit caches alike)
     constexpr int WQ = kWavesOneQuery;
@@ -1056,6 +1160,7 @@ hipError_t launch_dw(const MultiArgs& a, int64_t grid, hipStream_t s) {
     else if constexpr (CE == T)
         hipLaunchKernelGGL((paged_multi_kernel<T, T, D, false, kWavesRuns>), g, blk, 0, s, a);
     return hipGetLastError();
+    }
 }
 
 template <Elem T, Elem CE>
@@ -1111,6 +1216,8 @@ hipError_t launch_paged_multi(const MultiArgs& a, int dtype, int cache_dtype, in
     if (e == Elem::F16 && ce == Elem::F8) return launch_d<Elem::F16, Elem::F8>(a, head_dim, grid, stream);
     if (e == Elem::BF16 && ce == Elem::I8) return launch_d<Elem::BF16, Elem::I8>(a, head_dim, grid, stream);
     if (e == Elem::BF16 && ce == Elem::F8) return launch_d<Elem::BF16, Elem::F8>(a, head_dim, grid, stream);
+    if (e == Elem::F16 && ce == Elem::U4) return launch_d<Elem::F16, Elem::U4>(a, head_dim, grid, stream);
+    if (e == Elem::BF16 && ce == Elem::U4) return launch_d<Elem::BF16, Elem::U4>(a, head_dim, grid, stream);
     return hipErrorInvalidValue;
 }
 

@@ -195,11 +195,12 @@ int pow2_partition(int64_t count, int64_t max_tokens, int64_t wgs, int cap) {
 }
 
 // Decodes of 8 to 63 q heads per kv head with 16-bit q over a cache of q's
-// dtype or an 8-bit one run on the matrix cores (the short-run multi-query
-// kernel; see decode_mfma).
+// dtype or a quantized one (INT8, FP8; 4-bit from head_dim 128) run on the
+// matrix cores (the short-run multi-query kernel; see decode_mfma).
 bool decode_on_matrix_cores(int g, int window, pkv_dtype q_dtype, pkv_dtype cache_dtype) {
     return window == 0 && g >= 8 && g < 64 && (q_dtype == PKV_F16 || q_dtype == PKV_BF16) &&
-           (cache_dtype == q_dtype || cache_dtype == PKV_I8 || cache_dtype == PKV_F8_E4M3);
+           (cache_dtype == q_dtype || cache_dtype == PKV_I8 || cache_dtype == PKV_F8_E4M3 ||
+            cache_dtype == PKV_U4);
 }
 
 // Measured on MI355X: a work-group pays a chain of dependent memory round
@@ -461,8 +462,8 @@ pkv_status decode_mfma(void* out, float* m, float* l, float* o, const void* q, c
                        const int32_t* context_lens, int num_seqs, int num_q_heads,
                        int num_kv_heads, int head_dim, int64_t num_blocks, float scale, int P,
                        int NP, pkv_dtype dtype, pkv_dtype cache_dtype, hipStream_t stream) {
-    const bool q8 = cache_dtype != dtype;  // INT8 / FP8 codes with scales
-    if (q8 && k_new) {
+    const bool quant = cache_dtype != dtype;  // INT8 / FP8 / 4-bit codes with scales
+    if (quant && k_new) {
         // the new rows are quantized into their slots first (bit-exact as
         // pkv_kv_cache_write), then read back with the cache
         pkv::CacheWriteArgs w{k_new, v_new, const_cast<void*>(k_cache),
@@ -499,12 +500,12 @@ pkv_status decode_mfma(void* out, float* m, float* l, float* o, const void* q, c
     a.causal = 1;
     a.one_query = 1;
     a.exact_p = 1;
-    a.k_new = q8 ? nullptr : k_new;
-    a.v_new = q8 ? nullptr : v_new;
-    a.k_cache_w = q8 || !k_new ? nullptr : const_cast<void*>(k_cache);
-    a.v_cache_w = q8 || !k_new ? nullptr : const_cast<void*>(v_cache);
-    a.k_scale = q8 ? k_scale : nullptr;
-    a.v_scale = q8 ? v_scale : nullptr;
+    a.k_new = quant ? nullptr : k_new;
+    a.v_new = quant ? nullptr : v_new;
+    a.k_cache_w = quant || !k_new ? nullptr : const_cast<void*>(k_cache);
+    a.v_cache_w = quant || !k_new ? nullptr : const_cast<void*>(v_cache);
+    a.k_scale = quant ? k_scale : nullptr;
+    a.v_scale = quant ? v_scale : nullptr;
     a.scale_log2 = scale * 1.44269504088896340736f;
     if ((int64_t)num_seqs * num_kv_heads * a.row_tiles * NP > 0x7fffffff)
         return fail(PKV_ERR_SHAPE, "too many work items for one launch");

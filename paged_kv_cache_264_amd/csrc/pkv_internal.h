@@ -140,8 +140,10 @@ struct MultiArgs {
     const void* v_new;
     void* k_cache_w;
     void* v_cache_w;
-    // 8-bit caches (INT8, FP8; one query per sequence): the fp32 scale of
-    // every (slot, kv head), [num_blocks][Hkv][16]; null otherwise
+    // quantized caches (one query per sequence): INT8 / FP8, the fp32 scale
+    // of every (slot, kv head), [num_blocks][Hkv][16]; 4-bit, the fp32
+    // (x_min, range) pair of every (slot, kv head), [num_blocks][Hkv][16][2];
+    // null otherwise
     const float* k_scale;
     const float* v_scale;
     float scale_log2;
@@ -153,7 +155,7 @@ int64_t multi_row_groups(int max_rows, int head_dim);
 
 // Multi-query causal attention (fp16 / bf16 caches).  Returns
 // hipErrorInvalidValue for a combination with no kernel.
-// dtype: q's (the MFMA operand type); cache_dtype: the same, or an 8-bit
+// dtype: q's (the MFMA operand type); cache_dtype: the same, or a quantized
 // format with scales (the short-run kernel with one query per sequence only)
 hipError_t launch_paged_multi(const MultiArgs& a, int dtype, int cache_dtype, int head_dim,
                               hipStream_t stream);
