@@ -139,8 +139,8 @@ __device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, int off) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 // two 8-byte loads at off and off + 8 (arrays that are only 8-byte aligned)
-// (the builtin returns a generic two-element vector; its elements are taken
-// by subscript, as assigning it to an ext_vector_type would splat its first)
+// (the builtin returns a generic two-element vector, taken apart by
+// subscript: assigned to an ext_vector_type, only its first element survived)
 __device__ __forceinline__ float4 ld8x2(__amdgpu_buffer_rsrc_t r, int off) {
     const auto a = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
     const auto b = __builtin_amdgcn_raw_buffer_load_b64(r, off + 8, 0, 0);
