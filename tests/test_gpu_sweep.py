@@ -8,7 +8,9 @@ dtype pair, partition sizes from 16 tokens to the library default, and the
 three decode entry points (plain, fused append, sliding window with a random
 window).  Every case compares every output element with the oracle at the
 dtype bound, and checks that nothing is written around the output buffer or
-the caller's workspace (sentinel guard bands).
+the caller's workspace (sentinel guard bands).  A second sweep of 64 cases
+(default_rng([2027, i])) takes 8 to 63 q heads per kv head with 16-bit q,
+the decodes that run on the matrix cores, over every cache format.
 """
 from __future__ import annotations
 
@@ -103,6 +105,53 @@ def test_random_shape_sweep(pkv, chunk):
         assert err <= tol, (i, c, err)
         worst = max(worst, err / tol)
     print(f"[sweep chunk {chunk}] worst err/tol {worst:.3f}", flush=True)
+
+
+# The matrix-core decode (8 to 63 q heads per kv head, 16-bit q): groups
+# that fill one to four 16-row tiles, every cache format it takes, the plain
+# and fused calls, and (off the route) sliding windows.
+ROUTE_PAIRS = [("f16", "f16"), ("bf16", "bf16"), ("f16", "i8"), ("bf16", "i8"), ("f16", "f8"),
+               ("bf16", "f8"), ("f16", "u4"), ("bf16", "u4")]
+N_ROUTE, N_ROUTE_CHUNKS = 64, 4
+
+
+def draw_route_case(i: int) -> dict:
+    g = np.random.default_rng([2027, i])
+    dtype, cache = ROUTE_PAIRS[int(g.integers(len(ROUTE_PAIRS)))]
+    D = int(g.choice([128, 256])) if cache == "u4" else int(g.choice([64, 128, 256]))
+    group = int(g.choice([8, 12, 16, 24, 32, 48, 63]))
+    Hkv = int(g.integers(1, 3))
+    B = int(g.integers(1, 7))
+    lens = g.integers(0, 601, size=B)
+    lens[g.random(B) < 0.1] = 0
+    mode = str(g.choice(["decode", "append", "append", "sliding"]))
+    window = int(g.choice([1, 17, 100, 1000])) if mode == "sliding" else 0
+    P = int(g.choice([0, 0, 16, 64, 256]))
+    return dict(dtype=dtype, cache=cache, D=D, Hq=Hkv * group, Hkv=Hkv, lens=[int(x) for x in lens],
+                mode=mode, window=window, P=P, seed=5000 + i)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("chunk", range(N_ROUTE_CHUNKS))
+def test_matrix_core_decode_sweep(pkv, chunk):
+    per = N_ROUTE // N_ROUTE_CHUNKS
+    worst = 0.0
+    for i in range(chunk * per, (chunk + 1) * per):
+        c = draw_route_case(i)
+        err, tol = run_case(pkv, c)
+        print(f"[route {i}] {c['dtype']}/{c['cache']} D={c['D']} Hq={c['Hq']} Hkv={c['Hkv']} "
+              f"lens={c['lens']} {c['mode']} W={c['window']} P={c['P']} err={err:.2e} "
+              f"tol={tol:.1e}", flush=True)
+        assert err <= tol, (i, c, err)
+        worst = max(worst, err / tol)
+    print(f"[route chunk {chunk}] worst err/tol {worst:.3f}", flush=True)
+
+
+def test_route_sweep_covers_the_space():
+    cases = [draw_route_case(i) for i in range(N_ROUTE)]
+    assert {(c["dtype"], c["cache"]) for c in cases} == set(ROUTE_PAIRS)
+    assert {(c["Hq"] // c["Hkv"] + 15) // 16 for c in cases} == {1, 2, 3, 4}
+    assert {c["mode"] for c in cases} == {"decode", "append", "sliding"}
 
 
 def test_sweep_covers_the_space():
