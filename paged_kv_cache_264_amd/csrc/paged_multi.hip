@@ -38,6 +38,7 @@
 //     write (m, l, o) partials for the merge kernel.
 #include "pkv_device.h"
 #include "pkv_internal.h"
+#include "pkv_quant.h"
 
 namespace pkv {
 namespace {
@@ -318,22 +319,50 @@ __global__ __launch_bounds__(kWaves * 64) void paged_multi_kernel(MultiArgs a) {
     const int t_begin = part * span;
     const int t_end = min(n, t_begin + span);
     // The step's new token (one query per sequence, k_new given): position
-    // n - 1, row row_new of block jb_new.  If this partition holds it, lane l
-    // keeps 16 bytes of its K and V rows (chunk l % (D / 8)), which replace
-    // the cache's bytes for that row when the block is computed; so no
-    // work-group depends on another's store, and row tile 0 makes the store.
-    const bool append = CE == T && a.one_query && !a.group_rows && a.k_new != nullptr && n >= 1 &&
+    // n - 1, row row_new of block jb_new.  If this partition holds it, every
+    // lane keeps the 16 cache bytes of that row that it would load (chunk
+    // l % CPR): the row itself for a 16-bit cache; for a quantized cache its
+    // codes, from the cache write's own quantizer over the row's D / 8 lanes,
+    // with the row's scale or (x_min, range).  They replace what the cache
+    // holds when the block is computed, so no work-group depends on another's
+    // store; row tile 0 makes the store.
+    const bool append = a.one_query && !a.group_rows && a.k_new != nullptr && n >= 1 &&
                         t_end == n;  // uniform: the last partition
     const int jb_new = append ? (n - 1) / kBlockSize : -1;
     const int row_new = (n - 1) & (kBlockSize - 1);
-    constexpr int kChunks = D / 8;                  // 16-byte chunks per row
-    constexpr int kRowsPerLoad = 64 / kChunks;      // rows per 1 KiB wave load
-    const bool new_lane = lane / kChunks == row_new % kRowsPerLoad;
+    constexpr int kRowsPerLoad = 64 / CPR;          // rows per 1 KiB wave load
+    constexpr int LPR = D / 8;                      // the quantizer's lanes per row
+    const bool new_lane = lane / CPR == row_new % kRowsPerLoad;
     uint4 k_nw = make_uint4(0u, 0u, 0u, 0u), v_nw = make_uint4(0u, 0u, 0u, 0u);
+    uint2 kq_st = make_uint2(0u, 0u), vq_st = make_uint2(0u, 0u);  // lane < LPR: its codes
+    float k_s0 = 0.f, k_s1 = 0.f, v_s0 = 0.f, v_s1 = 0.f;  // the scale, or (x_min, range)
     if (append) {
-        const size_t at = (((size_t)b * a.num_kv_heads + kvh) * D + (lane % kChunks) * 8) * 2;
-        k_nw = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + at);
-        v_nw = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + at);
+        const size_t row = (size_t)b * a.num_kv_heads + kvh;
+        if constexpr (CE == T) {
+            const size_t at = (row * D + (lane % CPR) * 8) * 2;
+            k_nw = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + at);
+            v_nw = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + at);
+        } else {
+            // lane l quantizes elements 8 (l % LPR) .. + 7, as the cache write does
+            const size_t at = (row * D + (lane % LPR) * 8) * 2;
+            const uint4 kr = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + at);
+            const uint4 vr = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + at);
+            const uint32_t kw[4] = {kr.x, kr.y, kr.z, kr.w}, vw[4] = {vr.x, vr.y, vr.z, vr.w};
+            float kx[8], vx[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                Mfma<T>::unpack(kw[i], kx[2 * i], kx[2 * i + 1]);
+                Mfma<T>::unpack(vw[i], vx[2 * i], vx[2 * i + 1]);
+            }
+            // (the codes are gathered into chunks when the block is computed)
+            if constexpr (kU4) {
+                kq_st = make_uint2(quantize8_u4<LPR>(kx, k_s0, k_s1), 0u);
+                vq_st = make_uint2(quantize8_u4<LPR>(vx, v_s0, v_s1), 0u);
+            } else {
+                kq_st = quantize8<CE, LPR>(kx, k_s0);
+                vq_st = quantize8<CE, LPR>(vx, v_s0);
+            }
+        }
     }
     // the last query of the sequence sits at position n - 1 (causal), or every
     // query sees the whole context
@@ -461,18 +490,91 @@ __global__ __launch_bounds__(kWaves * 64) void paged_multi_kernel(MultiArgs a) {
         for (int u = 0; u < VL; ++u) r.v[u] = ld16(vr, (u * 64 + lane) * 16);
     };
     auto compute = [&](Regs& r) {
-        if (!kQ8 && append && r.ok && r.jb == jb_new) {  // uniform: the new token's block
+        if (append && r.ok && r.jb == jb_new) {  // uniform: the new token's block
+            if constexpr (kU4) {
+                // chunk c of the row (32 codes): quantizer lanes 4 c .. 4 c + 3
+                const int c0 = (lane % CPR) * 4;
+                k_nw = make_uint4(__shfl(kq_st.x, c0), __shfl(kq_st.x, c0 + 1),
+                                  __shfl(kq_st.x, c0 + 2), __shfl(kq_st.x, c0 + 3));
+                v_nw = make_uint4(__shfl(vq_st.x, c0), __shfl(vq_st.x, c0 + 1),
+                                  __shfl(vq_st.x, c0 + 2), __shfl(vq_st.x, c0 + 3));
+            } else if constexpr (kQ8) {
+                // chunk c of the row (16 codes): quantizer lanes 2 c and 2 c + 1
+                const int c0 = (lane % CPR) * 2;
+                k_nw = make_uint4(__shfl(kq_st.x, c0), __shfl(kq_st.y, c0),
+                                  __shfl(kq_st.x, c0 + 1), __shfl(kq_st.y, c0 + 1));
+                v_nw = make_uint4(__shfl(vq_st.x, c0), __shfl(vq_st.y, c0),
+                                  __shfl(vq_st.x, c0 + 1), __shfl(vq_st.y, c0 + 1));
+            }
 #pragma unroll
             for (int u = 0; u < VL; ++u)
                 if (new_lane && u == row_new / kRowsPerLoad) {
                     r.k[u] = k_nw;
                     r.v[u] = v_nw;
                 }
-            if (rt == 0 && new_lane) {
-                const size_t at = (((size_t)r.phys * a.num_kv_heads + kvh) * kRows + row_new) * ROW +
-                                  (lane % kChunks) * 16;
-                *reinterpret_cast<uint4*>(static_cast<char*>(a.k_cache_w) + at) = k_nw;
-                *reinterpret_cast<uint4*>(static_cast<char*>(a.v_cache_w) + at) = v_nw;
+            // the row's scale (or pair): token row_new is entry row_new % 4 of
+            // lane group row_new / 4
+            const int e = row_new & 3;
+            if (kQ8 && grp == row_new / 4) {
+                r.ks.x = e == 0 ? k_s0 : r.ks.x;
+                r.ks.y = e == 1 ? k_s0 : r.ks.y;
+                r.ks.z = e == 2 ? k_s0 : r.ks.z;
+                r.ks.w = e == 3 ? k_s0 : r.ks.w;
+                r.vs.x = e == 0 ? v_s0 : r.vs.x;
+                r.vs.y = e == 1 ? v_s0 : r.vs.y;
+                r.vs.z = e == 2 ? v_s0 : r.vs.z;
+                r.vs.w = e == 3 ? v_s0 : r.vs.w;
+            }
+            if (kU4 && grp == row_new / 4) {
+                // entries 0, 1 in ks / vs, 2, 3 in ks2 / vs2; (x_min, range)
+                // of an even entry in x, y, of an odd one in z, w (selects
+                // only: a reference into the register set would put it in
+                // memory)
+                const bool e0 = e == 0, e1 = e == 1, e2 = e == 2, e3 = e == 3;
+                r.ks.x = e0 ? k_s0 : r.ks.x;
+                r.ks.y = e0 ? k_s1 : r.ks.y;
+                r.ks.z = e1 ? k_s0 : r.ks.z;
+                r.ks.w = e1 ? k_s1 : r.ks.w;
+                r.ks2.x = e2 ? k_s0 : r.ks2.x;
+                r.ks2.y = e2 ? k_s1 : r.ks2.y;
+                r.ks2.z = e3 ? k_s0 : r.ks2.z;
+                r.ks2.w = e3 ? k_s1 : r.ks2.w;
+                r.vs.x = e0 ? v_s0 : r.vs.x;
+                r.vs.y = e0 ? v_s1 : r.vs.y;
+                r.vs.z = e1 ? v_s0 : r.vs.z;
+                r.vs.w = e1 ? v_s1 : r.vs.w;
+                r.vs2.x = e2 ? v_s0 : r.vs2.x;
+                r.vs2.y = e2 ? v_s1 : r.vs2.y;
+                r.vs2.z = e3 ? v_s0 : r.vs2.z;
+                r.vs2.w = e3 ? v_s1 : r.vs2.w;
+            }
+            if (rt == 0) {
+                const size_t srow = ((size_t)r.phys * a.num_kv_heads + kvh) * kRows + row_new;
+                char* kc = static_cast<char*>(a.k_cache_w);
+                char* vc = static_cast<char*>(a.v_cache_w);
+                if constexpr (CE == T) {
+                    if (new_lane) {
+                        const size_t at = srow * ROW + (lane % CPR) * 16;
+                        *reinterpret_cast<uint4*>(kc + at) = k_nw;
+                        *reinterpret_cast<uint4*>(vc + at) = v_nw;
+                    }
+                } else if (lane < LPR) {
+                    if constexpr (kU4) {
+                        *reinterpret_cast<uint32_t*>(kc + srow * (D / 2) + lane * 4) = kq_st.x;
+                        *reinterpret_cast<uint32_t*>(vc + srow * (D / 2) + lane * 4) = vq_st.x;
+                        if (lane == 0) {
+                            *reinterpret_cast<float2*>(a.k_scale_w + 2 * srow) = make_float2(k_s0, k_s1);
+                            *reinterpret_cast<float2*>(a.v_scale_w + 2 * srow) = make_float2(v_s0, v_s1);
+                        }
+                    } else {
+                        *reinterpret_cast<uint2*>(kc + srow * D + lane * 8) = kq_st;
+                        *reinterpret_cast<uint2*>(vc + srow * D + lane * 8) = vq_st;
+                        if (lane == 0) {
+                            a.k_scale_w[srow] = k_s0;
+                            a.v_scale_w[srow] = v_s0;
+                        }
+                    }
+                }
             }
         }
         // K through this wave's LDS tile into the MFMA A operand (lane:

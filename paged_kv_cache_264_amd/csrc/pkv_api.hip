@@ -447,10 +447,10 @@ pkv_status decode_phase1(void* out, float* m_part, float* l_part, float* o_part,
 // widened to q's dtype as they are staged, exactly; the K scale multiplies
 // the score, the V scale the weight).  Its softmax weights enter P.V as two
 // 16-bit parts (exact_p), so the result keeps the decode's precision.  With
-// new tokens over a 16-bit cache, the launch stores each sequence's row at
-// its context end and computes with the given row (one launch, as the decode
-// kernel's append); an 8-bit cache gets its quantized rows from a cache-write
-// launch first.  Measured (decode of U[512, 4096]
+// new tokens, the launch stores each sequence's row at its context end and
+// computes with the given row (one launch, as the decode kernel's append; for
+// a quantized cache the row is quantized by the cache write's own
+// quantizer, so the stored bytes are the same).  Measured (decode of U[512, 4096]
 // contexts, fp16 / bf16): 64 q / 8 kv heads x 64 sequences 145-147 ->
 // 103 us, x 256 sequences 585-591 -> 367 us, 32 q / 4 kv heads x 64
 // sequences 113-115 -> 63 us (the multi-query kernel with 16-bit weights);
@@ -463,18 +463,6 @@ pkv_status decode_mfma(void* out, float* m, float* l, float* o, const void* q, c
                        int num_kv_heads, int head_dim, int64_t num_blocks, float scale, int P,
                        int NP, pkv_dtype dtype, pkv_dtype cache_dtype, hipStream_t stream) {
     const bool quant = cache_dtype != dtype;  // INT8 / FP8 / 4-bit codes with scales
-    if (quant && k_new) {
-        // the new rows are quantized into their slots first (bit-exact as
-        // pkv_kv_cache_write), then read back with the cache
-        pkv::CacheWriteArgs w{k_new, v_new, const_cast<void*>(k_cache),
-                              const_cast<void*>(v_cache), const_cast<float*>(k_scale),
-                              const_cast<float*>(v_scale), nullptr, block_tables, context_lens,
-                              max_blocks_per_seq, num_seqs, num_blocks, num_kv_heads};
-        pkv_status s = hip_status(
-            pkv::launch_kv_cache_write(w, (int)dtype, (int)cache_dtype, head_dim, stream),
-            "new-token store launch");
-        if (s != PKV_OK) return s;
-    }
     const int g = num_q_heads / num_kv_heads;
     pkv::MultiArgs a{};
     a.out = out;
@@ -500,12 +488,14 @@ pkv_status decode_mfma(void* out, float* m, float* l, float* o, const void* q, c
     a.causal = 1;
     a.one_query = 1;
     a.exact_p = 1;
-    a.k_new = quant ? nullptr : k_new;
-    a.v_new = quant ? nullptr : v_new;
-    a.k_cache_w = quant || !k_new ? nullptr : const_cast<void*>(k_cache);
-    a.v_cache_w = quant || !k_new ? nullptr : const_cast<void*>(v_cache);
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_cache_w = k_new ? const_cast<void*>(k_cache) : nullptr;
+    a.v_cache_w = k_new ? const_cast<void*>(v_cache) : nullptr;
     a.k_scale = quant ? k_scale : nullptr;
     a.v_scale = quant ? v_scale : nullptr;
+    a.k_scale_w = quant && k_new ? const_cast<float*>(k_scale) : nullptr;
+    a.v_scale_w = quant && k_new ? const_cast<float*>(v_scale) : nullptr;
     a.scale_log2 = scale * 1.44269504088896340736f;
     if ((int64_t)num_seqs * num_kv_heads * a.row_tiles * NP > 0x7fffffff)
         return fail(PKV_ERR_SHAPE, "too many work items for one launch");

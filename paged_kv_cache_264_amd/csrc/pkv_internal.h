@@ -131,11 +131,12 @@ struct MultiArgs {
     // p = hi + lo (hi = p rounded, lo = the rest rounded), so the products
     // carry fp32-level weights instead of weights rounded to 16 bits
     int exact_p;
-    // With one_query: the step's new K and V rows [B][Hkv][D] (the cache's
-    // 16-bit dtype), or null.  Sequence b's row is position context_lens[b]
-    // - 1; the work-groups that read its block take the row from here
-    // instead of the cache, and the one of row tile 0 stores it into
-    // k_cache_w / v_cache_w (the pools k_cache / v_cache, writable).
+    // With one_query: the step's new K and V rows [B][Hkv][D] (q's 16-bit
+    // dtype), or null.  Sequence b's row is position context_lens[b] - 1;
+    // the work-groups that read its block take the row (quantized as the
+    // cache write does, for a quantized cache) from here instead of the
+    // cache, and the one of row tile 0 stores it into k_cache_w / v_cache_w
+    // (the pools k_cache / v_cache, writable).
     const void* k_new;
     const void* v_new;
     void* k_cache_w;
@@ -146,6 +147,10 @@ struct MultiArgs {
     // null otherwise
     const float* k_scale;
     const float* v_scale;
+    // with k_new over a quantized cache: k_scale / v_scale, writable (the
+    // new row's scale or pair is stored there)
+    float* k_scale_w;
+    float* v_scale_w;
     float scale_log2;
 };
 
