@@ -300,21 +300,18 @@ def main():
     achieved = launch_bytes / (dec_avg_ms * 1e-3) / 1e9
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     # The library runs decodes of 8 to 63 q heads per kv head with 16-bit q
-    # over a cache of q's dtype, INT8, FP8 or 4-bit (no window) on the matrix cores:
-    # the multi-query kernel, which also stores the new token of a 16-bit
-    # cache (a quantized cache gets it from a cache-write launch first); phase
-    # 1 alone keeps the decode kernel.
+    # over a cache of q's dtype, INT8, FP8 or 4-bit (no window) on the matrix
+    # cores: the multi-query kernel, which also stores (and quantizes) the
+    # new token; phase 1 alone keeps the decode kernel.
     g = batch.Hq // batch.Hkv
     mfma_route = (args.step == "fused" and not window and 8 <= g < 64 and
                   cfg["dtype"] in ("f16", "bf16") and cfg["cache"] in (cfg["dtype"], "i8", "f8", "u4"))
-    q8_write = mfma_route and cfg["cache"] in ("i8", "f8", "u4")
     sources = MULTI_SOURCES if mfma_route else KERNEL_SOURCES
     traffic, traffic_ratio = traffic_for(f"{args.config}/{args.step}", launch_bytes, sources)
     if mfma_route:
-        kernel_label = (("kv_cache_write_kernel + " if q8_write else "") + "paged_multi_kernel" +
-                        (" + paged_reduce_kernel" if NP > 1 else "") +
-                        (" (events span the step)" if q8_write or NP > 1 else ""))
-        launches = {"kv_cache_write_kernel": 1 if q8_write else 0, "paged_multi_kernel": 1,
+        kernel_label = "paged_multi_kernel" + (" + paged_reduce_kernel (events span both)"
+                                               if NP > 1 else "")
+        launches = {"kv_cache_write_kernel": 0, "paged_multi_kernel": 1,
                     "paged_reduce_kernel": 1 if NP > 1 else 0}
     else:
         kernel_label = "paged_decode_kernel" + (" + paged_reduce_kernel (events span both)"
