@@ -159,6 +159,17 @@ __device__ __forceinline__ void load_to_lds16(__amdgpu_buffer_rsrc_t r, char* ld
 // 16 codes of an 8-bit cache (INT8, or e4m3 FP8) as 16 values of the 16-bit
 // MFMA type T, in order: both formats' values are exact in fp16 and in bf16
 // (integers up to 127; e4m3's 4 significant bits and exponents 2^-9..2^8)
+// Two e4m3 codes (bytes 0, 1 of w, or 2, 3 with HI) as a pair of T, exactly
+// (gfx950's scaled convert with scale 1: every non-NaN code pair, both word
+// selects and both output types, matched the fp32 convert and a round-trip
+// pack on the GPU)
+template <Elem T, bool HI> __device__ __forceinline__ uint32_t fp8x2_to(uint32_t w) {
+    if constexpr (T == Elem::F16)
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
 template <Elem T, Elem CE>
 __device__ __forceinline__ void widen16(const uint4& w, uint4& lo, uint4& hi) {
     const uint32_t in[4] = {w.x, w.y, w.z, w.w};
@@ -167,7 +178,9 @@ __device__ __forceinline__ void widen16(const uint4& w, uint4& lo, uint4& hi) {
     for (int i = 0; i < 4; ++i) {
         float x0, x1, x2, x3;
         if constexpr (CE == Elem::F8) {
-            f8x4_to_f32(in[i], x0, x1, x2, x3);
+            out[2 * i] = fp8x2_to<T, false>(in[i]);
+            out[2 * i + 1] = fp8x2_to<T, true>(in[i]);
+            continue;
         } else {
             x0 = (float)(int8_t)(in[i] & 0xffu);
             x1 = (float)(int8_t)((in[i] >> 8) & 0xffu);
@@ -190,11 +203,13 @@ __device__ __forceinline__ void widen32_u4(const uint4& w, uint4 out[4]) {
     const uint32_t in[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        float l0, l1, l2, l3, h0, h1, h2, h3;
-        f8x4_to_f32(in[i] & 0x0F0F0F0Fu, l0, l1, l2, l3);         // elements 8i, 8i+2, ..
-        f8x4_to_f32((in[i] >> 4) & 0x0F0F0F0Fu, h0, h1, h2, h3);  // elements 8i+1, 8i+3, ..
-        out[i] = make_uint4(Mfma<T>::pack(l0, h0), Mfma<T>::pack(l1, h1), Mfma<T>::pack(l2, h2),
-                            Mfma<T>::pack(l3, h3));
+        const uint32_t lo = in[i] & 0x0F0F0F0Fu;         // elements 8i, 8i+2, 8i+4, 8i+6
+        const uint32_t hi = (in[i] >> 4) & 0x0F0F0F0Fu;  // elements 8i+1, 8i+3, ..
+        // bytes in element order: (8i, 8i+1, 8i+2, 8i+3) and (8i+4, .., 8i+7)
+        const uint32_t a = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+        const uint32_t b = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+        out[i] = make_uint4(fp8x2_to<T, false>(a), fp8x2_to<T, true>(a), fp8x2_to<T, false>(b),
+                            fp8x2_to<T, true>(b));
     }
 }
 constexpr float kU4Unscale = 512.0f;        // undoes widen32_u4's 2^-9
