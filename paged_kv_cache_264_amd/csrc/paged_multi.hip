@@ -156,9 +156,6 @@ __device__ __forceinline__ void load_to_lds16(__amdgpu_buffer_rsrc_t r, char* ld
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voffset, 0, 0, 0);
 }
 
-// 16 codes of an 8-bit cache (INT8, or e4m3 FP8) as 16 values of the 16-bit
-// MFMA type T, in order: both formats' values are exact in fp16 and in bf16
-// (integers up to 127; e4m3's 4 significant bits and exponents 2^-9..2^8)
 // Two e4m3 codes (bytes 0, 1 of w, or 2, 3 with HI) as a pair of T, exactly
 // (gfx950's scaled convert with scale 1: every non-NaN code pair, both word
 // selects and both output types, matched the fp32 convert and a round-trip
@@ -170,25 +167,24 @@ template <Elem T, bool HI> __device__ __forceinline__ uint32_t fp8x2_to(uint32_t
         return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
+// 16 codes of an 8-bit cache (INT8, or e4m3 FP8) as 16 values of the 16-bit
+// MFMA type T, in order: both formats' values are exact in fp16 and in bf16
+// (integers up to 127; e4m3's 4 significant bits and exponents 2^-9..2^8)
 template <Elem T, Elem CE>
 __device__ __forceinline__ void widen16(const uint4& w, uint4& lo, uint4& hi) {
     const uint32_t in[4] = {w.x, w.y, w.z, w.w};
     uint32_t out[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        float x0, x1, x2, x3;
         if constexpr (CE == Elem::F8) {
             out[2 * i] = fp8x2_to<T, false>(in[i]);
             out[2 * i + 1] = fp8x2_to<T, true>(in[i]);
-            continue;
-        } else {
-            x0 = (float)(int8_t)(in[i] & 0xffu);
-            x1 = (float)(int8_t)((in[i] >> 8) & 0xffu);
-            x2 = (float)(int8_t)((in[i] >> 16) & 0xffu);
-            x3 = (float)(int8_t)(in[i] >> 24);
+        } else {  // byte-select converts of the sign-extended codes, then a pack
+            out[2 * i] = Mfma<T>::pack((float)(int8_t)(in[i] & 0xffu),
+                                       (float)(int8_t)((in[i] >> 8) & 0xffu));
+            out[2 * i + 1] = Mfma<T>::pack((float)(int8_t)((in[i] >> 16) & 0xffu),
+                                           (float)(int8_t)(in[i] >> 24));
         }
-        out[2 * i] = Mfma<T>::pack(x0, x1);
-        out[2 * i + 1] = Mfma<T>::pack(x2, x3);
     }
     lo = make_uint4(out[0], out[1], out[2], out[3]);
     hi = make_uint4(out[4], out[5], out[6], out[7]);
@@ -197,7 +193,7 @@ __device__ __forceinline__ void widen16(const uint4& w, uint4& lo, uint4& hi) {
 // 32 codes of a 4-bit cache (two per byte, element 2k in the low nibble of
 // byte k) as 32 values code * 2^-9 of the 16-bit type T, in order: a byte c
 // <= 15 read as an e4m3 code is exactly c * 2^-9 (1..7 the subnormals, 8..15
-// the normals of exponent -6), so one packed fp8 convert widens two codes
+// the normals of exponent -6), so one scaled fp8 convert widens two codes
 template <Elem T>
 __device__ __forceinline__ void widen32_u4(const uint4& w, uint4 out[4]) {
     const uint32_t in[4] = {w.x, w.y, w.z, w.w};
