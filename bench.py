@@ -299,13 +299,14 @@ def main():
     dec_ms = per_launch_events(step, args.steps)
     achieved = launch_bytes / (dec_avg_ms * 1e-3) / 1e9
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    # The library runs decodes of 8 to 63 q heads per kv head with 16-bit q
-    # over a cache of q's dtype, INT8, FP8 or 4-bit (no window) on the matrix
-    # cores: the multi-query kernel, which also stores (and quantizes) the
+    # The library runs decodes with 16-bit q of 8 to 63 q heads per kv head
+    # over a cache of q's dtype, or 4 to 63 over an INT8, FP8 or 4-bit one (no
+    # window) on the matrix cores: the multi-query kernel, which also stores (and quantizes) the
     # new token; phase 1 alone keeps the decode kernel.
     g = batch.Hq // batch.Hkv
-    mfma_route = (args.step == "fused" and not window and 8 <= g < 64 and
-                  cfg["dtype"] in ("f16", "bf16") and cfg["cache"] in (cfg["dtype"], "i8", "f8", "u4"))
+    quant = cfg["cache"] in ("i8", "f8", "u4")
+    mfma_route = (args.step == "fused" and not window and (4 if quant else 8) <= g < 64 and
+                  cfg["dtype"] in ("f16", "bf16") and (cfg["cache"] == cfg["dtype"] or quant))
     sources = MULTI_SOURCES if mfma_route else KERNEL_SOURCES
     traffic, traffic_ratio = traffic_for(f"{args.config}/{args.step}", launch_bytes, sources)
     if mfma_route:

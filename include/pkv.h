@@ -136,9 +136,9 @@ pkv_status pkv_kv_cache_write(const void* k, const void* v, void* k_cache, void*
  * the other decode entry points) use when passed partition_size == 0, for a
  * cache of cache_dtype.  A power of two in [256, 8192], chosen from the sizes
  * and the tile the decode takes (one q head, several q heads of a kv head,
- * or the matrix-core path of 8 to 63 q heads per kv head with 16-bit q over
- * a cache of q's dtype, INT8, FP8 or 4-bit; for the quantized caches the
- * size assumes 16-bit q).  Returns 0 for invalid arguments.
+ * or the matrix-core path with 16-bit q of 8 to 63 q heads per kv head over
+ * a cache of q's dtype, or 4 to 63 over an INT8, FP8 or 4-bit one; for the
+ * quantized caches the size assumes 16-bit q).  Returns 0 for invalid arguments.
  */
 int pkv_default_partition_size(int num_seqs, int num_q_heads, int num_kv_heads,
                                int max_blocks_per_seq, pkv_dtype cache_dtype);
@@ -163,9 +163,10 @@ size_t pkv_decode_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads
  * softmax results are merged exactly (online softmax: caojiahao2 section 3.2).
  * Enqueues pkv_paged_attn_decode_partials with `out` set (sequences that fit
  * in one partition are finished there) followed by pkv_paged_attn_reduce with
- * skip_single_partition = 1, using the workspace for the partials.  With 8 to
- * 63 q heads per kv head, 16-bit q and a cache of q's dtype, INT8, FP8 or
- * 4-bit, the first phase runs on the matrix cores instead (the kv head's q heads as
+ * skip_single_partition = 1, using the workspace for the partials.  With
+ * 16-bit q and 8 to 63 q heads per kv head over a cache of q's dtype, or 4 to
+ * 63 over an INT8, FP8 or 4-bit one, the first phase runs on the matrix cores
+ * instead (the kv head's q heads as
  * matrix rows, the softmax weights entered as two 16-bit parts), to the same
  * error bound.
  *

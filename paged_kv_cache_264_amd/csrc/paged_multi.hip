@@ -58,7 +58,7 @@ constexpr int kRows = 16;
 // Waves per work-group of the short-run kernel.  Runs of several queries use
 // 4 (8 measured slower on MI355X: verify 381.7 -> 389.2 us per launch,
 // shared-prefix sampling decode 97.0 -> 98.8 us).  A single query per
-// sequence (decode of 8-63 q heads per kv head) fills at most one 16-row
+// sequence (decode of 4-63 q heads per kv head) fills at most one 16-row
 // tile, so its work-groups are few and short of loads in flight: 8 waves
 // there (head_dim up to 128) took a 64-sequence, 64 q / 8 kv head bf16
 // decode from 127.1 to 118.0 us.

@@ -194,13 +194,18 @@ int pow2_partition(int64_t count, int64_t max_tokens, int64_t wgs, int cap) {
     return P;
 }
 
-// Decodes of 8 to 63 q heads per kv head with 16-bit q over a cache of q's
-// dtype or a quantized one (INT8, FP8; 4-bit from head_dim 128) run on the
-// matrix cores (the short-run multi-query kernel; see decode_mfma).
+// Decodes with 16-bit q of 8 to 63 q heads per kv head over a cache of q's
+// dtype, or 4 to 63 over a quantized one (INT8, FP8; 4-bit from head_dim
+// 128), run on the matrix cores (the short-run multi-query kernel; see
+// decode_mfma).  Measured, fused step of 64 sequences U[512, 4096], decode
+// kernel against matrix cores: 4 q heads per kv head, INT8 / bf16 q 86.0 vs
+// 66.7 us, FP8 95.1 vs 72.0, 4-bit 81.6 vs 66.0, bf16 cache (128 x
+// U[1024, 8192]) 365.4 vs 367.3; 2 per kv head, INT8 125.4 vs 135.1, 4-bit
+// 88.9 vs 128.1.
 bool decode_on_matrix_cores(int g, int window, pkv_dtype q_dtype, pkv_dtype cache_dtype) {
-    return window == 0 && g >= 8 && g < 64 && (q_dtype == PKV_F16 || q_dtype == PKV_BF16) &&
-           (cache_dtype == q_dtype || cache_dtype == PKV_I8 || cache_dtype == PKV_F8_E4M3 ||
-            cache_dtype == PKV_U4);
+    const bool quant = cache_dtype == PKV_I8 || cache_dtype == PKV_F8_E4M3 || cache_dtype == PKV_U4;
+    return window == 0 && g >= (quant ? 4 : 8) && g < 64 &&
+           (q_dtype == PKV_F16 || q_dtype == PKV_BF16) && (cache_dtype == q_dtype || quant);
 }
 
 // Measured on MI355X: a work-group pays a chain of dependent memory round
@@ -439,7 +444,7 @@ pkv_status decode_phase1(void* out, float* m_part, float* l_part, float* o_part,
                       "paged decode launch");
 }
 
-// The decode of q-head groups of 8 to 63 per kv head (16-bit q; a cache of
+// The decode of q-head groups of 8 (4 over a quantized cache) to 63 per kv head (16-bit q; a cache of
 // q's dtype, INT8 or FP8; no window) on the matrix cores: the decode
 // kernel's tiles of 8 heads keep 8 dot products per K row in vector
 // registers and run at about half the HBM rate, while the short-run

@@ -139,7 +139,7 @@ def test_workspace_size(lib):
     assert d(4, 32, 8, 2048, BF16) == 4096       # GQA: 32 items, 32k tokens
     assert d(1, 32, 8, 2048, BF16) == 1024       # GQA: 8 items, 32k tokens
     assert d(64, 32, 8, 256, BF16) == 4096       # GQA: 512 items, 4k tokens (cap)
-    assert d(16, 32, 8, 256, I8) == 2048         # 4 heads per kv head, one INT8 tile: 128 tiles
+    assert d(16, 32, 8, 256, F16) == 2048        # 4 heads per kv head, one 16-bit tile: 128 tiles
     assert d(16, 16, 8, 256, U4) == 2048         # 2 heads per kv head, one 4-bit tile: 128 tiles
     # >= 1024 items already fill the chip: up to 8192 tokens
     assert d(128, 32, 8, 512, BF16) == 8192      # the GQA batch: no sequence split
@@ -150,8 +150,11 @@ def test_workspace_size(lib):
     assert d(16, 32, 32, 64, I8) == 1024
     assert d(1, 32, 32, 256, F16) == 256         # 4096 tokens: split
     assert d(1, 32, 8, 64, BF16) == 256          # GQA tiles keep the rule
-    # 8 to 63 q heads per kv head (the matrix cores; 16-bit q assumed for a
-    # quantized cache): the own rule over (sequence, kv head, 16-row tile) items
+    # 8 to 63 q heads per kv head, 4 to 63 over a quantized cache (the matrix
+    # cores; 16-bit q assumed for a quantized cache): the own rule over
+    # (sequence, kv head, 16-row tile) items
+    assert d(16, 32, 8, 256, I8) == 2048         # 4 per kv head: 128 row tiles, 4k tokens
+    assert d(4, 32, 8, 1024, F8) == 2048         # 32 row tiles, 16k tokens
     assert d(64, 32, 4, 256, I8) == 4096         # 256 row tiles, 4k tokens
     assert d(32, 32, 2, 256, U4) == 1024         # 64 row tiles, 4k tokens
     assert d(64, 64, 8, 256, F8) == 4096         # 512 row tiles (cap)

@@ -501,9 +501,10 @@ def test_large_batch_natural_order(pkv):
 def test_decode_append_matches_write_then_decode(pkv, dtype, cache, D, Hq, Hkv, P):
     """The fused step equals the cache write of the new tokens followed by the
     decode: cache bytes bit-exact against the oracle's write, outputs within
-    the dtype bound.  (8 to 63 q heads per kv head over a 16-bit cache take
-    the matrix cores, where one of a kv head's 1-3 row tiles stores the row
-    and every one computes with the given row.)"""
+    the dtype bound.  (With 16-bit q, 8 to 63 q heads per kv head, or 4 to 63
+    over a quantized cache, take the matrix cores, where one of a kv head's
+    1-3 row tiles stores the row, quantized there for a quantized cache, and
+    every one computes with it.)"""
     lens = [1, 16, 17, 300, 33, 0, 129]
     batch = W.make_batch(cfg=_cfg(dtype, cache, D, Hq, Hkv, lens, seed=D + P), device="cuda")
     gpu_populate(pkv, batch)

@@ -9,7 +9,7 @@ three decode entry points (plain, fused append, sliding window with a random
 window).  Every case compares every output element with the oracle at the
 dtype bound, and checks that nothing is written around the output buffer or
 the caller's workspace (sentinel guard bands).  A second sweep of 64 cases
-(default_rng([2027, i])) takes 8 to 63 q heads per kv head with 16-bit q,
+(default_rng([2027, i])) takes 4 to 63 q heads per kv head with 16-bit q,
 the decodes that run on the matrix cores, over every cache format.
 """
 from __future__ import annotations
@@ -107,9 +107,10 @@ def test_random_shape_sweep(pkv, chunk):
     print(f"[sweep chunk {chunk}] worst err/tol {worst:.3f}", flush=True)
 
 
-# The matrix-core decode (8 to 63 q heads per kv head, 16-bit q): groups
-# that fill one to four 16-row tiles, every cache format it takes, the plain
-# and fused calls, and (off the route) sliding windows.
+# The matrix-core decode (16-bit q; 8 to 63 q heads per kv head, 4 to 63
+# over a quantized cache): groups that fill one to four 16-row tiles, every
+# cache format it takes, the plain and fused calls, and (off the route)
+# sliding windows.
 ROUTE_PAIRS = [("f16", "f16"), ("bf16", "bf16"), ("f16", "i8"), ("bf16", "i8"), ("f16", "f8"),
                ("bf16", "f8"), ("f16", "u4"), ("bf16", "u4")]
 N_ROUTE, N_ROUTE_CHUNKS = 64, 4
@@ -119,7 +120,7 @@ def draw_route_case(i: int) -> dict:
     g = np.random.default_rng([2027, i])
     dtype, cache = ROUTE_PAIRS[int(g.integers(len(ROUTE_PAIRS)))]
     D = int(g.choice([128, 256])) if cache == "u4" else int(g.choice([64, 128, 256]))
-    group = int(g.choice([8, 12, 16, 24, 32, 48, 63]))
+    group = int(g.choice([4, 8, 12, 16, 24, 32, 48, 63]))
     Hkv = int(g.integers(1, 3))
     B = int(g.integers(1, 7))
     lens = g.integers(0, 601, size=B)
