@@ -16,7 +16,7 @@
 // dense contraction, so it runs on the matrix cores.
 //   * rows: the (query token, q head) pairs that read one kv head, 16 per
 //     tile; a work-group is one (sequence, kv head, row tile, partition) with
-//     4 waves (8 for one query per sequence), each streaming a contiguous run of the partition's blocks.
+//     4 waves (6 or 8 for one query per sequence), each streaming a contiguous run of the partition's blocks.
 //   * scores: S^T = K Q^T, one v_mfma_f32_16x16x32 per 32 channels.  The A
 //     operand is the K tile (lane l: token l%16, 8 channels), fetched from
 //     the pool in token order and staged in a per-wave LDS tile; the B
@@ -59,11 +59,16 @@ constexpr int kRows = 16;
 // 4 (8 measured slower on MI355X: verify 381.7 -> 389.2 us per launch,
 // shared-prefix sampling decode 97.0 -> 98.8 us).  A single query per
 // sequence (decode of 4-63 q heads per kv head) fills at most one 16-row
-// tile, so its work-groups are few and short of loads in flight: 8 waves
-// there (head_dim up to 128) took a 64-sequence, 64 q / 8 kv head bf16
-// decode from 127.1 to 118.0 us.
+// tile, so its work-groups are few and short of loads in flight: more waves
+// each stream a share of the item's blocks.  Over a 16-bit cache 6 (two
+// work-groups of 168 registers fit a CU; against 8, one per CU: 64 q / 8 kv
+// heads bf16 x 64 sequences 104.3 -> 103.2 us, 32 q / 4 kv heads 62.5 ->
+// 59.9, 32 q / 2 kv heads x 16 19.6 -> 18.5); over a quantized cache 8
+// (6 measured 3-17% slower: its per-block widening wants the waves).  Four
+// waves measured slower for both (127.1 against 118.0 us at 8, bf16).
 constexpr int kWavesRuns = 4;
-constexpr int kWavesOneQuery = 8;
+constexpr int kWavesOneQuery16 = 6;
+constexpr int kWavesOneQueryQ = 8;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kNegBig = -3.0e38f;
 // The running max of a row is the reference the weights are taken against,
@@ -1256,9 +1261,8 @@ hipError_t launch_dw(const MultiArgs& a, int64_t grid, hipStream_t s) {
     if constexpr (CE == Elem::U4 && D < 128) {
         return hipErrorInvalidValue;
     } else {
-    // (at head_dim 256 eight waves would spill registers to memory; four
-    // measured slower at 128 for 16-bit and 8-bit caches alike)
-    constexpr int WQ = kWavesOneQuery;
+    // (at head_dim 256 more than four waves would spill registers to memory)
+    constexpr int WQ = CE == T ? kWavesOneQuery16 : kWavesOneQueryQ;
     if constexpr (D <= 128) {
         if (a.one_query) {
             const dim3 blk(WQ * 64);
