@@ -497,14 +497,15 @@ def test_large_batch_natural_order(pkv):
 @pytest.mark.parametrize("dtype,cache,D,Hq,Hkv,P", _supported(
     [(d, c) + shape for d, c in PAIRS
      for shape in [(128, 8, 8, 0), (64, 16, 2, 32), (256, 4, 1, 64), (128, 8, 2, 0),
-                   (128, 16, 2, 64), (256, 16, 2, 0), (128, 48, 1, 64)]]))
+                   (128, 16, 2, 64), (256, 16, 2, 0), (128, 48, 1, 64), (128, 64, 16, 0),
+                   (128, 128, 16, 0)]]))
 def test_decode_append_matches_write_then_decode(pkv, dtype, cache, D, Hq, Hkv, P):
     """The fused step equals the cache write of the new tokens followed by the
     decode: cache bytes bit-exact against the oracle's write, outputs within
     the dtype bound.  (With 16-bit q, 8 to 63 q heads per kv head, or 4 to 63
     over a quantized cache, take the matrix cores, where one of a kv head's
     1-3 row tiles stores the row, quantized there for a quantized cache, and
-    every one computes with it.)"""
+    every one computes with it; 16 kv heads take the XCD head order.)"""
     lens = [1, 16, 17, 300, 33, 0, 129]
     batch = W.make_batch(cfg=_cfg(dtype, cache, D, Hq, Hkv, lens, seed=D + P), device="cuda")
     gpu_populate(pkv, batch)
